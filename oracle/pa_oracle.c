@@ -1,0 +1,460 @@
+/*
+ * pa_oracle.c -- plain, slow fp64 CPU oracle for paged GQA attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * bench's CPU-baseline leg may load this file's library.  It shares no code,
+ * header, table or helper with the HIP library; it decodes bf16 and fp8 itself
+ * and walks the block table itself.
+ *
+ * What it computes (all arithmetic in double):
+ *
+ *  decode   For sequence b with L cached tokens and query head h, the key/value
+ *           head is g = h / (Hq/Hkv) (contiguous grouping, as in the
+ *           `_fwd_grouped_kernel_stage1` of "vllm/attention/ops/
+ *           triton_decode_attention.py" and `cur_kv_head` in `_fwd_kernel` of
+ *           "vllm/attention/ops/prefix_prefill.py").  Token t lives in
+ *           physical page bt[b][t / P] at row t % P (the `Req_to_tokens`
+ *           lookup of `_fwd_kernel_stage1`; the `[num_blocks, P, Hkv, D]`
+ *           view of `_kv_cache_views` in the vLLM "b12x" backend page).
+ *           The query is the token at position L-1; its own key/value is
+ *           already in the cache (the b12x page writes the new token with
+ *           `do_kv_cache_update` before attention runs).
+ *           Keys t in [lo, L) are attended, lo = max(0, L-W) when a sliding
+ *           window W > 0 is given: a key is kept iff pos_q - pos_k < W
+ *           (the b12x page stores `window_left = sliding_window - 1`; the
+ *           prefix_prefill `_fwd_kernel` keeps `pos_q - pos_k < SLIDING_WINDOW`).
+ *             s_t   = scale * <q, k_t>,   k_t = dec(K) * k_scale
+ *             s_t   = c * tanh(s_t / c)   if the soft-cap c > 0 (applied after
+ *                                         the scale, as `logit_cap` in
+ *                                         `_fwd_kernel_stage1`)
+ *             out   = sum_t exp(s_t - m) v_t / sum_t exp(s_t - m),  m = max s_t
+ *             lse   = m + ln sum_t exp(s_t - m)
+ *           An empty key range (L == 0) gives a zero row and lse = -inf
+ *           (the b12x `forward` zero-fills its output when there is nothing
+ *           to attend).
+ *
+ *  split    The key range [lo, L) is cut into S contiguous parts of
+ *           ceil(n/S) tokens (the split partition of `_fwd_kernel_stage1`);
+ *           each non-empty part yields (o_s, lse_s) by the definition above
+ *           and the parts are merged as in `_fwd_kernel_stage2`:
+ *             out = sum_s exp(lse_s - M) o_s / sum_s exp(lse_s - M),
+ *             M = max_s lse_s, empty parts skipped.
+ *
+ *  extend   For sequence b with C cached tokens and n = cu[b+1]-cu[b] new
+ *           tokens, new row i sits at position C + i and attends to every
+ *           cached token j < C (through the pages, no causal mask) and to new
+ *           tokens C+i' with i' <= i (contiguous k_new/v_new rows cu[b]+i'),
+ *           with the same window rule, scale, soft-cap and softmax; the output
+ *           is the normalised softmax-weighted sum (the two loops of
+ *           `_fwd_kernel` in "vllm/attention/ops/prefix_prefill.py", and
+ *           the final `acc / l_i` of `_fwd_kernel_flash_attn_v2`).  The cache
+ *           scales apply to cached keys/values only; new rows are bf16.
+ *
+ * Element decoding:
+ *   bf16    the 16 bits are the high half of an IEEE binary32.
+ *   e4m3fn  OCP 8-bit float: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa
+ *           bits, subnormals when the exponent field is 0, S.1111.111 is NaN,
+ *           no infinities (largest finite 448).
+ *
+ * Threads: the outer (row) loop is shared between `threads` POSIX threads;
+ * each output row is computed by exactly one thread in a fixed order, so the
+ * result does not depend on the thread count.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORC_KV_BF16 = 0, ORC_KV_E4M3FN = 1 };
+
+double orc_bf16(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+double orc_e4m3fn(uint8_t bits)
+{
+    int sign = bits >> 7;
+    int expo = (bits >> 3) & 0xF;
+    int mant = bits & 0x7;
+    double mag;
+    if (expo == 0xF && mant == 0x7)
+        return NAN;
+    if (expo == 0)
+        mag = ldexp((double)mant, -9);              /* (mant/8) * 2^(1-7) */
+    else
+        mag = ldexp((double)(8 + mant), expo - 10); /* (1+mant/8) * 2^(expo-7) */
+    return sign ? -mag : mag;
+}
+
+/* One cached element: page `page`, row `row`, head `g`, lane `d`. */
+static double cache_elem(const void *pool, int kv_dtype, int64_t page, int row,
+                         int g, int d, int P, int Hkv, int D)
+{
+    int64_t idx = ((page * P + row) * (int64_t)Hkv + g) * D + d;
+    if (kv_dtype == ORC_KV_E4M3FN)
+        return orc_e4m3fn(((const uint8_t *)pool)[idx]);
+    return orc_bf16(((const uint16_t *)pool)[idx]);
+}
+
+/* ------------------------------------------------------------------ */
+/* Shared problem description                                          */
+/* ------------------------------------------------------------------ */
+typedef struct {
+    int B, Hq, Hkv, D, P, kv_dtype;
+    const uint16_t *q;          /* decode [B][Hq][D]; extend [total_q][Hq][D] */
+    const void *k_pool, *v_pool;/* [num_pages][P][Hkv][D] */
+    int64_t num_pages;
+    const int32_t *bt;          /* [B][bt_stride] */
+    int64_t bt_stride;
+    const int32_t *seq_lens;    /* decode: cached tokens incl. the query token */
+    double scale, softcap, k_scale, v_scale;
+    int window;
+    int num_splits;             /* decode: 0 = one pass over the key range */
+    /* extend */
+    const uint16_t *k_new, *v_new; /* [total_q][Hkv][D] */
+    const int32_t *cu_q, *ctx_lens;
+    const int64_t *rows;        /* token rows to compute (extend); NULL = all */
+    int64_t n_rows;
+    /* outputs */
+    double *out, *lse;
+    int status;
+} orc_problem;
+
+/*
+ * Softmax-weighted sum over a list of keys given as (score, value row).
+ * The definition: out = sum exp(s - m) v / sum exp(s - m), lse = m + ln(sum).
+ */
+static void softmax_sum(const double *s, const double *v, int64_t n, int D,
+                        double *out, double *lse)
+{
+    double m = -INFINITY, z = 0.0;
+    int64_t t;
+    int d;
+    for (d = 0; d < D; ++d)
+        out[d] = 0.0;
+    if (n == 0) {
+        *lse = -INFINITY;
+        return;
+    }
+    for (t = 0; t < n; ++t)
+        if (s[t] > m)
+            m = s[t];
+    for (t = 0; t < n; ++t) {
+        double w = exp(s[t] - m);
+        z += w;
+        for (d = 0; d < D; ++d)
+            out[d] += w * v[t * D + d];
+    }
+    for (d = 0; d < D; ++d)
+        out[d] /= z;
+    *lse = m + log(z);
+}
+
+static double cap_score(double s, double c)
+{
+    return c > 0.0 ? c * tanh(s / c) : s;
+}
+
+/* Gather keys [t0, t1) of (b, g) from the cache: scores against q, and values. */
+static void gather_cached(const orc_problem *pr, int b, int g, const double *q,
+                          int64_t t0, int64_t t1, double *s, double *v)
+{
+    int64_t t;
+    int d;
+    for (t = t0; t < t1; ++t) {
+        int64_t page = pr->bt[b * pr->bt_stride + t / pr->P];
+        int row = (int)(t % pr->P);
+        double dot = 0.0;
+        for (d = 0; d < pr->D; ++d) {
+            double k = cache_elem(pr->k_pool, pr->kv_dtype, page, row, g, d,
+                                  pr->P, pr->Hkv, pr->D) * pr->k_scale;
+            dot += q[d] * k;
+            v[(t - t0) * pr->D + d] =
+                cache_elem(pr->v_pool, pr->kv_dtype, page, row, g, d, pr->P,
+                           pr->Hkv, pr->D) * pr->v_scale;
+        }
+        s[t - t0] = cap_score(pr->scale * dot, pr->softcap);
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Decode                                                              */
+/* ------------------------------------------------------------------ */
+static void decode_row(const orc_problem *pr, int b, int h, double *q,
+                       double *s, double *v, double *os, double *lses)
+{
+    int G = pr->Hq / pr->Hkv;
+    int g = h / G;
+    int D = pr->D;
+    int64_t L = pr->seq_lens[b];
+    int64_t lo = (pr->window > 0 && L - pr->window > 0) ? L - pr->window : 0;
+    double *out = pr->out + ((int64_t)b * pr->Hq + h) * D;
+    double *lse = pr->lse + (int64_t)b * pr->Hq + h;
+    int d;
+
+    for (d = 0; d < D; ++d)
+        q[d] = orc_bf16(pr->q[((int64_t)b * pr->Hq + h) * D + d]);
+
+    if (pr->num_splits <= 0) {
+        gather_cached(pr, b, g, q, lo, L, s, v);
+        softmax_sum(s, v, L - lo, D, out, lse);
+        return;
+    }
+
+    /* Split partition, then the log-sum-exp merge of the parts. */
+    {
+        int S = pr->num_splits, sp;
+        int64_t n = L - lo;
+        int64_t len = (n + S - 1) / S;
+        double M = -INFINITY, z = 0.0;
+        for (sp = 0; sp < S; ++sp) {
+            int64_t a = lo + len * sp;
+            int64_t e = a + len < L ? a + len : L;
+            if (e <= a) {
+                lses[sp] = -INFINITY;
+                continue;
+            }
+            gather_cached(pr, b, g, q, a, e, s, v);
+            softmax_sum(s, v, e - a, D, os + (int64_t)sp * D, &lses[sp]);
+            if (lses[sp] > M)
+                M = lses[sp];
+        }
+        for (d = 0; d < D; ++d)
+            out[d] = 0.0;
+        if (M == -INFINITY) {
+            *lse = -INFINITY;
+            return;
+        }
+        for (sp = 0; sp < S; ++sp) {
+            double w;
+            if (lses[sp] == -INFINITY)
+                continue;
+            w = exp(lses[sp] - M);
+            z += w;
+            for (d = 0; d < D; ++d)
+                out[d] += w * os[(int64_t)sp * D + d];
+        }
+        for (d = 0; d < D; ++d)
+            out[d] /= z;
+        *lse = M + log(z);
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Extend                                                              */
+/* ------------------------------------------------------------------ */
+static void extend_row(const orc_problem *pr, int64_t r, int h, double *q,
+                       double *s, double *v)
+{
+    int G = pr->Hq / pr->Hkv;
+    int g = h / G;
+    int D = pr->D;
+    int b = 0, d;
+    int64_t C, i, pos, j, n = 0;
+    double lse;
+
+    while (b + 1 < pr->B && pr->cu_q[b + 1] <= r)
+        ++b;
+    C = pr->ctx_lens[b];
+    i = r - pr->cu_q[b];
+    pos = C + i;
+    for (d = 0; d < D; ++d)
+        q[d] = orc_bf16(pr->q[(r * pr->Hq + h) * D + d]);
+
+    /* cached keys j < C, through the block table */
+    for (j = 0; j < C; ++j) {
+        if (pr->window > 0 && pos - j >= pr->window)
+            continue;
+        gather_cached(pr, b, g, q, j, j + 1, s + n, v + n * D);
+        ++n;
+    }
+    /* new keys C + i' for i' <= i, contiguous rows */
+    for (j = 0; j <= i; ++j) {
+        int64_t row = pr->cu_q[b] + j;
+        double dot = 0.0;
+        if (pr->window > 0 && pos - (C + j) >= pr->window)
+            continue;
+        for (d = 0; d < D; ++d) {
+            dot += q[d] * orc_bf16(pr->k_new[(row * pr->Hkv + g) * D + d]);
+            v[n * D + d] = orc_bf16(pr->v_new[(row * pr->Hkv + g) * D + d]);
+        }
+        s[n] = cap_score(pr->scale * dot, pr->softcap);
+        ++n;
+    }
+    softmax_sum(s, v, n, D, pr->out + (r * pr->Hq + h) * D, &lse);
+}
+
+/* ------------------------------------------------------------------ */
+/* Threading: rows are dealt by an atomic counter.                     */
+/* ------------------------------------------------------------------ */
+typedef struct {
+    orc_problem *pr;
+    int is_extend;
+    int64_t n_items;
+    int64_t max_keys;
+    int64_t *next;
+    pthread_mutex_t *mu;
+} orc_job;
+
+static void *worker(void *arg)
+{
+    orc_job *job = (orc_job *)arg;
+    orc_problem *pr = job->pr;
+    int D = pr->D;
+    int S = pr->num_splits > 0 ? pr->num_splits : 1;
+    double *q = malloc(sizeof(double) * D);
+    double *s = malloc(sizeof(double) * (job->max_keys + 1));
+    double *v = malloc(sizeof(double) * (job->max_keys + 1) * D);
+    double *os = malloc(sizeof(double) * S * D);
+    double *lses = malloc(sizeof(double) * S);
+    if (!q || !s || !v || !os || !lses) {
+        pthread_mutex_lock(job->mu);
+        pr->status = -2;
+        pthread_mutex_unlock(job->mu);
+        goto done;
+    }
+    for (;;) {
+        int64_t it;
+        pthread_mutex_lock(job->mu);
+        it = (*job->next)++;
+        pthread_mutex_unlock(job->mu);
+        if (it >= job->n_items)
+            break;
+        if (job->is_extend) {
+            int64_t r = pr->rows ? pr->rows[it / pr->Hq] : it / pr->Hq;
+            extend_row(pr, r, (int)(it % pr->Hq), q, s, v);
+        } else {
+            decode_row(pr, (int)(it / pr->Hq), (int)(it % pr->Hq), q, s, v, os,
+                       lses);
+        }
+    }
+done:
+    free(q);
+    free(s);
+    free(v);
+    free(os);
+    free(lses);
+    return NULL;
+}
+
+static int run_jobs(orc_problem *pr, int is_extend, int64_t n_items,
+                    int64_t max_keys, int threads)
+{
+    pthread_t *tid;
+    orc_job job;
+    pthread_mutex_t mu = PTHREAD_MUTEX_INITIALIZER;
+    int64_t next = 0;
+    int t;
+    if (threads < 1)
+        threads = 1;
+    tid = malloc(sizeof(pthread_t) * threads);
+    if (!tid)
+        return -2;
+    job.pr = pr;
+    job.is_extend = is_extend;
+    job.n_items = n_items;
+    job.max_keys = max_keys;
+    job.next = &next;
+    job.mu = &mu;
+    pr->status = 0;
+    for (t = 0; t < threads; ++t)
+        pthread_create(&tid[t], NULL, worker, &job);
+    for (t = 0; t < threads; ++t)
+        pthread_join(tid[t], NULL);
+    free(tid);
+    return pr->status;
+}
+
+static int check_common(int B, int Hq, int Hkv, int D, int P, int kv_dtype)
+{
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || P <= 0)
+        return -1;
+    if (Hq % Hkv != 0)
+        return -1;
+    if (kv_dtype != ORC_KV_BF16 && kv_dtype != ORC_KV_E4M3FN)
+        return -1;
+    return 0;
+}
+
+/*
+ * Decode oracle.  out [B][Hq][D] and lse [B][Hq] (natural log) are written.
+ * num_splits == 0 evaluates the definition in one pass over the key range;
+ * num_splits > 0 evaluates the split partition and the log-sum-exp merge.
+ * Returns 0, -1 on a bad argument, -2 when memory runs out.
+ */
+int orc_decode(int B, int Hq, int Hkv, int D, int P, int kv_dtype,
+               const uint16_t *q, const void *k_pool, const void *v_pool,
+               int64_t num_pages, const int32_t *block_table,
+               int64_t bt_stride, const int32_t *seq_lens, double scale,
+               double softcap, int window, double k_scale, double v_scale,
+               int num_splits, double *out, double *lse, int threads)
+{
+    orc_problem pr;
+    int64_t max_keys = 0;
+    int b;
+    if (check_common(B, Hq, Hkv, D, P, kv_dtype) || num_splits < 0)
+        return -1;
+    memset(&pr, 0, sizeof pr);
+    pr.B = B; pr.Hq = Hq; pr.Hkv = Hkv; pr.D = D; pr.P = P;
+    pr.kv_dtype = kv_dtype;
+    pr.q = q; pr.k_pool = k_pool; pr.v_pool = v_pool;
+    pr.num_pages = num_pages;
+    pr.bt = block_table; pr.bt_stride = bt_stride; pr.seq_lens = seq_lens;
+    pr.scale = scale; pr.softcap = softcap; pr.window = window;
+    pr.k_scale = k_scale; pr.v_scale = v_scale;
+    pr.num_splits = num_splits;
+    pr.out = out; pr.lse = lse;
+    for (b = 0; b < B; ++b) {
+        if (seq_lens[b] < 0)
+            return -1;
+        if (seq_lens[b] > max_keys)
+            max_keys = seq_lens[b];
+    }
+    return run_jobs(&pr, 0, (int64_t)B * Hq, max_keys, threads);
+}
+
+/*
+ * Extend oracle.  Computes output rows for the token indices listed in
+ * `rows` (n_rows of them), or for every token when rows == NULL
+ * (n_rows = total_q).  out is [total_q][Hq][D]; only listed rows are written.
+ */
+int orc_extend(int B, int Hq, int Hkv, int D, int P, int kv_dtype,
+               const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
+               const int32_t *cu_seqlens_q, const int32_t *ctx_lens,
+               const void *k_pool, const void *v_pool, int64_t num_pages,
+               const int32_t *block_table, int64_t bt_stride, double scale,
+               double softcap, int window, double k_scale, double v_scale,
+               const int64_t *rows, int64_t n_rows, double *out, int threads)
+{
+    orc_problem pr;
+    int64_t max_keys = 0;
+    int b;
+    if (check_common(B, Hq, Hkv, D, P, kv_dtype) || B < 1)
+        return -1;
+    memset(&pr, 0, sizeof pr);
+    pr.B = B; pr.Hq = Hq; pr.Hkv = Hkv; pr.D = D; pr.P = P;
+    pr.kv_dtype = kv_dtype;
+    pr.q = q; pr.k_new = k_new; pr.v_new = v_new;
+    pr.cu_q = cu_seqlens_q; pr.ctx_lens = ctx_lens;
+    pr.k_pool = k_pool; pr.v_pool = v_pool; pr.num_pages = num_pages;
+    pr.bt = block_table; pr.bt_stride = bt_stride;
+    pr.scale = scale; pr.softcap = softcap; pr.window = window;
+    pr.k_scale = k_scale; pr.v_scale = v_scale;
+    pr.rows = rows; pr.n_rows = n_rows;
+    pr.out = out;
+    for (b = 0; b < B; ++b) {
+        int64_t n = cu_seqlens_q[b + 1] - cu_seqlens_q[b];
+        if (n < 0 || ctx_lens[b] < 0)
+            return -1;
+        if (ctx_lens[b] + n > max_keys)
+            max_keys = ctx_lens[b] + n;
+    }
+    if (!rows)
+        n_rows = cu_seqlens_q[B];
+    return run_jobs(&pr, 1, n_rows * Hq, max_keys, threads);
+}

@@ -1,0 +1,75 @@
+"""Dense references for pinning the oracle: torch's scaled_dot_product_attention
+in float64 on the CPU, fed with keys/values materialised through the block
+table by NumPy indexing.  (Test-side code; shares nothing with the oracle.)"""
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+from paged_gqa_attention_02_amd.inputs import bits_to_float
+
+
+def dense_tokens(kv, b, L, kv_dtype):
+    """Keys/values of sequence b, positions [0, L), as float64 [L, Hkv, D]."""
+    P = kv.page_size
+    t = np.arange(L)
+    pages = kv.block_table[b, t // P].astype(np.int64)
+    k = bits_to_float(kv.k_pool[pages, t % P], kv_dtype).astype(np.float64)
+    v = bits_to_float(kv.v_pool[pages, t % P], kv_dtype).astype(np.float64)
+    return k, v
+
+
+def _sdpa(q, k, v, scale, mask=None):
+    """q [H, n, D], k/v [H, m, D] float64 -> [H, n, D]."""
+    return F.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(k)[None],
+        torch.from_numpy(v)[None], attn_mask=mask, scale=scale)[0].numpy()
+
+
+def sdpa_decode(case):
+    """Decode without soft-cap through the library routine."""
+    assert case.softcap == 0
+    B, Hq, D = case.batch, case.num_q_heads, case.head_dim
+    G = Hq // case.num_kv_heads
+    out = np.zeros((B, Hq, D))
+    for b in range(B):
+        L = int(case.seq_lens[b])
+        lo = max(0, L - case.window) if case.window > 0 else 0
+        if L == 0:
+            continue
+        k, v = dense_tokens(case.kv, b, L, case.kv_dtype)
+        k = np.repeat(k[lo:] * case.k_scale, G, axis=1).transpose(1, 0, 2)
+        v = np.repeat(v[lo:] * case.v_scale, G, axis=1).transpose(1, 0, 2)
+        q = bits_to_float(case.q[b], "bf16").astype(np.float64)[:, None, :]
+        out[b] = _sdpa(q, np.ascontiguousarray(k), np.ascontiguousarray(v),
+                       case.scale)[:, 0, :]
+    return out
+
+
+def sdpa_extend(case):
+    """Extend without soft-cap: SDPA with an explicit keep-mask
+    (all cached keys, causal among new keys, optional window)."""
+    assert case.softcap == 0
+    Hq, D = case.num_q_heads, case.head_dim
+    G = Hq // case.num_kv_heads
+    out = np.zeros((case.total_q, Hq, D))
+    for b in range(case.batch):
+        a, e = int(case.cu_seqlens_q[b]), int(case.cu_seqlens_q[b + 1])
+        n, C = e - a, int(case.ctx_lens[b])
+        if n == 0:
+            continue
+        kc, vc = dense_tokens(case.kv, b, C, case.kv_dtype)
+        kn = bits_to_float(case.k_new[a:e], "bf16").astype(np.float64)
+        vn = bits_to_float(case.v_new[a:e], "bf16").astype(np.float64)
+        k = np.concatenate([kc * case.k_scale, kn])
+        v = np.concatenate([vc * case.v_scale, vn])
+        k = np.ascontiguousarray(np.repeat(k, G, axis=1).transpose(1, 0, 2))
+        v = np.ascontiguousarray(np.repeat(v, G, axis=1).transpose(1, 0, 2))
+        qpos = C + np.arange(n)[:, None]
+        kpos = np.arange(C + n)[None, :]
+        keep = kpos <= qpos
+        if case.window > 0:
+            keep &= (qpos - kpos) < case.window
+        q = bits_to_float(case.q[a:e], "bf16").astype(np.float64).transpose(1, 0, 2)
+        out[a:e] = _sdpa(np.ascontiguousarray(q), k, v, case.scale,
+                         torch.from_numpy(keep)).transpose(1, 0, 2)
+    return out

@@ -1,0 +1,328 @@
+"""Pins of the fp64 oracle against what the definitions and mathematics fix.
+
+Every check here runs on the CPU.  The oracle is compared with
+* torch's ``scaled_dot_product_attention`` in float64 (the textbook routine)
+  on keys/values materialised by NumPy indexing through the block table,
+* closed forms (one key, window 1, identical keys, zero scores, soft-cap
+  saturation, two-key softmax),
+* invariances the method guarantees (physical page order, page size, split
+  count), and
+* an independent NumPy brute force.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from paged_gqa_attention_02_amd import inputs as I
+from tests._dense import dense_tokens, sdpa_decode, sdpa_extend
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def close(a, b, rtol=1e-10, atol=1e-12):
+    np.testing.assert_allclose(a, b, rtol=rtol, atol=atol)
+
+
+def rand_decode(lens, Hq, Hkv, D, P, seed, **kw):
+    rng = np.random.default_rng(seed)
+    return I.make_decode(f"r{seed}", lens, Hq, Hkv, D, P, seed, lens_rng=rng, **kw)
+
+
+# ---------------------------------------------------------------- encodings
+def test_bf16_decode_all_codes(oracle_mod):
+    codes = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(codes.view(np.int16)).view(torch.bfloat16).double().numpy()
+    got = np.array([oracle_mod.decode_bf16(int(c)) for c in codes[::257]])
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref[::257]))
+    ok = ~np.isnan(got)
+    np.testing.assert_array_equal(got[ok], ref[::257][ok])
+
+
+def test_e4m3fn_decode_all_codes_vs_torch(oracle_mod):
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    got = np.array([oracle_mod.decode_e4m3fn(int(c)) for c in codes])
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(got)
+    np.testing.assert_array_equal(got[ok], ref[ok])
+
+
+def test_e4m3fn_published_values(oracle_mod):
+    with open(os.path.join(GOLDEN, "e4m3fn_values.json")) as f:
+        g = json.load(f)
+    for code, val in g["values"].items():
+        got = oracle_mod.decode_e4m3fn(int(code, 16))
+        if val == "nan":
+            assert math.isnan(got), code
+        else:
+            assert got == float(val) and math.copysign(1, got) == math.copysign(1, float(val)), code
+
+
+# ------------------------------------------------------ library routine pins
+@pytest.mark.parametrize("lens,Hq,Hkv,D,P,window", [
+    ([37, 100], 4, 1, 64, 16, 0),          # tiny workload shape
+    ([1, 17, 64, 65], 8, 2, 128, 16, 0),   # ragged, exact page multiples
+    ([33, 90, 7], 8, 8, 64, 1, 0),          # MHA, one token per page
+    ([200, 129], 16, 2, 128, 64, 0),        # G 8, large pages
+    ([150, 60, 300], 8, 2, 64, 16, 50),     # sliding window
+    ([150, 60, 300], 8, 2, 64, 16, 1),      # window of one key
+])
+def test_decode_equals_sdpa(oracle_mod, lens, Hq, Hkv, D, P, window):
+    case = rand_decode(lens, Hq, Hkv, D, P, 11, window=window)
+    out, _ = oracle_mod.decode(case)
+    close(out, sdpa_decode(case))
+
+
+def test_decode_fp8_equals_sdpa(oracle_mod):
+    case = rand_decode([40, 129, 300], 16, 2, 128, 16, 12, kv_dtype="fp8_e4m3",
+                       scale_range=(0.5, 2.0))
+    assert case.k_scale != 1.0 and case.v_scale != 1.0
+    out, _ = oracle_mod.decode(case)
+    close(out, sdpa_decode(case))
+
+
+def test_extend_no_context_is_causal_sdpa(oracle_mod):
+    case = I.make_extend("c0", [0, 0], [5, 33], 8, 2, 64, 16, 13)
+    got = oracle_mod.extend(case)
+    Hq, G = 8, 4
+    for b in range(2):
+        a, e = case.cu_seqlens_q[b], case.cu_seqlens_q[b + 1]
+        q = torch.from_numpy(I.bits_to_float(case.q[a:e]).astype(np.float64)).transpose(0, 1)
+        k = torch.from_numpy(I.bits_to_float(case.k_new[a:e]).astype(np.float64))
+        v = torch.from_numpy(I.bits_to_float(case.v_new[a:e]).astype(np.float64))
+        k = k.repeat_interleave(G, dim=1).transpose(0, 1)
+        v = v.repeat_interleave(G, dim=1).transpose(0, 1)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            q[None], k[None].contiguous(), v[None].contiguous(), is_causal=True,
+            scale=case.scale)[0].transpose(0, 1).numpy()
+        close(got[a:e], ref)
+
+
+@pytest.mark.parametrize("window,kv_dtype", [(0, "bf16"), (40, "bf16"), (0, "fp8_e4m3")])
+def test_extend_equals_masked_sdpa(oracle_mod, window, kv_dtype):
+    case = I.make_extend("e", [0, 37, 100], [3, 20, 45], 8, 2, 64, 16, 14,
+                         kv_dtype=kv_dtype, window=window,
+                         scale_range=(0.5, 2.0) if kv_dtype != "bf16" else None)
+    close(oracle_mod.extend(case), sdpa_extend(case))
+
+
+# ------------------------------------------------------------- closed forms
+def _tokens(Hkv, D, L, rng, fill=None):
+    x = rng.standard_normal((L, Hkv, D)).astype(np.float32) if fill is None else fill
+    return I.bf16_bits(x)
+
+
+def test_decode_one_key_is_v(oracle_mod):
+    rng = np.random.default_rng(1)
+    q = I.bf16_bits(rng.standard_normal((3, 8, 64)).astype(np.float32))
+    k, v = _tokens(2, 64, 3, rng), _tokens(2, 64, 3, rng)
+    case = I.decode_case_from_tokens("one", q, k, v, [1, 1, 1], 16, 5)
+    out, lse = oracle_mod.decode(case)
+    vv = I.bits_to_float(v).astype(np.float64)
+    for b in range(3):
+        for h in range(8):
+            np.testing.assert_array_equal(out[b, h], vv[b, h // 4])
+
+
+def test_decode_window_one_is_last_v(oracle_mod):
+    case = rand_decode([5, 70, 33], 8, 2, 64, 16, 2, window=1)
+    out, _ = oracle_mod.decode(case)
+    for b, L in enumerate(case.seq_lens):
+        _, v = dense_tokens(case.kv, b, int(L), "bf16")
+        for h in range(8):
+            np.testing.assert_array_equal(out[b, h], v[L - 1, h // 4])
+
+
+def test_decode_zero_scores_mean_and_lse(oracle_mod):
+    """q = 0 makes every score 0: out is the mean of V and lse = ln(n)."""
+    rng = np.random.default_rng(3)
+    lens = [7, 40]
+    q = I.bf16_bits(np.zeros((2, 4, 64), np.float32))
+    k, v = _tokens(1, 64, 47, rng), _tokens(1, 64, 47, rng)
+    case = I.decode_case_from_tokens("zero", q, k, v, lens, 16, 6)
+    out, lse = oracle_mod.decode(case)
+    vv = I.bits_to_float(v).astype(np.float64)
+    close(out[0], np.broadcast_to(vv[:7, 0].mean(0), (4, 64)))
+    close(out[1], np.broadcast_to(vv[7:, 0].mean(0), (4, 64)))
+    close(lse, np.log(np.array([[7.0] * 4, [40.0] * 4])))
+
+
+def test_decode_identical_keys_mean_v(oracle_mod):
+    rng = np.random.default_rng(4)
+    q = I.bf16_bits(rng.standard_normal((1, 4, 128)).astype(np.float32))
+    kk = np.repeat(rng.standard_normal((1, 1, 128)).astype(np.float32), 50, axis=0)
+    k, v = I.bf16_bits(kk), _tokens(1, 128, 50, rng)
+    case = I.decode_case_from_tokens("ident", q, k, v, [50], 16, 7)
+    out, _ = oracle_mod.decode(case)
+    close(out[0], np.broadcast_to(I.bits_to_float(v)[:, 0].astype(np.float64).mean(0), (4, 128)))
+
+
+def test_decode_gqa_head_map(oracle_mod):
+    """V of kv head g is the constant g, so q head h must give h // G."""
+    rng = np.random.default_rng(5)
+    Hq, Hkv, D, L = 16, 4, 64, 45
+    q = I.bf16_bits(rng.standard_normal((2, Hq, D)).astype(np.float32))
+    k = _tokens(Hkv, D, 2 * L, rng)
+    v = I.bf16_bits(np.broadcast_to(np.arange(Hkv, dtype=np.float32)[None, :, None],
+                                    (2 * L, Hkv, D)).copy())
+    case = I.decode_case_from_tokens("gqa", q, k, v, [L, L], 16, 8)
+    out, _ = oracle_mod.decode(case)
+    for h in range(Hq):
+        close(out[:, h], np.full((2, D), h // (Hq // Hkv), dtype=np.float64))
+
+
+def test_decode_two_keys_closed_form(oracle_mod):
+    """Keys e0*a and e0*c with q = e0: weights are a logistic of the score gap."""
+    D, a, c = 64, 2.0, -1.0
+    q = np.zeros((1, 1, D), np.float32); q[0, 0, 0] = 1.0
+    k = np.zeros((2, 1, D), np.float32); k[0, 0, 0] = a; k[1, 0, 0] = c
+    v = np.zeros((2, 1, D), np.float32); v[0, 0, :] = 1.5; v[1, 0, :] = -0.25
+    for cap in (0.0, 0.3):
+        case = I.decode_case_from_tokens("two", I.bf16_bits(q), I.bf16_bits(k),
+                                         I.bf16_bits(v), [2], 16, 9, softcap=cap)
+        out, lse = oracle_mod.decode(case)
+        s0, s1 = a / 8.0, c / 8.0                       # scale = 1/sqrt(64)
+        if cap > 0:
+            s0, s1 = cap * math.tanh(s0 / cap), cap * math.tanh(s1 / cap)
+        w0 = 1.0 / (1.0 + math.exp(s1 - s0))
+        close(out[0, 0], np.full(D, 1.5 * w0 - 0.25 * (1 - w0)))
+        close(lse[0, 0], math.log(math.exp(s0) + math.exp(s1)))
+
+
+def test_decode_softcap_saturation(oracle_mod):
+    """Scores far beyond +-c all saturate to +-c after the scale, so keys of
+    one sign weigh the same: out = (e^c S+ + e^-c S-) / (n+ e^c + n- e^-c)."""
+    D, n_pos, n_neg, cap = 64, 5, 3, 2.0
+    q = np.zeros((1, 1, D), np.float32); q[0, 0, 0] = 16.0
+    kk = np.zeros((8, 1, D), np.float32)
+    kk[:n_pos, 0, 0] = np.linspace(20, 60, n_pos)       # scores 40..120 >> c
+    kk[n_pos:, 0, 0] = -np.linspace(20, 60, n_neg)
+    rng = np.random.default_rng(10)
+    v = _tokens(1, D, 8, rng)
+    case = I.decode_case_from_tokens("sat", I.bf16_bits(q), I.bf16_bits(kk), v,
+                                     [8], 16, 11, softcap=cap)
+    out, _ = oracle_mod.decode(case)
+    vv = I.bits_to_float(v)[:, 0].astype(np.float64)
+    ep, en = math.exp(cap), math.exp(-cap)
+    ref = (ep * vv[:n_pos].sum(0) + en * vv[n_pos:].sum(0)) / (n_pos * ep + n_neg * en)
+    close(out[0, 0], ref, rtol=1e-9, atol=1e-9)
+
+
+def test_decode_huge_softcap_is_off(oracle_mod):
+    case = rand_decode([90, 33], 8, 2, 64, 16, 15)
+    a, _ = oracle_mod.decode(case)
+    case.softcap = 1e30
+    b, _ = oracle_mod.decode(case)
+    close(a, b)
+
+
+def test_decode_window_wider_than_sequence_is_off(oracle_mod):
+    case = rand_decode([90, 33], 8, 2, 64, 16, 16)
+    a, _ = oracle_mod.decode(case)
+    case.window = 91
+    b, _ = oracle_mod.decode(case)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_decode_empty_sequence_is_zero(oracle_mod):
+    case = rand_decode([0, 20, 0], 4, 1, 64, 16, 17)
+    out, lse = oracle_mod.decode(case)
+    assert not out[0].any() and not out[2].any()
+    assert np.all(np.isneginf(lse[[0, 2]]))
+    assert np.all(np.isfinite(out[1]))
+
+
+# -------------------------------------------------------------- invariances
+@pytest.mark.parametrize("splits", [1, 2, 3, 8, 32])
+def test_decode_split_invariance(oracle_mod, splits):
+    case = rand_decode([1, 31, 100, 257], 8, 2, 64, 16, 18, softcap=5.0, window=70)
+    a, la = oracle_mod.decode(case)
+    b, lb = oracle_mod.decode(case, num_splits=splits)
+    close(a, b)
+    close(la, lb)
+
+
+def test_decode_page_permutation_bit_identical(oracle_mod):
+    case = rand_decode([45, 200, 16], 8, 2, 64, 16, 19)
+    a, _ = oracle_mod.decode(case)
+    b, _ = oracle_mod.decode(I.relayout(case, 16, seed=99, pool_pages=40))
+    np.testing.assert_array_equal(a, b)
+
+
+def test_decode_page_size_bit_identical(oracle_mod):
+    case = rand_decode([45, 200, 130], 8, 2, 64, 16, 20, softcap=30.0)
+    ref, _ = oracle_mod.decode(case)
+    for P in (1, 64, 7):
+        got, _ = oracle_mod.decode(I.relayout(case, P, seed=P))
+        np.testing.assert_array_equal(ref, got)
+
+
+# ------------------------------------------------------------- cross-mode
+def _decode_from_extend(case, b, upto):
+    """A decode case over sequence b's context plus its first `upto` new tokens,
+    queried with new row upto-1."""
+    a = int(case.cu_seqlens_q[b])
+    C = int(case.ctx_lens[b])
+    t = np.arange(C)
+    P = case.kv.page_size
+    pages = case.kv.block_table[b, t // P].astype(np.int64)
+    k = np.concatenate([case.kv.k_pool[pages, t % P], case.k_new[a:a + upto]])
+    v = np.concatenate([case.kv.v_pool[pages, t % P], case.v_new[a:a + upto]])
+    q = case.q[a + upto - 1][None]
+    return I.decode_case_from_tokens("x", q, k, v, [C + upto], 16, 21,
+                                     softcap=case.softcap, window=case.window)
+
+
+def test_extend_rows_equal_decode(oracle_mod):
+    case = I.make_extend("x", [30, 64, 0], [1, 17, 9], 8, 2, 64, 16, 22,
+                         softcap=4.0, window=50)
+    ext = oracle_mod.extend(case)
+    for b in range(case.batch):
+        n = int(case.q_lens[b])
+        for upto in sorted({1, n}):
+            dec, _ = oracle_mod.decode(_decode_from_extend(case, b, upto))
+            close(ext[int(case.cu_seqlens_q[b]) + upto - 1], dec[0])
+
+
+def test_extend_row_subset(oracle_mod):
+    case = I.make_extend("s", [20, 70], [9, 30], 8, 2, 64, 16, 23)
+    full = oracle_mod.extend(case)
+    rows = np.array([0, 8, 9, 25, 38])
+    part = oracle_mod.extend(case, rows=rows)
+    np.testing.assert_array_equal(part[rows], full[rows])
+
+
+# -------------------------------------------------------------- brute force
+@pytest.mark.parametrize("n", [1])
+def test_decode_workload_brute_force(oracle_mod, n):
+    case = I.decode_config(n)
+    close(oracle_mod.decode(case)[0], oracle_mod.brute_decode(case))
+
+
+@pytest.mark.parametrize("kw", [
+    dict(lens=[300, 600, 17], Hq=32, Hkv=8, D=128, P=16),                        # llama-shaped
+    dict(lens=[700, 1000], Hq=32, Hkv=8, D=128, P=64, softcap=30.0),            # long-context-shaped
+    dict(lens=[16, 500, 90], Hq=64, Hkv=8, D=128, P=16, kv_dtype="fp8_e4m3",
+         window=256, scale_range=(0.5, 2.0)),                                    # fp8-shaped
+])
+def test_decode_shrunk_brute_force(oracle_mod, kw):
+    kw = dict(kw)
+    case = rand_decode(kw.pop("lens"), kw.pop("Hq"), kw.pop("Hkv"), kw.pop("D"),
+                       kw.pop("P"), 24, **kw)
+    close(oracle_mod.decode(case)[0], oracle_mod.brute_decode(case))
+
+
+def test_extend_shrunk_brute_force(oracle_mod):
+    case = I.make_extend("e", [100, 260], [40, 17], 32, 8, 128, 16, 25, softcap=3.0)
+    close(oracle_mod.extend(case), oracle_mod.brute_extend(case))
+
+
+def test_oracle_thread_count_independent(oracle_mod):
+    case = rand_decode([300, 41], 8, 2, 64, 16, 26)
+    a, _ = oracle_mod.decode(case, threads=1)
+    b, _ = oracle_mod.decode(case, threads=5)
+    np.testing.assert_array_equal(a, b)
