@@ -1,0 +1,220 @@
+/*
+ * paged_attn.h -- C ABI of the MI355X (gfx950) paged GQA attention library.
+ *
+ * The library computes attention of a batch of queries against a paged,
+ * block-table-indexed K/V cache with grouped-query heads, in two modes:
+ *
+ *   decode   one query token per sequence (the token at position L-1, whose
+ *            own key/value is already in the cache): split-KV partial
+ *            attention with log-sum-exp, then a merge of the splits.  This is
+ *            the computation of `decode_attention_fwd` and its kernels
+ *            `_fwd_grouped_kernel_stage1` / `_fwd_kernel_stage2` on the page
+ *            "vllm/attention/ops/triton_decode_attention.py".
+ *   extend   prefix-prefill: new query tokens attend to the sequence's cached
+ *            context through the pages (no mask) and causally to each other
+ *            (contiguous new K/V rows), as `context_attention_fwd` and
+ *            `_fwd_kernel` on the page "vllm/attention/ops/prefix_prefill.py".
+ *
+ * Problem parameters follow the statement of the problem on those pages and on
+ * the vLLM "b12x" backend page (`B12xPagedAttentionImpl.__init__`/`forward`):
+ * Q, the K/V page pools, the block table, per-sequence lengths, scale,
+ * soft-cap, sliding window, page size and the fp8 k/v descales.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - G = num_q_heads / num_kv_heads; query head h reads key/value head h / G.
+ * - K/V pools: element (page, row, kv_head, d) sits at
+ *     pool + page*kv_stride_page + row*kv_stride_tok + kv_head*kv_stride_head + d
+ *   (strides in elements; d is contiguous).  The dense layout
+ *   [num_pages, page_size, num_kv_heads, head_dim] is the `_kv_cache_views`
+ *   view of the b12x page; a [num_pages, num_kv_heads, page_size, head_dim]
+ *   layout is expressed by its strides.
+ * - Token t of sequence b sits in page block_table[b*bt_stride + t/page_size],
+ *   row t % page_size.  Only entries t/page_size < ceil(L_b/page_size) are
+ *   read; padding may hold anything (e.g. -1).
+ * - Sliding window W > 0 keeps key position j for query position p iff
+ *   p - j < W (the b12x page stores `window_left = W - 1`; prefix_prefill keeps
+ *   `pos_q - pos_k < SLIDING_WINDOW`).  W <= 0 means no window.
+ * - Soft-cap c > 0 replaces each scaled score s by c*tanh(s/c) (applied after
+ *   the scale, as `logit_cap` in `_fwd_kernel_stage1`); c <= 0 means off.
+ * - fp8 caches are OCP e4m3fn; a cached key is dec(K)*k_scale and a cached
+ *   value dec(V)*v_scale (per-tensor descales).  For bf16 caches pass 1.0.
+ * - Q, new K/V and the output are bf16 (round-to-nearest-even on output).
+ * - Every device pointer must be 16-byte aligned; every row stride must keep
+ *   16-byte alignment.
+ *
+ * Ownership and errors
+ * --------------------
+ * The caller owns every buffer, including the workspace; the library never
+ * allocates device memory, never synchronises, and keeps no state between
+ * calls.  Compute calls enqueue kernels on `hip_stream` (a hipStream_t, NULL =
+ * the null stream) and return; buffers must stay valid until the stream
+ * reaches that point.  All host-visible arguments are validated before
+ * anything is enqueued: on error nothing is launched and the output is
+ * untouched.  Contents of device buffers (lengths within the stated bounds,
+ * page ids within [0, num_pages), monotone cu_seqlens_q) are the caller's
+ * contract and are not checked.
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PAGED_ATTN_ABI_VERSION 1
+
+typedef enum {
+    PA_OK = 0,
+    PA_ERR_NULL_POINTER = 1,       /* a required pointer is NULL */
+    PA_ERR_INVALID_SHAPE = 2,      /* inconsistent sizes (b12x: ValueError) */
+    PA_ERR_UNSUPPORTED = 3,        /* valid but not built (b12x: NotImplementedError/TypeError) */
+    PA_ERR_WORKSPACE_TOO_SMALL = 4,/* workspace below plan->workspace_bytes (b12x: RuntimeError) */
+    PA_ERR_MISALIGNED = 5,         /* pointer or stride breaks 16-byte alignment */
+    PA_ERR_PLAN_MISMATCH = 6,      /* call arguments disagree with the plan */
+    PA_ERR_HIP = 7                 /* a HIP runtime call or launch failed */
+} pa_status;
+
+typedef enum { PA_KV_BF16 = 0, PA_KV_FP8_E4M3 = 1 } pa_kv_dtype;
+typedef enum { PA_MODE_DECODE = 0, PA_MODE_EXTEND = 1 } pa_mode;
+
+/* Host-side description of one call shape (plain values, no pointers). */
+typedef struct {
+    int32_t mode;              /* pa_mode */
+    int32_t num_seqs;          /* B >= 0 */
+    int32_t num_q_heads;       /* Hq, a multiple of num_kv_heads */
+    int32_t num_kv_heads;      /* Hkv >= 1; G = Hq/Hkv must be 1, 2, 4, 8 or 16 */
+    int32_t head_dim;          /* D: 64 or 128 (same for q/k and v) */
+    int32_t page_size;         /* P >= 1 */
+    int32_t kv_dtype;          /* pa_kv_dtype */
+    int32_t window;            /* sliding window W (<= 0: off) */
+    int32_t max_pages_per_seq; /* block-table row width in entries */
+    int32_t max_kv_len;        /* bound on cached tokens per sequence
+                                  (decode: seq_lens, incl. the query token;
+                                   extend: ctx_lens) */
+    int32_t total_q;           /* extend: rows of q/k_new/v_new/out */
+    int32_t max_q_len;         /* extend: bound on new tokens per sequence */
+    int32_t num_splits;        /* decode: 0 = plan chooses; > 0 caps the KV
+                                  splits per sequence at this number */
+} pa_problem;
+
+/* The plan: a plain value the caller owns (nothing to free).  Planning reads
+ * no device data, so it never depends on live lengths (the b12x page plans
+ * fixed capacities the same way). */
+typedef struct {
+    pa_problem prob;
+    int32_t num_splits;        /* decode: KV splits per sequence (grid x) */
+    int32_t tokens_per_split;  /* decode: tokens per split, a multiple of 32 */
+    int32_t waves_per_block;   /* decode: waves sharing one split */
+    int32_t num_cus;           /* compute units the plan was made for */
+    uint64_t workspace_bytes;  /* device scratch the compute call needs */
+    int32_t reserved[8];
+} pa_plan;
+
+/*
+ * paged_attn_plan -- choose the split-KV decomposition and size the workspace.
+ *
+ * Decode: every sequence's key range [lo, L) (lo = max(0, L-W) with a window)
+ * is cut into splits of `tokens_per_split` tokens; each (sequence, kv head,
+ * split) is one work item, and a merge combines the splits by log-sum-exp
+ * (the split partition and merge of `_fwd_kernel_stage1/2`).  The plan picks
+ * the split size from the batch, heads, max_kv_len and the device's compute
+ * unit count; prob->num_splits > 0 caps the splits per sequence.
+ * Extend: validates the shape; no workspace is needed.
+ *
+ * hip_device >= 0 queries that device's compute-unit count; hip_device < 0
+ * plans for an MI355X (256 compute units) without touching any device.
+ * Host only: no allocation, no launch.
+ */
+pa_status paged_attn_plan(const pa_problem* prob, int hip_device, pa_plan* out);
+
+/*
+ * paged_attn_decode -- one query token per sequence.
+ *
+ *   q             bf16 [B, Hq, D], sequence stride q_stride_b (elements),
+ *                 heads contiguous
+ *   k_pool,v_pool bf16 or e4m3fn pools (layout above), num_pages pages
+ *   block_table   int32 [B, >= ceil(L_b/P)] with row stride bt_stride
+ *   seq_lens      int32 [B]: L_b cached tokens including the query token
+ *                 (0 <= L_b <= prob.max_kv_len); L_b = 0 gives a zero row
+ *   page_size, window   must equal the plan's
+ *   scale         multiplies q.k (e.g. 1/sqrt(D))
+ *   softcap       c > 0 enables c*tanh(s/c)
+ *   k_scale,v_scale  fp8 descales (1.0 for bf16)
+ *   out           bf16 [B, Hq, D], sequence stride out_stride_b
+ *   workspace     >= plan->workspace_bytes of device memory (split partials)
+ */
+pa_status paged_attn_decode(const pa_plan* plan,
+                            const void* q, int64_t q_stride_b,
+                            const void* k_pool, const void* v_pool,
+                            int64_t kv_stride_page, int64_t kv_stride_tok,
+                            int64_t kv_stride_head, int64_t num_pages,
+                            const int32_t* block_table, int64_t bt_stride,
+                            const int32_t* seq_lens,
+                            int32_t page_size, float scale, float softcap,
+                            int32_t window, float k_scale, float v_scale,
+                            void* out, int64_t out_stride_b,
+                            void* workspace, uint64_t workspace_bytes,
+                            void* hip_stream);
+
+/*
+ * paged_attn_extend -- prefix-prefill of new tokens on top of a paged context.
+ *
+ *   q             bf16 [total_q, Hq, D] (rows of all sequences, concatenated)
+ *   k_new,v_new   bf16 [total_q, Hkv, D]: keys/values of the new tokens
+ *   cu_seqlens_q  int32 [B+1]: sequence b owns rows [cu[b], cu[b+1]),
+ *                 cu[0] = 0, cu[B] = total_q, cu[b+1]-cu[b] <= max_q_len
+ *   ctx_lens      int32 [B]: C_b cached tokens (<= prob.max_kv_len); new row
+ *                 i of sequence b sits at position C_b + i
+ *   k_pool...bt_stride  the cached context, as for decode
+ *   out           bf16 [total_q, Hq, D]
+ *   workspace     may be NULL when plan->workspace_bytes == 0
+ */
+pa_status paged_attn_extend(const pa_plan* plan,
+                            const void* q, const void* k_new, const void* v_new,
+                            const int32_t* cu_seqlens_q, const int32_t* ctx_lens,
+                            const void* k_pool, const void* v_pool,
+                            int64_t kv_stride_page, int64_t kv_stride_tok,
+                            int64_t kv_stride_head, int64_t num_pages,
+                            const int32_t* block_table, int64_t bt_stride,
+                            int32_t page_size, float scale, float softcap,
+                            int32_t window, float k_scale, float v_scale,
+                            void* out, void* workspace, uint64_t workspace_bytes,
+                            void* hip_stream);
+
+/*
+ * paged_attn_gather -- test aid: copy every cached key/value row
+ * (t in [0, L_b)) of every sequence, through the same address path the
+ * attention kernels use, into k_out/v_out [sum_b L_b, Hkv, D] (sequence-major,
+ * same element type as the pools).  A byte-exact check of the block-table
+ * gather.  Uses the plan's problem (decode mode) for shapes.
+ */
+pa_status paged_attn_gather(const pa_plan* plan,
+                            const void* k_pool, const void* v_pool,
+                            int64_t kv_stride_page, int64_t kv_stride_tok,
+                            int64_t kv_stride_head, int64_t num_pages,
+                            const int32_t* block_table, int64_t bt_stride,
+                            const int32_t* seq_lens,
+                            void* k_out, void* v_out, void* hip_stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* paged_attn_status_str(pa_status status);
+
+/* Writes a one-line summary of the plan into buf (always NUL-terminated);
+ * returns the length it wanted. */
+int paged_attn_plan_describe(const pa_plan* plan, char* buf, int buf_len);
+
+/* PAGED_ATTN_ABI_VERSION of the built library. */
+int paged_attn_abi_version(void);
+
+/* Path of the HIP runtime library this library resolved its symbols from
+ * (lets a host process check it shares one runtime with its allocator). */
+const char* paged_attn_hip_runtime_path(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTN_H */

@@ -1,0 +1,12 @@
+"""Paged GQA attention (split-KV decode and prefix-prefill extend) for MI355X.
+
+The computation runs in hand-written HIP kernels for gfx950 behind the C ABI
+of ``include/paged_attn.h`` (``libpaged_attn.so``); this package is its thin
+Python binding plus the seeded synthetic inputs used by tests and the bench.
+"""
+from .binding import (PA_MODE_DECODE, PA_MODE_EXTEND, PagedAttnError, Plan,  # noqa: F401
+                      decode, decode_plan, extend, extend_plan, gather, lib, plan,
+                      status_str)
+
+__all__ = ["PA_MODE_DECODE", "PA_MODE_EXTEND", "PagedAttnError", "Plan", "decode",
+           "decode_plan", "extend", "extend_plan", "gather", "lib", "plan", "status_str"]

@@ -1,0 +1,251 @@
+"""Python binding of ``libpaged_attn.so`` (the C ABI in include/paged_attn.h).
+
+Argument marshalling only: tensors become device pointers, element strides and
+the current HIP stream; every step of the computation runs in the library's
+kernels.  torch provides device memory and streams.  The library must be
+built (``python -m paged_gqa_attention_02_amd.build``); nothing here falls back
+to another implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpaged_attn.so")
+
+PA_MODE_DECODE, PA_MODE_EXTEND = 0, 1
+PA_KV = {"bf16": 0, "fp8_e4m3": 1}
+
+
+class PaProblem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "mode", "num_seqs", "num_q_heads", "num_kv_heads", "head_dim", "page_size",
+        "kv_dtype", "window", "max_pages_per_seq", "max_kv_len", "total_q",
+        "max_q_len", "num_splits")]
+
+
+class PaPlan(ctypes.Structure):
+    _fields_ = [("prob", PaProblem), ("num_splits", ctypes.c_int32),
+                ("tokens_per_split", ctypes.c_int32), ("waves_per_block", ctypes.c_int32),
+                ("num_cus", ctypes.c_int32), ("workspace_bytes", ctypes.c_uint64),
+                ("reserved", ctypes.c_int32 * 8)]
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {status_str(status)} (status {status})")
+
+
+_LIB = None
+
+
+def lib():
+    """Load the library once, after torch, so both share one HIP runtime."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run "
+                           "`python -m paged_gqa_attention_02_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    p, i32, i64, u64, f32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                             ctypes.c_uint64, ctypes.c_float)
+    PP = ctypes.POINTER(PaPlan)
+    L.paged_attn_plan.argtypes = [ctypes.POINTER(PaProblem), ctypes.c_int, PP]
+    L.paged_attn_plan.restype = ctypes.c_int
+    L.paged_attn_decode.argtypes = [PP, p, i64, p, p, i64, i64, i64, i64, p, i64, p,
+                                    i32, f32, f32, i32, f32, f32, p, i64, p, u64, p]
+    L.paged_attn_decode.restype = ctypes.c_int
+    L.paged_attn_extend.argtypes = [PP, p, p, p, p, p, p, p, i64, i64, i64, i64, p, i64,
+                                    i32, f32, f32, i32, f32, f32, p, p, u64, p]
+    L.paged_attn_extend.restype = ctypes.c_int
+    L.paged_attn_gather.argtypes = [PP, p, p, i64, i64, i64, i64, p, i64, p, p, p, p]
+    L.paged_attn_gather.restype = ctypes.c_int
+    L.paged_attn_status_str.argtypes = [ctypes.c_int]
+    L.paged_attn_status_str.restype = ctypes.c_char_p
+    L.paged_attn_plan_describe.argtypes = [PP, ctypes.c_char_p, ctypes.c_int]
+    L.paged_attn_plan_describe.restype = ctypes.c_int
+    L.paged_attn_abi_version.argtypes = []
+    L.paged_attn_abi_version.restype = ctypes.c_int
+    L.paged_attn_hip_runtime_path.argtypes = []
+    L.paged_attn_hip_runtime_path.restype = ctypes.c_char_p
+    rt = L.paged_attn_hip_runtime_path().decode()
+    torch_rt = os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")
+    if os.path.exists(torch_rt) and os.path.realpath(rt) != os.path.realpath(torch_rt):
+        raise RuntimeError(f"libpaged_attn.so resolved the HIP runtime {rt}, but torch "
+                           f"uses {torch_rt}; import torch before this library")
+    _LIB = L
+    return L
+
+
+def status_str(status: int) -> str:
+    return lib().paged_attn_status_str(status).decode()
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise PagedAttnError(fn, status)
+
+
+@dataclass
+class Plan:
+    c: PaPlan
+
+    @property
+    def num_splits(self) -> int:
+        return self.c.num_splits
+
+    @property
+    def tokens_per_split(self) -> int:
+        return self.c.tokens_per_split
+
+    @property
+    def workspace_bytes(self) -> int:
+        return self.c.workspace_bytes
+
+    @property
+    def problem(self) -> PaProblem:
+        return self.c.prob
+
+    def describe(self) -> str:
+        buf = ctypes.create_string_buffer(512)
+        lib().paged_attn_plan_describe(ctypes.byref(self.c), buf, 512)
+        return buf.value.decode()
+
+
+def plan(mode: int, num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+         page_size: int, kv_dtype: str = "bf16", window: int = 0,
+         max_pages_per_seq: int = 0, max_kv_len: int = 0, total_q: int = 0,
+         max_q_len: int = 0, num_splits: int = 0, device: Optional[int] = None) -> Plan:
+    """paged_attn_plan.  device=None plans for the current torch device when one
+    exists, else for an MI355X without touching a device."""
+    prob = PaProblem(mode, num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
+                     PA_KV[kv_dtype], window, max_pages_per_seq, max_kv_len, total_q,
+                     max_q_len, num_splits)
+    if device is None:
+        device = torch.cuda.current_device() if torch.cuda.is_available() else -1
+    out = PaPlan()
+    _check("paged_attn_plan", lib().paged_attn_plan(ctypes.byref(prob), device, ctypes.byref(out)))
+    return Plan(out)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _kv_dtype_name(t: torch.Tensor) -> str:
+    if t.dtype == torch.bfloat16:
+        return "bf16"
+    if t.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return "fp8_e4m3"
+    raise TypeError(f"unsupported K/V cache dtype {t.dtype}")
+
+
+def _pool_strides(k_pool: torch.Tensor, v_pool: torch.Tensor):
+    if k_pool.dim() != 4 or k_pool.shape != v_pool.shape or k_pool.stride() != v_pool.stride():
+        raise ValueError("k_pool/v_pool must be 4-D [pages, page_size, kv_heads, head_dim] "
+                         "views with equal shapes and strides")
+    if k_pool.stride(3) != 1:
+        raise ValueError("head_dim must be contiguous")
+    return k_pool.stride(0), k_pool.stride(1), k_pool.stride(2)
+
+
+def _workspace(pl: Plan, workspace, device):
+    if pl.workspace_bytes == 0:
+        return workspace
+    if workspace is None:
+        workspace = torch.empty(pl.workspace_bytes, dtype=torch.uint8, device=device)
+    return workspace
+
+
+def decode_plan(q: torch.Tensor, k_pool: torch.Tensor, block_table: torch.Tensor,
+                max_kv_len: int, window: int = 0, num_splits: int = 0) -> Plan:
+    """Plan a decode call for tensors shaped like these."""
+    B, Hq, D = q.shape
+    return plan(PA_MODE_DECODE, B, Hq, k_pool.shape[2], D, k_pool.shape[1],
+                _kv_dtype_name(k_pool), window, block_table.shape[1], max_kv_len,
+                num_splits=num_splits, device=q.device.index)
+
+
+def decode(pl: Plan, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+           block_table: torch.Tensor, seq_lens: torch.Tensor, scale: float,
+           softcap: float = 0.0, window: int = 0, k_scale: float = 1.0,
+           v_scale: float = 1.0, out: Optional[torch.Tensor] = None,
+           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """paged_attn_decode: q bf16 [B, Hq, D] -> out bf16 [B, Hq, D]."""
+    if q.dtype != torch.bfloat16 or q.dim() != 3 or q.stride(2) != 1 or q.stride(1) != q.shape[2]:
+        raise ValueError("q must be bf16 [B, Hq, D] with contiguous heads")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_table and seq_lens must be int32")
+    if block_table.stride(1) != 1:
+        raise ValueError("block_table rows must be contiguous")
+    if out is None:
+        out = torch.empty_like(q)
+    sp, st, sh = _pool_strides(k_pool, v_pool)
+    workspace = _workspace(pl, workspace, q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("paged_attn_decode", lib().paged_attn_decode(
+        ctypes.byref(pl.c), _ptr(q), q.stride(0), _ptr(k_pool), _ptr(v_pool), sp, st, sh,
+        k_pool.shape[0], _ptr(block_table), block_table.stride(0), _ptr(seq_lens),
+        k_pool.shape[1], float(scale), float(softcap), int(window), float(k_scale),
+        float(v_scale), _ptr(out), out.stride(0), _ptr(workspace), wbytes, _stream(stream)))
+    return out
+
+
+def extend_plan(q: torch.Tensor, k_pool: torch.Tensor, block_table: torch.Tensor,
+                num_seqs: int, max_kv_len: int, max_q_len: int, window: int = 0) -> Plan:
+    T, Hq, D = q.shape
+    return plan(PA_MODE_EXTEND, num_seqs, Hq, k_pool.shape[2], D, k_pool.shape[1],
+                _kv_dtype_name(k_pool), window, block_table.shape[1], max_kv_len,
+                total_q=T, max_q_len=max_q_len, device=q.device.index)
+
+
+def extend(pl: Plan, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+           cu_seqlens_q: torch.Tensor, ctx_lens: torch.Tensor, k_pool: torch.Tensor,
+           v_pool: torch.Tensor, block_table: torch.Tensor, scale: float,
+           softcap: float = 0.0, window: int = 0, k_scale: float = 1.0,
+           v_scale: float = 1.0, out: Optional[torch.Tensor] = None,
+           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """paged_attn_extend: q bf16 [total_q, Hq, D] -> out bf16 [total_q, Hq, D]."""
+    for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new)):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous bf16")
+    if cu_seqlens_q.dtype != torch.int32 or ctx_lens.dtype != torch.int32 \
+            or block_table.dtype != torch.int32:
+        raise TypeError("cu_seqlens_q, ctx_lens and block_table must be int32")
+    if out is None:
+        out = torch.empty_like(q)
+    sp, st, sh = _pool_strides(k_pool, v_pool)
+    workspace = _workspace(pl, workspace, q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("paged_attn_extend", lib().paged_attn_extend(
+        ctypes.byref(pl.c), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(cu_seqlens_q),
+        _ptr(ctx_lens), _ptr(k_pool), _ptr(v_pool), sp, st, sh, k_pool.shape[0],
+        _ptr(block_table), block_table.stride(0), k_pool.shape[1], float(scale),
+        float(softcap), int(window), float(k_scale), float(v_scale), _ptr(out),
+        _ptr(workspace), wbytes, _stream(stream)))
+    return out
+
+
+def gather(pl: Plan, k_pool: torch.Tensor, v_pool: torch.Tensor, block_table: torch.Tensor,
+           seq_lens: torch.Tensor, total_tokens: int, stream=None):
+    """paged_attn_gather: every cached row, dense [sum L, Hkv, D] (test aid)."""
+    sp, st, sh = _pool_strides(k_pool, v_pool)
+    shape = (total_tokens, k_pool.shape[2], k_pool.shape[3])
+    k_out = torch.empty(shape, dtype=k_pool.dtype, device=k_pool.device)
+    v_out = torch.empty(shape, dtype=k_pool.dtype, device=k_pool.device)
+    _check("paged_attn_gather", lib().paged_attn_gather(
+        ctypes.byref(pl.c), _ptr(k_pool), _ptr(v_pool), sp, st, sh, k_pool.shape[0],
+        _ptr(block_table), block_table.stride(0), _ptr(seq_lens), _ptr(k_out), _ptr(v_out),
+        _stream(stream)))
+    return k_out, v_out

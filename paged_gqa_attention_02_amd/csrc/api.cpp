@@ -1,0 +1,331 @@
+// api.cpp -- the C ABI: planning, argument validation, kernel launches.
+//
+// Validation mirrors the error conventions of the vLLM "b12x" backend page
+// (`B12xPagedAttentionImpl.__init__` / `forward`): shape inconsistencies
+// (its ValueError) -> PA_ERR_INVALID_SHAPE, unsupported features or dtypes
+// (NotImplementedError / TypeError) -> PA_ERR_UNSUPPORTED, scratch too small
+// (RuntimeError) -> PA_ERR_WORKSPACE_TOO_SMALL.  Everything is checked before
+// anything is enqueued.
+#include <dlfcn.h>
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "paged_attn.h"
+#include "pa_internal.h"
+
+namespace {
+
+using namespace pa;
+
+constexpr int kDefaultCus = 256;  // MI355X
+constexpr int kMinSplitTokens = 256;
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+int ilog2(int x) {
+    int s = 0;
+    while ((1 << s) < x) ++s;
+    return s;
+}
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t m) { return cdiv(a, m) * m; }
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+pa_status check_problem(const pa_problem& pr) {
+    if (pr.mode != PA_MODE_DECODE && pr.mode != PA_MODE_EXTEND) return PA_ERR_UNSUPPORTED;
+    if (pr.num_seqs < 0 || pr.num_q_heads <= 0 || pr.num_kv_heads <= 0 || pr.page_size <= 0 ||
+        pr.max_kv_len < 0 || pr.max_pages_per_seq < 0 || pr.num_splits < 0)
+        return PA_ERR_INVALID_SHAPE;
+    if (pr.num_q_heads % pr.num_kv_heads != 0) return PA_ERR_INVALID_SHAPE;
+    const int G = pr.num_q_heads / pr.num_kv_heads;
+    if (G > 16 || !is_pow2(G)) return PA_ERR_UNSUPPORTED;
+    if (pr.head_dim != 64 && pr.head_dim != 128) return PA_ERR_UNSUPPORTED;
+    if (pr.kv_dtype != PA_KV_BF16 && pr.kv_dtype != PA_KV_FP8_E4M3) return PA_ERR_UNSUPPORTED;
+    if (!is_pow2(pr.page_size) || pr.page_size > 4096) return PA_ERR_UNSUPPORTED;
+    if ((int64_t)pr.max_pages_per_seq < cdiv(pr.max_kv_len, pr.page_size))
+        return PA_ERR_INVALID_SHAPE;
+    if (pr.mode == PA_MODE_EXTEND) {
+        if (pr.total_q < 0 || pr.max_q_len < 0) return PA_ERR_INVALID_SHAPE;
+        if (pr.num_seqs > 0 && pr.total_q > 0 && pr.max_q_len == 0) return PA_ERR_INVALID_SHAPE;
+    }
+    return PA_OK;
+}
+
+// Tokens of a sequence's key range that one split may have to cover, rounded
+// out to whole 32-token tiles: the range starts at lo rounded down to 32.
+int64_t key_span(const pa_problem& pr) {
+    int64_t span = pr.max_kv_len;
+    if (pr.window > 0) span = std::min<int64_t>(span, (int64_t)pr.window + kTile - 1);
+    return span;
+}
+
+int elem_bytes(int kv_dtype) { return kv_dtype == PA_KV_FP8_E4M3 ? 1 : 2; }
+
+pa_status check_pools(const pa_plan& pl, const void* k_pool, const void* v_pool,
+                      int64_t s_page, int64_t s_tok, int64_t s_head, int64_t num_pages,
+                      const int32_t* block_table, int64_t bt_stride) {
+    const pa_problem& pr = pl.prob;
+    if (!k_pool || !v_pool || !block_table) return PA_ERR_NULL_POINTER;
+    if (s_page < 0 || s_tok < 0 || s_head < 0 || num_pages < 1) return PA_ERR_INVALID_SHAPE;
+    if (bt_stride < pr.max_pages_per_seq) return PA_ERR_INVALID_SHAPE;
+    const int64_t eb = elem_bytes(pr.kv_dtype);
+    if (!aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_MISALIGNED;
+    if ((s_page * eb) % 16 || (s_tok * eb) % 16 || (s_head * eb) % 16) return PA_ERR_MISALIGNED;
+    return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* paged_attn_status_str(pa_status s) {
+    switch (s) {
+        case PA_OK: return "ok";
+        case PA_ERR_NULL_POINTER: return "null pointer";
+        case PA_ERR_INVALID_SHAPE: return "invalid shape";
+        case PA_ERR_UNSUPPORTED: return "unsupported";
+        case PA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case PA_ERR_MISALIGNED: return "misaligned pointer or stride";
+        case PA_ERR_PLAN_MISMATCH: return "arguments do not match the plan";
+        case PA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+int paged_attn_abi_version(void) { return PAGED_ATTN_ABI_VERSION; }
+
+const char* paged_attn_hip_runtime_path(void) {
+    static char path[4096];
+    Dl_info info;
+    void* sym = reinterpret_cast<void*>(&hipGetDeviceCount);
+    if (dladdr(sym, &info) && info.dli_fname) {
+        snprintf(path, sizeof path, "%s", info.dli_fname);
+        return path;
+    }
+    return "";
+}
+
+pa_status paged_attn_plan(const pa_problem* prob, int hip_device, pa_plan* out) {
+    if (!prob || !out) return PA_ERR_NULL_POINTER;
+    const pa_problem pr = *prob;
+    pa_status st = check_problem(pr);
+    if (st != PA_OK) return st;
+
+    int cus = kDefaultCus;
+    if (hip_device >= 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, hip_device) != hipSuccess) return PA_ERR_HIP;
+        cus = prop.multiProcessorCount;
+    }
+
+    pa_plan pl;
+    memset(&pl, 0, sizeof pl);
+    pl.prob = pr;
+    pl.num_cus = cus;
+    pl.waves_per_block = kDecodeWaves;
+    pl.num_splits = 1;
+    pl.tokens_per_split = kTile;
+
+    if (pr.mode == PA_MODE_DECODE) {
+        const int64_t span = key_span(pr);
+        const int64_t units = (int64_t)pr.num_seqs * pr.num_kv_heads;
+        int64_t T;
+        if (pr.num_splits > 0) {
+            T = round_up(std::max<int64_t>(cdiv(span, pr.num_splits), 1), kTile);
+        } else {
+            // Aim for ~16 work items per compute unit, assuming sequences
+            // average half the bound; never split finer than kMinSplitTokens.
+            const int64_t target = 16LL * cus;
+            T = round_up(std::max<int64_t>(cdiv(units * span, 2 * target), 1), kTile);
+            T = std::max<int64_t>(T, kMinSplitTokens);
+        }
+        if (span > 0 && cdiv(span, T) > kMaxSplits) T = round_up(cdiv(span, kMaxSplits), kTile);
+        if (T > (int64_t)1 << 30) return PA_ERR_INVALID_SHAPE;
+        const int64_t S = span > 0 ? cdiv(span, T) : 1;
+        pl.tokens_per_split = (int32_t)T;
+        pl.num_splits = (int32_t)S;
+        if (S > 1) {
+            const int64_t rows = (int64_t)pr.num_seqs * pr.num_q_heads * S;
+            pl.workspace_bytes = (uint64_t)(round_up(rows * pr.head_dim * 4, 256) +
+                                            round_up(rows * 4, 256));
+        }
+    }
+    *out = pl;
+    return PA_OK;
+}
+
+int paged_attn_plan_describe(const pa_plan* pl, char* buf, int buf_len) {
+    char tmp[512];
+    int n;
+    if (!pl) {
+        n = snprintf(tmp, sizeof tmp, "(null plan)");
+    } else {
+        const pa_problem& p = pl->prob;
+        n = snprintf(tmp, sizeof tmp,
+                     "%s B=%d Hq=%d Hkv=%d D=%d P=%d kv=%s window=%d max_kv_len=%d "
+                     "splits=%d tokens_per_split=%d waves=%d cus=%d workspace=%llu",
+                     p.mode == PA_MODE_DECODE ? "decode" : "extend", p.num_seqs,
+                     p.num_q_heads, p.num_kv_heads, p.head_dim, p.page_size,
+                     p.kv_dtype == PA_KV_FP8_E4M3 ? "fp8_e4m3" : "bf16", p.window,
+                     p.max_kv_len, pl->num_splits, pl->tokens_per_split,
+                     pl->waves_per_block, pl->num_cus,
+                     (unsigned long long)pl->workspace_bytes);
+    }
+    if (buf && buf_len > 0) snprintf(buf, (size_t)buf_len, "%s", tmp);
+    return n;
+}
+
+pa_status paged_attn_decode(const pa_plan* plan, const void* q, int64_t q_stride_b,
+                            const void* k_pool, const void* v_pool, int64_t kv_stride_page,
+                            int64_t kv_stride_tok, int64_t kv_stride_head, int64_t num_pages,
+                            const int32_t* block_table, int64_t bt_stride,
+                            const int32_t* seq_lens, int32_t page_size, float scale,
+                            float softcap, int32_t window, float k_scale, float v_scale,
+                            void* out, int64_t out_stride_b, void* workspace,
+                            uint64_t workspace_bytes, void* hip_stream) {
+    if (!plan) return PA_ERR_NULL_POINTER;
+    const pa_plan& pl = *plan;
+    const pa_problem& pr = pl.prob;
+    pa_status st = check_problem(pr);
+    if (st != PA_OK) return st;
+    if (pr.mode != PA_MODE_DECODE) return PA_ERR_PLAN_MISMATCH;
+    if (page_size != pr.page_size || window != pr.window) return PA_ERR_PLAN_MISMATCH;
+    if (pl.tokens_per_split <= 0 || pl.tokens_per_split % kTile || pl.num_splits < 1 ||
+        pl.num_splits > kMaxSplits ||
+        (int64_t)pl.num_splits * pl.tokens_per_split < key_span(pr))
+        return PA_ERR_PLAN_MISMATCH;
+    if (pr.num_seqs == 0) return PA_OK;
+    if (!q || !seq_lens || !out) return PA_ERR_NULL_POINTER;
+    st = check_pools(pl, k_pool, v_pool, kv_stride_page, kv_stride_tok, kv_stride_head,
+                     num_pages, block_table, bt_stride);
+    if (st != PA_OK) return st;
+    const int64_t row = (int64_t)pr.num_q_heads * pr.head_dim;
+    if (q_stride_b < row || out_stride_b < row) return PA_ERR_INVALID_SHAPE;
+    if (!aligned16(q) || !aligned16(out) || (q_stride_b * 2) % 16 || (out_stride_b * 2) % 16)
+        return PA_ERR_MISALIGNED;
+    if (!isfinite(scale) || !isfinite(softcap) || !isfinite(k_scale) || !isfinite(v_scale))
+        return PA_ERR_INVALID_SHAPE;
+    uint64_t need = pl.num_splits > 1 ? pl.workspace_bytes : 0;
+    if (need > 0) {
+        if (workspace_bytes < need) return PA_ERR_WORKSPACE_TOO_SMALL;
+        if (!workspace) return PA_ERR_NULL_POINTER;
+        if (!aligned16(workspace)) return PA_ERR_MISALIGNED;
+    }
+
+    DecodeParams p;
+    memset(&p, 0, sizeof p);
+    p.q = q;
+    p.q_stride_b = q_stride_b;
+    p.k_pool = k_pool;
+    p.v_pool = v_pool;
+    p.s_page = kv_stride_page;
+    p.s_tok = kv_stride_tok;
+    p.s_head = kv_stride_head;
+    p.block_table = block_table;
+    p.bt_stride = bt_stride;
+    p.seq_lens = seq_lens;
+    p.num_q_heads = pr.num_q_heads;
+    p.group = pr.num_q_heads / pr.num_kv_heads;
+    p.page_shift = ilog2(pr.page_size);
+    p.window = pr.window;
+    p.tokens_per_split = pl.tokens_per_split;
+    p.num_splits = pl.num_splits;
+    const float kl2e = 1.4426950408889634f;
+    p.has_cap = softcap > 0.f;
+    p.qk_scale2 = scale * k_scale * kl2e;
+    if (p.has_cap) {
+        p.cap_c1 = 2.f * scale * k_scale * kl2e / softcap;
+        p.cap_c2 = softcap * kl2e;
+    }
+    p.v_scale = v_scale;
+    p.out = out;
+    p.out_stride_b = out_stride_b;
+    if (pl.num_splits > 1) {
+        const int64_t rows = (int64_t)pr.num_seqs * pr.num_q_heads * pl.num_splits;
+        p.part_o = static_cast<float*>(workspace);
+        p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                              round_up(rows * pr.head_dim * 4, 256));
+    }
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    const bool uniform = pr.page_size >= 16;
+    if (launch_decode(p, pr.head_dim, pr.kv_dtype == PA_KV_FP8_E4M3, uniform, pr.num_seqs,
+                      pr.num_kv_heads, stream) != hipSuccess)
+        return PA_ERR_HIP;
+    if (pl.num_splits > 1 &&
+        launch_decode_merge(p, pr.head_dim, pr.num_seqs, pr.num_kv_heads, stream) != hipSuccess)
+        return PA_ERR_HIP;
+    return PA_OK;
+}
+
+pa_status paged_attn_gather(const pa_plan* plan, const void* k_pool, const void* v_pool,
+                            int64_t kv_stride_page, int64_t kv_stride_tok,
+                            int64_t kv_stride_head, int64_t num_pages,
+                            const int32_t* block_table, int64_t bt_stride,
+                            const int32_t* seq_lens, void* k_out, void* v_out,
+                            void* hip_stream) {
+    if (!plan) return PA_ERR_NULL_POINTER;
+    const pa_plan& pl = *plan;
+    const pa_problem& pr = pl.prob;
+    pa_status st = check_problem(pr);
+    if (st != PA_OK) return st;
+    if (pr.num_seqs == 0) return PA_OK;
+    if (!seq_lens || !k_out || !v_out) return PA_ERR_NULL_POINTER;
+    st = check_pools(pl, k_pool, v_pool, kv_stride_page, kv_stride_tok, kv_stride_head,
+                     num_pages, block_table, bt_stride);
+    if (st != PA_OK) return st;
+    if (!aligned16(k_out) || !aligned16(v_out)) return PA_ERR_MISALIGNED;
+    GatherParams p;
+    memset(&p, 0, sizeof p);
+    p.k_pool = k_pool;
+    p.v_pool = v_pool;
+    p.s_page = kv_stride_page;
+    p.s_tok = kv_stride_tok;
+    p.s_head = kv_stride_head;
+    p.block_table = block_table;
+    p.bt_stride = bt_stride;
+    p.seq_lens = seq_lens;
+    p.num_seqs = pr.num_seqs;
+    p.num_kv_heads = pr.num_kv_heads;
+    p.page_shift = ilog2(pr.page_size);
+    p.k_out = k_out;
+    p.v_out = v_out;
+    if (launch_gather(p, pr.head_dim, pr.kv_dtype == PA_KV_FP8_E4M3,
+                      static_cast<hipStream_t>(hip_stream)) != hipSuccess)
+        return PA_ERR_HIP;
+    return PA_OK;
+}
+
+pa_status paged_attn_extend(const pa_plan* plan, const void* q, const void* k_new,
+                            const void* v_new, const int32_t* cu_seqlens_q,
+                            const int32_t* ctx_lens, const void* k_pool, const void* v_pool,
+                            int64_t kv_stride_page, int64_t kv_stride_tok,
+                            int64_t kv_stride_head, int64_t num_pages,
+                            const int32_t* block_table, int64_t bt_stride, int32_t page_size,
+                            float scale, float softcap, int32_t window, float k_scale,
+                            float v_scale, void* out, void* workspace, uint64_t workspace_bytes,
+                            void* hip_stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    if (!plan) return PA_ERR_NULL_POINTER;
+    const pa_plan& pl = *plan;
+    const pa_problem& pr = pl.prob;
+    pa_status st = check_problem(pr);
+    if (st != PA_OK) return st;
+    if (pr.mode != PA_MODE_EXTEND) return PA_ERR_PLAN_MISMATCH;
+    if (page_size != pr.page_size || window != pr.window) return PA_ERR_PLAN_MISMATCH;
+    if (pr.num_seqs == 0 || pr.total_q == 0) return PA_OK;
+    if (!q || !k_new || !v_new || !cu_seqlens_q || !ctx_lens || !out) return PA_ERR_NULL_POINTER;
+    st = check_pools(pl, k_pool, v_pool, kv_stride_page, kv_stride_tok, kv_stride_head,
+                     num_pages, block_table, bt_stride);
+    if (st != PA_OK) return st;
+    if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out))
+        return PA_ERR_MISALIGNED;
+    if (!isfinite(scale) || !isfinite(softcap) || !isfinite(k_scale) || !isfinite(v_scale))
+        return PA_ERR_INVALID_SHAPE;
+    return PA_ERR_UNSUPPORTED;  // extend kernel not built yet
+}
+
+}  // extern "C"

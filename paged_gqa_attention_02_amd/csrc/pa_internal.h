@@ -1,0 +1,86 @@
+// pa_internal.h -- argument blocks shared by the host API and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Decode works on tiles of 32 consecutive token positions; every split starts
+// on a multiple of 32.
+constexpr int kTile = 32;
+// Split partials of one sequence are merged through LDS: at most this many.
+constexpr int kMaxSplits = 256;
+// Waves that share one (sequence, kv head, split) work item.
+constexpr int kDecodeWaves = 4;
+
+struct DecodeParams {
+    const void* q;            // bf16 [B, Hq, D], row stride q_stride_b
+    int64_t q_stride_b;       // elements
+    const void* k_pool;       // bf16 | e4m3fn
+    const void* v_pool;
+    int64_t s_page, s_tok, s_head;   // pool strides in elements
+    const int32_t* block_table;
+    int64_t bt_stride;
+    const int32_t* seq_lens;
+    int32_t num_q_heads;
+    int32_t group;            // G = Hq / Hkv (1..16)
+    int32_t page_shift;       // log2(page_size)
+    int32_t window;           // <= 0: off
+    int32_t tokens_per_split; // multiple of kTile
+    int32_t num_splits;       // grid x; split partial stride
+    int32_t has_cap;
+    float qk_scale2;          // scale * k_scale * log2(e)           (no cap)
+    float cap_c1;             // 2 * scale * k_scale * log2(e) / c   (cap)
+    float cap_c2;             // c * log2(e)                         (cap)
+    float v_scale;
+    void* out;                // bf16 [B, Hq, D], row stride out_stride_b
+    int64_t out_stride_b;
+    float* part_o;            // [B, Hq, num_splits, D]
+    float* part_lse;          // [B, Hq, num_splits] (log2 domain)
+};
+
+struct GatherParams {
+    const void* k_pool;
+    const void* v_pool;
+    int64_t s_page, s_tok, s_head;
+    const int32_t* block_table;
+    int64_t bt_stride;
+    const int32_t* seq_lens;
+    int32_t num_seqs, num_kv_heads, page_shift;
+    void* k_out;
+    void* v_out;
+};
+
+struct ExtendParams {
+    const void* q;            // bf16 [total_q, Hq, D]
+    const void* k_new;        // bf16 [total_q, Hkv, D]
+    const void* v_new;
+    const int32_t* cu_seqlens_q;
+    const int32_t* ctx_lens;
+    const void* k_pool;
+    const void* v_pool;
+    int64_t s_page, s_tok, s_head;
+    const int32_t* block_table;
+    int64_t bt_stride;
+    int32_t num_q_heads, num_kv_heads, group;
+    int32_t page_shift;
+    int32_t window;
+    int32_t q_tiles;          // grid x bound: ceil(max_q_len / rows_per_tile)
+    int32_t has_cap;
+    float qk_scale2;          // scale * log2(e), for new (bf16) keys
+    float qk_scale2_ctx;      // scale * k_scale * log2(e), for cached keys
+    float cap_c1, cap_c1_ctx, cap_c2;
+    float v_scale;            // applied to the cached-value part of the sum
+    void* out;                // bf16 [total_q, Hq, D]
+};
+
+hipError_t launch_decode(const DecodeParams& p, int head_dim, bool fp8, bool uniform_pages,
+                         int num_seqs, int num_kv_heads, hipStream_t stream);
+hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, int num_seqs,
+                               int num_kv_heads, hipStream_t stream);
+hipError_t launch_gather(const GatherParams& p, int head_dim, bool fp8, hipStream_t stream);
+hipError_t launch_extend(const ExtendParams& p, int head_dim, bool fp8, int num_seqs,
+                         hipStream_t stream);
+
+}  // namespace pa

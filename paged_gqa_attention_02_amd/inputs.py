@@ -235,8 +235,8 @@ def decode_config(n: int, page_size: Optional[int] = None) -> DecodeCase:
 
     1  tiny: B 2, 4/1 heads, D 64, P 16, L {37, 100}, 64-page pool, 2 splits
     2  Llama-3-8B-shaped: B 64, 32/8 heads, D 128, P 16, L ~ U{512..4096}
-    3  long context: B 4, 32/8, D 128, P 64 (or 1), L ~ U{32768..131072},
-       soft-cap 30
+    3  long context: B 4, 32/8, D 128, P 64, L ~ U{32768..131072}, soft-cap 30;
+       another page_size re-pages the same logical tokens
     4  fp8 KV: B 256, 64/8, D 128, P 16, e4m3fn K/V with scales ~ U[0.5, 2],
        L lognormal (median 1024, sigma 1, clipped to [16, 8192]), window 4096
     """
@@ -250,8 +250,12 @@ def decode_config(n: int, page_size: Optional[int] = None) -> DecodeCase:
                            lens_rng=rng)
     if n == 3:
         lens = rng.integers(32768, 131072, size=4, endpoint=True)
-        return make_decode("long-context", lens, 32, 8, 128, page_size or 64, n,
-                           softcap=30.0, lens_rng=rng)
+        case = make_decode("long-context", lens, 32, 8, 128, 64, n, softcap=30.0,
+                           lens_rng=rng)
+        if page_size not in (None, 64):
+            # the same logical tokens, re-paged (seeded permutation of a new pool)
+            case = relayout(case, page_size, seed=100 + n)
+        return case
     if n == 4:
         lens = np.clip(np.rint(rng.lognormal(math.log(1024.0), 1.0, size=256)),
                        16, 8192).astype(np.int64)

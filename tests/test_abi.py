@@ -1,0 +1,151 @@
+"""The C ABI on the CPU: the library loads, exports every entry point the
+header declares, plans without a device, and rejects each bad argument with
+its status code before anything is launched."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch  # noqa: F401  (loads the HIP runtime the library shares)
+
+import paged_gqa_attention_02_amd as pa
+from paged_gqa_attention_02_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "paged_attn.h")
+
+OK, NULLP, SHAPE, UNSUP, WS, MISAL, MISMATCH, HIP = range(8)
+
+
+def header_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:pa_status|const char\*|int)\s+(paged_attn_\w+)\s*\(",
+                                 src, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = header_functions()
+    assert len(names) >= 8
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, re.M))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    lib = pa.lib()
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def test_abi_version_and_runtime():
+    assert pa.lib().paged_attn_abi_version() == 1
+    assert pa.lib().paged_attn_hip_runtime_path().decode().endswith(".so")
+
+
+def test_status_strings():
+    for s in range(8):
+        assert pa.status_str(s) and pa.status_str(s) != "unknown status"
+    assert pa.status_str(99) == "unknown status"
+
+
+def prob(**kw):
+    d = dict(mode=0, num_seqs=4, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
+             kv_dtype=0, window=0, max_pages_per_seq=256, max_kv_len=4096, total_q=0,
+             max_q_len=0, num_splits=0)
+    d.update(kw)
+    return B.PaProblem(**d)
+
+
+def plan_status(**kw):
+    out = B.PaPlan()
+    return pa.lib().paged_attn_plan(ctypes.byref(prob(**kw)), -1, ctypes.byref(out)), out
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({}, OK),
+    (dict(num_q_heads=30), SHAPE),
+    (dict(num_q_heads=8 * 32), UNSUP),           # G = 32
+    (dict(num_q_heads=24), UNSUP),               # G = 3
+    (dict(head_dim=96), UNSUP),
+    (dict(page_size=12), UNSUP),
+    (dict(kv_dtype=5), UNSUP),
+    (dict(mode=9), UNSUP),
+    (dict(max_pages_per_seq=255), SHAPE),
+    (dict(num_seqs=-1), SHAPE),
+    (dict(num_splits=-2), SHAPE),
+    (dict(mode=1, total_q=100, max_q_len=0), SHAPE),
+    (dict(mode=1, total_q=100, max_q_len=50), OK),
+])
+def test_plan_validation(kw, status):
+    assert plan_status(**kw)[0] == status
+
+
+def test_plan_decisions():
+    st, pl = plan_status()
+    assert st == OK and pl.tokens_per_split % 32 == 0
+    assert pl.num_splits * pl.tokens_per_split >= 4096
+    assert pl.workspace_bytes >= 4 * 32 * pl.num_splits * 129 * 4
+    st, pl = plan_status(num_seqs=2, num_q_heads=4, num_kv_heads=1, head_dim=64,
+                         max_pages_per_seq=7, max_kv_len=100, num_splits=2)
+    assert st == OK and pl.num_splits == 2 and pl.tokens_per_split == 64
+    st, pl = plan_status(window=4096, max_kv_len=8192, max_pages_per_seq=512)
+    assert st == OK and pl.num_splits * pl.tokens_per_split >= 4096 + 31
+    assert pl.num_splits * pl.tokens_per_split < 8192
+    st, pl = plan_status(max_kv_len=10 ** 7, max_pages_per_seq=10 ** 7 // 16 + 1)
+    assert st == OK and pl.num_splits <= 256
+    st, pl = plan_status(num_seqs=0)
+    assert st == OK
+    assert "splits=" in pa.Plan(pl).describe()
+
+
+# ---- decode argument validation: fake, never dereferenced, pointers ----
+A = 1 << 20          # 16-byte aligned fake address
+
+
+def decode_status(plan_kw=None, **kw):
+    st, pl = plan_status(**(plan_kw or {}))
+    assert st == OK
+    args = dict(q=A, q_stride_b=32 * 128, k=A, v=A, sp=16 * 8 * 128, st=8 * 128, sh=128,
+                num_pages=10, bt=A, bt_stride=256, sl=A, page_size=16, scale=0.1,
+                softcap=0.0, window=0, ks=1.0, vs=1.0, out=A, out_stride_b=32 * 128,
+                ws=A, ws_bytes=pl.workspace_bytes, stream=None)
+    args.update(kw)
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    return pa.lib().paged_attn_decode(
+        ctypes.byref(pl), v(args["q"]), args["q_stride_b"], v(args["k"]), v(args["v"]),
+        args["sp"], args["st"], args["sh"], args["num_pages"], v(args["bt"]),
+        args["bt_stride"], v(args["sl"]), args["page_size"], args["scale"], args["softcap"],
+        args["window"], args["ks"], args["vs"], v(args["out"]), args["out_stride_b"],
+        v(args["ws"]), args["ws_bytes"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), NULLP),
+    (dict(k=None), NULLP),
+    (dict(bt=None), NULLP),
+    (dict(sl=None), NULLP),
+    (dict(out=None), NULLP),
+    (dict(ws=None), NULLP),
+    (dict(page_size=32), MISMATCH),
+    (dict(window=5), MISMATCH),
+    (dict(q=A + 2), MISAL),
+    (dict(out=A + 8), MISAL),
+    (dict(v=A + 4), MISAL),
+    (dict(sh=100), MISAL),
+    (dict(q_stride_b=32 * 128 - 8), SHAPE),
+    (dict(bt_stride=100), SHAPE),
+    (dict(num_pages=0), SHAPE),
+    (dict(ws_bytes=100), WS),
+    (dict(scale=float("nan")), SHAPE),
+    (dict(softcap=float("inf")), SHAPE),
+])
+def test_decode_validation(kw, status):
+    assert decode_status(**kw) == status
+
+
+def test_decode_empty_batch_launches_nothing():
+    assert decode_status(plan_kw=dict(num_seqs=0), q=None, out=None, ws=None) == OK
+
+
+def test_decode_plan_mode_mismatch():
+    assert decode_status(plan_kw=dict(mode=1, total_q=10, max_q_len=10)) == MISMATCH
