@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Paged GQA attention on one MI355X: decode KV GB/s and us per call.
+
+    python bench.py [--steps K] [--warmup W] [--workload 2]
+
+One step is one pass of the whole decode path over one batch of synthetic
+input: the split pass (block-table gather, q.k, soft-cap/window mask, online
+softmax, p.v, split partials with log-sum-exp) and the merge of the splits.
+The default workload is the Llama-3-8B-shaped decode (64 sequences, 32/8
+heads, head_dim 128, bf16, page size 16, lengths uniform in [512, 4096]).
+Inputs are resident in HBM before timing starts; consecutive steps read
+different copies of the inputs so no step finds the previous step's data in
+the 256 MB last-level cache.  Prints one JSON line.
+
+Workloads 1-4 are the decode workloads of paged_gqa_attention_02_amd.inputs;
+5 is the prefix-prefill/extend workload (MFMA-bound; reports TFLOP/s).
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--page-size", type=int, default=None,
+                    help="long-context workload only: re-page the same tokens")
+    ap.add_argument("--splits", type=int, default=0, help="force the decode split cap")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU-baseline budget (0 disables the oracle leg)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def src_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "paged_gqa_attention_02_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str, workload: str, srcs):
+    """HBM bytes per launch from committed counter summaries, if they were
+    taken from the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}.traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256_16") != src_hash(*srcs):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(run_once, alg_units, unit_scale, unit, budget_s, threads, sample):
+    """Time the oracle (as it stands) on the host cores, repeating the sample
+    until the budget is used; returns the reported-baseline object."""
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        run_once(threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or el / reps * (reps + 1) > 3 * budget_s:
+            break
+    return {"value": alg_units * reps / el / unit_scale, "unit": unit, "cores": threads,
+            "kind": "oracle", "sample": f"{sample}; {reps} pass(es) in {el:.1f} s"}
+
+
+def copy_probe(torch):
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
+
+
+def bench_decode(args, torch, pa, I):
+    dev = "cuda:0"
+    case = I.decode_config(args.workload, page_size=args.page_size)
+    alg = case.algorithmic_bytes()
+    copies = max(2, math.ceil(2 * MALL_BYTES / max(case.kv_bytes(), 1)) + 1)
+    tensors = [I.decode_tensors(case, dev) for _ in range(copies)]
+    t0 = tensors[0]
+    plan = pa.decode_plan(t0["q"], t0["k_pool"], t0["block_table"], case.max_kv_len,
+                          window=case.window, num_splits=args.splits)
+    out = torch.empty_like(t0["q"])
+    ws = (torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+          if plan.workspace_bytes else None)
+
+    def stage(i, which):
+        t = tensors[i % copies]
+        pa.decode(plan, t["q"], t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
+                  case.scale, softcap=case.softcap, window=case.window,
+                  k_scale=case.k_scale, v_scale=case.v_scale, out=out, workspace=ws,
+                  stage=which)
+
+    for i in range(args.warmup):
+        stage(i, "partial")
+        stage(i, "merge")
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    w0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record()
+        stage(i, "partial")
+        ev[i][1].record()
+        stage(i, "merge")
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    part_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    merge_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    call_ms = sum(e[0].elapsed_time(e[2]) for e in ev) / K
+    ms_step = wall * 1e3 / K
+    achieved = alg / (part_ms * 1e-3) / 1e9
+    traffic = traffic_for("decode_partial", case.name, ["decode.hip", "pa_device.h"])
+    res = {
+        "metric": "paged-attn decode KV GB/s (fraction of HBM peak) + us/call on 1 MI355X",
+        "value": alg / (ms_step * 1e-3) / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if case.kv_dtype == "bf16" else "fp8_e4m3 KV, bf16 Q/out",
+        "data": "synthetic",
+        "config": {"workload": f"{case.name} decode", "batch": case.batch,
+                   "num_q_heads": case.num_q_heads, "num_kv_heads": case.num_kv_heads,
+                   "head_dim": case.head_dim, "page_size": case.page_size,
+                   "kv_dtype": case.kv_dtype, "window": case.window,
+                   "softcap": case.softcap, "total_tokens": int(case.seq_lens.sum()),
+                   "seed": args.workload, "input_copies": copies},
+        "us_per_call": call_ms * 1e3,
+        "hbm_frac": (alg / (ms_step * 1e-3) / 1e9) / HBM_PEAK_GBS,
+        "algorithmic_bytes": alg, "kv_bytes": case.kv_bytes(),
+        "kernel_us": {"decode_partial": part_ms * 1e3, "decode_merge": merge_ms * 1e3},
+        "plan": plan.describe(),
+        "roofline": {"bound": "hbm", "kernel": "decode_partial", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic},
+    }
+    if args.cpu_seconds > 0:
+        import oracle
+        thr = oracle.default_threads()
+        res["cpu_baseline"] = cpu_baseline(
+            lambda th: oracle.decode(case, threads=th), alg, 1e9, "GB/s",
+            args.cpu_seconds, thr,
+            f"the whole workload ({case.batch} sequences, {int(case.seq_lens.sum())} tokens)"
+            f", fp64 oracle")
+    return res
+
+
+def bench_extend(args, torch, pa, I):
+    dev = "cuda:0"
+    case = I.extend_config(5)
+    flops = case.flops()
+    t = I.extend_tensors(case, dev)
+    plan = pa.extend_plan(t["q"], t["k_pool"], t["block_table"], case.batch,
+                          case.max_kv_len, case.max_q_len, window=case.window)
+    out = torch.empty_like(t["q"])
+
+    def step():
+        pa.extend(plan, t["q"], t["k_new"], t["v_new"], t["cu_seqlens_q"], t["ctx_lens"],
+                  t["k_pool"], t["v_pool"], t["block_table"], case.scale,
+                  softcap=case.softcap, window=case.window, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    w0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record()
+        step()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    k_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    ms_step = wall * 1e3 / K
+    achieved = flops / (k_ms * 1e-3) / 1e12
+    res = {
+        "metric": "paged-attn extend TFLOP/s (fraction of MFMA bf16 peak) on 1 MI355X",
+        "value": flops / (ms_step * 1e-3) / 1e12, "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "extend", "batch": case.batch,
+                   "num_q_heads": case.num_q_heads, "num_kv_heads": case.num_kv_heads,
+                   "head_dim": case.head_dim, "page_size": case.kv.page_size,
+                   "total_q": case.total_q, "context_tokens": int(case.ctx_lens.sum()),
+                   "seed": 5},
+        "us_per_call": k_ms * 1e3, "algorithmic_flops": flops,
+        "roofline": {"bound": "mfma", "kernel": "extend", "achieved": achieved,
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": traffic_for("extend", "extend", ["extend.hip", "pa_device.h"])},
+    }
+    if args.cpu_seconds > 0:
+        import numpy as np
+        import oracle
+        thr = oracle.default_threads()
+        rng = np.random.default_rng(0)
+        rows = np.sort(rng.choice(case.total_q, size=64, replace=False))
+        pairs = 0
+        cu, ctx = case.cu_seqlens_q, case.ctx_lens
+        for r in rows:
+            b = int(np.searchsorted(cu, r, side="right") - 1)
+            pairs += int(ctx[b]) + int(r - cu[b]) + 1
+        res["cpu_baseline"] = cpu_baseline(
+            lambda th: oracle.extend(case, rows=rows, threads=th),
+            4 * case.head_dim * case.num_q_heads * pairs, 1e12, "TFLOP/s",
+            args.cpu_seconds, thr, "64 seeded random rows of the workload, all heads")
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this library runs on one GPU; --gpus {args.gpus} is not "
+              "supported (nothing is sharded across GPUs)", file=sys.stderr)
+        sys.exit(2)
+    sys.path.insert(0, ROOT)
+    import torch
+    if args.copy_probe:
+        copy_probe(torch)
+        return
+    import paged_gqa_attention_02_amd as pa
+    from paged_gqa_attention_02_amd import inputs as I
+    pa.lib()
+    res = bench_extend(args, torch, pa, I) if args.workload == 5 else \
+        bench_decode(args, torch, pa, I)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -160,6 +160,40 @@ pa_status paged_attn_decode(const pa_plan* plan,
                             void* hip_stream);
 
 /*
+ * paged_attn_decode_partial / paged_attn_decode_merge -- the two stages that
+ * paged_attn_decode enqueues, callable one at a time with the same arguments
+ * (the stage-1 partial pass and the stage-2 merge of `decode_attention_fwd`).
+ * The partial stage writes `out` for sequences whose key range fits one split
+ * and the workspace partials for the others; the merge stage completes `out`
+ * from the workspace (it launches nothing when the plan has one split).
+ * Calling partial then merge on one stream equals one paged_attn_decode.
+ */
+pa_status paged_attn_decode_partial(const pa_plan* plan,
+                                    const void* q, int64_t q_stride_b,
+                                    const void* k_pool, const void* v_pool,
+                                    int64_t kv_stride_page, int64_t kv_stride_tok,
+                                    int64_t kv_stride_head, int64_t num_pages,
+                                    const int32_t* block_table, int64_t bt_stride,
+                                    const int32_t* seq_lens,
+                                    int32_t page_size, float scale, float softcap,
+                                    int32_t window, float k_scale, float v_scale,
+                                    void* out, int64_t out_stride_b,
+                                    void* workspace, uint64_t workspace_bytes,
+                                    void* hip_stream);
+pa_status paged_attn_decode_merge(const pa_plan* plan,
+                                  const void* q, int64_t q_stride_b,
+                                  const void* k_pool, const void* v_pool,
+                                  int64_t kv_stride_page, int64_t kv_stride_tok,
+                                  int64_t kv_stride_head, int64_t num_pages,
+                                  const int32_t* block_table, int64_t bt_stride,
+                                  const int32_t* seq_lens,
+                                  int32_t page_size, float scale, float softcap,
+                                  int32_t window, float k_scale, float v_scale,
+                                  void* out, int64_t out_stride_b,
+                                  void* workspace, uint64_t workspace_bytes,
+                                  void* hip_stream);
+
+/*
  * paged_attn_extend -- prefix-prefill of new tokens on top of a paged context.
  *
  *   q             bf16 [total_q, Hq, D] (rows of all sequences, concatenated)

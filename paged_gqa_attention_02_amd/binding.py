@@ -58,9 +58,10 @@ def lib():
     PP = ctypes.POINTER(PaPlan)
     L.paged_attn_plan.argtypes = [ctypes.POINTER(PaProblem), ctypes.c_int, PP]
     L.paged_attn_plan.restype = ctypes.c_int
-    L.paged_attn_decode.argtypes = [PP, p, i64, p, p, i64, i64, i64, i64, p, i64, p,
-                                    i32, f32, f32, i32, f32, f32, p, i64, p, u64, p]
-    L.paged_attn_decode.restype = ctypes.c_int
+    for fn in ("paged_attn_decode", "paged_attn_decode_partial", "paged_attn_decode_merge"):
+        getattr(L, fn).argtypes = [PP, p, i64, p, p, i64, i64, i64, i64, p, i64, p,
+                                   i32, f32, f32, i32, f32, f32, p, i64, p, u64, p]
+        getattr(L, fn).restype = ctypes.c_int
     L.paged_attn_extend.argtypes = [PP, p, p, p, p, p, p, p, i64, i64, i64, i64, p, i64,
                                     i32, f32, f32, i32, f32, f32, p, p, u64, p]
     L.paged_attn_extend.restype = ctypes.c_int
@@ -181,8 +182,12 @@ def decode(pl: Plan, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor
            block_table: torch.Tensor, seq_lens: torch.Tensor, scale: float,
            softcap: float = 0.0, window: int = 0, k_scale: float = 1.0,
            v_scale: float = 1.0, out: Optional[torch.Tensor] = None,
-           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """paged_attn_decode: q bf16 [B, Hq, D] -> out bf16 [B, Hq, D]."""
+           workspace: Optional[torch.Tensor] = None, stream=None,
+           stage: str = "all") -> torch.Tensor:
+    """paged_attn_decode: q bf16 [B, Hq, D] -> out bf16 [B, Hq, D].
+    stage="partial" / "merge" calls paged_attn_decode_partial / _merge."""
+    fn = {"all": "paged_attn_decode", "partial": "paged_attn_decode_partial",
+          "merge": "paged_attn_decode_merge"}[stage]
     if q.dtype != torch.bfloat16 or q.dim() != 3 or q.stride(2) != 1 or q.stride(1) != q.shape[2]:
         raise ValueError("q must be bf16 [B, Hq, D] with contiguous heads")
     if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
@@ -194,7 +199,7 @@ def decode(pl: Plan, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor
     sp, st, sh = _pool_strides(k_pool, v_pool)
     workspace = _workspace(pl, workspace, q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("paged_attn_decode", lib().paged_attn_decode(
+    _check(fn, getattr(lib(), fn)(
         ctypes.byref(pl.c), _ptr(q), q.stride(0), _ptr(k_pool), _ptr(v_pool), sp, st, sh,
         k_pool.shape[0], _ptr(block_table), block_table.stride(0), _ptr(seq_lens),
         k_pool.shape[1], float(scale), float(softcap), int(window), float(k_scale),

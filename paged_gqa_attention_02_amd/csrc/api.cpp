@@ -22,7 +22,7 @@ namespace {
 using namespace pa;
 
 constexpr int kDefaultCus = 256;  // MI355X
-constexpr int kMinSplitTokens = 256;
+constexpr int kMinSplitTokens = 512;
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 int ilog2(int x) {
@@ -74,6 +74,10 @@ pa_status check_pools(const pa_plan& pl, const void* k_pool, const void* v_pool,
     const int64_t eb = elem_bytes(pr.kv_dtype);
     if (!aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_MISALIGNED;
     if ((s_page * eb) % 16 || (s_tok * eb) % 16 || (s_head * eb) % 16) return PA_ERR_MISALIGNED;
+    // byte offsets inside one page are 32-bit in the kernels
+    const int64_t in_page = ((int64_t)(pr.page_size - 1) * s_tok +
+                             (int64_t)(pr.num_kv_heads - 1) * s_head + pr.head_dim) * eb;
+    if (in_page >= ((int64_t)1 << 31)) return PA_ERR_UNSUPPORTED;
     return PA_OK;
 }
 
@@ -136,14 +140,20 @@ pa_status paged_attn_plan(const pa_problem* prob, int hip_device, pa_plan* out) 
         if (pr.num_splits > 0) {
             T = round_up(std::max<int64_t>(cdiv(span, pr.num_splits), 1), kTile);
         } else {
-            // Aim for ~16 work items per compute unit, assuming sequences
+            // Aim for ~8 work items per compute unit, assuming sequences
             // average half the bound; never split finer than kMinSplitTokens.
-            const int64_t target = 16LL * cus;
+            const int64_t target = 8LL * cus;
             T = round_up(std::max<int64_t>(cdiv(units * span, 2 * target), 1), kTile);
             T = std::max<int64_t>(T, kMinSplitTokens);
         }
         if (span > 0 && cdiv(span, T) > kMaxSplits) T = round_up(cdiv(span, kMaxSplits), kTile);
-        if (T > (int64_t)1 << 30) return PA_ERR_INVALID_SHAPE;
+        // A split's page list is staged in LDS: at most T/P + 2 entries.
+        const int64_t t_max = ((int64_t)(kMaxSplitPages - 2) * pr.page_size) / kTile * kTile;
+        T = std::min<int64_t>(T, t_max);
+        if (span > 0 && cdiv(span, T) > kMaxSplits) return PA_ERR_UNSUPPORTED;
+        if ((int64_t)cdiv(std::max<int64_t>(span, 1), T) * pr.num_seqs * pr.num_kv_heads >
+            (int64_t)INT32_MAX)
+            return PA_ERR_UNSUPPORTED;
         const int64_t S = span > 0 ? cdiv(span, T) : 1;
         pl.tokens_per_split = (int32_t)T;
         pl.num_splits = (int32_t)S;
@@ -178,14 +188,19 @@ int paged_attn_plan_describe(const pa_plan* pl, char* buf, int buf_len) {
     return n;
 }
 
-pa_status paged_attn_decode(const pa_plan* plan, const void* q, int64_t q_stride_b,
-                            const void* k_pool, const void* v_pool, int64_t kv_stride_page,
-                            int64_t kv_stride_tok, int64_t kv_stride_head, int64_t num_pages,
-                            const int32_t* block_table, int64_t bt_stride,
-                            const int32_t* seq_lens, int32_t page_size, float scale,
-                            float softcap, int32_t window, float k_scale, float v_scale,
-                            void* out, int64_t out_stride_b, void* workspace,
-                            uint64_t workspace_bytes, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+enum { kStagePartial = 1, kStageMerge = 2 };
+
+pa_status decode_impl(int stages, const pa_plan* plan, const void* q, int64_t q_stride_b,
+                      const void* k_pool, const void* v_pool, int64_t kv_stride_page,
+                      int64_t kv_stride_tok, int64_t kv_stride_head, int64_t num_pages,
+                      const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
+                      int32_t page_size, float scale, float softcap, int32_t window,
+                      float k_scale, float v_scale, void* out, int64_t out_stride_b,
+                      void* workspace, uint64_t workspace_bytes, void* hip_stream) {
     if (!plan) return PA_ERR_NULL_POINTER;
     const pa_plan& pl = *plan;
     const pa_problem& pr = pl.prob;
@@ -227,7 +242,9 @@ pa_status paged_attn_decode(const pa_plan* plan, const void* q, int64_t q_stride
     p.block_table = block_table;
     p.bt_stride = bt_stride;
     p.seq_lens = seq_lens;
+    p.num_seqs = pr.num_seqs;
     p.num_q_heads = pr.num_q_heads;
+    p.num_kv_heads = pr.num_kv_heads;
     p.group = pr.num_q_heads / pr.num_kv_heads;
     p.page_shift = ilog2(pr.page_size);
     p.window = pr.window;
@@ -251,13 +268,42 @@ pa_status paged_attn_decode(const pa_plan* plan, const void* q, int64_t q_stride
     }
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     const bool uniform = pr.page_size >= 16;
-    if (launch_decode(p, pr.head_dim, pr.kv_dtype == PA_KV_FP8_E4M3, uniform, pr.num_seqs,
+    if ((stages & kStagePartial) &&
+        launch_decode(p, pr.head_dim, pr.kv_dtype == PA_KV_FP8_E4M3, uniform, pr.num_seqs,
                       pr.num_kv_heads, stream) != hipSuccess)
         return PA_ERR_HIP;
-    if (pl.num_splits > 1 &&
+    if ((stages & kStageMerge) && pl.num_splits > 1 &&
         launch_decode_merge(p, pr.head_dim, pr.num_seqs, pr.num_kv_heads, stream) != hipSuccess)
         return PA_ERR_HIP;
     return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+#define PA_DECODE_ARGS                                                                      \
+    plan, q, q_stride_b, k_pool, v_pool, kv_stride_page, kv_stride_tok, kv_stride_head,     \
+        num_pages, block_table, bt_stride, seq_lens, page_size, scale, softcap, window,     \
+        k_scale, v_scale, out, out_stride_b, workspace, workspace_bytes, hip_stream
+#define PA_DECODE_PARAMS                                                                    \
+    const pa_plan *plan, const void *q, int64_t q_stride_b, const void *k_pool,             \
+        const void *v_pool, int64_t kv_stride_page, int64_t kv_stride_tok,                  \
+        int64_t kv_stride_head, int64_t num_pages, const int32_t *block_table,              \
+        int64_t bt_stride, const int32_t *seq_lens, int32_t page_size, float scale,         \
+        float softcap, int32_t window, float k_scale, float v_scale, void *out,             \
+        int64_t out_stride_b, void *workspace, uint64_t workspace_bytes, void *hip_stream
+
+pa_status paged_attn_decode(PA_DECODE_PARAMS) {
+    return decode_impl(kStagePartial | kStageMerge, PA_DECODE_ARGS);
+}
+
+pa_status paged_attn_decode_partial(PA_DECODE_PARAMS) {
+    return decode_impl(kStagePartial, PA_DECODE_ARGS);
+}
+
+pa_status paged_attn_decode_merge(PA_DECODE_PARAMS) {
+    return decode_impl(kStageMerge, PA_DECODE_ARGS);
 }
 
 pa_status paged_attn_gather(const pa_plan* plan, const void* k_pool, const void* v_pool,

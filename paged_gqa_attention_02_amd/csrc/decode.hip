@@ -95,21 +95,239 @@ struct VRow {
     }
 };
 
+// Addressing of one split.  Page ids come from the split's page list in LDS
+// (pages[i] = block_table[b][first_page + i]); the list index is clamped into
+// the list, so every address lies inside a page of the split whatever the
+// token: rows outside [t_begin, t_end) are read but their scores are masked
+// and their V rows zeroed by the consumer.  Per-lane parts of the addresses
+// that do not change from tile to tile are precomputed (bytes).
+struct TileCtx {
+    const int* pages;
+    int first_page, last_idx, t_begin, t_end, c, grp;
+    int64_t page_bytes;        // s_page * elem
+    int tok_bytes;             // s_tok * elem
+    int k_lane;                // kvh*s_head*elem + 16*grp (+ c*tok_bytes when UNIFORM)
+    int v_lane[4];             // kvh*s_head*elem + VBYTES*c (+ (4*grp + r)*tok_bytes when UNIFORM)
+};
+
+template <bool UNIFORM>
+__device__ __forceinline__ int64_t page_of(const TileCtx& x, int pshift, int t) {
+    const int idx = min(max((t >> pshift) - x.first_page, 0), x.last_idx);
+    if constexpr (UNIFORM)   // one page for the whole wave: keep it scalar
+        return (int64_t)__builtin_amdgcn_readfirstlane(x.pages[idx]);
+    return (int64_t)x.pages[idx];
+}
+
+// Streaming loads of K/V rows: every byte is read once, so they bypass
+// cache retention (nontemporal).
+template <typename T>
+__device__ __forceinline__ T load_stream(const uint8_t* ptr) {
+    return __builtin_nontemporal_load(reinterpret_cast<const T*>(ptr));
+}
+
+// K rows of a tile as S^T A operands: tokens 16h + c, h = 0, 1.  Load i of a
+// half reads the 16 bytes at 64*i of the lane's slice of the row.
+template <int D, bool FP8>
+struct KRegs {
+    static constexpr int N = FP8 ? D / 64 : D / 32;   // 16-byte loads per half
+    u32x4 w[2][N];
+};
+
 template <int D, bool FP8, bool UNIFORM>
-__global__ __launch_bounds__(kDecodeWaves * 64) void decode_partial_kernel(DecodeParams p) {
+__device__ __forceinline__ void issue_k(KRegs<D, FP8>& R, const DecodeParams& p,
+                                        const TileCtx& x, int t0) {
+    const uint8_t* pool = static_cast<const uint8_t*>(p.k_pool);
+    const int pmask = (1 << p.page_shift) - 1;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint8_t* ptr;
+        if constexpr (UNIFORM) {
+            // page_size is a multiple of 16: the half sits in one page
+            const int th = t0 + 16 * h;
+            const uint8_t* base = pool + page_of<true>(x, p.page_shift, th) * x.page_bytes +
+                                  (int64_t)((th & pmask) * x.tok_bytes);
+            ptr = base + x.k_lane;
+        } else {
+            const int t = t0 + 16 * h + x.c;
+            ptr = pool + page_of<false>(x, p.page_shift, t) * x.page_bytes +
+                  (int64_t)((t & pmask) * x.tok_bytes + x.k_lane);
+        }
+#pragma unroll
+        // (plain loads: each 128-byte line of a row is read by two
+        // consecutive instructions, and the second must find it cached)
+        for (int i = 0; i < KRegs<D, FP8>::N; ++i)
+            R.w[h][i] = *reinterpret_cast<const u32x4*>(ptr + 64 * i);
+    }
+}
+
+// V chunks of the 8 tokens this lane transposes for P*V.
+template <int D, bool FP8>
+struct VRegs {
+    typename VRow<D, FP8>::Raw w[8];
+};
+
+template <int D, bool FP8, bool UNIFORM>
+__device__ __forceinline__ void issue_v(VRegs<D, FP8>& R, const DecodeParams& p,
+                                        const TileCtx& x, int t0) {
+    using Raw = typename VRow<D, FP8>::Raw;
+    const uint8_t* pool = static_cast<const uint8_t*>(p.v_pool);
+    const int pmask = (1 << p.page_shift) - 1;
+    if constexpr (UNIFORM) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int th = t0 + 16 * h;
+            const uint8_t* base = pool + page_of<true>(x, p.page_shift, th) * x.page_bytes +
+                                  (int64_t)((th & pmask) * x.tok_bytes);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) R.w[4 * h + r] = load_stream<Raw>(base + x.v_lane[r]);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int t = t0 + tile_token(x.grp, i);
+            const uint8_t* ptr = pool + page_of<false>(x, p.page_shift, t) * x.page_bytes +
+                                 (int64_t)((t & pmask) * x.tok_bytes + x.v_lane[0]);
+            R.w[i] = load_stream<Raw>(ptr);
+        }
+    }
+}
+
+// S^T = K Q^T for one tile: s[h][j] is the score of token 16h + 4*grp + j for
+// the head of this lane's column.
+template <int D, bool FP8>
+__device__ __forceinline__ void tile_scores(f32x4 s[2], const KRegs<D, FP8>& R,
+                                            const u32x4* qop) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        s[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < KRegs<D, FP8>::N; ++i) {
+            const u32x4 w = R.w[h][i];
+            if constexpr (FP8) {
+                const u32x2 a = e4m3x4_to_bf16x4(w.x), bb = e4m3x4_to_bf16x4(w.y);
+                const u32x2 cc = e4m3x4_to_bf16x4(w.z), dd = e4m3x4_to_bf16x4(w.w);
+                s[h] = mfma_bf16_16x16x32(u32x4{a.x, a.y, bb.x, bb.y}, qop[2 * i], s[h]);
+                s[h] = mfma_bf16_16x16x32(u32x4{cc.x, cc.y, dd.x, dd.y}, qop[2 * i + 1], s[h]);
+            } else {
+                s[h] = mfma_bf16_16x16x32(w, qop[i], s[h]);
+            }
+        }
+    }
+}
+
+// Online-softmax state of one wave: running max / partial sum of the head in
+// this lane's MFMA column, and O rows 4*grp..4*grp+3 at d = VE*c + e.
+template <int D>
+struct Acc {
+    float m = -INFINITY;
+    float l = 0.f;
+    f32x4 o[D / 16];
+};
+
+// Scores -> probabilities (log2 domain), running max/sum, O rescale.
+// Returns the P operand (bf16) of P*V.
+template <int D, bool CAP>
+__device__ __forceinline__ u32x4 tile_softmax(Acc<D>& A, const f32x4 s[2],
+                                              const DecodeParams& p, const TileCtx& x, int t0,
+                                              bool full) {
+    constexpr int VE = D / 16;
+    float sc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        float v = (j < 4) ? s[0][j] : s[1][j - 4];
+        if constexpr (CAP) {
+            // c*tanh(y/c) = c - 2c / (exp(2y/c) + 1), times log2(e)
+            v = p.cap_c2 - 2.f * p.cap_c2 * fast_rcp(fast_exp2(v * p.cap_c1) + 1.f);
+        } else {
+            v *= p.qk_scale2;
+        }
+        sc[j] = v;
+    }
+    if (!full) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int t = t0 + tile_token(x.grp, j);
+            sc[j] = (t >= x.t_begin && t < x.t_end) ? sc[j] : -INFINITY;
+        }
+    }
+    float tmax = sc[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) tmax = fmaxf(tmax, sc[j]);
+    tmax = fmaxf(tmax, shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+    const float m_new = fmaxf(A.m, tmax);
+    const float alpha = fast_exp2(A.m - m_new);
+    float pr[8];
+    float psum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        pr[j] = fast_exp2(sc[j] - m_new);
+        psum += pr[j];
+    }
+    A.l = A.l * alpha + psum;
+    A.m = m_new;
+    // rescale O: row 4*grp + j belongs to head column 4*grp + j
+    float arow[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) arow[j] = __shfl(alpha, 4 * x.grp + j, 64);
+#pragma unroll
+    for (int e = 0; e < VE; ++e)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) A.o[e][j] *= arow[j];
+    return u32x4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
+                 pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])};
+}
+
+// O += P V, V rows transposed in registers (v_perm) into B operands.
+template <int D, bool FP8>
+__device__ __forceinline__ void tile_pv(Acc<D>& A, VRegs<D, FP8>& R, u32x4 pop,
+                                        const TileCtx& x, int t0, bool full) {
+    constexpr int VE = D / 16;
+    using VR = VRow<D, FP8>;
+    if (!full) {
+        // rows outside the key range may hold anything (NaN included): zero
+        // them in place (the buffer is refilled right after)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int t = t0 + tile_token(x.grp, i);
+            R.w[i] = (t >= x.t_begin && t < x.t_end) ? R.w[i] : VChunk<VR::kBytes>::zero();
+        }
+    }
+    VR vr[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) vr[i].from_raw(R.w[i]);
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+        const bool hi = e & 1;
+        const int wd = e >> 1;
+        const u32x4 bop = {pick_halves(vr[0].w[wd], vr[1].w[wd], hi),
+                           pick_halves(vr[2].w[wd], vr[3].w[wd], hi),
+                           pick_halves(vr[4].w[wd], vr[5].w[wd], hi),
+                           pick_halves(vr[6].w[wd], vr[7].w[wd], hi)};
+        A.o[e] = mfma_bf16_16x16x32(pop, bop, A.o[e]);
+        // build each B operand right before its MFMA (keeps 4 registers live,
+        // not 4*VE)
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <int D, bool FP8, bool UNIFORM, bool CAP, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kDecodeOccupancy)))
+void decode_partial_kernel(DecodeParams p) {
     constexpr int KK = D / 32;                  // QK MFMAs per 16-token half
     constexpr int VE = D / 16;                  // PV MFMAs per tile
-    constexpr int NW = kDecodeWaves;
-    using VR = VRow<D, FP8>;
-    using Raw = typename VR::Raw;
 
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave = NW == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c = lane & 15;
     const int grp = lane >> 4;
-    const int split = blockIdx.x;
-    const int kvh = blockIdx.y;
-    const int b = blockIdx.z;
+    // Work items are numbered kv-head fastest, then sequence, then split:
+    // blocks are dealt to the 8 XCDs by block id modulo 8, so this keeps the
+    // split index (whose upper values exist only for long sequences) out of
+    // the XCD choice and gives every XCD an even share of the work.
+    const int kvh = blockIdx.x % p.num_kv_heads;
+    const int b = (blockIdx.x / p.num_kv_heads) % p.num_seqs;
+    const int split = blockIdx.x / (p.num_kv_heads * p.num_seqs);
     const int G = p.group;
 
     const int L = p.seq_lens[b];
@@ -120,9 +338,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_partial_kernel(Decod
     // the partials)
     const int n_splits = L > lo ? min((L - base + T - 1) / T, p.num_splits) : 0;
 
-    __shared__ float sm_m[NW][16];
-    __shared__ float sm_l[NW][16];
-    __shared__ float sm_o[NW][16][D];
+    __shared__ int sm_pages[kMaxSplitPages];
 
     if (split >= n_splits) {
         if (split == 0) {   // nothing to attend: zero rows
@@ -141,6 +357,15 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_partial_kernel(Decod
     const int t_end = min(chunk0 + T, L);
     const int n_tiles = (t_end - chunk0 + kTile - 1) / kTile;
 
+    // The split's page list, once, into LDS: every later page lookup is an
+    // LDS read instead of a dependent global load.
+    const int first_page = t_begin >> p.page_shift;
+    const int n_pages = ((t_end - 1) >> p.page_shift) - first_page + 1;
+    {
+        const int32_t* bt_row = p.block_table + (int64_t)b * p.bt_stride + first_page;
+        for (int i = threadIdx.x; i < n_pages; i += NW * 64) sm_pages[i] = bt_row[i];
+    }
+
     // Q^T as the B operand: column c = query head kvh*G + c.  The contraction
     // index (grp, j) of MFMA kk stands for d = dq(kk, grp) + j; for fp8 K one
     // 16-byte load feeds two consecutive MFMAs, hence the different order.
@@ -155,208 +380,164 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_partial_kernel(Decod
             qop[kk] = (c < G) ? v : u32x4{0, 0, 0, 0};
         }
     }
+    __syncthreads();
 
-    const int32_t* bt_row = p.block_table + (int64_t)b * p.bt_stride;
-    const int pshift = p.page_shift;
-    const int pmask = (1 << pshift) - 1;
+    Acc<D> acc;
+#pragma unroll
+    for (int e = 0; e < VE; ++e) acc.o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    float m_run = -INFINITY;
-    float l_run = 0.f;
-    f32x4 o[VE];
+    TileCtx x;
+    {
+        constexpr int kElem = FP8 ? 1 : 2;
+        constexpr int kVBytes = VRow<D, FP8>::kBytes;
+        x.pages = sm_pages;
+        x.first_page = first_page;
+        x.last_idx = n_pages - 1;
+        x.t_begin = t_begin;
+        x.t_end = t_end;
+        x.c = c;
+        x.grp = grp;
+        x.page_bytes = p.s_page * kElem;
+        x.tok_bytes = (int)(p.s_tok * kElem);
+        const int head = (int)(kvh * p.s_head * kElem);
+        x.k_lane = head + 16 * grp + (UNIFORM ? c * x.tok_bytes : 0);
 #pragma unroll
-    for (int e = 0; e < VE; ++e) o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int r = 0; r < 4; ++r)
+            x.v_lane[r] = head + kVBytes * c + (UNIFORM ? (4 * grp + r) * x.tok_bytes : 0);
+    }
 
-    for (int it = wave; it < n_tiles; it += NW) {
-        const int t0 = chunk0 + it * kTile;
-        const bool full = (t0 >= t_begin) && (t0 + kTile <= t_end);
-
-        // ---- addresses: page of every token this lane touches ----
-        // K rows: tokens t0 + 16h + c (h = 0, 1).  V rows: t0 + tile_token(grp, i).
-        const uint8_t* kptr[2];
-        const uint8_t* vptr[8];
-        bool kval[2], vval[8];
-        if constexpr (UNIFORM) {
-            // page_size is a multiple of 16: each 16-token half sits in one page.
-            int64_t pg[2];
+    // K and V rotate through one register set each, holding SUB consecutive
+    // tiles of this wave: the next step's K rows are requested as soon as
+    // this step's scores are formed and its V rows as soon as this step's P*V
+    // is done, so about SUB tiles per wave are always in flight.  The last
+    // step is peeled off so that the steady-state loop issues its loads
+    // unconditionally (exact load counters); a missing tile of the last step
+    // is loaded as a repeat of the wave's last tile and not consumed.  This
+    // wave's tiles are wave, wave + NW, ...
+    constexpr int SUB = kDecodeSub;
+    KRegs<D, FP8> kr[SUB];
+    VRegs<D, FP8> vr[SUB];
+    const int my_tiles = wave < n_tiles ? (n_tiles - wave + NW - 1) / NW : 0;
+    const int my_steps = (my_tiles + SUB - 1) / SUB;
+    auto tile_t0 = [&](int i) { return chunk0 + (wave + min(i, my_tiles - 1) * NW) * kTile; };
+    if (my_tiles > 0) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int th = t0 + 16 * h;
-                const bool any = (th < t_end) && (th + 16 > t_begin);
-                pg[h] = any ? (int64_t)bt_row[th >> pshift] : 0;
+        for (int u = 0; u < SUB; ++u) issue_k<D, FP8, UNIFORM>(kr[u], p, x, tile_t0(u));
+#pragma unroll
+        for (int u = 0; u < SUB; ++u) issue_v<D, FP8, UNIFORM>(vr[u], p, x, tile_t0(u));
+        for (int st = 0; st + 1 < my_steps; ++st) {
+            f32x4 s[SUB][2];
+#pragma unroll
+            for (int u = 0; u < SUB; ++u) tile_scores<D, FP8>(s[u], kr[u], qop);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < SUB; ++u)
+                issue_k<D, FP8, UNIFORM>(kr[u], p, x, tile_t0((st + 1) * SUB + u));
+#pragma unroll
+            for (int u = 0; u < SUB; ++u) {
+                const int t0 = tile_t0(st * SUB + u);
+                const bool full = (t0 >= t_begin) && (t0 + kTile <= t_end);
+                const u32x4 pop = tile_softmax<D, CAP>(acc, s[u], p, x, t0, full);
+                tile_pv<D, FP8>(acc, vr[u], pop, x, t0, full);
             }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int th = t0 + 16 * h;
-                const int t = th + c;
-                kval[h] = (t >= t_begin) && (t < t_end);
-                const int row = kval[h] ? (th & pmask) + c : 0;
-                kptr[h] = row_ptr<FP8>(p.k_pool, kval[h] ? pg[h] : 0, row, kvh, p.s_page,
-                                       p.s_tok, p.s_head);
-            }
+            for (int u = 0; u < SUB; ++u)
+                issue_v<D, FP8, UNIFORM>(vr[u], p, x, tile_t0((st + 1) * SUB + u));
+        }
+        const int st = my_steps - 1;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int h = i >> 2;
-                const int th = t0 + 16 * h;
-                const int t = t0 + tile_token(grp, i);
-                vval[i] = (t >= t_begin) && (t < t_end);
-                const int row = vval[i] ? (th & pmask) + (t - th) : 0;
-                vptr[i] = row_ptr<FP8>(p.v_pool, vval[i] ? pg[h] : 0, row, kvh, p.s_page,
-                                       p.s_tok, p.s_head);
-            }
-        } else {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int t = t0 + 16 * h + c;
-                kval[h] = (t >= t_begin) && (t < t_end);
-                const int64_t pg = kval[h] ? (int64_t)bt_row[t >> pshift] : 0;
-                kptr[h] = row_ptr<FP8>(p.k_pool, pg, kval[h] ? (t & pmask) : 0, kvh, p.s_page,
-                                       p.s_tok, p.s_head);
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int t = t0 + tile_token(grp, i);
-                vval[i] = (t >= t_begin) && (t < t_end);
-                const int64_t pg = vval[i] ? (int64_t)bt_row[t >> pshift] : 0;
-                vptr[i] = row_ptr<FP8>(p.v_pool, pg, vval[i] ? (t & pmask) : 0, kvh, p.s_page,
-                                       p.s_tok, p.s_head);
+        for (int u = 0; u < SUB; ++u) {
+            if (st * SUB + u < my_tiles) {
+                const int t0 = tile_t0(st * SUB + u);
+                const bool full = (t0 >= t_begin) && (t0 + kTile <= t_end);
+                f32x4 s[2];
+                tile_scores<D, FP8>(s, kr[u], qop);
+                const u32x4 pop = tile_softmax<D, CAP>(acc, s, p, x, t0, full);
+                tile_pv<D, FP8>(acc, vr[u], pop, x, t0, full);
             }
         }
+    }
 
-        // ---- loads (issued together; invalid tokens read a safe row, then zeroed) ----
-        constexpr int KLOADS = FP8 ? KK / 2 : KK;
-        u32x4 kraw[2][KLOADS];
+    // ---- finish: softmax sum over the 4 lanes of each column ----
+    float l_tot = acc.l + shfl_xor(acc.l, 16);
+    l_tot += shfl_xor(l_tot, 32);
+    const bool direct = (n_splits == 1);
+    if constexpr (NW == 1) {
+        // Row r = 4*grp + j of O belongs to the head of column r: fetch that
+        // column's max and sum, normalise and store this lane's VE values.
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int j = 0; j < 4; ++j) {
+            const int r = 4 * grp + j;
+            const float lr = __shfl(l_tot, r, 64);
+            const float mr = __shfl(acc.m, r, 64);
+            if (r < G) {
+                const float inv = p.v_scale / lr;
+                const int h = kvh * G + r;
+                if (direct) {
+                    uint16_t* o16 = static_cast<uint16_t*>(p.out) +
+                                    (int64_t)b * p.out_stride_b + (int64_t)h * D + VE * c;
+                    uint32_t w[VE / 2];
 #pragma unroll
-            for (int i = 0; i < KLOADS; ++i) {
-                const int off = FP8 ? 64 * i + 16 * grp : 2 * (32 * i + 8 * grp);
-                kraw[h][i] = *reinterpret_cast<const u32x4*>(kptr[h] + off);
-            }
-        Raw vraw[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            vraw[i] = *reinterpret_cast<const Raw*>(vptr[i] + VR::kBytes * c);
-
-        // ---- S^T = K Q^T ----
-        f32x4 s[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            s[h] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int i = 0; i < KLOADS; ++i) {
-                u32x4 w = kval[h] ? kraw[h][i] : u32x4{0, 0, 0, 0};
-                if constexpr (FP8) {
-                    u32x2 a = e4m3x4_to_bf16x4(w.x), bb = e4m3x4_to_bf16x4(w.y);
-                    u32x2 cc = e4m3x4_to_bf16x4(w.z), dd = e4m3x4_to_bf16x4(w.w);
-                    s[h] = mfma_bf16_16x16x32(u32x4{a.x, a.y, bb.x, bb.y}, qop[2 * i], s[h]);
-                    s[h] = mfma_bf16_16x16x32(u32x4{cc.x, cc.y, dd.x, dd.y}, qop[2 * i + 1], s[h]);
+                    for (int e = 0; e < VE; e += 2)
+                        w[e / 2] = pack_bf16x2(acc.o[e][j] * inv, acc.o[e + 1][j] * inv);
+                    if constexpr (VE == 8)
+                        *reinterpret_cast<u32x4*>(o16) = u32x4{w[0], w[1], w[2], w[3]};
+                    else
+                        *reinterpret_cast<u32x2*>(o16) = u32x2{w[0], w[1]};
                 } else {
-                    s[h] = mfma_bf16_16x16x32(w, qop[i], s[h]);
+                    const int64_t row = ((int64_t)b * p.num_q_heads + h) * p.num_splits + split;
+                    float* po = p.part_o + row * D + VE * c;
+#pragma unroll
+                    for (int e = 0; e < VE; e += 4)
+                        *reinterpret_cast<f32x4*>(po + e) =
+                            f32x4{acc.o[e][j] * inv, acc.o[e + 1][j] * inv,
+                                  acc.o[e + 2][j] * inv, acc.o[e + 3][j] * inv};
+                    if (c == 0) p.part_lse[row] = mr + __log2f(lr);
                 }
             }
         }
-
-        // ---- scores in the log2 domain, mask, online softmax ----
-        float sc[8];
+    } else {
+        // combine the waves of this block through LDS
+        __shared__ float sm_m[NW][16];
+        __shared__ float sm_l[NW][16];
+        __shared__ float sm_o[NW][16][D];
+        if (grp == 0) {
+            sm_m[wave][c] = acc.m;
+            sm_l[wave][c] = l_tot;
+        }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            float x = (j < 4) ? s[0][j] : s[1][j - 4];
-            if (p.has_cap) {
-                // c*tanh(y/c) = c - 2c / (exp(2y/c) + 1), times log2(e)
-                x = p.cap_c2 - 2.f * p.cap_c2 * fast_rcp(fast_exp2(x * p.cap_c1) + 1.f);
+        for (int j = 0; j < 4; ++j) {
+            const int r = 4 * grp + j;
+            if (r < G) {
+#pragma unroll
+                for (int e = 0; e < VE; ++e) sm_o[wave][r][VE * c + e] = acc.o[e][j];
+            }
+        }
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
+            const int r = idx / D, d = idx % D;
+            float M = sm_m[0][r];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_m[w][r]);
+            float num = 0.f, lsum = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const float f = fast_exp2(sm_m[w][r] - M);
+                num += f * sm_o[w][r][d];
+                lsum += f * sm_l[w][r];
+            }
+            const float val = num / lsum * p.v_scale;
+            const int h = kvh * G + r;
+            if (direct) {
+                uint16_t* o16 = static_cast<uint16_t*>(p.out) + (int64_t)b * p.out_stride_b +
+                                (int64_t)h * D + d;
+                *o16 = (uint16_t)(pack_bf16x2(val, 0.f) & 0xffffu);
             } else {
-                x *= p.qk_scale2;
+                const int64_t row = ((int64_t)b * p.num_q_heads + h) * p.num_splits + split;
+                p.part_o[row * D + d] = val;
+                if (d == 0) p.part_lse[row] = M + __log2f(lsum);
             }
-            if (!full) {
-                const int t = t0 + tile_token(grp, j);
-                x = (t >= t_begin && t < t_end) ? x : -INFINITY;
-            }
-            sc[j] = x;
-        }
-        float tmax = sc[0];
-#pragma unroll
-        for (int j = 1; j < 8; ++j) tmax = fmaxf(tmax, sc[j]);
-        tmax = fmaxf(tmax, shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-        const float m_new = fmaxf(m_run, tmax);
-        const float alpha = fast_exp2(m_run - m_new);
-        float pr[8];
-        float psum = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            pr[j] = fast_exp2(sc[j] - m_new);
-            psum += pr[j];
-        }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-        const u32x4 pop = {pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
-                           pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])};
-
-        // rescale O: row 4*grp + j belongs to head column 4*grp + j
-        float arow[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) arow[j] = __shfl(alpha, 4 * grp + j, 64);
-#pragma unroll
-        for (int e = 0; e < VE; ++e)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) o[e][j] *= arow[j];
-
-        // ---- O += P V ----
-        VR vr[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) vr[i].from_raw(vval[i] ? vraw[i] : VChunk<VR::kBytes>::zero());
-#pragma unroll
-        for (int e = 0; e < VE; ++e) {
-            const bool hi = e & 1;
-            const int wd = e >> 1;
-            const u32x4 bop = {pick_halves(vr[0].w[wd], vr[1].w[wd], hi),
-                               pick_halves(vr[2].w[wd], vr[3].w[wd], hi),
-                               pick_halves(vr[4].w[wd], vr[5].w[wd], hi),
-                               pick_halves(vr[6].w[wd], vr[7].w[wd], hi)};
-            o[e] = mfma_bf16_16x16x32(pop, bop, o[e]);
-        }
-    }
-
-    // ---- combine the waves of this block ----
-    float l_tot = l_run + shfl_xor(l_run, 16);
-    l_tot += shfl_xor(l_tot, 32);
-    if (grp == 0) {
-        sm_m[wave][c] = m_run;
-        sm_l[wave][c] = l_tot;
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = 4 * grp + j;
-        if (r < G) {
-#pragma unroll
-            for (int e = 0; e < VE; ++e) sm_o[wave][r][VE * c + e] = o[e][j];
-        }
-    }
-    __syncthreads();
-
-    const bool direct = (n_splits == 1);
-    for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
-        const int r = idx / D, d = idx % D;
-        float M = sm_m[0][r];
-#pragma unroll
-        for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_m[w][r]);
-        float acc = 0.f, lsum = 0.f;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            const float f = fast_exp2(sm_m[w][r] - M);
-            acc += f * sm_o[w][r][d];
-            lsum += f * sm_l[w][r];
-        }
-        const float val = acc / lsum * p.v_scale;
-        const int h = kvh * G + r;
-        if (direct) {
-            uint16_t* o16 = static_cast<uint16_t*>(p.out) + (int64_t)b * p.out_stride_b +
-                            (int64_t)h * D + d;
-            *o16 = (uint16_t)(pack_bf16x2(val, 0.f) & 0xffffu);
-        } else {
-            const int64_t row = ((int64_t)b * p.num_q_heads + h) * p.num_splits + split;
-            p.part_o[row * D + d] = val;
-            if (d == 0) p.part_lse[row] = M + __log2f(lsum);
         }
     }
 }
@@ -442,9 +623,13 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherParams p) {
 
 template <int D, bool FP8, bool UNIFORM>
 hipError_t launch_decode_t(const DecodeParams& p, int B, int Hkv, hipStream_t stream) {
-    dim3 grid(p.num_splits, Hkv, B);
-    hipLaunchKernelGGL((decode_partial_kernel<D, FP8, UNIFORM>), grid, dim3(kDecodeWaves * 64),
-                       0, stream, p);
+    dim3 grid(p.num_splits * Hkv * B);
+    if (p.has_cap)
+        hipLaunchKernelGGL((decode_partial_kernel<D, FP8, UNIFORM, true, kDecodeWaves>),
+                           grid, dim3(kDecodeWaves * 64), 0, stream, p);
+    else
+        hipLaunchKernelGGL((decode_partial_kernel<D, FP8, UNIFORM, false, kDecodeWaves>),
+                           grid, dim3(kDecodeWaves * 64), 0, stream, p);
     return hipGetLastError();
 }
 

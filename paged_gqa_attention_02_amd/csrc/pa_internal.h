@@ -12,7 +12,22 @@ constexpr int kTile = 32;
 // Split partials of one sequence are merged through LDS: at most this many.
 constexpr int kMaxSplits = 256;
 // Waves that share one (sequence, kv head, split) work item.
-constexpr int kDecodeWaves = 4;
+#ifndef PA_DECODE_WAVES
+#define PA_DECODE_WAVES 1
+#endif
+// Tiles of 32 tokens a decode wave keeps in flight per pipeline step.
+#ifndef PA_DECODE_SUB
+#define PA_DECODE_SUB 2
+#endif
+constexpr int kDecodeSub = PA_DECODE_SUB;
+#ifndef PA_DECODE_OCCUPANCY
+#define PA_DECODE_OCCUPANCY 2
+#endif
+constexpr int kDecodeWaves = PA_DECODE_WAVES;
+constexpr int kDecodeOccupancy = PA_DECODE_OCCUPANCY;   // waves per SIMD the kernel must allow
+// Page-table entries of one split staged in LDS: a split of T tokens touches
+// at most T/page_size + 2 pages.
+constexpr int kMaxSplitPages = 2080;
 
 struct DecodeParams {
     const void* q;            // bf16 [B, Hq, D], row stride q_stride_b
@@ -23,7 +38,9 @@ struct DecodeParams {
     const int32_t* block_table;
     int64_t bt_stride;
     const int32_t* seq_lens;
+    int32_t num_seqs;
     int32_t num_q_heads;
+    int32_t num_kv_heads;
     int32_t group;            // G = Hq / Hkv (1..16)
     int32_t page_shift;       // log2(page_size)
     int32_t window;           // <= 0: off
