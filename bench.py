@@ -90,6 +90,22 @@ def copy_probe(torch):
     print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
 
 
+def time_steps(torch, step, K):
+    """K back-to-back steps: wall-clock ms per step, and HIP-event ms per
+    step on the stream the kernels are launched on (torch's current stream,
+    which the binding passes to the library)."""
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record()
+    for i in range(K):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    return wall * 1e3 / K, e0.elapsed_time(e1) / K
+
+
 def bench_decode(args, torch, pa, I):
     dev = "cuda:0"
     case = I.decode_config(args.workload, page_size=args.page_size)
@@ -100,37 +116,21 @@ def bench_decode(args, torch, pa, I):
     plan = pa.decode_plan(t0["q"], t0["k_pool"], t0["block_table"], case.max_kv_len,
                           window=case.window, num_splits=args.splits)
     out = torch.empty_like(t0["q"])
-    ws = (torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
-          if plan.workspace_bytes else None)
+    ws = pa.workspace_for(plan, dev)
 
-    def stage(i, which):
+    def step(i):
         t = tensors[i % copies]
         pa.decode(plan, t["q"], t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
                   case.scale, softcap=case.softcap, window=case.window,
-                  k_scale=case.k_scale, v_scale=case.v_scale, out=out, workspace=ws,
-                  stage=which)
+                  k_scale=case.k_scale, v_scale=case.v_scale, out=out, workspace=ws)
 
     for i in range(args.warmup):
-        stage(i, "partial")
-        stage(i, "merge")
-    torch.cuda.synchronize()
+        step(i)
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    w0 = time.perf_counter()
-    for i in range(K):
-        ev[i][0].record()
-        stage(i, "partial")
-        ev[i][1].record()
-        stage(i, "merge")
-        ev[i][2].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    part_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
-    merge_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
-    call_ms = sum(e[0].elapsed_time(e[2]) for e in ev) / K
-    ms_step = wall * 1e3 / K
-    achieved = alg / (part_ms * 1e-3) / 1e9
-    traffic = traffic_for("decode_partial", case.name, ["decode.hip", "pa_device.h"])
+    ms_step, ev_ms = time_steps(torch, step, K)
+    # one kernel per step: the event time per step is its launch duration
+    achieved = alg / (ev_ms * 1e-3) / 1e9
+    traffic = traffic_for("decode_split", case.name, ["decode.hip", "pa_device.h"])
     res = {
         "metric": "paged-attn decode KV GB/s (fraction of HBM peak) + us/call on 1 MI355X",
         "value": alg / (ms_step * 1e-3) / 1e9,
@@ -146,12 +146,11 @@ def bench_decode(args, torch, pa, I):
                    "kv_dtype": case.kv_dtype, "window": case.window,
                    "softcap": case.softcap, "total_tokens": int(case.seq_lens.sum()),
                    "seed": args.workload, "input_copies": copies},
-        "us_per_call": call_ms * 1e3,
+        "us_per_call": ev_ms * 1e3,
         "hbm_frac": (alg / (ms_step * 1e-3) / 1e9) / HBM_PEAK_GBS,
         "algorithmic_bytes": alg, "kv_bytes": case.kv_bytes(),
-        "kernel_us": {"decode_partial": part_ms * 1e3, "decode_merge": merge_ms * 1e3},
         "plan": plan.describe(),
-        "roofline": {"bound": "hbm", "kernel": "decode_partial", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": "decode_split", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic},
     }
@@ -182,18 +181,8 @@ def bench_extend(args, torch, pa, I):
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
-    w0 = time.perf_counter()
-    for i in range(K):
-        ev[i][0].record()
-        step()
-        ev[i][1].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    k_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
-    ms_step = wall * 1e3 / K
+    ms_step, k_ms = time_steps(torch, lambda i: step(), K)
     achieved = flops / (k_ms * 1e-3) / 1e12
     res = {
         "metric": "paged-attn extend TFLOP/s (fraction of MFMA bf16 peak) on 1 MI355X",

@@ -96,8 +96,8 @@ typedef struct {
                                    extend: ctx_lens) */
     int32_t total_q;           /* extend: rows of q/k_new/v_new/out */
     int32_t max_q_len;         /* extend: bound on new tokens per sequence */
-    int32_t num_splits;        /* decode: 0 = plan chooses; > 0 caps the KV
-                                  splits per sequence at this number */
+    int32_t num_splits;        /* decode: 0 = plan chooses; > 0 forces the
+                                  number of split-pass pieces (waves) */
 } pa_problem;
 
 /* The plan: a plain value the caller owns (nothing to free).  Planning reads
@@ -105,9 +105,9 @@ typedef struct {
  * fixed capacities the same way). */
 typedef struct {
     pa_problem prob;
-    int32_t num_splits;        /* decode: KV splits per sequence (grid x) */
-    int32_t tokens_per_split;  /* decode: tokens per split, a multiple of 32 */
-    int32_t waves_per_block;   /* decode: waves sharing one split */
+    int32_t num_splits;        /* decode: split-pass pieces = persistent waves */
+    int32_t tokens_per_split;  /* decode: tile granularity of the pieces (32) */
+    int32_t waves_per_block;   /* decode: waves per block (1) */
     int32_t num_cus;           /* compute units the plan was made for */
     uint64_t workspace_bytes;  /* device scratch the compute call needs */
     int32_t reserved[8];
@@ -116,12 +116,13 @@ typedef struct {
 /*
  * paged_attn_plan -- choose the split-KV decomposition and size the workspace.
  *
- * Decode: every sequence's key range [lo, L) (lo = max(0, L-W) with a window)
- * is cut into splits of `tokens_per_split` tokens; each (sequence, kv head,
- * split) is one work item, and a merge combines the splits by log-sum-exp
- * (the split partition and merge of `_fwd_kernel_stage1/2`).  The plan picks
- * the split size from the batch, heads, max_kv_len and the device's compute
- * unit count; prob->num_splits > 0 caps the splits per sequence.
+ * Decode: the 32-token tiles of every (sequence, kv head) key range [lo, L)
+ * (lo = max(0, L-W) with a window), laid end to end, are cut into
+ * out->num_splits equal contiguous pieces, one per persistent wave of the
+ * split pass; the plan takes as many as the device keeps resident (compute
+ * units x resident waves per unit), or prob->num_splits when that is > 0.
+ * Pieces of one key range are merged by log-sum-exp (the split partition
+ * and merge of `_fwd_kernel_stage1/2`; any partition gives the same result).
  * Extend: validates the shape; no workspace is needed.
  *
  * hip_device >= 0 queries that device's compute-unit count; hip_device < 0
@@ -144,7 +145,14 @@ pa_status paged_attn_plan(const pa_problem* prob, int hip_device, pa_plan* out);
  *   softcap       c > 0 enables c*tanh(s/c)
  *   k_scale,v_scale  fp8 descales (1.0 for bf16)
  *   out           bf16 [B, Hq, D], sequence stride out_stride_b
- *   workspace     >= plan->workspace_bytes of device memory (split partials)
+ *   workspace     >= plan->workspace_bytes of device memory (split partials);
+ *                 calls that share a workspace must not overlap
+ *
+ * Two kernels run: the key ranges of all (sequence, kv head) pairs, laid end
+ * to end, are cut into plan->num_splits equal pieces, one per persistent
+ * wave of the split pass; a second kernel merges by log-sum-exp every pair
+ * that spans several pieces (the split/merge of `_fwd_grouped_kernel_stage1`
+ * / `_fwd_kernel_stage2`).
  */
 pa_status paged_attn_decode(const pa_plan* plan,
                             const void* q, int64_t q_stride_b,
@@ -158,40 +166,6 @@ pa_status paged_attn_decode(const pa_plan* plan,
                             void* out, int64_t out_stride_b,
                             void* workspace, uint64_t workspace_bytes,
                             void* hip_stream);
-
-/*
- * paged_attn_decode_partial / paged_attn_decode_merge -- the two stages that
- * paged_attn_decode enqueues, callable one at a time with the same arguments
- * (the stage-1 partial pass and the stage-2 merge of `decode_attention_fwd`).
- * The partial stage writes `out` for sequences whose key range fits one split
- * and the workspace partials for the others; the merge stage completes `out`
- * from the workspace (it launches nothing when the plan has one split).
- * Calling partial then merge on one stream equals one paged_attn_decode.
- */
-pa_status paged_attn_decode_partial(const pa_plan* plan,
-                                    const void* q, int64_t q_stride_b,
-                                    const void* k_pool, const void* v_pool,
-                                    int64_t kv_stride_page, int64_t kv_stride_tok,
-                                    int64_t kv_stride_head, int64_t num_pages,
-                                    const int32_t* block_table, int64_t bt_stride,
-                                    const int32_t* seq_lens,
-                                    int32_t page_size, float scale, float softcap,
-                                    int32_t window, float k_scale, float v_scale,
-                                    void* out, int64_t out_stride_b,
-                                    void* workspace, uint64_t workspace_bytes,
-                                    void* hip_stream);
-pa_status paged_attn_decode_merge(const pa_plan* plan,
-                                  const void* q, int64_t q_stride_b,
-                                  const void* k_pool, const void* v_pool,
-                                  int64_t kv_stride_page, int64_t kv_stride_tok,
-                                  int64_t kv_stride_head, int64_t num_pages,
-                                  const int32_t* block_table, int64_t bt_stride,
-                                  const int32_t* seq_lens,
-                                  int32_t page_size, float scale, float softcap,
-                                  int32_t window, float k_scale, float v_scale,
-                                  void* out, int64_t out_stride_b,
-                                  void* workspace, uint64_t workspace_bytes,
-                                  void* hip_stream);
 
 /*
  * paged_attn_extend -- prefix-prefill of new tokens on top of a paged context.

@@ -6,7 +6,8 @@ Python binding plus the seeded synthetic inputs used by tests and the bench.
 """
 from .binding import (PA_MODE_DECODE, PA_MODE_EXTEND, PagedAttnError, Plan,  # noqa: F401
                       decode, decode_plan, extend, extend_plan, gather, lib, plan,
-                      status_str)
+                      status_str, workspace_for)
 
 __all__ = ["PA_MODE_DECODE", "PA_MODE_EXTEND", "PagedAttnError", "Plan", "decode",
-           "decode_plan", "extend", "extend_plan", "gather", "lib", "plan", "status_str"]
+           "decode_plan", "extend", "extend_plan", "gather", "lib", "plan", "status_str",
+           "workspace_for"]

@@ -58,10 +58,9 @@ def lib():
     PP = ctypes.POINTER(PaPlan)
     L.paged_attn_plan.argtypes = [ctypes.POINTER(PaProblem), ctypes.c_int, PP]
     L.paged_attn_plan.restype = ctypes.c_int
-    for fn in ("paged_attn_decode", "paged_attn_decode_partial", "paged_attn_decode_merge"):
-        getattr(L, fn).argtypes = [PP, p, i64, p, p, i64, i64, i64, i64, p, i64, p,
-                                   i32, f32, f32, i32, f32, f32, p, i64, p, u64, p]
-        getattr(L, fn).restype = ctypes.c_int
+    L.paged_attn_decode.argtypes = [PP, p, i64, p, p, i64, i64, i64, i64, p, i64, p,
+                                    i32, f32, f32, i32, f32, f32, p, i64, p, u64, p]
+    L.paged_attn_decode.restype = ctypes.c_int
     L.paged_attn_extend.argtypes = [PP, p, p, p, p, p, p, p, i64, i64, i64, i64, p, i64,
                                     i32, f32, f32, i32, f32, f32, p, p, u64, p]
     L.paged_attn_extend.restype = ctypes.c_int
@@ -161,12 +160,17 @@ def _pool_strides(k_pool: torch.Tensor, v_pool: torch.Tensor):
     return k_pool.stride(0), k_pool.stride(1), k_pool.stride(2)
 
 
-def _workspace(pl: Plan, workspace, device):
+def workspace_for(pl: Plan, device) -> Optional[torch.Tensor]:
+    """Device scratch of plan.workspace_bytes bytes (None when none is needed)."""
     if pl.workspace_bytes == 0:
+        return None
+    return torch.empty(pl.workspace_bytes, dtype=torch.uint8, device=device)
+
+
+def _workspace(pl: Plan, workspace, device):
+    if pl.workspace_bytes == 0 or workspace is not None:
         return workspace
-    if workspace is None:
-        workspace = torch.empty(pl.workspace_bytes, dtype=torch.uint8, device=device)
-    return workspace
+    return workspace_for(pl, device)
 
 
 def decode_plan(q: torch.Tensor, k_pool: torch.Tensor, block_table: torch.Tensor,
@@ -182,12 +186,10 @@ def decode(pl: Plan, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor
            block_table: torch.Tensor, seq_lens: torch.Tensor, scale: float,
            softcap: float = 0.0, window: int = 0, k_scale: float = 1.0,
            v_scale: float = 1.0, out: Optional[torch.Tensor] = None,
-           workspace: Optional[torch.Tensor] = None, stream=None,
-           stage: str = "all") -> torch.Tensor:
+           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """paged_attn_decode: q bf16 [B, Hq, D] -> out bf16 [B, Hq, D].
-    stage="partial" / "merge" calls paged_attn_decode_partial / _merge."""
-    fn = {"all": "paged_attn_decode", "partial": "paged_attn_decode_partial",
-          "merge": "paged_attn_decode_merge"}[stage]
+    A workspace passed in needs plan.workspace_bytes bytes."""
+    fn = "paged_attn_decode"
     if q.dtype != torch.bfloat16 or q.dim() != 3 or q.stride(2) != 1 or q.stride(1) != q.shape[2]:
         raise ValueError("q must be bf16 [B, Hq, D] with contiguous heads")
     if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:

@@ -21,8 +21,8 @@ namespace {
 
 using namespace pa;
 
-constexpr int kDefaultCus = 256;  // MI355X
-constexpr int kMinSplitTokens = 512;
+constexpr int kDefaultCus = 256;        // MI355X
+constexpr int kDefaultWavesPerCu = 8;   // split-pass occupancy when no device is queried
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 int ilog2(int x) {
@@ -52,14 +52,6 @@ pa_status check_problem(const pa_problem& pr) {
         if (pr.num_seqs > 0 && pr.total_q > 0 && pr.max_q_len == 0) return PA_ERR_INVALID_SHAPE;
     }
     return PA_OK;
-}
-
-// Tokens of a sequence's key range that one split may have to cover, rounded
-// out to whole 32-token tiles: the range starts at lo rounded down to 32.
-int64_t key_span(const pa_problem& pr) {
-    int64_t span = pr.max_kv_len;
-    if (pr.window > 0) span = std::min<int64_t>(span, (int64_t)pr.window + kTile - 1);
-    return span;
 }
 
 int elem_bytes(int kv_dtype) { return kv_dtype == PA_KV_FP8_E4M3 ? 1 : 2; }
@@ -129,39 +121,38 @@ pa_status paged_attn_plan(const pa_problem* prob, int hip_device, pa_plan* out) 
     memset(&pl, 0, sizeof pl);
     pl.prob = pr;
     pl.num_cus = cus;
-    pl.waves_per_block = kDecodeWaves;
+    pl.waves_per_block = 1;
     pl.num_splits = 1;
     pl.tokens_per_split = kTile;
 
     if (pr.mode == PA_MODE_DECODE) {
-        const int64_t span = key_span(pr);
-        const int64_t units = (int64_t)pr.num_seqs * pr.num_kv_heads;
-        int64_t T;
+        // Split pass: persistent waves, each owning an equal contiguous range
+        // of the tiles of all segments.  By default as many as the device
+        // keeps resident; prob.num_splits > 0 forces the count.
+        int64_t workers;
         if (pr.num_splits > 0) {
-            T = round_up(std::max<int64_t>(cdiv(span, pr.num_splits), 1), kTile);
+            workers = pr.num_splits;
         } else {
-            // Aim for ~8 work items per compute unit, assuming sequences
-            // average half the bound; never split finer than kMinSplitTokens.
-            const int64_t target = 8LL * cus;
-            T = round_up(std::max<int64_t>(cdiv(units * span, 2 * target), 1), kTile);
-            T = std::max<int64_t>(T, kMinSplitTokens);
+            int per_cu = kDefaultWavesPerCu;
+            if (hip_device >= 0) {
+                int cur = -1;
+                if (hipGetDevice(&cur) != hipSuccess) return PA_ERR_HIP;
+                if (cur != hip_device && hipSetDevice(hip_device) != hipSuccess) return PA_ERR_HIP;
+                const hipError_t e = decode_waves_per_cu(pr.head_dim, pr.kv_dtype == PA_KV_FP8_E4M3,
+                                                         pr.page_size >= 16, &per_cu);
+                if (cur != hip_device) (void)hipSetDevice(cur);
+                if (e != hipSuccess || per_cu < 1) return PA_ERR_HIP;
+            }
+            workers = (int64_t)cus * per_cu;
         }
-        if (span > 0 && cdiv(span, T) > kMaxSplits) T = round_up(cdiv(span, kMaxSplits), kTile);
-        // A split's page list is staged in LDS: at most T/P + 2 entries.
-        const int64_t t_max = ((int64_t)(kMaxSplitPages - 2) * pr.page_size) / kTile * kTile;
-        T = std::min<int64_t>(T, t_max);
-        if (span > 0 && cdiv(span, T) > kMaxSplits) return PA_ERR_UNSUPPORTED;
-        if ((int64_t)cdiv(std::max<int64_t>(span, 1), T) * pr.num_seqs * pr.num_kv_heads >
-            (int64_t)INT32_MAX)
-            return PA_ERR_UNSUPPORTED;
-        const int64_t S = span > 0 ? cdiv(span, T) : 1;
-        pl.tokens_per_split = (int32_t)T;
-        pl.num_splits = (int32_t)S;
-        if (S > 1) {
-            const int64_t rows = (int64_t)pr.num_seqs * pr.num_q_heads * S;
-            pl.workspace_bytes = (uint64_t)(round_up(rows * pr.head_dim * 4, 256) +
-                                            round_up(rows * 4, 256));
-        }
+        if (workers > kMaxWorkers) return PA_ERR_UNSUPPORTED;
+        pl.num_splits = (int32_t)workers;
+        pl.tokens_per_split = kTile;
+        pl.waves_per_block = 1;
+        const int64_t G = pr.num_q_heads / pr.num_kv_heads;
+        const int64_t rows = workers * 2 * G;
+        pl.workspace_bytes = (uint64_t)(round_up(rows * pr.head_dim * 4, 256) +
+                                        round_up(rows * 4, 256));
     }
     *out = pl;
     return PA_OK;
@@ -192,9 +183,7 @@ int paged_attn_plan_describe(const pa_plan* pl, char* buf, int buf_len) {
 
 namespace {
 
-enum { kStagePartial = 1, kStageMerge = 2 };
-
-pa_status decode_impl(int stages, const pa_plan* plan, const void* q, int64_t q_stride_b,
+pa_status decode_impl(const pa_plan* plan, const void* q, int64_t q_stride_b,
                       const void* k_pool, const void* v_pool, int64_t kv_stride_page,
                       int64_t kv_stride_tok, int64_t kv_stride_head, int64_t num_pages,
                       const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
@@ -208,9 +197,7 @@ pa_status decode_impl(int stages, const pa_plan* plan, const void* q, int64_t q_
     if (st != PA_OK) return st;
     if (pr.mode != PA_MODE_DECODE) return PA_ERR_PLAN_MISMATCH;
     if (page_size != pr.page_size || window != pr.window) return PA_ERR_PLAN_MISMATCH;
-    if (pl.tokens_per_split <= 0 || pl.tokens_per_split % kTile || pl.num_splits < 1 ||
-        pl.num_splits > kMaxSplits ||
-        (int64_t)pl.num_splits * pl.tokens_per_split < key_span(pr))
+    if (pl.tokens_per_split != kTile || pl.num_splits < 1 || pl.num_splits > kMaxWorkers)
         return PA_ERR_PLAN_MISMATCH;
     if (pr.num_seqs == 0) return PA_OK;
     if (!q || !seq_lens || !out) return PA_ERR_NULL_POINTER;
@@ -223,7 +210,7 @@ pa_status decode_impl(int stages, const pa_plan* plan, const void* q, int64_t q_
         return PA_ERR_MISALIGNED;
     if (!isfinite(scale) || !isfinite(softcap) || !isfinite(k_scale) || !isfinite(v_scale))
         return PA_ERR_INVALID_SHAPE;
-    uint64_t need = pl.num_splits > 1 ? pl.workspace_bytes : 0;
+    const uint64_t need = pl.workspace_bytes;
     if (need > 0) {
         if (workspace_bytes < need) return PA_ERR_WORKSPACE_TOO_SMALL;
         if (!workspace) return PA_ERR_NULL_POINTER;
@@ -248,8 +235,6 @@ pa_status decode_impl(int stages, const pa_plan* plan, const void* q, int64_t q_
     p.group = pr.num_q_heads / pr.num_kv_heads;
     p.page_shift = ilog2(pr.page_size);
     p.window = pr.window;
-    p.tokens_per_split = pl.tokens_per_split;
-    p.num_splits = pl.num_splits;
     const float kl2e = 1.4426950408889634f;
     p.has_cap = softcap > 0.f;
     p.qk_scale2 = scale * k_scale * kl2e;
@@ -260,20 +245,19 @@ pa_status decode_impl(int stages, const pa_plan* plan, const void* q, int64_t q_
     p.v_scale = v_scale;
     p.out = out;
     p.out_stride_b = out_stride_b;
-    if (pl.num_splits > 1) {
-        const int64_t rows = (int64_t)pr.num_seqs * pr.num_q_heads * pl.num_splits;
-        p.part_o = static_cast<float*>(workspace);
-        p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                              round_up(rows * pr.head_dim * 4, 256));
+    {
+        const int64_t rows = (int64_t)pl.num_splits * 2 * p.group;
+        char* ws = static_cast<char*>(workspace);
+        p.part_o = reinterpret_cast<float*>(ws);
+        p.part_lse = reinterpret_cast<float*>(ws + round_up(rows * pr.head_dim * 4, 256));
     }
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     const bool uniform = pr.page_size >= 16;
-    if ((stages & kStagePartial) &&
-        launch_decode(p, pr.head_dim, pr.kv_dtype == PA_KV_FP8_E4M3, uniform, pr.num_seqs,
-                      pr.num_kv_heads, stream) != hipSuccess)
+    if (launch_decode(p, pr.head_dim, pr.kv_dtype == PA_KV_FP8_E4M3, uniform, pl.num_splits,
+                      stream) != hipSuccess)
         return PA_ERR_HIP;
-    if ((stages & kStageMerge) && pl.num_splits > 1 &&
-        launch_decode_merge(p, pr.head_dim, pr.num_seqs, pr.num_kv_heads, stream) != hipSuccess)
+    if (launch_decode_merge(p, pr.head_dim, pl.num_splits, pr.num_seqs, pr.num_kv_heads,
+                            stream) != hipSuccess)
         return PA_ERR_HIP;
     return PA_OK;
 }
@@ -295,15 +279,7 @@ extern "C" {
         int64_t out_stride_b, void *workspace, uint64_t workspace_bytes, void *hip_stream
 
 pa_status paged_attn_decode(PA_DECODE_PARAMS) {
-    return decode_impl(kStagePartial | kStageMerge, PA_DECODE_ARGS);
-}
-
-pa_status paged_attn_decode_partial(PA_DECODE_PARAMS) {
-    return decode_impl(kStagePartial, PA_DECODE_ARGS);
-}
-
-pa_status paged_attn_decode_merge(PA_DECODE_PARAMS) {
-    return decode_impl(kStageMerge, PA_DECODE_ARGS);
+    return decode_impl(PA_DECODE_ARGS);
 }
 
 pa_status paged_attn_gather(const pa_plan* plan, const void* k_pool, const void* v_pool,

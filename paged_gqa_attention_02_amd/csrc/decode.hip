@@ -1,22 +1,36 @@
 // decode.hip -- split-KV paged GQA decode for gfx950.
 //
-// One work item is (sequence b, kv head g, split s): the tokens
-// [base + s*T, base + (s+1)*T) of the key range [lo, L), where lo = L - W
-// under a sliding window, base = lo rounded down to 32 and T the plan's
-// tokens_per_split.  This is the split-KV scheme of `_fwd_grouped_kernel_stage1`
-// (partial softmax-weighted sum plus its log-sum-exp per split) and
-// `_fwd_kernel_stage2` (merge of the splits) on the page
-// "vllm/attention/ops/triton_decode_attention.py"; the splits here have a
-// fixed token count instead of an equal share of each sequence, so long and
-// short sequences produce equally sized work items.
+// The computation is the split-KV scheme of `_fwd_grouped_kernel_stage1`
+// (partial softmax-weighted sums with their log-sum-exp over contiguous
+// pieces of a sequence's key range) and `_fwd_kernel_stage2` (merge of the
+// pieces) on the page "vllm/attention/ops/triton_decode_attention.py".  Any
+// contiguous partition of the key range gives the same result, so the
+// partition here is chosen for the machine (stream-K):
 //
-// A work item is one block of kDecodeWaves waves; wave w takes the 32-token
-// tiles w, w + kDecodeWaves, ... of the split and the waves combine through
-// LDS at the end.  Per tile one wave computes, for all G query heads of the
-// kv head at once (every K/V byte is read once for the whole group):
-//   S^T[32 x 16] = K[32 x D] * Q^T[D x 16]       (v_mfma_f32_16x16x32_bf16,
-//                                                 K rows read from HBM straight
-//                                                 into the A operand)
+//   * a segment is one (sequence b, kv head g): the 32-token tiles covering
+//     the key range [lo, L) (lo = L - W under a sliding window, tiles start at
+//     lo rounded down to 32);
+//   * all segments are laid end to end (sequence-major, kv head minor) and
+//     the resulting list of N tiles is cut into W equal contiguous ranges, W
+//     = the persistent waves the chip holds; wave w owns tiles
+//     [floor(w*N/W), floor((w+1)*N/W));
+//   * a wave walks its range; a segment it covers completely is normalised
+//     and written to the output directly, the (at most two) segments it
+//     covers in part leave a partial (normalised sum + log2-sum-exp) in the
+//     wave's two workspace slots;
+//   * a second kernel merges the partials of every segment that spans
+//     several waves (the merge of `_fwd_kernel_stage2`) and writes zero rows
+//     for sequences with no keys.
+//
+// Every wave gets the same number of tiles whatever the length mix, and no
+// wave waits for another.
+//
+// Per tile one wave computes, for all G query heads of the kv head at once
+// (every K/V byte is read once for the whole group):
+//   S^T[32 x 16] = K[32 x D] * Q^T[D x 16]       (v_mfma_f32_16x16x32_bf16;
+//                                                 K rows are loaded whole and
+//                                                 re-read from a per-wave LDS
+//                                                 tile in the A layout)
 //   online softmax in the log2 domain (scores of one head live in the 4 lanes
 //   of one MFMA column; max by two cross-lane exchanges)
 //   O[16 x D] += P[16 x 32] * V[32 x D]          (P is the S^T accumulator
@@ -27,7 +41,9 @@
 // Rows of Q^T beyond G are zero; their results are never stored.
 //
 // Memory: every lane load is 16 bytes (8 bytes for fp8 V / D=64 bf16 V) of a
-// K or V row; one wave load instruction for V covers four whole rows.
+// K or V row, nontemporal; one wave load instruction covers whole rows (4 of
+// K or V for bf16 D=128).  A wave keeps the next tile's K and V in flight
+// while it computes the current one.
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -107,6 +123,8 @@ struct TileCtx {
     int64_t page_bytes;        // s_page * elem
     int tok_bytes;             // s_tok * elem
     int k_lane;                // kvh*s_head*elem + 16*grp (+ c*tok_bytes when UNIFORM)
+    int k_row;                 // whole-row K loads: the lane's row within a load
+    int k_row_lane;            // kvh*s_head*elem + 16*column (+ k_row*tok_bytes when UNIFORM)
     int v_lane[4];             // kvh*s_head*elem + VBYTES*c (+ (4*grp + r)*tok_bytes when UNIFORM)
 };
 
@@ -152,11 +170,85 @@ __device__ __forceinline__ void issue_k(KRegs<D, FP8>& R, const DecodeParams& p,
             ptr = pool + page_of<false>(x, p.page_shift, t) * x.page_bytes +
                   (int64_t)((t & pmask) * x.tok_bytes + x.k_lane);
         }
-#pragma unroll
         // (plain loads: each 128-byte line of a row is read by two
         // consecutive instructions, and the second must find it cached)
+#pragma unroll
         for (int i = 0; i < KRegs<D, FP8>::N; ++i)
             R.w[h][i] = *reinterpret_cast<const u32x4*>(ptr + 64 * i);
+    }
+}
+
+// K rows of a tile loaded whole (every wave load instruction reads complete
+// rows, rows_per_load of them), to be transposed through LDS into the S^T A
+// operands.  Row `rows_per_load*i + lane/lanes_per_row` of the tile, 16 bytes
+// at 16*(lane % lanes_per_row).
+template <int D, bool FP8>
+struct KRowRegs {
+    static constexpr int kRowBytes = D * (FP8 ? 1 : 2);
+    static constexpr int kLanesPerRow = kRowBytes / 16;
+    static constexpr int kRowsPerLoad = 64 / kLanesPerRow;
+    static constexpr int N = kTile / kRowsPerLoad;          // loads per tile
+    static constexpr int kLdsStride = kRowBytes + 16;       // padded LDS row
+    u32x4 w[N];
+};
+
+template <int D, bool FP8, bool UNIFORM>
+__device__ __forceinline__ void issue_k_rows(KRowRegs<D, FP8>& R, const DecodeParams& p,
+                                             const TileCtx& x, int t0) {
+    using KR = KRowRegs<D, FP8>;
+    const uint8_t* pool = static_cast<const uint8_t*>(p.k_pool);
+    const int pmask = (1 << p.page_shift) - 1;
+#pragma unroll
+    for (int i = 0; i < KR::N; ++i) {
+        const int row0 = KR::kRowsPerLoad * i;              // first row of this load
+        const uint8_t* ptr;
+        if constexpr (UNIFORM) {
+            const int th = t0 + (row0 & 16);               // the half holding the rows
+            ptr = pool + page_of<true>(x, p.page_shift, th) * x.page_bytes +
+                  (int64_t)(((th & pmask) + (row0 & 15)) * x.tok_bytes) + x.k_row_lane;
+        } else {
+            const int t = t0 + row0 + x.k_row;
+            ptr = pool + page_of<false>(x, p.page_shift, t) * x.page_bytes +
+                  (int64_t)((t & pmask) * x.tok_bytes + x.k_row_lane);
+        }
+        R.w[i] = load_stream<u32x4>(ptr);
+    }
+}
+
+// Registers -> LDS tile [32 rows][kLdsStride bytes].
+template <int D, bool FP8>
+__device__ __forceinline__ void stage_k(const KRowRegs<D, FP8>& R, uint8_t* lds, int lane) {
+    using KR = KRowRegs<D, FP8>;
+    const int row = lane / KR::kLanesPerRow, col = lane % KR::kLanesPerRow;
+#pragma unroll
+    for (int i = 0; i < KR::N; ++i)
+        *reinterpret_cast<u32x4*>(lds + (KR::kRowsPerLoad * i + row) * KR::kLdsStride + 16 * col) =
+            R.w[i];
+}
+
+// S^T = K Q^T with the K rows read back from the LDS tile in the A layout
+// (row 16h + c, the lane's slice as in issue_k).
+template <int D, bool FP8>
+__device__ __forceinline__ void tile_scores_lds(f32x4 s[2], const uint8_t* lds,
+                                                const u32x4* qop, int c, int grp) {
+    using KR = KRowRegs<D, FP8>;
+    constexpr int NL = FP8 ? D / 64 : D / 32;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        s[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const uint8_t* rowp = lds + (16 * h + c) * KR::kLdsStride + 16 * grp;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const u32x4 w = *reinterpret_cast<const u32x4*>(rowp + 64 * i);
+            if constexpr (FP8) {
+                const u32x2 a = e4m3x4_to_bf16x4(w.x), bb = e4m3x4_to_bf16x4(w.y);
+                const u32x2 cc = e4m3x4_to_bf16x4(w.z), dd = e4m3x4_to_bf16x4(w.w);
+                s[h] = mfma_bf16_16x16x32(u32x4{a.x, a.y, bb.x, bb.y}, qop[2 * i], s[h]);
+                s[h] = mfma_bf16_16x16x32(u32x4{cc.x, cc.y, dd.x, dd.y}, qop[2 * i + 1], s[h]);
+            } else {
+                s[h] = mfma_bf16_16x16x32(w, qop[i], s[h]);
+            }
+        }
     }
 }
 
@@ -311,161 +403,289 @@ __device__ __forceinline__ void tile_pv(Acc<D>& A, VRegs<D, FP8>& R, u32x4 pop,
     }
 }
 
-template <int D, bool FP8, bool UNIFORM, bool CAP, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kDecodeOccupancy)))
-void decode_partial_kernel(DecodeParams p) {
+// ---------------------------------------------------------------------------
+// Segment geometry (shared by the split pass and the merge)
+// ---------------------------------------------------------------------------
+struct SeqRange {
+    int L, lo, base, tiles;   // tiles: 32-token tiles from base covering [lo, L)
+};
+
+__device__ __forceinline__ SeqRange seq_range(const DecodeParams& p, int b) {
+    SeqRange r;
+    r.L = p.seq_lens[b];
+    r.lo = (p.window > 0 && r.L > p.window) ? r.L - p.window : 0;
+    r.base = r.lo & ~(kTile - 1);
+    r.tiles = r.L > r.lo ? (r.L - r.base + kTile - 1) / kTile : 0;
+    return r;
+}
+
+__device__ __forceinline__ int64_t wave_sum64(int64_t v) {
+#pragma unroll
+    for (int k = 32; k >= 1; k >>= 1) v += __shfl_xor(v, k, 64);
+    return v;
+}
+
+// Total tiles N over all segments (every lane gets the sum).
+__device__ __forceinline__ int64_t total_tiles(const DecodeParams& p) {
+    const int lane = __lane_id();
+    int64_t n = 0;
+    for (int b0 = 0; b0 < p.num_seqs; b0 += 64) {
+        const int b = b0 + lane;
+        n += b < p.num_seqs ? (int64_t)seq_range(p, b).tiles : 0;
+    }
+    return wave_sum64(n) * p.num_kv_heads;
+}
+
+// Sequence whose segments contain global tile `pos` (< N), and the global
+// index of its first tile.  Sequences without tiles are skipped.
+__device__ __forceinline__ void find_seq(const DecodeParams& p, int64_t pos, int& b_out,
+                                         int64_t& start_out) {
+    const int lane = __lane_id();
+    int64_t carry = 0;
+    for (int b0 = 0; b0 < p.num_seqs; b0 += 64) {
+        const int b = b0 + lane;
+        int64_t n = b < p.num_seqs ? (int64_t)seq_range(p, b).tiles * p.num_kv_heads : 0;
+        // inclusive scan across the wave
+        int64_t incl = n;
+#pragma unroll
+        for (int k = 1; k < 64; k <<= 1) {
+            const int64_t t = __shfl_up(incl, k, 64);
+            if (lane >= k) incl += t;
+        }
+        const int64_t total = __shfl(incl, 63, 64);
+        if (carry + total > pos) {
+            const uint64_t hit = __ballot(carry + incl > pos);
+            const int j = __builtin_ctzll(hit);
+            b_out = b0 + j;
+            start_out = carry + __shfl(incl - n, j, 64);
+            return;
+        }
+        carry += total;
+    }
+    b_out = p.num_seqs;
+    start_out = carry;
+}
+
+// First tile of wave w's range.
+__device__ __forceinline__ int64_t range_start(int64_t w, int64_t N, int64_t W) {
+    return w * N / W;
+}
+
+// Partial slots of wave w: slot 0 holds its first segment when incomplete,
+// slot 1 its last one when incomplete (a middle segment is always complete).
+__device__ __forceinline__ int64_t part_row(const DecodeParams& p, int64_t w, int slot) {
+    return (w * 2 + slot) * p.group;
+}
+
+// Wave holding global tile t: the largest w with floor(w*N/W) <= t.
+__device__ __forceinline__ int64_t tile_owner(int64_t t, int64_t N, int64_t W) {
+    return ((t + 1) * W + N - 1) / N - 1;
+}
+
+// Partial row of wave wv's piece of the segment starting at global tile
+// seg0 (slot 0 when the wave's range starts inside the segment, else slot 1),
+// or -1 when the wave's range is empty (possible when N < W).
+__device__ __forceinline__ int piece_row(const DecodeParams& p, int64_t wv, int64_t seg0,
+                                         int64_t N, int64_t W) {
+    const int64_t a = range_start(wv, N, W);
+    if (a == range_start(wv + 1, N, W)) return -1;
+    return (int)part_row(p, wv, a >= seg0 ? 0 : 1);
+}
+
+// ---------------------------------------------------------------------------
+// Split pass: persistent waves, one contiguous range of tiles each
+// ---------------------------------------------------------------------------
+template <int D, bool FP8, bool UNIFORM, bool CAP>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kDecodeOccupancy)))
+void decode_split_kernel(DecodeParams p) {
     constexpr int KK = D / 32;                  // QK MFMAs per 16-token half
     constexpr int VE = D / 16;                  // PV MFMAs per tile
+    constexpr int SUB = kDecodeSub;
 
-    const int lane = threadIdx.x & 63;
-    const int wave = NW == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x;
     const int c = lane & 15;
     const int grp = lane >> 4;
-    // Work items are numbered kv-head fastest, then sequence, then split:
-    // blocks are dealt to the 8 XCDs by block id modulo 8, so this keeps the
-    // split index (whose upper values exist only for long sequences) out of
-    // the XCD choice and gives every XCD an even share of the work.
-    const int kvh = blockIdx.x % p.num_kv_heads;
-    const int b = (blockIdx.x / p.num_kv_heads) % p.num_seqs;
-    const int split = blockIdx.x / (p.num_kv_heads * p.num_seqs);
     const int G = p.group;
-
-    const int L = p.seq_lens[b];
-    const int lo = (p.window > 0 && L > p.window) ? L - p.window : 0;
-    const int base = lo & ~(kTile - 1);
-    const int T = p.tokens_per_split;
-    // (min with the grid: lengths beyond the planned bound cannot index past
-    // the partials)
-    const int n_splits = L > lo ? min((L - base + T - 1) / T, p.num_splits) : 0;
+    const int64_t W = gridDim.x;
+    const int64_t w = blockIdx.x;
 
     __shared__ int sm_pages[kMaxSplitPages];
+#if PA_DECODE_KLDS
+    __shared__ __attribute__((aligned(16))) uint8_t sm_k[kTile * KRowRegs<D, FP8>::kLdsStride];
+#endif
 
-    if (split >= n_splits) {
-        if (split == 0) {   // nothing to attend: zero rows
-            for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
-                const int r = idx / D, d = idx % D;
-                uint16_t* o = static_cast<uint16_t*>(p.out) + (int64_t)b * p.out_stride_b +
-                              (int64_t)(kvh * G + r) * D + d;
-                *o = 0;
+    const int64_t N = total_tiles(p);
+
+    const int64_t r0 = range_start(w, N, W);
+    const int64_t r1 = range_start(w + 1, N, W);
+    if (r0 >= r1) return;
+
+    int b;
+    int64_t seq_start;
+    find_seq(p, r0, b, seq_start);
+    SeqRange sr = seq_range(p, b);
+
+    // tiles of one chunk whose pages fit the LDS page list
+    const int chunk_tiles = ((kMaxSplitPages - 2) << p.page_shift) / kTile;
+    constexpr int kElem = FP8 ? 1 : 2;
+    constexpr int kVBytes = VRow<D, FP8>::kBytes;
+
+    int64_t pos = r0;
+    int slot = 0;
+    while (pos < r1) {
+        const int n = sr.tiles;                               // > 0 here
+        const int kvh = (int)((pos - seq_start) / n);
+        const int i0 = (int)((pos - seq_start) % n);
+        const int64_t seg_end = seq_start + (int64_t)(kvh + 1) * n;
+        const int cnt = (int)(min(r1, seg_end) - pos);
+        const bool complete = (i0 == 0) && (cnt == n);
+
+        // ---- Q^T as the B operand: column c = query head kvh*G + c ----
+        // The contraction index (grp, j) of MFMA kk stands for d = dq(kk, grp)
+        // + j; for fp8 K one 16-byte load feeds two consecutive MFMAs.
+        u32x4 qop[KK];
+        {
+            const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
+                                   (int64_t)b * p.q_stride_b +
+                                   (int64_t)(kvh * G + (c < G ? c : 0)) * D;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                const int d0 = FP8 ? 64 * (kk / 2) + 16 * grp + 8 * (kk % 2) : 32 * kk + 8 * grp;
+                const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + d0);
+                qop[kk] = (c < G) ? v : u32x4{0, 0, 0, 0};
             }
         }
-        return;
-    }
 
-    const int chunk0 = base + split * T;
-    const int t_begin = max(chunk0, lo);
-    const int t_end = min(chunk0 + T, L);
-    const int n_tiles = (t_end - chunk0 + kTile - 1) / kTile;
-
-    // The split's page list, once, into LDS: every later page lookup is an
-    // LDS read instead of a dependent global load.
-    const int first_page = t_begin >> p.page_shift;
-    const int n_pages = ((t_end - 1) >> p.page_shift) - first_page + 1;
-    {
-        const int32_t* bt_row = p.block_table + (int64_t)b * p.bt_stride + first_page;
-        for (int i = threadIdx.x; i < n_pages; i += NW * 64) sm_pages[i] = bt_row[i];
-    }
-
-    // Q^T as the B operand: column c = query head kvh*G + c.  The contraction
-    // index (grp, j) of MFMA kk stands for d = dq(kk, grp) + j; for fp8 K one
-    // 16-byte load feeds two consecutive MFMAs, hence the different order.
-    u32x4 qop[KK];
-    {
-        const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + (int64_t)b * p.q_stride_b +
-                               (int64_t)(kvh * G + (c < G ? c : 0)) * D;
+        Acc<D> acc;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            const int d0 = FP8 ? 64 * (kk / 2) + 16 * grp + 8 * (kk % 2) : 32 * kk + 8 * grp;
-            u32x4 v = *reinterpret_cast<const u32x4*>(qrow + d0);
-            qop[kk] = (c < G) ? v : u32x4{0, 0, 0, 0};
-        }
-    }
-    __syncthreads();
+        for (int e = 0; e < VE; ++e) acc.o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    Acc<D> acc;
-#pragma unroll
-    for (int e = 0; e < VE; ++e) acc.o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    TileCtx x;
-    {
-        constexpr int kElem = FP8 ? 1 : 2;
-        constexpr int kVBytes = VRow<D, FP8>::kBytes;
-        x.pages = sm_pages;
-        x.first_page = first_page;
-        x.last_idx = n_pages - 1;
-        x.t_begin = t_begin;
-        x.t_end = t_end;
+        TileCtx x;
         x.c = c;
         x.grp = grp;
         x.page_bytes = p.s_page * kElem;
         x.tok_bytes = (int)(p.s_tok * kElem);
-        const int head = (int)(kvh * p.s_head * kElem);
-        x.k_lane = head + 16 * grp + (UNIFORM ? c * x.tok_bytes : 0);
+        {
+            const int head = (int)(kvh * p.s_head * kElem);
+            x.k_lane = head + 16 * grp + (UNIFORM ? c * x.tok_bytes : 0);
+            using KR = KRowRegs<D, FP8>;
+            x.k_row = lane / KR::kLanesPerRow;
+            x.k_row_lane = head + 16 * (lane % KR::kLanesPerRow) +
+                           (UNIFORM ? x.k_row * x.tok_bytes : 0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            x.v_lane[r] = head + kVBytes * c + (UNIFORM ? (4 * grp + r) * x.tok_bytes : 0);
-    }
-
-    // K and V rotate through one register set each, holding SUB consecutive
-    // tiles of this wave: the next step's K rows are requested as soon as
-    // this step's scores are formed and its V rows as soon as this step's P*V
-    // is done, so about SUB tiles per wave are always in flight.  The last
-    // step is peeled off so that the steady-state loop issues its loads
-    // unconditionally (exact load counters); a missing tile of the last step
-    // is loaded as a repeat of the wave's last tile and not consumed.  This
-    // wave's tiles are wave, wave + NW, ...
-    constexpr int SUB = kDecodeSub;
-    KRegs<D, FP8> kr[SUB];
-    VRegs<D, FP8> vr[SUB];
-    const int my_tiles = wave < n_tiles ? (n_tiles - wave + NW - 1) / NW : 0;
-    const int my_steps = (my_tiles + SUB - 1) / SUB;
-    auto tile_t0 = [&](int i) { return chunk0 + (wave + min(i, my_tiles - 1) * NW) * kTile; };
-    if (my_tiles > 0) {
-#pragma unroll
-        for (int u = 0; u < SUB; ++u) issue_k<D, FP8, UNIFORM>(kr[u], p, x, tile_t0(u));
-#pragma unroll
-        for (int u = 0; u < SUB; ++u) issue_v<D, FP8, UNIFORM>(vr[u], p, x, tile_t0(u));
-        for (int st = 0; st + 1 < my_steps; ++st) {
-            f32x4 s[SUB][2];
-#pragma unroll
-            for (int u = 0; u < SUB; ++u) tile_scores<D, FP8>(s[u], kr[u], qop);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int u = 0; u < SUB; ++u)
-                issue_k<D, FP8, UNIFORM>(kr[u], p, x, tile_t0((st + 1) * SUB + u));
-#pragma unroll
-            for (int u = 0; u < SUB; ++u) {
-                const int t0 = tile_t0(st * SUB + u);
-                const bool full = (t0 >= t_begin) && (t0 + kTile <= t_end);
-                const u32x4 pop = tile_softmax<D, CAP>(acc, s[u], p, x, t0, full);
-                tile_pv<D, FP8>(acc, vr[u], pop, x, t0, full);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int u = 0; u < SUB; ++u)
-                issue_v<D, FP8, UNIFORM>(vr[u], p, x, tile_t0((st + 1) * SUB + u));
+            for (int r = 0; r < 4; ++r)
+                x.v_lane[r] = head + kVBytes * c + (UNIFORM ? (4 * grp + r) * x.tok_bytes : 0);
         }
-        const int st = my_steps - 1;
-#pragma unroll
-        for (int u = 0; u < SUB; ++u) {
-            if (st * SUB + u < my_tiles) {
-                const int t0 = tile_t0(st * SUB + u);
-                const bool full = (t0 >= t_begin) && (t0 + kTile <= t_end);
+        x.pages = sm_pages;
+
+        // ---- the piece's tiles, chunk by chunk (page list staged in LDS) ----
+        for (int c0 = 0; c0 < cnt; c0 += chunk_tiles) {
+            const int ct = min(cnt - c0, chunk_tiles);
+            const int tile0 = sr.base + (i0 + c0) * kTile;
+            x.t_begin = max(tile0, sr.lo);
+            x.t_end = min(tile0 + ct * kTile, sr.L);
+            x.first_page = x.t_begin >> p.page_shift;
+            const int n_pages = ((x.t_end - 1) >> p.page_shift) - x.first_page + 1;
+            x.last_idx = n_pages - 1;
+            __syncthreads();     // previous chunk's readers are done with the list
+            {
+                const int32_t* bt_row =
+                    p.block_table + (int64_t)b * p.bt_stride + x.first_page;
+                for (int i = lane; i < n_pages; i += 64) sm_pages[i] = bt_row[i];
+            }
+            __syncthreads();
+
+#if PA_DECODE_KLDS
+            // K rows are loaded whole (nontemporal) and transposed through the
+            // wave's LDS tile; the registers are free for the next tile's K as
+            // soon as they are staged, V rotates as below.  The last tile is
+            // peeled off so the steady loop issues its loads unconditionally.
+            {
+                KRowRegs<D, FP8> kr;
+                VRegs<D, FP8> vr;
+                auto tile_t0 = [&](int i) { return tile0 + min(i, ct - 1) * kTile; };
+                issue_k_rows<D, FP8, UNIFORM>(kr, p, x, tile_t0(0));
+                issue_v<D, FP8, UNIFORM>(vr, p, x, tile_t0(0));
+                for (int i = 0; i + 1 < ct; ++i) {
+                    const int t0 = tile_t0(i);
+                    const bool full = (t0 >= x.t_begin) && (t0 + kTile <= x.t_end);
+                    stage_k<D, FP8>(kr, sm_k, lane);
+                    __syncthreads();
+                    issue_k_rows<D, FP8, UNIFORM>(kr, p, x, tile_t0(i + 1));
+                    f32x4 s[2];
+                    tile_scores_lds<D, FP8>(s, sm_k, qop, c, grp);
+                    const u32x4 pop = tile_softmax<D, CAP>(acc, s, p, x, t0, full);
+                    tile_pv<D, FP8>(acc, vr, pop, x, t0, full);
+                    __syncthreads();
+                    issue_v<D, FP8, UNIFORM>(vr, p, x, tile_t0(i + 1));
+                }
+                const int t0 = tile_t0(ct - 1);
+                const bool full = (t0 >= x.t_begin) && (t0 + kTile <= x.t_end);
+                stage_k<D, FP8>(kr, sm_k, lane);
+                __syncthreads();
                 f32x4 s[2];
-                tile_scores<D, FP8>(s, kr[u], qop);
+                tile_scores_lds<D, FP8>(s, sm_k, qop, c, grp);
                 const u32x4 pop = tile_softmax<D, CAP>(acc, s, p, x, t0, full);
-                tile_pv<D, FP8>(acc, vr[u], pop, x, t0, full);
+                tile_pv<D, FP8>(acc, vr, pop, x, t0, full);
+                __syncthreads();
             }
+#else
+            // K and V rotate through one register set each, holding SUB
+            // consecutive tiles: the next step's K rows are requested as soon
+            // as this step's scores are formed and its V rows as soon as this
+            // step's P*V is done.  The last step is peeled off so that the
+            // steady-state loop issues its loads unconditionally (exact load
+            // counters); a missing tile of the last step is loaded as a repeat
+            // of the chunk's last tile and not consumed.
+            KRegs<D, FP8> kr[SUB];
+            VRegs<D, FP8> vr[SUB];
+            const int steps = (ct + SUB - 1) / SUB;
+            auto tile_t0 = [&](int i) { return tile0 + min(i, ct - 1) * kTile; };
+#pragma unroll
+            for (int u = 0; u < SUB; ++u) issue_k<D, FP8, UNIFORM>(kr[u], p, x, tile_t0(u));
+#pragma unroll
+            for (int u = 0; u < SUB; ++u) issue_v<D, FP8, UNIFORM>(vr[u], p, x, tile_t0(u));
+            for (int st = 0; st + 1 < steps; ++st) {
+                f32x4 s[SUB][2];
+#pragma unroll
+                for (int u = 0; u < SUB; ++u) tile_scores<D, FP8>(s[u], kr[u], qop);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int u = 0; u < SUB; ++u)
+                    issue_k<D, FP8, UNIFORM>(kr[u], p, x, tile_t0((st + 1) * SUB + u));
+#pragma unroll
+                for (int u = 0; u < SUB; ++u) {
+                    const int t0 = tile_t0(st * SUB + u);
+                    const bool full = (t0 >= x.t_begin) && (t0 + kTile <= x.t_end);
+                    const u32x4 pop = tile_softmax<D, CAP>(acc, s[u], p, x, t0, full);
+                    tile_pv<D, FP8>(acc, vr[u], pop, x, t0, full);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int u = 0; u < SUB; ++u)
+                    issue_v<D, FP8, UNIFORM>(vr[u], p, x, tile_t0((st + 1) * SUB + u));
+            }
+            {
+                const int st = steps - 1;
+#pragma unroll
+                for (int u = 0; u < SUB; ++u) {
+                    if (st * SUB + u < ct) {
+                        const int t0 = tile_t0(st * SUB + u);
+                        const bool full = (t0 >= x.t_begin) && (t0 + kTile <= x.t_end);
+                        f32x4 s[2];
+                        tile_scores<D, FP8>(s, kr[u], qop);
+                        const u32x4 pop = tile_softmax<D, CAP>(acc, s, p, x, t0, full);
+                        tile_pv<D, FP8>(acc, vr[u], pop, x, t0, full);
+                    }
+                }
+            }
+#endif
         }
-    }
 
-    // ---- finish: softmax sum over the 4 lanes of each column ----
-    float l_tot = acc.l + shfl_xor(acc.l, 16);
-    l_tot += shfl_xor(l_tot, 32);
-    const bool direct = (n_splits == 1);
-    if constexpr (NW == 1) {
-        // Row r = 4*grp + j of O belongs to the head of column r: fetch that
-        // column's max and sum, normalise and store this lane's VE values.
+        // ---- finish the piece: sum over the 4 lanes of each column, then
+        // row r = 4*grp + j of O (head of column r) is normalised and stored ----
+        float l_tot = acc.l + shfl_xor(acc.l, 16);
+        l_tot += shfl_xor(l_tot, 32);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = 4 * grp + j;
@@ -473,20 +693,20 @@ void decode_partial_kernel(DecodeParams p) {
             const float mr = __shfl(acc.m, r, 64);
             if (r < G) {
                 const float inv = p.v_scale / lr;
-                const int h = kvh * G + r;
-                if (direct) {
+                if (complete) {
                     uint16_t* o16 = static_cast<uint16_t*>(p.out) +
-                                    (int64_t)b * p.out_stride_b + (int64_t)h * D + VE * c;
-                    uint32_t w[VE / 2];
+                                    (int64_t)b * p.out_stride_b +
+                                    (int64_t)(kvh * G + r) * D + VE * c;
+                    uint32_t wv[VE / 2];
 #pragma unroll
                     for (int e = 0; e < VE; e += 2)
-                        w[e / 2] = pack_bf16x2(acc.o[e][j] * inv, acc.o[e + 1][j] * inv);
+                        wv[e / 2] = pack_bf16x2(acc.o[e][j] * inv, acc.o[e + 1][j] * inv);
                     if constexpr (VE == 8)
-                        *reinterpret_cast<u32x4*>(o16) = u32x4{w[0], w[1], w[2], w[3]};
+                        *reinterpret_cast<u32x4*>(o16) = u32x4{wv[0], wv[1], wv[2], wv[3]};
                     else
-                        *reinterpret_cast<u32x2*>(o16) = u32x2{w[0], w[1]};
+                        *reinterpret_cast<u32x2*>(o16) = u32x2{wv[0], wv[1]};
                 } else {
-                    const int64_t row = ((int64_t)b * p.num_q_heads + h) * p.num_splits + split;
+                    const int64_t row = part_row(p, w, slot) + r;
                     float* po = p.part_o + row * D + VE * c;
 #pragma unroll
                     for (int e = 0; e < VE; e += 4)
@@ -497,101 +717,141 @@ void decode_partial_kernel(DecodeParams p) {
                 }
             }
         }
-    } else {
-        // combine the waves of this block through LDS
-        __shared__ float sm_m[NW][16];
-        __shared__ float sm_l[NW][16];
-        __shared__ float sm_o[NW][16][D];
-        if (grp == 0) {
-            sm_m[wave][c] = acc.m;
-            sm_l[wave][c] = l_tot;
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 4 * grp + j;
-            if (r < G) {
-#pragma unroll
-                for (int e = 0; e < VE; ++e) sm_o[wave][r][VE * c + e] = acc.o[e][j];
-            }
-        }
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
-            const int r = idx / D, d = idx % D;
-            float M = sm_m[0][r];
-#pragma unroll
-            for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_m[w][r]);
-            float num = 0.f, lsum = 0.f;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                const float f = fast_exp2(sm_m[w][r] - M);
-                num += f * sm_o[w][r][d];
-                lsum += f * sm_l[w][r];
-            }
-            const float val = num / lsum * p.v_scale;
-            const int h = kvh * G + r;
-            if (direct) {
-                uint16_t* o16 = static_cast<uint16_t*>(p.out) + (int64_t)b * p.out_stride_b +
-                                (int64_t)h * D + d;
-                *o16 = (uint16_t)(pack_bf16x2(val, 0.f) & 0xffffu);
-            } else {
-                const int64_t row = ((int64_t)b * p.num_q_heads + h) * p.num_splits + split;
-                p.part_o[row * D + d] = val;
-                if (d == 0) p.part_lse[row] = M + __log2f(lsum);
-            }
+
+        // ---- next piece ----
+        pos += cnt;
+        slot = 1;
+        if (pos < r1 && pos == seq_start + (int64_t)n * p.num_kv_heads) {
+            seq_start = pos;
+            do {
+                ++b;
+                sr = seq_range(p, b);
+            } while (sr.tiles == 0);
         }
     }
 }
 
-// Merge of the split partials of one (sequence, kv head): for each query head,
-// out = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M)  (`_fwd_kernel_stage2`).
-// The per-split weights are formed once per head in LDS.
+// ---------------------------------------------------------------------------
+// Merge: one block per segment.  Segments inside one wave's range were written
+// by the split pass; the others are combined here from the partials of the
+// waves that cover them, out = sum_i 2^(lse_i - M) o_i / sum_i 2^(lse_i - M)
+// (`_fwd_kernel_stage2`).  Sequences with no keys get zero rows.
+// ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
-    const int kvh = blockIdx.x;
-    const int b = blockIdx.y;
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int num_workers) {
+    constexpr int kChunk = 512;              // pieces tabulated in LDS at a time
+    constexpr int kPer = (16 * D + 255) / 256;
+    const int kvh = blockIdx.x % p.num_kv_heads;
+    const int b = blockIdx.x / p.num_kv_heads;
     const int G = p.group;
-    const int L = p.seq_lens[b];
-    const int lo = (p.window > 0 && L > p.window) ? L - p.window : 0;
-    const int base = lo & ~(kTile - 1);
-    const int T = p.tokens_per_split;
-    const int n = L > lo ? min((L - base + T - 1) / T, p.num_splits) : 0;
-    if (n <= 1) return;
-
-    __shared__ float wts[16][kMaxSplits];
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int64_t row0 = ((int64_t)b * p.num_q_heads + kvh * G) * p.num_splits;
-
-    for (int idx = threadIdx.x; idx < G * n; idx += 256) {
-        const int r = idx / n, s = idx % n;
-        wts[r][s] = p.part_lse[row0 + (int64_t)r * p.num_splits + s];
+    const SeqRange sr = seq_range(p, b);
+    uint16_t* out = static_cast<uint16_t*>(p.out) + (int64_t)b * p.out_stride_b +
+                    (int64_t)kvh * G * D;
+    if (sr.tiles == 0) {
+        for (int idx = threadIdx.x; idx < G * D; idx += 256) out[idx] = 0;
+        return;
     }
-    __syncthreads();
-    for (int r = wave; r < G; r += 4) {
-        float mx = -INFINITY;
-        for (int s = lane; s < n; s += 64) mx = fmaxf(mx, wts[r][s]);
-#pragma unroll
-        for (int k = 32; k >= 1; k >>= 1) mx = fmaxf(mx, shfl_xor(mx, k));
-        float sum = 0.f;
-        for (int s = lane; s < n; s += 64) {
-            const float e = fast_exp2(wts[r][s] - mx);
-            wts[r][s] = e;
-            sum += e;
+    __shared__ int64_t sm_geo[2];
+    __shared__ int sm_row[kChunk];           // partial row of piece i (-1: empty range)
+    __shared__ float sm_w[kChunk][16];       // lse, then weight, of piece i for head row r
+    __shared__ float sm_max[16], sm_sum[16];
+    if (threadIdx.x < 64) {
+        // one pass over the lengths: all tiles, and the tiles before sequence b
+        const int lane = threadIdx.x;
+        int64_t all = 0, before = 0;
+        for (int b0 = 0; b0 < p.num_seqs; b0 += 64) {
+            const int bb = b0 + lane;
+            const int64_t t = bb < p.num_seqs ? (int64_t)seq_range(p, bb).tiles : 0;
+            all += t;
+            before += bb < b ? t : 0;
         }
-#pragma unroll
-        for (int k = 32; k >= 1; k >>= 1) sum += shfl_xor(sum, k);
-        const float inv = 1.f / sum;
-        for (int s = lane; s < n; s += 64) wts[r][s] *= inv;
+        all = wave_sum64(all);
+        before = wave_sum64(before);
+        if (lane == 0) {
+            sm_geo[0] = all * p.num_kv_heads;
+            sm_geo[1] = before * p.num_kv_heads + (int64_t)kvh * sr.tiles;
+        }
+    }
+    if (threadIdx.x < 16) {
+        sm_max[threadIdx.x] = -INFINITY;
+        sm_sum[threadIdx.x] = 0.f;
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-        const int r = idx / D, d = idx % D;
-        const float* po = p.part_o + (row0 + (int64_t)r * p.num_splits) * D + d;
-        float acc = 0.f;
-        for (int s = 0; s < n; ++s) acc += wts[r][s] * po[(int64_t)s * D];
-        uint16_t* o16 = static_cast<uint16_t*>(p.out) + (int64_t)b * p.out_stride_b +
-                        (int64_t)(kvh * G + r) * D + d;
-        *o16 = (uint16_t)(pack_bf16x2(acc, 0.f) & 0xffffu);
+    const int64_t N = sm_geo[0], seg0 = sm_geo[1], seg1 = seg0 + sr.tiles;
+    const int64_t W = num_workers;
+    const int64_t w0 = tile_owner(seg0, N, W), w1 = tile_owner(seg1 - 1, N, W);
+    if (w0 == w1) return;                    // written whole by one wave
+    const int64_t npieces = w1 - w0 + 1;
+    const bool one_chunk = npieces <= kChunk;
+
+    // partial rows of the pieces, and their lse values, into LDS
+    auto fill = [&](int64_t base, int cnt) {
+        for (int i = threadIdx.x; i < cnt; i += 256)
+            sm_row[i] = piece_row(p, w0 + base + i, seg0, N, W);
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < cnt * G; idx += 256) {
+            const int i = idx / G, r = idx % G;
+            sm_w[i][r] = sm_row[i] >= 0 ? p.part_lse[sm_row[i] + r] : -INFINITY;
+        }
+        __syncthreads();
+    };
+    // pass 1: per head row, running max and sum of 2^lse over the pieces
+    for (int64_t base = 0; base < npieces; base += kChunk) {
+        const int cnt = (int)min<int64_t>(kChunk, npieces - base);
+        fill(base, cnt);
+        const int r = threadIdx.x >> 4, l = threadIdx.x & 15;   // 16 threads per row
+        if (r < G) {
+            float mx = -INFINITY;
+            for (int i = l; i < cnt; i += 16) mx = fmaxf(mx, sm_w[i][r]);
+#pragma unroll
+            for (int k = 8; k >= 1; k >>= 1) mx = fmaxf(mx, __shfl_xor(mx, k, 16));
+            const float m_old = sm_max[r];
+            const float m_new = fmaxf(m_old, mx);
+            float sum = 0.f;
+            for (int i = l; i < cnt; i += 16)
+                if (sm_w[i][r] != -INFINITY) sum += fast_exp2(sm_w[i][r] - m_new);
+#pragma unroll
+            for (int k = 8; k >= 1; k >>= 1) sum += __shfl_xor(sum, k, 16);
+            if (l == 0) {
+                // (a chunk of empty ranges leaves max and sum untouched)
+                const float keep = m_old == -INFINITY ? 0.f : fast_exp2(m_old - m_new);
+                sm_sum[r] = sm_sum[r] * keep + sum;
+                sm_max[r] = m_new;
+            }
+        }
+        __syncthreads();
+    }
+    // pass 2: out = sum_i w_i o_i, w_i = 2^(lse_i - M) / S
+    float accv[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) accv[k] = 0.f;
+    for (int64_t base = 0; base < npieces; base += kChunk) {
+        const int cnt = (int)min<int64_t>(kChunk, npieces - base);
+        if (!one_chunk) fill(base, cnt);     // (one chunk: the table is still there)
+        for (int idx = threadIdx.x; idx < cnt * G; idx += 256) {
+            const int i = idx / G, r = idx % G;
+            const float v = sm_w[i][r];
+            sm_w[i][r] = v == -INFINITY ? 0.f : fast_exp2(v - sm_max[r]) / sm_sum[r];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const int idx = threadIdx.x + 256 * k;
+            if (idx < G * D) {
+                const int r = idx / D, d = idx % D;
+                float a = accv[k];
+                for (int i = 0; i < cnt; ++i)
+                    if (sm_row[i] >= 0)
+                        a += sm_w[i][r] * p.part_o[(int64_t)(sm_row[i] + r) * D + d];
+                accv[k] = a;
+            }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int idx = threadIdx.x + 256 * k;
+        if (idx < G * D) out[idx] = (uint16_t)(pack_bf16x2(accv[k], 0.f) & 0xffffu);
     }
 }
 
@@ -622,40 +882,60 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherParams p) {
 }
 
 template <int D, bool FP8, bool UNIFORM>
-hipError_t launch_decode_t(const DecodeParams& p, int B, int Hkv, hipStream_t stream) {
-    dim3 grid(p.num_splits * Hkv * B);
+hipError_t launch_decode_t(const DecodeParams& p, int workers, hipStream_t stream) {
+    dim3 grid(workers);
     if (p.has_cap)
-        hipLaunchKernelGGL((decode_partial_kernel<D, FP8, UNIFORM, true, kDecodeWaves>),
-                           grid, dim3(kDecodeWaves * 64), 0, stream, p);
+        hipLaunchKernelGGL((decode_split_kernel<D, FP8, UNIFORM, true>), grid, dim3(64), 0,
+                           stream, p);
     else
-        hipLaunchKernelGGL((decode_partial_kernel<D, FP8, UNIFORM, false, kDecodeWaves>),
-                           grid, dim3(kDecodeWaves * 64), 0, stream, p);
+        hipLaunchKernelGGL((decode_split_kernel<D, FP8, UNIFORM, false>), grid, dim3(64), 0,
+                           stream, p);
     return hipGetLastError();
+}
+
+template <int D, bool FP8, bool UNIFORM>
+const void* split_kernel_ptr() {
+    return reinterpret_cast<const void*>(&decode_split_kernel<D, FP8, UNIFORM, false>);
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams& p, int head_dim, bool fp8, bool uniform_pages,
-                         int B, int Hkv, hipStream_t stream) {
+                         int workers, hipStream_t stream) {
     if (head_dim == 128) {
-        if (fp8) return uniform_pages ? launch_decode_t<128, true, true>(p, B, Hkv, stream)
-                                      : launch_decode_t<128, true, false>(p, B, Hkv, stream);
-        return uniform_pages ? launch_decode_t<128, false, true>(p, B, Hkv, stream)
-                             : launch_decode_t<128, false, false>(p, B, Hkv, stream);
+        if (fp8) return uniform_pages ? launch_decode_t<128, true, true>(p, workers, stream)
+                                      : launch_decode_t<128, true, false>(p, workers, stream);
+        return uniform_pages ? launch_decode_t<128, false, true>(p, workers, stream)
+                             : launch_decode_t<128, false, false>(p, workers, stream);
     }
-    if (fp8) return uniform_pages ? launch_decode_t<64, true, true>(p, B, Hkv, stream)
-                                  : launch_decode_t<64, true, false>(p, B, Hkv, stream);
-    return uniform_pages ? launch_decode_t<64, false, true>(p, B, Hkv, stream)
-                         : launch_decode_t<64, false, false>(p, B, Hkv, stream);
+    if (fp8) return uniform_pages ? launch_decode_t<64, true, true>(p, workers, stream)
+                                  : launch_decode_t<64, true, false>(p, workers, stream);
+    return uniform_pages ? launch_decode_t<64, false, true>(p, workers, stream)
+                         : launch_decode_t<64, false, false>(p, workers, stream);
 }
 
-hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, int B, int Hkv,
-                               hipStream_t stream) {
-    dim3 grid(Hkv, B);
+hipError_t decode_waves_per_cu(int head_dim, bool fp8, bool uniform_pages, int* out) {
+    const void* f;
     if (head_dim == 128)
-        hipLaunchKernelGGL(decode_merge_kernel<128>, grid, dim3(256), 0, stream, p);
+        f = fp8 ? (uniform_pages ? split_kernel_ptr<128, true, true>()
+                                 : split_kernel_ptr<128, true, false>())
+                : (uniform_pages ? split_kernel_ptr<128, false, true>()
+                                 : split_kernel_ptr<128, false, false>());
     else
-        hipLaunchKernelGGL(decode_merge_kernel<64>, grid, dim3(256), 0, stream, p);
+        f = fp8 ? (uniform_pages ? split_kernel_ptr<64, true, true>()
+                                 : split_kernel_ptr<64, true, false>())
+                : (uniform_pages ? split_kernel_ptr<64, false, true>()
+                                 : split_kernel_ptr<64, false, false>());
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, f, 64, 0);
+}
+
+hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, int workers, int B,
+                               int Hkv, hipStream_t stream) {
+    dim3 grid((unsigned)B * Hkv);
+    if (head_dim == 128)
+        hipLaunchKernelGGL(decode_merge_kernel<128>, grid, dim3(256), 0, stream, p, workers);
+    else
+        hipLaunchKernelGGL(decode_merge_kernel<64>, grid, dim3(256), 0, stream, p, workers);
     return hipGetLastError();
 }
 

@@ -9,24 +9,24 @@ namespace pa {
 // Decode works on tiles of 32 consecutive token positions; every split starts
 // on a multiple of 32.
 constexpr int kTile = 32;
-// Split partials of one sequence are merged through LDS: at most this many.
-constexpr int kMaxSplits = 256;
-// Waves that share one (sequence, kv head, split) work item.
-#ifndef PA_DECODE_WAVES
-#define PA_DECODE_WAVES 1
-#endif
+// Upper bound on the persistent split-pass waves (a forced count included).
+constexpr int kMaxWorkers = 1 << 20;
 // Tiles of 32 tokens a decode wave keeps in flight per pipeline step.
 #ifndef PA_DECODE_SUB
-#define PA_DECODE_SUB 2
+#define PA_DECODE_SUB 1
 #endif
 constexpr int kDecodeSub = PA_DECODE_SUB;
+// K rows loaded whole and transposed through LDS (1) or loaded straight into
+// the MFMA operand layout (0).
+#ifndef PA_DECODE_KLDS
+#define PA_DECODE_KLDS 1
+#endif
 #ifndef PA_DECODE_OCCUPANCY
 #define PA_DECODE_OCCUPANCY 2
 #endif
-constexpr int kDecodeWaves = PA_DECODE_WAVES;
 constexpr int kDecodeOccupancy = PA_DECODE_OCCUPANCY;   // waves per SIMD the kernel must allow
-// Page-table entries of one split staged in LDS: a split of T tokens touches
-// at most T/page_size + 2 pages.
+// Page-table entries staged in LDS for one chunk of a wave's range: a chunk
+// of T tokens touches at most T/page_size + 2 pages.
 constexpr int kMaxSplitPages = 2080;
 
 struct DecodeParams {
@@ -44,8 +44,6 @@ struct DecodeParams {
     int32_t group;            // G = Hq / Hkv (1..16)
     int32_t page_shift;       // log2(page_size)
     int32_t window;           // <= 0: off
-    int32_t tokens_per_split; // multiple of kTile
-    int32_t num_splits;       // grid x; split partial stride
     int32_t has_cap;
     float qk_scale2;          // scale * k_scale * log2(e)           (no cap)
     float cap_c1;             // 2 * scale * k_scale * log2(e) / c   (cap)
@@ -53,8 +51,8 @@ struct DecodeParams {
     float v_scale;
     void* out;                // bf16 [B, Hq, D], row stride out_stride_b
     int64_t out_stride_b;
-    float* part_o;            // [B, Hq, num_splits, D]
-    float* part_lse;          // [B, Hq, num_splits] (log2 domain)
+    float* part_o;            // [workers, 2, G, D]: partial of a segment a wave covers in part
+    float* part_lse;          // [workers, 2, G] (log2 domain)
 };
 
 struct GatherParams {
@@ -93,9 +91,11 @@ struct ExtendParams {
 };
 
 hipError_t launch_decode(const DecodeParams& p, int head_dim, bool fp8, bool uniform_pages,
-                         int num_seqs, int num_kv_heads, hipStream_t stream);
-hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, int num_seqs,
+                         int workers, hipStream_t stream);
+hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, int workers, int num_seqs,
                                int num_kv_heads, hipStream_t stream);
+// Resident split-pass waves per compute unit (occupancy of the kernel variant).
+hipError_t decode_waves_per_cu(int head_dim, bool fp8, bool uniform_pages, int* out);
 hipError_t launch_gather(const GatherParams& p, int head_dim, bool fp8, hipStream_t stream);
 hipError_t launch_extend(const ExtendParams& p, int head_dim, bool fp8, int num_seqs,
                          hipStream_t stream);

@@ -87,8 +87,10 @@ def test_shapes(lens, Hq, Hkv, D, P, kw):
     check(case, what=f"lens={lens}")
 
 
-@pytest.mark.parametrize("splits", [1, 2, 3, 8, 32])
+@pytest.mark.parametrize("splits", [1, 2, 3, 8, 32, 257, 5000])
 def test_split_counts(splits):
+    """Any cut of the tile list into `splits` ranges gives the same result
+    (5000 ranges exceed the tiles: empty ranges must write nothing)."""
     case = rand_case([1, 31, 100, 257, 1000, 4000], 32, 8, 128, 16, 7, softcap=10.0,
                      window=900)
     check(case, num_splits=splits, what=f"S={splits}")
