@@ -145,7 +145,9 @@ pa_status paged_attn_plan(const pa_problem* prob, int hip_device, pa_plan* out);
  *   softcap       c > 0 enables c*tanh(s/c)
  *   k_scale,v_scale  fp8 descales (1.0 for bf16)
  *   out           bf16 [B, Hq, D], sequence stride out_stride_b
- *   workspace     >= plan->workspace_bytes of device memory (split partials);
+ *   workspace     >= plan->workspace_bytes of device memory (split partials
+ *                 and each sequence's tile offset, written by the split pass
+ *                 and read by the merge; no initial contents needed);
  *                 calls that share a workspace must not overlap
  *
  * Two kernels run: the key ranges of all (sequence, kv head) pairs, laid end
@@ -166,6 +168,38 @@ pa_status paged_attn_decode(const pa_plan* plan,
                             void* out, int64_t out_stride_b,
                             void* workspace, uint64_t workspace_bytes,
                             void* hip_stream);
+
+/*
+ * paged_attn_decode_split, paged_attn_decode_merge -- the two kernels of
+ * paged_attn_decode enqueued one call at a time, with the same arguments and
+ * checks.  split followed by merge on one stream, with one workspace and
+ * nothing writing that workspace in between, is paged_attn_decode (bit for
+ * bit).  For callers that time or schedule the two passes separately.
+ */
+pa_status paged_attn_decode_split(const pa_plan* plan,
+                                  const void* q, int64_t q_stride_b,
+                                  const void* k_pool, const void* v_pool,
+                                  int64_t kv_stride_page, int64_t kv_stride_tok,
+                                  int64_t kv_stride_head, int64_t num_pages,
+                                  const int32_t* block_table, int64_t bt_stride,
+                                  const int32_t* seq_lens,
+                                  int32_t page_size, float scale, float softcap,
+                                  int32_t window, float k_scale, float v_scale,
+                                  void* out, int64_t out_stride_b,
+                                  void* workspace, uint64_t workspace_bytes,
+                                  void* hip_stream);
+pa_status paged_attn_decode_merge(const pa_plan* plan,
+                                  const void* q, int64_t q_stride_b,
+                                  const void* k_pool, const void* v_pool,
+                                  int64_t kv_stride_page, int64_t kv_stride_tok,
+                                  int64_t kv_stride_head, int64_t num_pages,
+                                  const int32_t* block_table, int64_t bt_stride,
+                                  const int32_t* seq_lens,
+                                  int32_t page_size, float scale, float softcap,
+                                  int32_t window, float k_scale, float v_scale,
+                                  void* out, int64_t out_stride_b,
+                                  void* workspace, uint64_t workspace_bytes,
+                                  void* hip_stream);
 
 /*
  * paged_attn_extend -- prefix-prefill of new tokens on top of a paged context.

@@ -61,6 +61,9 @@ def lib():
     L.paged_attn_decode.argtypes = [PP, p, i64, p, p, i64, i64, i64, i64, p, i64, p,
                                     i32, f32, f32, i32, f32, f32, p, i64, p, u64, p]
     L.paged_attn_decode.restype = ctypes.c_int
+    for fn in ("paged_attn_decode_split", "paged_attn_decode_merge"):
+        getattr(L, fn).argtypes = L.paged_attn_decode.argtypes
+        getattr(L, fn).restype = ctypes.c_int
     L.paged_attn_extend.argtypes = [PP, p, p, p, p, p, p, p, i64, i64, i64, i64, p, i64,
                                     i32, f32, f32, i32, f32, f32, p, p, u64, p]
     L.paged_attn_extend.restype = ctypes.c_int
@@ -189,7 +192,31 @@ def decode(pl: Plan, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor
            workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """paged_attn_decode: q bf16 [B, Hq, D] -> out bf16 [B, Hq, D].
     A workspace passed in needs plan.workspace_bytes bytes."""
-    fn = "paged_attn_decode"
+    return _decode("paged_attn_decode", pl, q, k_pool, v_pool, block_table, seq_lens, scale,
+                   softcap, window, k_scale, v_scale, out, workspace, stream)
+
+
+def decode_split(pl: Plan, q, k_pool, v_pool, block_table, seq_lens, scale, softcap=0.0,
+                 window=0, k_scale=1.0, v_scale=1.0, out=None, workspace=None, stream=None):
+    """paged_attn_decode_split: the split pass alone (writes the segments one
+    wave covers whole to `out`, the others to the workspace)."""
+    return _decode("paged_attn_decode_split", pl, q, k_pool, v_pool, block_table, seq_lens,
+                   scale, softcap, window, k_scale, v_scale, out, workspace, stream)
+
+
+def decode_merge(pl: Plan, q, k_pool, v_pool, block_table, seq_lens, scale, softcap=0.0,
+                 window=0, k_scale=1.0, v_scale=1.0, out=None, workspace=None, stream=None):
+    """paged_attn_decode_merge: the merge pass alone, over the workspace the
+    split pass left."""
+    return _decode("paged_attn_decode_merge", pl, q, k_pool, v_pool, block_table, seq_lens,
+                   scale, softcap, window, k_scale, v_scale, out, workspace, stream)
+
+
+def _decode(fn, pl, q, k_pool, v_pool, block_table, seq_lens, scale, softcap, window,
+            k_scale, v_scale, out, workspace, stream):
+    if fn != "paged_attn_decode" and (out is None or (workspace is None and
+                                                      pl.workspace_bytes > 0)):
+        raise ValueError(f"{fn}: the passes share `out` and the workspace; pass both")
     if q.dtype != torch.bfloat16 or q.dim() != 3 or q.stride(2) != 1 or q.stride(1) != q.shape[2]:
         raise ValueError("q must be bf16 [B, Hq, D] with contiguous heads")
     if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:

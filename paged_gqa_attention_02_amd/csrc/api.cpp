@@ -40,6 +40,8 @@ pa_status check_problem(const pa_problem& pr) {
         pr.max_kv_len < 0 || pr.max_pages_per_seq < 0 || pr.num_splits < 0)
         return PA_ERR_INVALID_SHAPE;
     if (pr.num_q_heads % pr.num_kv_heads != 0) return PA_ERR_INVALID_SHAPE;
+    // one merge block per (sequence, query head): the grid is 31-bit
+    if ((int64_t)pr.num_seqs * pr.num_q_heads >= ((int64_t)1 << 31)) return PA_ERR_UNSUPPORTED;
     const int G = pr.num_q_heads / pr.num_kv_heads;
     if (G > 16 || !is_pow2(G)) return PA_ERR_UNSUPPORTED;
     if (pr.head_dim != 64 && pr.head_dim != 128) return PA_ERR_UNSUPPORTED;
@@ -151,8 +153,10 @@ pa_status paged_attn_plan(const pa_problem* prob, int hip_device, pa_plan* out) 
         pl.waves_per_block = 1;
         const int64_t G = pr.num_q_heads / pr.num_kv_heads;
         const int64_t rows = workers * 2 * G;
+        // partial rows, their log-sum-exp, and each sequence's first tile
         pl.workspace_bytes = (uint64_t)(round_up(rows * pr.head_dim * 4, 256) +
-                                        round_up(rows * 4, 256));
+                                        round_up(rows * 4, 256) +
+                                        round_up(8 * ((int64_t)pr.num_seqs + 1), 256));
     }
     *out = pl;
     return PA_OK;
@@ -183,7 +187,10 @@ int paged_attn_plan_describe(const pa_plan* pl, char* buf, int buf_len) {
 
 namespace {
 
-pa_status decode_impl(const pa_plan* plan, const void* q, int64_t q_stride_b,
+// Passes of a decode call: the split pass, the merge, or both in order.
+enum DecodePasses { kSplitPass = 1, kMergePass = 2, kBothPasses = 3 };
+
+pa_status decode_impl(int passes, const pa_plan* plan, const void* q, int64_t q_stride_b,
                       const void* k_pool, const void* v_pool, int64_t kv_stride_page,
                       int64_t kv_stride_tok, int64_t kv_stride_head, int64_t num_pages,
                       const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
@@ -249,14 +256,18 @@ pa_status decode_impl(const pa_plan* plan, const void* q, int64_t q_stride_b,
         const int64_t rows = (int64_t)pl.num_splits * 2 * p.group;
         char* ws = static_cast<char*>(workspace);
         p.part_o = reinterpret_cast<float*>(ws);
-        p.part_lse = reinterpret_cast<float*>(ws + round_up(rows * pr.head_dim * 4, 256));
+        const int64_t o_bytes = round_up(rows * pr.head_dim * 4, 256);
+        p.part_lse = reinterpret_cast<float*>(ws + o_bytes);
+        p.seq_tile0 = reinterpret_cast<int64_t*>(ws + o_bytes + round_up(rows * 4, 256));
     }
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     const bool uniform = pr.page_size >= 16;
-    if (launch_decode(p, pr.head_dim, pr.kv_dtype == PA_KV_FP8_E4M3, uniform, pl.num_splits,
+    if ((passes & kSplitPass) &&
+        launch_decode(p, pr.head_dim, pr.kv_dtype == PA_KV_FP8_E4M3, uniform, pl.num_splits,
                       stream) != hipSuccess)
         return PA_ERR_HIP;
-    if (launch_decode_merge(p, pr.head_dim, pl.num_splits, pr.num_seqs, pr.num_kv_heads,
+    if ((passes & kMergePass) &&
+        launch_decode_merge(p, pr.head_dim, pl.num_splits, pr.num_seqs, pr.num_kv_heads,
                             stream) != hipSuccess)
         return PA_ERR_HIP;
     return PA_OK;
@@ -279,7 +290,15 @@ extern "C" {
         int64_t out_stride_b, void *workspace, uint64_t workspace_bytes, void *hip_stream
 
 pa_status paged_attn_decode(PA_DECODE_PARAMS) {
-    return decode_impl(PA_DECODE_ARGS);
+    return decode_impl(kBothPasses, PA_DECODE_ARGS);
+}
+
+pa_status paged_attn_decode_split(PA_DECODE_PARAMS) {
+    return decode_impl(kSplitPass, PA_DECODE_ARGS);
+}
+
+pa_status paged_attn_decode_merge(PA_DECODE_PARAMS) {
+    return decode_impl(kMergePass, PA_DECODE_ARGS);
 }
 
 pa_status paged_attn_gather(const pa_plan* plan, const void* k_pool, const void* v_pool,

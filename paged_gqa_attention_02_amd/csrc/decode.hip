@@ -483,13 +483,15 @@ __device__ __forceinline__ int64_t tile_owner(int64_t t, int64_t N, int64_t W) {
 }
 
 // Partial row of wave wv's piece of the segment starting at global tile
-// seg0 (slot 0 when the wave's range starts inside the segment, else slot 1),
-// or -1 when the wave's range is empty (possible when N < W).
-__device__ __forceinline__ int piece_row(const DecodeParams& p, int64_t wv, int64_t seg0,
-                                         int64_t N, int64_t W) {
-    const int64_t a = range_start(wv, N, W);
-    if (a == range_start(wv + 1, N, W)) return -1;
-    return (int)part_row(p, wv, a >= seg0 ? 0 : 1);
+// seg0, whose first tile wave w0 owns, or -1 when wv's range is empty
+// (possible only when N < W).  The owner's range may start before the
+// segment (its piece is then the range's last one: slot 1); a later wave's
+// range starts inside the segment (slot 0).
+__device__ __forceinline__ int piece_row(const DecodeParams& p, int64_t wv, int64_t w0,
+                                         int64_t seg0, int64_t N, int64_t W) {
+    if (wv == w0) return (int)part_row(p, wv, range_start(wv, N, W) >= seg0 ? 0 : 1);
+    if (N < W && range_start(wv, N, W) == range_start(wv + 1, N, W)) return -1;
+    return (int)part_row(p, wv, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -500,7 +502,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kDecodeOccup
 void decode_split_kernel(DecodeParams p) {
     constexpr int KK = D / 32;                  // QK MFMAs per 16-token half
     constexpr int VE = D / 16;                  // PV MFMAs per tile
+#if !PA_DECODE_KLDS
     constexpr int SUB = kDecodeSub;
+#endif
 
     const int lane = threadIdx.x;
     const int c = lane & 15;
@@ -515,6 +519,7 @@ void decode_split_kernel(DecodeParams p) {
 #endif
 
     const int64_t N = total_tiles(p);
+    if (w == 0 && lane == 0) p.seq_tile0[p.num_seqs] = N;
 
     const int64_t r0 = range_start(w, N, W);
     const int64_t r1 = range_start(w + 1, N, W);
@@ -539,6 +544,7 @@ void decode_split_kernel(DecodeParams p) {
         const int64_t seg_end = seq_start + (int64_t)(kvh + 1) * n;
         const int cnt = (int)(min(r1, seg_end) - pos);
         const bool complete = (i0 == 0) && (cnt == n);
+        if (kvh == 0 && i0 == 0 && lane == 0) p.seq_tile0[b] = seq_start;
 
         // ---- Q^T as the B operand: column c = query head kvh*G + c ----
         // The contraction index (grp, j) of MFMA kk stands for d = dq(kk, grp)
@@ -732,126 +738,99 @@ void decode_split_kernel(DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Merge: one block per segment.  Segments inside one wave's range were written
-// by the split pass; the others are combined here from the partials of the
-// waves that cover them, out = sum_i 2^(lse_i - M) o_i / sum_i 2^(lse_i - M)
-// (`_fwd_kernel_stage2`).  Sequences with no keys get zero rows.
+// Merge: one block per (segment, query-head row r).  Segments inside one
+// wave's range were written by the split pass; the others are combined here
+// from the partials of the waves that cover them,
+//   out = sum_i 2^(lse_i - M) o_i / sum_i 2^(lse_i - M)    (`_fwd_kernel_stage2`).
+// Threads are (column quad q, piece lane pl): each folds the pieces
+// pl, pl + kR, ... of its four columns into a running (max, sum, acc) --
+// the log-sum-exp values and the partial rows are loaded in the same round --
+// and the kR piece lanes are then combined through LDS.  Sequences with no
+// keys get zero rows.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int num_workers) {
-    constexpr int kChunk = 512;              // pieces tabulated in LDS at a time
-    constexpr int kPer = (16 * D + 255) / 256;
-    const int kvh = blockIdx.x % p.num_kv_heads;
-    const int b = blockIdx.x / p.num_kv_heads;
+    constexpr int kQ = D / 4;                // threads per row, 4 columns each
+    constexpr int kR = 256 / kQ;             // piece lanes
+    constexpr int kBatch = 4;                // pieces in flight per thread
     const int G = p.group;
+    const int r = blockIdx.x % G;
+    const int seg = blockIdx.x / G;
+    const int kvh = seg % p.num_kv_heads;
+    const int b = seg / p.num_kv_heads;
+    const int q = threadIdx.x % kQ, pl = threadIdx.x / kQ;
     const SeqRange sr = seq_range(p, b);
     uint16_t* out = static_cast<uint16_t*>(p.out) + (int64_t)b * p.out_stride_b +
-                    (int64_t)kvh * G * D;
+                    (int64_t)(kvh * G + r) * D + 4 * q;
     if (sr.tiles == 0) {
-        for (int idx = threadIdx.x; idx < G * D; idx += 256) out[idx] = 0;
+        if (pl == 0) *reinterpret_cast<u32x2*>(out) = u32x2{0u, 0u};
         return;
     }
-    __shared__ int64_t sm_geo[2];
-    __shared__ int sm_row[kChunk];           // partial row of piece i (-1: empty range)
-    __shared__ float sm_w[kChunk][16];       // lse, then weight, of piece i for head row r
-    __shared__ float sm_max[16], sm_sum[16];
-    if (threadIdx.x < 64) {
-        // one pass over the lengths: all tiles, and the tiles before sequence b
-        const int lane = threadIdx.x;
-        int64_t all = 0, before = 0;
-        for (int b0 = 0; b0 < p.num_seqs; b0 += 64) {
-            const int bb = b0 + lane;
-            const int64_t t = bb < p.num_seqs ? (int64_t)seq_range(p, bb).tiles : 0;
-            all += t;
-            before += bb < b ? t : 0;
-        }
-        all = wave_sum64(all);
-        before = wave_sum64(before);
-        if (lane == 0) {
-            sm_geo[0] = all * p.num_kv_heads;
-            sm_geo[1] = before * p.num_kv_heads + (int64_t)kvh * sr.tiles;
-        }
-    }
-    if (threadIdx.x < 16) {
-        sm_max[threadIdx.x] = -INFINITY;
-        sm_sum[threadIdx.x] = 0.f;
-    }
-    __syncthreads();
-    const int64_t N = sm_geo[0], seg0 = sm_geo[1], seg1 = seg0 + sr.tiles;
+    // N tiles in all and the first global tile of this segment, as the split
+    // pass found them
+    const int64_t N = p.seq_tile0[p.num_seqs];
+    const int64_t seg0 = p.seq_tile0[b] + (int64_t)kvh * sr.tiles;
     const int64_t W = num_workers;
-    const int64_t w0 = tile_owner(seg0, N, W), w1 = tile_owner(seg1 - 1, N, W);
+    const int64_t w0 = tile_owner(seg0, N, W), w1 = tile_owner(seg0 + sr.tiles - 1, N, W);
     if (w0 == w1) return;                    // written whole by one wave
     const int64_t npieces = w1 - w0 + 1;
-    const bool one_chunk = npieces <= kChunk;
 
-    // partial rows of the pieces, and their lse values, into LDS
-    auto fill = [&](int64_t base, int cnt) {
-        for (int i = threadIdx.x; i < cnt; i += 256)
-            sm_row[i] = piece_row(p, w0 + base + i, seg0, N, W);
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < cnt * G; idx += 256) {
-            const int i = idx / G, r = idx % G;
-            sm_w[i][r] = sm_row[i] >= 0 ? p.part_lse[sm_row[i] + r] : -INFINITY;
-        }
-        __syncthreads();
-    };
-    // pass 1: per head row, running max and sum of 2^lse over the pieces
-    for (int64_t base = 0; base < npieces; base += kChunk) {
-        const int cnt = (int)min<int64_t>(kChunk, npieces - base);
-        fill(base, cnt);
-        const int r = threadIdx.x >> 4, l = threadIdx.x & 15;   // 16 threads per row
-        if (r < G) {
-            float mx = -INFINITY;
-            for (int i = l; i < cnt; i += 16) mx = fmaxf(mx, sm_w[i][r]);
+    float m = -INFINITY, sum = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t i0 = pl; i0 < npieces; i0 += kR * kBatch) {
+        float lse[kBatch];
+        f32x4 o[kBatch];
 #pragma unroll
-            for (int k = 8; k >= 1; k >>= 1) mx = fmaxf(mx, __shfl_xor(mx, k, 16));
-            const float m_old = sm_max[r];
-            const float m_new = fmaxf(m_old, mx);
-            float sum = 0.f;
-            for (int i = l; i < cnt; i += 16)
-                if (sm_w[i][r] != -INFINITY) sum += fast_exp2(sm_w[i][r] - m_new);
-#pragma unroll
-            for (int k = 8; k >= 1; k >>= 1) sum += __shfl_xor(sum, k, 16);
-            if (l == 0) {
-                // (a chunk of empty ranges leaves max and sum untouched)
-                const float keep = m_old == -INFINITY ? 0.f : fast_exp2(m_old - m_new);
-                sm_sum[r] = sm_sum[r] * keep + sum;
-                sm_max[r] = m_new;
+        for (int u = 0; u < kBatch; ++u) {
+            const int64_t i = i0 + (int64_t)kR * u;
+            const int row = i < npieces ? piece_row(p, w0 + i, w0, seg0, N, W) : -1;
+            lse[u] = -INFINITY;
+            o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (row >= 0) {
+                lse[u] = p.part_lse[row + r];
+                o[u] = *reinterpret_cast<const f32x4*>(p.part_o + (int64_t)(row + r) * D + 4 * q);
             }
         }
-        __syncthreads();
-    }
-    // pass 2: out = sum_i w_i o_i, w_i = 2^(lse_i - M) / S
-    float accv[kPer];
+        float bm = lse[0];
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) accv[k] = 0.f;
-    for (int64_t base = 0; base < npieces; base += kChunk) {
-        const int cnt = (int)min<int64_t>(kChunk, npieces - base);
-        if (!one_chunk) fill(base, cnt);     // (one chunk: the table is still there)
-        for (int idx = threadIdx.x; idx < cnt * G; idx += 256) {
-            const int i = idx / G, r = idx % G;
-            const float v = sm_w[i][r];
-            sm_w[i][r] = v == -INFINITY ? 0.f : fast_exp2(v - sm_max[r]) / sm_sum[r];
+        for (int u = 1; u < kBatch; ++u) bm = fmaxf(bm, lse[u]);
+        if (bm == -INFINITY) continue;
+        const float mn = fmaxf(m, bm);
+        const float f = m == -INFINITY ? 0.f : fast_exp2(m - mn);
+        sum *= f;
+        acc *= f;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const float w = lse[u] == -INFINITY ? 0.f : fast_exp2(lse[u] - mn);
+            sum += w;
+            acc += w * o[u];
         }
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < kPer; ++k) {
-            const int idx = threadIdx.x + 256 * k;
-            if (idx < G * D) {
-                const int r = idx / D, d = idx % D;
-                float a = accv[k];
-                for (int i = 0; i < cnt; ++i)
-                    if (sm_row[i] >= 0)
-                        a += sm_w[i][r] * p.part_o[(int64_t)(sm_row[i] + r) * D + d];
-                accv[k] = a;
-            }
-        }
-        __syncthreads();
+        m = mn;
     }
+
+    __shared__ float sm_m[kR], sm_s[kR];
+    __shared__ f32x4 sm_acc[kR][kQ];
+    if (q == 0) {
+        sm_m[pl] = m;
+        sm_s[pl] = sum;
+    }
+    sm_acc[pl][q] = acc;
+    __syncthreads();
+    if (pl == 0) {
+        float M = sm_m[0];
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-        const int idx = threadIdx.x + 256 * k;
-        if (idx < G * D) out[idx] = (uint16_t)(pack_bf16x2(accv[k], 0.f) & 0xffffu);
+        for (int j = 1; j < kR; ++j) M = fmaxf(M, sm_m[j]);
+        float S = 0.f;
+        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < kR; ++j) {
+            const float f = sm_m[j] == -INFINITY ? 0.f : fast_exp2(sm_m[j] - M);
+            S += f * sm_s[j];
+            a += f * sm_acc[j][q];
+        }
+        const float inv = 1.f / S;
+        *reinterpret_cast<u32x2*>(out) =
+            u32x2{pack_bf16x2(a.x * inv, a.y * inv), pack_bf16x2(a.z * inv, a.w * inv)};
     }
 }
 
@@ -931,7 +910,7 @@ hipError_t decode_waves_per_cu(int head_dim, bool fp8, bool uniform_pages, int* 
 
 hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, int workers, int B,
                                int Hkv, hipStream_t stream) {
-    dim3 grid((unsigned)B * Hkv);
+    dim3 grid((unsigned)B * Hkv * p.group);
     if (head_dim == 128)
         hipLaunchKernelGGL(decode_merge_kernel<128>, grid, dim3(256), 0, stream, p, workers);
     else

@@ -53,6 +53,8 @@ struct DecodeParams {
     int64_t out_stride_b;
     float* part_o;            // [workers, 2, G, D]: partial of a segment a wave covers in part
     float* part_lse;          // [workers, 2, G] (log2 domain)
+    int64_t* seq_tile0;       // [B + 1]: first global tile of sequence b (written when it
+                              // has tiles); entry B = all tiles.  Split pass -> merge.
 };
 
 struct GatherParams {

@@ -73,6 +73,7 @@ def plan_status(**kw):
     (dict(max_pages_per_seq=255), SHAPE),
     (dict(num_seqs=-1), SHAPE),
     (dict(num_splits=-2), SHAPE),
+    (dict(num_seqs=1 << 26), UNSUP),             # B x Hq reaches 2^31
     (dict(mode=1, total_q=100, max_q_len=0), SHAPE),
     (dict(mode=1, total_q=100, max_q_len=50), OK),
 ])
@@ -105,7 +106,10 @@ def test_plan_decisions():
 A = 1 << 20          # 16-byte aligned fake address
 
 
-def decode_status(plan_kw=None, **kw):
+DECODE_FNS = ["paged_attn_decode", "paged_attn_decode_split", "paged_attn_decode_merge"]
+
+
+def decode_status(plan_kw=None, fn="paged_attn_decode", **kw):
     st, pl = plan_status(**(plan_kw or {}))
     assert st == OK
     args = dict(q=A, q_stride_b=32 * 128, k=A, v=A, sp=16 * 8 * 128, st=8 * 128, sh=128,
@@ -114,7 +118,7 @@ def decode_status(plan_kw=None, **kw):
                 ws=A, ws_bytes=pl.workspace_bytes, stream=None)
     args.update(kw)
     v = lambda x: None if x is None else ctypes.c_void_p(x)
-    return pa.lib().paged_attn_decode(
+    return getattr(pa.lib(), fn)(
         ctypes.byref(pl), v(args["q"]), args["q_stride_b"], v(args["k"]), v(args["v"]),
         args["sp"], args["st"], args["sh"], args["num_pages"], v(args["bt"]),
         args["bt_stride"], v(args["sl"]), args["page_size"], args["scale"], args["softcap"],
@@ -142,8 +146,9 @@ def decode_status(plan_kw=None, **kw):
     (dict(scale=float("nan")), SHAPE),
     (dict(softcap=float("inf")), SHAPE),
 ])
-def test_decode_validation(kw, status):
-    assert decode_status(**kw) == status
+@pytest.mark.parametrize("fn", DECODE_FNS)
+def test_decode_validation(fn, kw, status):
+    assert decode_status(fn=fn, **kw) == status
 
 
 def test_decode_empty_batch_launches_nothing():

@@ -48,7 +48,7 @@ def test_workload_full_size(n, P):
     check(case, what=f"workload {n} P={case.page_size}")
 
 
-@pytest.mark.parametrize("splits", [8, 32])
+@pytest.mark.parametrize("splits", [8, 32, 20000])
 def test_long_context_forced_splits(splits):
     case = I.decode_config(3)
     out, pl = check(case, num_splits=splits, what=f"long-context S<={splits}")
@@ -94,6 +94,26 @@ def test_split_counts(splits):
     case = rand_case([1, 31, 100, 257, 1000, 4000], 32, 8, 128, 16, 7, softcap=10.0,
                      window=900)
     check(case, num_splits=splits, what=f"S={splits}")
+
+
+@pytest.mark.parametrize("n", [2, 3])
+def test_split_then_merge_is_decode(n):
+    """The two passes enqueued by separate calls give decode's bytes."""
+    case = I.decode_config(n)
+    say(f"[decode] split+merge vs decode, workload {n}")
+    t = I.decode_tensors(case, DEV)
+    pl = pa.decode_plan(t["q"], t["k_pool"], t["block_table"], case.max_kv_len,
+                        window=case.window)
+    args = (pl, t["q"], t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"], case.scale)
+    kw = dict(softcap=case.softcap, window=case.window, k_scale=case.k_scale,
+              v_scale=case.v_scale)
+    ws = pa.workspace_for(pl, DEV)
+    whole = pa.decode(*args, workspace=ws, **kw)
+    out = torch.full_like(whole, float("nan"))
+    pa.decode_split(*args, out=out, workspace=ws, **kw)
+    pa.decode_merge(*args, out=out, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), whole.view(torch.int16))
 
 
 def test_all_empty():
