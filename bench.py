@@ -27,6 +27,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 MALL_BYTES = 256 << 20
+# the sources the split-pass kernel is compiled from (counter figures taken
+# from other sources are not reported)
+DECODE_SPLIT_SOURCES = ["decode.hip", "decode_geom.h", "pa_device.h", "pa_internal.h"]
 
 
 def parse():
@@ -151,7 +154,7 @@ def bench_decode(args, torch, pa, I):
     split_ms = time_first_pass(torch, lambda i: call(pa.decode_split, i),
                                lambda i: call(pa.decode_merge, i), K)
     achieved = alg / (split_ms * 1e-3) / 1e9
-    traffic = traffic_for("decode_split", case.name, ["decode.hip", "pa_device.h"])
+    traffic = traffic_for("decode_split", case.name, DECODE_SPLIT_SOURCES)
     res = {
         "metric": "paged-attn decode KV GB/s (fraction of HBM peak) + us/call on 1 MI355X",
         "value": alg / (ms_step * 1e-3) / 1e9,
@@ -220,7 +223,8 @@ def bench_extend(args, torch, pa, I):
         "roofline": {"bound": "mfma", "kernel": "extend", "achieved": achieved,
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": traffic_for("extend", "extend", ["extend.hip", "pa_device.h"])},
+                     "traffic": traffic_for("extend", "extend",
+                                            ["extend.hip", "pa_device.h", "pa_internal.h"])},
     }
     if args.cpu_seconds > 0:
         import numpy as np

@@ -153,10 +153,11 @@ pa_status paged_attn_plan(const pa_problem* prob, int hip_device, pa_plan* out) 
         pl.waves_per_block = 1;
         const int64_t G = pr.num_q_heads / pr.num_kv_heads;
         const int64_t rows = workers * 2 * G;
-        // partial rows, their log-sum-exp, and each sequence's first tile
+        // partial rows, their log-sum-exp, and one record per segment
         pl.workspace_bytes = (uint64_t)(round_up(rows * pr.head_dim * 4, 256) +
                                         round_up(rows * 4, 256) +
-                                        round_up(8 * ((int64_t)pr.num_seqs + 1), 256));
+                                        round_up(16 * (int64_t)pr.num_seqs *
+                                                     pr.num_kv_heads, 256));
     }
     *out = pl;
     return PA_OK;
@@ -258,7 +259,7 @@ pa_status decode_impl(int passes, const pa_plan* plan, const void* q, int64_t q_
         p.part_o = reinterpret_cast<float*>(ws);
         const int64_t o_bytes = round_up(rows * pr.head_dim * 4, 256);
         p.part_lse = reinterpret_cast<float*>(ws + o_bytes);
-        p.seq_tile0 = reinterpret_cast<int64_t*>(ws + o_bytes + round_up(rows * 4, 256));
+        p.seg_rec = reinterpret_cast<int32_t*>(ws + o_bytes + round_up(rows * 4, 256));
     }
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     const bool uniform = pr.page_size >= 16;
@@ -267,8 +268,8 @@ pa_status decode_impl(int passes, const pa_plan* plan, const void* q, int64_t q_
                       stream) != hipSuccess)
         return PA_ERR_HIP;
     if ((passes & kMergePass) &&
-        launch_decode_merge(p, pr.head_dim, pl.num_splits, pr.num_seqs, pr.num_kv_heads,
-                            stream) != hipSuccess)
+        launch_decode_merge(p, pr.head_dim, pr.num_seqs, pr.num_kv_heads, stream) !=
+            hipSuccess)
         return PA_ERR_HIP;
     return PA_OK;
 }

@@ -44,6 +44,7 @@
 // K or V row, nontemporal; one wave load instruction covers whole rows (4 of
 // K or V for bf16 D=128).  A wave keeps the next tile's K and V in flight
 // while it computes the current one.
+#include "decode_geom.h"
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -57,15 +58,6 @@ namespace {
 // with this choice the S^T accumulator is already the P operand.
 __device__ __forceinline__ int tile_token(int grp, int j) {
     return (j < 4) ? 4 * grp + j : 16 + 4 * grp + (j - 4);
-}
-
-template <bool FP8>
-__device__ __forceinline__ const uint8_t* row_ptr(const void* pool, int64_t page, int row,
-                                                  int head, int64_t s_page, int64_t s_tok,
-                                                  int64_t s_head) {
-    constexpr int64_t kElem = FP8 ? 1 : 2;
-    return static_cast<const uint8_t*>(pool) +
-           (page * s_page + (int64_t)row * s_tok + (int64_t)head * s_head) * kElem;
 }
 
 // V bytes per lane per token: D/16 elements.
@@ -122,7 +114,6 @@ struct TileCtx {
     int first_page, last_idx, t_begin, t_end, c, grp;
     int64_t page_bytes;        // s_page * elem
     int tok_bytes;             // s_tok * elem
-    int k_lane;                // kvh*s_head*elem + 16*grp (+ c*tok_bytes when UNIFORM)
     int k_row;                 // whole-row K loads: the lane's row within a load
     int k_row_lane;            // kvh*s_head*elem + 16*column (+ k_row*tok_bytes when UNIFORM)
     int v_lane[4];             // kvh*s_head*elem + VBYTES*c (+ (4*grp + r)*tok_bytes when UNIFORM)
@@ -141,41 +132,6 @@ __device__ __forceinline__ int64_t page_of(const TileCtx& x, int pshift, int t) 
 template <typename T>
 __device__ __forceinline__ T load_stream(const uint8_t* ptr) {
     return __builtin_nontemporal_load(reinterpret_cast<const T*>(ptr));
-}
-
-// K rows of a tile as S^T A operands: tokens 16h + c, h = 0, 1.  Load i of a
-// half reads the 16 bytes at 64*i of the lane's slice of the row.
-template <int D, bool FP8>
-struct KRegs {
-    static constexpr int N = FP8 ? D / 64 : D / 32;   // 16-byte loads per half
-    u32x4 w[2][N];
-};
-
-template <int D, bool FP8, bool UNIFORM>
-__device__ __forceinline__ void issue_k(KRegs<D, FP8>& R, const DecodeParams& p,
-                                        const TileCtx& x, int t0) {
-    const uint8_t* pool = static_cast<const uint8_t*>(p.k_pool);
-    const int pmask = (1 << p.page_shift) - 1;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const uint8_t* ptr;
-        if constexpr (UNIFORM) {
-            // page_size is a multiple of 16: the half sits in one page
-            const int th = t0 + 16 * h;
-            const uint8_t* base = pool + page_of<true>(x, p.page_shift, th) * x.page_bytes +
-                                  (int64_t)((th & pmask) * x.tok_bytes);
-            ptr = base + x.k_lane;
-        } else {
-            const int t = t0 + 16 * h + x.c;
-            ptr = pool + page_of<false>(x, p.page_shift, t) * x.page_bytes +
-                  (int64_t)((t & pmask) * x.tok_bytes + x.k_lane);
-        }
-        // (plain loads: each 128-byte line of a row is read by two
-        // consecutive instructions, and the second must find it cached)
-#pragma unroll
-        for (int i = 0; i < KRegs<D, FP8>::N; ++i)
-            R.w[h][i] = *reinterpret_cast<const u32x4*>(ptr + 64 * i);
-    }
 }
 
 // K rows of a tile loaded whole (every wave load instruction reads complete
@@ -284,29 +240,6 @@ __device__ __forceinline__ void issue_v(VRegs<D, FP8>& R, const DecodeParams& p,
     }
 }
 
-// S^T = K Q^T for one tile: s[h][j] is the score of token 16h + 4*grp + j for
-// the head of this lane's column.
-template <int D, bool FP8>
-__device__ __forceinline__ void tile_scores(f32x4 s[2], const KRegs<D, FP8>& R,
-                                            const u32x4* qop) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        s[h] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < KRegs<D, FP8>::N; ++i) {
-            const u32x4 w = R.w[h][i];
-            if constexpr (FP8) {
-                const u32x2 a = e4m3x4_to_bf16x4(w.x), bb = e4m3x4_to_bf16x4(w.y);
-                const u32x2 cc = e4m3x4_to_bf16x4(w.z), dd = e4m3x4_to_bf16x4(w.w);
-                s[h] = mfma_bf16_16x16x32(u32x4{a.x, a.y, bb.x, bb.y}, qop[2 * i], s[h]);
-                s[h] = mfma_bf16_16x16x32(u32x4{cc.x, cc.y, dd.x, dd.y}, qop[2 * i + 1], s[h]);
-            } else {
-                s[h] = mfma_bf16_16x16x32(w, qop[i], s[h]);
-            }
-        }
-    }
-}
-
 // Online-softmax state of one wave: running max / partial sum of the head in
 // this lane's MFMA column, and O rows 4*grp..4*grp+3 at d = VE*c + e.
 template <int D>
@@ -404,97 +337,6 @@ __device__ __forceinline__ void tile_pv(Acc<D>& A, VRegs<D, FP8>& R, u32x4 pop,
 }
 
 // ---------------------------------------------------------------------------
-// Segment geometry (shared by the split pass and the merge)
-// ---------------------------------------------------------------------------
-struct SeqRange {
-    int L, lo, base, tiles;   // tiles: 32-token tiles from base covering [lo, L)
-};
-
-__device__ __forceinline__ SeqRange seq_range(const DecodeParams& p, int b) {
-    SeqRange r;
-    r.L = p.seq_lens[b];
-    r.lo = (p.window > 0 && r.L > p.window) ? r.L - p.window : 0;
-    r.base = r.lo & ~(kTile - 1);
-    r.tiles = r.L > r.lo ? (r.L - r.base + kTile - 1) / kTile : 0;
-    return r;
-}
-
-__device__ __forceinline__ int64_t wave_sum64(int64_t v) {
-#pragma unroll
-    for (int k = 32; k >= 1; k >>= 1) v += __shfl_xor(v, k, 64);
-    return v;
-}
-
-// Total tiles N over all segments (every lane gets the sum).
-__device__ __forceinline__ int64_t total_tiles(const DecodeParams& p) {
-    const int lane = __lane_id();
-    int64_t n = 0;
-    for (int b0 = 0; b0 < p.num_seqs; b0 += 64) {
-        const int b = b0 + lane;
-        n += b < p.num_seqs ? (int64_t)seq_range(p, b).tiles : 0;
-    }
-    return wave_sum64(n) * p.num_kv_heads;
-}
-
-// Sequence whose segments contain global tile `pos` (< N), and the global
-// index of its first tile.  Sequences without tiles are skipped.
-__device__ __forceinline__ void find_seq(const DecodeParams& p, int64_t pos, int& b_out,
-                                         int64_t& start_out) {
-    const int lane = __lane_id();
-    int64_t carry = 0;
-    for (int b0 = 0; b0 < p.num_seqs; b0 += 64) {
-        const int b = b0 + lane;
-        int64_t n = b < p.num_seqs ? (int64_t)seq_range(p, b).tiles * p.num_kv_heads : 0;
-        // inclusive scan across the wave
-        int64_t incl = n;
-#pragma unroll
-        for (int k = 1; k < 64; k <<= 1) {
-            const int64_t t = __shfl_up(incl, k, 64);
-            if (lane >= k) incl += t;
-        }
-        const int64_t total = __shfl(incl, 63, 64);
-        if (carry + total > pos) {
-            const uint64_t hit = __ballot(carry + incl > pos);
-            const int j = __builtin_ctzll(hit);
-            b_out = b0 + j;
-            start_out = carry + __shfl(incl - n, j, 64);
-            return;
-        }
-        carry += total;
-    }
-    b_out = p.num_seqs;
-    start_out = carry;
-}
-
-// First tile of wave w's range.
-__device__ __forceinline__ int64_t range_start(int64_t w, int64_t N, int64_t W) {
-    return w * N / W;
-}
-
-// Partial slots of wave w: slot 0 holds its first segment when incomplete,
-// slot 1 its last one when incomplete (a middle segment is always complete).
-__device__ __forceinline__ int64_t part_row(const DecodeParams& p, int64_t w, int slot) {
-    return (w * 2 + slot) * p.group;
-}
-
-// Wave holding global tile t: the largest w with floor(w*N/W) <= t.
-__device__ __forceinline__ int64_t tile_owner(int64_t t, int64_t N, int64_t W) {
-    return ((t + 1) * W + N - 1) / N - 1;
-}
-
-// Partial row of wave wv's piece of the segment starting at global tile
-// seg0, whose first tile wave w0 owns, or -1 when wv's range is empty
-// (possible only when N < W).  The owner's range may start before the
-// segment (its piece is then the range's last one: slot 1); a later wave's
-// range starts inside the segment (slot 0).
-__device__ __forceinline__ int piece_row(const DecodeParams& p, int64_t wv, int64_t w0,
-                                         int64_t seg0, int64_t N, int64_t W) {
-    if (wv == w0) return (int)part_row(p, wv, range_start(wv, N, W) >= seg0 ? 0 : 1);
-    if (N < W && range_start(wv, N, W) == range_start(wv + 1, N, W)) return -1;
-    return (int)part_row(p, wv, 0);
-}
-
-// ---------------------------------------------------------------------------
 // Split pass: persistent waves, one contiguous range of tiles each
 // ---------------------------------------------------------------------------
 template <int D, bool FP8, bool UNIFORM, bool CAP>
@@ -502,9 +344,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kDecodeOccup
 void decode_split_kernel(DecodeParams p) {
     constexpr int KK = D / 32;                  // QK MFMAs per 16-token half
     constexpr int VE = D / 16;                  // PV MFMAs per tile
-#if !PA_DECODE_KLDS
-    constexpr int SUB = kDecodeSub;
-#endif
 
     const int lane = threadIdx.x;
     const int c = lane & 15;
@@ -514,16 +353,16 @@ void decode_split_kernel(DecodeParams p) {
     const int64_t w = blockIdx.x;
 
     __shared__ int sm_pages[kMaxSplitPages];
-#if PA_DECODE_KLDS
     __shared__ __attribute__((aligned(16))) uint8_t sm_k[kTile * KRowRegs<D, FP8>::kLdsStride];
-#endif
 
     const int64_t N = total_tiles(p);
-    if (w == 0 && lane == 0) p.seq_tile0[p.num_seqs] = N;
-
     const int64_t r0 = range_start(w, N, W);
     const int64_t r1 = range_start(w + 1, N, W);
-    if (r0 >= r1) return;
+    if (r0 >= r1) {
+        // an empty range (N < W): the merge may read this wave's slot 0
+        if (lane < G) p.part_lse[part_row(p, w, 0) + lane] = -INFINITY;
+        return;
+    }
 
     int b;
     int64_t seq_start;
@@ -544,7 +383,13 @@ void decode_split_kernel(DecodeParams p) {
         const int64_t seg_end = seq_start + (int64_t)(kvh + 1) * n;
         const int cnt = (int)(min(r1, seg_end) - pos);
         const bool complete = (i0 == 0) && (cnt == n);
-        if (kvh == 0 && i0 == 0 && lane == 0) p.seq_tile0[b] = seq_start;
+        if (i0 == 0 && lane == 0) {
+            // this wave owns the segment's first tile: tell the merge which
+            // waves cover it
+            const int64_t w_last = complete ? w : tile_owner(seg_end - 1, N, W);
+            *reinterpret_cast<int4*>(p.seg_rec + 4 * ((int64_t)b * p.num_kv_heads + kvh)) =
+                int4{(int)w, (int)w_last, slot, 0};
+        }
 
         // ---- Q^T as the B operand: column c = query head kvh*G + c ----
         // The contraction index (grp, j) of MFMA kk stands for d = dq(kk, grp)
@@ -573,7 +418,6 @@ void decode_split_kernel(DecodeParams p) {
         x.tok_bytes = (int)(p.s_tok * kElem);
         {
             const int head = (int)(kvh * p.s_head * kElem);
-            x.k_lane = head + 16 * grp + (UNIFORM ? c * x.tok_bytes : 0);
             using KR = KRowRegs<D, FP8>;
             x.k_row = lane / KR::kLanesPerRow;
             x.k_row_lane = head + 16 * (lane % KR::kLanesPerRow) +
@@ -601,11 +445,11 @@ void decode_split_kernel(DecodeParams p) {
             }
             __syncthreads();
 
-#if PA_DECODE_KLDS
             // K rows are loaded whole (nontemporal) and transposed through the
-            // wave's LDS tile; the registers are free for the next tile's K as
-            // soon as they are staged, V rotates as below.  The last tile is
-            // peeled off so the steady loop issues its loads unconditionally.
+            // wave's LDS tile, so their registers take the next tile's K as
+            // soon as they are staged; V's registers take the next tile's V
+            // once P*V is done.  The last tile is peeled off so the steady
+            // loop issues its loads unconditionally (exact load counters).
             {
                 KRowRegs<D, FP8> kr;
                 VRegs<D, FP8> vr;
@@ -635,57 +479,6 @@ void decode_split_kernel(DecodeParams p) {
                 tile_pv<D, FP8>(acc, vr, pop, x, t0, full);
                 __syncthreads();
             }
-#else
-            // K and V rotate through one register set each, holding SUB
-            // consecutive tiles: the next step's K rows are requested as soon
-            // as this step's scores are formed and its V rows as soon as this
-            // step's P*V is done.  The last step is peeled off so that the
-            // steady-state loop issues its loads unconditionally (exact load
-            // counters); a missing tile of the last step is loaded as a repeat
-            // of the chunk's last tile and not consumed.
-            KRegs<D, FP8> kr[SUB];
-            VRegs<D, FP8> vr[SUB];
-            const int steps = (ct + SUB - 1) / SUB;
-            auto tile_t0 = [&](int i) { return tile0 + min(i, ct - 1) * kTile; };
-#pragma unroll
-            for (int u = 0; u < SUB; ++u) issue_k<D, FP8, UNIFORM>(kr[u], p, x, tile_t0(u));
-#pragma unroll
-            for (int u = 0; u < SUB; ++u) issue_v<D, FP8, UNIFORM>(vr[u], p, x, tile_t0(u));
-            for (int st = 0; st + 1 < steps; ++st) {
-                f32x4 s[SUB][2];
-#pragma unroll
-                for (int u = 0; u < SUB; ++u) tile_scores<D, FP8>(s[u], kr[u], qop);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int u = 0; u < SUB; ++u)
-                    issue_k<D, FP8, UNIFORM>(kr[u], p, x, tile_t0((st + 1) * SUB + u));
-#pragma unroll
-                for (int u = 0; u < SUB; ++u) {
-                    const int t0 = tile_t0(st * SUB + u);
-                    const bool full = (t0 >= x.t_begin) && (t0 + kTile <= x.t_end);
-                    const u32x4 pop = tile_softmax<D, CAP>(acc, s[u], p, x, t0, full);
-                    tile_pv<D, FP8>(acc, vr[u], pop, x, t0, full);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int u = 0; u < SUB; ++u)
-                    issue_v<D, FP8, UNIFORM>(vr[u], p, x, tile_t0((st + 1) * SUB + u));
-            }
-            {
-                const int st = steps - 1;
-#pragma unroll
-                for (int u = 0; u < SUB; ++u) {
-                    if (st * SUB + u < ct) {
-                        const int t0 = tile_t0(st * SUB + u);
-                        const bool full = (t0 >= x.t_begin) && (t0 + kTile <= x.t_end);
-                        f32x4 s[2];
-                        tile_scores<D, FP8>(s, kr[u], qop);
-                        const u32x4 pop = tile_softmax<D, CAP>(acc, s, p, x, t0, full);
-                        tile_pv<D, FP8>(acc, vr[u], pop, x, t0, full);
-                    }
-                }
-            }
-#endif
         }
 
         // ---- finish the piece: sum over the 4 lanes of each column, then
@@ -737,129 +530,6 @@ void decode_split_kernel(DecodeParams p) {
     }
 }
 
-// ---------------------------------------------------------------------------
-// Merge: one block per (segment, query-head row r).  Segments inside one
-// wave's range were written by the split pass; the others are combined here
-// from the partials of the waves that cover them,
-//   out = sum_i 2^(lse_i - M) o_i / sum_i 2^(lse_i - M)    (`_fwd_kernel_stage2`).
-// Threads are (column quad q, piece lane pl): each folds the pieces
-// pl, pl + kR, ... of its four columns into a running (max, sum, acc) --
-// the log-sum-exp values and the partial rows are loaded in the same round --
-// and the kR piece lanes are then combined through LDS.  Sequences with no
-// keys get zero rows.
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int num_workers) {
-    constexpr int kQ = D / 4;                // threads per row, 4 columns each
-    constexpr int kR = 256 / kQ;             // piece lanes
-    constexpr int kBatch = 4;                // pieces in flight per thread
-    const int G = p.group;
-    const int r = blockIdx.x % G;
-    const int seg = blockIdx.x / G;
-    const int kvh = seg % p.num_kv_heads;
-    const int b = seg / p.num_kv_heads;
-    const int q = threadIdx.x % kQ, pl = threadIdx.x / kQ;
-    const SeqRange sr = seq_range(p, b);
-    uint16_t* out = static_cast<uint16_t*>(p.out) + (int64_t)b * p.out_stride_b +
-                    (int64_t)(kvh * G + r) * D + 4 * q;
-    if (sr.tiles == 0) {
-        if (pl == 0) *reinterpret_cast<u32x2*>(out) = u32x2{0u, 0u};
-        return;
-    }
-    // N tiles in all and the first global tile of this segment, as the split
-    // pass found them
-    const int64_t N = p.seq_tile0[p.num_seqs];
-    const int64_t seg0 = p.seq_tile0[b] + (int64_t)kvh * sr.tiles;
-    const int64_t W = num_workers;
-    const int64_t w0 = tile_owner(seg0, N, W), w1 = tile_owner(seg0 + sr.tiles - 1, N, W);
-    if (w0 == w1) return;                    // written whole by one wave
-    const int64_t npieces = w1 - w0 + 1;
-
-    float m = -INFINITY, sum = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int64_t i0 = pl; i0 < npieces; i0 += kR * kBatch) {
-        float lse[kBatch];
-        f32x4 o[kBatch];
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int64_t i = i0 + (int64_t)kR * u;
-            const int row = i < npieces ? piece_row(p, w0 + i, w0, seg0, N, W) : -1;
-            lse[u] = -INFINITY;
-            o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (row >= 0) {
-                lse[u] = p.part_lse[row + r];
-                o[u] = *reinterpret_cast<const f32x4*>(p.part_o + (int64_t)(row + r) * D + 4 * q);
-            }
-        }
-        float bm = lse[0];
-#pragma unroll
-        for (int u = 1; u < kBatch; ++u) bm = fmaxf(bm, lse[u]);
-        if (bm == -INFINITY) continue;
-        const float mn = fmaxf(m, bm);
-        const float f = m == -INFINITY ? 0.f : fast_exp2(m - mn);
-        sum *= f;
-        acc *= f;
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const float w = lse[u] == -INFINITY ? 0.f : fast_exp2(lse[u] - mn);
-            sum += w;
-            acc += w * o[u];
-        }
-        m = mn;
-    }
-
-    __shared__ float sm_m[kR], sm_s[kR];
-    __shared__ f32x4 sm_acc[kR][kQ];
-    if (q == 0) {
-        sm_m[pl] = m;
-        sm_s[pl] = sum;
-    }
-    sm_acc[pl][q] = acc;
-    __syncthreads();
-    if (pl == 0) {
-        float M = sm_m[0];
-#pragma unroll
-        for (int j = 1; j < kR; ++j) M = fmaxf(M, sm_m[j]);
-        float S = 0.f;
-        f32x4 a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < kR; ++j) {
-            const float f = sm_m[j] == -INFINITY ? 0.f : fast_exp2(sm_m[j] - M);
-            S += f * sm_s[j];
-            a += f * sm_acc[j][q];
-        }
-        const float inv = 1.f / S;
-        *reinterpret_cast<u32x2*>(out) =
-            u32x2{pack_bf16x2(a.x * inv, a.y * inv), pack_bf16x2(a.z * inv, a.w * inv)};
-    }
-}
-
-// Copy every cached row of every sequence to a dense [sum L, Hkv, D] array
-// through row_ptr (the address path of the attention kernels).
-template <int D, bool FP8>
-__global__ __launch_bounds__(256) void gather_kernel(GatherParams p) {
-    constexpr int kRowBytes = D * (FP8 ? 1 : 2);
-    constexpr int kChunks = kRowBytes / 16;
-    const int kvh = blockIdx.x;
-    const int b = blockIdx.y;
-    int64_t off = 0;
-    for (int i = 0; i < b; ++i) off += p.seq_lens[i];
-    const int L = p.seq_lens[b];
-    const int pmask = (1 << p.page_shift) - 1;
-    const int32_t* bt_row = p.block_table + (int64_t)b * p.bt_stride;
-    for (int idx = threadIdx.x; idx < L * kChunks; idx += 256) {
-        const int t = idx / kChunks, ch = idx % kChunks;
-        const int64_t pg = bt_row[t >> p.page_shift];
-        const int64_t dst = ((off + t) * p.num_kv_heads + kvh) * kRowBytes + 16 * ch;
-        const uint8_t* ks = row_ptr<FP8>(p.k_pool, pg, t & pmask, kvh, p.s_page, p.s_tok, p.s_head);
-        const uint8_t* vs = row_ptr<FP8>(p.v_pool, pg, t & pmask, kvh, p.s_page, p.s_tok, p.s_head);
-        *reinterpret_cast<u32x4*>(static_cast<uint8_t*>(p.k_out) + dst) =
-            *reinterpret_cast<const u32x4*>(ks + 16 * ch);
-        *reinterpret_cast<u32x4*>(static_cast<uint8_t*>(p.v_out) + dst) =
-            *reinterpret_cast<const u32x4*>(vs + 16 * ch);
-    }
-}
-
 template <int D, bool FP8, bool UNIFORM>
 hipError_t launch_decode_t(const DecodeParams& p, int workers, hipStream_t stream) {
     dim3 grid(workers);
@@ -906,28 +576,6 @@ hipError_t decode_waves_per_cu(int head_dim, bool fp8, bool uniform_pages, int* 
                 : (uniform_pages ? split_kernel_ptr<64, false, true>()
                                  : split_kernel_ptr<64, false, false>());
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, f, 64, 0);
-}
-
-hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, int workers, int B,
-                               int Hkv, hipStream_t stream) {
-    dim3 grid((unsigned)B * Hkv * p.group);
-    if (head_dim == 128)
-        hipLaunchKernelGGL(decode_merge_kernel<128>, grid, dim3(256), 0, stream, p, workers);
-    else
-        hipLaunchKernelGGL(decode_merge_kernel<64>, grid, dim3(256), 0, stream, p, workers);
-    return hipGetLastError();
-}
-
-hipError_t launch_gather(const GatherParams& p, int head_dim, bool fp8, hipStream_t stream) {
-    dim3 grid(p.num_kv_heads, p.num_seqs);
-    if (head_dim == 128) {
-        if (fp8) hipLaunchKernelGGL((gather_kernel<128, true>), grid, dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL((gather_kernel<128, false>), grid, dim3(256), 0, stream, p);
-    } else {
-        if (fp8) hipLaunchKernelGGL((gather_kernel<64, true>), grid, dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL((gather_kernel<64, false>), grid, dim3(256), 0, stream, p);
-    }
-    return hipGetLastError();
 }
 
 }  // namespace pa

@@ -1,0 +1,104 @@
+// decode_geom.h -- where the decode kernels find things: the address of a
+// cached row, and the stream-K cut of all (sequence, kv head) key ranges
+// into the split pass's per-wave tile ranges.  Shared by the split pass, the
+// merge and the gather.
+//
+// A segment is one (sequence b, kv head g): the 32-token tiles from
+// base = lo rounded down to 32 that cover the key range [lo, L), lo = L - W
+// under a sliding window W.  Segments are laid end to end, sequence-major and
+// kv head minor, into one list of N tiles; wave w of W owns the tiles
+// [floor(w*N/W), floor((w+1)*N/W)).
+#pragma once
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+// Address of (page, row, head) of a pool, strides in elements.
+template <bool FP8>
+__device__ __forceinline__ const uint8_t* row_ptr(const void* pool, int64_t page, int row,
+                                                  int head, int64_t s_page, int64_t s_tok,
+                                                  int64_t s_head) {
+    constexpr int64_t kElem = FP8 ? 1 : 2;
+    return static_cast<const uint8_t*>(pool) +
+           (page * s_page + (int64_t)row * s_tok + (int64_t)head * s_head) * kElem;
+}
+
+struct SeqRange {
+    int L, lo, base, tiles;   // tiles: 32-token tiles from base covering [lo, L)
+};
+
+__device__ __forceinline__ SeqRange seq_range(const DecodeParams& p, int b) {
+    SeqRange r;
+    r.L = p.seq_lens[b];
+    r.lo = (p.window > 0 && r.L > p.window) ? r.L - p.window : 0;
+    r.base = r.lo & ~(kTile - 1);
+    r.tiles = r.L > r.lo ? (r.L - r.base + kTile - 1) / kTile : 0;
+    return r;
+}
+
+__device__ __forceinline__ int64_t wave_sum64(int64_t v) {
+#pragma unroll
+    for (int k = 32; k >= 1; k >>= 1) v += __shfl_xor(v, k, 64);
+    return v;
+}
+
+// Total tiles N over all segments (every lane gets the sum).
+__device__ __forceinline__ int64_t total_tiles(const DecodeParams& p) {
+    const int lane = __lane_id();
+    int64_t n = 0;
+    for (int b0 = 0; b0 < p.num_seqs; b0 += 64) {
+        const int b = b0 + lane;
+        n += b < p.num_seqs ? (int64_t)seq_range(p, b).tiles : 0;
+    }
+    return wave_sum64(n) * p.num_kv_heads;
+}
+
+// Sequence whose segments contain global tile `pos` (< N), and the global
+// index of its first tile.  Sequences without tiles are skipped.
+__device__ __forceinline__ void find_seq(const DecodeParams& p, int64_t pos, int& b_out,
+                                         int64_t& start_out) {
+    const int lane = __lane_id();
+    int64_t carry = 0;
+    for (int b0 = 0; b0 < p.num_seqs; b0 += 64) {
+        const int b = b0 + lane;
+        int64_t n = b < p.num_seqs ? (int64_t)seq_range(p, b).tiles * p.num_kv_heads : 0;
+        // inclusive scan across the wave
+        int64_t incl = n;
+#pragma unroll
+        for (int k = 1; k < 64; k <<= 1) {
+            const int64_t t = __shfl_up(incl, k, 64);
+            if (lane >= k) incl += t;
+        }
+        const int64_t total = __shfl(incl, 63, 64);
+        if (carry + total > pos) {
+            const uint64_t hit = __ballot(carry + incl > pos);
+            const int j = __builtin_ctzll(hit);
+            b_out = b0 + j;
+            start_out = carry + __shfl(incl - n, j, 64);
+            return;
+        }
+        carry += total;
+    }
+    b_out = p.num_seqs;
+    start_out = carry;
+}
+
+// First tile of wave w's range.
+__device__ __forceinline__ int64_t range_start(int64_t w, int64_t N, int64_t W) {
+    return w * N / W;
+}
+
+// Partial slots of wave w: slot 0 holds its first segment when incomplete,
+// slot 1 its last one when incomplete (a middle segment is always complete).
+__device__ __forceinline__ int64_t part_row(const DecodeParams& p, int64_t w, int slot) {
+    return (w * 2 + slot) * p.group;
+}
+
+// Wave holding global tile t: the largest w with floor(w*N/W) <= t.
+__device__ __forceinline__ int64_t tile_owner(int64_t t, int64_t N, int64_t W) {
+    return ((t + 1) * W + N - 1) / N - 1;
+}
+
+}  // namespace pa

@@ -11,16 +11,6 @@ namespace pa {
 constexpr int kTile = 32;
 // Upper bound on the persistent split-pass waves (a forced count included).
 constexpr int kMaxWorkers = 1 << 20;
-// Tiles of 32 tokens a decode wave keeps in flight per pipeline step.
-#ifndef PA_DECODE_SUB
-#define PA_DECODE_SUB 1
-#endif
-constexpr int kDecodeSub = PA_DECODE_SUB;
-// K rows loaded whole and transposed through LDS (1) or loaded straight into
-// the MFMA operand layout (0).
-#ifndef PA_DECODE_KLDS
-#define PA_DECODE_KLDS 1
-#endif
 #ifndef PA_DECODE_OCCUPANCY
 #define PA_DECODE_OCCUPANCY 2
 #endif
@@ -53,8 +43,9 @@ struct DecodeParams {
     int64_t out_stride_b;
     float* part_o;            // [workers, 2, G, D]: partial of a segment a wave covers in part
     float* part_lse;          // [workers, 2, G] (log2 domain)
-    int64_t* seq_tile0;       // [B + 1]: first global tile of sequence b (written when it
-                              // has tiles); entry B = all tiles.  Split pass -> merge.
+    int32_t* seg_rec;         // [B * Hkv][4]: for a segment with keys, the waves owning its
+                              // first and last tile and the first one's slot (written by
+                              // the owner of the first tile).  Split pass -> merge.
 };
 
 struct GatherParams {
@@ -94,7 +85,7 @@ struct ExtendParams {
 
 hipError_t launch_decode(const DecodeParams& p, int head_dim, bool fp8, bool uniform_pages,
                          int workers, hipStream_t stream);
-hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, int workers, int num_seqs,
+hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, int num_seqs,
                                int num_kv_heads, hipStream_t stream);
 // Resident split-pass waves per compute unit (occupancy of the kernel variant).
 hipError_t decode_waves_per_cu(int head_dim, bool fp8, bool uniform_pages, int* out);
