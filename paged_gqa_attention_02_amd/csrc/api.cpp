@@ -52,6 +52,11 @@ pa_status check_problem(const pa_problem& pr) {
     if (pr.mode == PA_MODE_EXTEND) {
         if (pr.total_q < 0 || pr.max_q_len < 0) return PA_ERR_INVALID_SHAPE;
         if (pr.num_seqs > 0 && pr.total_q > 0 && pr.max_q_len == 0) return PA_ERR_INVALID_SHAPE;
+        // key positions are 32-bit, and the grid is (row tiles x sequences x kv heads)
+        if ((int64_t)pr.max_kv_len + pr.max_q_len >= ((int64_t)1 << 30)) return PA_ERR_UNSUPPORTED;
+        const int64_t tiles = cdiv((int64_t)pr.max_q_len * (pr.num_q_heads / pr.num_kv_heads),
+                                   extend_rows_per_block());
+        if (tiles * pr.num_seqs * pr.num_kv_heads >= ((int64_t)1 << 31)) return PA_ERR_UNSUPPORTED;
     }
     return PA_OK;
 }
@@ -367,7 +372,43 @@ pa_status paged_attn_extend(const pa_plan* plan, const void* q, const void* k_ne
         return PA_ERR_MISALIGNED;
     if (!isfinite(scale) || !isfinite(softcap) || !isfinite(k_scale) || !isfinite(v_scale))
         return PA_ERR_INVALID_SHAPE;
-    return PA_ERR_UNSUPPORTED;  // extend kernel not built yet
+
+    ExtendParams p;
+    memset(&p, 0, sizeof p);
+    p.q = q;
+    p.k_new = k_new;
+    p.v_new = v_new;
+    p.cu_seqlens_q = cu_seqlens_q;
+    p.ctx_lens = ctx_lens;
+    p.k_pool = k_pool;
+    p.v_pool = v_pool;
+    p.s_page = kv_stride_page;
+    p.s_tok = kv_stride_tok;
+    p.s_head = kv_stride_head;
+    p.block_table = block_table;
+    p.bt_stride = bt_stride;
+    p.num_seqs = pr.num_seqs;
+    p.num_q_heads = pr.num_q_heads;
+    p.num_kv_heads = pr.num_kv_heads;
+    p.group = pr.num_q_heads / pr.num_kv_heads;
+    p.page_shift = ilog2(pr.page_size);
+    p.window = pr.window;
+    p.q_tiles = (int32_t)cdiv((int64_t)pr.max_q_len * p.group, extend_rows_per_block());
+    const float kl2e = 1.4426950408889634f;
+    p.has_cap = softcap > 0.f;
+    p.qk_scale2 = scale * kl2e;
+    p.qk_scale2_ctx = scale * k_scale * kl2e;
+    if (p.has_cap) {
+        p.cap_c1 = 2.f * scale * kl2e / softcap;
+        p.cap_c1_ctx = 2.f * scale * k_scale * kl2e / softcap;
+        p.cap_c2 = softcap * kl2e;
+    }
+    p.v_scale = v_scale;
+    p.out = out;
+    if (launch_extend(p, pr.head_dim, pr.kv_dtype == PA_KV_FP8_E4M3, pr.num_seqs,
+                      static_cast<hipStream_t>(hip_stream)) != hipSuccess)
+        return PA_ERR_HIP;
+    return PA_OK;
 }
 
 }  // extern "C"

@@ -71,10 +71,10 @@ struct ExtendParams {
     int64_t s_page, s_tok, s_head;
     const int32_t* block_table;
     int64_t bt_stride;
-    int32_t num_q_heads, num_kv_heads, group;
+    int32_t num_seqs, num_q_heads, num_kv_heads, group;
     int32_t page_shift;
     int32_t window;
-    int32_t q_tiles;          // grid x bound: ceil(max_q_len / rows_per_tile)
+    int32_t q_tiles;          // row tiles per (sequence, kv head): ceil(max_q_len * G / rows)
     int32_t has_cap;
     float qk_scale2;          // scale * log2(e), for new (bf16) keys
     float qk_scale2_ctx;      // scale * k_scale * log2(e), for cached keys
@@ -92,5 +92,7 @@ hipError_t decode_waves_per_cu(int head_dim, bool fp8, bool uniform_pages, int* 
 hipError_t launch_gather(const GatherParams& p, int head_dim, bool fp8, hipStream_t stream);
 hipError_t launch_extend(const ExtendParams& p, int head_dim, bool fp8, int num_seqs,
                          hipStream_t stream);
+// Rows (new token, query head) one extend block covers.
+int extend_rows_per_block();
 
 }  // namespace pa
