@@ -61,4 +61,25 @@ __device__ __forceinline__ T shfl_xor(T v, int mask) {
     return __shfl_xor(v, mask, 64);
 }
 
+// Max / sum over the four lanes l, l^16, l^32, l^48 (one MFMA column), with
+// the gfx950 lane swaps: permlane32_swap(v, v) leaves v's two 32-lane halves
+// in its two results, permlane16_swap(v, v) the two 16-lane rows of each
+// pair; combining the two results of each step reduces over the pair.
+__device__ __forceinline__ float col4_max(float v) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float col4_sum(float v) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 }  // namespace pa
