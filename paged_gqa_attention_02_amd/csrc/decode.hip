@@ -278,9 +278,13 @@ __device__ __forceinline__ u32x4 tile_softmax(Acc<D>& A, const f32x4 s[2],
     float tmax = sc[0];
 #pragma unroll
     for (int j = 1; j < 8; ++j) tmax = fmaxf(tmax, sc[j]);
-    tmax = fmaxf(tmax, shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-    const float m_new = fmaxf(A.m, tmax);
+    tmax = col4_max(tmax);
+    // Lazy rescale: a head's reference max m moves only when a score exceeds
+    // it by more than kSlack (log2 units), so p <= 2^kSlack and O is rescaled
+    // on few tiles (every tile has a valid key, so the first one moves m).
+    constexpr float kSlack = 8.f;
+    const bool move = __any(tmax > A.m + kSlack);
+    const float m_new = move ? fmaxf(A.m, tmax) : A.m;
     const float alpha = fast_exp2(A.m - m_new);
     float pr[8];
     float psum = 0.f;
@@ -291,14 +295,16 @@ __device__ __forceinline__ u32x4 tile_softmax(Acc<D>& A, const f32x4 s[2],
     }
     A.l = A.l * alpha + psum;
     A.m = m_new;
-    // rescale O: row 4*grp + j belongs to head column 4*grp + j
-    float arow[4];
+    if (move) {
+        // rescale O: row 4*grp + j belongs to head column 4*grp + j
+        float arow[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) arow[j] = __shfl(alpha, 4 * x.grp + j, 64);
+        for (int j = 0; j < 4; ++j) arow[j] = __shfl(alpha, 4 * x.grp + j, 64);
 #pragma unroll
-    for (int e = 0; e < VE; ++e)
+        for (int e = 0; e < VE; ++e)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) A.o[e][j] *= arow[j];
+            for (int j = 0; j < 4; ++j) A.o[e][j] *= arow[j];
+    }
     return u32x4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
                  pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])};
 }
@@ -483,8 +489,7 @@ void decode_split_kernel(DecodeParams p) {
 
         // ---- finish the piece: sum over the 4 lanes of each column, then
         // row r = 4*grp + j of O (head of column r) is normalised and stored ----
-        float l_tot = acc.l + shfl_xor(acc.l, 16);
-        l_tot += shfl_xor(l_tot, 32);
+        const float l_tot = col4_sum(acc.l);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = 4 * grp + j;
