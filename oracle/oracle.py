@@ -37,6 +37,11 @@ def bind(path: str):
     L.orc_bf16.restype = d
     L.orc_e4m3fn.argtypes = [ctypes.c_uint8]
     L.orc_e4m3fn.restype = d
+    L.orc_e4m3fn_encode.argtypes = [ctypes.c_float]
+    L.orc_e4m3fn_encode.restype = ctypes.c_uint8
+    L.orc_cache_append.argtypes = [i64, i, i, i, i, p, p, i64, p, p, i64, i64, i64, i64, p,
+                                   ctypes.c_float, ctypes.c_float]
+    L.orc_cache_append.restype = i
     return L
 
 
@@ -99,6 +104,29 @@ def extend(case, rows: Optional[np.ndarray] = None,
     if rc != 0:
         raise RuntimeError(f"orc_extend failed: {rc}")
     return out
+
+
+def encode_e4m3fn(x: float, clib=None) -> int:
+    """e4m3fn code nearest to the float32 x (ties to even, saturating)."""
+    return (clib or lib()).orc_e4m3fn_encode(x)
+
+
+def cache_append(key: np.ndarray, value: np.ndarray, k_pool: np.ndarray,
+                 v_pool: np.ndarray, slot_mapping: np.ndarray, kv_dtype: str,
+                 k_scale: float = 1.0, v_scale: float = 1.0, clib=None):
+    """Cache append of bf16 key/value bits [T, Hkv, D] into copies of the
+    pools [num_pages, P, Hkv, D] (uint16 or uint8 bits) at int64 slots;
+    returns the new pools."""
+    T, Hkv, D = key.shape
+    kp, vp = np.array(k_pool, copy=True), np.array(v_pool, copy=True)
+    num_pages, P = kp.shape[0], kp.shape[1]
+    kb, vb, sm = _c(key), _c(value), _c(np.asarray(slot_mapping, dtype=np.int64))
+    rc = (clib or lib()).orc_cache_append(T, Hkv, D, P, _KV[kv_dtype], _ptr(kb), _ptr(vb),
+                                          Hkv * D, _ptr(kp), _ptr(vp), P * Hkv * D, Hkv * D, D,
+                                          num_pages, _ptr(sm), k_scale, v_scale)
+    if rc != 0:
+        raise RuntimeError(f"orc_cache_append failed: {rc}")
+    return kp, vp
 
 
 def decode_bf16(bits: int, clib=None) -> float:

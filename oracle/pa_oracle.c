@@ -50,6 +50,17 @@
  *           the final `acc / l_i` of `_fwd_kernel_flash_attn_v2`).  The cache
  *           scales apply to cached keys/values only; new rows are bf16.
  *
+ *  append   The cache write that precedes attention (`do_kv_cache_update` on
+ *           the vLLM "b12x" backend page, which hands key, value, the
+ *           caches, `slot_mapping` and the k/v scales to
+ *           `reshape_and_cache_flash`): new token i goes to flat slot
+ *           s = slot_mapping[i] -- page s / P, row s % P -- for every kv head;
+ *           s < 0 marks a padding token that is not written.  A bf16 cache
+ *           receives the bf16 element unchanged; an e4m3fn cache receives
+ *           enc(x / scale), the quotient a correctly rounded fp32 division
+ *           and enc the nearest e4m3fn value (ties to the even code,
+ *           magnitudes past 448 saturating to 448, NaN to NaN).
+ *
  * Element decoding:
  *   bf16    the 16 bits are the high half of an IEEE binary32.
  *   e4m3fn  OCP 8-bit float: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa
@@ -457,4 +468,67 @@ int orc_extend(int B, int Hq, int Hkv, int D, int P, int kv_dtype,
     if (!rows)
         n_rows = cu_seqlens_q[B];
     return run_jobs(&pr, 1, n_rows * Hq, max_keys, threads);
+}
+
+/* e4m3fn code nearest to the float x: the table of the 127 finite
+ * non-negative codes is searched for the closest magnitude (ties go to the
+ * even code); NaN keeps its sign with the NaN code, everything past the
+ * largest finite value lands on it. */
+uint8_t orc_e4m3fn_encode(float x)
+{
+    uint8_t sign = signbit(x) ? 0x80 : 0x00;
+    double a = fabs((double)x);
+    int best = 0, c;
+    double best_d = INFINITY;
+    if (isnan(x))
+        return (uint8_t)(sign | 0x7F);
+    if (a > 448.0)          /* saturation (the distances would lose precision) */
+        a = 448.0;
+    for (c = 0; c <= 0x7E; ++c) {
+        double d = fabs(orc_e4m3fn((uint8_t)c) - a);
+        if (d < best_d || (d == best_d && (c & 1) == 0 && (best & 1) == 1)) {
+            best_d = d;
+            best = c;
+        }
+    }
+    return (uint8_t)(sign | best);
+}
+
+/* Cache append: key/value bf16 rows [num_tokens, Hkv, D] with token stride
+ * `row_stride` elements; the pools as in decode (strides in elements). */
+int orc_cache_append(int64_t num_tokens, int Hkv, int D, int P, int kv_dtype,
+                     const uint16_t *key, const uint16_t *value, int64_t row_stride,
+                     void *k_pool, void *v_pool, int64_t s_page, int64_t s_tok,
+                     int64_t s_head, int64_t num_pages, const int64_t *slot_mapping,
+                     float k_scale, float v_scale)
+{
+    int64_t i;
+    if (num_tokens < 0 || Hkv < 1 || D < 1 || P < 1 ||
+        (kv_dtype != ORC_KV_BF16 && kv_dtype != ORC_KV_E4M3FN))
+        return -1;
+    for (i = 0; i < num_tokens; ++i) {
+        int64_t slot = slot_mapping[i], page, off;
+        int h, d;
+        if (slot < 0)
+            continue;
+        page = slot / P;
+        if (page >= num_pages)
+            return -2;
+        for (h = 0; h < Hkv; ++h) {
+            off = page * s_page + (slot % P) * s_tok + (int64_t)h * s_head;
+            for (d = 0; d < D; ++d) {
+                uint16_t kb = key[i * row_stride + (int64_t)h * D + d];
+                uint16_t vb = value[i * row_stride + (int64_t)h * D + d];
+                if (kv_dtype == ORC_KV_BF16) {
+                    ((uint16_t *)k_pool)[off + d] = kb;
+                    ((uint16_t *)v_pool)[off + d] = vb;
+                } else {
+                    float kf = (float)orc_bf16(kb), vf = (float)orc_bf16(vb);
+                    ((uint8_t *)k_pool)[off + d] = orc_e4m3fn_encode(kf / k_scale);
+                    ((uint8_t *)v_pool)[off + d] = orc_e4m3fn_encode(vf / v_scale);
+                }
+            }
+        }
+    }
+    return 0;
 }

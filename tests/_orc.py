@@ -19,5 +19,11 @@ class Oracle:
     def decode_e4m3fn(self, bits):
         return oracle.decode_e4m3fn(bits, clib=self.clib)
 
+    def encode_e4m3fn(self, x):
+        return oracle.encode_e4m3fn(x, clib=self.clib)
+
+    def cache_append(self, *args, **kw):
+        return oracle.cache_append(*args, clib=self.clib, **kw)
+
     brute_decode = staticmethod(oracle.brute_decode)
     brute_extend = staticmethod(oracle.brute_extend)

@@ -326,3 +326,92 @@ def test_oracle_thread_count_independent(oracle_mod):
     a, _ = oracle_mod.decode(case, threads=1)
     b, _ = oracle_mod.decode(case, threads=5)
     np.testing.assert_array_equal(a, b)
+
+
+# ---------------------------------------------------------------- cache append
+def test_e4m3fn_encode_round_trips_every_code(oracle_mod):
+    """Every finite code (both signs, both zeros) is its own nearest value."""
+    for c in range(256):
+        if c & 0x7F == 0x7F:
+            continue
+        x = float(np.float32(oracle_mod.decode_e4m3fn(c)))
+        if c == 0x80:
+            x = -0.0
+        assert oracle_mod.encode_e4m3fn(x) == c, hex(c)
+
+
+def test_e4m3fn_encode_ties_to_even(oracle_mod):
+    """The midpoint of two neighbouring codes goes to the even one."""
+    vals = [oracle_mod.decode_e4m3fn(c) for c in range(0x7F)]
+    for c in range(0x7E):
+        mid = (vals[c] + vals[c + 1]) / 2          # exact in float32
+        want = c if c % 2 == 0 else c + 1
+        assert oracle_mod.encode_e4m3fn(mid) == want, hex(c)
+        assert oracle_mod.encode_e4m3fn(-mid) == 0x80 | want, hex(c)
+
+
+def test_e4m3fn_encode_matches_torch(oracle_mod):
+    """Round to nearest even on random in-range floats, against torch's own
+    float32 -> float8_e4m3fn cast."""
+    rng = np.random.default_rng(11)
+    mag = np.exp(rng.uniform(np.log(2.0 ** -12), np.log(440.0), 4000))
+    x = (mag * rng.choice([-1.0, 1.0], mag.size)).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle_mod.encode_e4m3fn(float(v)) for v in x], dtype=np.uint8)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_e4m3fn_encode_saturates_and_keeps_nan(oracle_mod):
+    assert oracle_mod.encode_e4m3fn(449.0) == 0x7E
+    assert oracle_mod.encode_e4m3fn(1e30) == 0x7E
+    assert oracle_mod.encode_e4m3fn(float("-inf")) == 0xFE
+    assert oracle_mod.encode_e4m3fn(float("nan")) & 0x7F == 0x7F
+
+
+def _append_case(kv_dtype, seed, T=37, Hkv=4, D=64, P=16, num_pages=9):
+    rng = np.random.default_rng(seed)
+    key = I.bf16_bits(rng.standard_normal((T, Hkv, D), dtype=np.float32) * 3)
+    value = I.bf16_bits(rng.standard_normal((T, Hkv, D), dtype=np.float32) * 3)
+    pdt = np.uint16 if kv_dtype == "bf16" else np.uint8
+    info = np.iinfo(pdt)
+    k_pool = rng.integers(0, info.max, size=(num_pages, P, Hkv, D), dtype=pdt)
+    v_pool = rng.integers(0, info.max, size=(num_pages, P, Hkv, D), dtype=pdt)
+    slots = rng.permutation(num_pages * P)[:T].astype(np.int64)
+    slots[::5] = -1                                 # padding tokens
+    return key, value, k_pool, v_pool, slots
+
+
+def test_cache_append_bf16_round_trip(oracle_mod):
+    """A bf16 cache holds the new rows unchanged at their slots; every other
+    row (including the slots of padding tokens) keeps its old bits."""
+    key, value, k_pool, v_pool, slots = _append_case("bf16", 21)
+    kp, vp = oracle_mod.cache_append(key, value, k_pool, v_pool, slots, "bf16")
+    P = k_pool.shape[1]
+    live = slots >= 0
+    np.testing.assert_array_equal(kp[slots[live] // P, slots[live] % P], key[live])
+    np.testing.assert_array_equal(vp[slots[live] // P, slots[live] % P], value[live])
+    mask = np.ones(k_pool.shape[:2], dtype=bool)
+    mask[slots[live] // P, slots[live] % P] = False
+    np.testing.assert_array_equal(kp[mask], k_pool[mask])
+    np.testing.assert_array_equal(vp[mask], v_pool[mask])
+
+
+def test_cache_append_fp8_quantises_quotient(oracle_mod):
+    """An e4m3fn cache holds the new rows divided by their scale (float32) and
+    cast to e4m3fn (torch's cast as the reference)."""
+    key, value, k_pool, v_pool, slots = _append_case("fp8_e4m3", 22)
+    ks, vs = 0.75, 1.6
+    kp, vp = oracle_mod.cache_append(key, value, k_pool, v_pool, slots, "fp8_e4m3",
+                                     k_scale=ks, v_scale=vs)
+    P = k_pool.shape[1]
+    live = slots >= 0
+
+    def ref(bits, s):
+        f = I.bits_to_float(bits, "bf16").astype(np.float32) / np.float32(s)
+        return torch.from_numpy(f).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+    np.testing.assert_array_equal(kp[slots[live] // P, slots[live] % P], ref(key[live], ks))
+    np.testing.assert_array_equal(vp[slots[live] // P, slots[live] % P], ref(value[live], vs))
+    mask = np.ones(k_pool.shape[:2], dtype=bool)
+    mask[slots[live] // P, slots[live] % P] = False
+    np.testing.assert_array_equal(kp[mask], k_pool[mask])

@@ -43,6 +43,11 @@ MUTANTS = [
     ("new-key-row", "int64_t row = pr->cu_q[b] + j;", "int64_t row = pr->cu_q[b] + j + (j < i);"),
     ("new-key-head", "pr->k_new[(row * pr->Hkv + g) * D + d]", "pr->k_new[(row * pr->Hkv) * D + d]"),
     ("ctx-len-seq", "C = pr->ctx_lens[b];", "C = pr->ctx_lens[pr->B - 1 - b];"),
+    ("e4m3-enc-tie-odd", "(c & 1) == 0 && (best & 1) == 1", "(c & 1) == 1 && (best & 1) == 0"),
+    ("e4m3-enc-sign", "signbit(x) ? 0x80 : 0x00", "signbit(x) ? 0x00 : 0x80"),
+    ("append-row", "(slot % P) * s_tok", "((slot + 1) % P) * s_tok"),
+    ("append-scale", "orc_e4m3fn_encode(kf / k_scale)", "orc_e4m3fn_encode(kf * k_scale)"),
+    ("append-value-from-key", "uint16_t vb = value[", "uint16_t vb = key["),
 ]
 
 
