@@ -43,6 +43,10 @@ def parse():
     ap.add_argument("--splits", type=int, default=0, help="force the decode split cap")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU-baseline budget (0 disables the oracle leg)")
+    ap.add_argument("--op", default="attention", choices=["attention", "append"],
+                    help="append: KV-cache append of the extend workload's new tokens")
+    ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8_e4m3"],
+                    help="cache element type for --op append")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -244,6 +248,56 @@ def bench_extend(args, torch, pa, I):
     return res
 
 
+def bench_append(args, torch, pa, I):
+    """The extend workload's new tokens (bf16 K/V rows) written into a paged
+    cache at each sequence's next positions (one kernel per step)."""
+    import numpy as np
+    dev = "cuda:0"
+    case = I.extend_config(5)
+    T, Hkv, D, P = case.total_q, case.num_kv_heads, case.head_dim, 16
+    lens = [int(c) + int(n) for c, n in zip(case.ctx_lens, case.q_lens)]
+    rng = np.random.default_rng(5)
+    table, num_pages = I.deal_pages(lens, P, rng)
+    slots = np.concatenate([table[b, (int(c) + np.arange(int(n))) // P] * P +
+                            (int(c) + np.arange(int(n))) % P
+                            for b, (c, n) in enumerate(zip(case.ctx_lens, case.q_lens))])
+    fp8 = args.kv_dtype == "fp8_e4m3"
+    elem = 1 if fp8 else 2
+    alg = T * Hkv * D * (2 + elem) * 2 + 8 * T
+    copies = max(2, math.ceil(2 * MALL_BYTES / (T * Hkv * D * 2 * 2)) + 1)
+    kv = [(torch.randn(T, Hkv, D, device=dev).to(torch.bfloat16),
+           torch.randn(T, Hkv, D, device=dev).to(torch.bfloat16)) for _ in range(copies)]
+    pdt = torch.float8_e4m3fn if fp8 else torch.bfloat16
+    k_pool = torch.zeros(num_pages, P, Hkv, D, dtype=pdt, device=dev)
+    v_pool = torch.zeros_like(k_pool)
+    st = torch.from_numpy(slots.astype(np.int64)).to(dev)
+    ks, vs = (0.8, 1.3) if fp8 else (1.0, 1.0)
+
+    def step(i):
+        k, v = kv[i % copies]
+        pa.cache_append(k, v, k_pool, v_pool, st, k_scale=ks, v_scale=vs)
+
+    for i in range(args.warmup):
+        step(i)
+    K = args.steps
+    ms_step, ev_ms = time_steps(torch, step, K)
+    achieved = alg / (ev_ms * 1e-3) / 1e9
+    return {
+        "metric": "paged KV-cache append GB/s (fraction of HBM peak) on 1 MI355X",
+        "value": alg / (ms_step * 1e-3) / 1e9, "unit": "GB/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 in, " + ("fp8_e4m3" if fp8 else "bf16") + " cache", "data": "synthetic",
+        "config": {"workload": "append of the extend workload's new tokens", "tokens": T,
+                   "num_kv_heads": Hkv, "head_dim": D, "page_size": P,
+                   "kv_dtype": args.kv_dtype, "input_copies": copies},
+        "us_per_call": ev_ms * 1e3, "algorithmic_bytes": alg,
+        "roofline": {"bound": "hbm", "kernel": "cache_append", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None},
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -258,8 +312,12 @@ def main():
     import paged_gqa_attention_02_amd as pa
     from paged_gqa_attention_02_amd import inputs as I
     pa.lib()
-    res = bench_extend(args, torch, pa, I) if args.workload == 5 else \
-        bench_decode(args, torch, pa, I)
+    if args.op == "append":
+        res = bench_append(args, torch, pa, I)
+    elif args.workload == 5:
+        res = bench_extend(args, torch, pa, I)
+    else:
+        res = bench_decode(args, torch, pa, I)
     print(json.dumps(res), flush=True)
 
 

@@ -227,6 +227,36 @@ pa_status paged_attn_extend(const pa_plan* plan,
                             void* hip_stream);
 
 /*
+ * paged_attn_cache_append -- write new tokens' keys and values into the
+ * paged caches (the `do_kv_cache_update` step on the vLLM "b12x" backend
+ * page, which passes key, value, the caches, `slot_mapping` and the k/v
+ * scales to `reshape_and_cache_flash`).
+ *
+ *   key, value    bf16 [num_tokens, num_kv_heads, head_dim], heads contiguous,
+ *                 token stride kv_row_stride (elements)
+ *   k_pool,v_pool the caches, layout and strides as for decode
+ *   slot_mapping  int64 [num_tokens]: token i goes to page s / page_size, row
+ *                 s % page_size (s = slot_mapping[i]) for every kv head;
+ *                 s < 0 skips the token (padding).  0 <= s < num_pages *
+ *                 page_size and distinct slots are the caller's contract.
+ *   kv_dtype      PA_KV_BF16: the rows are copied unchanged.
+ *                 PA_KV_FP8_E4M3: each element x is stored as e4m3fn(x / scale)
+ *                 (k_scale for keys, v_scale for values; IEEE fp32 division,
+ *                 round to nearest even, saturating at +-448, NaN kept);
+ *                 scales must be finite and > 0.
+ *
+ * One kernel on hip_stream; no workspace.  head_dim 64 or 128, page_size a
+ * power of two up to 4096, 16-byte aligned pointers and strides.
+ */
+pa_status paged_attn_cache_append(const void* key, const void* value, int64_t num_tokens,
+                                  int64_t kv_row_stride, int32_t num_kv_heads,
+                                  int32_t head_dim, void* k_pool, void* v_pool,
+                                  int64_t kv_stride_page, int64_t kv_stride_tok,
+                                  int64_t kv_stride_head, int64_t num_pages, int32_t page_size,
+                                  int32_t kv_dtype, const int64_t* slot_mapping, float k_scale,
+                                  float v_scale, void* hip_stream);
+
+/*
  * paged_attn_gather -- test aid: copy every cached key/value row
  * (t in [0, L_b)) of every sequence, through the same address path the
  * attention kernels use, into k_out/v_out [sum_b L_b, Hkv, D] (sequence-major,

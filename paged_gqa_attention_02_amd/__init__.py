@@ -5,9 +5,9 @@ of ``include/paged_attn.h`` (``libpaged_attn.so``); this package is its thin
 Python binding plus the seeded synthetic inputs used by tests and the bench.
 """
 from .binding import (PA_MODE_DECODE, PA_MODE_EXTEND, PagedAttnError, Plan,  # noqa: F401
-                      decode, decode_merge, decode_plan, decode_split, extend,
+                      cache_append, decode, decode_merge, decode_plan, decode_split, extend,
                       extend_plan, gather, lib, plan, status_str, workspace_for)
 
-__all__ = ["PA_MODE_DECODE", "PA_MODE_EXTEND", "PagedAttnError", "Plan", "decode",
+__all__ = ["PA_MODE_DECODE", "PA_MODE_EXTEND", "PagedAttnError", "Plan", "cache_append", "decode",
            "decode_merge", "decode_plan", "decode_split", "extend", "extend_plan", "gather", "lib", "plan", "status_str",
            "workspace_for"]

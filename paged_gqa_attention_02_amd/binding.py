@@ -68,6 +68,10 @@ def lib():
                                     i32, f32, f32, i32, f32, f32, p, p, u64, p]
     L.paged_attn_extend.restype = ctypes.c_int
     L.paged_attn_gather.argtypes = [PP, p, p, i64, i64, i64, i64, p, i64, p, p, p, p]
+    L.paged_attn_cache_append.argtypes = [p, p, i64, i64, ctypes.c_int32, ctypes.c_int32, p, p,
+                                          i64, i64, i64, i64, ctypes.c_int32, ctypes.c_int32, p,
+                                          ctypes.c_float, ctypes.c_float, p]
+    L.paged_attn_cache_append.restype = ctypes.c_int
     L.paged_attn_gather.restype = ctypes.c_int
     L.paged_attn_status_str.argtypes = [ctypes.c_int]
     L.paged_attn_status_str.restype = ctypes.c_char_p
@@ -269,6 +273,27 @@ def extend(pl: Plan, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
         float(softcap), int(window), float(k_scale), float(v_scale), _ptr(out),
         _ptr(workspace), wbytes, _stream(stream)))
     return out
+
+
+def cache_append(key: torch.Tensor, value: torch.Tensor, k_pool: torch.Tensor,
+                 v_pool: torch.Tensor, slot_mapping: torch.Tensor, k_scale: float = 1.0,
+                 v_scale: float = 1.0, stream=None) -> None:
+    """paged_attn_cache_append: key/value bf16 [T, Hkv, D] into the pools at
+    int64 slots (slot < 0: skipped)."""
+    for name, t in (("key", key), ("value", value)):
+        if t.dtype != torch.bfloat16 or t.dim() != 3 or t.stride(2) != 1 \
+                or t.stride(1) != t.shape[2]:
+            raise ValueError(f"{name} must be bf16 [T, Hkv, D] with contiguous heads")
+    if key.shape != value.shape or key.stride() != value.stride():
+        raise ValueError("key and value must have the same shape and strides")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (key.shape[0],):
+        raise TypeError("slot_mapping must be int64 [T]")
+    sp, st, sh = _pool_strides(k_pool, v_pool)
+    T, Hkv, D = key.shape
+    _check("paged_attn_cache_append", lib().paged_attn_cache_append(
+        _ptr(key), _ptr(value), T, key.stride(0), Hkv, D, _ptr(k_pool), _ptr(v_pool), sp, st,
+        sh, k_pool.shape[0], k_pool.shape[1], PA_KV[_kv_dtype_name(k_pool)],
+        _ptr(slot_mapping), float(k_scale), float(v_scale), _stream(stream)))
 
 
 def gather(pl: Plan, k_pool: torch.Tensor, v_pool: torch.Tensor, block_table: torch.Tensor,

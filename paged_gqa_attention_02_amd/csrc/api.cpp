@@ -345,6 +345,55 @@ pa_status paged_attn_gather(const pa_plan* plan, const void* k_pool, const void*
     return PA_OK;
 }
 
+pa_status paged_attn_cache_append(const void* key, const void* value, int64_t num_tokens,
+                                  int64_t kv_row_stride, int32_t num_kv_heads,
+                                  int32_t head_dim, void* k_pool, void* v_pool,
+                                  int64_t kv_stride_page, int64_t kv_stride_tok,
+                                  int64_t kv_stride_head, int64_t num_pages, int32_t page_size,
+                                  int32_t kv_dtype, const int64_t* slot_mapping, float k_scale,
+                                  float v_scale, void* hip_stream) {
+    if (num_tokens < 0 || num_kv_heads < 1 || page_size < 1 || num_pages < 1)
+        return PA_ERR_INVALID_SHAPE;
+    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+    if (kv_dtype != PA_KV_BF16 && kv_dtype != PA_KV_FP8_E4M3) return PA_ERR_UNSUPPORTED;
+    if (!is_pow2(page_size) || page_size > 4096) return PA_ERR_UNSUPPORTED;
+    if (num_tokens == 0) return PA_OK;
+    if (!key || !value || !k_pool || !v_pool || !slot_mapping) return PA_ERR_NULL_POINTER;
+    const int64_t row = (int64_t)num_kv_heads * head_dim;
+    if (kv_row_stride < row || kv_stride_page < 0 || kv_stride_tok < 0 || kv_stride_head < 0)
+        return PA_ERR_INVALID_SHAPE;
+    if (num_tokens * (row / 8) >= ((int64_t)1 << 40)) return PA_ERR_UNSUPPORTED;
+    const int64_t eb = elem_bytes(kv_dtype);
+    if (!aligned16(key) || !aligned16(value) || !aligned16(k_pool) || !aligned16(v_pool) ||
+        (kv_row_stride * 2) % 16 || (kv_stride_page * eb) % 16 || (kv_stride_tok * eb) % 16 ||
+        (kv_stride_head * eb) % 16)
+        return PA_ERR_MISALIGNED;
+    if (kv_dtype == PA_KV_FP8_E4M3 &&
+        !(isfinite(k_scale) && isfinite(v_scale) && k_scale > 0.f && v_scale > 0.f))
+        return PA_ERR_INVALID_SHAPE;
+    AppendParams p;
+    memset(&p, 0, sizeof p);
+    p.key = key;
+    p.value = value;
+    p.row_stride = kv_row_stride;
+    p.k_pool = k_pool;
+    p.v_pool = v_pool;
+    p.s_page = kv_stride_page;
+    p.s_tok = kv_stride_tok;
+    p.s_head = kv_stride_head;
+    p.slot_mapping = slot_mapping;
+    p.num_tokens = num_tokens;
+    p.num_kv_heads = num_kv_heads;
+    p.head_dim = head_dim;
+    p.page_shift = ilog2(page_size);
+    p.k_scale = k_scale;
+    p.v_scale = v_scale;
+    if (launch_cache_append(p, kv_dtype == PA_KV_FP8_E4M3, static_cast<hipStream_t>(hip_stream)) !=
+        hipSuccess)
+        return PA_ERR_HIP;
+    return PA_OK;
+}
+
 pa_status paged_attn_extend(const pa_plan* plan, const void* q, const void* k_new,
                             const void* v_new, const int32_t* cu_seqlens_q,
                             const int32_t* ctx_lens, const void* k_pool, const void* v_pool,

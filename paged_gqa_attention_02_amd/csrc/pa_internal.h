@@ -83,6 +83,20 @@ struct ExtendParams {
     void* out;                // bf16 [total_q, Hq, D]
 };
 
+struct AppendParams {
+    const void* key;          // bf16 [num_tokens, Hkv, D], token stride row_stride
+    const void* value;
+    int64_t row_stride;       // elements
+    void* k_pool;             // bf16 | e4m3fn, strides in elements
+    void* v_pool;
+    int64_t s_page, s_tok, s_head;
+    const int64_t* slot_mapping;
+    int64_t num_tokens;
+    int32_t num_kv_heads, head_dim, page_shift;
+    float k_scale, v_scale;   // e4m3fn caches: stored value = enc(x / scale)
+};
+
+hipError_t launch_cache_append(const AppendParams& p, bool fp8, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int head_dim, bool fp8, bool uniform_pages,
                          int workers, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, int num_seqs,

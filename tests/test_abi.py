@@ -157,3 +157,41 @@ def test_decode_empty_batch_launches_nothing():
 
 def test_decode_plan_mode_mismatch():
     assert decode_status(plan_kw=dict(mode=1, total_q=10, max_q_len=10)) == MISMATCH
+
+
+# ---- cache append argument validation: fake, never dereferenced, pointers ----
+def append_status(**kw):
+    args = dict(key=A, value=A, T=8, row_stride=8 * 128, Hkv=8, D=128, k=A, v=A,
+                sp=16 * 8 * 128, st=8 * 128, sh=128, num_pages=10, P=16, kv=0, slots=A,
+                ks=1.0, vs=1.0)
+    args.update(kw)
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    return pa.lib().paged_attn_cache_append(
+        v(args["key"]), v(args["value"]), args["T"], args["row_stride"], args["Hkv"],
+        args["D"], v(args["k"]), v(args["v"]), args["sp"], args["st"], args["sh"],
+        args["num_pages"], args["P"], args["kv"], v(args["slots"]), args["ks"], args["vs"],
+        None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(key=None), NULLP),
+    (dict(slots=None), NULLP),
+    (dict(k=None), NULLP),
+    (dict(D=96), UNSUP),
+    (dict(P=12), UNSUP),
+    (dict(kv=3), UNSUP),
+    (dict(Hkv=0), SHAPE),
+    (dict(T=-1), SHAPE),
+    (dict(row_stride=8 * 128 - 8), SHAPE),
+    (dict(key=A + 8), MISAL),
+    (dict(v=A + 4), MISAL),
+    (dict(row_stride=8 * 128 + 4), MISAL),
+    (dict(kv=1, ks=0.0), SHAPE),
+    (dict(kv=1, vs=float("nan")), SHAPE),
+])
+def test_cache_append_validation(kw, status):
+    assert append_status(**kw) == status
+
+
+def test_cache_append_no_tokens_launches_nothing():
+    assert append_status(T=0, key=None, value=None, slots=None) == OK
