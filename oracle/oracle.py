@@ -37,6 +37,8 @@ def bind(path: str):
     L.orc_bf16.restype = d
     L.orc_e4m3fn.argtypes = [ctypes.c_uint8]
     L.orc_e4m3fn.restype = d
+    L.orc_verify.argtypes = [i, i, i, i, i, i, i, p, p, p, i64, p, i64, p, d, d, i, d, d, p, i]
+    L.orc_verify.restype = i
     L.orc_e4m3fn_encode.argtypes = [ctypes.c_float]
     L.orc_e4m3fn_encode.restype = ctypes.c_uint8
     L.orc_cache_append.argtypes = [i64, i, i, i, i, p, p, i64, p, p, i64, i64, i64, i64, p,
@@ -103,6 +105,25 @@ def extend(case, rows: Optional[np.ndarray] = None,
                           threads or default_threads())
     if rc != 0:
         raise RuntimeError(f"orc_extend failed: {rc}")
+    return out
+
+
+def verify(case, q: np.ndarray, threads: Optional[int] = None, clib=None) -> np.ndarray:
+    """fp64 verify of the decode case's sequences with query rows q (bf16 bits
+    [B, q_len, Hq, D]); the last q_len cached tokens of each sequence are the
+    query tokens.  Returns out [B, q_len, Hq, D]."""
+    B, ql, Hq, D = q.shape
+    out = np.zeros((B, ql, Hq, D), dtype=np.float64)
+    qb = _c(q)
+    kp, vp, bt = _c(case.kv.k_pool), _c(case.kv.v_pool), _c(case.kv.block_table)
+    sl = _c(case.seq_lens)
+    rc = (clib or lib()).orc_verify(B, Hq, case.num_kv_heads, D, case.kv.page_size,
+                                    _KV[case.kv_dtype], ql, _ptr(qb), _ptr(kp), _ptr(vp),
+                                    kp.shape[0], _ptr(bt), bt.shape[1], _ptr(sl), case.scale,
+                                    case.softcap, case.window, case.k_scale, case.v_scale,
+                                    _ptr(out), threads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"orc_verify failed: {rc}")
     return out
 
 

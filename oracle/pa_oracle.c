@@ -50,6 +50,13 @@
  *           the final `acc / l_i` of `_fwd_kernel_flash_attn_v2`).  The cache
  *           scales apply to cached keys/values only; new rows are bf16.
  *
+ *  verify   q_len query rows per sequence (the speculative verify step of
+ *           the vLLM "b12x" backend page: `1 + num_speculative_tokens` rows
+ *           for every request, their keys/values already in the cache and
+ *           counted by seq_lens).  Row i of sequence b sits at position
+ *           L - q_len + i and attends causally to the cached tokens up to
+ *           it: the decode definition with L replaced by L - q_len + i + 1.
+ *
  *  append   The cache write that precedes attention (`do_kv_cache_update` on
  *           the vLLM "b12x" backend page, which hands key, value, the
  *           caches, `slot_mapping` and the k/v scales to
@@ -126,6 +133,7 @@ typedef struct {
     double scale, softcap, k_scale, v_scale;
     int window;
     int num_splits;             /* decode: 0 = one pass over the key range */
+    int q_len;                  /* verify: query rows per sequence */
     /* extend */
     const uint16_t *k_new, *v_new; /* [total_q][Hkv][D] */
     const int32_t *cu_q, *ctx_lens;
@@ -257,6 +265,33 @@ static void decode_row(const orc_problem *pr, int b, int h, double *q,
 }
 
 /* ------------------------------------------------------------------ */
+/* Verify: q_len query rows per sequence, the last q_len cached tokens. */
+/* Row i sits at position L - q_len + i, so its keys are the first      */
+/* L - q_len + i + 1 tokens (causal), with the decode window rule.      */
+/* ------------------------------------------------------------------ */
+static void verify_row(const orc_problem *pr, int64_t it, double *q, double *s, double *v)
+{
+    int Hq = pr->Hq, D = pr->D, ql = pr->q_len;
+    int h = (int)(it % Hq);
+    int64_t bi = it / Hq;                       /* (sequence, row) */
+    int b = (int)(bi / ql), i = (int)(bi % ql);
+    int64_t L = (int64_t)pr->seq_lens[b] - ql + i + 1;
+    int64_t lo = (pr->window > 0 && L - pr->window > 0) ? L - pr->window : 0;
+    double *out = pr->out + (bi * Hq + h) * D;
+    double lse;
+    int d;
+    if (L <= 0) {                               /* nothing to attend: zero row */
+        for (d = 0; d < D; ++d)
+            out[d] = 0.0;
+        return;
+    }
+    for (d = 0; d < D; ++d)
+        q[d] = orc_bf16(pr->q[(bi * Hq + h) * D + d]);
+    gather_cached(pr, b, h / (Hq / pr->Hkv), q, lo, L, s, v);
+    softmax_sum(s, v, L - lo, D, out, &lse);
+}
+
+/* ------------------------------------------------------------------ */
 /* Extend                                                              */
 /* ------------------------------------------------------------------ */
 static void extend_row(const orc_problem *pr, int64_t r, int h, double *q,
@@ -336,7 +371,9 @@ static void *worker(void *arg)
         pthread_mutex_unlock(job->mu);
         if (it >= job->n_items)
             break;
-        if (job->is_extend) {
+        if (job->is_extend == 2) {
+            verify_row(pr, it, q, s, v);
+        } else if (job->is_extend) {
             int64_t r = pr->rows ? pr->rows[it / pr->Hq] : it / pr->Hq;
             extend_row(pr, r, (int)(it % pr->Hq), q, s, v);
         } else {
@@ -531,4 +568,38 @@ int orc_cache_append(int64_t num_tokens, int Hkv, int D, int P, int kv_dtype,
         }
     }
     return 0;
+}
+
+/*
+ * Verify oracle: q [B][q_len][Hq][D] (bf16), seq_lens counting the q_len
+ * query tokens themselves; out [B][q_len][Hq][D].
+ */
+int orc_verify(int B, int Hq, int Hkv, int D, int P, int kv_dtype, int q_len,
+               const uint16_t *q, const void *k_pool, const void *v_pool,
+               int64_t num_pages, const int32_t *block_table, int64_t bt_stride,
+               const int32_t *seq_lens, double scale, double softcap, int window,
+               double k_scale, double v_scale, double *out, int threads)
+{
+    orc_problem pr;
+    int64_t max_keys = 0;
+    int b;
+    if (check_common(B, Hq, Hkv, D, P, kv_dtype) || q_len < 1)
+        return -1;
+    memset(&pr, 0, sizeof pr);
+    pr.B = B; pr.Hq = Hq; pr.Hkv = Hkv; pr.D = D; pr.P = P;
+    pr.kv_dtype = kv_dtype;
+    pr.q = q; pr.k_pool = k_pool; pr.v_pool = v_pool;
+    pr.num_pages = num_pages;
+    pr.bt = block_table; pr.bt_stride = bt_stride; pr.seq_lens = seq_lens;
+    pr.scale = scale; pr.softcap = softcap; pr.window = window;
+    pr.k_scale = k_scale; pr.v_scale = v_scale;
+    pr.q_len = q_len;
+    pr.out = out;
+    for (b = 0; b < B; ++b) {
+        if (seq_lens[b] < 0)
+            return -1;
+        if (seq_lens[b] > max_keys)
+            max_keys = seq_lens[b];
+    }
+    return run_jobs(&pr, 2, (int64_t)B * q_len * Hq, max_keys, threads);
 }

@@ -73,3 +73,26 @@ def sdpa_extend(case):
         out[a:e] = _sdpa(np.ascontiguousarray(q), k, v, case.scale,
                          torch.from_numpy(keep)).transpose(1, 0, 2)
     return out
+
+
+def sdpa_verify(case, q_bits):
+    """Verify without soft-cap: the last q_len cached tokens of every sequence
+    are the query tokens; SDPA with a causal (and window) keep-mask."""
+    assert case.softcap == 0
+    B, ql, Hq, D = q_bits.shape
+    G = Hq // case.num_kv_heads
+    out = np.zeros((B, ql, Hq, D))
+    for b in range(B):
+        L = int(case.seq_lens[b])
+        k, v = dense_tokens(case.kv, b, L, case.kv_dtype)
+        k = np.ascontiguousarray(np.repeat(k * case.k_scale, G, axis=1).transpose(1, 0, 2))
+        v = np.ascontiguousarray(np.repeat(v * case.v_scale, G, axis=1).transpose(1, 0, 2))
+        qpos = L - ql + np.arange(ql)[:, None]
+        kpos = np.arange(L)[None, :]
+        keep = kpos <= qpos
+        if case.window > 0:
+            keep &= (qpos - kpos) < case.window
+        q = bits_to_float(q_bits[b], "bf16").astype(np.float64).transpose(1, 0, 2)
+        out[b] = _sdpa(np.ascontiguousarray(q), k, v, case.scale,
+                       torch.from_numpy(keep)).transpose(1, 0, 2)
+    return out

@@ -19,6 +19,9 @@ class Oracle:
     def decode_e4m3fn(self, bits):
         return oracle.decode_e4m3fn(bits, clib=self.clib)
 
+    def verify(self, case, q, threads=None):
+        return oracle.verify(case, q, threads, clib=self.clib)
+
     def encode_e4m3fn(self, x):
         return oracle.encode_e4m3fn(x, clib=self.clib)
 

@@ -48,6 +48,10 @@ MUTANTS = [
     ("append-row", "(slot % P) * s_tok", "((slot + 1) % P) * s_tok"),
     ("append-scale", "orc_e4m3fn_encode(kf / k_scale)", "orc_e4m3fn_encode(kf * k_scale)"),
     ("append-value-from-key", "uint16_t vb = value[", "uint16_t vb = key["),
+    ("verify-causal", "int64_t L = (int64_t)pr->seq_lens[b] - ql + i + 1;",
+     "int64_t L = (int64_t)pr->seq_lens[b] - ql + i;"),
+    ("verify-row-order", "int b = (int)(bi / ql), i = (int)(bi % ql);",
+     "int b = (int)(bi / ql), i = ql - 1 - (int)(bi % ql);"),
 ]
 
 
