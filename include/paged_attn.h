@@ -10,6 +10,12 @@
  *            the computation of `decode_attention_fwd` and its kernels
  *            `_fwd_grouped_kernel_stage1` / `_fwd_kernel_stage2` on the page
  *            "vllm/attention/ops/triton_decode_attention.py".
+ *   verify   q_len query tokens per sequence (the speculative verify step of
+ *            the b12x page: `1 + num_speculative_tokens` rows for every
+ *            request, whose keys/values are already in the cache): token i
+ *            at position L - q_len + i attends causally to the cached tokens
+ *            up to and including itself, through the same split/merge kernels
+ *            as decode.
  *   extend   prefix-prefill: new query tokens attend to the sequence's cached
  *            context through the pages (no mask) and causally to each other
  *            (contiguous new K/V rows), as `context_attention_fwd` and
@@ -78,7 +84,7 @@ typedef enum {
 } pa_status;
 
 typedef enum { PA_KV_BF16 = 0, PA_KV_FP8_E4M3 = 1 } pa_kv_dtype;
-typedef enum { PA_MODE_DECODE = 0, PA_MODE_EXTEND = 1 } pa_mode;
+typedef enum { PA_MODE_DECODE = 0, PA_MODE_EXTEND = 1, PA_MODE_VERIFY = 2 } pa_mode;
 
 /* Host-side description of one call shape (plain values, no pointers). */
 typedef struct {
@@ -92,10 +98,12 @@ typedef struct {
     int32_t window;            /* sliding window W (<= 0: off) */
     int32_t max_pages_per_seq; /* block-table row width in entries */
     int32_t max_kv_len;        /* bound on cached tokens per sequence
-                                  (decode: seq_lens, incl. the query token;
-                                   extend: ctx_lens) */
+                                  (decode/verify: seq_lens, incl. the query
+                                   tokens; extend: ctx_lens) */
     int32_t total_q;           /* extend: rows of q/k_new/v_new/out */
-    int32_t max_q_len;         /* extend: bound on new tokens per sequence */
+    int32_t max_q_len;         /* extend: bound on new tokens per sequence;
+                                  verify: the query tokens per sequence
+                                  (q_len >= 1, G * q_len <= 16) */
     int32_t num_splits;        /* decode: 0 = plan chooses; > 0 forces the
                                   number of split-pass pieces (waves) */
 } pa_problem;
@@ -123,6 +131,8 @@ typedef struct {
  * units x resident waves per unit), or prob->num_splits when that is > 0.
  * Pieces of one key range are merged by log-sum-exp (the split partition
  * and merge of `_fwd_kernel_stage1/2`; any partition gives the same result).
+ * Verify: as decode, with lo = max(0, L - q_len + 1 - W), the window start of
+ * the first query token.
  * Extend: validates the shape; no workspace is needed.
  *
  * hip_device >= 0 queries that device's compute-unit count; hip_device < 0
@@ -200,6 +210,37 @@ pa_status paged_attn_decode_merge(const pa_plan* plan,
                                   void* out, int64_t out_stride_b,
                                   void* workspace, uint64_t workspace_bytes,
                                   void* hip_stream);
+
+/*
+ * paged_attn_verify -- q_len query tokens per sequence against the cache
+ * (speculative verification; q_len = plan->prob.max_q_len, the plan made
+ * with mode PA_MODE_VERIFY).  The arguments are paged_attn_decode's, except:
+ *
+ *   q             bf16 [B, q_len, Hq, D]: token i of sequence b at
+ *                 q + b*q_stride_b + i*Hq*D (q_stride_b >= q_len*Hq*D)
+ *   seq_lens      L_b cached tokens including all q_len query tokens; token i
+ *                 sits at position L_b - q_len + i and attends to the keys
+ *                 j <= L_b - q_len + i (and, with a window, j > that - W);
+ *                 a token with no such key (L_b - q_len + i < 0) gets a zero row
+ *   out           bf16 [B, q_len, Hq, D], sequence stride out_stride_b
+ *                 (>= q_len*Hq*D)
+ *
+ * The G*q_len (token, head) rows of a kv head share every K/V tile load: one
+ * pass over the cache serves all q_len tokens.  Same kernels, workspace rules
+ * and errors as paged_attn_decode.
+ */
+pa_status paged_attn_verify(const pa_plan* plan,
+                            const void* q, int64_t q_stride_b,
+                            const void* k_pool, const void* v_pool,
+                            int64_t kv_stride_page, int64_t kv_stride_tok,
+                            int64_t kv_stride_head, int64_t num_pages,
+                            const int32_t* block_table, int64_t bt_stride,
+                            const int32_t* seq_lens,
+                            int32_t page_size, float scale, float softcap,
+                            int32_t window, float k_scale, float v_scale,
+                            void* out, int64_t out_stride_b,
+                            void* workspace, uint64_t workspace_bytes,
+                            void* hip_stream);
 
 /*
  * paged_attn_extend -- prefix-prefill of new tokens on top of a paged context.

@@ -1,13 +1,16 @@
-"""Paged GQA attention (split-KV decode and prefix-prefill extend) for MI355X.
+"""Paged GQA attention (split-KV decode, speculative verify and prefix-prefill
+extend) for MI355X.
 
 The computation runs in hand-written HIP kernels for gfx950 behind the C ABI
 of ``include/paged_attn.h`` (``libpaged_attn.so``); this package is its thin
 Python binding plus the seeded synthetic inputs used by tests and the bench.
 """
-from .binding import (PA_MODE_DECODE, PA_MODE_EXTEND, PagedAttnError, Plan,  # noqa: F401
-                      cache_append, decode, decode_merge, decode_plan, decode_split, extend,
-                      extend_plan, gather, lib, plan, status_str, workspace_for)
+from .binding import (PA_MODE_DECODE, PA_MODE_EXTEND, PA_MODE_VERIFY,  # noqa: F401
+                      PagedAttnError, Plan, cache_append, decode, decode_merge, decode_plan,
+                      decode_split, extend, extend_plan, gather, lib, plan, status_str, verify,
+                      verify_plan, workspace_for)
 
-__all__ = ["PA_MODE_DECODE", "PA_MODE_EXTEND", "PagedAttnError", "Plan", "cache_append", "decode",
-           "decode_merge", "decode_plan", "decode_split", "extend", "extend_plan", "gather", "lib", "plan", "status_str",
+__all__ = ["PA_MODE_DECODE", "PA_MODE_EXTEND", "PA_MODE_VERIFY", "PagedAttnError", "Plan",
+           "cache_append", "decode", "decode_merge", "decode_plan", "decode_split", "extend",
+           "extend_plan", "gather", "lib", "plan", "status_str", "verify", "verify_plan",
            "workspace_for"]

@@ -17,7 +17,7 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpaged_attn.so")
 
-PA_MODE_DECODE, PA_MODE_EXTEND = 0, 1
+PA_MODE_DECODE, PA_MODE_EXTEND, PA_MODE_VERIFY = 0, 1, 2
 PA_KV = {"bf16": 0, "fp8_e4m3": 1}
 
 
@@ -61,7 +61,7 @@ def lib():
     L.paged_attn_decode.argtypes = [PP, p, i64, p, p, i64, i64, i64, i64, p, i64, p,
                                     i32, f32, f32, i32, f32, f32, p, i64, p, u64, p]
     L.paged_attn_decode.restype = ctypes.c_int
-    for fn in ("paged_attn_decode_split", "paged_attn_decode_merge"):
+    for fn in ("paged_attn_decode_split", "paged_attn_decode_merge", "paged_attn_verify"):
         getattr(L, fn).argtypes = L.paged_attn_decode.argtypes
         getattr(L, fn).restype = ctypes.c_int
     L.paged_attn_extend.argtypes = [PP, p, p, p, p, p, p, p, i64, i64, i64, i64, p, i64,
@@ -216,19 +216,53 @@ def decode_merge(pl: Plan, q, k_pool, v_pool, block_table, seq_lens, scale, soft
                    scale, softcap, window, k_scale, v_scale, out, workspace, stream)
 
 
+def verify_plan(q: torch.Tensor, k_pool: torch.Tensor, block_table: torch.Tensor,
+                max_kv_len: int, window: int = 0, num_splits: int = 0) -> Plan:
+    """Plan a verify call for q shaped [B, q_len, Hq, D]."""
+    B, q_len, Hq, D = q.shape
+    return plan(PA_MODE_VERIFY, B, Hq, k_pool.shape[2], D, k_pool.shape[1],
+                _kv_dtype_name(k_pool), window, block_table.shape[1], max_kv_len,
+                max_q_len=q_len, num_splits=num_splits, device=q.device.index)
+
+
+def verify(pl: Plan, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+           block_table: torch.Tensor, seq_lens: torch.Tensor, scale: float,
+           softcap: float = 0.0, window: int = 0, k_scale: float = 1.0,
+           v_scale: float = 1.0, out: Optional[torch.Tensor] = None,
+           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """paged_attn_verify: q bf16 [B, q_len, Hq, D] -> out bf16 [B, q_len, Hq, D];
+    seq_lens count the q_len query tokens, which are already in the cache."""
+    return _decode("paged_attn_verify", pl, q, k_pool, v_pool, block_table, seq_lens, scale,
+                   softcap, window, k_scale, v_scale, out, workspace, stream)
+
+
+def _rows_contiguous(t: torch.Tensor) -> bool:
+    """All dims after the first are dense (the sequence stride is free)."""
+    step = 1
+    for d in range(t.dim() - 1, 0, -1):
+        if t.shape[d] > 1 and t.stride(d) != step:
+            return False
+        step *= t.shape[d]
+    return True
+
+
 def _decode(fn, pl, q, k_pool, v_pool, block_table, seq_lens, scale, softcap, window,
             k_scale, v_scale, out, workspace, stream):
-    if fn != "paged_attn_decode" and (out is None or (workspace is None and
-                                                      pl.workspace_bytes > 0)):
+    if fn not in ("paged_attn_decode", "paged_attn_verify") and (
+            out is None or (workspace is None and pl.workspace_bytes > 0)):
         raise ValueError(f"{fn}: the passes share `out` and the workspace; pass both")
-    if q.dtype != torch.bfloat16 or q.dim() != 3 or q.stride(2) != 1 or q.stride(1) != q.shape[2]:
-        raise ValueError("q must be bf16 [B, Hq, D] with contiguous heads")
+    dims = 4 if fn == "paged_attn_verify" else 3
+    shape = "[B, q_len, Hq, D]" if dims == 4 else "[B, Hq, D]"
+    if q.dtype != torch.bfloat16 or q.dim() != dims or not _rows_contiguous(q):
+        raise ValueError(f"q must be bf16 {shape}, dense after the sequence dimension")
     if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
         raise TypeError("block_table and seq_lens must be int32")
     if block_table.stride(1) != 1:
         raise ValueError("block_table rows must be contiguous")
     if out is None:
         out = torch.empty_like(q)
+    if out.dtype != torch.bfloat16 or out.shape != q.shape or not _rows_contiguous(out):
+        raise ValueError(f"out must be bf16 {shape} like q, dense after the sequence dimension")
     sp, st, sh = _pool_strides(k_pool, v_pool)
     workspace = _workspace(pl, workspace, q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -263,6 +297,8 @@ def extend(pl: Plan, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
         raise TypeError("cu_seqlens_q, ctx_lens and block_table must be int32")
     if out is None:
         out = torch.empty_like(q)
+    if out.dtype != torch.bfloat16 or out.shape != q.shape or not _rows_contiguous(out):
+        raise ValueError(f"out must be bf16 {shape} like q, dense after the sequence dimension")
     sp, st, sh = _pool_strides(k_pool, v_pool)
     workspace = _workspace(pl, workspace, q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

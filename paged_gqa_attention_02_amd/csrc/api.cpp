@@ -35,7 +35,8 @@ int64_t round_up(int64_t a, int64_t m) { return cdiv(a, m) * m; }
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
 pa_status check_problem(const pa_problem& pr) {
-    if (pr.mode != PA_MODE_DECODE && pr.mode != PA_MODE_EXTEND) return PA_ERR_UNSUPPORTED;
+    if (pr.mode != PA_MODE_DECODE && pr.mode != PA_MODE_EXTEND && pr.mode != PA_MODE_VERIFY)
+        return PA_ERR_UNSUPPORTED;
     if (pr.num_seqs < 0 || pr.num_q_heads <= 0 || pr.num_kv_heads <= 0 || pr.page_size <= 0 ||
         pr.max_kv_len < 0 || pr.max_pages_per_seq < 0 || pr.num_splits < 0)
         return PA_ERR_INVALID_SHAPE;
@@ -49,6 +50,11 @@ pa_status check_problem(const pa_problem& pr) {
     if (!is_pow2(pr.page_size) || pr.page_size > 4096) return PA_ERR_UNSUPPORTED;
     if ((int64_t)pr.max_pages_per_seq < cdiv(pr.max_kv_len, pr.page_size))
         return PA_ERR_INVALID_SHAPE;
+    if (pr.mode == PA_MODE_VERIFY) {
+        // max_q_len query rows per sequence, G * q_len MFMA columns (<= 16)
+        if (pr.max_q_len < 1) return PA_ERR_INVALID_SHAPE;
+        if ((int64_t)G * pr.max_q_len > 16) return PA_ERR_UNSUPPORTED;
+    }
     if (pr.mode == PA_MODE_EXTEND) {
         if (pr.total_q < 0 || pr.max_q_len < 0) return PA_ERR_INVALID_SHAPE;
         if (pr.num_seqs > 0 && pr.total_q > 0 && pr.max_q_len == 0) return PA_ERR_INVALID_SHAPE;
@@ -132,7 +138,7 @@ pa_status paged_attn_plan(const pa_problem* prob, int hip_device, pa_plan* out) 
     pl.num_splits = 1;
     pl.tokens_per_split = kTile;
 
-    if (pr.mode == PA_MODE_DECODE) {
+    if (pr.mode == PA_MODE_DECODE || pr.mode == PA_MODE_VERIFY) {
         // Split pass: persistent waves, each owning an equal contiguous range
         // of the tiles of all segments.  By default as many as the device
         // keeps resident; prob.num_splits > 0 forces the count.
@@ -156,8 +162,8 @@ pa_status paged_attn_plan(const pa_problem* prob, int hip_device, pa_plan* out) 
         pl.num_splits = (int32_t)workers;
         pl.tokens_per_split = kTile;
         pl.waves_per_block = 1;
-        const int64_t G = pr.num_q_heads / pr.num_kv_heads;
-        const int64_t rows = workers * 2 * G;
+        const int64_t q_len = pr.mode == PA_MODE_VERIFY ? pr.max_q_len : 1;
+        const int64_t rows = workers * 2 * (pr.num_q_heads / pr.num_kv_heads) * q_len;
         // partial rows, their log-sum-exp, and one record per segment
         pl.workspace_bytes = (uint64_t)(round_up(rows * pr.head_dim * 4, 256) +
                                         round_up(rows * 4, 256) +
@@ -178,7 +184,8 @@ int paged_attn_plan_describe(const pa_plan* pl, char* buf, int buf_len) {
         n = snprintf(tmp, sizeof tmp,
                      "%s B=%d Hq=%d Hkv=%d D=%d P=%d kv=%s window=%d max_kv_len=%d "
                      "splits=%d tokens_per_split=%d waves=%d cus=%d workspace=%llu",
-                     p.mode == PA_MODE_DECODE ? "decode" : "extend", p.num_seqs,
+                     p.mode == PA_MODE_DECODE ? "decode"
+                     : p.mode == PA_MODE_VERIFY ? "verify" : "extend", p.num_seqs,
                      p.num_q_heads, p.num_kv_heads, p.head_dim, p.page_size,
                      p.kv_dtype == PA_KV_FP8_E4M3 ? "fp8_e4m3" : "bf16", p.window,
                      p.max_kv_len, pl->num_splits, pl->tokens_per_split,
@@ -196,7 +203,7 @@ namespace {
 // Passes of a decode call: the split pass, the merge, or both in order.
 enum DecodePasses { kSplitPass = 1, kMergePass = 2, kBothPasses = 3 };
 
-pa_status decode_impl(int passes, const pa_plan* plan, const void* q, int64_t q_stride_b,
+pa_status decode_impl(int passes, int mode, const pa_plan* plan, const void* q, int64_t q_stride_b,
                       const void* k_pool, const void* v_pool, int64_t kv_stride_page,
                       int64_t kv_stride_tok, int64_t kv_stride_head, int64_t num_pages,
                       const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
@@ -208,7 +215,7 @@ pa_status decode_impl(int passes, const pa_plan* plan, const void* q, int64_t q_
     const pa_problem& pr = pl.prob;
     pa_status st = check_problem(pr);
     if (st != PA_OK) return st;
-    if (pr.mode != PA_MODE_DECODE) return PA_ERR_PLAN_MISMATCH;
+    if (pr.mode != mode) return PA_ERR_PLAN_MISMATCH;
     if (page_size != pr.page_size || window != pr.window) return PA_ERR_PLAN_MISMATCH;
     if (pl.tokens_per_split != kTile || pl.num_splits < 1 || pl.num_splits > kMaxWorkers)
         return PA_ERR_PLAN_MISMATCH;
@@ -217,8 +224,10 @@ pa_status decode_impl(int passes, const pa_plan* plan, const void* q, int64_t q_
     st = check_pools(pl, k_pool, v_pool, kv_stride_page, kv_stride_tok, kv_stride_head,
                      num_pages, block_table, bt_stride);
     if (st != PA_OK) return st;
+    // verify: q_len query rows per sequence, each Hq*D contiguous
+    const int32_t q_len = mode == PA_MODE_VERIFY ? pr.max_q_len : 1;
     const int64_t row = (int64_t)pr.num_q_heads * pr.head_dim;
-    if (q_stride_b < row || out_stride_b < row) return PA_ERR_INVALID_SHAPE;
+    if (q_stride_b < q_len * row || out_stride_b < q_len * row) return PA_ERR_INVALID_SHAPE;
     if (!aligned16(q) || !aligned16(out) || (q_stride_b * 2) % 16 || (out_stride_b * 2) % 16)
         return PA_ERR_MISALIGNED;
     if (!isfinite(scale) || !isfinite(softcap) || !isfinite(k_scale) || !isfinite(v_scale))
@@ -246,6 +255,10 @@ pa_status decode_impl(int passes, const pa_plan* plan, const void* q, int64_t q_
     p.num_q_heads = pr.num_q_heads;
     p.num_kv_heads = pr.num_kv_heads;
     p.group = pr.num_q_heads / pr.num_kv_heads;
+    p.q_len = q_len;
+    p.rows = p.group * q_len;
+    p.q_stride_t = row;
+    p.out_stride_t = row;
     p.page_shift = ilog2(pr.page_size);
     p.window = pr.window;
     const float kl2e = 1.4426950408889634f;
@@ -259,7 +272,7 @@ pa_status decode_impl(int passes, const pa_plan* plan, const void* q, int64_t q_
     p.out = out;
     p.out_stride_b = out_stride_b;
     {
-        const int64_t rows = (int64_t)pl.num_splits * 2 * p.group;
+        const int64_t rows = (int64_t)pl.num_splits * 2 * p.rows;
         char* ws = static_cast<char*>(workspace);
         p.part_o = reinterpret_cast<float*>(ws);
         const int64_t o_bytes = round_up(rows * pr.head_dim * 4, 256);
@@ -296,15 +309,19 @@ extern "C" {
         int64_t out_stride_b, void *workspace, uint64_t workspace_bytes, void *hip_stream
 
 pa_status paged_attn_decode(PA_DECODE_PARAMS) {
-    return decode_impl(kBothPasses, PA_DECODE_ARGS);
+    return decode_impl(kBothPasses, PA_MODE_DECODE, PA_DECODE_ARGS);
 }
 
 pa_status paged_attn_decode_split(PA_DECODE_PARAMS) {
-    return decode_impl(kSplitPass, PA_DECODE_ARGS);
+    return decode_impl(kSplitPass, PA_MODE_DECODE, PA_DECODE_ARGS);
 }
 
 pa_status paged_attn_decode_merge(PA_DECODE_PARAMS) {
-    return decode_impl(kMergePass, PA_DECODE_ARGS);
+    return decode_impl(kMergePass, PA_MODE_DECODE, PA_DECODE_ARGS);
+}
+
+pa_status paged_attn_verify(PA_DECODE_PARAMS) {
+    return decode_impl(kBothPasses, PA_MODE_VERIFY, PA_DECODE_ARGS);
 }
 
 pa_status paged_attn_gather(const pa_plan* plan, const void* k_pool, const void* v_pool,

@@ -44,6 +44,8 @@
 // K or V row, nontemporal; one wave load instruction covers whole rows (4 of
 // K or V for bf16 D=128).  A wave keeps the next tile's K and V in flight
 // while it computes the current one.
+#include <climits>
+
 #include "decode_geom.h"
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -112,6 +114,8 @@ struct VRow {
 struct TileCtx {
     const int* pages;
     int first_page, last_idx, t_begin, t_end, c, grp;
+    int lim, wlo;              // this lane's column: keys t with wlo <= t <= lim (verify)
+    int full_lo, full_hi;      // tiles inside [full_lo, full_hi) are valid for every column
     int64_t page_bytes;        // s_page * elem
     int tok_bytes;             // s_tok * elem
     int k_row;                 // whole-row K loads: the lane's row within a load
@@ -272,7 +276,8 @@ __device__ __forceinline__ u32x4 tile_softmax(Acc<D>& A, const f32x4 s[2],
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int t = t0 + tile_token(x.grp, j);
-            sc[j] = (t >= x.t_begin && t < x.t_end) ? sc[j] : -INFINITY;
+            const bool keep = t >= x.t_begin && t < x.t_end && t <= x.lim && t >= x.wlo;
+            sc[j] = keep ? sc[j] : -INFINITY;
         }
     }
     float tmax = sc[0];
@@ -285,12 +290,14 @@ __device__ __forceinline__ u32x4 tile_softmax(Acc<D>& A, const f32x4 s[2],
     constexpr float kSlack = 8.f;
     const bool move = __any(tmax > A.m + kSlack);
     const float m_new = move ? fmaxf(A.m, tmax) : A.m;
-    const float alpha = fast_exp2(A.m - m_new);
+    // (a column with no key yet keeps m = -inf: exponents are taken against 0)
+    const float ms = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(A.m - ms);
     float pr[8];
     float psum = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        pr[j] = fast_exp2(sc[j] - m_new);
+        pr[j] = fast_exp2(sc[j] - ms);
         psum += pr[j];
     }
     A.l = A.l * alpha + psum;
@@ -366,7 +373,7 @@ void decode_split_kernel(DecodeParams p) {
     const int64_t r1 = range_start(w + 1, N, W);
     if (r0 >= r1) {
         // an empty range (N < W): the merge may read this wave's slot 0
-        if (lane < G) p.part_lse[part_row(p, w, 0) + lane] = -INFINITY;
+        if (lane < p.rows) p.part_lse[part_row(p, w, 0) + lane] = -INFINITY;
         return;
     }
 
@@ -397,19 +404,20 @@ void decode_split_kernel(DecodeParams p) {
                 int4{(int)w, (int)w_last, slot, 0};
         }
 
-        // ---- Q^T as the B operand: column c = query head kvh*G + c ----
-        // The contraction index (grp, j) of MFMA kk stands for d = dq(kk, grp)
-        // + j; for fp8 K one 16-byte load feeds two consecutive MFMAs.
+        // ---- Q^T as the B operand: column c = query token c / G, head
+        // kvh*G + c % G.  The contraction index (grp, j) of MFMA kk stands for
+        // d = dq(kk, grp) + j; for fp8 K one 16-byte load feeds two MFMAs.
         u32x4 qop[KK];
         {
+            const int cc = c < p.rows ? c : 0;
             const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
-                                   (int64_t)b * p.q_stride_b +
-                                   (int64_t)(kvh * G + (c < G ? c : 0)) * D;
+                                   (int64_t)b * p.q_stride_b + (int64_t)(cc / G) * p.q_stride_t +
+                                   (int64_t)(kvh * G + cc % G) * D;
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
                 const int d0 = FP8 ? 64 * (kk / 2) + 16 * grp + 8 * (kk % 2) : 32 * kk + 8 * grp;
                 const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + d0);
-                qop[kk] = (c < G) ? v : u32x4{0, 0, 0, 0};
+                qop[kk] = (c < p.rows) ? v : u32x4{0, 0, 0, 0};
             }
         }
 
@@ -433,6 +441,10 @@ void decode_split_kernel(DecodeParams p) {
                 x.v_lane[r] = head + kVBytes * c + (UNIFORM ? (4 * grp + r) * x.tok_bytes : 0);
         }
         x.pages = sm_pages;
+        // causal limit and window start of this lane's column (query token c / G
+        // at position L - q_len + c / G); for decode these never bind
+        x.lim = sr.L - p.q_len + (c < p.rows ? c / G : 0);
+        x.wlo = p.window > 0 ? x.lim - p.window + 1 : INT_MIN;
 
         // ---- the piece's tiles, chunk by chunk (page list staged in LDS) ----
         for (int c0 = 0; c0 < cnt; c0 += chunk_tiles) {
@@ -440,6 +452,8 @@ void decode_split_kernel(DecodeParams p) {
             const int tile0 = sr.base + (i0 + c0) * kTile;
             x.t_begin = max(tile0, sr.lo);
             x.t_end = min(tile0 + ct * kTile, sr.L);
+            x.full_lo = max(x.t_begin, p.window > 0 ? sr.L - p.window : 0);
+            x.full_hi = min(x.t_end, sr.L - p.q_len + 1);
             x.first_page = x.t_begin >> p.page_shift;
             const int n_pages = ((x.t_end - 1) >> p.page_shift) - x.first_page + 1;
             x.last_idx = n_pages - 1;
@@ -464,7 +478,7 @@ void decode_split_kernel(DecodeParams p) {
                 issue_v<D, FP8, UNIFORM>(vr, p, x, tile_t0(0));
                 for (int i = 0; i + 1 < ct; ++i) {
                     const int t0 = tile_t0(i);
-                    const bool full = (t0 >= x.t_begin) && (t0 + kTile <= x.t_end);
+                    const bool full = (t0 >= x.full_lo) && (t0 + kTile <= x.full_hi);
                     stage_k<D, FP8>(kr, sm_k, lane);
                     __syncthreads();
                     issue_k_rows<D, FP8, UNIFORM>(kr, p, x, tile_t0(i + 1));
@@ -476,7 +490,7 @@ void decode_split_kernel(DecodeParams p) {
                     issue_v<D, FP8, UNIFORM>(vr, p, x, tile_t0(i + 1));
                 }
                 const int t0 = tile_t0(ct - 1);
-                const bool full = (t0 >= x.t_begin) && (t0 + kTile <= x.t_end);
+                const bool full = (t0 >= x.full_lo) && (t0 + kTile <= x.full_hi);
                 stage_k<D, FP8>(kr, sm_k, lane);
                 __syncthreads();
                 f32x4 s[2];
@@ -495,12 +509,14 @@ void decode_split_kernel(DecodeParams p) {
             const int r = 4 * grp + j;
             const float lr = __shfl(l_tot, r, 64);
             const float mr = __shfl(acc.m, r, 64);
-            if (r < G) {
-                const float inv = p.v_scale / lr;
+            if (r < p.rows) {
+                // (a column with no key: zero row, lse = -inf for the merge)
+                const float inv = lr > 0.f ? p.v_scale / lr : 0.f;
                 if (complete) {
                     uint16_t* o16 = static_cast<uint16_t*>(p.out) +
                                     (int64_t)b * p.out_stride_b +
-                                    (int64_t)(kvh * G + r) * D + VE * c;
+                                    (int64_t)(r / G) * p.out_stride_t +
+                                    (int64_t)(kvh * G + r % G) * D + VE * c;
                     uint32_t wv[VE / 2];
 #pragma unroll
                     for (int e = 0; e < VE; e += 2)

@@ -32,7 +32,8 @@ struct SeqRange {
 __device__ __forceinline__ SeqRange seq_range(const DecodeParams& p, int b) {
     SeqRange r;
     r.L = p.seq_lens[b];
-    r.lo = (p.window > 0 && r.L > p.window) ? r.L - p.window : 0;
+    // the first query token (position L - q_len) has the earliest window
+    r.lo = (p.window > 0 && r.L - p.q_len + 1 > p.window) ? r.L - p.q_len + 1 - p.window : 0;
     r.base = r.lo & ~(kTile - 1);
     r.tiles = r.L > r.lo ? (r.L - r.base + kTile - 1) / kTile : 0;
     return r;
@@ -93,7 +94,7 @@ __device__ __forceinline__ int64_t range_start(int64_t w, int64_t N, int64_t W) 
 // Partial slots of wave w: slot 0 holds its first segment when incomplete,
 // slot 1 its last one when incomplete (a middle segment is always complete).
 __device__ __forceinline__ int64_t part_row(const DecodeParams& p, int64_t w, int slot) {
-    return (w * 2 + slot) * p.group;
+    return (w * 2 + slot) * p.rows;
 }
 
 // Wave holding global tile t: the largest w with floor(w*N/W) <= t.

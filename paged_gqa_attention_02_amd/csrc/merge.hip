@@ -8,7 +8,8 @@ namespace pa {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Merge: one block per (segment, group of `rows` query-head rows).  Segments
+// Merge: one block per (segment, group of `per_block` rows; a row is a
+// (query token, query head) of the kv head).  Segments
 // inside one wave's range were written by the split pass; the others are
 // combined here from the partials of the waves w0..w1 that cover them, per
 // query-head row r,
@@ -24,23 +25,27 @@ namespace {
 constexpr int kMergeThreads = 512;
 
 template <int D>
-__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParams p, int rows) {
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParams p,
+                                                                     int per_block) {
     constexpr int kQ = D / 4;                // column quads per row
     constexpr int kBatch = 4;                // pieces in flight per thread
     const int G = p.group;
-    const int groups = G / rows;
-    const int items = rows * kQ;             // <= 16 * 32 = kMergeThreads
-    const int kR = kMergeThreads / items;    // piece lanes (rows and kQ are powers of 2)
+    const int groups = p.rows / per_block;   // blocks per segment
+    const int items = per_block * kQ;        // <= 16 * 32 = kMergeThreads
+    const int kR = kMergeThreads / items;    // piece lanes
+    // (rows not a power of two: the threads past kR * items only join the barrier)
+    const bool idle = (int)threadIdx.x >= kR * items;
     const int seg = blockIdx.x / groups;
     const int kvh = seg % p.num_kv_heads;
     const int b = seg / p.num_kv_heads;
     const int it = threadIdx.x % items, pl = threadIdx.x / items;
-    const int r = (blockIdx.x % groups) * rows + it / kQ, q = it % kQ;
+    // row r of the segment: query token r / G, head kvh*G + r % G
+    const int r = (blockIdx.x % groups) * per_block + it / kQ, q = it % kQ;
     const int L = p.seq_lens[b];
     const int4 rec = *reinterpret_cast<const int4*>(p.seg_rec + 4 * (int64_t)seg);
     // row r, columns 4q..4q+3 of out
     uint16_t* out = static_cast<uint16_t*>(p.out) + (int64_t)b * p.out_stride_b +
-                    (int64_t)(kvh * G + r) * D + 4 * q;
+                    (int64_t)(r / G) * p.out_stride_t + (int64_t)(kvh * G + r % G) * D + 4 * q;
     if (L <= 0) {
         if (pl == 0) *reinterpret_cast<u32x2*>(out) = u32x2{0u, 0u};
         return;
@@ -50,7 +55,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
 
     float m = -INFINITY, sum = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int i0 = pl; i0 < npieces; i0 += kR * kBatch) {
+    for (int i0 = idle ? npieces : pl; i0 < npieces; i0 += kR * kBatch) {
         float lse[kBatch];
         f32x4 o[kBatch];
 #pragma unroll
@@ -105,7 +110,8 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
         sum = S;
         acc = a;
     }
-    const float inv = 1.f / sum;
+    if (pl != 0) return;                     // (idle threads when kR == 1)
+    const float inv = sum > 0.f ? 1.f / sum : 0.f;   // (a row with no key: zeros)
     *reinterpret_cast<u32x2*>(out) =
         u32x2{pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv)};
 }
@@ -114,18 +120,19 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
 
 hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, int B, int Hkv,
                                hipStream_t stream) {
-    // Rows of a segment per block: all G when there are enough segments to
-    // fill the chip, fewer (more blocks, more piece lanes each) otherwise.
+    // Rows of a segment per block: all of them when there are enough segments
+    // to fill the chip, a divisor of them (more blocks, more piece lanes
+    // each) otherwise.
     const int64_t segs = (int64_t)B * Hkv;
-    int rows = p.group;
-    while (rows > 1 && segs * (p.group / rows) < 1024) rows /= 2;
-    dim3 grid((unsigned)(segs * (p.group / rows)));
+    int per_block = p.rows;
+    while (per_block % 2 == 0 && segs * (p.rows / per_block) < 1024) per_block /= 2;
+    dim3 grid((unsigned)(segs * (p.rows / per_block)));
     if (head_dim == 128)
         hipLaunchKernelGGL(decode_merge_kernel<128>, grid, dim3(kMergeThreads), 0, stream, p,
-                           rows);
+                           per_block);
     else
         hipLaunchKernelGGL(decode_merge_kernel<64>, grid, dim3(kMergeThreads), 0, stream, p,
-                           rows);
+                           per_block);
     return hipGetLastError();
 }
 

@@ -32,6 +32,10 @@ struct DecodeParams {
     int32_t num_q_heads;
     int32_t num_kv_heads;
     int32_t group;            // G = Hq / Hkv (1..16)
+    int32_t q_len;            // query rows per sequence (1: decode; > 1: verify)
+    int32_t rows;             // MFMA columns used: G * q_len <= 16; column c is query
+                              // token c / G, head c % G of the kv head
+    int64_t q_stride_t, out_stride_t;   // elements between a sequence's query tokens
     int32_t page_shift;       // log2(page_size)
     int32_t window;           // <= 0: off
     int32_t has_cap;
@@ -41,8 +45,8 @@ struct DecodeParams {
     float v_scale;
     void* out;                // bf16 [B, Hq, D], row stride out_stride_b
     int64_t out_stride_b;
-    float* part_o;            // [workers, 2, G, D]: partial of a segment a wave covers in part
-    float* part_lse;          // [workers, 2, G] (log2 domain)
+    float* part_o;            // [workers, 2, rows, D]: partial of a segment a wave covers in part
+    float* part_lse;          // [workers, 2, rows] (log2 domain)
     int32_t* seg_rec;         // [B * Hkv][4]: for a segment with keys, the waves owning its
                               // first and last tile and the first one's slot (written by
                               // the owner of the first tile).  Split pass -> merge.

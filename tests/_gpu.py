@@ -25,6 +25,21 @@ def run_decode(case, num_splits=None, tensors=None, pool_view=None):
     return out, pl
 
 
+def run_verify(case, q_bits, num_splits=None, tensors=None):
+    """paged_attn_verify on a decode case's cache with query rows q_bits
+    (bf16 bits [B, q_len, Hq, D])."""
+    t = tensors or I.decode_tensors(case, DEV)
+    q = I._dev(q_bits, DEV, torch.bfloat16)
+    ns = case.num_splits if num_splits is None else num_splits
+    pl = pa.verify_plan(q, t["k_pool"], t["block_table"], case.max_kv_len,
+                        window=case.window, num_splits=ns)
+    out = pa.verify(pl, q, t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
+                    case.scale, softcap=case.softcap, window=case.window,
+                    k_scale=case.k_scale, v_scale=case.v_scale)
+    torch.cuda.synchronize()
+    return out, pl
+
+
 def run_extend(case, tensors=None):
     t = tensors or I.extend_tensors(case, DEV)
     pl = pa.extend_plan(t["q"], t["k_pool"], t["block_table"], case.batch,

@@ -76,6 +76,9 @@ def plan_status(**kw):
     (dict(num_seqs=1 << 26), UNSUP),             # B x Hq reaches 2^31
     (dict(mode=1, total_q=100, max_q_len=0), SHAPE),
     (dict(mode=1, total_q=100, max_q_len=50), OK),
+    (dict(mode=2, max_q_len=4), OK),             # verify: G * q_len = 16
+    (dict(mode=2, max_q_len=5), UNSUP),          # 20 rows per kv head
+    (dict(mode=2, max_q_len=0), SHAPE),
 ])
 def test_plan_validation(kw, status):
     assert plan_status(**kw)[0] == status
@@ -157,6 +160,38 @@ def test_decode_empty_batch_launches_nothing():
 
 def test_decode_plan_mode_mismatch():
     assert decode_status(plan_kw=dict(mode=1, total_q=10, max_q_len=10)) == MISMATCH
+    assert decode_status(plan_kw=dict(mode=2, max_q_len=2)) == MISMATCH
+    assert decode_status(fn="paged_attn_verify") == MISMATCH
+
+
+VERIFY = dict(mode=2, max_q_len=4)
+ROW = 32 * 128
+
+
+def test_verify_plan_sizes_rows():
+    """The verify workspace holds G * q_len partial rows per slot."""
+    st, dec = plan_status()
+    st2, ver = plan_status(**VERIFY)
+    assert st == st2 == OK and ver.num_splits == dec.num_splits
+    assert ver.workspace_bytes >= ver.num_splits * 2 * 16 * 129 * 4
+    assert ver.workspace_bytes > 3 * dec.workspace_bytes
+    assert "verify" in pa.Plan(ver).describe()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q_stride_b=4 * ROW - 8, out_stride_b=4 * ROW), SHAPE),
+    (dict(q_stride_b=4 * ROW, out_stride_b=3 * ROW), SHAPE),
+    (dict(q_stride_b=4 * ROW, out_stride_b=4 * ROW, q=None), NULLP),
+    (dict(q_stride_b=4 * ROW, out_stride_b=4 * ROW, ws_bytes=100), WS),
+    (dict(q_stride_b=4 * ROW, out_stride_b=4 * ROW, window=3), MISMATCH),
+])
+def test_verify_validation(kw, status):
+    assert decode_status(plan_kw=VERIFY, fn="paged_attn_verify", **kw) == status
+
+
+def test_verify_empty_batch_launches_nothing():
+    assert decode_status(plan_kw=dict(VERIFY, num_seqs=0), fn="paged_attn_verify", q=None,
+                         out=None, ws=None) == OK
 
 
 # ---- cache append argument validation: fake, never dereferenced, pointers ----
