@@ -103,7 +103,7 @@ typedef struct {
     int32_t total_q;           /* extend: rows of q/k_new/v_new/out */
     int32_t max_q_len;         /* extend: bound on new tokens per sequence;
                                   verify: the query tokens per sequence
-                                  (q_len >= 1, G * q_len <= 16) */
+                                  (q_len >= 1, G * q_len <= 64) */
     int32_t num_splits;        /* decode: 0 = plan chooses; > 0 forces the
                                   number of split-pass pieces (waves) */
 } pa_problem;
@@ -113,9 +113,11 @@ typedef struct {
  * fixed capacities the same way). */
 typedef struct {
     pa_problem prob;
-    int32_t num_splits;        /* decode: split-pass pieces = persistent waves */
-    int32_t tokens_per_split;  /* decode: tile granularity of the pieces (32) */
-    int32_t waves_per_block;   /* decode: waves per block (1) */
+    int32_t num_splits;        /* decode/verify: split-pass pieces = persistent
+                                  blocks */
+    int32_t tokens_per_split;  /* decode/verify: tile granularity of the pieces (32) */
+    int32_t waves_per_block;   /* decode/verify: waves per block, one per 16
+                                  query rows (token, head) of a kv head */
     int32_t num_cus;           /* compute units the plan was made for */
     uint64_t workspace_bytes;  /* device scratch the compute call needs */
     int32_t reserved[8];
@@ -126,9 +128,11 @@ typedef struct {
  *
  * Decode: the 32-token tiles of every (sequence, kv head) key range [lo, L)
  * (lo = max(0, L-W) with a window), laid end to end, are cut into
- * out->num_splits equal contiguous pieces, one per persistent wave of the
+ * out->num_splits equal contiguous pieces, one per persistent block of the
  * split pass; the plan takes as many as the device keeps resident (compute
- * units x resident waves per unit), or prob->num_splits when that is > 0.
+ * units x resident blocks per unit), or prob->num_splits when that is > 0.
+ * A block has one wave per 16 query rows of a kv head (G for decode,
+ * G * q_len for verify); its waves walk the same tiles.
  * Pieces of one key range are merged by log-sum-exp (the split partition
  * and merge of `_fwd_kernel_stage1/2`; any partition gives the same result).
  * Verify: as decode, with lo = max(0, L - q_len + 1 - W), the window start of
@@ -162,7 +166,7 @@ pa_status paged_attn_plan(const pa_problem* prob, int hip_device, pa_plan* out);
  *
  * Two kernels run: the key ranges of all (sequence, kv head) pairs, laid end
  * to end, are cut into plan->num_splits equal pieces, one per persistent
- * wave of the split pass; a second kernel merges by log-sum-exp every pair
+ * block of the split pass; a second kernel merges by log-sum-exp every pair
  * that spans several pieces (the split/merge of `_fwd_grouped_kernel_stage1`
  * / `_fwd_kernel_stage2`).
  */
@@ -225,9 +229,10 @@ pa_status paged_attn_decode_merge(const pa_plan* plan,
  *   out           bf16 [B, q_len, Hq, D], sequence stride out_stride_b
  *                 (>= q_len*Hq*D)
  *
- * The G*q_len (token, head) rows of a kv head share every K/V tile load: one
- * pass over the cache serves all q_len tokens.  Same kernels, workspace rules
- * and errors as paged_attn_decode.
+ * The G*q_len (token, head) rows of a kv head are served by one block (a
+ * wave per 16 rows) walking each K/V tile once from HBM: one pass over the
+ * cache serves all q_len tokens.  Same kernels, workspace rules and errors as
+ * paged_attn_decode.
  */
 pa_status paged_attn_verify(const pa_plan* plan,
                             const void* q, int64_t q_stride_b,

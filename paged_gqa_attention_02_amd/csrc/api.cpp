@@ -51,9 +51,9 @@ pa_status check_problem(const pa_problem& pr) {
     if ((int64_t)pr.max_pages_per_seq < cdiv(pr.max_kv_len, pr.page_size))
         return PA_ERR_INVALID_SHAPE;
     if (pr.mode == PA_MODE_VERIFY) {
-        // max_q_len query rows per sequence, G * q_len MFMA columns (<= 16)
+        // max_q_len query rows per sequence: G * q_len MFMA columns, 16 per wave
         if (pr.max_q_len < 1) return PA_ERR_INVALID_SHAPE;
-        if ((int64_t)G * pr.max_q_len > 16) return PA_ERR_UNSUPPORTED;
+        if ((int64_t)G * pr.max_q_len > kMaxDecodeRows) return PA_ERR_UNSUPPORTED;
     }
     if (pr.mode == PA_MODE_EXTEND) {
         if (pr.total_q < 0 || pr.max_q_len < 0) return PA_ERR_INVALID_SHAPE;
@@ -65,6 +65,12 @@ pa_status check_problem(const pa_problem& pr) {
         if (tiles * pr.num_seqs * pr.num_kv_heads >= ((int64_t)1 << 31)) return PA_ERR_UNSUPPORTED;
     }
     return PA_OK;
+}
+
+// Split-pass waves per block: one per 16 query rows of a kv head.
+int decode_waves_per_block(const pa_problem& pr) {
+    const int q_len = pr.mode == PA_MODE_VERIFY ? pr.max_q_len : 1;
+    return ((pr.num_q_heads / pr.num_kv_heads) * q_len + 15) / 16;
 }
 
 int elem_bytes(int kv_dtype) { return kv_dtype == PA_KV_FP8_E4M3 ? 1 : 2; }
@@ -139,20 +145,23 @@ pa_status paged_attn_plan(const pa_problem* prob, int hip_device, pa_plan* out) 
     pl.tokens_per_split = kTile;
 
     if (pr.mode == PA_MODE_DECODE || pr.mode == PA_MODE_VERIFY) {
-        // Split pass: persistent waves, each owning an equal contiguous range
-        // of the tiles of all segments.  By default as many as the device
-        // keeps resident; prob.num_splits > 0 forces the count.
+        // Split pass: persistent blocks, each owning an equal contiguous range
+        // of the tiles of all segments, one wave per 16 query rows of a
+        // segment.  By default as many blocks as the device keeps resident;
+        // prob.num_splits > 0 forces the count.
+        const int nw = decode_waves_per_block(pr);
         int64_t workers;
         if (pr.num_splits > 0) {
             workers = pr.num_splits;
         } else {
-            int per_cu = kDefaultWavesPerCu;
+            int per_cu = kDefaultWavesPerCu / nw;
             if (hip_device >= 0) {
                 int cur = -1;
                 if (hipGetDevice(&cur) != hipSuccess) return PA_ERR_HIP;
                 if (cur != hip_device && hipSetDevice(hip_device) != hipSuccess) return PA_ERR_HIP;
-                const hipError_t e = decode_waves_per_cu(pr.head_dim, pr.kv_dtype == PA_KV_FP8_E4M3,
-                                                         pr.page_size >= 16, &per_cu);
+                const hipError_t e = decode_blocks_per_cu(pr.head_dim,
+                                                          pr.kv_dtype == PA_KV_FP8_E4M3,
+                                                          pr.page_size >= 16, nw, &per_cu);
                 if (cur != hip_device) (void)hipSetDevice(cur);
                 if (e != hipSuccess || per_cu < 1) return PA_ERR_HIP;
             }
@@ -161,7 +170,7 @@ pa_status paged_attn_plan(const pa_problem* prob, int hip_device, pa_plan* out) 
         if (workers > kMaxWorkers) return PA_ERR_UNSUPPORTED;
         pl.num_splits = (int32_t)workers;
         pl.tokens_per_split = kTile;
-        pl.waves_per_block = 1;
+        pl.waves_per_block = nw;
         const int64_t q_len = pr.mode == PA_MODE_VERIFY ? pr.max_q_len : 1;
         const int64_t rows = workers * 2 * (pr.num_q_heads / pr.num_kv_heads) * q_len;
         // partial rows, their log-sum-exp, and one record per segment
@@ -217,7 +226,8 @@ pa_status decode_impl(int passes, int mode, const pa_plan* plan, const void* q, 
     if (st != PA_OK) return st;
     if (pr.mode != mode) return PA_ERR_PLAN_MISMATCH;
     if (page_size != pr.page_size || window != pr.window) return PA_ERR_PLAN_MISMATCH;
-    if (pl.tokens_per_split != kTile || pl.num_splits < 1 || pl.num_splits > kMaxWorkers)
+    if (pl.tokens_per_split != kTile || pl.num_splits < 1 || pl.num_splits > kMaxWorkers ||
+        pl.waves_per_block != decode_waves_per_block(pr))
         return PA_ERR_PLAN_MISMATCH;
     if (pr.num_seqs == 0) return PA_OK;
     if (!q || !seq_lens || !out) return PA_ERR_NULL_POINTER;
@@ -282,8 +292,8 @@ pa_status decode_impl(int passes, int mode, const pa_plan* plan, const void* q, 
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     const bool uniform = pr.page_size >= 16;
     if ((passes & kSplitPass) &&
-        launch_decode(p, pr.head_dim, pr.kv_dtype == PA_KV_FP8_E4M3, uniform, pl.num_splits,
-                      stream) != hipSuccess)
+        launch_decode(p, pr.head_dim, pr.kv_dtype == PA_KV_FP8_E4M3, uniform,
+                      pl.waves_per_block, pl.num_splits, stream) != hipSuccess)
         return PA_ERR_HIP;
     if ((passes & kMergePass) &&
         launch_decode_merge(p, pr.head_dim, pr.num_seqs, pr.num_kv_heads, stream) !=

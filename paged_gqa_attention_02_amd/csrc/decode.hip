@@ -352,28 +352,35 @@ __device__ __forceinline__ void tile_pv(Acc<D>& A, VRegs<D, FP8>& R, u32x4 pop,
 // ---------------------------------------------------------------------------
 // Split pass: persistent waves, one contiguous range of tiles each
 // ---------------------------------------------------------------------------
-template <int D, bool FP8, bool UNIFORM, bool CAP>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kDecodeOccupancy)))
+template <int D, bool FP8, bool UNIFORM, bool CAP, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(kDecodeOccupancy)))
 void decode_split_kernel(DecodeParams p) {
     constexpr int KK = D / 32;                  // QK MFMAs per 16-token half
     constexpr int VE = D / 16;                  // PV MFMAs per tile
 
-    const int lane = threadIdx.x;
+    // NW waves per block walk the same tiles; wave wv owns the 16 MFMA
+    // columns (query rows) 16*wv .. 16*wv + 15 of the segment.
+    const int lane = threadIdx.x & 63;
+    const int wv = NW == 1 ? 0 : (int)(threadIdx.x >> 6);
     const int c = lane & 15;
     const int grp = lane >> 4;
+    const int cg = 16 * wv + c;                 // this lane's query row
     const int G = p.group;
     const int64_t W = gridDim.x;
     const int64_t w = blockIdx.x;
 
     __shared__ int sm_pages[kMaxSplitPages];
-    __shared__ __attribute__((aligned(16))) uint8_t sm_k[kTile * KRowRegs<D, FP8>::kLdsStride];
+    __shared__ __attribute__((aligned(16)))
+    uint8_t sm_kw[NW][kTile * KRowRegs<D, FP8>::kLdsStride];
+    uint8_t* const sm_k = sm_kw[wv];            // the wave's own K tile
 
     const int64_t N = total_tiles(p);
     const int64_t r0 = range_start(w, N, W);
     const int64_t r1 = range_start(w + 1, N, W);
     if (r0 >= r1) {
         // an empty range (N < W): the merge may read this wave's slot 0
-        if (lane < p.rows) p.part_lse[part_row(p, w, 0) + lane] = -INFINITY;
+        for (int i = threadIdx.x; i < p.rows; i += 64 * NW)
+            p.part_lse[part_row(p, w, 0) + i] = -INFINITY;
         return;
     }
 
@@ -396,7 +403,7 @@ void decode_split_kernel(DecodeParams p) {
         const int64_t seg_end = seq_start + (int64_t)(kvh + 1) * n;
         const int cnt = (int)(min(r1, seg_end) - pos);
         const bool complete = (i0 == 0) && (cnt == n);
-        if (i0 == 0 && lane == 0) {
+        if (i0 == 0 && threadIdx.x == 0) {
             // this wave owns the segment's first tile: tell the merge which
             // waves cover it
             const int64_t w_last = complete ? w : tile_owner(seg_end - 1, N, W);
@@ -404,12 +411,13 @@ void decode_split_kernel(DecodeParams p) {
                 int4{(int)w, (int)w_last, slot, 0};
         }
 
-        // ---- Q^T as the B operand: column c = query token c / G, head
-        // kvh*G + c % G.  The contraction index (grp, j) of MFMA kk stands for
-        // d = dq(kk, grp) + j; for fp8 K one 16-byte load feeds two MFMAs.
+        // ---- Q^T as the B operand: column c is query row cg = 16*wv + c,
+        // token cg / G, head kvh*G + cg % G.  The contraction index (grp, j) of
+        // MFMA kk stands for d = dq(kk, grp) + j; for fp8 K one 16-byte load
+        // feeds two MFMAs.
         u32x4 qop[KK];
         {
-            const int cc = c < p.rows ? c : 0;
+            const int cc = cg < p.rows ? cg : 0;
             const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
                                    (int64_t)b * p.q_stride_b + (int64_t)(cc / G) * p.q_stride_t +
                                    (int64_t)(kvh * G + cc % G) * D;
@@ -417,7 +425,7 @@ void decode_split_kernel(DecodeParams p) {
             for (int kk = 0; kk < KK; ++kk) {
                 const int d0 = FP8 ? 64 * (kk / 2) + 16 * grp + 8 * (kk % 2) : 32 * kk + 8 * grp;
                 const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + d0);
-                qop[kk] = (c < p.rows) ? v : u32x4{0, 0, 0, 0};
+                qop[kk] = (cg < p.rows) ? v : u32x4{0, 0, 0, 0};
             }
         }
 
@@ -441,9 +449,9 @@ void decode_split_kernel(DecodeParams p) {
                 x.v_lane[r] = head + kVBytes * c + (UNIFORM ? (4 * grp + r) * x.tok_bytes : 0);
         }
         x.pages = sm_pages;
-        // causal limit and window start of this lane's column (query token c / G
-        // at position L - q_len + c / G); for decode these never bind
-        x.lim = sr.L - p.q_len + (c < p.rows ? c / G : 0);
+        // causal limit and window start of this lane's column (query token
+        // cg / G at position L - q_len + cg / G); for decode these never bind
+        x.lim = sr.L - p.q_len + (cg < p.rows ? cg / G : 0);
         x.wlo = p.window > 0 ? x.lim - p.window + 1 : INT_MIN;
 
         // ---- the piece's tiles, chunk by chunk (page list staged in LDS) ----
@@ -461,7 +469,7 @@ void decode_split_kernel(DecodeParams p) {
             {
                 const int32_t* bt_row =
                     p.block_table + (int64_t)b * p.bt_stride + x.first_page;
-                for (int i = lane; i < n_pages; i += 64) sm_pages[i] = bt_row[i];
+                for (int i = threadIdx.x; i < n_pages; i += 64 * NW) sm_pages[i] = bt_row[i];
             }
             __syncthreads();
 
@@ -502,31 +510,33 @@ void decode_split_kernel(DecodeParams p) {
         }
 
         // ---- finish the piece: sum over the 4 lanes of each column, then
-        // row r = 4*grp + j of O (head of column r) is normalised and stored ----
+        // row r = 4*grp + j of O (query row rg = 16*wv + r) is normalised and
+        // stored ----
         const float l_tot = col4_sum(acc.l);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = 4 * grp + j;
+            const int rg = 16 * wv + r;
             const float lr = __shfl(l_tot, r, 64);
             const float mr = __shfl(acc.m, r, 64);
-            if (r < p.rows) {
+            if (rg < p.rows) {
                 // (a column with no key: zero row, lse = -inf for the merge)
                 const float inv = lr > 0.f ? p.v_scale / lr : 0.f;
                 if (complete) {
                     uint16_t* o16 = static_cast<uint16_t*>(p.out) +
                                     (int64_t)b * p.out_stride_b +
-                                    (int64_t)(r / G) * p.out_stride_t +
-                                    (int64_t)(kvh * G + r % G) * D + VE * c;
-                    uint32_t wv[VE / 2];
+                                    (int64_t)(rg / G) * p.out_stride_t +
+                                    (int64_t)(kvh * G + rg % G) * D + VE * c;
+                    uint32_t ov[VE / 2];
 #pragma unroll
                     for (int e = 0; e < VE; e += 2)
-                        wv[e / 2] = pack_bf16x2(acc.o[e][j] * inv, acc.o[e + 1][j] * inv);
+                        ov[e / 2] = pack_bf16x2(acc.o[e][j] * inv, acc.o[e + 1][j] * inv);
                     if constexpr (VE == 8)
-                        *reinterpret_cast<u32x4*>(o16) = u32x4{wv[0], wv[1], wv[2], wv[3]};
+                        *reinterpret_cast<u32x4*>(o16) = u32x4{ov[0], ov[1], ov[2], ov[3]};
                     else
-                        *reinterpret_cast<u32x2*>(o16) = u32x2{wv[0], wv[1]};
+                        *reinterpret_cast<u32x2*>(o16) = u32x2{ov[0], ov[1]};
                 } else {
-                    const int64_t row = part_row(p, w, slot) + r;
+                    const int64_t row = part_row(p, w, slot) + rg;
                     float* po = p.part_o + row * D + VE * c;
 #pragma unroll
                     for (int e = 0; e < VE; e += 4)
@@ -551,52 +561,52 @@ void decode_split_kernel(DecodeParams p) {
     }
 }
 
-template <int D, bool FP8, bool UNIFORM>
-hipError_t launch_decode_t(const DecodeParams& p, int workers, hipStream_t stream) {
-    dim3 grid(workers);
-    if (p.has_cap)
-        hipLaunchKernelGGL((decode_split_kernel<D, FP8, UNIFORM, true>), grid, dim3(64), 0,
-                           stream, p);
-    else
-        hipLaunchKernelGGL((decode_split_kernel<D, FP8, UNIFORM, false>), grid, dim3(64), 0,
-                           stream, p);
-    return hipGetLastError();
+using SplitFn = void (*)(DecodeParams);
+
+template <int D, bool FP8, bool UNIFORM, bool CAP>
+SplitFn split_by_waves(int nw) {
+    switch (nw) {
+        case 1: return decode_split_kernel<D, FP8, UNIFORM, CAP, 1>;
+        case 2: return decode_split_kernel<D, FP8, UNIFORM, CAP, 2>;
+        case 3: return decode_split_kernel<D, FP8, UNIFORM, CAP, 3>;
+        case 4: return decode_split_kernel<D, FP8, UNIFORM, CAP, 4>;
+        default: return nullptr;
+    }
 }
 
-template <int D, bool FP8, bool UNIFORM>
-const void* split_kernel_ptr() {
-    return reinterpret_cast<const void*>(&decode_split_kernel<D, FP8, UNIFORM, false>);
+template <int D, bool FP8>
+SplitFn split_by_pages(bool uniform, bool cap, int nw) {
+    if (uniform) return cap ? split_by_waves<D, FP8, true, true>(nw)
+                            : split_by_waves<D, FP8, true, false>(nw);
+    return cap ? split_by_waves<D, FP8, false, true>(nw) : split_by_waves<D, FP8, false, false>(nw);
+}
+
+SplitFn split_kernel(int head_dim, bool fp8, bool uniform, bool cap, int nw) {
+    if (head_dim == 128)
+        return fp8 ? split_by_pages<128, true>(uniform, cap, nw)
+                   : split_by_pages<128, false>(uniform, cap, nw);
+    if (head_dim == 64)
+        return fp8 ? split_by_pages<64, true>(uniform, cap, nw)
+                   : split_by_pages<64, false>(uniform, cap, nw);
+    return nullptr;
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams& p, int head_dim, bool fp8, bool uniform_pages,
-                         int workers, hipStream_t stream) {
-    if (head_dim == 128) {
-        if (fp8) return uniform_pages ? launch_decode_t<128, true, true>(p, workers, stream)
-                                      : launch_decode_t<128, true, false>(p, workers, stream);
-        return uniform_pages ? launch_decode_t<128, false, true>(p, workers, stream)
-                             : launch_decode_t<128, false, false>(p, workers, stream);
-    }
-    if (fp8) return uniform_pages ? launch_decode_t<64, true, true>(p, workers, stream)
-                                  : launch_decode_t<64, true, false>(p, workers, stream);
-    return uniform_pages ? launch_decode_t<64, false, true>(p, workers, stream)
-                         : launch_decode_t<64, false, false>(p, workers, stream);
+                         int waves_per_block, int workers, hipStream_t stream) {
+    const SplitFn f = split_kernel(head_dim, fp8, uniform_pages, p.has_cap != 0, waves_per_block);
+    if (!f) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(f, dim3(workers), dim3(64 * waves_per_block), 0, stream, p);
+    return hipGetLastError();
 }
 
-hipError_t decode_waves_per_cu(int head_dim, bool fp8, bool uniform_pages, int* out) {
-    const void* f;
-    if (head_dim == 128)
-        f = fp8 ? (uniform_pages ? split_kernel_ptr<128, true, true>()
-                                 : split_kernel_ptr<128, true, false>())
-                : (uniform_pages ? split_kernel_ptr<128, false, true>()
-                                 : split_kernel_ptr<128, false, false>());
-    else
-        f = fp8 ? (uniform_pages ? split_kernel_ptr<64, true, true>()
-                                 : split_kernel_ptr<64, true, false>())
-                : (uniform_pages ? split_kernel_ptr<64, false, true>()
-                                 : split_kernel_ptr<64, false, false>());
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, f, 64, 0);
+hipError_t decode_blocks_per_cu(int head_dim, bool fp8, bool uniform_pages, int waves_per_block,
+                                int* out) {
+    const SplitFn f = split_kernel(head_dim, fp8, uniform_pages, false, waves_per_block);
+    if (!f) return hipErrorInvalidValue;
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, reinterpret_cast<const void*>(f),
+                                                        64 * waves_per_block, 0);
 }
 
 }  // namespace pa

@@ -31,7 +31,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
     constexpr int kBatch = 4;                // pieces in flight per thread
     const int G = p.group;
     const int groups = p.rows / per_block;   // blocks per segment
-    const int items = per_block * kQ;        // <= 16 * 32 = kMergeThreads
+    const int items = per_block * kQ;        // <= kMergeThreads (the launch caps per_block)
     const int kR = kMergeThreads / items;    // piece lanes
     // (rows not a power of two: the threads past kR * items only join the barrier)
     const bool idle = (int)threadIdx.x >= kR * items;
@@ -124,7 +124,10 @@ hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, int B, int H
     // to fill the chip, a divisor of them (more blocks, more piece lanes
     // each) otherwise.
     const int64_t segs = (int64_t)B * Hkv;
+    // at most kMergeThreads / (D/4) rows per block (16 for D = 128)
+    const int max_rows = kMergeThreads / (head_dim / 4);
     int per_block = p.rows;
+    while (per_block > max_rows || p.rows % per_block) --per_block;
     while (per_block % 2 == 0 && segs * (p.rows / per_block) < 1024) per_block /= 2;
     dim3 grid((unsigned)(segs * (p.rows / per_block)));
     if (head_dim == 128)

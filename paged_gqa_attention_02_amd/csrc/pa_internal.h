@@ -101,12 +101,16 @@ struct AppendParams {
 };
 
 hipError_t launch_cache_append(const AppendParams& p, bool fp8, hipStream_t stream);
+// Split pass: `workers` persistent blocks of waves_per_block (1..4) waves; wave
+// i of a block serves query rows 16i..16i+15 of every segment.
 hipError_t launch_decode(const DecodeParams& p, int head_dim, bool fp8, bool uniform_pages,
-                         int workers, hipStream_t stream);
+                         int waves_per_block, int workers, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, int num_seqs,
                                int num_kv_heads, hipStream_t stream);
-// Resident split-pass waves per compute unit (occupancy of the kernel variant).
-hipError_t decode_waves_per_cu(int head_dim, bool fp8, bool uniform_pages, int* out);
+// Resident split-pass blocks per compute unit (occupancy of the kernel variant).
+hipError_t decode_blocks_per_cu(int head_dim, bool fp8, bool uniform_pages, int waves_per_block,
+                                int* out);
+constexpr int kMaxDecodeRows = 64;   // query rows per kv head: 16 per wave, 4 waves
 hipError_t launch_gather(const GatherParams& p, int head_dim, bool fp8, hipStream_t stream);
 hipError_t launch_extend(const ExtendParams& p, int head_dim, bool fp8, int num_seqs,
                          hipStream_t stream);

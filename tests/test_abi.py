@@ -77,7 +77,8 @@ def plan_status(**kw):
     (dict(mode=1, total_q=100, max_q_len=0), SHAPE),
     (dict(mode=1, total_q=100, max_q_len=50), OK),
     (dict(mode=2, max_q_len=4), OK),             # verify: G * q_len = 16
-    (dict(mode=2, max_q_len=5), UNSUP),          # 20 rows per kv head
+    (dict(mode=2, max_q_len=16), OK),            # 64 rows per kv head: 4 waves
+    (dict(mode=2, max_q_len=17), UNSUP),         # 68 rows per kv head
     (dict(mode=2, max_q_len=0), SHAPE),
 ])
 def test_plan_validation(kw, status):
@@ -169,13 +170,19 @@ ROW = 32 * 128
 
 
 def test_verify_plan_sizes_rows():
-    """The verify workspace holds G * q_len partial rows per slot."""
+    """The verify workspace holds G * q_len partial rows per slot; a block
+    has one wave per 16 rows, and the plan keeps 8 waves per compute unit."""
     st, dec = plan_status()
     st2, ver = plan_status(**VERIFY)
     assert st == st2 == OK and ver.num_splits == dec.num_splits
+    assert dec.waves_per_block == ver.waves_per_block == 1
     assert ver.workspace_bytes >= ver.num_splits * 2 * 16 * 129 * 4
     assert ver.workspace_bytes > 3 * dec.workspace_bytes
     assert "verify" in pa.Plan(ver).describe()
+    for q_len, nw, blocks in [(5, 2, 4), (8, 2, 4), (12, 3, 2), (16, 4, 2)]:
+        st, pl = plan_status(mode=2, max_q_len=q_len)
+        assert st == OK and pl.waves_per_block == nw and pl.num_splits == 256 * blocks
+        assert pl.workspace_bytes >= pl.num_splits * 2 * 4 * q_len * 129 * 4
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -187,6 +194,16 @@ def test_verify_plan_sizes_rows():
 ])
 def test_verify_validation(kw, status):
     assert decode_status(plan_kw=VERIFY, fn="paged_attn_verify", **kw) == status
+
+
+def test_verify_plan_waves_must_match():
+    st, pl = plan_status(mode=2, max_q_len=8)
+    assert st == OK
+    pl.waves_per_block = 1
+    args = [A, 4 * ROW * 2, A, A, 16 * 8 * 128, 8 * 128, 128, 10, A, 256, A, 16, 0.1, 0.0, 0,
+            1.0, 1.0, A, 4 * ROW * 2, A, pl.workspace_bytes, None]
+    v = [ctypes.c_void_p(x) if i in (0, 2, 3, 8, 10, 17, 19) else x for i, x in enumerate(args)]
+    assert pa.lib().paged_attn_verify(ctypes.byref(pl), *v) == MISMATCH
 
 
 def test_verify_empty_batch_launches_nothing():

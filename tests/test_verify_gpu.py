@@ -66,6 +66,28 @@ def test_verify_forced_splits(splits):
     check(case, q, num_splits=splits, what=f"splits<={splits}")
 
 
+@pytest.mark.parametrize("lens,Hq,Hkv,D,P,q_len,kw", [
+    ([1, 4, 6, 9, 300, 2100], 32, 8, 128, 16, 8, {}),               # 32 rows: 2 waves
+    ([3, 700, 1500], 32, 8, 128, 16, 5, dict(softcap=30.0)),        # 20 rows
+    ([5, 900, 3000], 64, 8, 128, 16, 8,                              # 64 rows: 4 waves
+     dict(kv_dtype="fp8_e4m3", scale_range=(0.5, 2.0), window=512)),
+    ([17, 1000], 48, 3, 64, 8, 3, {}),                              # 48 rows: 3 waves, D 64
+    ([40, 600, 2], 4, 4, 128, 1, 40, dict(window=25)),              # MHA, 40 rows, P 1
+    ([33, 65, 1200], 16, 16, 64, 32, 17, {}),                       # 17 rows (prime)
+])
+def test_verify_many_rows(lens, Hq, Hkv, D, P, q_len, kw):
+    """More than 16 query rows per kv head: one wave per 16 rows, all of a
+    block's waves walking the same tiles."""
+    case, q = verify_case(lens, Hq, Hkv, D, P, q_len, 400 + q_len, **kw)
+    check(case, q, what="many rows")
+
+
+@pytest.mark.parametrize("splits", [3, 40, 3000])
+def test_verify_many_rows_forced_splits(splits):
+    case, q = verify_case([2500, 9, 800], 64, 8, 128, 16, 6, 88, softcap=20.0)
+    check(case, q, num_splits=splits, what=f"48 rows splits<={splits}")
+
+
 def test_verify_one_token_is_decode():
     """q_len = 1 runs the decode computation: identical bits to paged_attn_decode."""
     case, q = verify_case([37, 500, 4000], 32, 8, 128, 16, 1, 91, softcap=30.0)
