@@ -43,8 +43,11 @@ def parse():
     ap.add_argument("--splits", type=int, default=0, help="force the decode split cap")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU-baseline budget (0 disables the oracle leg)")
-    ap.add_argument("--op", default="attention", choices=["attention", "append"],
-                    help="append: KV-cache append of the extend workload's new tokens")
+    ap.add_argument("--op", default="attention", choices=["attention", "append", "verify"],
+                    help="append: KV-cache append of the extend workload's new tokens; "
+                         "verify: --q-len query tokens per sequence on a decode workload")
+    ap.add_argument("--q-len", type=int, default=4,
+                    help="query tokens per sequence for --op verify (1 + speculative tokens)")
     ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8_e4m3"],
                     help="cache element type for --op append")
     ap.add_argument("--copy-probe", action="store_true",
@@ -193,6 +196,60 @@ def bench_decode(args, torch, pa, I):
     return res
 
 
+def bench_verify(args, torch, pa, I):
+    """Speculative verify: a decode workload's batch with q_len query tokens
+    per sequence (its last q_len cached tokens), one split pass and merge."""
+    import numpy as np
+    dev = "cuda:0"
+    case = I.decode_config(args.workload, page_size=args.page_size)
+    ql = args.q_len
+    alg = case.verify_bytes(ql)
+    copies = max(2, math.ceil(2 * MALL_BYTES / max(case.kv_bytes(), 1)) + 1)
+    tensors = [I.decode_tensors(case, dev) for _ in range(copies)]
+    rng = np.random.default_rng(1000 + args.workload)
+    q = I._dev(I.bf16_bits(rng.standard_normal(
+        (case.batch, ql, case.num_q_heads, case.head_dim), dtype=np.float32)), dev,
+        torch.bfloat16)
+    t0 = tensors[0]
+    plan = pa.verify_plan(q, t0["k_pool"], t0["block_table"], case.max_kv_len,
+                          window=case.window, num_splits=args.splits)
+    out = torch.empty_like(q)
+    ws = pa.workspace_for(plan, dev)
+
+    def step(i):
+        t = tensors[i % copies]
+        pa.verify(plan, q, t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
+                  case.scale, softcap=case.softcap, window=case.window,
+                  k_scale=case.k_scale, v_scale=case.v_scale, out=out, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    K = args.steps
+    ms_step, ev_ms = time_steps(torch, step, K)
+    achieved = alg / (ev_ms * 1e-3) / 1e9
+    rows = ql * case.num_q_heads // case.num_kv_heads
+    return {
+        "metric": "paged-attn verify KV GB/s (fraction of HBM peak) + us/call on 1 MI355X",
+        "value": alg / (ms_step * 1e-3) / 1e9, "unit": "GB/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if case.kv_dtype == "bf16" else "fp8_e4m3 KV, bf16 Q/out",
+        "data": "synthetic",
+        "config": {"workload": f"{case.name} verify, q_len {ql}", "batch": case.batch,
+                   "q_len": ql, "rows_per_kv_head": rows,
+                   "num_q_heads": case.num_q_heads, "num_kv_heads": case.num_kv_heads,
+                   "head_dim": case.head_dim, "page_size": case.page_size,
+                   "kv_dtype": case.kv_dtype, "window": case.window,
+                   "softcap": case.softcap, "total_tokens": int(case.seq_lens.sum()),
+                   "seed": args.workload, "input_copies": copies},
+        "us_per_call": ev_ms * 1e3, "algorithmic_bytes": alg,
+        "plan": plan.describe(),
+        "roofline": {"bound": "hbm", "kernel": "decode_split + merge (whole call)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+    }
+
+
 def bench_extend(args, torch, pa, I):
     dev = "cuda:0"
     case = I.extend_config(5)
@@ -314,6 +371,10 @@ def main():
     pa.lib()
     if args.op == "append":
         res = bench_append(args, torch, pa, I)
+    elif args.op == "verify":
+        if args.workload == 5:
+            sys.exit("bench.py: --op verify runs on a decode workload (1-4)")
+        res = bench_verify(args, torch, pa, I)
     elif args.workload == 5:
         res = bench_extend(args, torch, pa, I)
     else:

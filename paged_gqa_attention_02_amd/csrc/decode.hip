@@ -131,11 +131,13 @@ __device__ __forceinline__ int64_t page_of(const TileCtx& x, int pshift, int t) 
     return (int64_t)x.pages[idx];
 }
 
-// Streaming loads of K/V rows: every byte is read once, so they bypass
-// cache retention (nontemporal).
-template <typename T>
+// Loads of K/V rows.  With one wave per block every byte is read once, so
+// they bypass cache retention (nontemporal, NT); the waves of a larger block
+// read the same rows, and plain loads let the later ones hit in L2.
+template <typename T, bool NT>
 __device__ __forceinline__ T load_stream(const uint8_t* ptr) {
-    return __builtin_nontemporal_load(reinterpret_cast<const T*>(ptr));
+    if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const T*>(ptr));
+    else return *reinterpret_cast<const T*>(ptr);
 }
 
 // K rows of a tile loaded whole (every wave load instruction reads complete
@@ -152,7 +154,7 @@ struct KRowRegs {
     u32x4 w[N];
 };
 
-template <int D, bool FP8, bool UNIFORM>
+template <int D, bool FP8, bool UNIFORM, bool NT>
 __device__ __forceinline__ void issue_k_rows(KRowRegs<D, FP8>& R, const DecodeParams& p,
                                              const TileCtx& x, int t0) {
     using KR = KRowRegs<D, FP8>;
@@ -171,7 +173,7 @@ __device__ __forceinline__ void issue_k_rows(KRowRegs<D, FP8>& R, const DecodePa
             ptr = pool + page_of<false>(x, p.page_shift, t) * x.page_bytes +
                   (int64_t)((t & pmask) * x.tok_bytes + x.k_row_lane);
         }
-        R.w[i] = load_stream<u32x4>(ptr);
+        R.w[i] = load_stream<u32x4, NT>(ptr);
     }
 }
 
@@ -218,7 +220,7 @@ struct VRegs {
     typename VRow<D, FP8>::Raw w[8];
 };
 
-template <int D, bool FP8, bool UNIFORM>
+template <int D, bool FP8, bool UNIFORM, bool NT>
 __device__ __forceinline__ void issue_v(VRegs<D, FP8>& R, const DecodeParams& p,
                                         const TileCtx& x, int t0) {
     using Raw = typename VRow<D, FP8>::Raw;
@@ -231,7 +233,7 @@ __device__ __forceinline__ void issue_v(VRegs<D, FP8>& R, const DecodeParams& p,
             const uint8_t* base = pool + page_of<true>(x, p.page_shift, th) * x.page_bytes +
                                   (int64_t)((th & pmask) * x.tok_bytes);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) R.w[4 * h + r] = load_stream<Raw>(base + x.v_lane[r]);
+            for (int r = 0; r < 4; ++r) R.w[4 * h + r] = load_stream<Raw, NT>(base + x.v_lane[r]);
         }
     } else {
 #pragma unroll
@@ -239,7 +241,7 @@ __device__ __forceinline__ void issue_v(VRegs<D, FP8>& R, const DecodeParams& p,
             const int t = t0 + tile_token(x.grp, i);
             const uint8_t* ptr = pool + page_of<false>(x, p.page_shift, t) * x.page_bytes +
                                  (int64_t)((t & pmask) * x.tok_bytes + x.v_lane[0]);
-            R.w[i] = load_stream<Raw>(ptr);
+            R.w[i] = load_stream<Raw, NT>(ptr);
         }
     }
 }
@@ -482,20 +484,20 @@ void decode_split_kernel(DecodeParams p) {
                 KRowRegs<D, FP8> kr;
                 VRegs<D, FP8> vr;
                 auto tile_t0 = [&](int i) { return tile0 + min(i, ct - 1) * kTile; };
-                issue_k_rows<D, FP8, UNIFORM>(kr, p, x, tile_t0(0));
-                issue_v<D, FP8, UNIFORM>(vr, p, x, tile_t0(0));
+                issue_k_rows<D, FP8, UNIFORM, NW == 1>(kr, p, x, tile_t0(0));
+                issue_v<D, FP8, UNIFORM, NW == 1>(vr, p, x, tile_t0(0));
                 for (int i = 0; i + 1 < ct; ++i) {
                     const int t0 = tile_t0(i);
                     const bool full = (t0 >= x.full_lo) && (t0 + kTile <= x.full_hi);
                     stage_k<D, FP8>(kr, sm_k, lane);
                     __syncthreads();
-                    issue_k_rows<D, FP8, UNIFORM>(kr, p, x, tile_t0(i + 1));
+                    issue_k_rows<D, FP8, UNIFORM, NW == 1>(kr, p, x, tile_t0(i + 1));
                     f32x4 s[2];
                     tile_scores_lds<D, FP8>(s, sm_k, qop, c, grp);
                     const u32x4 pop = tile_softmax<D, CAP>(acc, s, p, x, t0, full);
                     tile_pv<D, FP8>(acc, vr, pop, x, t0, full);
                     __syncthreads();
-                    issue_v<D, FP8, UNIFORM>(vr, p, x, tile_t0(i + 1));
+                    issue_v<D, FP8, UNIFORM, NW == 1>(vr, p, x, tile_t0(i + 1));
                 }
                 const int t0 = tile_t0(ct - 1);
                 const bool full = (t0 >= x.full_lo) && (t0 + kTile <= x.full_hi);

@@ -180,6 +180,19 @@ class DecodeCase:
         elem = 2 if self.kv_dtype == "bf16" else 1
         return self.attended_tokens() * self.num_kv_heads * self.head_dim * 2 * elem
 
+    def verify_bytes(self, q_len: int) -> int:
+        """Algorithmic bytes of a verify call with q_len query tokens per
+        sequence: K/V of keys [max(0, L - q_len + 1 - W), L), Q and out rows,
+        table entries, lengths (split partials excluded)."""
+        B, Hq, D, P = self.batch, self.num_q_heads, self.head_dim, self.page_size
+        L = self.seq_lens.astype(np.int64)
+        lo = (np.maximum(L - q_len + 1 - self.window, 0) if self.window > 0
+              else np.zeros_like(L))
+        elem = 2 if self.kv_dtype == "bf16" else 1
+        pages = np.where(L > lo, (L - 1) // P - lo // P + 1, 0)
+        kv = int((L - lo).sum()) * self.num_kv_heads * D * 2 * elem
+        return int(kv + 2 * B * q_len * Hq * D * 2 + 4 * pages.sum() + 4 * B)
+
     def algorithmic_bytes(self) -> int:
         """K/V + Q + out + table entries + lengths (split partials excluded)."""
         B, Hq, D, P = self.batch, self.num_q_heads, self.head_dim, self.page_size
