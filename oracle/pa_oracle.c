@@ -57,6 +57,24 @@
  *           L - q_len + i and attends causally to the cached tokens up to
  *           it: the decode definition with L replaced by L - q_len + i + 1.
  *
+ *  sinks    Optional per-query-head fp32 logits sink[h] (`attention_sink_bias`
+ *           handed to `bind` by the vLLM "b12x" backend page, shape
+ *           [num_heads], kept in fp32 after weight loading; the kernel that
+ *           uses it is not printed).  Read as an attention sink: one more
+ *           logit in the softmax normaliser that carries no value,
+ *             out = sum_t exp(s_t - m) v_t / (exp(sink - m) + sum_t exp(s_t - m)),
+ *             m = max(sink, max_t s_t),  lse = m + ln(that denominator);
+ *           the sink is taken as it is (not scaled, not soft-capped).  With
+ *           splits it enters the merge once:
+ *             out = sum_s exp(lse_s - M) o_s / (exp(sink - M) + sum_s exp(lse_s - M)).
+ *           A row with no key is still a zero row.
+ *
+ *  descales Optional per-request fp32 descales kd[b], vd[b] (the b12x
+ *           `_prepare_fp8_descales` gives one value per request): a cached
+ *           key of sequence b is dec(K) * k_scale * kd[b], a cached value
+ *           dec(V) * v_scale * vd[b].  New extend rows are not cache
+ *           elements and take no descale.
+ *
  *  append   The cache write that precedes attention (`do_kv_cache_update` on
  *           the vLLM "b12x" backend page, which hands key, value, the
  *           caches, `slot_mapping` and the k/v scales to
@@ -131,6 +149,8 @@ typedef struct {
     int64_t bt_stride;
     const int32_t *seq_lens;    /* decode: cached tokens incl. the query token */
     double scale, softcap, k_scale, v_scale;
+    const float *sinks;         /* [Hq] or NULL */
+    const float *k_desc, *v_desc; /* [B] per-request descales or NULL */
     int window;
     int num_splits;             /* decode: 0 = one pass over the key range */
     int q_len;                  /* verify: query rows per sequence */
@@ -145,13 +165,15 @@ typedef struct {
 } orc_problem;
 
 /*
- * Softmax-weighted sum over a list of keys given as (score, value row).
- * The definition: out = sum exp(s - m) v / sum exp(s - m), lse = m + ln(sum).
+ * Softmax-weighted sum over a list of keys given as (score, value row), with
+ * an optional sink logit (-inf: none) that joins the normaliser only.
+ * The definition: out = sum exp(s - m) v / (exp(sink - m) + sum exp(s - m)),
+ * lse = m + ln(that denominator), m = max(sink, max s).
  */
 static void softmax_sum(const double *s, const double *v, int64_t n, int D,
-                        double *out, double *lse)
+                        double sink, double *out, double *lse)
 {
-    double m = -INFINITY, z = 0.0;
+    double m = sink, z = 0.0;
     int64_t t;
     int d;
     for (d = 0; d < D; ++d)
@@ -163,6 +185,8 @@ static void softmax_sum(const double *s, const double *v, int64_t n, int D,
     for (t = 0; t < n; ++t)
         if (s[t] > m)
             m = s[t];
+    if (sink > -INFINITY)
+        z = exp(sink - m);
     for (t = 0; t < n; ++t) {
         double w = exp(s[t] - m);
         z += w;
@@ -179,10 +203,18 @@ static double cap_score(double s, double c)
     return c > 0.0 ? c * tanh(s / c) : s;
 }
 
+/* The sink logit of query head h (-inf when there are none). */
+static double sink_of(const orc_problem *pr, int h)
+{
+    return pr->sinks ? (double)pr->sinks[h] : -INFINITY;
+}
+
 /* Gather keys [t0, t1) of (b, g) from the cache: scores against q, and values. */
 static void gather_cached(const orc_problem *pr, int b, int g, const double *q,
                           int64_t t0, int64_t t1, double *s, double *v)
 {
+    double ks = pr->k_scale * (pr->k_desc ? (double)pr->k_desc[b] : 1.0);
+    double vs = pr->v_scale * (pr->v_desc ? (double)pr->v_desc[b] : 1.0);
     int64_t t;
     int d;
     for (t = t0; t < t1; ++t) {
@@ -191,11 +223,11 @@ static void gather_cached(const orc_problem *pr, int b, int g, const double *q,
         double dot = 0.0;
         for (d = 0; d < pr->D; ++d) {
             double k = cache_elem(pr->k_pool, pr->kv_dtype, page, row, g, d,
-                                  pr->P, pr->Hkv, pr->D) * pr->k_scale;
+                                  pr->P, pr->Hkv, pr->D) * ks;
             dot += q[d] * k;
             v[(t - t0) * pr->D + d] =
                 cache_elem(pr->v_pool, pr->kv_dtype, page, row, g, d, pr->P,
-                           pr->Hkv, pr->D) * pr->v_scale;
+                           pr->Hkv, pr->D) * vs;
         }
         s[t - t0] = cap_score(pr->scale * dot, pr->softcap);
     }
@@ -221,7 +253,7 @@ static void decode_row(const orc_problem *pr, int b, int h, double *q,
 
     if (pr->num_splits <= 0) {
         gather_cached(pr, b, g, q, lo, L, s, v);
-        softmax_sum(s, v, L - lo, D, out, lse);
+        softmax_sum(s, v, L - lo, D, sink_of(pr, h), out, lse);
         return;
     }
 
@@ -239,7 +271,7 @@ static void decode_row(const orc_problem *pr, int b, int h, double *q,
                 continue;
             }
             gather_cached(pr, b, g, q, a, e, s, v);
-            softmax_sum(s, v, e - a, D, os + (int64_t)sp * D, &lses[sp]);
+            softmax_sum(s, v, e - a, D, -INFINITY, os + (int64_t)sp * D, &lses[sp]);
             if (lses[sp] > M)
                 M = lses[sp];
         }
@@ -249,6 +281,10 @@ static void decode_row(const orc_problem *pr, int b, int h, double *q,
             *lse = -INFINITY;
             return;
         }
+        if (sink_of(pr, h) > M)
+            M = sink_of(pr, h);
+        if (sink_of(pr, h) > -INFINITY)
+            z = exp(sink_of(pr, h) - M);
         for (sp = 0; sp < S; ++sp) {
             double w;
             if (lses[sp] == -INFINITY)
@@ -288,7 +324,7 @@ static void verify_row(const orc_problem *pr, int64_t it, double *q, double *s, 
     for (d = 0; d < D; ++d)
         q[d] = orc_bf16(pr->q[(bi * Hq + h) * D + d]);
     gather_cached(pr, b, h / (Hq / pr->Hkv), q, lo, L, s, v);
-    softmax_sum(s, v, L - lo, D, out, &lse);
+    softmax_sum(s, v, L - lo, D, sink_of(pr, h), out, &lse);
 }
 
 /* ------------------------------------------------------------------ */
@@ -332,7 +368,7 @@ static void extend_row(const orc_problem *pr, int64_t r, int h, double *q,
         s[n] = cap_score(pr->scale * dot, pr->softcap);
         ++n;
     }
-    softmax_sum(s, v, n, D, pr->out + (r * pr->Hq + h) * D, &lse);
+    softmax_sum(s, v, n, D, sink_of(pr, h), pr->out + (r * pr->Hq + h) * D, &lse);
 }
 
 /* ------------------------------------------------------------------ */
@@ -433,14 +469,16 @@ static int check_common(int B, int Hq, int Hkv, int D, int P, int kv_dtype)
  * Decode oracle.  out [B][Hq][D] and lse [B][Hq] (natural log) are written.
  * num_splits == 0 evaluates the definition in one pass over the key range;
  * num_splits > 0 evaluates the split partition and the log-sum-exp merge.
- * Returns 0, -1 on a bad argument, -2 when memory runs out.
+ * sinks [Hq] and the per-request descales k_desc/v_desc [B] are optional
+ * (NULL: none / 1).  Returns 0, -1 on a bad argument, -2 when memory runs out.
  */
 int orc_decode(int B, int Hq, int Hkv, int D, int P, int kv_dtype,
                const uint16_t *q, const void *k_pool, const void *v_pool,
                int64_t num_pages, const int32_t *block_table,
                int64_t bt_stride, const int32_t *seq_lens, double scale,
                double softcap, int window, double k_scale, double v_scale,
-               int num_splits, double *out, double *lse, int threads)
+               int num_splits, double *out, double *lse, int threads,
+               const float *sinks, const float *k_desc, const float *v_desc)
 {
     orc_problem pr;
     int64_t max_keys = 0;
@@ -455,6 +493,7 @@ int orc_decode(int B, int Hq, int Hkv, int D, int P, int kv_dtype,
     pr.bt = block_table; pr.bt_stride = bt_stride; pr.seq_lens = seq_lens;
     pr.scale = scale; pr.softcap = softcap; pr.window = window;
     pr.k_scale = k_scale; pr.v_scale = v_scale;
+    pr.sinks = sinks; pr.k_desc = k_desc; pr.v_desc = v_desc;
     pr.num_splits = num_splits;
     pr.out = out; pr.lse = lse;
     for (b = 0; b < B; ++b) {
@@ -470,6 +509,7 @@ int orc_decode(int B, int Hq, int Hkv, int D, int P, int kv_dtype,
  * Extend oracle.  Computes output rows for the token indices listed in
  * `rows` (n_rows of them), or for every token when rows == NULL
  * (n_rows = total_q).  out is [total_q][Hq][D]; only listed rows are written.
+ * sinks, k_desc, v_desc as for orc_decode.
  */
 int orc_extend(int B, int Hq, int Hkv, int D, int P, int kv_dtype,
                const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
@@ -477,7 +517,8 @@ int orc_extend(int B, int Hq, int Hkv, int D, int P, int kv_dtype,
                const void *k_pool, const void *v_pool, int64_t num_pages,
                const int32_t *block_table, int64_t bt_stride, double scale,
                double softcap, int window, double k_scale, double v_scale,
-               const int64_t *rows, int64_t n_rows, double *out, int threads)
+               const int64_t *rows, int64_t n_rows, double *out, int threads,
+               const float *sinks, const float *k_desc, const float *v_desc)
 {
     orc_problem pr;
     int64_t max_keys = 0;
@@ -493,6 +534,7 @@ int orc_extend(int B, int Hq, int Hkv, int D, int P, int kv_dtype,
     pr.bt = block_table; pr.bt_stride = bt_stride;
     pr.scale = scale; pr.softcap = softcap; pr.window = window;
     pr.k_scale = k_scale; pr.v_scale = v_scale;
+    pr.sinks = sinks; pr.k_desc = k_desc; pr.v_desc = v_desc;
     pr.rows = rows; pr.n_rows = n_rows;
     pr.out = out;
     for (b = 0; b < B; ++b) {
@@ -572,13 +614,15 @@ int orc_cache_append(int64_t num_tokens, int Hkv, int D, int P, int kv_dtype,
 
 /*
  * Verify oracle: q [B][q_len][Hq][D] (bf16), seq_lens counting the q_len
- * query tokens themselves; out [B][q_len][Hq][D].
+ * query tokens themselves; out [B][q_len][Hq][D].  sinks, k_desc, v_desc as
+ * for orc_decode.
  */
 int orc_verify(int B, int Hq, int Hkv, int D, int P, int kv_dtype, int q_len,
                const uint16_t *q, const void *k_pool, const void *v_pool,
                int64_t num_pages, const int32_t *block_table, int64_t bt_stride,
                const int32_t *seq_lens, double scale, double softcap, int window,
-               double k_scale, double v_scale, double *out, int threads)
+               double k_scale, double v_scale, double *out, int threads,
+               const float *sinks, const float *k_desc, const float *v_desc)
 {
     orc_problem pr;
     int64_t max_keys = 0;
@@ -593,6 +637,7 @@ int orc_verify(int B, int Hq, int Hkv, int D, int P, int kv_dtype, int q_len,
     pr.bt = block_table; pr.bt_stride = bt_stride; pr.seq_lens = seq_lens;
     pr.scale = scale; pr.softcap = softcap; pr.window = window;
     pr.k_scale = k_scale; pr.v_scale = v_scale;
+    pr.sinks = sinks; pr.k_desc = k_desc; pr.v_desc = v_desc;
     pr.q_len = q_len;
     pr.out = out;
     for (b = 0; b < B; ++b) {

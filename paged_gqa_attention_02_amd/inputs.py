@@ -156,6 +156,9 @@ class DecodeCase:
     num_splits: int = 0         # 0 = chosen by the plan
     k_tok: Optional[np.ndarray] = None   # logical tokens [sum L, Hkv, D] (bits)
     v_tok: Optional[np.ndarray] = None
+    sinks: Optional[np.ndarray] = None      # float32 [Hq] sink logits (None: off)
+    k_descale: Optional[np.ndarray] = None  # float32 [B] per-request descales (None: 1)
+    v_descale: Optional[np.ndarray] = None
 
     @property
     def batch(self) -> int:
@@ -299,6 +302,9 @@ class ExtendCase:
     window: int = 0
     k_scale: float = 1.0
     v_scale: float = 1.0
+    sinks: Optional[np.ndarray] = None      # float32 [Hq] sink logits (None: off)
+    k_descale: Optional[np.ndarray] = None  # float32 [B] per-request cache descales
+    v_descale: Optional[np.ndarray] = None
 
     @property
     def batch(self) -> int:
@@ -398,6 +404,29 @@ def kv_torch_dtype(kv_dtype: str) -> torch.dtype:
     return torch.bfloat16 if kv_dtype == "bf16" else torch.float8_e4m3fn
 
 
+def with_extras(case, seed: int, sinks: bool = True, descales: bool = False,
+                sink_range: tuple[float, float] = (0.0, 8.0),
+                descale_range: tuple[float, float] = (0.5, 2.0)):
+    """Give a decode or extend case seeded sink logits ~ U(sink_range) per
+    query head and/or per-request descales ~ U(descale_range), drawn from
+    default_rng(seed) in that order (sinks, k descales, v descales)."""
+    rng = np.random.default_rng(seed)
+    if sinks:
+        case.sinks = rng.uniform(*sink_range, size=case.num_q_heads).astype(np.float32)
+    if descales:
+        case.k_descale = rng.uniform(*descale_range, size=case.batch).astype(np.float32)
+        case.v_descale = rng.uniform(*descale_range, size=case.batch).astype(np.float32)
+    return case
+
+
+def _extra_tensors(case, device) -> dict:
+    out = {}
+    for name in ("sinks", "k_descale", "v_descale"):
+        a = getattr(case, name, None)
+        out[name] = None if a is None else _dev(np.asarray(a, dtype=np.float32), device)
+    return out
+
+
 def decode_tensors(case: DecodeCase, device) -> dict:
     kd = kv_torch_dtype(case.kv_dtype)
     return dict(
@@ -406,6 +435,7 @@ def decode_tensors(case: DecodeCase, device) -> dict:
         v_pool=_dev(case.kv.v_pool, device, kd),
         block_table=_dev(case.kv.block_table, device),
         seq_lens=_dev(case.seq_lens, device),
+        **_extra_tensors(case, device),
     )
 
 
@@ -420,6 +450,7 @@ def extend_tensors(case: ExtendCase, device) -> dict:
         k_pool=_dev(case.kv.k_pool, device, kd),
         v_pool=_dev(case.kv.v_pool, device, kd),
         block_table=_dev(case.kv.block_table, device),
+        **_extra_tensors(case, device),
     )
 
 

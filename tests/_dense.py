@@ -18,11 +18,31 @@ def dense_tokens(kv, b, L, kv_dtype):
     return k, v
 
 
-def _sdpa(q, k, v, scale, mask=None):
-    """q [H, n, D], k/v [H, m, D] float64 -> [H, n, D]."""
+def _sdpa(q, k, v, scale, mask=None, sinks=None):
+    """q [H, n, D], k/v [H, m, D] float64 -> [H, n, D].  `mask` is a boolean
+    keep-mask [n, m].  `sinks` [H] adds, per head, one more key whose value
+    row is zero and whose score is the sink logit: a zero key (score 0)
+    with the sink as an additive mask term."""
+    if sinks is not None:
+        H, n, D = q.shape
+        m = k.shape[1]
+        k = np.concatenate([k, np.zeros((H, 1, D))], axis=1)
+        v = np.concatenate([v, np.zeros((H, 1, D))], axis=1)
+        bias = np.zeros((H, n, m + 1))
+        if mask is not None:
+            bias[:, :, :m] = np.where(mask.numpy(), 0.0, -np.inf)[None]
+        bias[:, :, m] = np.asarray(sinks, dtype=np.float64)[:, None]
+        mask = torch.from_numpy(bias)
     return F.scaled_dot_product_attention(
         torch.from_numpy(q)[None], torch.from_numpy(k)[None],
         torch.from_numpy(v)[None], attn_mask=mask, scale=scale)[0].numpy()
+
+
+def _scales(case, b):
+    """Cache scales of sequence b: per-tensor times the per-request descale."""
+    ks = case.k_scale * (1.0 if case.k_descale is None else float(case.k_descale[b]))
+    vs = case.v_scale * (1.0 if case.v_descale is None else float(case.v_descale[b]))
+    return ks, vs
 
 
 def sdpa_decode(case):
@@ -37,11 +57,12 @@ def sdpa_decode(case):
         if L == 0:
             continue
         k, v = dense_tokens(case.kv, b, L, case.kv_dtype)
-        k = np.repeat(k[lo:] * case.k_scale, G, axis=1).transpose(1, 0, 2)
-        v = np.repeat(v[lo:] * case.v_scale, G, axis=1).transpose(1, 0, 2)
+        ks, vs = _scales(case, b)
+        k = np.repeat(k[lo:] * ks, G, axis=1).transpose(1, 0, 2)
+        v = np.repeat(v[lo:] * vs, G, axis=1).transpose(1, 0, 2)
         q = bits_to_float(case.q[b], "bf16").astype(np.float64)[:, None, :]
         out[b] = _sdpa(q, np.ascontiguousarray(k), np.ascontiguousarray(v),
-                       case.scale)[:, 0, :]
+                       case.scale, sinks=case.sinks)[:, 0, :]
     return out
 
 
@@ -60,8 +81,9 @@ def sdpa_extend(case):
         kc, vc = dense_tokens(case.kv, b, C, case.kv_dtype)
         kn = bits_to_float(case.k_new[a:e], "bf16").astype(np.float64)
         vn = bits_to_float(case.v_new[a:e], "bf16").astype(np.float64)
-        k = np.concatenate([kc * case.k_scale, kn])
-        v = np.concatenate([vc * case.v_scale, vn])
+        ks, vs = _scales(case, b)
+        k = np.concatenate([kc * ks, kn])
+        v = np.concatenate([vc * vs, vn])
         k = np.ascontiguousarray(np.repeat(k, G, axis=1).transpose(1, 0, 2))
         v = np.ascontiguousarray(np.repeat(v, G, axis=1).transpose(1, 0, 2))
         qpos = C + np.arange(n)[:, None]
@@ -71,7 +93,7 @@ def sdpa_extend(case):
             keep &= (qpos - kpos) < case.window
         q = bits_to_float(case.q[a:e], "bf16").astype(np.float64).transpose(1, 0, 2)
         out[a:e] = _sdpa(np.ascontiguousarray(q), k, v, case.scale,
-                         torch.from_numpy(keep)).transpose(1, 0, 2)
+                         torch.from_numpy(keep), sinks=case.sinks).transpose(1, 0, 2)
     return out
 
 
@@ -85,8 +107,9 @@ def sdpa_verify(case, q_bits):
     for b in range(B):
         L = int(case.seq_lens[b])
         k, v = dense_tokens(case.kv, b, L, case.kv_dtype)
-        k = np.ascontiguousarray(np.repeat(k * case.k_scale, G, axis=1).transpose(1, 0, 2))
-        v = np.ascontiguousarray(np.repeat(v * case.v_scale, G, axis=1).transpose(1, 0, 2))
+        ks, vs = _scales(case, b)
+        k = np.ascontiguousarray(np.repeat(k * ks, G, axis=1).transpose(1, 0, 2))
+        v = np.ascontiguousarray(np.repeat(v * vs, G, axis=1).transpose(1, 0, 2))
         qpos = L - ql + np.arange(ql)[:, None]
         kpos = np.arange(L)[None, :]
         keep = kpos <= qpos
@@ -94,5 +117,5 @@ def sdpa_verify(case, q_bits):
             keep &= (qpos - kpos) < case.window
         q = bits_to_float(q_bits[b], "bf16").astype(np.float64).transpose(1, 0, 2)
         out[b] = _sdpa(np.ascontiguousarray(q), k, v, case.scale,
-                       torch.from_numpy(keep)).transpose(1, 0, 2)
+                       torch.from_numpy(keep), sinks=case.sinks).transpose(1, 0, 2)
     return out

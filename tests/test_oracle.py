@@ -463,3 +463,87 @@ def test_verify_one_row_is_decode(oracle_mod):
     got = oracle_mod.verify(case, q)[:, 0]
     ref, _ = oracle_mod.decode(case)
     np.testing.assert_array_equal(got, ref)
+
+
+# ------------------------------------------------- sinks and per-request descales
+def test_sinks_absent_or_far_below_change_nothing(oracle_mod):
+    """A sink logit of -inf, or one e^-10000 below every score, leaves every
+    output bit unchanged."""
+    case = rand_decode([1, 40, 300], 8, 2, 64, 16, 60, softcap=20.0, window=100)
+    ref, lse = oracle_mod.decode(case)
+    for val in (-np.inf, -1e4):
+        case.sinks = np.full(8, val, dtype=np.float32)
+        got, lse2 = oracle_mod.decode(case)
+        np.testing.assert_array_equal(got, ref)
+        np.testing.assert_array_equal(lse2, lse)
+
+
+@pytest.mark.parametrize("kv_dtype,window", [("bf16", 0), ("bf16", 50), ("fp8_e4m3", 0)])
+def test_decode_sinks_equal_sdpa_with_a_zero_value_key(oracle_mod, kv_dtype, window):
+    kw = dict(kv_dtype=kv_dtype, window=window)
+    if kv_dtype != "bf16":
+        kw["scale_range"] = (0.5, 2.0)
+    case = I.with_extras(rand_decode([1, 9, 130, 700], 16, 4, 64, 16, 61, **kw), 61,
+                         descales=True)
+    assert np.ptp(case.sinks) > 1.0          # distinct per head
+    close(oracle_mod.decode(case)[0], sdpa_decode(case))
+
+
+@pytest.mark.parametrize("window", [0, 40])
+def test_extend_sinks_and_descales_equal_masked_sdpa(oracle_mod, window):
+    case = I.with_extras(I.make_extend("sx", [0, 33, 100], [5, 17, 40], 8, 2, 64, 16, 62,
+                                       window=window), 62, descales=True)
+    close(oracle_mod.extend(case), sdpa_extend(case))
+
+
+def test_verify_sinks_equal_masked_sdpa(oracle_mod):
+    case, q = _verify_case([2, 40, 130], 8, 2, 64, 16, 4, 63)
+    I.with_extras(case, 63, descales=True)
+    close(oracle_mod.verify(case, q), sdpa_verify(case, q))
+
+
+def test_sink_identical_keys_closed_form(oracle_mod):
+    """n identical keys with score s, sink z: out = mean(V) * n e^s / (n e^s + e^z)."""
+    rng = np.random.default_rng(64)
+    n, D = 50, 128
+    q = I.bf16_bits(rng.standard_normal((1, 4, D)).astype(np.float32))
+    kk = np.repeat(rng.standard_normal((1, 1, D)).astype(np.float32), n, axis=0)
+    k, v = I.bf16_bits(kk), _tokens(1, D, n, rng)
+    case = I.decode_case_from_tokens("ident-sink", q, k, v, [n], 16, 8)
+    case.sinks = np.array([0.0, 2.5, 6.0, -3.0], dtype=np.float32)
+    out, lse = oracle_mod.decode(case)
+    kf = I.bits_to_float(k)[0, 0].astype(np.float64)
+    vmean = I.bits_to_float(v)[:, 0].astype(np.float64).mean(0)
+    for h in range(4):
+        s = case.scale * float(I.bits_to_float(q[0, h]).astype(np.float64) @ kf)
+        z = float(case.sinks[h])
+        close(out[0, h], vmean * (n * math.exp(s)) / (n * math.exp(s) + math.exp(z)))
+        close(lse[0, h], math.log(n * math.exp(s) + math.exp(z)))
+
+
+@pytest.mark.parametrize("splits", [2, 7, 40])
+def test_sinks_split_invariance(oracle_mod, splits):
+    """The sink joins the merged normaliser once, whatever the partition."""
+    case = I.with_extras(rand_decode([1, 31, 100, 257], 8, 2, 64, 16, 65, softcap=5.0,
+                                     window=70), 65, descales=True)
+    a, la = oracle_mod.decode(case)
+    b, lb = oracle_mod.decode(case, num_splits=splits)
+    close(a, b)
+    close(la, lb)
+
+
+def test_per_request_descales_are_per_sequence_scales(oracle_mod):
+    """Per-request descales kd[b], vd[b] give, for every sequence, exactly the
+    result of a per-tensor call with k_scale*kd[b], v_scale*vd[b]."""
+    case = I.with_extras(rand_decode([20, 90, 300], 8, 2, 64, 16, 66, kv_dtype="fp8_e4m3",
+                                     scale_range=(0.5, 2.0)), 66, sinks=False,
+                         descales=True)
+    got, _ = oracle_mod.decode(case)
+    kd, vd = case.k_descale, case.v_descale
+    base_k, base_v = case.k_scale, case.v_scale
+    case.k_descale = case.v_descale = None
+    for b in range(case.batch):
+        case.k_scale = base_k * float(kd[b])
+        case.v_scale = base_v * float(vd[b])
+        ref, _ = oracle_mod.decode(case)
+        np.testing.assert_array_equal(got[b], ref[b])

@@ -29,8 +29,8 @@ MUTANTS = [
     ("row-in-page", "int row = (int)(t % pr->P);", "int row = (int)((t + 1) % pr->P);"),
     ("layout-transposed", "int64_t idx = ((page * P + row) * (int64_t)Hkv + g) * D + d;",
      "int64_t idx = ((page * P + row) * (int64_t)D + d) * Hkv + g;"),
-    ("no-k-scale", "pr->P, pr->Hkv, pr->D) * pr->k_scale;", "pr->P, pr->Hkv, pr->D);"),
-    ("no-v-scale", "pr->Hkv, pr->D) * pr->v_scale;", "pr->Hkv, pr->D);"),
+    ("no-k-scale", "pr->P, pr->Hkv, pr->D) * ks;", "pr->P, pr->Hkv, pr->D);"),
+    ("no-v-scale", "pr->Hkv, pr->D) * vs;", "pr->Hkv, pr->D);"),
     ("merge-sign", "w = exp(lses[sp] - M);", "w = exp(M - lses[sp]);"),
     ("split-drops-token", "int64_t e = a + len < L ? a + len : L;",
      "int64_t e = a + len < L ? a + len - 1 : L;"),
@@ -52,6 +52,18 @@ MUTANTS = [
      "int64_t L = (int64_t)pr->seq_lens[b] - ql + i;"),
     ("verify-row-order", "int b = (int)(bi / ql), i = (int)(bi % ql);",
      "int b = (int)(bi / ql), i = ql - 1 - (int)(bi % ql);"),
+    ("sink-scaled", "return pr->sinks ? (double)pr->sinks[h] : -INFINITY;",
+     "return pr->sinks ? pr->scale * (double)pr->sinks[h] : -INFINITY;"),
+    ("sink-kv-head", "return pr->sinks ? (double)pr->sinks[h] : -INFINITY;",
+     "return pr->sinks ? (double)pr->sinks[h % pr->Hkv] : -INFINITY;"),
+    ("sink-sign", "        z = exp(sink - m);", "        z = exp(m - sink);"),
+    ("sink-in-every-split", "softmax_sum(s, v, e - a, D, -INFINITY,",
+     "softmax_sum(s, v, e - a, D, sink_of(pr, h),"),
+    ("sink-missing-from-merge", "            z = exp(sink_of(pr, h) - M);", "            z = 0.0;"),
+    ("descale-first-request", "(pr->k_desc ? (double)pr->k_desc[b] : 1.0)",
+     "(pr->k_desc ? (double)pr->k_desc[0] : 1.0)"),
+    ("v-descale-from-k", "(pr->v_desc ? (double)pr->v_desc[b] : 1.0)",
+     "(pr->v_desc ? (double)pr->k_desc[b] : 1.0)"),
 ]
 
 
