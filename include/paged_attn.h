@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define PAGED_ATTN_ABI_VERSION 1
+#define PAGED_ATTN_ABI_VERSION 2
 
 typedef enum {
     PA_OK = 0,
@@ -85,6 +85,34 @@ typedef enum {
 
 typedef enum { PA_KV_BF16 = 0, PA_KV_FP8_E4M3 = 1 } pa_kv_dtype;
 typedef enum { PA_MODE_DECODE = 0, PA_MODE_EXTEND = 1, PA_MODE_VERIFY = 2 } pa_mode;
+
+/*
+ * Optional inputs of a compute call (the `attention_sink_bias`, `k_descale`
+ * and `v_descale` that the vLLM "b12x" backend page hands to its kernel's
+ * `bind`).  Pass NULL for none, or leave members NULL.  Device pointers,
+ * 4-byte aligned; contents are read by the kernels and not checked.
+ *
+ *   sinks         fp32 [Hq]: one logit per query head that joins the softmax
+ *                 normaliser and carries no value:
+ *                   out = sum_j e^{s_j} v_j / (e^{sink[h]} + sum_j e^{s_j}),
+ *                 s_j the scaled (and soft-capped) scores; the sink itself is
+ *                 neither scaled nor capped.  A row with no key stays zero.
+ *   k_descale,    fp32 per-request cache descales (finite, > 0): a cached key
+ *   v_descale     of request b is dec(K) * k_scale * k_descale[b'] (values
+ *                 alike), b' = b when num_descales > 1, else 0.  New extend
+ *                 rows are not cache elements and take no descale.
+ *   num_descales  entries behind k_descale/v_descale: 1 (shared by every
+ *                 request) or >= B; anything else is PA_ERR_INVALID_SHAPE
+ *                 (the b12x `_prepare_fp8_descales` expands a single value,
+ *                 slices a longer tensor and rejects a shorter one).
+ */
+typedef struct {
+    const float* sinks;
+    const float* k_descale;
+    const float* v_descale;
+    int32_t num_descales;
+    int32_t reserved;
+} pa_extras;
 
 /* Host-side description of one call shape (plain values, no pointers). */
 typedef struct {
@@ -163,6 +191,8 @@ pa_status paged_attn_plan(const pa_problem* prob, int hip_device, pa_plan* out);
  *                 and each sequence's tile offset, written by the split pass
  *                 and read by the merge; no initial contents needed);
  *                 calls that share a workspace must not overlap
+ *   extras        optional sinks and per-request descales (see pa_extras),
+ *                 or NULL
  *
  * Two kernels run: the key ranges of all (sequence, kv head) pairs, laid end
  * to end, are cut into plan->num_splits equal pieces, one per persistent
@@ -181,6 +211,7 @@ pa_status paged_attn_decode(const pa_plan* plan,
                             int32_t window, float k_scale, float v_scale,
                             void* out, int64_t out_stride_b,
                             void* workspace, uint64_t workspace_bytes,
+                            const pa_extras* extras,
                             void* hip_stream);
 
 /*
@@ -201,6 +232,7 @@ pa_status paged_attn_decode_split(const pa_plan* plan,
                                   int32_t window, float k_scale, float v_scale,
                                   void* out, int64_t out_stride_b,
                                   void* workspace, uint64_t workspace_bytes,
+                                  const pa_extras* extras,
                                   void* hip_stream);
 pa_status paged_attn_decode_merge(const pa_plan* plan,
                                   const void* q, int64_t q_stride_b,
@@ -213,6 +245,7 @@ pa_status paged_attn_decode_merge(const pa_plan* plan,
                                   int32_t window, float k_scale, float v_scale,
                                   void* out, int64_t out_stride_b,
                                   void* workspace, uint64_t workspace_bytes,
+                                  const pa_extras* extras,
                                   void* hip_stream);
 
 /*
@@ -245,6 +278,7 @@ pa_status paged_attn_verify(const pa_plan* plan,
                             int32_t window, float k_scale, float v_scale,
                             void* out, int64_t out_stride_b,
                             void* workspace, uint64_t workspace_bytes,
+                            const pa_extras* extras,
                             void* hip_stream);
 
 /*
@@ -259,6 +293,8 @@ pa_status paged_attn_verify(const pa_plan* plan,
  *   k_pool...bt_stride  the cached context, as for decode
  *   out           bf16 [total_q, Hq, D]
  *   workspace     may be NULL when plan->workspace_bytes == 0
+ *   extras        optional sinks and per-request descales (see pa_extras),
+ *                 or NULL; descales apply to the cached context only
  */
 pa_status paged_attn_extend(const pa_plan* plan,
                             const void* q, const void* k_new, const void* v_new,
@@ -270,6 +306,7 @@ pa_status paged_attn_extend(const pa_plan* plan,
                             int32_t page_size, float scale, float softcap,
                             int32_t window, float k_scale, float v_scale,
                             void* out, void* workspace, uint64_t workspace_bytes,
+                            const pa_extras* extras,
                             void* hip_stream);
 
 /*

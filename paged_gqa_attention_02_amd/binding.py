@@ -21,6 +21,12 @@ PA_MODE_DECODE, PA_MODE_EXTEND, PA_MODE_VERIFY = 0, 1, 2
 PA_KV = {"bf16": 0, "fp8_e4m3": 1}
 
 
+class PaExtras(ctypes.Structure):
+    _fields_ = [("sinks", ctypes.c_void_p), ("k_descale", ctypes.c_void_p),
+                ("v_descale", ctypes.c_void_p), ("num_descales", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
 class PaProblem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "mode", "num_seqs", "num_q_heads", "num_kv_heads", "head_dim", "page_size",
@@ -58,14 +64,15 @@ def lib():
     PP = ctypes.POINTER(PaPlan)
     L.paged_attn_plan.argtypes = [ctypes.POINTER(PaProblem), ctypes.c_int, PP]
     L.paged_attn_plan.restype = ctypes.c_int
+    PX = ctypes.POINTER(PaExtras)
     L.paged_attn_decode.argtypes = [PP, p, i64, p, p, i64, i64, i64, i64, p, i64, p,
-                                    i32, f32, f32, i32, f32, f32, p, i64, p, u64, p]
+                                    i32, f32, f32, i32, f32, f32, p, i64, p, u64, PX, p]
     L.paged_attn_decode.restype = ctypes.c_int
     for fn in ("paged_attn_decode_split", "paged_attn_decode_merge", "paged_attn_verify"):
         getattr(L, fn).argtypes = L.paged_attn_decode.argtypes
         getattr(L, fn).restype = ctypes.c_int
     L.paged_attn_extend.argtypes = [PP, p, p, p, p, p, p, p, i64, i64, i64, i64, p, i64,
-                                    i32, f32, f32, i32, f32, f32, p, p, u64, p]
+                                    i32, f32, f32, i32, f32, f32, p, p, u64, PX, p]
     L.paged_attn_extend.restype = ctypes.c_int
     L.paged_attn_gather.argtypes = [PP, p, p, i64, i64, i64, i64, p, i64, p, p, p, p]
     L.paged_attn_cache_append.argtypes = [p, p, i64, i64, ctypes.c_int32, ctypes.c_int32, p, p,
@@ -145,6 +152,24 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _extras(sinks, k_descale, v_descale):
+    """pa_extras for optional fp32 device tensors (None when all are None):
+    sinks [Hq]; k_descale/v_descale with 1 or >= B entries."""
+    if sinks is None and k_descale is None and v_descale is None:
+        return None
+    for name, t in (("sinks", sinks), ("k_descale", k_descale), ("v_descale", v_descale)):
+        if t is not None and (t.dtype != torch.float32 or t.dim() != 1 or
+                              not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous fp32 vector")
+    n = [t.numel() for t in (k_descale, v_descale) if t is not None]
+    if len(n) == 2 and n[0] != n[1]:
+        raise ValueError("k_descale and v_descale must have the same length")
+    ex = PaExtras(None if sinks is None else sinks.data_ptr(),
+                  None if k_descale is None else k_descale.data_ptr(),
+                  None if v_descale is None else v_descale.data_ptr(), n[0] if n else 0, 0)
+    return ctypes.byref(ex)
+
+
 def _stream(stream) -> ctypes.c_void_p:
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
@@ -193,27 +218,34 @@ def decode(pl: Plan, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor
            block_table: torch.Tensor, seq_lens: torch.Tensor, scale: float,
            softcap: float = 0.0, window: int = 0, k_scale: float = 1.0,
            v_scale: float = 1.0, out: Optional[torch.Tensor] = None,
-           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+           workspace: Optional[torch.Tensor] = None, stream=None, sinks=None,
+           k_descale=None, v_descale=None) -> torch.Tensor:
     """paged_attn_decode: q bf16 [B, Hq, D] -> out bf16 [B, Hq, D].
-    A workspace passed in needs plan.workspace_bytes bytes."""
+    A workspace passed in needs plan.workspace_bytes bytes.  sinks: fp32 [Hq]
+    sink logits; k_descale/v_descale: fp32 per-request descales (1 or >= B)."""
     return _decode("paged_attn_decode", pl, q, k_pool, v_pool, block_table, seq_lens, scale,
-                   softcap, window, k_scale, v_scale, out, workspace, stream)
+                   softcap, window, k_scale, v_scale, out, workspace, stream,
+                   sinks, k_descale, v_descale)
 
 
 def decode_split(pl: Plan, q, k_pool, v_pool, block_table, seq_lens, scale, softcap=0.0,
-                 window=0, k_scale=1.0, v_scale=1.0, out=None, workspace=None, stream=None):
+                 window=0, k_scale=1.0, v_scale=1.0, out=None, workspace=None, stream=None,
+                 sinks=None, k_descale=None, v_descale=None):
     """paged_attn_decode_split: the split pass alone (writes the segments one
-    wave covers whole to `out`, the others to the workspace)."""
+    block covers whole to `out`, the others to the workspace)."""
     return _decode("paged_attn_decode_split", pl, q, k_pool, v_pool, block_table, seq_lens,
-                   scale, softcap, window, k_scale, v_scale, out, workspace, stream)
+                   scale, softcap, window, k_scale, v_scale, out, workspace, stream,
+                   sinks, k_descale, v_descale)
 
 
 def decode_merge(pl: Plan, q, k_pool, v_pool, block_table, seq_lens, scale, softcap=0.0,
-                 window=0, k_scale=1.0, v_scale=1.0, out=None, workspace=None, stream=None):
+                 window=0, k_scale=1.0, v_scale=1.0, out=None, workspace=None, stream=None,
+                 sinks=None, k_descale=None, v_descale=None):
     """paged_attn_decode_merge: the merge pass alone, over the workspace the
     split pass left."""
     return _decode("paged_attn_decode_merge", pl, q, k_pool, v_pool, block_table, seq_lens,
-                   scale, softcap, window, k_scale, v_scale, out, workspace, stream)
+                   scale, softcap, window, k_scale, v_scale, out, workspace, stream,
+                   sinks, k_descale, v_descale)
 
 
 def verify_plan(q: torch.Tensor, k_pool: torch.Tensor, block_table: torch.Tensor,
@@ -229,15 +261,19 @@ def verify(pl: Plan, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor
            block_table: torch.Tensor, seq_lens: torch.Tensor, scale: float,
            softcap: float = 0.0, window: int = 0, k_scale: float = 1.0,
            v_scale: float = 1.0, out: Optional[torch.Tensor] = None,
-           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+           workspace: Optional[torch.Tensor] = None, stream=None, sinks=None,
+           k_descale=None, v_descale=None) -> torch.Tensor:
     """paged_attn_verify: q bf16 [B, q_len, Hq, D] -> out bf16 [B, q_len, Hq, D];
     seq_lens count the q_len query tokens, which are already in the cache."""
     return _decode("paged_attn_verify", pl, q, k_pool, v_pool, block_table, seq_lens, scale,
-                   softcap, window, k_scale, v_scale, out, workspace, stream)
+                   softcap, window, k_scale, v_scale, out, workspace, stream,
+                   sinks, k_descale, v_descale)
 
 
 def _rows_contiguous(t: torch.Tensor) -> bool:
     """All dims after the first are dense (the sequence stride is free)."""
+    if t.numel() == 0:
+        return True
     step = 1
     for d in range(t.dim() - 1, 0, -1):
         if t.shape[d] > 1 and t.stride(d) != step:
@@ -247,7 +283,8 @@ def _rows_contiguous(t: torch.Tensor) -> bool:
 
 
 def _decode(fn, pl, q, k_pool, v_pool, block_table, seq_lens, scale, softcap, window,
-            k_scale, v_scale, out, workspace, stream):
+            k_scale, v_scale, out, workspace, stream, sinks=None, k_descale=None,
+            v_descale=None):
     if fn not in ("paged_attn_decode", "paged_attn_verify") and (
             out is None or (workspace is None and pl.workspace_bytes > 0)):
         raise ValueError(f"{fn}: the passes share `out` and the workspace; pass both")
@@ -270,7 +307,8 @@ def _decode(fn, pl, q, k_pool, v_pool, block_table, seq_lens, scale, softcap, wi
         ctypes.byref(pl.c), _ptr(q), q.stride(0), _ptr(k_pool), _ptr(v_pool), sp, st, sh,
         k_pool.shape[0], _ptr(block_table), block_table.stride(0), _ptr(seq_lens),
         k_pool.shape[1], float(scale), float(softcap), int(window), float(k_scale),
-        float(v_scale), _ptr(out), out.stride(0), _ptr(workspace), wbytes, _stream(stream)))
+        float(v_scale), _ptr(out), out.stride(0), _ptr(workspace), wbytes,
+        _extras(sinks, k_descale, v_descale), _stream(stream)))
     return out
 
 
@@ -287,8 +325,10 @@ def extend(pl: Plan, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
            v_pool: torch.Tensor, block_table: torch.Tensor, scale: float,
            softcap: float = 0.0, window: int = 0, k_scale: float = 1.0,
            v_scale: float = 1.0, out: Optional[torch.Tensor] = None,
-           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """paged_attn_extend: q bf16 [total_q, Hq, D] -> out bf16 [total_q, Hq, D]."""
+           workspace: Optional[torch.Tensor] = None, stream=None, sinks=None,
+           k_descale=None, v_descale=None) -> torch.Tensor:
+    """paged_attn_extend: q bf16 [total_q, Hq, D] -> out bf16 [total_q, Hq, D].
+    sinks / k_descale / v_descale as for decode (descales: cached context only)."""
     for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new)):
         if t.dtype != torch.bfloat16 or not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous bf16")
@@ -297,8 +337,8 @@ def extend(pl: Plan, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
         raise TypeError("cu_seqlens_q, ctx_lens and block_table must be int32")
     if out is None:
         out = torch.empty_like(q)
-    if out.dtype != torch.bfloat16 or out.shape != q.shape or not _rows_contiguous(out):
-        raise ValueError(f"out must be bf16 {shape} like q, dense after the sequence dimension")
+    if out.dtype != torch.bfloat16 or out.shape != q.shape or not out.is_contiguous():
+        raise ValueError("out must be contiguous bf16 [total_q, Hq, D] like q")
     sp, st, sh = _pool_strides(k_pool, v_pool)
     workspace = _workspace(pl, workspace, q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -307,7 +347,7 @@ def extend(pl: Plan, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
         _ptr(ctx_lens), _ptr(k_pool), _ptr(v_pool), sp, st, sh, k_pool.shape[0],
         _ptr(block_table), block_table.stride(0), k_pool.shape[1], float(scale),
         float(softcap), int(window), float(k_scale), float(v_scale), _ptr(out),
-        _ptr(workspace), wbytes, _stream(stream)))
+        _ptr(workspace), wbytes, _extras(sinks, k_descale, v_descale), _stream(stream)))
     return out
 
 

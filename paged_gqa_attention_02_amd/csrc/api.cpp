@@ -75,6 +75,36 @@ int decode_waves_per_block(const pa_problem& pr) {
 
 int elem_bytes(int kv_dtype) { return kv_dtype == PA_KV_FP8_E4M3 ? 1 : 2; }
 
+// Optional sinks and per-request descales (NULL extras: none).
+struct Extras {
+    const float* sinks = nullptr;
+    const float* k_desc = nullptr;
+    const float* v_desc = nullptr;
+    int32_t per_seq = 0;
+};
+
+pa_status read_extras(const pa_extras* ex, int32_t num_seqs, Extras* out) {
+    *out = Extras{};
+    if (!ex) return PA_OK;
+    const auto aligned4 = [](const void* ptr) {
+        return (reinterpret_cast<uintptr_t>(ptr) & 3u) == 0;
+    };
+    if (!aligned4(ex->sinks) || !aligned4(ex->k_descale) || !aligned4(ex->v_descale))
+        return PA_ERR_MISALIGNED;
+    if (ex->k_descale || ex->v_descale) {
+        // one value for every request, or one per request (b12x
+        // `_prepare_fp8_descales`: a single value is expanded, a longer
+        // tensor is sliced, anything shorter is rejected)
+        if (ex->num_descales < 1) return PA_ERR_INVALID_SHAPE;
+        if (ex->num_descales > 1 && ex->num_descales < num_seqs) return PA_ERR_INVALID_SHAPE;
+        out->per_seq = ex->num_descales > 1;
+    }
+    out->sinks = ex->sinks;
+    out->k_desc = ex->k_descale;
+    out->v_desc = ex->v_descale;
+    return PA_OK;
+}
+
 pa_status check_pools(const pa_plan& pl, const void* k_pool, const void* v_pool,
                       int64_t s_page, int64_t s_tok, int64_t s_head, int64_t num_pages,
                       const int32_t* block_table, int64_t bt_stride) {
@@ -218,7 +248,8 @@ pa_status decode_impl(int passes, int mode, const pa_plan* plan, const void* q, 
                       const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
                       int32_t page_size, float scale, float softcap, int32_t window,
                       float k_scale, float v_scale, void* out, int64_t out_stride_b,
-                      void* workspace, uint64_t workspace_bytes, void* hip_stream) {
+                      void* workspace, uint64_t workspace_bytes, const pa_extras* extras,
+                      void* hip_stream) {
     if (!plan) return PA_ERR_NULL_POINTER;
     const pa_plan& pl = *plan;
     const pa_problem& pr = pl.prob;
@@ -242,6 +273,9 @@ pa_status decode_impl(int passes, int mode, const pa_plan* plan, const void* q, 
         return PA_ERR_MISALIGNED;
     if (!isfinite(scale) || !isfinite(softcap) || !isfinite(k_scale) || !isfinite(v_scale))
         return PA_ERR_INVALID_SHAPE;
+    Extras ex;
+    st = read_extras(extras, pr.num_seqs, &ex);
+    if (st != PA_OK) return st;
     const uint64_t need = pl.workspace_bytes;
     if (need > 0) {
         if (workspace_bytes < need) return PA_ERR_WORKSPACE_TOO_SMALL;
@@ -279,6 +313,10 @@ pa_status decode_impl(int passes, int mode, const pa_plan* plan, const void* q, 
         p.cap_c2 = softcap * kl2e;
     }
     p.v_scale = v_scale;
+    p.sinks = ex.sinks;
+    p.k_desc = ex.k_desc;
+    p.v_desc = ex.v_desc;
+    p.desc_per_seq = ex.per_seq;
     p.out = out;
     p.out_stride_b = out_stride_b;
     {
@@ -309,14 +347,15 @@ extern "C" {
 #define PA_DECODE_ARGS                                                                      \
     plan, q, q_stride_b, k_pool, v_pool, kv_stride_page, kv_stride_tok, kv_stride_head,     \
         num_pages, block_table, bt_stride, seq_lens, page_size, scale, softcap, window,     \
-        k_scale, v_scale, out, out_stride_b, workspace, workspace_bytes, hip_stream
+        k_scale, v_scale, out, out_stride_b, workspace, workspace_bytes, extras, hip_stream
 #define PA_DECODE_PARAMS                                                                    \
     const pa_plan *plan, const void *q, int64_t q_stride_b, const void *k_pool,             \
         const void *v_pool, int64_t kv_stride_page, int64_t kv_stride_tok,                  \
         int64_t kv_stride_head, int64_t num_pages, const int32_t *block_table,              \
         int64_t bt_stride, const int32_t *seq_lens, int32_t page_size, float scale,         \
         float softcap, int32_t window, float k_scale, float v_scale, void *out,             \
-        int64_t out_stride_b, void *workspace, uint64_t workspace_bytes, void *hip_stream
+        int64_t out_stride_b, void *workspace, uint64_t workspace_bytes,                   \
+        const pa_extras *extras, void *hip_stream
 
 pa_status paged_attn_decode(PA_DECODE_PARAMS) {
     return decode_impl(kBothPasses, PA_MODE_DECODE, PA_DECODE_ARGS);
@@ -429,7 +468,7 @@ pa_status paged_attn_extend(const pa_plan* plan, const void* q, const void* k_ne
                             const int32_t* block_table, int64_t bt_stride, int32_t page_size,
                             float scale, float softcap, int32_t window, float k_scale,
                             float v_scale, void* out, void* workspace, uint64_t workspace_bytes,
-                            void* hip_stream) {
+                            const pa_extras* extras, void* hip_stream) {
     (void)workspace;
     (void)workspace_bytes;
     if (!plan) return PA_ERR_NULL_POINTER;
@@ -448,9 +487,16 @@ pa_status paged_attn_extend(const pa_plan* plan, const void* q, const void* k_ne
         return PA_ERR_MISALIGNED;
     if (!isfinite(scale) || !isfinite(softcap) || !isfinite(k_scale) || !isfinite(v_scale))
         return PA_ERR_INVALID_SHAPE;
+    Extras ex;
+    st = read_extras(extras, pr.num_seqs, &ex);
+    if (st != PA_OK) return st;
 
     ExtendParams p;
     memset(&p, 0, sizeof p);
+    p.sinks = ex.sinks;
+    p.k_desc = ex.k_desc;
+    p.v_desc = ex.v_desc;
+    p.desc_per_seq = ex.per_seq;
     p.q = q;
     p.k_new = k_new;
     p.v_new = v_new;

@@ -115,6 +115,7 @@ struct TileCtx {
     const int* pages;
     int first_page, last_idx, t_begin, t_end, c, grp;
     int lim, wlo;              // this lane's column: keys t with wlo <= t <= lim (verify)
+    float qk2, c1;             // the segment's score scale (or soft-cap factor), log2 units
     int full_lo, full_hi;      // tiles inside [full_lo, full_hi) are valid for every column
     int64_t page_bytes;        // s_page * elem
     int tok_bytes;             // s_tok * elem
@@ -268,9 +269,9 @@ __device__ __forceinline__ u32x4 tile_softmax(Acc<D>& A, const f32x4 s[2],
         float v = (j < 4) ? s[0][j] : s[1][j - 4];
         if constexpr (CAP) {
             // c*tanh(y/c) = c - 2c / (exp(2y/c) + 1), times log2(e)
-            v = p.cap_c2 - 2.f * p.cap_c2 * fast_rcp(fast_exp2(v * p.cap_c1) + 1.f);
+            v = p.cap_c2 - 2.f * p.cap_c2 * fast_rcp(fast_exp2(v * x.c1) + 1.f);
         } else {
-            v *= p.qk_scale2;
+            v *= x.qk2;
         }
         sc[j] = v;
     }
@@ -438,6 +439,16 @@ void decode_split_kernel(DecodeParams p) {
         TileCtx x;
         x.c = c;
         x.grp = grp;
+        // per-request cache descales of sequence b (uniform loads)
+        float vsc = p.v_scale;
+        x.qk2 = p.qk_scale2;
+        x.c1 = p.cap_c1;
+        if (p.k_desc) {
+            const float kd = p.k_desc[p.desc_per_seq ? b : 0];
+            x.qk2 *= kd;
+            x.c1 *= kd;
+        }
+        if (p.v_desc) vsc *= p.v_desc[p.desc_per_seq ? b : 0];
         x.page_bytes = p.s_page * kElem;
         x.tok_bytes = (int)(p.s_tok * kElem);
         {
@@ -523,8 +534,12 @@ void decode_split_kernel(DecodeParams p) {
             const float mr = __shfl(acc.m, r, 64);
             if (rg < p.rows) {
                 // (a column with no key: zero row, lse = -inf for the merge)
-                const float inv = lr > 0.f ? p.v_scale / lr : 0.f;
                 if (complete) {
+                    // a sink logit joins the normaliser (no value row)
+                    float den = lr;
+                    if (p.sinks)
+                        den += fast_exp2(p.sinks[kvh * G + rg % G] * kLog2e - mr);
+                    const float inv = lr > 0.f ? vsc / den : 0.f;
                     uint16_t* o16 = static_cast<uint16_t*>(p.out) +
                                     (int64_t)b * p.out_stride_b +
                                     (int64_t)(rg / G) * p.out_stride_t +
@@ -538,6 +553,7 @@ void decode_split_kernel(DecodeParams p) {
                     else
                         *reinterpret_cast<u32x2*>(o16) = u32x2{ov[0], ov[1]};
                 } else {
+                    const float inv = lr > 0.f ? vsc / lr : 0.f;
                     const int64_t row = part_row(p, w, slot) + rg;
                     float* po = p.part_o + row * D + VE * c;
 #pragma unroll

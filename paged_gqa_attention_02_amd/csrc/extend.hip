@@ -387,7 +387,7 @@ __device__ __forceinline__ void tile_compute(const uint8_t* kl, const uint8_t* v
 }
 
 template <int D, bool FP8, int MODE>
-__global__ __launch_bounds__(kExtThreads, kExtOccupancy) void extend_kernel(ExtendParams p) {
+__global__ __launch_bounds__(kExtThreads, kExtOccupancy) void extend_kernel(ExtendParams pk) {
     using TL = Tile<D>;
     constexpr int kDS = D / 32;        // QK contraction steps
     constexpr int kVE = D / 16;        // PV MFMAs per (row block, key step)
@@ -398,6 +398,7 @@ __global__ __launch_bounds__(kExtThreads, kExtOccupancy) void extend_kernel(Exte
     __shared__ __attribute__((aligned(1024))) uint8_t sm_v1[TL::kBytes];
     __shared__ int sm_pages[kExtPages];
 
+    ExtendParams p = pk;
     const int G = p.group;
     const int segs = p.num_seqs * p.num_kv_heads;
     // heavier tiles (later tokens, more keys) first; all tiles of one
@@ -410,6 +411,13 @@ __global__ __launch_bounds__(kExtThreads, kExtOccupancy) void extend_kernel(Exte
     si.q0 = p.cu_seqlens_q[si.b];
     si.n = p.cu_seqlens_q[si.b + 1] - si.q0;
     si.C = p.ctx_lens[si.b];
+    // per-request descales of the cached part (uniform loads)
+    if (p.k_desc) {
+        const float kd = p.k_desc[p.desc_per_seq ? si.b : 0];
+        p.qk_scale2_ctx *= kd;
+        p.cap_c1_ctx *= kd;
+    }
+    if (p.v_desc) p.v_scale *= p.v_desc[p.desc_per_seq ? si.b : 0];
     const int T = kExtRows / G;        // tokens per block
     const int t0 = mt * T;
     if (t0 >= si.n) return;            // (uniform over the block)
@@ -557,7 +565,10 @@ __global__ __launch_bounds__(kExtThreads, kExtOccupancy) void extend_kernel(Exte
         const int r = (wave * kRB + rb) * 16 + c;
         uint16_t* orow = static_cast<uint16_t*>(p.out) +
                          ((int64_t)(si.q0 + row_t[rb]) * p.num_q_heads + si.kvh * G + r % G) * D;
-        const float inv = 1.f / lt;
+        // a sink logit joins the normaliser (no value row)
+        float den = lt;
+        if (p.sinks) den += fast_exp2(p.sinks[si.kvh * G + r % G] * kLog2e - A.m[rb]);
+        const float inv = 1.f / den;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             uint32_t wv[kVE / 2];

@@ -109,8 +109,11 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
         }
         sum = S;
         acc = a;
+        m = M;
     }
     if (pl != 0) return;                     // (idle threads when kR == 1)
+    // a sink logit joins the normaliser once (no value row)
+    if (p.sinks && sum > 0.f) sum += fast_exp2(p.sinks[kvh * G + r % G] * kLog2e - m);
     const float inv = sum > 0.f ? 1.f / sum : 0.f;   // (a row with no key: zeros)
     *reinterpret_cast<u32x2*>(out) =
         u32x2{pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv)};

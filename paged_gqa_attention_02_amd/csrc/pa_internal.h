@@ -43,6 +43,10 @@ struct DecodeParams {
     float cap_c1;             // 2 * scale * k_scale * log2(e) / c   (cap)
     float cap_c2;             // c * log2(e)                         (cap)
     float v_scale;
+    const float* sinks;       // [Hq] sink logits (natural-log units) or null
+    const float* k_desc;      // per-request cache descales or null; request b
+    const float* v_desc;      //   uses entry desc_per_seq ? b : 0
+    int32_t desc_per_seq;
     void* out;                // bf16 [B, Hq, D], row stride out_stride_b
     int64_t out_stride_b;
     float* part_o;            // [workers, 2, rows, D]: partial of a segment a wave covers in part
@@ -84,6 +88,10 @@ struct ExtendParams {
     float qk_scale2_ctx;      // scale * k_scale * log2(e), for cached keys
     float cap_c1, cap_c1_ctx, cap_c2;
     float v_scale;            // applied to the cached-value part of the sum
+    const float* sinks;       // [Hq] sink logits (natural-log units) or null
+    const float* k_desc;      // per-request cache descales or null (as decode)
+    const float* v_desc;
+    int32_t desc_per_seq;
     void* out;                // bf16 [total_q, Hq, D]
 };
 

@@ -10,6 +10,11 @@ DEV = "cuda:0"
 ATOL = RTOL = 1e-2      # |err| <= 1e-2 + 1e-2*|ref| for bf16/fp8-KV outputs
 
 
+def extras(t: dict) -> dict:
+    """The optional sink / descale tensors of a case's device tensors."""
+    return {k: t.get(k) for k in ("sinks", "k_descale", "v_descale")}
+
+
 def run_decode(case, num_splits=None, tensors=None, pool_view=None):
     t = tensors or I.decode_tensors(case, DEV)
     kp, vp = t["k_pool"], t["v_pool"]
@@ -20,7 +25,7 @@ def run_decode(case, num_splits=None, tensors=None, pool_view=None):
                         window=case.window, num_splits=ns)
     out = pa.decode(pl, t["q"], kp, vp, t["block_table"], t["seq_lens"], case.scale,
                     softcap=case.softcap, window=case.window, k_scale=case.k_scale,
-                    v_scale=case.v_scale)
+                    v_scale=case.v_scale, **extras(t))
     torch.cuda.synchronize()
     return out, pl
 
@@ -35,7 +40,7 @@ def run_verify(case, q_bits, num_splits=None, tensors=None):
                         window=case.window, num_splits=ns)
     out = pa.verify(pl, q, t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
                     case.scale, softcap=case.softcap, window=case.window,
-                    k_scale=case.k_scale, v_scale=case.v_scale)
+                    k_scale=case.k_scale, v_scale=case.v_scale, **extras(t))
     torch.cuda.synchronize()
     return out, pl
 
@@ -47,7 +52,7 @@ def run_extend(case, tensors=None):
     out = pa.extend(pl, t["q"], t["k_new"], t["v_new"], t["cu_seqlens_q"], t["ctx_lens"],
                     t["k_pool"], t["v_pool"], t["block_table"], case.scale,
                     softcap=case.softcap, window=case.window, k_scale=case.k_scale,
-                    v_scale=case.v_scale)
+                    v_scale=case.v_scale, **extras(t))
     torch.cuda.synchronize()
     return out, pl
 

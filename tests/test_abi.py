@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_runtime():
-    assert pa.lib().paged_attn_abi_version() == 1
+    assert pa.lib().paged_attn_abi_version() == 2
     assert pa.lib().paged_attn_hip_runtime_path().decode().endswith(".so")
 
 
@@ -119,15 +119,16 @@ def decode_status(plan_kw=None, fn="paged_attn_decode", **kw):
     args = dict(q=A, q_stride_b=32 * 128, k=A, v=A, sp=16 * 8 * 128, st=8 * 128, sh=128,
                 num_pages=10, bt=A, bt_stride=256, sl=A, page_size=16, scale=0.1,
                 softcap=0.0, window=0, ks=1.0, vs=1.0, out=A, out_stride_b=32 * 128,
-                ws=A, ws_bytes=pl.workspace_bytes, stream=None)
+                ws=A, ws_bytes=pl.workspace_bytes, extras=None, stream=None)
     args.update(kw)
     v = lambda x: None if x is None else ctypes.c_void_p(x)
+    ex = None if args["extras"] is None else ctypes.byref(B.PaExtras(*args["extras"]))
     return getattr(pa.lib(), fn)(
         ctypes.byref(pl), v(args["q"]), args["q_stride_b"], v(args["k"]), v(args["v"]),
         args["sp"], args["st"], args["sh"], args["num_pages"], v(args["bt"]),
         args["bt_stride"], v(args["sl"]), args["page_size"], args["scale"], args["softcap"],
         args["window"], args["ks"], args["vs"], v(args["out"]), args["out_stride_b"],
-        v(args["ws"]), args["ws_bytes"], args["stream"])
+        v(args["ws"]), args["ws_bytes"], ex, args["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -149,6 +150,13 @@ def decode_status(plan_kw=None, fn="paged_attn_decode", **kw):
     (dict(ws_bytes=100), WS),
     (dict(scale=float("nan")), SHAPE),
     (dict(softcap=float("inf")), SHAPE),
+    # extras (sinks, k_descale, v_descale, num_descales, reserved): B = 4
+    (dict(extras=(A + 2, None, None, 0, 0)), MISAL),
+    (dict(extras=(None, A, A + 1, 4, 0)), MISAL),
+    (dict(extras=(None, A, A, 0, 0)), SHAPE),
+    (dict(extras=(None, A, None, 2, 0)), SHAPE),
+    (dict(extras=(None, None, A, 3, 0)), SHAPE),
+    (dict(extras=(A, A, A, 4, 0), ws_bytes=100), WS),   # accepted, then the workspace
 ])
 @pytest.mark.parametrize("fn", DECODE_FNS)
 def test_decode_validation(fn, kw, status):
@@ -201,7 +209,7 @@ def test_verify_plan_waves_must_match():
     assert st == OK
     pl.waves_per_block = 1
     args = [A, 4 * ROW * 2, A, A, 16 * 8 * 128, 8 * 128, 128, 10, A, 256, A, 16, 0.1, 0.0, 0,
-            1.0, 1.0, A, 4 * ROW * 2, A, pl.workspace_bytes, None]
+            1.0, 1.0, A, 4 * ROW * 2, A, pl.workspace_bytes, None, None]
     v = [ctypes.c_void_p(x) if i in (0, 2, 3, 8, 10, 17, 19) else x for i, x in enumerate(args)]
     assert pa.lib().paged_attn_verify(ctypes.byref(pl), *v) == MISMATCH
 
@@ -209,6 +217,39 @@ def test_verify_plan_waves_must_match():
 def test_verify_empty_batch_launches_nothing():
     assert decode_status(plan_kw=dict(VERIFY, num_seqs=0), fn="paged_attn_verify", q=None,
                          out=None, ws=None) == OK
+
+
+# ---- extend argument validation: fake, never dereferenced, pointers ----
+def extend_status(**kw):
+    st, pl = plan_status(mode=1, total_q=100, max_q_len=50)
+    assert st == OK
+    args = dict(q=A, kn=A, vn=A, cu=A, ctx=A, k=A, v=A, sp=16 * 8 * 128, st=8 * 128, sh=128,
+                num_pages=10, bt=A, bt_stride=256, page_size=16, scale=0.1, softcap=0.0,
+                window=0, ks=1.0, vs=1.0, out=A, extras=None)
+    args.update(kw)
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    ex = None if args["extras"] is None else ctypes.byref(B.PaExtras(*args["extras"]))
+    return pa.lib().paged_attn_extend(
+        ctypes.byref(pl), v(args["q"]), v(args["kn"]), v(args["vn"]), v(args["cu"]),
+        v(args["ctx"]), v(args["k"]), v(args["v"]), args["sp"], args["st"], args["sh"],
+        args["num_pages"], v(args["bt"]), args["bt_stride"], args["page_size"], args["scale"],
+        args["softcap"], args["window"], args["ks"], args["vs"], v(args["out"]), None, 0, ex,
+        None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), NULLP),
+    (dict(cu=None), NULLP),
+    (dict(kn=A + 8), MISAL),
+    (dict(page_size=32), MISMATCH),
+    (dict(window=4), MISMATCH),
+    (dict(ks=float("inf")), SHAPE),
+    (dict(extras=(A + 1, None, None, 0, 0)), MISAL),
+    (dict(extras=(None, A, A, 3, 0)), SHAPE),
+    (dict(extras=(None, A, A, -1, 0)), SHAPE),
+])
+def test_extend_validation(kw, status):
+    assert extend_status(**kw) == status
 
 
 # ---- cache append argument validation: fake, never dereferenced, pointers ----
