@@ -313,11 +313,13 @@ def _decode(fn, pl, q, k_pool, v_pool, block_table, seq_lens, scale, softcap, wi
 
 
 def extend_plan(q: torch.Tensor, k_pool: torch.Tensor, block_table: torch.Tensor,
-                num_seqs: int, max_kv_len: int, max_q_len: int, window: int = 0) -> Plan:
+                num_seqs: int, max_kv_len: int, max_q_len: int, window: int = 0,
+                num_splits: int = 0) -> Plan:
+    """Plan an extend call; num_splits > 0 forces the persistent block count."""
     T, Hq, D = q.shape
     return plan(PA_MODE_EXTEND, num_seqs, Hq, k_pool.shape[2], D, k_pool.shape[1],
                 _kv_dtype_name(k_pool), window, block_table.shape[1], max_kv_len,
-                total_q=T, max_q_len=max_q_len, device=q.device.index)
+                total_q=T, max_q_len=max_q_len, num_splits=num_splits, device=q.device.index)
 
 
 def extend(pl: Plan, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,

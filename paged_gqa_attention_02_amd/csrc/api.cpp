@@ -23,6 +23,7 @@ using namespace pa;
 
 constexpr int kDefaultCus = 256;        // MI355X
 constexpr int kDefaultWavesPerCu = 8;   // split-pass occupancy when no device is queried
+constexpr int kDefaultExtendBlocksPerCu = 2;   // extend occupancy when no device is queried
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 int ilog2(int x) {
@@ -58,13 +59,31 @@ pa_status check_problem(const pa_problem& pr) {
     if (pr.mode == PA_MODE_EXTEND) {
         if (pr.total_q < 0 || pr.max_q_len < 0) return PA_ERR_INVALID_SHAPE;
         if (pr.num_seqs > 0 && pr.total_q > 0 && pr.max_q_len == 0) return PA_ERR_INVALID_SHAPE;
-        // key positions are 32-bit, and the grid is (row tiles x sequences x kv heads)
+        // key positions are 32-bit; items are (sequence, kv head, row tile)
         if ((int64_t)pr.max_kv_len + pr.max_q_len >= ((int64_t)1 << 30)) return PA_ERR_UNSUPPORTED;
         const int64_t tiles = cdiv((int64_t)pr.max_q_len * (pr.num_q_heads / pr.num_kv_heads),
                                    extend_rows_per_block());
-        if (tiles * pr.num_seqs * pr.num_kv_heads >= ((int64_t)1 << 31)) return PA_ERR_UNSUPPORTED;
+        if (tiles * pr.num_seqs * pr.num_kv_heads > kMaxExtendItems) return PA_ERR_UNSUPPORTED;
     }
     return PA_OK;
+}
+
+// Extend workspace: the items' tile prefix, their block records, and two
+// partial slots (log2-sum-exp, rows) per persistent block.
+struct ExtLayout {
+    int64_t items, rec, lse, o, total;
+};
+
+ExtLayout extend_layout(const pa_problem& pr, int64_t workers) {
+    ExtLayout L;
+    const int64_t rows = extend_rows_per_block();
+    L.items = cdiv((int64_t)pr.max_q_len * (pr.num_q_heads / pr.num_kv_heads), rows) *
+              pr.num_seqs * pr.num_kv_heads;
+    L.rec = round_up((L.items + 1) * 8, 256);
+    L.lse = L.rec + round_up(L.items * 16, 256);
+    L.o = L.lse + round_up(workers * 2 * rows * 4, 256);
+    L.total = L.o + round_up(workers * 2 * rows * pr.head_dim * 4, 256);
+    return L;
 }
 
 // Split-pass waves per block: one per 16 query rows of a kv head.
@@ -208,6 +227,32 @@ pa_status paged_attn_plan(const pa_problem* prob, int hip_device, pa_plan* out) 
                                         round_up(rows * 4, 256) +
                                         round_up(16 * (int64_t)pr.num_seqs *
                                                      pr.num_kv_heads, 256));
+    }
+    if (pr.mode == PA_MODE_EXTEND) {
+        // Persistent blocks, each owning an equal contiguous range of the key
+        // tiles of all (sequence, kv head, row tile) items; as many as the
+        // device keeps resident, or prob.num_splits when > 0.
+        int64_t workers;
+        if (pr.num_splits > 0) {
+            workers = pr.num_splits;
+        } else {
+            int per_cu = kDefaultExtendBlocksPerCu;
+            if (hip_device >= 0) {
+                int cur = -1;
+                if (hipGetDevice(&cur) != hipSuccess) return PA_ERR_HIP;
+                if (cur != hip_device && hipSetDevice(hip_device) != hipSuccess) return PA_ERR_HIP;
+                const hipError_t e =
+                    extend_blocks_per_cu(pr.head_dim, pr.kv_dtype == PA_KV_FP8_E4M3, &per_cu);
+                if (cur != hip_device) (void)hipSetDevice(cur);
+                if (e != hipSuccess || per_cu < 1) return PA_ERR_HIP;
+            }
+            workers = (int64_t)cus * per_cu;
+        }
+        if (workers > kMaxWorkers) return PA_ERR_UNSUPPORTED;
+        pl.num_splits = (int32_t)workers;
+        pl.tokens_per_split = 64;
+        pl.waves_per_block = 4;
+        pl.workspace_bytes = (uint64_t)extend_layout(pr, workers).total;
     }
     *out = pl;
     return PA_OK;
@@ -469,8 +514,6 @@ pa_status paged_attn_extend(const pa_plan* plan, const void* q, const void* k_ne
                             float scale, float softcap, int32_t window, float k_scale,
                             float v_scale, void* out, void* workspace, uint64_t workspace_bytes,
                             const pa_extras* extras, void* hip_stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     if (!plan) return PA_ERR_NULL_POINTER;
     const pa_plan& pl = *plan;
     const pa_problem& pr = pl.prob;
@@ -478,6 +521,9 @@ pa_status paged_attn_extend(const pa_plan* plan, const void* q, const void* k_ne
     if (st != PA_OK) return st;
     if (pr.mode != PA_MODE_EXTEND) return PA_ERR_PLAN_MISMATCH;
     if (page_size != pr.page_size || window != pr.window) return PA_ERR_PLAN_MISMATCH;
+    if (pl.num_splits < 1 || pl.num_splits > kMaxWorkers ||
+        pl.workspace_bytes != (uint64_t)extend_layout(pr, pl.num_splits).total)
+        return PA_ERR_PLAN_MISMATCH;
     if (pr.num_seqs == 0 || pr.total_q == 0) return PA_OK;
     if (!q || !k_new || !v_new || !cu_seqlens_q || !ctx_lens || !out) return PA_ERR_NULL_POINTER;
     st = check_pools(pl, k_pool, v_pool, kv_stride_page, kv_stride_tok, kv_stride_head,
@@ -490,9 +536,20 @@ pa_status paged_attn_extend(const pa_plan* plan, const void* q, const void* k_ne
     Extras ex;
     st = read_extras(extras, pr.num_seqs, &ex);
     if (st != PA_OK) return st;
+    if (workspace_bytes < pl.workspace_bytes) return PA_ERR_WORKSPACE_TOO_SMALL;
+    if (!workspace) return PA_ERR_NULL_POINTER;
+    if (!aligned16(workspace)) return PA_ERR_MISALIGNED;
 
     ExtendParams p;
     memset(&p, 0, sizeof p);
+    {
+        const ExtLayout L = extend_layout(pr, pl.num_splits);
+        char* ws = static_cast<char*>(workspace);
+        p.pfx = reinterpret_cast<int64_t*>(ws);
+        p.rec = reinterpret_cast<int32_t*>(ws + L.rec);
+        p.part_lse = reinterpret_cast<float*>(ws + L.lse);
+        p.part_o = reinterpret_cast<float*>(ws + L.o);
+    }
     p.sinks = ex.sinks;
     p.k_desc = ex.k_desc;
     p.v_desc = ex.v_desc;
@@ -527,7 +584,7 @@ pa_status paged_attn_extend(const pa_plan* plan, const void* q, const void* k_ne
     }
     p.v_scale = v_scale;
     p.out = out;
-    if (launch_extend(p, pr.head_dim, pr.kv_dtype == PA_KV_FP8_E4M3, pr.num_seqs,
+    if (launch_extend(p, pr.head_dim, pr.kv_dtype == PA_KV_FP8_E4M3, pl.num_splits,
                       static_cast<hipStream_t>(hip_stream)) != hipSuccess)
         return PA_ERR_HIP;
     return PA_OK;

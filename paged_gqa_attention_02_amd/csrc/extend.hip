@@ -140,6 +140,78 @@ __device__ __forceinline__ void stage_direct(const ExtendParams& p, const SeqInf
     }
 }
 
+// bf16 with page size >= 16: a run (kRowsPer rows) never crosses a page, so
+// each run takes one wave-uniform base address (its page from the staged
+// list, or its first new row) and every lane a fixed offset: its row within
+// the run times the row stride, plus its swizzled chunk (the swizzle of the
+// rows a wave stages does not change from run to run).  A run that holds
+// both context and new keys, or new rows past the sequence, takes the
+// per-lane path above.
+template <int D>
+struct StageLane {
+    uint32_t ctx_off, new_off;
+    __device__ __forceinline__ void init(const ExtendParams& p) {
+        using TL = Tile<D>;
+        constexpr int kRowsPer = 1024 / TL::kPitch;
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int slot = lane % TL::kSlots;
+        const int row = wave * kRowsPer + lane / TL::kSlots;   // its first run's row
+        const uint32_t chunk = 16 * (slot ^ (row & (TL::kSlots - 1)));
+        ctx_off = (uint32_t)(lane / TL::kSlots) * (uint32_t)(p.s_tok * 2) + chunk;
+        new_off = (uint32_t)(lane / TL::kSlots) * (uint32_t)(p.num_kv_heads * D * 2) + chunk;
+    }
+};
+
+template <int D>
+__device__ __forceinline__ void stage_runs(const ExtendParams& p, const SeqInfo& si, int jt,
+                                           uint8_t* kd, uint8_t* vd, const StageLane<D>& sl) {
+    using TL = Tile<D>;
+    constexpr int kRowsPer = 1024 / TL::kPitch;
+    constexpr int kRuns = kExtKeys / kRowsPer;
+    constexpr int kPer = kRuns / kExtWaves;                  // runs per wave
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int pmask = (1 << p.page_shift) - 1;
+    // the runs' page ids first (one wait for all of them)
+    int pg[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int j0 = jt + (wave + k * kExtWaves) * kRowsPer;
+        const int idx = min(max((j0 >> p.page_shift) - si.pg0, 0), kExtPages - 1);
+        pg[k] = si.pages[idx];
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int run = wave + k * kExtWaves;
+        const int j0 = jt + run * kRowsPer;                  // the run's first key
+        const uint8_t *kb, *vb;
+        uint32_t off;
+        if (j0 + kRowsPer <= si.C) {
+            const int64_t page = __builtin_amdgcn_readfirstlane(pg[k]);
+            const int64_t o = (page * p.s_page + (int64_t)(j0 & pmask) * p.s_tok +
+                               (int64_t)si.kvh * p.s_head) * 2;
+            kb = static_cast<const uint8_t*>(p.k_pool) + o;
+            vb = static_cast<const uint8_t*>(p.v_pool) + o;
+            off = sl.ctx_off;
+        } else if (j0 >= si.C && j0 + kRowsPer <= si.C + si.n) {
+            const int64_t o = ((int64_t)(si.q0 + j0 - si.C) * p.num_kv_heads + si.kvh) * D * 2;
+            kb = static_cast<const uint8_t*>(p.k_new) + o;
+            vb = static_cast<const uint8_t*>(p.v_new) + o;
+            off = sl.new_off;
+        } else {
+            const int lane = threadIdx.x & 63;
+            const int row = run * kRowsPer + lane / TL::kSlots;
+            key_rows<D, false>(p, si, jt + row, kb, vb);
+            off = 16 * ((lane % TL::kSlots) ^ (row & (TL::kSlots - 1)));
+        }
+        __builtin_amdgcn_global_load_lds(
+            (const void __attribute__((address_space(1)))*)(kb + off),
+            (void __attribute__((address_space(3)))*)(kd + run * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(
+            (const void __attribute__((address_space(1)))*)(vb + off),
+            (void __attribute__((address_space(3)))*)(vd + run * 1024), 16, 0, 0);
+    }
+}
+
 // fp8: global -> registers (16 elements a thread), converted and written to
 // the swizzled LDS tile as bf16.  Threads past kRowsPerPass * kLanesPerRow idle.
 template <int D>
@@ -210,20 +282,29 @@ struct ExtAcc {
 
 // Per-lane byte offsets of the operand reads inside a swizzled tile: K row
 // 16kb + c, slot 4ds + grp is at kb*16*pitch + koff[ds]; V row
-// 32ks + step_key(grp, jj), slot c is at ks*32*pitch + (jj >= 4 ? 16*pitch : 0)
-// + voff[jj & 3] (rows 16 apart share the swizzle).
+// 32ks + step_key(grp, jj), slot c, 8-byte half h is at ks*32*pitch +
+// (jj >= 4 ? 16*pitch : 0) + voff[h][jj & 3] (rows 16 apart share the swizzle).
 template <int D>
 struct LaneOffs {
     int koff[D / 32];
-    int voff[4];
+    int voff[D == 128 ? 2 : 1][4];   // [half][j]
     __device__ __forceinline__ void init(int c, int grp) {
         using TL = Tile<D>;
 #pragma unroll
         for (int ds = 0; ds < D / 32; ++ds) koff[ds] = TL::off(c, 4 * ds + grp);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            voff[j] = (D == 128) ? TL::off(4 * grp + j, c)
-                                 : TL::off(4 * grp + j, c >> 1) + 8 * (c & 1);
+        for (int j = 0; j < 4; ++j) {
+            if constexpr (D == 128) {
+                // lanes c >= 8 read the other 8-byte half first, so 16 lanes
+                // reading one row cover all banks once (their data then
+                // belongs to MFMA e ^ 4: see the finish)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    voff[h][j] = TL::off(4 * grp + j, c) + 8 * (h ^ (c >> 3));
+            } else {
+                voff[0][j] = TL::off(4 * grp + j, c >> 1) + 8 * (c & 1);
+            }
+        }
     }
 };
 
@@ -368,8 +449,7 @@ __device__ __forceinline__ void tile_compute(const uint8_t* kl, const uint8_t* v
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj)
                 vr[jj] = *reinterpret_cast<const u32x2*>(
-                    vl + ks * 32 * kPitch + (jj >= 4 ? 16 * kPitch : 0) + lo.voff[jj & 3] +
-                    8 * half);
+                    vl + ks * 32 * kPitch + (jj >= 4 ? 16 * kPitch : 0) + lo.voff[half][jj & 3]);
 #pragma unroll
             for (int e2 = 0; e2 < 4; ++e2) {
                 const int w = e2 >> 1, e = 4 * half + e2;
@@ -386,31 +466,104 @@ __device__ __forceinline__ void tile_compute(const uint8_t* kl, const uint8_t* v
     }
 }
 
+// An item: row tile mt (kExtRows rows (token, head)) of sequence b, kv head
+// kvh, and the key tiles [jt0, jt0 + 64 * ntiles) its rows attend (from the
+// window start of its first token to its last token).  Items are numbered
+// i = (b * Hkv + kvh) * q_tiles + mt, so the row tiles of one (sequence, kv
+// head), which read the same keys, are neighbours; ntiles = 0 for a row tile
+// past the sequence's new tokens.
+struct Item {
+    int b, kvh, mt, q0, n, C, t0, t1, jt0, ntiles;
+};
+
+__device__ __forceinline__ Item item_of(const ExtendParams& p, int64_t i) {
+    Item it;
+    it.mt = (int)(i % p.q_tiles);
+    const int seg = (int)(i / p.q_tiles);
+    it.kvh = seg % p.num_kv_heads;
+    it.b = seg / p.num_kv_heads;
+    it.q0 = p.cu_seqlens_q[it.b];
+    it.n = p.cu_seqlens_q[it.b + 1] - it.q0;
+    it.C = p.ctx_lens[it.b];
+    const int T = kExtRows / p.group;                // tokens per row tile
+    it.t0 = it.mt * T;
+    it.t1 = min(it.n, it.t0 + T);
+    it.jt0 = 0;
+    it.ntiles = 0;
+    if (it.t0 < it.n) {
+        const int pos_first = it.C + it.t0, pos_last = it.C + it.t1 - 1;
+        const int j_lo = p.window > 0 ? max(0, pos_first - p.window + 1) : 0;
+        it.jt0 = j_lo & ~(kExtKeys - 1);
+        it.ntiles = (pos_last + 1 - it.jt0 + kExtKeys - 1) / kExtKeys;
+    }
+    return it;
+}
+
+__device__ __forceinline__ int64_t ext_items(const ExtendParams& p) {
+    return (int64_t)p.num_seqs * p.num_kv_heads * p.q_tiles;
+}
+
+// Partial row r of slot `slot` of persistent block w.
+__device__ __forceinline__ int64_t ext_part_row(int64_t w, int slot, int r) {
+    return (w * 2 + slot) * kExtRows + r;
+}
+
+// ---------------------------------------------------------------------------
+// Tile prefix over the items: pfx[i] = key tiles of items 0..i-1 (one block).
+// ---------------------------------------------------------------------------
+constexpr int kScanThreads = 1024;
+
+__global__ __launch_bounds__(kScanThreads) void extend_scan_kernel(ExtendParams p) {
+    __shared__ int64_t sm_sum[kScanThreads / 64];
+    const int64_t items = ext_items(p);
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    int64_t base = 0;
+    if (threadIdx.x == 0) p.pfx[0] = 0;
+    for (int64_t c0 = 0; c0 < items; c0 += kScanThreads) {
+        const int64_t i = c0 + threadIdx.x;
+        int v = i < items ? item_of(p, i).ntiles : 0;       // < 2^24 each
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int u = __shfl_up(v, d, 64);
+            if (lane >= d) v += u;
+        }
+        if (lane == 63) sm_sum[wv] = v;
+        __syncthreads();
+        int64_t off = 0, total = 0;
+        for (int k = 0; k < kScanThreads / 64; ++k) {
+            off += k < wv ? sm_sum[k] : 0;
+            total += sm_sum[k];
+        }
+        if (i < items) p.pfx[i + 1] = base + off + v;
+        base += total;
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// One piece: key tiles [from, to) of item `it`, computed by the whole block.
+// A complete piece (all tiles of the item) writes bf16 rows of `out`; a part
+// writes normalised fp32 rows and their log2-sum-exp to the block's slot.
+// ---------------------------------------------------------------------------
+struct ExtLds {
+    uint8_t *k0, *v0, *k1, *v1;
+    int* pages;
+};
+
 template <int D, bool FP8, int MODE>
-__global__ __launch_bounds__(kExtThreads, kExtOccupancy) void extend_kernel(ExtendParams pk) {
-    using TL = Tile<D>;
+__device__ __forceinline__ void extend_piece(const ExtendParams& pk, const Item& it, int from,
+                                             int to, bool complete, int64_t w, int slot,
+                                             const ExtLds& L) {
     constexpr int kDS = D / 32;        // QK contraction steps
     constexpr int kVE = D / 16;        // PV MFMAs per (row block, key step)
-    // two buffers of K and V (tile `it` in buffer it & 1)
-    __shared__ __attribute__((aligned(1024))) uint8_t sm_k0[TL::kBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t sm_v0[TL::kBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t sm_k1[TL::kBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t sm_v1[TL::kBytes];
-    __shared__ int sm_pages[kExtPages];
-
     ExtendParams p = pk;
     const int G = p.group;
-    const int segs = p.num_seqs * p.num_kv_heads;
-    // heavier tiles (later tokens, more keys) first; all tiles of one
-    // (sequence, kv head) on one XCD when segs is a multiple of 8
-    const int seg = blockIdx.x % segs;
-    const int mt = p.q_tiles - 1 - (int)(blockIdx.x / segs);
     SeqInfo si;
-    si.b = seg / p.num_kv_heads;
-    si.kvh = seg % p.num_kv_heads;
-    si.q0 = p.cu_seqlens_q[si.b];
-    si.n = p.cu_seqlens_q[si.b + 1] - si.q0;
-    si.C = p.ctx_lens[si.b];
+    si.b = it.b;
+    si.kvh = it.kvh;
+    si.q0 = it.q0;
+    si.n = it.n;
+    si.C = it.C;
     // per-request descales of the cached part (uniform loads)
     if (p.k_desc) {
         const float kd = p.k_desc[p.desc_per_seq ? si.b : 0];
@@ -418,10 +571,7 @@ __global__ __launch_bounds__(kExtThreads, kExtOccupancy) void extend_kernel(Exte
         p.cap_c1_ctx *= kd;
     }
     if (p.v_desc) p.v_scale *= p.v_desc[p.desc_per_seq ? si.b : 0];
-    const int T = kExtRows / G;        // tokens per block
-    const int t0 = mt * T;
-    if (t0 >= si.n) return;            // (uniform over the block)
-    const int t1 = min(si.n, t0 + T);
+    const int t0 = it.t0, t1 = it.t1;
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int c = lane & 15, grp = lane >> 4;
@@ -448,13 +598,12 @@ __global__ __launch_bounds__(kExtThreads, kExtOccupancy) void extend_kernel(Exte
 
     // ---- key range ----
     const int pos_first = si.C + t0, pos_last = si.C + t1 - 1;
-    const int j_lo = p.window > 0 ? max(0, pos_first - p.window + 1) : 0;
-    const int jt0 = j_lo & ~(kExtKeys - 1);
-    const int ntiles = (pos_last + 1 - jt0 + kExtKeys - 1) / kExtKeys;
+    const int jt0 = it.jt0;
+    const int ntiles = it.ntiles;
 
     // Context page ids in LDS, kExtPages at a time: `need(jt)` reloads the list
     // (between barriers) when tile jt's context keys are not all in it.
-    si.pages = sm_pages;
+    si.pages = L.pages;
     si.pg0 = -kExtPages;
     auto need = [&](int jt) {
         const int last = min(jt + kExtKeys, si.C) - 1;          // last context key
@@ -465,7 +614,7 @@ __global__ __launch_bounds__(kExtThreads, kExtOccupancy) void extend_kernel(Exte
         si.pg0 = jt >> p.page_shift;
         const int cnt = min(kExtPages, ((si.C - 1) >> p.page_shift) - si.pg0 + 1);
         const int32_t* row = p.block_table + (int64_t)si.b * p.bt_stride + si.pg0;
-        for (int i = threadIdx.x; i < cnt; i += kExtThreads) sm_pages[i] = row[i];
+        for (int i = threadIdx.x; i < cnt; i += kExtThreads) L.pages[i] = row[i];
         __syncthreads();
     };
 
@@ -480,11 +629,11 @@ __global__ __launch_bounds__(kExtThreads, kExtOccupancy) void extend_kernel(Exte
         for (int e = 0; e < kVE; ++e) A.o[rb][e] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // ---- the tiles, in phases of one kind: tiles [it_win, it_diag) need no
-    // mask (inside every row's window and below every row's diagonal); the
-    // tile holding key C mixes context and new keys.  A phase of full
-    // single-kind tiles runs the FAST variant, the others the general one;
-    // each phase is its own loop. ----
+    // ---- the tiles [from, to), in phases of one kind: tiles [it_win,
+    // it_diag) need no mask (inside every row's window and below every row's
+    // diagonal); the tile holding key C mixes context and new keys.  A phase
+    // of full single-kind tiles runs the FAST variant, the others the general
+    // one; each phase is its own loop. ----
     const int nd = pos_first - (kExtKeys - 1) - jt0;     // tiles it <= nd/64 end at or
     const int it_diag = nd < 0 ? 0 : nd / kExtKeys + 1;   // before the first row's diagonal
     const int it_win = p.window > 0 ? max(0, (pos_last - p.window + 1 - jt0 + kExtKeys - 1) /
@@ -495,27 +644,33 @@ __global__ __launch_bounds__(kExtThreads, kExtOccupancy) void extend_kernel(Exte
     cut[2] = (it_split >= cut[1] && it_split < cut[4]) ? it_split : cut[4];
     cut[3] = (it_split >= cut[1] && it_split < cut[4]) ? it_split + 1 : cut[4];
     // phases: [cut0,cut1) general, [cut1,cut2) fast, [cut2,cut3) general (split),
-    //         [cut3,cut4) fast, [cut4,cut5) general
+    //         [cut3,cut4) fast, [cut4,cut5) general; each clipped to [from, to)
+#pragma unroll
+    for (int k = 0; k < 6; ++k) cut[k] = min(max(cut[k], from), to);
 
     if constexpr (!FP8) {
+        StageLane<D> sl;
+        sl.init(p);
+        const bool runs = p.page_shift >= 4;                 // runs stay inside a page
         auto stage = [&](int jt, uint8_t* kd, uint8_t* vd) {
             need(jt);
-            stage_direct<D>(p, si, jt, kd, vd);
+            if (runs) stage_runs<D>(p, si, jt, kd, vd, sl);
+            else stage_direct<D>(p, si, jt, kd, vd);
         };
-        auto run = [&](int from, int to, auto fast) {
-            for (int it = from; it < to; ++it) {
-                const int jt = jt0 + it * kExtKeys;
-                uint8_t* kc = (it & 1) ? sm_k1 : sm_k0;
-                uint8_t* vc = (it & 1) ? sm_v1 : sm_v0;
-                if (it + 1 < ntiles) stage(jt + kExtKeys, (it & 1) ? sm_k0 : sm_k1,
-                                           (it & 1) ? sm_v0 : sm_v1);
+        auto run = [&](int a, int e, auto fast) {
+            for (int i = a; i < e; ++i) {
+                const int jt = jt0 + i * kExtKeys;
+                uint8_t* kc = (i & 1) ? L.k1 : L.k0;
+                uint8_t* vc = (i & 1) ? L.v1 : L.v0;
+                if (i + 1 < to) stage(jt + kExtKeys, (i & 1) ? L.k0 : L.k1,
+                                      (i & 1) ? L.v0 : L.v1);
                 tile_compute<D, MODE, decltype(fast)::value>(kc, vc, lo, qop, A, p, si, pos_q,
                                                              pos_first, pos_last, jt);
                 wait_vm0();
                 __syncthreads();
             }
         };
-        stage(jt0, sm_k0, sm_v0);
+        stage(jt0 + from * kExtKeys, (from & 1) ? L.k1 : L.k0, (from & 1) ? L.v1 : L.v0);
         wait_vm0();
         __syncthreads();
         run(cut[0], cut[1], std::false_type{});
@@ -534,21 +689,21 @@ __global__ __launch_bounds__(kExtThreads, kExtOccupancy) void extend_kernel(Exte
             stage8_store<D>(sk, kd);
             stage8_store<D>(sv, vd);
         };
-        auto run = [&](int from, int to, auto fast) {
-            for (int it = from; it < to; ++it) {
-                const int jt = jt0 + it * kExtKeys;
-                const bool more = it + 1 < ntiles;
+        auto run = [&](int a, int e, auto fast) {
+            for (int i = a; i < e; ++i) {
+                const int jt = jt0 + i * kExtKeys;
+                const bool more = i + 1 < to;
                 if (more) load(jt + kExtKeys);
-                tile_compute<D, MODE, decltype(fast)::value>((it & 1) ? sm_k1 : sm_k0,
-                                                             (it & 1) ? sm_v1 : sm_v0, lo, qop,
+                tile_compute<D, MODE, decltype(fast)::value>((i & 1) ? L.k1 : L.k0,
+                                                             (i & 1) ? L.v1 : L.v0, lo, qop,
                                                              A, p, si, pos_q, pos_first,
                                                              pos_last, jt);
-                if (more) store((it & 1) ? sm_k0 : sm_k1, (it & 1) ? sm_v0 : sm_v1);
+                if (more) store((i & 1) ? L.k0 : L.k1, (i & 1) ? L.v0 : L.v1);
                 __syncthreads();
             }
         };
-        load(jt0);
-        store(sm_k0, sm_v0);
+        load(jt0 + from * kExtKeys);
+        store((from & 1) ? L.k1 : L.k0, (from & 1) ? L.v1 : L.v0);
         __syncthreads();
         run(cut[0], cut[1], std::false_type{});
         run(cut[1], cut[2], std::true_type{});
@@ -557,60 +712,225 @@ __global__ __launch_bounds__(kExtThreads, kExtOccupancy) void extend_kernel(Exte
         run(cut[4], cut[5], std::false_type{});
     }
 
-    // ---- finish: O^T[d][row c] / l, d = kVE*(4grp + j) + e ----
+    // ---- finish: O^T[d][row c] / l, d = kVE*(4grp + j) + (e ^ sw): for D = 128
+    // the O^T rows 8..15 (grp >= 2) hold their two 4-element halves swapped
+    // (see LaneOffs) ----
+    const int sw = (kVE == 8 && grp >= 2) ? 4 : 0;
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
         const float lt = col4_sum(A.l[rb]);
         if (!row_ok[rb]) continue;
         const int r = (wave * kRB + rb) * 16 + c;
-        uint16_t* orow = static_cast<uint16_t*>(p.out) +
-                         ((int64_t)(si.q0 + row_t[rb]) * p.num_q_heads + si.kvh * G + r % G) * D;
-        // a sink logit joins the normaliser (no value row)
-        float den = lt;
-        if (p.sinks) den += fast_exp2(p.sinks[si.kvh * G + r % G] * kLog2e - A.m[rb]);
-        const float inv = 1.f / den;
+        if (complete) {
+            uint16_t* orow = static_cast<uint16_t*>(p.out) +
+                             ((int64_t)(si.q0 + row_t[rb]) * p.num_q_heads + si.kvh * G + r % G) *
+                                 D;
+            // a sink logit joins the normaliser (no value row)
+            float den = lt;
+            if (p.sinks) den += fast_exp2(p.sinks[si.kvh * G + r % G] * kLog2e - A.m[rb]);
+            const float inv = 1.f / den;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            uint32_t wv[kVE / 2];
+            for (int j = 0; j < 4; ++j) {
+                uint32_t wv[kVE / 2];
 #pragma unroll
-            for (int e = 0; e < kVE; e += 2)
-                wv[e / 2] = pack_bf16x2(A.o[rb][e][j] * inv, A.o[rb][e + 1][j] * inv);
-            uint16_t* dst = orow + kVE * (4 * grp + j);
-            if constexpr (kVE == 8)
-                *reinterpret_cast<u32x4*>(dst) = u32x4{wv[0], wv[1], wv[2], wv[3]};
-            else
-                *reinterpret_cast<u32x2*>(dst) = u32x2{wv[0], wv[1]};
+                for (int e = 0; e < kVE; e += 2)
+                    wv[e / 2] = pack_bf16x2(A.o[rb][e][j] * inv, A.o[rb][e + 1][j] * inv);
+                uint16_t* dst = orow + kVE * (4 * grp + j);
+                if constexpr (kVE == 8) {
+                    *reinterpret_cast<u32x2*>(dst + sw) = u32x2{wv[0], wv[1]};
+                    *reinterpret_cast<u32x2*>(dst + (4 ^ sw)) = u32x2{wv[2], wv[3]};
+                } else {
+                    *reinterpret_cast<u32x2*>(dst) = u32x2{wv[0], wv[1]};
+                }
+            }
+        } else {
+            // a part: normalised rows and log2-sum-exp (no sink), for the merge
+            const int64_t prow = ext_part_row(w, slot, r);
+            const float inv = 1.f / lt;
+            float* po = p.part_o + prow * D;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int e = 0; e < kVE; e += 4)
+                    *reinterpret_cast<f32x4*>(po + kVE * (4 * grp + j) + (e ^ sw)) =
+                        f32x4{A.o[rb][e][j] * inv, A.o[rb][e + 1][j] * inv,
+                              A.o[rb][e + 2][j] * inv, A.o[rb][e + 3][j] * inv};
+            if (grp == 0) p.part_lse[prow] = A.m[rb] + __log2f(lt);
         }
     }
 }
 
+// ---------------------------------------------------------------------------
+// Persistent blocks: block w owns key tiles [w*N/W, (w+1)*N/W) of the items
+// laid end to end (N tiles in all), cut into pieces at item boundaries.  The
+// owner of an item's first tile records which blocks cover it.
+// ---------------------------------------------------------------------------
+template <int D, bool FP8, int MODE>
+__global__ __launch_bounds__(kExtThreads, kExtOccupancy) void extend_kernel(ExtendParams p) {
+    using TL = Tile<D>;
+    // two buffers of K and V (tile `it` in buffer it & 1)
+    __shared__ __attribute__((aligned(1024))) uint8_t sm_k0[TL::kBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t sm_v0[TL::kBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t sm_k1[TL::kBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t sm_v1[TL::kBytes];
+    __shared__ int sm_pages[kExtPages];
+    const ExtLds L{sm_k0, sm_v0, sm_k1, sm_v1, sm_pages};
+
+    // Blocks are dealt to the 8 XCDs in turn; the logical index w gives each
+    // XCD a contiguous run of the tile stream, so the row tiles of one
+    // (sequence, kv head) share its L2.
+    const int64_t W = gridDim.x;
+    const int64_t w = (W % 8 == 0) ? (int64_t)(blockIdx.x % 8) * (W / 8) + blockIdx.x / 8
+                                    : (int64_t)blockIdx.x;
+    const int64_t items = ext_items(p);
+    const int64_t N = p.pfx[items];
+    const int64_t r0 = w * N / W, r1 = (w + 1) * N / W;
+    if (r0 >= r1) {
+        // an empty range (N < W): the merge may read this block's slot 0
+        for (int r = threadIdx.x; r < kExtRows; r += kExtThreads)
+            p.part_lse[ext_part_row(w, 0, r)] = -INFINITY;
+        return;
+    }
+    // the item holding tile r0: the last i with pfx[i] <= r0
+    int64_t lo = 0, hi = items;
+    while (hi - lo > 1) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (p.pfx[mid] <= r0) lo = mid;
+        else hi = mid;
+    }
+    int64_t i = lo;
+    int64_t pos = r0;
+    int slot = 0;
+    while (pos < r1) {
+        while (p.pfx[i + 1] <= pos) ++i;                 // (items without tiles)
+        const Item it = item_of(p, i);
+        const int64_t start = p.pfx[i], end = p.pfx[i + 1];
+        const int from = (int)(pos - start);
+        const int to = (int)(min(r1, end) - start);
+        const bool complete = from == 0 && to == it.ntiles;
+        if (from == 0 && threadIdx.x == 0) {
+            // the owner of the item's first tile: which blocks cover it
+            const int64_t w_last = complete ? w : ((end * W + N - 1) / N - 1);
+            *reinterpret_cast<int4*>(p.rec + 4 * i) = int4{(int)w, (int)w_last, slot, 0};
+        }
+        extend_piece<D, FP8, MODE>(p, it, from, to, complete, w, slot, L);
+        pos += to - from;
+        slot = 1;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Merge: kMergeSlices blocks per item covered by several blocks, each taking a
+// slice of its rows; per row and column quad, the pieces' rows weighted by
+// 2^(lse - max) (the stage-2 merge of the decode page), a sink joining the
+// sum once.  A thread folds kMergeUnits (row, quad) units side by side.
+// ---------------------------------------------------------------------------
+constexpr int kExtMergeThreads = 256;
+constexpr int kMergeSlices = 4;
+
+template <int D>
+__global__ __launch_bounds__(kExtMergeThreads) void extend_merge_kernel(ExtendParams p) {
+    constexpr int kQ = D / 4;
+    constexpr int kSliceRows = kExtRows / kMergeSlices;
+    constexpr int kUnits = kSliceRows * kQ / kExtMergeThreads;
+    const int64_t i = blockIdx.x / kMergeSlices;
+    const int slice = blockIdx.x % kMergeSlices;
+    const Item it = item_of(p, i);
+    if (it.ntiles == 0) return;
+    const int4 rec = *reinterpret_cast<const int4*>(p.rec + 4 * i);
+    if (rec.x == rec.y) return;                          // written whole by one block
+    const int G = p.group;
+    const int rows = (it.t1 - it.t0) * G;
+    if (slice * kSliceRows >= rows) return;
+    float m[kUnits], sum[kUnits];
+    f32x4 acc[kUnits];
+#pragma unroll
+    for (int k = 0; k < kUnits; ++k) {
+        m[k] = -INFINITY;
+        sum[k] = 0.f;
+        acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int piece = 0; piece <= rec.y - rec.x; ++piece) {
+        const int64_t base = ext_part_row(rec.x + piece, piece == 0 ? rec.z : 0, 0);
+        float lse[kUnits];
+        f32x4 o[kUnits];
+#pragma unroll
+        for (int k = 0; k < kUnits; ++k) {
+            const int u = threadIdx.x + kExtMergeThreads * k;
+            const int r = slice * kSliceRows + u / kQ, q = u % kQ;
+            lse[k] = -INFINITY;
+            o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (r < rows) {
+                lse[k] = p.part_lse[base + r];
+                o[k] = *reinterpret_cast<const f32x4*>(p.part_o + (base + r) * D + 4 * q);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kUnits; ++k) {
+            if (lse[k] == -INFINITY) continue;          // (an empty block's slot)
+            const float mn = fmaxf(m[k], lse[k]);
+            const float f = m[k] == -INFINITY ? 0.f : fast_exp2(m[k] - mn);
+            const float wt = fast_exp2(lse[k] - mn);
+            sum[k] = sum[k] * f + wt;
+            acc[k] = acc[k] * f + wt * o[k];
+            m[k] = mn;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kUnits; ++k) {
+        const int u = threadIdx.x + kExtMergeThreads * k;
+        const int r = slice * kSliceRows + u / kQ, q = u % kQ;
+        if (r >= rows) continue;
+        const int h = it.kvh * G + r % G;
+        float s = sum[k];
+        if (p.sinks && s > 0.f) s += fast_exp2(p.sinks[h] * kLog2e - m[k]);
+        const float inv = s > 0.f ? 1.f / s : 0.f;
+        uint16_t* dst = static_cast<uint16_t*>(p.out) +
+                        ((int64_t)(it.q0 + it.t0 + r / G) * p.num_q_heads + h) * D + 4 * q;
+        *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(acc[k].x * inv, acc[k].y * inv),
+                                               pack_bf16x2(acc[k].z * inv, acc[k].w * inv)};
+    }
+}
+
 template <int D, bool FP8>
-hipError_t launch_extend_t(const ExtendParams& p, unsigned blocks, hipStream_t stream) {
-    const bool fold = !p.has_cap && p.qk_scale2 > 0.f && p.qk_scale2_ctx > 0.f;
-    if (p.has_cap)
-        hipLaunchKernelGGL((extend_kernel<D, FP8, kCap>), dim3(blocks), dim3(kExtThreads), 0,
-                           stream, p);
-    else if (fold)
-        hipLaunchKernelGGL((extend_kernel<D, FP8, kFold>), dim3(blocks), dim3(kExtThreads), 0,
-                           stream, p);
-    else
-        hipLaunchKernelGGL((extend_kernel<D, FP8, kScale>), dim3(blocks), dim3(kExtThreads), 0,
-                           stream, p);
-    return hipGetLastError();
+const void* extend_kernel_ptr(int mode) {
+    if (mode == kCap) return reinterpret_cast<const void*>(&extend_kernel<D, FP8, kCap>);
+    if (mode == kFold) return reinterpret_cast<const void*>(&extend_kernel<D, FP8, kFold>);
+    return reinterpret_cast<const void*>(&extend_kernel<D, FP8, kScale>);
+}
+
+const void* extend_kernel_for(int head_dim, bool fp8, int mode) {
+    if (head_dim == 128)
+        return fp8 ? extend_kernel_ptr<128, true>(mode) : extend_kernel_ptr<128, false>(mode);
+    return fp8 ? extend_kernel_ptr<64, true>(mode) : extend_kernel_ptr<64, false>(mode);
 }
 
 }  // namespace
 
 int extend_rows_per_block() { return kExtRows; }
 
-hipError_t launch_extend(const ExtendParams& p, int head_dim, bool fp8, int num_seqs,
+hipError_t launch_extend(const ExtendParams& p, int head_dim, bool fp8, int workers,
                          hipStream_t stream) {
-    const unsigned blocks = (unsigned)p.q_tiles * (unsigned)num_seqs * (unsigned)p.num_kv_heads;
+    const int mode = p.has_cap ? kCap
+                     : (p.qk_scale2 > 0.f && p.qk_scale2_ctx > 0.f) ? kFold : kScale;
+    hipLaunchKernelGGL(extend_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, p);
+    const void* f = extend_kernel_for(head_dim, fp8, mode);
+    void* args[] = {const_cast<ExtendParams*>(&p)};
+    hipError_t e = hipLaunchKernel(f, dim3(workers), dim3(kExtThreads), args, 0, stream);
+    if (e != hipSuccess) return e;
+    const int64_t items = (int64_t)p.num_seqs * p.num_kv_heads * p.q_tiles;
     if (head_dim == 128)
-        return fp8 ? launch_extend_t<128, true>(p, blocks, stream)
-                   : launch_extend_t<128, false>(p, blocks, stream);
-    return fp8 ? launch_extend_t<64, true>(p, blocks, stream)
-               : launch_extend_t<64, false>(p, blocks, stream);
+        hipLaunchKernelGGL(extend_merge_kernel<128>, dim3((unsigned)(items * kMergeSlices)),
+                           dim3(kExtMergeThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL(extend_merge_kernel<64>, dim3((unsigned)(items * kMergeSlices)),
+                           dim3(kExtMergeThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t extend_blocks_per_cu(int head_dim, bool fp8, int* out) {
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        out, extend_kernel_for(head_dim, fp8, kFold), kExtThreads, 0);
 }
 
 }  // namespace pa

@@ -93,6 +93,11 @@ struct ExtendParams {
     const float* v_desc;
     int32_t desc_per_seq;
     void* out;                // bf16 [total_q, Hq, D]
+    // persistent-block split of the key tiles (workspace)
+    int64_t* pfx;             // [items + 1]: key tiles of items 0..i-1
+    int32_t* rec;             // [items][4]: blocks covering an item, first block's slot
+    float* part_lse;          // [workers][2][rows per block] (log2 domain)
+    float* part_o;            // [workers][2][rows per block][D]
 };
 
 struct AppendParams {
@@ -120,8 +125,13 @@ hipError_t decode_blocks_per_cu(int head_dim, bool fp8, bool uniform_pages, int 
                                 int* out);
 constexpr int kMaxDecodeRows = 64;   // query rows per kv head: 16 per wave, 4 waves
 hipError_t launch_gather(const GatherParams& p, int head_dim, bool fp8, hipStream_t stream);
-hipError_t launch_extend(const ExtendParams& p, int head_dim, bool fp8, int num_seqs,
+// Extend: a scan of the items' tile counts, `workers` persistent blocks, and a
+// merge of the items several blocks cover.
+hipError_t launch_extend(const ExtendParams& p, int head_dim, bool fp8, int workers,
                          hipStream_t stream);
+// Resident extend blocks per compute unit.
+hipError_t extend_blocks_per_cu(int head_dim, bool fp8, int* out);
+constexpr int64_t kMaxExtendItems = (int64_t)1 << 24;   // (sequence, kv head, row tile)
 // Rows (new token, query head) one extend block covers.
 int extend_rows_per_block();
 

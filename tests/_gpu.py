@@ -45,10 +45,11 @@ def run_verify(case, q_bits, num_splits=None, tensors=None):
     return out, pl
 
 
-def run_extend(case, tensors=None):
+def run_extend(case, tensors=None, num_splits=0):
     t = tensors or I.extend_tensors(case, DEV)
     pl = pa.extend_plan(t["q"], t["k_pool"], t["block_table"], case.batch,
-                        case.max_kv_len, case.max_q_len, window=case.window)
+                        case.max_kv_len, case.max_q_len, window=case.window,
+                        num_splits=num_splits)
     out = pa.extend(pl, t["q"], t["k_new"], t["v_new"], t["cu_seqlens_q"], t["ctx_lens"],
                     t["k_pool"], t["v_pool"], t["block_table"], case.scale,
                     softcap=case.softcap, window=case.window, k_scale=case.k_scale,

@@ -225,7 +225,7 @@ def extend_status(**kw):
     assert st == OK
     args = dict(q=A, kn=A, vn=A, cu=A, ctx=A, k=A, v=A, sp=16 * 8 * 128, st=8 * 128, sh=128,
                 num_pages=10, bt=A, bt_stride=256, page_size=16, scale=0.1, softcap=0.0,
-                window=0, ks=1.0, vs=1.0, out=A, extras=None)
+                window=0, ks=1.0, vs=1.0, out=A, extras=None, ws=A, ws_bytes=pl.workspace_bytes)
     args.update(kw)
     v = lambda x: None if x is None else ctypes.c_void_p(x)
     ex = None if args["extras"] is None else ctypes.byref(B.PaExtras(*args["extras"]))
@@ -233,8 +233,8 @@ def extend_status(**kw):
         ctypes.byref(pl), v(args["q"]), v(args["kn"]), v(args["vn"]), v(args["cu"]),
         v(args["ctx"]), v(args["k"]), v(args["v"]), args["sp"], args["st"], args["sh"],
         args["num_pages"], v(args["bt"]), args["bt_stride"], args["page_size"], args["scale"],
-        args["softcap"], args["window"], args["ks"], args["vs"], v(args["out"]), None, 0, ex,
-        None)
+        args["softcap"], args["window"], args["ks"], args["vs"], v(args["out"]), v(args["ws"]),
+        args["ws_bytes"], ex, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -247,9 +247,25 @@ def extend_status(**kw):
     (dict(extras=(A + 1, None, None, 0, 0)), MISAL),
     (dict(extras=(None, A, A, 3, 0)), SHAPE),
     (dict(extras=(None, A, A, -1, 0)), SHAPE),
+    (dict(ws_bytes=100), WS),
+    (dict(ws=None), NULLP),
+    (dict(ws=A + 8), MISAL),
 ])
 def test_extend_validation(kw, status):
     assert extend_status(**kw) == status
+
+
+def test_extend_plan_persistent_blocks():
+    """Extend plans 2 persistent blocks per compute unit without a device, and
+    a workspace for the tile prefix, the records and two partial slots of 128
+    rows per block."""
+    st, pl = plan_status(mode=1, total_q=100, max_q_len=50)
+    assert st == OK and pl.num_splits == 512 and pl.waves_per_block == 4
+    items = 4 * 8 * 2          # seqs x kv heads x ceil(50 * 4 / 128)
+    assert pl.workspace_bytes >= (items + 1) * 8 + items * 16 + 512 * 2 * 128 * 129 * 4
+    st, pl2 = plan_status(mode=1, total_q=100, max_q_len=50, num_splits=7)
+    assert st == OK and pl2.num_splits == 7 and pl2.workspace_bytes < pl.workspace_bytes
+    assert plan_status(mode=1, total_q=1 << 30, max_q_len=1 << 29, num_seqs=64)[0] == UNSUP
 
 
 # ---- cache append argument validation: fake, never dereferenced, pointers ----

@@ -37,12 +37,12 @@ def ctx_tokens(case):
     return np.concatenate(ks), np.concatenate(vs)
 
 
-def check(case, what="", rows=None):
+def check(case, what="", rows=None, num_splits=0):
     say(f"[extend] {what} B={case.batch} ctx={list(case.ctx_lens)[:8]} "
         f"q={list(case.q_lens)[:8]} Hq={case.num_q_heads} Hkv={case.num_kv_heads} "
         f"D={case.head_dim} P={case.kv.page_size} kv={case.kv_dtype} W={case.window} "
-        f"cap={case.softcap}")
-    out, _ = run_extend(case)
+        f"cap={case.softcap} splits={num_splits}")
+    out, _ = run_extend(case, num_splits=num_splits)
     got = to_f64(out)
     ref = oracle.extend(case, rows=rows)
     if rows is not None:
@@ -78,6 +78,29 @@ def test_extend_workload_sampled_rows():
 def test_extend_shapes(ctx, ql, Hq, Hkv, D, P, kw):
     case = case_of(ctx, ql, Hq, Hkv, D, P, 200 + len(ctx) + sum(ql) % 97, **kw)
     check(case, f"ctx={ctx} q={ql}")
+
+
+@pytest.mark.parametrize("splits", [1, 3, 8, 61, 700, 20000])
+def test_extend_persistent_block_counts(splits):
+    """Any number of persistent blocks gives the same rows: one block walking
+    every item, few blocks splitting items into parts merged by log-sum-exp,
+    more blocks than key tiles (empty blocks)."""
+    case = case_of([300, 0, 1500, 77], [200, 64, 33, 129], 32, 8, 128, 16, 600,
+                   softcap=25.0)
+    check(case, f"{splits} blocks", num_splits=splits)
+
+
+@pytest.mark.parametrize("kw", [dict(window=300), dict(kv_dtype="fp8_e4m3",
+                                                       scale_range=(0.5, 2.0))])
+def test_extend_parts_with_window_and_fp8(kw):
+    case = case_of([900, 40], [150, 300], 16, 4, 128, 16, 601, **kw)
+    check(case, f"parts {kw}", num_splits=13)
+
+
+def test_extend_parts_with_sinks():
+    case = I.with_extras(case_of([1200, 5], [100, 60], 32, 8, 128, 16, 602), 602,
+                         descales=True)
+    check(case, "parts with sinks", num_splits=9)
 
 
 def test_extend_single_row_is_decode():
