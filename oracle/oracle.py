@@ -28,17 +28,17 @@ def bind(path: str):
     L = ctypes.CDLL(path)
     p, i, i64, d = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
     L.orc_decode.argtypes = [i, i, i, i, i, i, p, p, p, i64, p, i64, p,
-                             d, d, i, d, d, i, p, p, i, p, p, p]
+                             d, d, i, d, d, i, p, p, i, p, p, p, p]
     L.orc_decode.restype = i
     L.orc_extend.argtypes = [i, i, i, i, i, i, p, p, p, p, p, p, p, i64, p,
-                             i64, d, d, i, d, d, p, i64, p, i, p, p, p]
+                             i64, d, d, i, d, d, p, i64, p, i, p, p, p, p]
     L.orc_extend.restype = i
     L.orc_bf16.argtypes = [ctypes.c_uint16]
     L.orc_bf16.restype = d
     L.orc_e4m3fn.argtypes = [ctypes.c_uint8]
     L.orc_e4m3fn.restype = d
     L.orc_verify.argtypes = [i, i, i, i, i, i, i, p, p, p, i64, p, i64, p, d, d, i, d, d, p, i,
-                             p, p, p]
+                             p, p, p, p]
     L.orc_verify.restype = i
     L.orc_e4m3fn_encode.argtypes = [ctypes.c_float]
     L.orc_e4m3fn_encode.restype = ctypes.c_uint8
@@ -70,12 +70,12 @@ def _c(a: np.ndarray) -> np.ndarray:
 
 
 def _extras(case):
-    """fp32 sinks [Hq] and per-request descales [B] of a case (None = off),
-    kept alive by the caller while the C call runs."""
+    """fp32 sinks [Hq], per-request descales [B] and ALiBi slopes [Hq] of a
+    case (None = off), kept alive by the caller while the C call runs."""
     def f32(name):
         a = getattr(case, name, None)
         return None if a is None else np.ascontiguousarray(a, dtype=np.float32)
-    return f32("sinks"), f32("k_descale"), f32("v_descale")
+    return f32("sinks"), f32("k_descale"), f32("v_descale"), f32("alibi_slopes")
 
 
 def decode(case, num_splits: int = 0, threads: Optional[int] = None, clib=None):
@@ -85,13 +85,13 @@ def decode(case, num_splits: int = 0, threads: Optional[int] = None, clib=None):
     lse = np.zeros((B, Hq), dtype=np.float64)
     q, kp, vp = _c(case.q), _c(case.kv.k_pool), _c(case.kv.v_pool)
     bt, sl = _c(case.kv.block_table), _c(case.seq_lens)
-    sk, kd, vd = _extras(case)
+    sk, kd, vd, al = _extras(case)
     rc = (clib or lib()).orc_decode(B, Hq, case.num_kv_heads, D, case.page_size,
                           _KV[case.kv_dtype], _ptr(q), _ptr(kp), _ptr(vp),
                           kp.shape[0], _ptr(bt), bt.shape[1], _ptr(sl),
                           case.scale, case.softcap, case.window, case.k_scale,
                           case.v_scale, num_splits, _ptr(out), _ptr(lse),
-                          threads or default_threads(), _ptr(sk), _ptr(kd), _ptr(vd))
+                          threads or default_threads(), _ptr(sk), _ptr(kd), _ptr(vd), _ptr(al))
     if rc != 0:
         raise RuntimeError(f"orc_decode failed: {rc}")
     return out, lse
@@ -107,14 +107,14 @@ def extend(case, rows: Optional[np.ndarray] = None,
     cu, ctx = _c(case.cu_seqlens_q), _c(case.ctx_lens)
     kp, vp, bt = _c(case.kv.k_pool), _c(case.kv.v_pool), _c(case.kv.block_table)
     r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
-    sk, kd, vd = _extras(case)
+    sk, kd, vd, al = _extras(case)
     rc = (clib or lib()).orc_extend(case.batch, Hq, case.num_kv_heads, D, case.kv.page_size,
                           _KV[case.kv_dtype], _ptr(q), _ptr(kn), _ptr(vn),
                           _ptr(cu), _ptr(ctx), _ptr(kp), _ptr(vp), kp.shape[0],
                           _ptr(bt), bt.shape[1], case.scale, case.softcap,
                           case.window, case.k_scale, case.v_scale, _ptr(r),
                           0 if r is None else r.shape[0], _ptr(out),
-                          threads or default_threads(), _ptr(sk), _ptr(kd), _ptr(vd))
+                          threads or default_threads(), _ptr(sk), _ptr(kd), _ptr(vd), _ptr(al))
     if rc != 0:
         raise RuntimeError(f"orc_extend failed: {rc}")
     return out
@@ -129,13 +129,13 @@ def verify(case, q: np.ndarray, threads: Optional[int] = None, clib=None) -> np.
     qb = _c(q)
     kp, vp, bt = _c(case.kv.k_pool), _c(case.kv.v_pool), _c(case.kv.block_table)
     sl = _c(case.seq_lens)
-    sk, kd, vd = _extras(case)
+    sk, kd, vd, al = _extras(case)
     rc = (clib or lib()).orc_verify(B, Hq, case.num_kv_heads, D, case.kv.page_size,
                                     _KV[case.kv_dtype], ql, _ptr(qb), _ptr(kp), _ptr(vp),
                                     kp.shape[0], _ptr(bt), bt.shape[1], _ptr(sl), case.scale,
                                     case.softcap, case.window, case.k_scale, case.v_scale,
                                     _ptr(out), threads or default_threads(), _ptr(sk),
-                                    _ptr(kd), _ptr(vd))
+                                    _ptr(kd), _ptr(vd), _ptr(al))
     if rc != 0:
         raise RuntimeError(f"orc_verify failed: {rc}")
     return out
@@ -200,8 +200,10 @@ def _softmax_rows(scores: np.ndarray) -> np.ndarray:
 
 
 def _no_extras(case):
-    if any(getattr(case, n, None) is not None for n in ("sinks", "k_descale", "v_descale")):
-        raise ValueError("the brute-force formulation takes no sinks or per-request descales")
+    if any(getattr(case, n, None) is not None
+           for n in ("sinks", "k_descale", "v_descale", "alibi_slopes")):
+        raise ValueError("the brute-force formulation takes no sinks, per-request descales "
+                         "or ALiBi")
 
 
 def brute_decode(case) -> np.ndarray:

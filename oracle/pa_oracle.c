@@ -69,6 +69,14 @@
  *             out = sum_s exp(lse_s - M) o_s / (exp(sink - M) + sum_s exp(lse_s - M)).
  *           A row with no key is still a zero row.
  *
+ *  alibi    Optional per-query-head fp32 slopes a[h] (`_fwd_kernel_alibi` on
+ *           the prefix_prefill page, whose `Alibi_slopes` is indexed by the
+ *           query head): a key at position j seen from a query at position p
+ *           gets the bias a[h] * (j - p) added to its scaled (and capped)
+ *           score.  Keys after the query are masked as without ALiBi (that
+ *           page's `alibi <= 0` test is this causal limit for the positive
+ *           slopes ALiBi uses); the window rule is unchanged.
+ *
  *  descales Optional per-request fp32 descales kd[b], vd[b] (the b12x
  *           `_prepare_fp8_descales` gives one value per request): a cached
  *           key of sequence b is dec(K) * k_scale * kd[b], a cached value
@@ -150,6 +158,7 @@ typedef struct {
     const int32_t *seq_lens;    /* decode: cached tokens incl. the query token */
     double scale, softcap, k_scale, v_scale;
     const float *sinks;         /* [Hq] or NULL */
+    const float *alibi;         /* [Hq] ALiBi slopes or NULL */
     const float *k_desc, *v_desc; /* [B] per-request descales or NULL */
     int window;
     int num_splits;             /* decode: 0 = one pass over the key range */
@@ -209,6 +218,12 @@ static double sink_of(const orc_problem *pr, int h)
     return pr->sinks ? (double)pr->sinks[h] : -INFINITY;
 }
 
+/* The ALiBi bias of a key at position j for query head h at position pos. */
+static double alibi_bias(const orc_problem *pr, int h, int64_t j, int64_t pos)
+{
+    return pr->alibi ? (double)pr->alibi[h] * (double)(j - pos) : 0.0;
+}
+
 /* Gather keys [t0, t1) of (b, g) from the cache: scores against q, and values. */
 static void gather_cached(const orc_problem *pr, int b, int g, const double *q,
                           int64_t t0, int64_t t1, double *s, double *v)
@@ -252,7 +267,10 @@ static void decode_row(const orc_problem *pr, int b, int h, double *q,
         q[d] = orc_bf16(pr->q[((int64_t)b * pr->Hq + h) * D + d]);
 
     if (pr->num_splits <= 0) {
+        int64_t t;
         gather_cached(pr, b, g, q, lo, L, s, v);
+        for (t = lo; t < L; ++t)
+            s[t - lo] += alibi_bias(pr, h, t, L - 1);
         softmax_sum(s, v, L - lo, D, sink_of(pr, h), out, lse);
         return;
     }
@@ -271,6 +289,11 @@ static void decode_row(const orc_problem *pr, int b, int h, double *q,
                 continue;
             }
             gather_cached(pr, b, g, q, a, e, s, v);
+            {
+                int64_t t;
+                for (t = a; t < e; ++t)
+                    s[t - a] += alibi_bias(pr, h, t, L - 1);
+            }
             softmax_sum(s, v, e - a, D, -INFINITY, os + (int64_t)sp * D, &lses[sp]);
             if (lses[sp] > M)
                 M = lses[sp];
@@ -324,6 +347,11 @@ static void verify_row(const orc_problem *pr, int64_t it, double *q, double *s, 
     for (d = 0; d < D; ++d)
         q[d] = orc_bf16(pr->q[(bi * Hq + h) * D + d]);
     gather_cached(pr, b, h / (Hq / pr->Hkv), q, lo, L, s, v);
+    {
+        int64_t t;
+        for (t = lo; t < L; ++t)
+            s[t - lo] += alibi_bias(pr, h, t, L - 1);     /* query at L - 1 */
+    }
     softmax_sum(s, v, L - lo, D, sink_of(pr, h), out, &lse);
 }
 
@@ -353,6 +381,7 @@ static void extend_row(const orc_problem *pr, int64_t r, int h, double *q,
         if (pr->window > 0 && pos - j >= pr->window)
             continue;
         gather_cached(pr, b, g, q, j, j + 1, s + n, v + n * D);
+        s[n] += alibi_bias(pr, h, j, pos);
         ++n;
     }
     /* new keys C + i' for i' <= i, contiguous rows */
@@ -365,7 +394,7 @@ static void extend_row(const orc_problem *pr, int64_t r, int h, double *q,
             dot += q[d] * orc_bf16(pr->k_new[(row * pr->Hkv + g) * D + d]);
             v[n * D + d] = orc_bf16(pr->v_new[(row * pr->Hkv + g) * D + d]);
         }
-        s[n] = cap_score(pr->scale * dot, pr->softcap);
+        s[n] = cap_score(pr->scale * dot, pr->softcap) + alibi_bias(pr, h, C + j, pos);
         ++n;
     }
     softmax_sum(s, v, n, D, sink_of(pr, h), pr->out + (r * pr->Hq + h) * D, &lse);
@@ -469,8 +498,8 @@ static int check_common(int B, int Hq, int Hkv, int D, int P, int kv_dtype)
  * Decode oracle.  out [B][Hq][D] and lse [B][Hq] (natural log) are written.
  * num_splits == 0 evaluates the definition in one pass over the key range;
  * num_splits > 0 evaluates the split partition and the log-sum-exp merge.
- * sinks [Hq] and the per-request descales k_desc/v_desc [B] are optional
- * (NULL: none / 1).  Returns 0, -1 on a bad argument, -2 when memory runs out.
+ * sinks [Hq], the per-request descales k_desc/v_desc [B] and the ALiBi
+ * slopes alibi [Hq] are optional (NULL: none / 1 / none).  Returns 0, -1 on a bad argument, -2 when memory runs out.
  */
 int orc_decode(int B, int Hq, int Hkv, int D, int P, int kv_dtype,
                const uint16_t *q, const void *k_pool, const void *v_pool,
@@ -478,7 +507,8 @@ int orc_decode(int B, int Hq, int Hkv, int D, int P, int kv_dtype,
                int64_t bt_stride, const int32_t *seq_lens, double scale,
                double softcap, int window, double k_scale, double v_scale,
                int num_splits, double *out, double *lse, int threads,
-               const float *sinks, const float *k_desc, const float *v_desc)
+               const float *sinks, const float *k_desc, const float *v_desc,
+               const float *alibi)
 {
     orc_problem pr;
     int64_t max_keys = 0;
@@ -493,7 +523,7 @@ int orc_decode(int B, int Hq, int Hkv, int D, int P, int kv_dtype,
     pr.bt = block_table; pr.bt_stride = bt_stride; pr.seq_lens = seq_lens;
     pr.scale = scale; pr.softcap = softcap; pr.window = window;
     pr.k_scale = k_scale; pr.v_scale = v_scale;
-    pr.sinks = sinks; pr.k_desc = k_desc; pr.v_desc = v_desc;
+    pr.sinks = sinks; pr.k_desc = k_desc; pr.v_desc = v_desc; pr.alibi = alibi;
     pr.num_splits = num_splits;
     pr.out = out; pr.lse = lse;
     for (b = 0; b < B; ++b) {
@@ -509,7 +539,7 @@ int orc_decode(int B, int Hq, int Hkv, int D, int P, int kv_dtype,
  * Extend oracle.  Computes output rows for the token indices listed in
  * `rows` (n_rows of them), or for every token when rows == NULL
  * (n_rows = total_q).  out is [total_q][Hq][D]; only listed rows are written.
- * sinks, k_desc, v_desc as for orc_decode.
+ * sinks, k_desc, v_desc, alibi as for orc_decode.
  */
 int orc_extend(int B, int Hq, int Hkv, int D, int P, int kv_dtype,
                const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
@@ -518,7 +548,8 @@ int orc_extend(int B, int Hq, int Hkv, int D, int P, int kv_dtype,
                const int32_t *block_table, int64_t bt_stride, double scale,
                double softcap, int window, double k_scale, double v_scale,
                const int64_t *rows, int64_t n_rows, double *out, int threads,
-               const float *sinks, const float *k_desc, const float *v_desc)
+               const float *sinks, const float *k_desc, const float *v_desc,
+               const float *alibi)
 {
     orc_problem pr;
     int64_t max_keys = 0;
@@ -534,7 +565,7 @@ int orc_extend(int B, int Hq, int Hkv, int D, int P, int kv_dtype,
     pr.bt = block_table; pr.bt_stride = bt_stride;
     pr.scale = scale; pr.softcap = softcap; pr.window = window;
     pr.k_scale = k_scale; pr.v_scale = v_scale;
-    pr.sinks = sinks; pr.k_desc = k_desc; pr.v_desc = v_desc;
+    pr.sinks = sinks; pr.k_desc = k_desc; pr.v_desc = v_desc; pr.alibi = alibi;
     pr.rows = rows; pr.n_rows = n_rows;
     pr.out = out;
     for (b = 0; b < B; ++b) {
@@ -614,15 +645,16 @@ int orc_cache_append(int64_t num_tokens, int Hkv, int D, int P, int kv_dtype,
 
 /*
  * Verify oracle: q [B][q_len][Hq][D] (bf16), seq_lens counting the q_len
- * query tokens themselves; out [B][q_len][Hq][D].  sinks, k_desc, v_desc as
- * for orc_decode.
+ * query tokens themselves; out [B][q_len][Hq][D].  sinks, k_desc, v_desc,
+ * alibi as for orc_decode.
  */
 int orc_verify(int B, int Hq, int Hkv, int D, int P, int kv_dtype, int q_len,
                const uint16_t *q, const void *k_pool, const void *v_pool,
                int64_t num_pages, const int32_t *block_table, int64_t bt_stride,
                const int32_t *seq_lens, double scale, double softcap, int window,
                double k_scale, double v_scale, double *out, int threads,
-               const float *sinks, const float *k_desc, const float *v_desc)
+               const float *sinks, const float *k_desc, const float *v_desc,
+               const float *alibi)
 {
     orc_problem pr;
     int64_t max_keys = 0;
@@ -637,7 +669,7 @@ int orc_verify(int B, int Hq, int Hkv, int D, int P, int kv_dtype, int q_len,
     pr.bt = block_table; pr.bt_stride = bt_stride; pr.seq_lens = seq_lens;
     pr.scale = scale; pr.softcap = softcap; pr.window = window;
     pr.k_scale = k_scale; pr.v_scale = v_scale;
-    pr.sinks = sinks; pr.k_desc = k_desc; pr.v_desc = v_desc;
+    pr.sinks = sinks; pr.k_desc = k_desc; pr.v_desc = v_desc; pr.alibi = alibi;
     pr.q_len = q_len;
     pr.out = out;
     for (b = 0; b < B; ++b) {

@@ -159,6 +159,7 @@ class DecodeCase:
     sinks: Optional[np.ndarray] = None      # float32 [Hq] sink logits (None: off)
     k_descale: Optional[np.ndarray] = None  # float32 [B] per-request descales (None: 1)
     v_descale: Optional[np.ndarray] = None
+    alibi_slopes: Optional[np.ndarray] = None   # float32 [Hq] ALiBi slopes (None: off)
 
     @property
     def batch(self) -> int:
@@ -305,6 +306,7 @@ class ExtendCase:
     sinks: Optional[np.ndarray] = None      # float32 [Hq] sink logits (None: off)
     k_descale: Optional[np.ndarray] = None  # float32 [B] per-request cache descales
     v_descale: Optional[np.ndarray] = None
+    alibi_slopes: Optional[np.ndarray] = None   # float32 [Hq] ALiBi slopes (None: off)
 
     @property
     def batch(self) -> int:
@@ -404,24 +406,40 @@ def kv_torch_dtype(kv_dtype: str) -> torch.dtype:
     return torch.bfloat16 if kv_dtype == "bf16" else torch.float8_e4m3fn
 
 
+def alibi_slopes(num_heads: int) -> np.ndarray:
+    """The ALiBi head slopes: for n heads (n a power of two) the geometric
+    sequence 2^(-8/n), 2^(-16/n), ..., 2^(-8); for other n the slopes of the
+    next lower power of two m, then every other slope of 2m."""
+    def pow2(n):
+        return [2.0 ** (-8.0 * (i + 1) / n) for i in range(n)]
+    m = 1 << (num_heads.bit_length() - 1)
+    s = pow2(m)
+    if m < num_heads:
+        s += pow2(2 * m)[0::2][: num_heads - m]
+    return np.asarray(s, dtype=np.float32)
+
+
 def with_extras(case, seed: int, sinks: bool = True, descales: bool = False,
-                sink_range: tuple[float, float] = (0.0, 8.0),
+                alibi: bool = False, sink_range: tuple[float, float] = (0.0, 8.0),
                 descale_range: tuple[float, float] = (0.5, 2.0)):
     """Give a decode or extend case seeded sink logits ~ U(sink_range) per
     query head and/or per-request descales ~ U(descale_range), drawn from
-    default_rng(seed) in that order (sinks, k descales, v descales)."""
+    default_rng(seed) in that order (sinks, k descales, v descales), and/or
+    the ALiBi slopes of its query heads."""
     rng = np.random.default_rng(seed)
     if sinks:
         case.sinks = rng.uniform(*sink_range, size=case.num_q_heads).astype(np.float32)
     if descales:
         case.k_descale = rng.uniform(*descale_range, size=case.batch).astype(np.float32)
         case.v_descale = rng.uniform(*descale_range, size=case.batch).astype(np.float32)
+    if alibi:
+        case.alibi_slopes = alibi_slopes(case.num_q_heads)
     return case
 
 
 def _extra_tensors(case, device) -> dict:
     out = {}
-    for name in ("sinks", "k_descale", "v_descale"):
+    for name in ("sinks", "k_descale", "v_descale", "alibi_slopes"):
         a = getattr(case, name, None)
         out[name] = None if a is None else _dev(np.asarray(a, dtype=np.float32), device)
     return out

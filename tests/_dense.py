@@ -18,24 +18,39 @@ def dense_tokens(kv, b, L, kv_dtype):
     return k, v
 
 
-def _sdpa(q, k, v, scale, mask=None, sinks=None):
+def _sdpa(q, k, v, scale, mask=None, sinks=None, bias=None):
     """q [H, n, D], k/v [H, m, D] float64 -> [H, n, D].  `mask` is a boolean
-    keep-mask [n, m].  `sinks` [H] adds, per head, one more key whose value
-    row is zero and whose score is the sink logit: a zero key (score 0)
+    keep-mask [n, m]; `bias` [H, n, m] is added to the scaled scores (as
+    torch's float attn_mask).  `sinks` [H] adds, per head, one more key whose
+    value row is zero and whose score is the sink logit: a zero key (score 0)
     with the sink as an additive mask term."""
-    if sinks is not None:
+    if sinks is not None or bias is not None:
         H, n, D = q.shape
         m = k.shape[1]
-        k = np.concatenate([k, np.zeros((H, 1, D))], axis=1)
-        v = np.concatenate([v, np.zeros((H, 1, D))], axis=1)
-        bias = np.zeros((H, n, m + 1))
+        extra = 1 if sinks is not None else 0
+        if extra:
+            k = np.concatenate([k, np.zeros((H, 1, D))], axis=1)
+            v = np.concatenate([v, np.zeros((H, 1, D))], axis=1)
+        fm = np.zeros((H, n, m + extra))
+        if bias is not None:
+            fm[:, :, :m] = bias
         if mask is not None:
-            bias[:, :, :m] = np.where(mask.numpy(), 0.0, -np.inf)[None]
-        bias[:, :, m] = np.asarray(sinks, dtype=np.float64)[:, None]
-        mask = torch.from_numpy(bias)
+            fm[:, :, :m] = np.where(mask.numpy()[None], fm[:, :, :m], -np.inf)
+        if extra:
+            fm[:, :, m] = np.asarray(sinks, dtype=np.float64)[:, None]
+        mask = torch.from_numpy(fm)
     return F.scaled_dot_product_attention(
         torch.from_numpy(q)[None], torch.from_numpy(k)[None],
         torch.from_numpy(v)[None], attn_mask=mask, scale=scale)[0].numpy()
+
+
+def _alibi(case, qpos, kpos):
+    """ALiBi biases slope[h] * (key position - query position), [H, n, m]
+    (None without slopes)."""
+    if getattr(case, "alibi_slopes", None) is None:
+        return None
+    sl = np.asarray(case.alibi_slopes, dtype=np.float64)[:, None, None]
+    return sl * (kpos - qpos).astype(np.float64)[None]
 
 
 def _scales(case, b):
@@ -62,7 +77,8 @@ def sdpa_decode(case):
         v = np.repeat(v[lo:] * vs, G, axis=1).transpose(1, 0, 2)
         q = bits_to_float(case.q[b], "bf16").astype(np.float64)[:, None, :]
         out[b] = _sdpa(q, np.ascontiguousarray(k), np.ascontiguousarray(v),
-                       case.scale, sinks=case.sinks)[:, 0, :]
+                       case.scale, sinks=case.sinks,
+                       bias=_alibi(case, np.array([[L - 1]]), np.arange(lo, L)[None, :]))[:, 0, :]
     return out
 
 
@@ -93,7 +109,8 @@ def sdpa_extend(case):
             keep &= (qpos - kpos) < case.window
         q = bits_to_float(case.q[a:e], "bf16").astype(np.float64).transpose(1, 0, 2)
         out[a:e] = _sdpa(np.ascontiguousarray(q), k, v, case.scale,
-                         torch.from_numpy(keep), sinks=case.sinks).transpose(1, 0, 2)
+                         torch.from_numpy(keep), sinks=case.sinks,
+                         bias=_alibi(case, qpos, kpos)).transpose(1, 0, 2)
     return out
 
 
@@ -117,5 +134,6 @@ def sdpa_verify(case, q_bits):
             keep &= (qpos - kpos) < case.window
         q = bits_to_float(q_bits[b], "bf16").astype(np.float64).transpose(1, 0, 2)
         out[b] = _sdpa(np.ascontiguousarray(q), k, v, case.scale,
-                       torch.from_numpy(keep), sinks=case.sinks).transpose(1, 0, 2)
+                       torch.from_numpy(keep), sinks=case.sinks,
+                       bias=_alibi(case, qpos, kpos)).transpose(1, 0, 2)
     return out

@@ -547,3 +547,62 @@ def test_per_request_descales_are_per_sequence_scales(oracle_mod):
         case.v_scale = base_v * float(vd[b])
         ref, _ = oracle_mod.decode(case)
         np.testing.assert_array_equal(got[b], ref[b])
+
+
+# ------------------------------------------------------------------- ALiBi
+def test_alibi_slopes_published_sequence(oracle_mod):
+    """The ALiBi slopes of 8 heads are 2^-1 .. 2^-8; 12 heads take the 8
+    then every other one of 16."""
+    np.testing.assert_array_equal(I.alibi_slopes(8), 2.0 ** -np.arange(1, 9))
+    s16 = 2.0 ** (-0.5 * np.arange(1, 17))
+    np.testing.assert_allclose(I.alibi_slopes(12), np.concatenate([2.0 ** -np.arange(1, 9),
+                                                                  s16[0::2][:4]]), rtol=1e-7)
+
+
+def test_alibi_zero_slopes_change_nothing(oracle_mod):
+    case = rand_decode([1, 40, 300], 8, 2, 64, 16, 70, window=100)
+    ref, lse = oracle_mod.decode(case)
+    case.alibi_slopes = np.zeros(8, dtype=np.float32)
+    got, lse2 = oracle_mod.decode(case)
+    np.testing.assert_array_equal(got, ref)
+    np.testing.assert_array_equal(lse2, lse)
+
+
+@pytest.mark.parametrize("window", [0, 60])
+def test_decode_alibi_equals_sdpa_with_bias(oracle_mod, window):
+    case = I.with_extras(rand_decode([1, 9, 130, 700], 16, 4, 64, 16, 71, window=window),
+                         71, sinks=True, alibi=True)
+    close(oracle_mod.decode(case)[0], sdpa_decode(case))
+    a, _ = oracle_mod.decode(case)
+    b, _ = oracle_mod.decode(case, num_splits=7)
+    close(a, b)
+
+
+@pytest.mark.parametrize("window", [0, 40])
+def test_extend_alibi_equals_masked_sdpa_with_bias(oracle_mod, window):
+    case = I.with_extras(I.make_extend("al", [0, 33, 100], [5, 17, 40], 12, 3, 64, 16, 72,
+                                       window=window), 72, sinks=False, alibi=True)
+    close(oracle_mod.extend(case), sdpa_extend(case))
+
+
+def test_verify_alibi_equals_masked_sdpa_with_bias(oracle_mod):
+    case, q = _verify_case([2, 40, 130], 8, 2, 64, 16, 4, 73)
+    I.with_extras(case, 73, sinks=False, alibi=True)
+    close(oracle_mod.verify(case, q), sdpa_verify(case, q))
+
+
+def test_alibi_two_keys_closed_form(oracle_mod):
+    """Two keys with scores s0, s1 one position apart: the later key's weight
+    is sigmoid(s1 - s0 + slope)."""
+    rng = np.random.default_rng(74)
+    q = I.bf16_bits(rng.standard_normal((1, 2, 64)).astype(np.float32))
+    k, v = _tokens(1, 64, 2, rng), _tokens(1, 64, 2, rng)
+    case = I.decode_case_from_tokens("two-alibi", q, k, v, [2], 16, 9)
+    case.alibi_slopes = np.array([0.5, 3.0], dtype=np.float32)
+    out, _ = oracle_mod.decode(case)
+    kf, vf = I.bits_to_float(k).astype(np.float64), I.bits_to_float(v).astype(np.float64)
+    for h in range(2):
+        qf = I.bits_to_float(q[0, h]).astype(np.float64)
+        s0, s1 = case.scale * (qf @ kf[0, 0]), case.scale * (qf @ kf[1, 0])
+        w1 = 1.0 / (1.0 + math.exp(-(s1 - s0 + float(case.alibi_slopes[h]))))
+        close(out[0, h], (1 - w1) * vf[0, 0] + w1 * vf[1, 0])

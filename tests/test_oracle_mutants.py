@@ -64,6 +64,13 @@ MUTANTS = [
      "(pr->k_desc ? (double)pr->k_desc[0] : 1.0)"),
     ("v-descale-from-k", "(pr->v_desc ? (double)pr->v_desc[b] : 1.0)",
      "(pr->v_desc ? (double)pr->k_desc[b] : 1.0)"),
+    ("alibi-sign", "(double)pr->alibi[h] * (double)(j - pos)",
+     "(double)pr->alibi[h] * (double)(pos - j)"),
+    ("alibi-kv-head", "(double)pr->alibi[h] * (double)(j - pos)",
+     "(double)pr->alibi[h % pr->Hkv] * (double)(j - pos)"),
+    ("alibi-decode-pos", "s[t - lo] += alibi_bias(pr, h, t, L - 1);\n        softmax_sum",
+     "s[t - lo] += alibi_bias(pr, h, t, L);\n        softmax_sum"),
+    ("alibi-new-key-pos", "+ alibi_bias(pr, h, C + j, pos);", "+ alibi_bias(pr, h, j, pos);"),
 ]
 
 
