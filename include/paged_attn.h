@@ -89,7 +89,7 @@ typedef enum { PA_MODE_DECODE = 0, PA_MODE_EXTEND = 1, PA_MODE_VERIFY = 2 } pa_m
 /*
  * Optional inputs of a compute call (the `attention_sink_bias`, `k_descale`
  * and `v_descale` that the vLLM "b12x" backend page hands to its kernel's
- * `bind`).  Pass NULL for none, or leave members NULL.  Device pointers,
+ * `bind`, and ALiBi slopes).  Pass NULL for none, or leave members NULL.  Device pointers,
  * 4-byte aligned; contents are read by the kernels and not checked.
  *
  *   sinks         fp32 [Hq]: one logit per query head that joins the softmax
@@ -101,6 +101,11 @@ typedef enum { PA_MODE_DECODE = 0, PA_MODE_EXTEND = 1, PA_MODE_VERIFY = 2 } pa_m
  *   v_descale     of request b is dec(K) * k_scale * k_descale[b'] (values
  *                 alike), b' = b when num_descales > 1, else 0.  New extend
  *                 rows are not cache elements and take no descale.
+ *   alibi_slopes  fp32 [Hq]: ALiBi slope a[h] of each query head (the
+ *                 `Alibi_slopes` of `_fwd_kernel_alibi` on the prefix_prefill
+ *                 page): a key at position j seen from a query at position p
+ *                 gets a[h] * (j - p) added to its scaled (and capped) score;
+ *                 causal limit, window and sinks apply as without it.
  *   num_descales  entries behind k_descale/v_descale: 1 (shared by every
  *                 request) or >= B; anything else is PA_ERR_INVALID_SHAPE
  *                 (the b12x `_prepare_fp8_descales` expands a single value,
@@ -110,6 +115,7 @@ typedef struct {
     const float* sinks;
     const float* k_descale;
     const float* v_descale;
+    const float* alibi_slopes;
     int32_t num_descales;
     int32_t reserved;
 } pa_extras;

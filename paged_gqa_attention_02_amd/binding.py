@@ -23,8 +23,8 @@ PA_KV = {"bf16": 0, "fp8_e4m3": 1}
 
 class PaExtras(ctypes.Structure):
     _fields_ = [("sinks", ctypes.c_void_p), ("k_descale", ctypes.c_void_p),
-                ("v_descale", ctypes.c_void_p), ("num_descales", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("v_descale", ctypes.c_void_p), ("alibi_slopes", ctypes.c_void_p),
+                ("num_descales", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class PaProblem(ctypes.Structure):
@@ -152,21 +152,22 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _extras(sinks, k_descale, v_descale):
+def _extras(sinks, k_descale, v_descale, alibi_slopes=None):
     """pa_extras for optional fp32 device tensors (None when all are None):
-    sinks [Hq]; k_descale/v_descale with 1 or >= B entries."""
-    if sinks is None and k_descale is None and v_descale is None:
+    sinks [Hq]; k_descale/v_descale with 1 or >= B entries; alibi_slopes [Hq]."""
+    if sinks is None and k_descale is None and v_descale is None and alibi_slopes is None:
         return None
-    for name, t in (("sinks", sinks), ("k_descale", k_descale), ("v_descale", v_descale)):
+    for name, t in (("sinks", sinks), ("k_descale", k_descale), ("v_descale", v_descale),
+                    ("alibi_slopes", alibi_slopes)):
         if t is not None and (t.dtype != torch.float32 or t.dim() != 1 or
                               not t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous fp32 vector")
     n = [t.numel() for t in (k_descale, v_descale) if t is not None]
     if len(n) == 2 and n[0] != n[1]:
         raise ValueError("k_descale and v_descale must have the same length")
-    ex = PaExtras(None if sinks is None else sinks.data_ptr(),
-                  None if k_descale is None else k_descale.data_ptr(),
-                  None if v_descale is None else v_descale.data_ptr(), n[0] if n else 0, 0)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    ex = PaExtras(ptr(sinks), ptr(k_descale), ptr(v_descale), ptr(alibi_slopes),
+                  n[0] if n else 0, 0)
     return ctypes.byref(ex)
 
 
@@ -219,33 +220,33 @@ def decode(pl: Plan, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor
            softcap: float = 0.0, window: int = 0, k_scale: float = 1.0,
            v_scale: float = 1.0, out: Optional[torch.Tensor] = None,
            workspace: Optional[torch.Tensor] = None, stream=None, sinks=None,
-           k_descale=None, v_descale=None) -> torch.Tensor:
+           k_descale=None, v_descale=None, alibi_slopes=None) -> torch.Tensor:
     """paged_attn_decode: q bf16 [B, Hq, D] -> out bf16 [B, Hq, D].
     A workspace passed in needs plan.workspace_bytes bytes.  sinks: fp32 [Hq]
     sink logits; k_descale/v_descale: fp32 per-request descales (1 or >= B)."""
     return _decode("paged_attn_decode", pl, q, k_pool, v_pool, block_table, seq_lens, scale,
                    softcap, window, k_scale, v_scale, out, workspace, stream,
-                   sinks, k_descale, v_descale)
+                   sinks, k_descale, v_descale, alibi_slopes)
 
 
 def decode_split(pl: Plan, q, k_pool, v_pool, block_table, seq_lens, scale, softcap=0.0,
                  window=0, k_scale=1.0, v_scale=1.0, out=None, workspace=None, stream=None,
-                 sinks=None, k_descale=None, v_descale=None):
+                 sinks=None, k_descale=None, v_descale=None, alibi_slopes=None):
     """paged_attn_decode_split: the split pass alone (writes the segments one
     block covers whole to `out`, the others to the workspace)."""
     return _decode("paged_attn_decode_split", pl, q, k_pool, v_pool, block_table, seq_lens,
                    scale, softcap, window, k_scale, v_scale, out, workspace, stream,
-                   sinks, k_descale, v_descale)
+                   sinks, k_descale, v_descale, alibi_slopes)
 
 
 def decode_merge(pl: Plan, q, k_pool, v_pool, block_table, seq_lens, scale, softcap=0.0,
                  window=0, k_scale=1.0, v_scale=1.0, out=None, workspace=None, stream=None,
-                 sinks=None, k_descale=None, v_descale=None):
+                 sinks=None, k_descale=None, v_descale=None, alibi_slopes=None):
     """paged_attn_decode_merge: the merge pass alone, over the workspace the
     split pass left."""
     return _decode("paged_attn_decode_merge", pl, q, k_pool, v_pool, block_table, seq_lens,
                    scale, softcap, window, k_scale, v_scale, out, workspace, stream,
-                   sinks, k_descale, v_descale)
+                   sinks, k_descale, v_descale, alibi_slopes)
 
 
 def verify_plan(q: torch.Tensor, k_pool: torch.Tensor, block_table: torch.Tensor,
@@ -262,12 +263,12 @@ def verify(pl: Plan, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor
            softcap: float = 0.0, window: int = 0, k_scale: float = 1.0,
            v_scale: float = 1.0, out: Optional[torch.Tensor] = None,
            workspace: Optional[torch.Tensor] = None, stream=None, sinks=None,
-           k_descale=None, v_descale=None) -> torch.Tensor:
+           k_descale=None, v_descale=None, alibi_slopes=None) -> torch.Tensor:
     """paged_attn_verify: q bf16 [B, q_len, Hq, D] -> out bf16 [B, q_len, Hq, D];
     seq_lens count the q_len query tokens, which are already in the cache."""
     return _decode("paged_attn_verify", pl, q, k_pool, v_pool, block_table, seq_lens, scale,
                    softcap, window, k_scale, v_scale, out, workspace, stream,
-                   sinks, k_descale, v_descale)
+                   sinks, k_descale, v_descale, alibi_slopes)
 
 
 def _rows_contiguous(t: torch.Tensor) -> bool:
@@ -284,7 +285,7 @@ def _rows_contiguous(t: torch.Tensor) -> bool:
 
 def _decode(fn, pl, q, k_pool, v_pool, block_table, seq_lens, scale, softcap, window,
             k_scale, v_scale, out, workspace, stream, sinks=None, k_descale=None,
-            v_descale=None):
+            v_descale=None, alibi_slopes=None):
     if fn not in ("paged_attn_decode", "paged_attn_verify") and (
             out is None or (workspace is None and pl.workspace_bytes > 0)):
         raise ValueError(f"{fn}: the passes share `out` and the workspace; pass both")
@@ -308,7 +309,7 @@ def _decode(fn, pl, q, k_pool, v_pool, block_table, seq_lens, scale, softcap, wi
         k_pool.shape[0], _ptr(block_table), block_table.stride(0), _ptr(seq_lens),
         k_pool.shape[1], float(scale), float(softcap), int(window), float(k_scale),
         float(v_scale), _ptr(out), out.stride(0), _ptr(workspace), wbytes,
-        _extras(sinks, k_descale, v_descale), _stream(stream)))
+        _extras(sinks, k_descale, v_descale, alibi_slopes), _stream(stream)))
     return out
 
 
@@ -328,9 +329,10 @@ def extend(pl: Plan, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
            softcap: float = 0.0, window: int = 0, k_scale: float = 1.0,
            v_scale: float = 1.0, out: Optional[torch.Tensor] = None,
            workspace: Optional[torch.Tensor] = None, stream=None, sinks=None,
-           k_descale=None, v_descale=None) -> torch.Tensor:
+           k_descale=None, v_descale=None, alibi_slopes=None) -> torch.Tensor:
     """paged_attn_extend: q bf16 [total_q, Hq, D] -> out bf16 [total_q, Hq, D].
-    sinks / k_descale / v_descale as for decode (descales: cached context only)."""
+    sinks / k_descale / v_descale / alibi_slopes as for decode (descales: cached
+    context only)."""
     for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new)):
         if t.dtype != torch.bfloat16 or not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous bf16")
@@ -349,7 +351,8 @@ def extend(pl: Plan, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
         _ptr(ctx_lens), _ptr(k_pool), _ptr(v_pool), sp, st, sh, k_pool.shape[0],
         _ptr(block_table), block_table.stride(0), k_pool.shape[1], float(scale),
         float(softcap), int(window), float(k_scale), float(v_scale), _ptr(out),
-        _ptr(workspace), wbytes, _extras(sinks, k_descale, v_descale), _stream(stream)))
+        _ptr(workspace), wbytes, _extras(sinks, k_descale, v_descale, alibi_slopes),
+        _stream(stream)))
     return out
 
 

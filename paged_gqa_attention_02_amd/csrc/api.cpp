@@ -97,6 +97,7 @@ int elem_bytes(int kv_dtype) { return kv_dtype == PA_KV_FP8_E4M3 ? 1 : 2; }
 // Optional sinks and per-request descales (NULL extras: none).
 struct Extras {
     const float* sinks = nullptr;
+    const float* alibi = nullptr;
     const float* k_desc = nullptr;
     const float* v_desc = nullptr;
     int32_t per_seq = 0;
@@ -108,7 +109,8 @@ pa_status read_extras(const pa_extras* ex, int32_t num_seqs, Extras* out) {
     const auto aligned4 = [](const void* ptr) {
         return (reinterpret_cast<uintptr_t>(ptr) & 3u) == 0;
     };
-    if (!aligned4(ex->sinks) || !aligned4(ex->k_descale) || !aligned4(ex->v_descale))
+    if (!aligned4(ex->sinks) || !aligned4(ex->k_descale) || !aligned4(ex->v_descale) ||
+        !aligned4(ex->alibi_slopes))
         return PA_ERR_MISALIGNED;
     if (ex->k_descale || ex->v_descale) {
         // one value for every request, or one per request (b12x
@@ -119,6 +121,7 @@ pa_status read_extras(const pa_extras* ex, int32_t num_seqs, Extras* out) {
         out->per_seq = ex->num_descales > 1;
     }
     out->sinks = ex->sinks;
+    out->alibi = ex->alibi_slopes;
     out->k_desc = ex->k_descale;
     out->v_desc = ex->v_descale;
     return PA_OK;
@@ -359,6 +362,7 @@ pa_status decode_impl(int passes, int mode, const pa_plan* plan, const void* q, 
     }
     p.v_scale = v_scale;
     p.sinks = ex.sinks;
+    p.alibi = ex.alibi;
     p.k_desc = ex.k_desc;
     p.v_desc = ex.v_desc;
     p.desc_per_seq = ex.per_seq;
@@ -551,6 +555,7 @@ pa_status paged_attn_extend(const pa_plan* plan, const void* q, const void* k_ne
         p.part_o = reinterpret_cast<float*>(ws + L.o);
     }
     p.sinks = ex.sinks;
+    p.alibi = ex.alibi;
     p.k_desc = ex.k_desc;
     p.v_desc = ex.v_desc;
     p.desc_per_seq = ex.per_seq;

@@ -116,6 +116,7 @@ struct TileCtx {
     int first_page, last_idx, t_begin, t_end, c, grp;
     int lim, wlo;              // this lane's column: keys t with wlo <= t <= lim (verify)
     float qk2, c1;             // the segment's score scale (or soft-cap factor), log2 units
+    float al2;                 // this lane's column: ALiBi slope, log2 units per position
     int full_lo, full_hi;      // tiles inside [full_lo, full_hi) are valid for every column
     int64_t page_bytes;        // s_page * elem
     int tok_bytes;             // s_tok * elem
@@ -258,7 +259,10 @@ struct Acc {
 
 // Scores -> probabilities (log2 domain), running max/sum, O rescale.
 // Returns the P operand (bf16) of P*V.
-template <int D, bool CAP>
+// Score modes of the split pass (template flags).
+enum SplitScore { kScoreCap = 1, kScoreAlibi = 2 };
+
+template <int D, int SCORE>
 __device__ __forceinline__ u32x4 tile_softmax(Acc<D>& A, const f32x4 s[2],
                                               const DecodeParams& p, const TileCtx& x, int t0,
                                               bool full) {
@@ -267,13 +271,19 @@ __device__ __forceinline__ u32x4 tile_softmax(Acc<D>& A, const f32x4 s[2],
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         float v = (j < 4) ? s[0][j] : s[1][j - 4];
-        if constexpr (CAP) {
+        if constexpr ((SCORE & kScoreCap) != 0) {
             // c*tanh(y/c) = c - 2c / (exp(2y/c) + 1), times log2(e)
             v = p.cap_c2 - 2.f * p.cap_c2 * fast_rcp(fast_exp2(v * x.c1) + 1.f);
         } else {
             v *= x.qk2;
         }
         sc[j] = v;
+    }
+    if constexpr ((SCORE & kScoreAlibi) != 0) {
+        // ALiBi: slope * (key - query position), the query sitting at lim
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            sc[j] += x.al2 * (float)(t0 + tile_token(x.grp, j) - x.lim);
     }
     if (!full) {
 #pragma unroll
@@ -355,7 +365,7 @@ __device__ __forceinline__ void tile_pv(Acc<D>& A, VRegs<D, FP8>& R, u32x4 pop,
 // ---------------------------------------------------------------------------
 // Split pass: persistent waves, one contiguous range of tiles each
 // ---------------------------------------------------------------------------
-template <int D, bool FP8, bool UNIFORM, bool CAP, int NW>
+template <int D, bool FP8, bool UNIFORM, int SCORE, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(kDecodeOccupancy)))
 void decode_split_kernel(DecodeParams p) {
     constexpr int KK = D / 32;                  // QK MFMAs per 16-token half
@@ -465,6 +475,7 @@ void decode_split_kernel(DecodeParams p) {
         // causal limit and window start of this lane's column (query token
         // cg / G at position L - q_len + cg / G); for decode these never bind
         x.lim = sr.L - p.q_len + (cg < p.rows ? cg / G : 0);
+        x.al2 = p.alibi ? p.alibi[kvh * G + (cg < p.rows ? cg : 0) % G] * kLog2e : 0.f;
         x.wlo = p.window > 0 ? x.lim - p.window + 1 : INT_MIN;
 
         // ---- the piece's tiles, chunk by chunk (page list staged in LDS) ----
@@ -505,7 +516,7 @@ void decode_split_kernel(DecodeParams p) {
                     issue_k_rows<D, FP8, UNIFORM, NW == 1>(kr, p, x, tile_t0(i + 1));
                     f32x4 s[2];
                     tile_scores_lds<D, FP8>(s, sm_k, qop, c, grp);
-                    const u32x4 pop = tile_softmax<D, CAP>(acc, s, p, x, t0, full);
+                    const u32x4 pop = tile_softmax<D, SCORE>(acc, s, p, x, t0, full);
                     tile_pv<D, FP8>(acc, vr, pop, x, t0, full);
                     __syncthreads();
                     issue_v<D, FP8, UNIFORM, NW == 1>(vr, p, x, tile_t0(i + 1));
@@ -516,7 +527,7 @@ void decode_split_kernel(DecodeParams p) {
                 __syncthreads();
                 f32x4 s[2];
                 tile_scores_lds<D, FP8>(s, sm_k, qop, c, grp);
-                const u32x4 pop = tile_softmax<D, CAP>(acc, s, p, x, t0, full);
+                const u32x4 pop = tile_softmax<D, SCORE>(acc, s, p, x, t0, full);
                 tile_pv<D, FP8>(acc, vr, pop, x, t0, full);
                 __syncthreads();
             }
@@ -581,31 +592,40 @@ void decode_split_kernel(DecodeParams p) {
 
 using SplitFn = void (*)(DecodeParams);
 
-template <int D, bool FP8, bool UNIFORM, bool CAP>
+template <int D, bool FP8, bool UNIFORM, int SCORE>
 SplitFn split_by_waves(int nw) {
     switch (nw) {
-        case 1: return decode_split_kernel<D, FP8, UNIFORM, CAP, 1>;
-        case 2: return decode_split_kernel<D, FP8, UNIFORM, CAP, 2>;
-        case 3: return decode_split_kernel<D, FP8, UNIFORM, CAP, 3>;
-        case 4: return decode_split_kernel<D, FP8, UNIFORM, CAP, 4>;
+        case 1: return decode_split_kernel<D, FP8, UNIFORM, SCORE, 1>;
+        case 2: return decode_split_kernel<D, FP8, UNIFORM, SCORE, 2>;
+        case 3: return decode_split_kernel<D, FP8, UNIFORM, SCORE, 3>;
+        case 4: return decode_split_kernel<D, FP8, UNIFORM, SCORE, 4>;
         default: return nullptr;
     }
 }
 
-template <int D, bool FP8>
-SplitFn split_by_pages(bool uniform, bool cap, int nw) {
-    if (uniform) return cap ? split_by_waves<D, FP8, true, true>(nw)
-                            : split_by_waves<D, FP8, true, false>(nw);
-    return cap ? split_by_waves<D, FP8, false, true>(nw) : split_by_waves<D, FP8, false, false>(nw);
+template <int D, bool FP8, bool UNIFORM>
+SplitFn split_by_score(int score, int nw) {
+    switch (score) {
+        case 0: return split_by_waves<D, FP8, UNIFORM, 0>(nw);
+        case kScoreCap: return split_by_waves<D, FP8, UNIFORM, kScoreCap>(nw);
+        case kScoreAlibi: return split_by_waves<D, FP8, UNIFORM, kScoreAlibi>(nw);
+        default: return split_by_waves<D, FP8, UNIFORM, kScoreCap | kScoreAlibi>(nw);
+    }
 }
 
-SplitFn split_kernel(int head_dim, bool fp8, bool uniform, bool cap, int nw) {
+template <int D, bool FP8>
+SplitFn split_by_pages(bool uniform, int score, int nw) {
+    return uniform ? split_by_score<D, FP8, true>(score, nw)
+                   : split_by_score<D, FP8, false>(score, nw);
+}
+
+SplitFn split_kernel(int head_dim, bool fp8, bool uniform, int score, int nw) {
     if (head_dim == 128)
-        return fp8 ? split_by_pages<128, true>(uniform, cap, nw)
-                   : split_by_pages<128, false>(uniform, cap, nw);
+        return fp8 ? split_by_pages<128, true>(uniform, score, nw)
+                   : split_by_pages<128, false>(uniform, score, nw);
     if (head_dim == 64)
-        return fp8 ? split_by_pages<64, true>(uniform, cap, nw)
-                   : split_by_pages<64, false>(uniform, cap, nw);
+        return fp8 ? split_by_pages<64, true>(uniform, score, nw)
+                   : split_by_pages<64, false>(uniform, score, nw);
     return nullptr;
 }
 
@@ -613,7 +633,8 @@ SplitFn split_kernel(int head_dim, bool fp8, bool uniform, bool cap, int nw) {
 
 hipError_t launch_decode(const DecodeParams& p, int head_dim, bool fp8, bool uniform_pages,
                          int waves_per_block, int workers, hipStream_t stream) {
-    const SplitFn f = split_kernel(head_dim, fp8, uniform_pages, p.has_cap != 0, waves_per_block);
+    const int score = (p.has_cap ? kScoreCap : 0) | (p.alibi ? kScoreAlibi : 0);
+    const SplitFn f = split_kernel(head_dim, fp8, uniform_pages, score, waves_per_block);
     if (!f) return hipErrorInvalidValue;
     hipLaunchKernelGGL(f, dim3(workers), dim3(64 * waves_per_block), 0, stream, p);
     return hipGetLastError();
@@ -621,7 +642,7 @@ hipError_t launch_decode(const DecodeParams& p, int head_dim, bool fp8, bool uni
 
 hipError_t decode_blocks_per_cu(int head_dim, bool fp8, bool uniform_pages, int waves_per_block,
                                 int* out) {
-    const SplitFn f = split_kernel(head_dim, fp8, uniform_pages, false, waves_per_block);
+    const SplitFn f = split_kernel(head_dim, fp8, uniform_pages, 0, waves_per_block);
     if (!f) return hipErrorInvalidValue;
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, reinterpret_cast<const void*>(f),
                                                         64 * waves_per_block, 0);

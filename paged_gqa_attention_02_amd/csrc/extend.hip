@@ -66,6 +66,7 @@ enum ScoreMode {
                   // exp2(s*scale - m) (a positive scale commutes with the max)
     kScale = 1,   // no cap, any scale: s*scale per score
     kCap = 2,     // soft-cap c*tanh(s*scale/c), per score
+    kAlibi = 4,   // flag on kScale / kCap: plus slope * (key - query position)
 };
 
 // Key position (0..31) inside a 32-key step for MFMA contraction slot
@@ -327,9 +328,13 @@ __device__ __forceinline__ float logit(float v, const ExtendParams& p, bool ctx,
 template <int D, int MODE, bool MASK, bool SPLIT>
 __device__ __forceinline__ void tile_softmax(f32x4 (&s)[kRB][4], u32x4 (&pop)[kRB][2],
                                              ExtAcc<D>& A, const ExtendParams& p,
-                                             const SeqInfo& si, const int (&pos_q)[kRB], int jt) {
+                                             const SeqInfo& si, const int (&pos_q)[kRB],
+                                             const float (&al2)[kRB], int jt) {
     constexpr int kVE = D / 16;
-    constexpr bool kFolded = MODE == kFold && !SPLIT;
+    constexpr int kBase = MODE & 3;
+    constexpr bool kAl = (MODE & kAlibi) != 0;
+    constexpr bool kFolded = kBase == kFold && !SPLIT;
+    static_assert(!(kAl && kBase == kFold), "ALiBi takes the per-score path");
     const int grp = (threadIdx.x & 63) >> 4;
     const bool all_ctx = jt + kExtKeys <= si.C;
     const float qs = all_ctx ? p.qk_scale2_ctx : p.qk_scale2;
@@ -346,7 +351,8 @@ __device__ __forceinline__ void tile_softmax(f32x4 (&s)[kRB][4], u32x4 (&pop)[kR
                 const int key = key0 + 16 * kb + j;
                 float v = s[rb][kb][j];
                 if constexpr (!kFolded)
-                    v = logit<MODE == kFold ? kScale : MODE, SPLIT>(v, p, key < si.C, qs, c1);
+                    v = logit<kBase == kFold ? kScale : kBase, SPLIT>(v, p, key < si.C, qs, c1);
+                if constexpr (kAl) v += al2[rb] * (float)(key - pos_q[rb]);
                 if constexpr (MASK) {
                     const bool keep = key <= pos_q[rb] &&
                                       (p.window <= 0 || pos_q[rb] - key < p.window);
@@ -410,8 +416,8 @@ __device__ __forceinline__ void tile_compute(const uint8_t* kl, const uint8_t* v
                                              const LaneOffs<D>& lo,
                                              const u32x4 (&qop)[kRB][D / 32], ExtAcc<D>& A,
                                              const ExtendParams& p, const SeqInfo& si,
-                                             const int (&pos_q)[kRB], int pos_first,
-                                             int pos_last, int jt) {
+                                             const int (&pos_q)[kRB], const float (&al2)[kRB],
+                                             int jt) {
     constexpr int kPitch = Tile<D>::kPitch;
     constexpr int kDS = D / 32;
     constexpr int kVE = D / 16;
@@ -433,10 +439,8 @@ __device__ __forceinline__ void tile_compute(const uint8_t* kl, const uint8_t* v
     }
 
     // ---- scale / cap, mask, online softmax; P^T operands ----
-    (void)pos_first;
-    (void)pos_last;
     u32x4 pop[kRB][2];
-    tile_softmax<D, MODE, !FAST, !FAST>(s, pop, A, p, si, pos_q, jt);
+    tile_softmax<D, MODE, !FAST, !FAST>(s, pop, A, p, si, pos_q, al2, jt);
 
     // ---- O^T += V^T P^T: lane c supplies d = kVE*c + e of MFMA e.  V rows
     // are read in 8-byte quarters of 4 elements (D = 128: d 8c..8c+3, then
@@ -579,6 +583,7 @@ __device__ __forceinline__ void extend_piece(const ExtendParams& pk, const Item&
     // ---- rows of this lane's column blocks, and Q^T as B operands ----
     int row_t[kRB], pos_q[kRB];
     bool row_ok[kRB];
+    float al2[kRB];                    // ALiBi slope of the row's head, log2 units
     u32x4 qop[kRB][kDS];
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
@@ -586,6 +591,7 @@ __device__ __forceinline__ void extend_piece(const ExtendParams& pk, const Item&
         row_t[rb] = t0 + r / G;
         row_ok[rb] = row_t[rb] < t1;
         pos_q[rb] = si.C + row_t[rb];
+        al2[rb] = p.alibi ? p.alibi[si.kvh * G + r % G] * kLog2e : 0.f;
         const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
                                ((int64_t)(si.q0 + (row_ok[rb] ? row_t[rb] : t0)) * p.num_q_heads +
                                 si.kvh * G + r % G) * D;
@@ -665,7 +671,7 @@ __device__ __forceinline__ void extend_piece(const ExtendParams& pk, const Item&
                 if (i + 1 < to) stage(jt + kExtKeys, (i & 1) ? L.k0 : L.k1,
                                       (i & 1) ? L.v0 : L.v1);
                 tile_compute<D, MODE, decltype(fast)::value>(kc, vc, lo, qop, A, p, si, pos_q,
-                                                             pos_first, pos_last, jt);
+                                                             al2, jt);
                 wait_vm0();
                 __syncthreads();
             }
@@ -696,8 +702,7 @@ __device__ __forceinline__ void extend_piece(const ExtendParams& pk, const Item&
                 if (more) load(jt + kExtKeys);
                 tile_compute<D, MODE, decltype(fast)::value>((i & 1) ? L.k1 : L.k0,
                                                              (i & 1) ? L.v1 : L.v0, lo, qop,
-                                                             A, p, si, pos_q, pos_first,
-                                                             pos_last, jt);
+                                                             A, p, si, pos_q, al2, jt);
                 if (more) store((i & 1) ? L.k0 : L.k1, (i & 1) ? L.v0 : L.v1);
                 __syncthreads();
             }
@@ -894,9 +899,15 @@ __global__ __launch_bounds__(kExtMergeThreads) void extend_merge_kernel(ExtendPa
 
 template <int D, bool FP8>
 const void* extend_kernel_ptr(int mode) {
-    if (mode == kCap) return reinterpret_cast<const void*>(&extend_kernel<D, FP8, kCap>);
-    if (mode == kFold) return reinterpret_cast<const void*>(&extend_kernel<D, FP8, kFold>);
-    return reinterpret_cast<const void*>(&extend_kernel<D, FP8, kScale>);
+    switch (mode) {
+        case kCap: return reinterpret_cast<const void*>(&extend_kernel<D, FP8, kCap>);
+        case kFold: return reinterpret_cast<const void*>(&extend_kernel<D, FP8, kFold>);
+        case kScale | kAlibi:
+            return reinterpret_cast<const void*>(&extend_kernel<D, FP8, kScale | kAlibi>);
+        case kCap | kAlibi:
+            return reinterpret_cast<const void*>(&extend_kernel<D, FP8, kCap | kAlibi>);
+        default: return reinterpret_cast<const void*>(&extend_kernel<D, FP8, kScale>);
+    }
 }
 
 const void* extend_kernel_for(int head_dim, bool fp8, int mode) {
@@ -911,7 +922,8 @@ int extend_rows_per_block() { return kExtRows; }
 
 hipError_t launch_extend(const ExtendParams& p, int head_dim, bool fp8, int workers,
                          hipStream_t stream) {
-    const int mode = p.has_cap ? kCap
+    const int mode = p.has_cap ? (p.alibi ? kCap | kAlibi : kCap)
+                     : p.alibi ? kScale | kAlibi
                      : (p.qk_scale2 > 0.f && p.qk_scale2_ctx > 0.f) ? kFold : kScale;
     hipLaunchKernelGGL(extend_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, p);
     const void* f = extend_kernel_for(head_dim, fp8, mode);

@@ -44,6 +44,7 @@ struct DecodeParams {
     float cap_c2;             // c * log2(e)                         (cap)
     float v_scale;
     const float* sinks;       // [Hq] sink logits (natural-log units) or null
+    const float* alibi;       // [Hq] ALiBi slopes (natural-log units per position) or null
     const float* k_desc;      // per-request cache descales or null; request b
     const float* v_desc;      //   uses entry desc_per_seq ? b : 0
     int32_t desc_per_seq;
@@ -89,6 +90,7 @@ struct ExtendParams {
     float cap_c1, cap_c1_ctx, cap_c2;
     float v_scale;            // applied to the cached-value part of the sum
     const float* sinks;       // [Hq] sink logits (natural-log units) or null
+    const float* alibi;       // [Hq] ALiBi slopes or null
     const float* k_desc;      // per-request cache descales or null (as decode)
     const float* v_desc;
     int32_t desc_per_seq;

@@ -12,7 +12,7 @@ ATOL = RTOL = 1e-2      # |err| <= 1e-2 + 1e-2*|ref| for bf16/fp8-KV outputs
 
 def extras(t: dict) -> dict:
     """The optional sink / descale tensors of a case's device tensors."""
-    return {k: t.get(k) for k in ("sinks", "k_descale", "v_descale")}
+    return {k: t.get(k) for k in ("sinks", "k_descale", "v_descale", "alibi_slopes")}
 
 
 def run_decode(case, num_splits=None, tensors=None, pool_view=None):

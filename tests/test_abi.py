@@ -150,13 +150,14 @@ def decode_status(plan_kw=None, fn="paged_attn_decode", **kw):
     (dict(ws_bytes=100), WS),
     (dict(scale=float("nan")), SHAPE),
     (dict(softcap=float("inf")), SHAPE),
-    # extras (sinks, k_descale, v_descale, num_descales, reserved): B = 4
-    (dict(extras=(A + 2, None, None, 0, 0)), MISAL),
-    (dict(extras=(None, A, A + 1, 4, 0)), MISAL),
-    (dict(extras=(None, A, A, 0, 0)), SHAPE),
-    (dict(extras=(None, A, None, 2, 0)), SHAPE),
-    (dict(extras=(None, None, A, 3, 0)), SHAPE),
-    (dict(extras=(A, A, A, 4, 0), ws_bytes=100), WS),   # accepted, then the workspace
+    # extras (sinks, k_descale, v_descale, alibi_slopes, num_descales, reserved): B = 4
+    (dict(extras=(A + 2, None, None, None, 0, 0)), MISAL),
+    (dict(extras=(None, A, A + 1, None, 4, 0)), MISAL),
+    (dict(extras=(None, A, A, None, 0, 0)), SHAPE),
+    (dict(extras=(None, A, None, None, 2, 0)), SHAPE),
+    (dict(extras=(None, None, None, A + 2, 0, 0)), MISAL),
+    (dict(extras=(None, None, A, None, 3, 0)), SHAPE),
+    (dict(extras=(A, A, A, None, 4, 0), ws_bytes=100), WS),   # accepted, then the workspace
 ])
 @pytest.mark.parametrize("fn", DECODE_FNS)
 def test_decode_validation(fn, kw, status):
@@ -244,9 +245,9 @@ def extend_status(**kw):
     (dict(page_size=32), MISMATCH),
     (dict(window=4), MISMATCH),
     (dict(ks=float("inf")), SHAPE),
-    (dict(extras=(A + 1, None, None, 0, 0)), MISAL),
-    (dict(extras=(None, A, A, 3, 0)), SHAPE),
-    (dict(extras=(None, A, A, -1, 0)), SHAPE),
+    (dict(extras=(A + 1, None, None, None, 0, 0)), MISAL),
+    (dict(extras=(None, A, A, None, 3, 0)), SHAPE),
+    (dict(extras=(None, A, A, None, -1, 0)), SHAPE),
     (dict(ws_bytes=100), WS),
     (dict(ws=None), NULLP),
     (dict(ws=A + 8), MISAL),

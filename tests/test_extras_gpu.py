@@ -103,3 +103,40 @@ def test_extend_sinks_descales(kw):
     say(f"[extras] extend {kw}")
     out, _ = run_extend(case)
     assert_close(to_f64(out), oracle.extend(case), f"extend sinks {kw}")
+
+
+# ------------------------------------------------------------------- ALiBi
+@pytest.mark.parametrize("lens,Hq,Hkv,D,P,splits,kw", [
+    ([1, 2, 33, 100, 1000], 8, 2, 128, 16, None, {}),
+    ([5, 700, 3000], 32, 8, 128, 16, 40, dict(softcap=30.0)),
+    ([64, 900, 1500], 16, 16, 64, 8, None, dict(window=300)),
+    ([900, 1, 64, 4000], 64, 8, 128, 16, 40,
+     dict(kv_dtype="fp8_e4m3", scale_range=(0.5, 2.0))),
+])
+def test_decode_alibi(lens, Hq, Hkv, D, P, splits, kw):
+    case = I.with_extras(I.make_decode("al", lens, Hq, Hkv, D, P, 560,
+                                       lens_rng=np.random.default_rng(560), **kw),
+                         561, sinks=False, alibi=True)
+    say(f"[extras] decode alibi lens={lens} Hq={Hq} D={D} splits={splits} {kw}")
+    out, pl = run_decode(case, splits)
+    assert_close(to_f64(out), oracle.decode(case)[0], f"decode alibi ({pl.describe()})")
+
+
+def test_verify_alibi_with_sinks():
+    case = I.with_extras(I.make_decode("alv", [3, 300, 1800], 32, 8, 128, 16, 562,
+                                       lens_rng=np.random.default_rng(562)), 563, alibi=True)
+    q = I.bf16_bits(np.random.default_rng(564).standard_normal((3, 6, 32, 128),
+                                                               dtype=np.float32))
+    out, pl = run_verify(case, q, 25)
+    assert_close(to_f64(out), oracle.verify(case, q), f"verify alibi ({pl.describe()})")
+
+
+@pytest.mark.parametrize("kw,splits", [({}, 0), (dict(softcap=25.0), 11),
+                                       (dict(window=200), 0),
+                                       (dict(kv_dtype="fp8_e4m3", scale_range=(0.5, 2.0)), 7)])
+def test_extend_alibi(kw, splits):
+    case = I.with_extras(I.make_extend("xa", [0, 70, 1000], [3, 130, 260], 32, 8, 128, 16,
+                                       565, **kw), 566, sinks=False, alibi=True)
+    say(f"[extras] extend alibi {kw} splits={splits}")
+    out, _ = run_extend(case, num_splits=splits)
+    assert_close(to_f64(out), oracle.extend(case), f"extend alibi {kw}")
