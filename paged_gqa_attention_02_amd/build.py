@@ -7,6 +7,7 @@ Every kernel is compiled with packed-fp32 VALU instructions disabled.
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -24,19 +25,36 @@ def flags():
             "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
 
 
-def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC] + flags() + ["-shared", "-o", tmp] + srcs + ["-ldl"]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _run(cmd):
     res = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in res.stderr.splitlines()
                     if "packed-fp32-ops" not in l and l.strip())
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if err and verbose:
-        print(err, file=sys.stderr)
+    return res.returncode, err
+
+
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    """Compile every source to an object in parallel (one hipcc each), then
+    link the shared library; the library is replaced only when all succeed."""
+    srcs = [os.path.join(CSRC, s) for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, os.path.basename(s) + ".o") for s in srcs]
+    cmds = [[HIPCC] + flags() + ["-c", "-o", o, s] for s, o in zip(srcs, objs)]
+    jobs = jobs or min(len(cmds), os.cpu_count() or 1, 8)
+    if verbose:
+        for c in cmds:
+            print(" ".join(c), flush=True)
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        results = list(ex.map(_run, cmds))
+    for (rc, err), s in zip(results, srcs):
+        if rc != 0:
+            raise RuntimeError(f"hipcc failed on {os.path.basename(s)} ({rc}):\n{err}")
+        if err and verbose:
+            print(err, file=sys.stderr)
+    tmp = LIB + ".tmp"
+    rc, err = _run([HIPCC] + flags() + ["-shared", "-o", tmp] + objs + ["-ldl"])
+    if rc != 0:
+        raise RuntimeError(f"hipcc link failed ({rc}):\n{err}")
     os.replace(tmp, LIB)
     return LIB
 
