@@ -190,6 +190,59 @@ __device__ __forceinline__ void stage_k(const KRowRegs<D, FP8>& R, uint8_t* lds,
             R.w[i];
 }
 
+// Blocks of NW > 1 waves share each tile: wave wv loads the row groups
+// i = wv, wv + NW, ... (kRowsPerLoad rows each) of K and of V and stages them
+// into the block's K and V tiles in LDS; every wave then reads its operands
+// from those tiles.
+template <int D, bool FP8, int NW>
+struct SharedRows {
+    using KR = KRowRegs<D, FP8>;
+    static constexpr int M = (KR::N + NW - 1) / NW;        // row groups per wave
+    u32x4 k[M], v[M];
+};
+
+template <int D, bool FP8, bool UNIFORM, int NW>
+__device__ __forceinline__ void issue_shared(SharedRows<D, FP8, NW>& R, const DecodeParams& p,
+                                             const TileCtx& x, int t0, int wv) {
+    using KR = KRowRegs<D, FP8>;
+    const uint8_t* kpool = static_cast<const uint8_t*>(p.k_pool);
+    const uint8_t* vpool = static_cast<const uint8_t*>(p.v_pool);
+    const int pmask = (1 << p.page_shift) - 1;
+#pragma unroll
+    for (int m = 0; m < SharedRows<D, FP8, NW>::M; ++m) {
+        const int i = wv + NW * m;
+        if (i >= KR::N) break;                              // (uniform per wave)
+        const int row0 = KR::kRowsPerLoad * i;
+        int64_t off;
+        if constexpr (UNIFORM) {
+            const int th = t0 + (row0 & 16);
+            off = page_of<true>(x, p.page_shift, th) * x.page_bytes +
+                  (int64_t)(((th & pmask) + (row0 & 15)) * x.tok_bytes) + x.k_row_lane;
+        } else {
+            const int t = t0 + row0 + x.k_row;
+            off = page_of<false>(x, p.page_shift, t) * x.page_bytes +
+                  (int64_t)((t & pmask) * x.tok_bytes + x.k_row_lane);
+        }
+        R.k[m] = load_stream<u32x4, true>(kpool + off);
+        R.v[m] = load_stream<u32x4, true>(vpool + off);
+    }
+}
+
+template <int D, bool FP8, int NW>
+__device__ __forceinline__ void stage_shared(const SharedRows<D, FP8, NW>& R, uint8_t* kl,
+                                             uint8_t* vl, int lane, int wv) {
+    using KR = KRowRegs<D, FP8>;
+    const int row = lane / KR::kLanesPerRow, col = lane % KR::kLanesPerRow;
+#pragma unroll
+    for (int m = 0; m < SharedRows<D, FP8, NW>::M; ++m) {
+        const int i = wv + NW * m;
+        if (i >= KR::N) break;
+        const int o = (KR::kRowsPerLoad * i + row) * KR::kLdsStride + 16 * col;
+        *reinterpret_cast<u32x4*>(kl + o) = R.k[m];
+        *reinterpret_cast<u32x4*>(vl + o) = R.v[m];
+    }
+}
+
 // S^T = K Q^T with the K rows read back from the LDS tile in the A layout
 // (row 16h + c, the lane's slice as in issue_k).
 template <int D, bool FP8>
@@ -246,6 +299,18 @@ __device__ __forceinline__ void issue_v(VRegs<D, FP8>& R, const DecodeParams& p,
             R.w[i] = load_stream<Raw, NT>(ptr);
         }
     }
+}
+
+// V chunks of the lane's 8 tokens (as issue_v) read from the block's V tile.
+template <int D, bool FP8>
+__device__ __forceinline__ void read_v_lds(VRegs<D, FP8>& R, const uint8_t* vl, int c,
+                                           int grp) {
+    using Raw = typename VRow<D, FP8>::Raw;
+    using KR = KRowRegs<D, FP8>;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        R.w[i] = *reinterpret_cast<const Raw*>(vl + tile_token(grp, i) * KR::kLdsStride +
+                                               VRow<D, FP8>::kBytes * c);
 }
 
 // Online-softmax state of one wave: running max / partial sum of the head in
@@ -383,9 +448,11 @@ void decode_split_kernel(DecodeParams p) {
     const int64_t w = blockIdx.x;
 
     __shared__ int sm_pages[kMaxSplitPages];
+    // one wave: its own K tile; several: the block's shared K and V tiles
     __shared__ __attribute__((aligned(16)))
-    uint8_t sm_kw[NW][kTile * KRowRegs<D, FP8>::kLdsStride];
-    uint8_t* const sm_k = sm_kw[wv];            // the wave's own K tile
+    uint8_t sm_kv[NW == 1 ? 1 : 2][kTile * KRowRegs<D, FP8>::kLdsStride];
+    uint8_t* const sm_k = sm_kv[0];
+    uint8_t* const sm_v = sm_kv[NW == 1 ? 0 : 1];
 
     const int64_t N = total_tiles(p);
     const int64_t r0 = range_start(w, N, W);
@@ -502,7 +569,7 @@ void decode_split_kernel(DecodeParams p) {
             // soon as they are staged; V's registers take the next tile's V
             // once P*V is done.  The last tile is peeled off so the steady
             // loop issues its loads unconditionally (exact load counters).
-            {
+            if constexpr (NW == 1) {
                 KRowRegs<D, FP8> kr;
                 VRegs<D, FP8> vr;
                 auto tile_t0 = [&](int i) { return tile0 + min(i, ct - 1) * kTile; };
@@ -530,6 +597,25 @@ void decode_split_kernel(DecodeParams p) {
                 const u32x4 pop = tile_softmax<D, SCORE>(acc, s, p, x, t0, full);
                 tile_pv<D, FP8>(acc, vr, pop, x, t0, full);
                 __syncthreads();
+            } else {
+                // NW > 1: each wave loads and stages its share of K and V
+                SharedRows<D, FP8, NW> R;
+                auto tile_t0 = [&](int i) { return tile0 + min(i, ct - 1) * kTile; };
+                issue_shared<D, FP8, UNIFORM, NW>(R, p, x, tile_t0(0), wv);
+                for (int i = 0; i < ct; ++i) {
+                    const int t0 = tile_t0(i);
+                    const bool full = (t0 >= x.full_lo) && (t0 + kTile <= x.full_hi);
+                    stage_shared<D, FP8, NW>(R, sm_k, sm_v, lane, wv);
+                    __syncthreads();
+                    if (i + 1 < ct) issue_shared<D, FP8, UNIFORM, NW>(R, p, x, tile_t0(i + 1), wv);
+                    f32x4 s[2];
+                    tile_scores_lds<D, FP8>(s, sm_k, qop, c, grp);
+                    const u32x4 pop = tile_softmax<D, SCORE>(acc, s, p, x, t0, full);
+                    VRegs<D, FP8> vr;
+                    read_v_lds<D, FP8>(vr, sm_v, c, grp);
+                    tile_pv<D, FP8>(acc, vr, pop, x, t0, full);
+                    __syncthreads();
+                }
             }
         }
 
