@@ -91,6 +91,13 @@ struct Tile {
     static __device__ __forceinline__ int off(int row, int slot) {
         return row * kPitch + 16 * (slot ^ (row & (kSlots - 1)));
     }
+    // V tiles: slot s of row r is stored at slot s ^ vswz(r), so the four
+    // rows a 16-lane transposing read takes (4 consecutive keys, 32 bytes
+    // each) fall on four different 32-byte bank groups.
+    static __device__ __forceinline__ int vswz(int row) { return 2 * (row & 3); }
+    static __device__ __forceinline__ int voff(int row, int slot) {
+        return row * kPitch + 16 * (slot ^ vswz(row));
+    }
 };
 
 // Addresses of key j's K and V rows: context rows through the staged page list
@@ -131,12 +138,13 @@ __device__ __forceinline__ void stage_direct(const ExtendParams& p, const SeqInf
         const int row = run * kRowsPer + lane / TL::kSlots;
         const uint8_t *k, *v;
         key_rows<D, false>(p, si, jt + row, k, v);
-        const int chunk = 16 * (slot ^ (row & (TL::kSlots - 1)));
+        const int kchunk = 16 * (slot ^ (row & (TL::kSlots - 1)));
+        const int vchunk = 16 * (slot ^ TL::vswz(row));
         __builtin_amdgcn_global_load_lds(
-            (const void __attribute__((address_space(1)))*)(k + chunk),
+            (const void __attribute__((address_space(1)))*)(k + kchunk),
             (void __attribute__((address_space(3)))*)(kd + run * 1024), 16, 0, 0);
         __builtin_amdgcn_global_load_lds(
-            (const void __attribute__((address_space(1)))*)(v + chunk),
+            (const void __attribute__((address_space(1)))*)(v + vchunk),
             (void __attribute__((address_space(3)))*)(vd + run * 1024), 16, 0, 0);
     }
 }
@@ -150,16 +158,22 @@ __device__ __forceinline__ void stage_direct(const ExtendParams& p, const SeqInf
 // per-lane path above.
 template <int D>
 struct StageLane {
-    uint32_t ctx_off, new_off;
+    uint32_t ctx_off, new_off;       // K
+    uint32_t vctx_off, vnew_off;     // V (its own swizzle)
     __device__ __forceinline__ void init(const ExtendParams& p) {
         using TL = Tile<D>;
         constexpr int kRowsPer = 1024 / TL::kPitch;
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
         const int slot = lane % TL::kSlots;
         const int row = wave * kRowsPer + lane / TL::kSlots;   // its first run's row
-        const uint32_t chunk = 16 * (slot ^ (row & (TL::kSlots - 1)));
-        ctx_off = (uint32_t)(lane / TL::kSlots) * (uint32_t)(p.s_tok * 2) + chunk;
-        new_off = (uint32_t)(lane / TL::kSlots) * (uint32_t)(p.num_kv_heads * D * 2) + chunk;
+        const uint32_t kchunk = 16 * (slot ^ (row & (TL::kSlots - 1)));
+        const uint32_t vchunk = 16 * (slot ^ TL::vswz(row));
+        const uint32_t ctx_row = (uint32_t)(lane / TL::kSlots) * (uint32_t)(p.s_tok * 2);
+        const uint32_t new_row = (uint32_t)(lane / TL::kSlots) * (uint32_t)(p.num_kv_heads * D * 2);
+        ctx_off = ctx_row + kchunk;
+        new_off = new_row + kchunk;
+        vctx_off = ctx_row + vchunk;
+        vnew_off = new_row + vchunk;
     }
 };
 
@@ -185,7 +199,7 @@ __device__ __forceinline__ void stage_runs(const ExtendParams& p, const SeqInfo&
         const int run = wave + k * kExtWaves;
         const int j0 = jt + run * kRowsPer;                  // the run's first key
         const uint8_t *kb, *vb;
-        uint32_t off;
+        uint32_t off, voff;
         if (j0 + kRowsPer <= si.C) {
             const int64_t page = __builtin_amdgcn_readfirstlane(pg[k]);
             const int64_t o = (page * p.s_page + (int64_t)(j0 & pmask) * p.s_tok +
@@ -193,22 +207,25 @@ __device__ __forceinline__ void stage_runs(const ExtendParams& p, const SeqInfo&
             kb = static_cast<const uint8_t*>(p.k_pool) + o;
             vb = static_cast<const uint8_t*>(p.v_pool) + o;
             off = sl.ctx_off;
+            voff = sl.vctx_off;
         } else if (j0 >= si.C && j0 + kRowsPer <= si.C + si.n) {
             const int64_t o = ((int64_t)(si.q0 + j0 - si.C) * p.num_kv_heads + si.kvh) * D * 2;
             kb = static_cast<const uint8_t*>(p.k_new) + o;
             vb = static_cast<const uint8_t*>(p.v_new) + o;
             off = sl.new_off;
+            voff = sl.vnew_off;
         } else {
             const int lane = threadIdx.x & 63;
             const int row = run * kRowsPer + lane / TL::kSlots;
             key_rows<D, false>(p, si, jt + row, kb, vb);
             off = 16 * ((lane % TL::kSlots) ^ (row & (TL::kSlots - 1)));
+            voff = 16 * ((lane % TL::kSlots) ^ TL::vswz(row));
         }
         __builtin_amdgcn_global_load_lds(
             (const void __attribute__((address_space(1)))*)(kb + off),
             (void __attribute__((address_space(3)))*)(kd + run * 1024), 16, 0, 0);
         __builtin_amdgcn_global_load_lds(
-            (const void __attribute__((address_space(1)))*)(vb + off),
+            (const void __attribute__((address_space(1)))*)(vb + voff),
             (void __attribute__((address_space(3)))*)(vd + run * 1024), 16, 0, 0);
     }
 }
@@ -248,7 +265,7 @@ __device__ __forceinline__ void stage8_load(Stage8<D>& S, const ExtendParams& p,
     }
 }
 
-template <int D>
+template <int D, bool V>
 __device__ __forceinline__ void stage8_store(const Stage8<D>& S, uint8_t* lds) {
     using ST = Stage8<D>;
     using TL = Tile<D>;
@@ -264,8 +281,10 @@ __device__ __forceinline__ void stage8_store(const Stage8<D>& S, uint8_t* lds) {
             lo = u32x4{e0.x, e0.y, e1.x, e1.y};
             hi = u32x4{e2.x, e2.y, e3.x, e3.y};
         }
-        *reinterpret_cast<u32x4*>(lds + TL::off(row, 2 * chunk)) = lo;
-        *reinterpret_cast<u32x4*>(lds + TL::off(row, 2 * chunk + 1)) = hi;
+        const int o0 = V ? TL::voff(row, 2 * chunk) : TL::off(row, 2 * chunk);
+        const int o1 = V ? TL::voff(row, 2 * chunk + 1) : TL::off(row, 2 * chunk + 1);
+        *reinterpret_cast<u32x4*>(lds + o0) = lo;
+        *reinterpret_cast<u32x4*>(lds + o1) = hi;
     }
 }
 
@@ -281,33 +300,37 @@ struct ExtAcc {
     f32x4 o[kRB][kVE];
 };
 
-// Per-lane byte offsets of the operand reads inside a swizzled tile: K row
-// 16kb + c, slot 4ds + grp is at kb*16*pitch + koff[ds]; V row
-// 32ks + step_key(grp, jj), slot c, 8-byte half h is at ks*32*pitch +
-// (jj >= 4 ? 16*pitch : 0) + voff[h][jj & 3] (rows 16 apart share the swizzle).
+// Per-lane byte offsets of the operand reads inside a swizzled tile.
+//   K: row 16kb + c, slot 4ds + grp is at kb*16*pitch + koff[ds].
+//   V: transposing reads (ds_read_b64_tr_b16: within each 16 lanes, lane i
+//      receives element e from the 8 bytes lane 4e + i/4 read, element i % 4).
+//      Lane (grp, s = 4e + q) reads key row 32ks + 16h + 4grp + e, elements
+//      16*dblk + 4q .. +3, at ks*32*pitch + h*16*pitch + vtr[dblk]; lane i
+//      then holds d = 16*dblk + i of keys 32ks + 16h + 4grp + 0..3, the A
+//      operand of O^T += V^T P^T in the step_key order.
 template <int D>
 struct LaneOffs {
     int koff[D / 32];
-    int voff[D == 128 ? 2 : 1][4];   // [half][j]
+    int vtr[D / 16];
     __device__ __forceinline__ void init(int c, int grp) {
         using TL = Tile<D>;
 #pragma unroll
         for (int ds = 0; ds < D / 32; ++ds) koff[ds] = TL::off(c, 4 * ds + grp);
+        const int e = c >> 2, q = c & 3;
+        const int row = 4 * grp + e;                    // (+ 32ks + 16h: same swizzle)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if constexpr (D == 128) {
-                // lanes c >= 8 read the other 8-byte half first, so 16 lanes
-                // reading one row cover all banks once (their data then
-                // belongs to MFMA e ^ 4: see the finish)
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-                    voff[h][j] = TL::off(4 * grp + j, c) + 8 * (h ^ (c >> 3));
-            } else {
-                voff[0][j] = TL::off(4 * grp + j, c >> 1) + 8 * (c & 1);
-            }
-        }
+        for (int dblk = 0; dblk < D / 16; ++dblk)
+            vtr[dblk] = TL::voff(row, 2 * dblk + (q >> 1)) + 8 * (q & 1);
     }
 };
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* p) {
+    const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16*)(p));
+    return __builtin_bit_cast(u32x2, r);
+}
 
 // Logit (log2 domain) of a raw score for kScale / kCap.  SPLIT: the tile
 // holds context and new keys, whose scales differ.
@@ -442,30 +465,18 @@ __device__ __forceinline__ void tile_compute(const uint8_t* kl, const uint8_t* v
     u32x4 pop[kRB][2];
     tile_softmax<D, MODE, !FAST, !FAST>(s, pop, A, p, si, pos_q, al2, jt);
 
-    // ---- O^T += V^T P^T: lane c supplies d = kVE*c + e of MFMA e.  V rows
-    // are read in 8-byte quarters of 4 elements (D = 128: d 8c..8c+3, then
-    // 8c+4..8c+7; D = 64: d 4c..4c+3) ----
+    // ---- O^T += V^T P^T: MFMA dblk covers d = 16*dblk .. +15; its A operand
+    // (V^T rows d, keys in step_key order) comes from two transposing reads ----
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-        for (int half = 0; half < kVE / 4; ++half) {
-            u32x2 vr[8];
+        for (int dblk = 0; dblk < kVE; ++dblk) {
+            const u32x2 v0 = lds_read_tr16(vl + ks * 32 * kPitch + lo.vtr[dblk]);
+            const u32x2 v1 = lds_read_tr16(vl + ks * 32 * kPitch + 16 * kPitch + lo.vtr[dblk]);
+            const u32x4 a = {v0.x, v0.y, v1.x, v1.y};
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj)
-                vr[jj] = *reinterpret_cast<const u32x2*>(
-                    vl + ks * 32 * kPitch + (jj >= 4 ? 16 * kPitch : 0) + lo.voff[half][jj & 3]);
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-                const int w = e2 >> 1, e = 4 * half + e2;
-                const bool hi = e2 & 1;
-                const u32x4 a = {pick_halves(vr[0][w], vr[1][w], hi),
-                                 pick_halves(vr[2][w], vr[3][w], hi),
-                                 pick_halves(vr[4][w], vr[5][w], hi),
-                                 pick_halves(vr[6][w], vr[7][w], hi)};
-#pragma unroll
-                for (int rb = 0; rb < kRB; ++rb)
-                    A.o[rb][e] = mfma_bf16_16x16x32(a, pop[rb][ks], A.o[rb][e]);
-            }
+            for (int rb = 0; rb < kRB; ++rb)
+                A.o[rb][dblk] = mfma_bf16_16x16x32(a, pop[rb][ks], A.o[rb][dblk]);
         }
     }
 }
@@ -692,8 +703,8 @@ __device__ __forceinline__ void extend_piece(const ExtendParams& pk, const Item&
             stage8_load<D>(sv, p, si, jt, true);
         };
         auto store = [&](uint8_t* kd, uint8_t* vd) {
-            stage8_store<D>(sk, kd);
-            stage8_store<D>(sv, vd);
+            stage8_store<D, false>(sk, kd);
+            stage8_store<D, true>(sv, vd);
         };
         auto run = [&](int a, int e, auto fast) {
             for (int i = a; i < e; ++i) {
@@ -717,10 +728,8 @@ __device__ __forceinline__ void extend_piece(const ExtendParams& pk, const Item&
         run(cut[4], cut[5], std::false_type{});
     }
 
-    // ---- finish: O^T[d][row c] / l, d = kVE*(4grp + j) + (e ^ sw): for D = 128
-    // the O^T rows 8..15 (grp >= 2) hold their two 4-element halves swapped
-    // (see LaneOffs) ----
-    const int sw = (kVE == 8 && grp >= 2) ? 4 : 0;
+    // ---- finish: O^T[d][row c] / l; MFMA dblk, accumulator row 4grp + j
+    // holds d = 16*dblk + 4grp + j ----
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
         const float lt = col4_sum(A.l[rb]);
@@ -735,31 +744,18 @@ __device__ __forceinline__ void extend_piece(const ExtendParams& pk, const Item&
             if (p.sinks) den += fast_exp2(p.sinks[si.kvh * G + r % G] * kLog2e - A.m[rb]);
             const float inv = 1.f / den;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                uint32_t wv[kVE / 2];
-#pragma unroll
-                for (int e = 0; e < kVE; e += 2)
-                    wv[e / 2] = pack_bf16x2(A.o[rb][e][j] * inv, A.o[rb][e + 1][j] * inv);
-                uint16_t* dst = orow + kVE * (4 * grp + j);
-                if constexpr (kVE == 8) {
-                    *reinterpret_cast<u32x2*>(dst + sw) = u32x2{wv[0], wv[1]};
-                    *reinterpret_cast<u32x2*>(dst + (4 ^ sw)) = u32x2{wv[2], wv[3]};
-                } else {
-                    *reinterpret_cast<u32x2*>(dst) = u32x2{wv[0], wv[1]};
-                }
-            }
+            for (int dblk = 0; dblk < kVE; ++dblk)
+                *reinterpret_cast<u32x2*>(orow + 16 * dblk + 4 * grp) =
+                    u32x2{pack_bf16x2(A.o[rb][dblk][0] * inv, A.o[rb][dblk][1] * inv),
+                          pack_bf16x2(A.o[rb][dblk][2] * inv, A.o[rb][dblk][3] * inv)};
         } else {
             // a part: normalised rows and log2-sum-exp (no sink), for the merge
             const int64_t prow = ext_part_row(w, slot, r);
             const float inv = 1.f / lt;
             float* po = p.part_o + prow * D;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int e = 0; e < kVE; e += 4)
-                    *reinterpret_cast<f32x4*>(po + kVE * (4 * grp + j) + (e ^ sw)) =
-                        f32x4{A.o[rb][e][j] * inv, A.o[rb][e + 1][j] * inv,
-                              A.o[rb][e + 2][j] * inv, A.o[rb][e + 3][j] * inv};
+            for (int dblk = 0; dblk < kVE; ++dblk)
+                *reinterpret_cast<f32x4*>(po + 16 * dblk + 4 * grp) = A.o[rb][dblk] * inv;
             if (grp == 0) p.part_lse[prow] = A.m[rb] + __log2f(lt);
         }
     }
