@@ -27,7 +27,7 @@ def bind(path: str):
     """Load a build of pa_oracle.c and declare its C signatures."""
     L = ctypes.CDLL(path)
     p, i, i64, d = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
-    L.orc_decode.argtypes = [i, i, i, i, i, i, p, p, p, i64, p, i64, p,
+    L.orc_decode.argtypes = [i, i, i, i, i, i, i, p, p, p, i64, p, i64, p,
                              d, d, i, d, d, i, p, p, i, p, p, p, p]
     L.orc_decode.restype = i
     L.orc_extend.argtypes = [i, i, i, i, i, i, p, p, p, p, p, p, p, i64, p,
@@ -79,14 +79,16 @@ def _extras(case):
 
 
 def decode(case, num_splits: int = 0, threads: Optional[int] = None, clib=None):
-    """fp64 decode of a DecodeCase -> (out [B,Hq,D] float64, lse [B,Hq])."""
+    """fp64 decode of a DecodeCase -> (out [B,Hq,Dv] float64, lse [B,Hq]);
+    Dv = case.head_dim_v (the value head dim; head_dim unless set)."""
     B, Hq, D = case.batch, case.num_q_heads, case.head_dim
-    out = np.zeros((B, Hq, D), dtype=np.float64)
+    Dv = getattr(case, "head_dim_v", 0) or D
+    out = np.zeros((B, Hq, Dv), dtype=np.float64)
     lse = np.zeros((B, Hq), dtype=np.float64)
     q, kp, vp = _c(case.q), _c(case.kv.k_pool), _c(case.kv.v_pool)
     bt, sl = _c(case.kv.block_table), _c(case.seq_lens)
     sk, kd, vd, al = _extras(case)
-    rc = (clib or lib()).orc_decode(B, Hq, case.num_kv_heads, D, case.page_size,
+    rc = (clib or lib()).orc_decode(B, Hq, case.num_kv_heads, D, Dv, case.page_size,
                           _KV[case.kv_dtype], _ptr(q), _ptr(kp), _ptr(vp),
                           kp.shape[0], _ptr(bt), bt.shape[1], _ptr(sl),
                           case.scale, case.softcap, case.window, case.k_scale,
@@ -211,8 +213,9 @@ def brute_decode(case) -> np.ndarray:
     bf = _elem_table("bf16")
     kt = _elem_table(case.kv_dtype)
     B, Hq, D = case.batch, case.num_q_heads, case.head_dim
+    Dv = getattr(case, "head_dim_v", 0) or D
     G = Hq // case.num_kv_heads
-    out = np.zeros((B, Hq, D))
+    out = np.zeros((B, Hq, Dv))
     for b in range(B):
         L = int(case.seq_lens[b])
         lo = max(0, L - case.window) if case.window > 0 else 0
@@ -220,7 +223,7 @@ def brute_decode(case) -> np.ndarray:
             continue
         k, v = _dense_seq(case.kv, b, L, case.kv_dtype, kt)
         k = k[lo:] * case.k_scale
-        v = v[lo:] * case.v_scale
+        v = v[lo:, :, :Dv] * case.v_scale      # value: the row's first Dv entries
         for h in range(Hq):
             q = bf[case.q[b, h].astype(np.int64)]
             s = case.scale * (k[:, h // G, :] @ q)

@@ -77,6 +77,16 @@
  *           page's `alibi <= 0` test is this causal limit for the positive
  *           slopes ALiBi uses); the window rule is unchanged.
  *
+ *  latent   Decode with a value head dim Dv smaller than the key head dim D
+ *           (the grouped kernel `_fwd_grouped_kernel_stage1` of the decode
+ *           page takes Lk != Lv, e.g. Lk = 576 split as 512 + 64 and
+ *           Lv = 512): the scores use all D entries of q and of the key row,
+ *           and the value of token t is the first Dv entries of the value
+ *           pool's row at t's place; the value pool has the key pool's
+ *           layout (rows of D entries).  A latent cache passes one pool as
+ *           both, so the value is the first Dv entries of the key row.  The
+ *           output rows have Dv entries.  Dv = D is ordinary decode.
+ *
  *  descales Optional per-request fp32 descales kd[b], vd[b] (the b12x
  *           `_prepare_fp8_descales` gives one value per request): a cached
  *           key of sequence b is dec(K) * k_scale * kd[b], a cached value
@@ -150,6 +160,7 @@ static double cache_elem(const void *pool, int kv_dtype, int64_t page, int row,
 /* ------------------------------------------------------------------ */
 typedef struct {
     int B, Hq, Hkv, D, P, kv_dtype;
+    int Dv;                     /* value entries per row (<= D; decode only < D) */
     const uint16_t *q;          /* decode [B][Hq][D]; extend [total_q][Hq][D] */
     const void *k_pool, *v_pool;/* [num_pages][P][Hkv][D] */
     int64_t num_pages;
@@ -240,10 +251,12 @@ static void gather_cached(const orc_problem *pr, int b, int g, const double *q,
             double k = cache_elem(pr->k_pool, pr->kv_dtype, page, row, g, d,
                                   pr->P, pr->Hkv, pr->D) * ks;
             dot += q[d] * k;
-            v[(t - t0) * pr->D + d] =
+        }
+        /* the value: the first Dv entries of the value pool's row */
+        for (d = 0; d < pr->Dv; ++d)
+            v[(t - t0) * pr->Dv + d] =
                 cache_elem(pr->v_pool, pr->kv_dtype, page, row, g, d, pr->P,
                            pr->Hkv, pr->D) * vs;
-        }
         s[t - t0] = cap_score(pr->scale * dot, pr->softcap);
     }
 }
@@ -256,10 +269,10 @@ static void decode_row(const orc_problem *pr, int b, int h, double *q,
 {
     int G = pr->Hq / pr->Hkv;
     int g = h / G;
-    int D = pr->D;
+    int D = pr->D, Dv = pr->Dv;
     int64_t L = pr->seq_lens[b];
     int64_t lo = (pr->window > 0 && L - pr->window > 0) ? L - pr->window : 0;
-    double *out = pr->out + ((int64_t)b * pr->Hq + h) * D;
+    double *out = pr->out + ((int64_t)b * pr->Hq + h) * Dv;
     double *lse = pr->lse + (int64_t)b * pr->Hq + h;
     int d;
 
@@ -271,7 +284,7 @@ static void decode_row(const orc_problem *pr, int b, int h, double *q,
         gather_cached(pr, b, g, q, lo, L, s, v);
         for (t = lo; t < L; ++t)
             s[t - lo] += alibi_bias(pr, h, t, L - 1);
-        softmax_sum(s, v, L - lo, D, sink_of(pr, h), out, lse);
+        softmax_sum(s, v, L - lo, Dv, sink_of(pr, h), out, lse);
         return;
     }
 
@@ -294,11 +307,11 @@ static void decode_row(const orc_problem *pr, int b, int h, double *q,
                 for (t = a; t < e; ++t)
                     s[t - a] += alibi_bias(pr, h, t, L - 1);
             }
-            softmax_sum(s, v, e - a, D, -INFINITY, os + (int64_t)sp * D, &lses[sp]);
+            softmax_sum(s, v, e - a, Dv, -INFINITY, os + (int64_t)sp * Dv, &lses[sp]);
             if (lses[sp] > M)
                 M = lses[sp];
         }
-        for (d = 0; d < D; ++d)
+        for (d = 0; d < Dv; ++d)
             out[d] = 0.0;
         if (M == -INFINITY) {
             *lse = -INFINITY;
@@ -314,10 +327,10 @@ static void decode_row(const orc_problem *pr, int b, int h, double *q,
                 continue;
             w = exp(lses[sp] - M);
             z += w;
-            for (d = 0; d < D; ++d)
-                out[d] += w * os[(int64_t)sp * D + d];
+            for (d = 0; d < Dv; ++d)
+                out[d] += w * os[(int64_t)sp * Dv + d];
         }
-        for (d = 0; d < D; ++d)
+        for (d = 0; d < Dv; ++d)
             out[d] /= z;
         *lse = M + log(z);
     }
@@ -495,13 +508,14 @@ static int check_common(int B, int Hq, int Hkv, int D, int P, int kv_dtype)
 }
 
 /*
- * Decode oracle.  out [B][Hq][D] and lse [B][Hq] (natural log) are written.
+ * Decode oracle.  out [B][Hq][Dv] and lse [B][Hq] (natural log) are written;
+ * Dv is the value head dim (0: D; else 1 <= Dv <= D, see "latent" above).
  * num_splits == 0 evaluates the definition in one pass over the key range;
  * num_splits > 0 evaluates the split partition and the log-sum-exp merge.
  * sinks [Hq], the per-request descales k_desc/v_desc [B] and the ALiBi
  * slopes alibi [Hq] are optional (NULL: none / 1 / none).  Returns 0, -1 on a bad argument, -2 when memory runs out.
  */
-int orc_decode(int B, int Hq, int Hkv, int D, int P, int kv_dtype,
+int orc_decode(int B, int Hq, int Hkv, int D, int Dv, int P, int kv_dtype,
                const uint16_t *q, const void *k_pool, const void *v_pool,
                int64_t num_pages, const int32_t *block_table,
                int64_t bt_stride, const int32_t *seq_lens, double scale,
@@ -515,8 +529,12 @@ int orc_decode(int B, int Hq, int Hkv, int D, int P, int kv_dtype,
     int b;
     if (check_common(B, Hq, Hkv, D, P, kv_dtype) || num_splits < 0)
         return -1;
+    if (Dv == 0)
+        Dv = D;
+    if (Dv < 1 || Dv > D)
+        return -1;
     memset(&pr, 0, sizeof pr);
-    pr.B = B; pr.Hq = Hq; pr.Hkv = Hkv; pr.D = D; pr.P = P;
+    pr.B = B; pr.Hq = Hq; pr.Hkv = Hkv; pr.D = D; pr.Dv = Dv; pr.P = P;
     pr.kv_dtype = kv_dtype;
     pr.q = q; pr.k_pool = k_pool; pr.v_pool = v_pool;
     pr.num_pages = num_pages;
@@ -557,7 +575,7 @@ int orc_extend(int B, int Hq, int Hkv, int D, int P, int kv_dtype,
     if (check_common(B, Hq, Hkv, D, P, kv_dtype) || B < 1)
         return -1;
     memset(&pr, 0, sizeof pr);
-    pr.B = B; pr.Hq = Hq; pr.Hkv = Hkv; pr.D = D; pr.P = P;
+    pr.B = B; pr.Hq = Hq; pr.Hkv = Hkv; pr.D = D; pr.Dv = D; pr.P = P;
     pr.kv_dtype = kv_dtype;
     pr.q = q; pr.k_new = k_new; pr.v_new = v_new;
     pr.cu_q = cu_seqlens_q; pr.ctx_lens = ctx_lens;
@@ -662,7 +680,7 @@ int orc_verify(int B, int Hq, int Hkv, int D, int P, int kv_dtype, int q_len,
     if (check_common(B, Hq, Hkv, D, P, kv_dtype) || q_len < 1)
         return -1;
     memset(&pr, 0, sizeof pr);
-    pr.B = B; pr.Hq = Hq; pr.Hkv = Hkv; pr.D = D; pr.P = P;
+    pr.B = B; pr.Hq = Hq; pr.Hkv = Hkv; pr.D = D; pr.Dv = D; pr.P = P;
     pr.kv_dtype = kv_dtype;
     pr.q = q; pr.k_pool = k_pool; pr.v_pool = v_pool;
     pr.num_pages = num_pages;

@@ -114,7 +114,9 @@ def page_tokens(k_tok: np.ndarray, v_tok: np.ndarray, lens: Sequence[int],
     nan = BF16_NAN_BITS if k_tok.dtype == np.uint16 else E4M3_NAN_BITS
     table, num_pages = deal_pages(lens, page_size, rng, pool_pages)
     k_pool = scatter_tokens(k_tok, lens, table, page_size, num_pages, nan)
-    v_pool = scatter_tokens(v_tok, lens, table, page_size, num_pages, nan)
+    # one array for both when the values are the keys' rows (a latent cache)
+    v_pool = (k_pool if v_tok is k_tok else
+              scatter_tokens(v_tok, lens, table, page_size, num_pages, nan))
     return PagedKV(k_pool, v_pool, table, page_size)
 
 
@@ -160,6 +162,8 @@ class DecodeCase:
     k_descale: Optional[np.ndarray] = None  # float32 [B] per-request descales (None: 1)
     v_descale: Optional[np.ndarray] = None
     alibi_slopes: Optional[np.ndarray] = None   # float32 [Hq] ALiBi slopes (None: off)
+    head_dim_v: int = 0         # value head dim (0: head_dim); smaller: the value
+                                # is the first head_dim_v entries of the pool row
 
     @property
     def batch(self) -> int:
@@ -168,6 +172,15 @@ class DecodeCase:
     @property
     def page_size(self) -> int:
         return self.kv.page_size
+
+    @property
+    def dv(self) -> int:
+        return self.head_dim_v or self.head_dim
+
+    @property
+    def latent_alias(self) -> bool:
+        """One pool holds keys and values (a latent cache)."""
+        return self.kv.v_pool is self.kv.k_pool
 
     @property
     def max_kv_len(self) -> int:
@@ -180,9 +193,11 @@ class DecodeCase:
         return int(L.sum())
 
     def kv_bytes(self) -> int:
-        """Algorithmic K+V bytes one decode call must read."""
+        """Algorithmic K+V bytes one decode call must read (a latent cache:
+        each key row once, its first head_dim_v entries being the value)."""
         elem = 2 if self.kv_dtype == "bf16" else 1
-        return self.attended_tokens() * self.num_kv_heads * self.head_dim * 2 * elem
+        per_row = self.head_dim + (0 if self.latent_alias else self.dv)
+        return self.attended_tokens() * self.num_kv_heads * per_row * elem
 
     def verify_bytes(self, q_len: int) -> int:
         """Algorithmic bytes of a verify call with q_len query tokens per
@@ -203,7 +218,7 @@ class DecodeCase:
         L = self.seq_lens.astype(np.int64)
         lo = np.maximum(L - self.window, 0) if self.window > 0 else np.zeros_like(L)
         pages = np.where(L > lo, (L - 1) // P - lo // P + 1, 0)
-        return int(self.kv_bytes() + 2 * B * Hq * D * 2 + 4 * pages.sum() + 4 * B)
+        return int(self.kv_bytes() + B * Hq * (D + self.dv) * 2 + 4 * pages.sum() + 4 * B)
 
 
 def make_decode(name: str, lens: Sequence[int], Hq: int, Hkv: int, D: int,
@@ -280,6 +295,46 @@ def decode_config(n: int, page_size: Optional[int] = None) -> DecodeCase:
                            kv_dtype="fp8_e4m3", window=4096,
                            scale_range=(0.5, 2.0), lens_rng=rng)
     raise ValueError(f"no decode workload {n}")
+
+
+def make_mla_decode(name: str, lens: Sequence[int], Hq: int, Hkv: int, D: int, Dv: int,
+                    page_size: int, seed: int, alias: bool = True, softcap: float = 0.0,
+                    window: int = 0, num_splits: int = 0,
+                    lens_rng: Optional[np.random.Generator] = None) -> DecodeCase:
+    """A decode case over a latent cache: q ``[B, Hq, D]``, key rows of D
+    entries whose first Dv entries are the value (alias: one pool for both),
+    or (alias False) a separate value pool of the same layout whose entries
+    past Dv are NaN bits (never read).  Draw order after the lengths: page
+    permutation, Q, latent rows, separate value rows."""
+    rng = lens_rng if lens_rng is not None else np.random.default_rng(seed)
+    lens = [int(x) for x in lens]
+    B = len(lens)
+    table, num_pages = deal_pages(lens, page_size, rng)
+    q = bf16_bits(_normal(rng, (B, Hq, D)))
+    k_tok = bf16_bits(_normal(rng, (sum(lens), Hkv, D)))
+    if alias:
+        v_tok = k_tok
+    else:
+        v_tok = bf16_bits(_normal(rng, (sum(lens), Hkv, D)))
+        v_tok[:, :, Dv:] = BF16_NAN_BITS
+    k_pool = scatter_tokens(k_tok, lens, table, page_size, num_pages, BF16_NAN_BITS)
+    v_pool = (k_pool if alias else
+              scatter_tokens(v_tok, lens, table, page_size, num_pages, BF16_NAN_BITS))
+    return DecodeCase(name=name, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                      kv_dtype="bf16", q=q, kv=PagedKV(k_pool, v_pool, table, page_size),
+                      seq_lens=np.asarray(lens, dtype=np.int32),
+                      scale=1.0 / math.sqrt(D), softcap=softcap, window=window,
+                      num_splits=num_splits, k_tok=k_tok, v_tok=v_tok, head_dim_v=Dv)
+
+
+def mla_config(num_q_heads: int = 16, batch: int = 128, page_size: int = 64) -> DecodeCase:
+    """Latent-cache (MLA) decode shaped like DeepSeek-V3: one kv head of 576
+    entries (512 latent + 64 rope), values the first 512, query heads 16 (a
+    tensor-parallel shard of 128) or all 128, L ~ U{512..4096}, seed 6."""
+    rng = np.random.default_rng(6)
+    lens = rng.integers(512, 4096, size=batch, endpoint=True)
+    return make_mla_decode(f"mla-h{num_q_heads}", lens, num_q_heads, 1, 576, 512, page_size,
+                           6, lens_rng=rng)
 
 
 # --------------------------------------------------------------------------
@@ -447,10 +502,11 @@ def _extra_tensors(case, device) -> dict:
 
 def decode_tensors(case: DecodeCase, device) -> dict:
     kd = kv_torch_dtype(case.kv_dtype)
+    k_pool = _dev(case.kv.k_pool, device, kd)
     return dict(
         q=_dev(case.q, device, torch.bfloat16),
-        k_pool=_dev(case.kv.k_pool, device, kd),
-        v_pool=_dev(case.kv.v_pool, device, kd),
+        k_pool=k_pool,
+        v_pool=k_pool if case.kv.v_pool is case.kv.k_pool else _dev(case.kv.v_pool, device, kd),
         block_table=_dev(case.kv.block_table, device),
         seq_lens=_dev(case.seq_lens, device),
         **_extra_tensors(case, device),

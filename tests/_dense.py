@@ -61,17 +61,20 @@ def _scales(case, b):
 
 
 def sdpa_decode(case):
-    """Decode without soft-cap through the library routine."""
+    """Decode without soft-cap through the library routine (value head dim
+    Dv = case.dv: torch's routine takes a value width other than the key's)."""
     assert case.softcap == 0
     B, Hq, D = case.batch, case.num_q_heads, case.head_dim
+    Dv = getattr(case, "dv", D)
     G = Hq // case.num_kv_heads
-    out = np.zeros((B, Hq, D))
+    out = np.zeros((B, Hq, Dv))
     for b in range(B):
         L = int(case.seq_lens[b])
         lo = max(0, L - case.window) if case.window > 0 else 0
         if L == 0:
             continue
         k, v = dense_tokens(case.kv, b, L, case.kv_dtype)
+        v = v[:, :, :Dv]                  # the value: the row's first Dv entries
         ks, vs = _scales(case, b)
         k = np.repeat(k[lo:] * ks, G, axis=1).transpose(1, 0, 2)
         v = np.repeat(v[lo:] * vs, G, axis=1).transpose(1, 0, 2)

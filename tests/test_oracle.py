@@ -606,3 +606,80 @@ def test_alibi_two_keys_closed_form(oracle_mod):
         s0, s1 = case.scale * (qf @ kf[0, 0]), case.scale * (qf @ kf[1, 0])
         w1 = 1.0 / (1.0 + math.exp(-(s1 - s0 + float(case.alibi_slopes[h]))))
         close(out[0, h], (1 - w1) * vf[0, 0] + w1 * vf[1, 0])
+
+
+# ---------------------------------------------------------------- latent cache (Dv < D)
+def _mla(lens, Hq, Hkv, D, Dv, P, seed, **kw):
+    rng = np.random.default_rng(seed)
+    return I.make_mla_decode(f"m{seed}", lens, Hq, Hkv, D, Dv, P, seed, lens_rng=rng, **kw)
+
+
+@pytest.mark.parametrize("D,Dv,Hq,Hkv,alias,window", [
+    (576, 512, 16, 1, True, 0), (576, 512, 8, 2, False, 0), (288, 256, 4, 1, True, 30),
+    (64, 32, 6, 3, False, 0)])
+def test_latent_decode_equals_sdpa_with_narrow_values(oracle_mod, D, Dv, Hq, Hkv, alias, window):
+    """torch's SDPA with value rows of Dv entries (the first Dv of each pool
+    row) against the oracle; the separate pool's entries past Dv are NaN, so
+    reading any of them would show."""
+    case = _mla([37, 100, 64], Hq, Hkv, D, Dv, 16, 60 + D + Hq, alias=alias, window=window)
+    got, _ = oracle_mod.decode(case)
+    assert got.shape == (3, Hq, Dv)
+    assert np.isfinite(got).all()
+    close(got, sdpa_decode(case))
+
+
+def test_latent_alias_equals_a_copied_value_pool(oracle_mod):
+    """One pool for keys and values gives bit for bit what a separate pool
+    holding the same bits gives."""
+    case = _mla([50, 9, 130], 16, 1, 576, 512, 16, 71)
+    import dataclasses
+    sep = dataclasses.replace(case, kv=dataclasses.replace(case.kv,
+                                                           v_pool=case.kv.k_pool.copy()))
+    assert not sep.latent_alias and case.latent_alias
+    a, la = oracle_mod.decode(case)
+    b, lb = oracle_mod.decode(sep)
+    np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(la, lb)
+
+
+def test_latent_full_width_value_is_ordinary_decode(oracle_mod):
+    """head_dim_v = head_dim is ordinary decode (bit-identical)."""
+    case = rand_decode([40, 77], 8, 2, 64, 16, 72)
+    import dataclasses
+    a, _ = oracle_mod.decode(case)
+    b, _ = oracle_mod.decode(dataclasses.replace(case, head_dim_v=64))
+    np.testing.assert_array_equal(a, b)
+
+
+def test_latent_value_entries_are_the_prefix(oracle_mod):
+    """Zeroing the key entries past Dv in q changes the scores only through
+    those entries: with q's tail zero the result equals ordinary decode of
+    the truncated rows (D = Dv) with the same scale."""
+    import dataclasses
+    case = _mla([33, 70], 4, 1, 64, 32, 16, 73, alias=True)
+    q = case.q.copy()
+    q[:, :, 32:] = 0
+    full = dataclasses.replace(case, q=q)
+    trunc = dataclasses.replace(
+        case, q=np.ascontiguousarray(q[:, :, :32]), head_dim=32, head_dim_v=0,
+        kv=dataclasses.replace(case.kv, k_pool=np.ascontiguousarray(case.kv.k_pool[..., :32]),
+                               v_pool=np.ascontiguousarray(case.kv.k_pool[..., :32])))
+    a, la = oracle_mod.decode(full)
+    b, lb = oracle_mod.decode(trunc)
+    close(a, b, rtol=1e-12, atol=1e-14)
+    close(la, lb, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("splits", [2, 5, 16])
+def test_latent_split_invariance(oracle_mod, splits):
+    case = _mla([300, 45, 1], 16, 1, 288, 256, 16, 74, softcap=20.0)
+    a, la = oracle_mod.decode(case)
+    b, lb = oracle_mod.decode(case, num_splits=splits)
+    close(a, b)
+    close(la, lb)
+
+
+def test_latent_brute_force(oracle_mod):
+    case = _mla([64, 23], 16, 1, 576, 512, 64, 75, alias=False, softcap=10.0, window=40)
+    got, _ = oracle_mod.decode(case)
+    close(got, oracle_mod.brute_decode(case))

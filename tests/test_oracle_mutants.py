@@ -57,8 +57,8 @@ MUTANTS = [
     ("sink-kv-head", "return pr->sinks ? (double)pr->sinks[h] : -INFINITY;",
      "return pr->sinks ? (double)pr->sinks[h % pr->Hkv] : -INFINITY;"),
     ("sink-sign", "        z = exp(sink - m);", "        z = exp(m - sink);"),
-    ("sink-in-every-split", "softmax_sum(s, v, e - a, D, -INFINITY,",
-     "softmax_sum(s, v, e - a, D, sink_of(pr, h),"),
+    ("sink-in-every-split", "softmax_sum(s, v, e - a, Dv, -INFINITY,",
+     "softmax_sum(s, v, e - a, Dv, sink_of(pr, h),"),
     ("sink-missing-from-merge", "            z = exp(sink_of(pr, h) - M);", "            z = 0.0;"),
     ("descale-first-request", "(pr->k_desc ? (double)pr->k_desc[b] : 1.0)",
      "(pr->k_desc ? (double)pr->k_desc[0] : 1.0)"),
@@ -71,6 +71,14 @@ MUTANTS = [
     ("alibi-decode-pos", "s[t - lo] += alibi_bias(pr, h, t, L - 1);\n        softmax_sum",
      "s[t - lo] += alibi_bias(pr, h, t, L);\n        softmax_sum"),
     ("alibi-new-key-pos", "+ alibi_bias(pr, h, C + j, pos);", "+ alibi_bias(pr, h, j, pos);"),
+    ("latent-value-pitch", "cache_elem(pr->v_pool, pr->kv_dtype, page, row, g, d, pr->P,\n"
+     "                           pr->Hkv, pr->D) * vs;",
+     "cache_elem(pr->v_pool, pr->kv_dtype, page, row, g, d, pr->P,\n"
+     "                           pr->Hkv, pr->Dv) * vs;"),
+    ("latent-value-suffix", "cache_elem(pr->v_pool, pr->kv_dtype, page, row, g, d, pr->P,",
+     "cache_elem(pr->v_pool, pr->kv_dtype, page, row, g, pr->D - pr->Dv + d, pr->P,"),
+    ("latent-value-from-key-pool", "cache_elem(pr->v_pool, pr->kv_dtype, page, row, g, d, pr->P,",
+     "cache_elem(pr->k_pool, pr->kv_dtype, page, row, g, d, pr->P,"),
 ]
 
 
