@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define PAGED_ATTN_ABI_VERSION 2
+#define PAGED_ATTN_ABI_VERSION 3
 
 typedef enum {
     PA_OK = 0,
@@ -125,8 +125,10 @@ typedef struct {
     int32_t mode;              /* pa_mode */
     int32_t num_seqs;          /* B >= 0 */
     int32_t num_q_heads;       /* Hq, a multiple of num_kv_heads */
-    int32_t num_kv_heads;      /* Hkv >= 1; G = Hq/Hkv must be 1, 2, 4, 8 or 16 */
-    int32_t head_dim;          /* D: 64 or 128 (same for q/k and v) */
+    int32_t num_kv_heads;      /* Hkv >= 1; G = Hq/Hkv must be 1, 2, 4, 8 or 16
+                                  (latent cache: 1 .. 128) */
+    int32_t head_dim;          /* D: 64 or 128 (q/k and v alike); latent cache:
+                                  576 or 288 (q/k) */
     int32_t page_size;         /* P >= 1 */
     int32_t kv_dtype;          /* pa_kv_dtype */
     int32_t window;            /* sliding window W (<= 0: off) */
@@ -140,6 +142,15 @@ typedef struct {
                                   (q_len >= 1, G * q_len <= 64) */
     int32_t num_splits;        /* decode: 0 = plan chooses; > 0 forces the
                                   number of split-pass pieces (waves) */
+    int32_t head_dim_v;        /* value head dim: 0 (or head_dim) = head_dim;
+                                  head_dim_v < head_dim selects a latent cache
+                                  (decode, bf16, (576, 512) or (288, 256)):
+                                  the value of a token is the first
+                                  head_dim_v entries of the value pool's row,
+                                  read with the key strides; pass v_pool =
+                                  k_pool for a latent cache whose value is the
+                                  key row's prefix (`_fwd_grouped_kernel_stage1`
+                                  with Lk = 576 = 512 + 64, Lv = 512) */
 } pa_problem;
 
 /* The plan: a plain value the caller owns (nothing to free).  Planning reads
@@ -183,7 +194,8 @@ pa_status paged_attn_plan(const pa_problem* prob, int hip_device, pa_plan* out);
  * paged_attn_decode -- one query token per sequence.
  *
  *   q             bf16 [B, Hq, D], sequence stride q_stride_b (elements),
- *                 heads contiguous
+ *                 heads contiguous (latent cache: D = head_dim, the value
+ *                 rows and out have Dv = head_dim_v entries)
  *   k_pool,v_pool bf16 or e4m3fn pools (layout above), num_pages pages
  *   block_table   int32 [B, >= ceil(L_b/P)] with row stride bt_stride
  *   seq_lens      int32 [B]: L_b cached tokens including the query token
@@ -219,6 +231,14 @@ pa_status paged_attn_decode(const pa_plan* plan,
                             void* workspace, uint64_t workspace_bytes,
                             const pa_extras* extras,
                             void* hip_stream);
+
+/*
+ * Latent cache (prob.head_dim_v < prob.head_dim): the same call with
+ * q [B, Hq, D] and out [B, Hq, Dv]; v_pool's rows are read at the key rows'
+ * places with the key strides and their first Dv entries are the values.
+ * When v_pool == k_pool each row is read once (the values come from the key
+ * rows already loaded).  bf16 caches only; G up to 128.
+ */
 
 /*
  * paged_attn_decode_split, paged_attn_decode_merge -- the two kernels of

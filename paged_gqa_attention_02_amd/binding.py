@@ -18,6 +18,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpaged_attn.so")
 
 PA_MODE_DECODE, PA_MODE_EXTEND, PA_MODE_VERIFY = 0, 1, 2
+ABI_VERSION = 3          # PAGED_ATTN_ABI_VERSION these structures mirror
 PA_KV = {"bf16": 0, "fp8_e4m3": 1}
 
 
@@ -31,7 +32,7 @@ class PaProblem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "mode", "num_seqs", "num_q_heads", "num_kv_heads", "head_dim", "page_size",
         "kv_dtype", "window", "max_pages_per_seq", "max_kv_len", "total_q",
-        "max_q_len", "num_splits")]
+        "max_q_len", "num_splits", "head_dim_v")]
 
 
 class PaPlan(ctypes.Structure):
@@ -88,6 +89,9 @@ def lib():
     L.paged_attn_abi_version.restype = ctypes.c_int
     L.paged_attn_hip_runtime_path.argtypes = []
     L.paged_attn_hip_runtime_path.restype = ctypes.c_char_p
+    if L.paged_attn_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{LIB_PATH} has ABI version {L.paged_attn_abi_version()}, this "
+                           f"binding expects {ABI_VERSION}; rebuild the library")
     rt = L.paged_attn_hip_runtime_path().decode()
     torch_rt = os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")
     if os.path.exists(torch_rt) and os.path.realpath(rt) != os.path.realpath(torch_rt):
@@ -135,12 +139,14 @@ class Plan:
 def plan(mode: int, num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
          page_size: int, kv_dtype: str = "bf16", window: int = 0,
          max_pages_per_seq: int = 0, max_kv_len: int = 0, total_q: int = 0,
-         max_q_len: int = 0, num_splits: int = 0, device: Optional[int] = None) -> Plan:
+         max_q_len: int = 0, num_splits: int = 0, device: Optional[int] = None,
+         head_dim_v: int = 0) -> Plan:
     """paged_attn_plan.  device=None plans for the current torch device when one
-    exists, else for an MI355X without touching a device."""
+    exists, else for an MI355X without touching a device.  head_dim_v <
+    head_dim: a latent cache (values are the first head_dim_v entries)."""
     prob = PaProblem(mode, num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
                      PA_KV[kv_dtype], window, max_pages_per_seq, max_kv_len, total_q,
-                     max_q_len, num_splits)
+                     max_q_len, num_splits, head_dim_v)
     if device is None:
         device = torch.cuda.current_device() if torch.cuda.is_available() else -1
     out = PaPlan()
@@ -207,12 +213,14 @@ def _workspace(pl: Plan, workspace, device):
 
 
 def decode_plan(q: torch.Tensor, k_pool: torch.Tensor, block_table: torch.Tensor,
-                max_kv_len: int, window: int = 0, num_splits: int = 0) -> Plan:
-    """Plan a decode call for tensors shaped like these."""
+                max_kv_len: int, window: int = 0, num_splits: int = 0,
+                head_dim_v: int = 0) -> Plan:
+    """Plan a decode call for tensors shaped like these (head_dim_v: the value
+    width of a latent cache, 0 = the key width)."""
     B, Hq, D = q.shape
     return plan(PA_MODE_DECODE, B, Hq, k_pool.shape[2], D, k_pool.shape[1],
                 _kv_dtype_name(k_pool), window, block_table.shape[1], max_kv_len,
-                num_splits=num_splits, device=q.device.index)
+                num_splits=num_splits, device=q.device.index, head_dim_v=head_dim_v)
 
 
 def decode(pl: Plan, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
@@ -221,7 +229,9 @@ def decode(pl: Plan, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor
            v_scale: float = 1.0, out: Optional[torch.Tensor] = None,
            workspace: Optional[torch.Tensor] = None, stream=None, sinks=None,
            k_descale=None, v_descale=None, alibi_slopes=None) -> torch.Tensor:
-    """paged_attn_decode: q bf16 [B, Hq, D] -> out bf16 [B, Hq, D].
+    """paged_attn_decode: q bf16 [B, Hq, D] -> out bf16 [B, Hq, D] (a plan
+    with head_dim_v = Dv < D: out [B, Hq, Dv], values the first Dv entries of
+    v_pool's rows; pass v_pool = k_pool for a latent cache).
     A workspace passed in needs plan.workspace_bytes bytes.  sinks: fp32 [Hq]
     sink logits; k_descale/v_descale: fp32 per-request descales (1 or >= B)."""
     return _decode("paged_attn_decode", pl, q, k_pool, v_pool, block_table, seq_lens, scale,
@@ -297,10 +307,13 @@ def _decode(fn, pl, q, k_pool, v_pool, block_table, seq_lens, scale, softcap, wi
         raise TypeError("block_table and seq_lens must be int32")
     if block_table.stride(1) != 1:
         raise ValueError("block_table rows must be contiguous")
+    dv = pl.problem.head_dim_v or q.shape[-1]
+    oshape = q.shape[:-1] + (dv,)
     if out is None:
-        out = torch.empty_like(q)
-    if out.dtype != torch.bfloat16 or out.shape != q.shape or not _rows_contiguous(out):
-        raise ValueError(f"out must be bf16 {shape} like q, dense after the sequence dimension")
+        out = torch.empty(oshape, dtype=torch.bfloat16, device=q.device)
+    if out.dtype != torch.bfloat16 or out.shape != oshape or not _rows_contiguous(out):
+        raise ValueError(f"out must be bf16 {shape} like q (last dim {dv}), dense after the "
+                         "sequence dimension")
     sp, st, sh = _pool_strides(k_pool, v_pool)
     workspace = _workspace(pl, workspace, q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -14,7 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpaged_attn.so")
-SOURCES = ["api.cpp", "decode.hip", "merge.hip", "gather.hip", "extend.hip", "append.hip"]
+SOURCES = ["api.cpp", "decode.hip", "merge.hip", "gather.hip", "extend.hip", "append.hip",
+           "mla.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -35,18 +35,37 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t m) { return cdiv(a, m) * m; }
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
+// A latent cache: values narrower than keys (the value is the first
+// head_dim_v entries of the row).
+bool is_latent(const pa_problem& pr) {
+    return pr.head_dim_v != 0 && pr.head_dim_v != pr.head_dim;
+}
+
+// Entries of a value (and output) row.
+int value_dim(const pa_problem& pr) { return is_latent(pr) ? pr.head_dim_v : pr.head_dim; }
+
 pa_status check_problem(const pa_problem& pr) {
     if (pr.mode != PA_MODE_DECODE && pr.mode != PA_MODE_EXTEND && pr.mode != PA_MODE_VERIFY)
         return PA_ERR_UNSUPPORTED;
     if (pr.num_seqs < 0 || pr.num_q_heads <= 0 || pr.num_kv_heads <= 0 || pr.page_size <= 0 ||
-        pr.max_kv_len < 0 || pr.max_pages_per_seq < 0 || pr.num_splits < 0)
+        pr.max_kv_len < 0 || pr.max_pages_per_seq < 0 || pr.num_splits < 0 ||
+        pr.head_dim_v < 0)
         return PA_ERR_INVALID_SHAPE;
     if (pr.num_q_heads % pr.num_kv_heads != 0) return PA_ERR_INVALID_SHAPE;
     // one merge block per (sequence, query head): the grid is 31-bit
     if ((int64_t)pr.num_seqs * pr.num_q_heads >= ((int64_t)1 << 31)) return PA_ERR_UNSUPPORTED;
     const int G = pr.num_q_heads / pr.num_kv_heads;
-    if (G > 16 || !is_pow2(G)) return PA_ERR_UNSUPPORTED;
-    if (pr.head_dim != 64 && pr.head_dim != 128) return PA_ERR_UNSUPPORTED;
+    if (is_latent(pr)) {
+        // decode over a bf16 latent cache, (576, 512) or (288, 256), G <= 128
+        if (pr.mode != PA_MODE_DECODE || pr.kv_dtype != PA_KV_BF16) return PA_ERR_UNSUPPORTED;
+        if (!((pr.head_dim == 576 && pr.head_dim_v == 512) ||
+              (pr.head_dim == 288 && pr.head_dim_v == 256)))
+            return PA_ERR_UNSUPPORTED;
+        if (G > kMaxLatentGroup) return PA_ERR_UNSUPPORTED;
+    } else {
+        if (G > 16 || !is_pow2(G)) return PA_ERR_UNSUPPORTED;
+        if (pr.head_dim != 64 && pr.head_dim != 128) return PA_ERR_UNSUPPORTED;
+    }
     if (pr.kv_dtype != PA_KV_BF16 && pr.kv_dtype != PA_KV_FP8_E4M3) return PA_ERR_UNSUPPORTED;
     if (!is_pow2(pr.page_size) || pr.page_size > 4096) return PA_ERR_UNSUPPORTED;
     if ((int64_t)pr.max_pages_per_seq < cdiv(pr.max_kv_len, pr.page_size))
@@ -86,10 +105,17 @@ ExtLayout extend_layout(const pa_problem& pr, int64_t workers) {
     return L;
 }
 
-// Split-pass waves per block: one per 16 query rows of a kv head.
+// Split-pass waves per block: one per 16 query rows of a kv head (latent
+// cache: rounded up to 1, 2, 4 or 8).
 int decode_waves_per_block(const pa_problem& pr) {
     const int q_len = pr.mode == PA_MODE_VERIFY ? pr.max_q_len : 1;
-    return ((pr.num_q_heads / pr.num_kv_heads) * q_len + 15) / 16;
+    const int nw = ((pr.num_q_heads / pr.num_kv_heads) * q_len + 15) / 16;
+    if (is_latent(pr)) {
+        int p2 = 1;
+        while (p2 < nw) p2 *= 2;
+        return p2;
+    }
+    return nw;
 }
 
 int elem_bytes(int kv_dtype) { return kv_dtype == PA_KV_FP8_E4M3 ? 1 : 2; }
@@ -206,14 +232,18 @@ pa_status paged_attn_plan(const pa_problem* prob, int hip_device, pa_plan* out) 
         if (pr.num_splits > 0) {
             workers = pr.num_splits;
         } else {
-            int per_cu = kDefaultWavesPerCu / nw;
+            // latent cache: two blocks of at most two waves share a compute
+            // unit's LDS (the plan assumes v_pool == k_pool)
+            int per_cu = is_latent(pr) ? (nw <= 2 ? 2 : 1) : kDefaultWavesPerCu / nw;
             if (hip_device >= 0) {
                 int cur = -1;
                 if (hipGetDevice(&cur) != hipSuccess) return PA_ERR_HIP;
                 if (cur != hip_device && hipSetDevice(hip_device) != hipSuccess) return PA_ERR_HIP;
-                const hipError_t e = decode_blocks_per_cu(pr.head_dim,
-                                                          pr.kv_dtype == PA_KV_FP8_E4M3,
-                                                          pr.page_size >= 16, nw, &per_cu);
+                const hipError_t e =
+                    is_latent(pr)
+                        ? mla_blocks_per_cu(pr.head_dim, pr.head_dim_v, true, nw, &per_cu)
+                        : decode_blocks_per_cu(pr.head_dim, pr.kv_dtype == PA_KV_FP8_E4M3,
+                                               pr.page_size >= 16, nw, &per_cu);
                 if (cur != hip_device) (void)hipSetDevice(cur);
                 if (e != hipSuccess || per_cu < 1) return PA_ERR_HIP;
             }
@@ -226,7 +256,7 @@ pa_status paged_attn_plan(const pa_problem* prob, int hip_device, pa_plan* out) 
         const int64_t q_len = pr.mode == PA_MODE_VERIFY ? pr.max_q_len : 1;
         const int64_t rows = workers * 2 * (pr.num_q_heads / pr.num_kv_heads) * q_len;
         // partial rows, their log-sum-exp, and one record per segment
-        pl.workspace_bytes = (uint64_t)(round_up(rows * pr.head_dim * 4, 256) +
+        pl.workspace_bytes = (uint64_t)(round_up(rows * value_dim(pr) * 4, 256) +
                                         round_up(rows * 4, 256) +
                                         round_up(16 * (int64_t)pr.num_seqs *
                                                      pr.num_kv_heads, 256));
@@ -269,11 +299,11 @@ int paged_attn_plan_describe(const pa_plan* pl, char* buf, int buf_len) {
     } else {
         const pa_problem& p = pl->prob;
         n = snprintf(tmp, sizeof tmp,
-                     "%s B=%d Hq=%d Hkv=%d D=%d P=%d kv=%s window=%d max_kv_len=%d "
+                     "%s B=%d Hq=%d Hkv=%d D=%d Dv=%d P=%d kv=%s window=%d max_kv_len=%d "
                      "splits=%d tokens_per_split=%d waves=%d cus=%d workspace=%llu",
                      p.mode == PA_MODE_DECODE ? "decode"
                      : p.mode == PA_MODE_VERIFY ? "verify" : "extend", p.num_seqs,
-                     p.num_q_heads, p.num_kv_heads, p.head_dim, p.page_size,
+                     p.num_q_heads, p.num_kv_heads, p.head_dim, value_dim(p), p.page_size,
                      p.kv_dtype == PA_KV_FP8_E4M3 ? "fp8_e4m3" : "bf16", p.window,
                      p.max_kv_len, pl->num_splits, pl->tokens_per_split,
                      pl->waves_per_block, pl->num_cus,
@@ -313,10 +343,12 @@ pa_status decode_impl(int passes, int mode, const pa_plan* plan, const void* q, 
     st = check_pools(pl, k_pool, v_pool, kv_stride_page, kv_stride_tok, kv_stride_head,
                      num_pages, block_table, bt_stride);
     if (st != PA_OK) return st;
-    // verify: q_len query rows per sequence, each Hq*D contiguous
+    // verify: q_len query rows per sequence, each Hq*D contiguous (out rows
+    // Hq*Dv)
     const int32_t q_len = mode == PA_MODE_VERIFY ? pr.max_q_len : 1;
     const int64_t row = (int64_t)pr.num_q_heads * pr.head_dim;
-    if (q_stride_b < q_len * row || out_stride_b < q_len * row) return PA_ERR_INVALID_SHAPE;
+    const int64_t orow = (int64_t)pr.num_q_heads * value_dim(pr);
+    if (q_stride_b < q_len * row || out_stride_b < q_len * orow) return PA_ERR_INVALID_SHAPE;
     if (!aligned16(q) || !aligned16(out) || (q_stride_b * 2) % 16 || (out_stride_b * 2) % 16)
         return PA_ERR_MISALIGNED;
     if (!isfinite(scale) || !isfinite(softcap) || !isfinite(k_scale) || !isfinite(v_scale))
@@ -350,7 +382,7 @@ pa_status decode_impl(int passes, int mode, const pa_plan* plan, const void* q, 
     p.q_len = q_len;
     p.rows = p.group * q_len;
     p.q_stride_t = row;
-    p.out_stride_t = row;
+    p.out_stride_t = orow;
     p.page_shift = ilog2(pr.page_size);
     p.window = pr.window;
     const float kl2e = 1.4426950408889634f;
@@ -372,18 +404,23 @@ pa_status decode_impl(int passes, int mode, const pa_plan* plan, const void* q, 
         const int64_t rows = (int64_t)pl.num_splits * 2 * p.rows;
         char* ws = static_cast<char*>(workspace);
         p.part_o = reinterpret_cast<float*>(ws);
-        const int64_t o_bytes = round_up(rows * pr.head_dim * 4, 256);
+        const int64_t o_bytes = round_up(rows * value_dim(pr) * 4, 256);
         p.part_lse = reinterpret_cast<float*>(ws + o_bytes);
         p.seg_rec = reinterpret_cast<int32_t*>(ws + o_bytes + round_up(rows * 4, 256));
     }
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     const bool uniform = pr.page_size >= 16;
-    if ((passes & kSplitPass) &&
-        launch_decode(p, pr.head_dim, pr.kv_dtype == PA_KV_FP8_E4M3, uniform,
-                      pl.waves_per_block, pl.num_splits, stream) != hipSuccess)
-        return PA_ERR_HIP;
+    if (passes & kSplitPass) {
+        const hipError_t e =
+            is_latent(pr)
+                ? launch_mla_decode(p, pr.head_dim, pr.head_dim_v, k_pool == v_pool,
+                                    pl.waves_per_block, pl.num_splits, stream)
+                : launch_decode(p, pr.head_dim, pr.kv_dtype == PA_KV_FP8_E4M3, uniform,
+                                pl.waves_per_block, pl.num_splits, stream);
+        if (e != hipSuccess) return PA_ERR_HIP;
+    }
     if ((passes & kMergePass) &&
-        launch_decode_merge(p, pr.head_dim, pr.num_seqs, pr.num_kv_heads, stream) !=
+        launch_decode_merge(p, value_dim(pr), pr.num_seqs, pr.num_kv_heads, stream) !=
             hipSuccess)
         return PA_ERR_HIP;
     return PA_OK;
@@ -433,6 +470,7 @@ pa_status paged_attn_gather(const pa_plan* plan, const void* k_pool, const void*
     const pa_problem& pr = pl.prob;
     pa_status st = check_problem(pr);
     if (st != PA_OK) return st;
+    if (is_latent(pr)) return PA_ERR_UNSUPPORTED;   // rows of 64 or 128 entries only
     if (pr.num_seqs == 0) return PA_OK;
     if (!seq_lens || !k_out || !v_out) return PA_ERR_NULL_POINTER;
     st = check_pools(pl, k_pool, v_pool, kv_stride_page, kv_stride_tok, kv_stride_head,

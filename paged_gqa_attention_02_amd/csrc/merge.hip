@@ -127,18 +127,32 @@ hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, int B, int H
     // to fill the chip, a divisor of them (more blocks, more piece lanes
     // each) otherwise.
     const int64_t segs = (int64_t)B * Hkv;
-    // at most kMergeThreads / (D/4) rows per block (16 for D = 128)
+    // at most kMergeThreads / (D/4) rows per block (16 for D = 128, 4 for 512)
     const int max_rows = kMergeThreads / (head_dim / 4);
     int per_block = p.rows;
     while (per_block > max_rows || p.rows % per_block) --per_block;
     while (per_block % 2 == 0 && segs * (p.rows / per_block) < 1024) per_block /= 2;
     dim3 grid((unsigned)(segs * (p.rows / per_block)));
-    if (head_dim == 128)
-        hipLaunchKernelGGL(decode_merge_kernel<128>, grid, dim3(kMergeThreads), 0, stream, p,
-                           per_block);
-    else
-        hipLaunchKernelGGL(decode_merge_kernel<64>, grid, dim3(kMergeThreads), 0, stream, p,
-                           per_block);
+    switch (head_dim) {
+        case 64:
+            hipLaunchKernelGGL(decode_merge_kernel<64>, grid, dim3(kMergeThreads), 0, stream, p,
+                               per_block);
+            break;
+        case 128:
+            hipLaunchKernelGGL(decode_merge_kernel<128>, grid, dim3(kMergeThreads), 0, stream, p,
+                               per_block);
+            break;
+        case 256:       // latent-cache values
+            hipLaunchKernelGGL(decode_merge_kernel<256>, grid, dim3(kMergeThreads), 0, stream, p,
+                               per_block);
+            break;
+        case 512:
+            hipLaunchKernelGGL(decode_merge_kernel<512>, grid, dim3(kMergeThreads), 0, stream, p,
+                               per_block);
+            break;
+        default:
+            return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -1,0 +1,458 @@
+// mla.hip -- split pass of paged decode over a latent KV cache for gfx950:
+// the query/key head dim DQK is larger than the value head dim DV, and the
+// value of a token is the first DV entries of its row (Lk = 576 split as
+// 512 + 64, Lv = 512, or 288 = 256 + 32 and 256: the `BLOCK_DMODEL` /
+// `BLOCK_DPE` / `BLOCK_DV` choice of `_decode_grouped_att_m_fwd` on the
+// decode page "vllm/attention/ops/triton_decode_attention.py").
+//
+// The value rows are read at the key rows' places with the key strides; a
+// latent cache passes one pool as both, and then the value operands come from
+// the key tile already in LDS (each row crosses HBM once).  The stream-K cut
+// of the key ranges, the partial slots, the segment records and the merge are
+// those of the decode split pass (decode_geom.h, merge.hip).
+//
+// Work: persistent blocks of NW waves walk the tiles of their range; wave wv
+// owns query rows (the heads of the kv head) 16wv .. 16wv + 15, and the G
+// heads share every staged byte.  Per 32-key tile, with
+// v_mfma_f32_16x16x32_bf16:
+//   S^T[32 keys x 16 rows] = K[32 x DQK] Q^T[DQK x 16]   K from LDS in the A
+//                                                      layout, Q^T in registers
+//   online softmax per row (one MFMA column: 4 lanes hold its keys)
+//   O^T[DV x 16] += V^T[DV x 32] P^T[32 x 16]          P^T is the S^T
+//                                                      accumulator; V^T from
+//                                                      transposing LDS reads
+// LDS tile: a main region (entries [0, DV) of 32 rows, 2*DV bytes a row) and a
+// rope region (entries [DV, DQK)), each row's 16-byte slots XOR-swizzled so
+// the operand reads of a quarter wave (K: 16 rows, one slot; V: 8 rows, 32
+// bytes each) hit distinct banks.  Tiles are filled by direct global->LDS
+// loads (lane i of a wave fills bytes 16i..16i+15 of a 1 KB run): a main run
+// is whole rows, a rope run 8 (or 16) rows.  Two buffers: the next tile's
+// loads are in flight while this tile is computed.
+#include <climits>
+
+#include "decode_geom.h"
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int kMlaPages = 1024;        // page ids staged in LDS for one chunk
+
+template <int DQK, int DV>
+struct MlaTile {
+    static constexpr int kMainPitch = 2 * DV;              // bytes per main row
+    static constexpr int kMainSlots = kMainPitch / 16;
+    static constexpr int kRopePitch = 2 * (DQK - DV);
+    static constexpr int kRopeSlots = kRopePitch / 16;
+    static constexpr int kMainBytes = kTile * kMainPitch;
+    static constexpr int kKBytes = kMainBytes + kTile * kRopePitch;
+    static constexpr int kMainRows = 1024 / kMainPitch;    // rows per 1 KB run
+    static constexpr int kRopeRows = 1024 / kRopePitch;
+    static constexpr int kMainRuns = kTile / kMainRows;
+    static constexpr int kRopeRuns = kTile / kRopeRows;
+    static_assert(kMainPitch % 256 == 0 && kMainPitch <= 1024 && kMainSlots >= 16,
+                  "main rows start on bank 0 and hold at least 16 slots");
+    static_assert(kRopeSlots == 8 || kRopeSlots == 4, "rope rows of 128 or 64 bytes");
+    // Main region: slot s of row r sits at slot s ^ mswz(r) (< 16, so inside
+    // the row).  K reads: 16 rows, one slot -> 16 distinct values of the
+    // swizzle = 16 bank groups.  V reads: 8 consecutive rows (4 per 16
+    // lanes), 32 bytes each -> mswz(r) >> 1 = r & 7 puts them on 8 distinct
+    // 32-byte groups.
+    static __device__ __forceinline__ int mswz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+    // Rope region (rows of 128 / 64 bytes, two / four rows per 256 bytes):
+    // (row parity, swizzle) resp. (row mod 4, swizzle) distinct over 16 rows.
+    static __device__ __forceinline__ int rswz(int r) {
+        return kRopeSlots == 8 ? (r >> 1) & 7 : (r >> 2) & 3;
+    }
+};
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: within each 16 lanes, lane i receives element e of the
+// 8 bytes lane 4e + i/4 addressed, element i % 4.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* p) {
+    const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16*)(p));
+    return __builtin_bit_cast(u32x2, r);
+}
+
+// Wait for this wave's direct-to-LDS loads (vmcnt 0; expcnt and lgkmcnt at
+// their maxima).
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Where the rows of a chunk of tiles come from.
+struct MlaChunk {
+    const uint8_t* kbase;     // k_pool + kv head offset (bytes)
+    const uint8_t* vbase;
+    int64_t page_bytes;
+    int tok_bytes;
+    int page_shift, first_page;
+    int t_begin, t_end;       // keys of the chunk inside the key range
+    const int* pages;         // LDS: block_table[b][first_page ...]
+};
+
+// Stage the K rows (and, without ALIAS, the V rows) of the tile at t0 into
+// LDS.  Runs: K main, K rope, then V main; wave wv issues runs wv, wv + NW,
+// ...  Rows outside [t_begin, t_end) load a row inside it (finite data; the
+// softmax masks them).
+template <int DQK, int DV, int NW, bool ALIAS>
+__device__ __forceinline__ void mla_stage(const MlaChunk& ch, int t0, bool uniform,
+                                          uint8_t* kt, uint8_t* vt, int wv, int lane) {
+    using T = MlaTile<DQK, DV>;
+    constexpr int kRuns = T::kMainRuns + T::kRopeRuns + (ALIAS ? 0 : T::kMainRuns);
+    constexpr int kPer = (kRuns + NW - 1) / NW;
+    const int pmask = (1 << ch.page_shift) - 1;
+    // page_size >= 32: the whole tile lies in one page
+    const int64_t tile_page = uniform ? ch.pages[(t0 >> ch.page_shift) - ch.first_page] : 0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int run = wv + k * NW;
+        if (run >= kRuns) break;
+        int row, off;
+        const uint8_t* base;
+        uint8_t* dst;
+        if (run < T::kMainRuns) {
+            row = run * T::kMainRows + lane / T::kMainSlots;
+            off = 16 * ((lane % T::kMainSlots) ^ T::mswz(row));
+            base = ch.kbase;
+            dst = kt + run * 1024;
+        } else if (run < T::kMainRuns + T::kRopeRuns) {
+            const int rr = run - T::kMainRuns;
+            row = rr * T::kRopeRows + lane / T::kRopeSlots;
+            off = 2 * DV + 16 * ((lane % T::kRopeSlots) ^ T::rswz(row));
+            base = ch.kbase;
+            dst = kt + T::kMainBytes + rr * 1024;
+        } else {
+            const int rr = run - T::kMainRuns - T::kRopeRuns;
+            row = rr * T::kMainRows + lane / T::kMainSlots;
+            off = 16 * ((lane % T::kMainSlots) ^ T::mswz(row));
+            base = ch.vbase;
+            dst = vt + rr * 1024;
+        }
+        const int t = min(max(t0 + row, ch.t_begin), ch.t_end - 1);
+        const int64_t page =
+            uniform ? tile_page : (int64_t)ch.pages[(t >> ch.page_shift) - ch.first_page];
+        const uint8_t* src =
+            base + page * ch.page_bytes + (uint32_t)((t & pmask) * ch.tok_bytes + off);
+        __builtin_amdgcn_global_load_lds(
+            (const void __attribute__((address_space(1)))*)(src),
+            (void __attribute__((address_space(3)))*)(dst), 16, 0, 0);
+    }
+}
+
+// Per-lane byte offsets of the operand reads inside a tile (rows 16kb + c
+// and 16h + 4grp + e share the swizzle of c and 4grp + e).
+//   K main, MFMA step ds (entries 32ds + 8grp ..): kmain[ds & 3] + 256 (ds >> 2)
+//   K rope, step ds: krope[ds]
+//   V^T block dblk (entries 16dblk ..): vtr[dblk & 7] + 256 (dblk >> 3)
+template <int DQK, int DV>
+struct MlaOffs {
+    static constexpr int kRopeSteps = (DQK - DV) / 32;
+    int kmain[4];
+    int krope[kRopeSteps];
+    int vtr[8];
+    __device__ __forceinline__ void init(int c, int grp, int lane) {
+        using T = MlaTile<DQK, DV>;
+        const int m = T::mswz(c);
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            kmain[v] = c * T::kMainPitch + 64 * (v ^ (m >> 2)) + 16 * (grp ^ (m & 3));
+        const int r = T::rswz(c);
+#pragma unroll
+        for (int ds = 0; ds < kRopeSteps; ++ds)
+            krope[ds] = T::kMainBytes + c * T::kRopePitch + 16 * ((4 * ds + grp) ^ r);
+        // transposing reads: lane (grp, 4e + q) reads row 4grp + e, entries
+        // 16dblk + 4q .. +3 (logical slot 2dblk + q/2, byte 8(q % 2) in it)
+        const int e = (lane & 15) >> 2, q = lane & 3;
+        const int row = 4 * grp + e;
+        const int mv = T::mswz(row);
+#pragma unroll
+        for (int v = 0; v < 8; ++v)
+            vtr[v] = row * T::kMainPitch + 32 * (v ^ (mv >> 1)) + 16 * ((q >> 1) ^ (mv & 1)) +
+                     8 * (q & 1);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Split pass
+// ---------------------------------------------------------------------------
+template <int DQK, int DV, int NW, bool ALIAS>
+__global__ __launch_bounds__(64 * NW) void mla_split_kernel(DecodeParams p) {
+    using T = MlaTile<DQK, DV>;
+    constexpr int KM = DV / 32;                // QK steps over the main entries
+    constexpr int KR = (DQK - DV) / 32;        // QK steps over the rope entries
+    constexpr int VE = DV / 16;                // PV MFMAs per tile
+
+    const int lane = threadIdx.x & 63;
+    const int wv = NW == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c = lane & 15, grp = lane >> 4;
+    const int cg = 16 * wv + c;                // this lane's query row (head of the kv head)
+    const int G = p.group;
+    const int64_t W = gridDim.x;
+    const int64_t w = blockIdx.x;
+
+    __shared__ int sm_pages[kMlaPages];
+    __shared__ __attribute__((aligned(1024))) uint8_t sm_k[2][T::kKBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t sm_v[ALIAS ? 1 : 2][ALIAS ? 16 : T::kMainBytes];
+
+    const int64_t N = total_tiles(p);
+    const int64_t r0 = range_start(w, N, W);
+    const int64_t r1 = range_start(w + 1, N, W);
+    if (r0 >= r1) {
+        // an empty range (N < W): the merge may read this block's slot 0
+        for (int i = threadIdx.x; i < p.rows; i += 64 * NW)
+            p.part_lse[part_row(p, w, 0) + i] = -INFINITY;
+        return;
+    }
+
+    int b;
+    int64_t seq_start;
+    find_seq(p, r0, b, seq_start);
+    SeqRange sr = seq_range(p, b);
+
+    const int chunk_tiles = ((kMlaPages - 2) << p.page_shift) / kTile;
+    const bool uniform = p.page_shift >= 5;
+
+    MlaOffs<DQK, DV> lo;
+    lo.init(c, grp, lane);
+
+    int64_t pos = r0;
+    int slot = 0;
+    while (pos < r1) {
+        const int n = sr.tiles;                               // > 0 here
+        const int kvh = (int)((pos - seq_start) / n);
+        const int i0 = (int)((pos - seq_start) % n);
+        const int64_t seg_end = seq_start + (int64_t)(kvh + 1) * n;
+        const int cnt = (int)(min(r1, seg_end) - pos);
+        const bool complete = (i0 == 0) && (cnt == n);
+        if (i0 == 0 && threadIdx.x == 0) {
+            // this block owns the segment's first tile: tell the merge which
+            // blocks cover it
+            const int64_t w_last = complete ? w : tile_owner(seg_end - 1, N, W);
+            *reinterpret_cast<int4*>(p.seg_rec + 4 * ((int64_t)b * p.num_kv_heads + kvh)) =
+                int4{(int)w, (int)w_last, slot, 0};
+        }
+
+        // ---- Q^T as B operands: column c is head kvh*G + cg; step ds covers
+        // entries 32ds + 8grp + j (main), DV + 32ds + 8grp + j (rope) ----
+        u32x4 qop[KM + KR];
+        {
+            const int cc = cg < p.rows ? cg : 0;
+            const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
+                                   (int64_t)b * p.q_stride_b + (int64_t)(kvh * G + cc) * DQK;
+#pragma unroll
+            for (int ds = 0; ds < KM + KR; ++ds) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 32 * ds + 8 * grp);
+                qop[ds] = cg < p.rows ? v : u32x4{0, 0, 0, 0};
+            }
+        }
+
+        // per-request cache descales of sequence b (uniform loads)
+        float vsc = p.v_scale, qk2 = p.qk_scale2, c1 = p.cap_c1;
+        if (p.k_desc) {
+            const float kd = p.k_desc[p.desc_per_seq ? b : 0];
+            qk2 *= kd;
+            c1 *= kd;
+        }
+        if (p.v_desc) vsc *= p.v_desc[p.desc_per_seq ? b : 0];
+        const float al2 = p.alibi ? p.alibi[kvh * G + (cg < p.rows ? cg : 0)] * kLog2e : 0.f;
+        const int qpos = sr.L - 1;                            // the query token's position
+
+        f32x4 o[VE];
+#pragma unroll
+        for (int e = 0; e < VE; ++e) o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float m = -INFINITY, l = 0.f;
+
+        MlaChunk ch;
+        ch.kbase = static_cast<const uint8_t*>(p.k_pool) + (int64_t)kvh * p.s_head * 2;
+        ch.vbase = static_cast<const uint8_t*>(p.v_pool) + (int64_t)kvh * p.s_head * 2;
+        ch.page_bytes = p.s_page * 2;
+        ch.tok_bytes = (int)(p.s_tok * 2);
+        ch.page_shift = p.page_shift;
+        ch.pages = sm_pages;
+
+        // ---- the piece's tiles, chunk by chunk (page list staged in LDS) ----
+        for (int c0 = 0; c0 < cnt; c0 += chunk_tiles) {
+            const int ct = min(cnt - c0, chunk_tiles);
+            const int tile0 = sr.base + (i0 + c0) * kTile;
+            ch.t_begin = max(tile0, sr.lo);
+            ch.t_end = min(tile0 + ct * kTile, sr.L);
+            ch.first_page = ch.t_begin >> p.page_shift;
+            const int n_pages = ((ch.t_end - 1) >> p.page_shift) - ch.first_page + 1;
+            __syncthreads();     // the previous chunk's readers are done with the list
+            {
+                const int32_t* bt = p.block_table + (int64_t)b * p.bt_stride + ch.first_page;
+                for (int i = threadIdx.x; i < n_pages; i += 64 * NW) sm_pages[i] = bt[i];
+            }
+            __syncthreads();
+
+            mla_stage<DQK, DV, NW, ALIAS>(ch, tile0, uniform, sm_k[0], sm_v[0], wv, lane);
+            wait_vm0();
+            __syncthreads();
+            for (int i = 0; i < ct; ++i) {
+                const int t0 = tile0 + i * kTile;
+                const uint8_t* kt = sm_k[i & 1];
+                const uint8_t* vt = ALIAS ? kt : sm_v[ALIAS ? 0 : (i & 1)];
+                if (i + 1 < ct)
+                    mla_stage<DQK, DV, NW, ALIAS>(ch, t0 + kTile, uniform, sm_k[(i + 1) & 1],
+                                                  sm_v[ALIAS ? 0 : ((i + 1) & 1)], wv, lane);
+
+                // ---- S^T = K Q^T: s[kb][j] = score of key t0 + 16kb + 4grp + j ----
+                f32x4 s[2];
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    const uint8_t* kr = kt + kb * 16 * T::kMainPitch;
+#pragma unroll
+                    for (int ds = 0; ds < KM; ++ds) {
+                        const u32x4 a = *reinterpret_cast<const u32x4*>(
+                            kr + lo.kmain[ds & 3] + 256 * (ds >> 2));
+                        s[kb] = mfma_bf16_16x16x32(a, qop[ds], s[kb]);
+                    }
+                    const uint8_t* rr = kt + kb * 16 * T::kRopePitch;
+#pragma unroll
+                    for (int ds = 0; ds < KR; ++ds) {
+                        const u32x4 a = *reinterpret_cast<const u32x4*>(rr + lo.krope[ds]);
+                        s[kb] = mfma_bf16_16x16x32(a, qop[KM + ds], s[kb]);
+                    }
+                }
+
+                // ---- scale / cap, ALiBi, mask; online softmax (log2 units) ----
+                const bool full = t0 >= ch.t_begin && t0 + kTile <= ch.t_end;
+                float tmax = -INFINITY;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int key = t0 + 16 * kb + 4 * grp + j;
+                        float v = s[kb][j];
+                        v = p.has_cap ? p.cap_c2 - 2.f * p.cap_c2 * fast_rcp(fast_exp2(v * c1) + 1.f)
+                                      : v * qk2;
+                        if (p.alibi) v += al2 * (float)(key - qpos);
+                        if (!full) v = (key >= ch.t_begin && key < ch.t_end) ? v : -INFINITY;
+                        s[kb][j] = v;
+                        tmax = fmaxf(tmax, v);
+                    }
+                tmax = col4_max(tmax);
+                // Lazy rescale: the reference max moves only when a score
+                // exceeds it by more than kSlack (log2 units), so p <= 2^kSlack.
+                constexpr float kSlack = 8.f;
+                const bool move = __any(tmax > m + kSlack);
+                const float m_new = move ? fmaxf(m, tmax) : m;
+                const float ms = m_new == -INFINITY ? 0.f : m_new;
+                const float alpha = fast_exp2(m - ms);
+                float psum = 0.f;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float pr = fast_exp2(s[kb][j] - ms);
+                        psum += pr;
+                        s[kb][j] = pr;
+                    }
+                l = l * alpha + psum;
+                m = m_new;
+                if (move) {
+#pragma unroll
+                    for (int e = 0; e < VE; ++e) o[e] *= alpha;
+                }
+                // P^T as the B operand: contraction slot (grp, jj) is key
+                // 4grp + jj (jj < 4) or 16 + 4grp + jj - 4
+                const u32x4 pop = {pack_bf16x2(s[0][0], s[0][1]), pack_bf16x2(s[0][2], s[0][3]),
+                                   pack_bf16x2(s[1][0], s[1][1]), pack_bf16x2(s[1][2], s[1][3])};
+
+                // ---- O^T += V^T P^T: two transposing reads per 16 entries ----
+#pragma unroll
+                for (int dblk = 0; dblk < VE; ++dblk) {
+                    const int off = lo.vtr[dblk & 7] + 256 * (dblk >> 3);
+                    const u32x2 v0 = lds_read_tr16(vt + off);
+                    const u32x2 v1 = lds_read_tr16(vt + 16 * T::kMainPitch + off);
+                    const u32x4 a = {v0.x, v0.y, v1.x, v1.y};
+                    o[dblk] = mfma_bf16_16x16x32(a, pop, o[dblk]);
+                }
+                wait_vm0();
+                __syncthreads();
+            }
+        }
+
+        // ---- finish the piece: row cg, entries 16dblk + 4grp + j ----
+        const float lt = col4_sum(l);
+        if (cg < p.rows) {
+            if (complete) {
+                // a sink logit joins the normaliser (no value row)
+                float den = lt;
+                if (p.sinks) den += fast_exp2(p.sinks[kvh * G + cg] * kLog2e - m);
+                const float inv = lt > 0.f ? vsc / den : 0.f;
+                uint16_t* orow = static_cast<uint16_t*>(p.out) + (int64_t)b * p.out_stride_b +
+                                 (int64_t)(kvh * G + cg) * DV;
+#pragma unroll
+                for (int dblk = 0; dblk < VE; ++dblk)
+                    *reinterpret_cast<u32x2*>(orow + 16 * dblk + 4 * grp) =
+                        u32x2{pack_bf16x2(o[dblk][0] * inv, o[dblk][1] * inv),
+                              pack_bf16x2(o[dblk][2] * inv, o[dblk][3] * inv)};
+            } else {
+                const int64_t row = part_row(p, w, slot) + cg;
+                const float inv = lt > 0.f ? vsc / lt : 0.f;
+                float* po = p.part_o + row * DV;
+#pragma unroll
+                for (int dblk = 0; dblk < VE; ++dblk)
+                    *reinterpret_cast<f32x4*>(po + 16 * dblk + 4 * grp) = o[dblk] * inv;
+                if (grp == 0) p.part_lse[row] = lt > 0.f ? m + __log2f(lt) : -INFINITY;
+            }
+        }
+
+        // ---- next piece ----
+        pos += cnt;
+        slot = 1;
+        if (pos < r1 && pos == seq_start + (int64_t)n * p.num_kv_heads) {
+            seq_start = pos;
+            do {
+                ++b;
+                sr = seq_range(p, b);
+            } while (sr.tiles == 0);
+        }
+    }
+}
+
+using MlaFn = void (*)(DecodeParams);
+
+template <int DQK, int DV, bool ALIAS>
+MlaFn mla_by_waves(int nw) {
+    switch (nw) {
+        case 1: return mla_split_kernel<DQK, DV, 1, ALIAS>;
+        case 2: return mla_split_kernel<DQK, DV, 2, ALIAS>;
+        case 4: return mla_split_kernel<DQK, DV, 4, ALIAS>;
+        case 8: return mla_split_kernel<DQK, DV, 8, ALIAS>;
+        default: return nullptr;
+    }
+}
+
+MlaFn mla_kernel(int dqk, int dv, bool alias, int nw) {
+    if (dqk == 576 && dv == 512)
+        return alias ? mla_by_waves<576, 512, true>(nw) : mla_by_waves<576, 512, false>(nw);
+    if (dqk == 288 && dv == 256)
+        return alias ? mla_by_waves<288, 256, true>(nw) : mla_by_waves<288, 256, false>(nw);
+    return nullptr;
+}
+
+}  // namespace
+
+hipError_t launch_mla_decode(const DecodeParams& p, int head_dim, int head_dim_v, bool alias,
+                             int waves_per_block, int workers, hipStream_t stream) {
+    const MlaFn f = mla_kernel(head_dim, head_dim_v, alias, waves_per_block);
+    if (!f) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(f, dim3(workers), dim3(64 * waves_per_block), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t mla_blocks_per_cu(int head_dim, int head_dim_v, bool alias, int waves_per_block,
+                             int* out) {
+    const MlaFn f = mla_kernel(head_dim, head_dim_v, alias, waves_per_block);
+    if (!f) return hipErrorInvalidValue;
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, reinterpret_cast<const void*>(f),
+                                                        64 * waves_per_block, 0);
+}
+
+}  // namespace pa

@@ -31,7 +31,7 @@ struct DecodeParams {
     int32_t num_seqs;
     int32_t num_q_heads;
     int32_t num_kv_heads;
-    int32_t group;            // G = Hq / Hkv (1..16)
+    int32_t group;            // G = Hq / Hkv (1..16; latent cache: 1..128)
     int32_t q_len;            // query rows per sequence (1: decode; > 1: verify)
     int32_t rows;             // MFMA columns used: G * q_len <= 16; column c is query
                               // token c / G, head c % G of the kv head
@@ -50,7 +50,7 @@ struct DecodeParams {
     int32_t desc_per_seq;
     void* out;                // bf16 [B, Hq, D], row stride out_stride_b
     int64_t out_stride_b;
-    float* part_o;            // [workers, 2, rows, D]: partial of a segment a wave covers in part
+    float* part_o;            // [workers, 2, rows, Dv]: partial of a segment a wave covers in part
     float* part_lse;          // [workers, 2, rows] (log2 domain)
     int32_t* seg_rec;         // [B * Hkv][4]: for a segment with keys, the waves owning its
                               // first and last tile and the first one's slot (written by
@@ -126,6 +126,13 @@ hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, int num_seqs
 hipError_t decode_blocks_per_cu(int head_dim, bool fp8, bool uniform_pages, int waves_per_block,
                                 int* out);
 constexpr int kMaxDecodeRows = 64;   // query rows per kv head: 16 per wave, 4 waves
+// Latent-cache decode (head_dim_v < head_dim, bf16): the split pass; the
+// merge is launch_decode_merge with head_dim_v.  alias: v_pool == k_pool.
+hipError_t launch_mla_decode(const DecodeParams& p, int head_dim, int head_dim_v, bool alias,
+                             int waves_per_block, int workers, hipStream_t stream);
+hipError_t mla_blocks_per_cu(int head_dim, int head_dim_v, bool alias, int waves_per_block,
+                             int* out);
+constexpr int kMaxLatentGroup = 128;   // query heads per kv head: 16 per wave, 8 waves
 hipError_t launch_gather(const GatherParams& p, int head_dim, bool fp8, hipStream_t stream);
 // Extend: a scan of the items' tile counts, `workers` persistent blocks, and a
 // merge of the items several blocks cover.

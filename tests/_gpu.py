@@ -22,7 +22,8 @@ def run_decode(case, num_splits=None, tensors=None, pool_view=None):
         kp, vp = pool_view(kp), pool_view(vp)
     ns = case.num_splits if num_splits is None else num_splits
     pl = pa.decode_plan(t["q"], kp, t["block_table"], case.max_kv_len,
-                        window=case.window, num_splits=ns)
+                        window=case.window, num_splits=ns,
+                        head_dim_v=getattr(case, "head_dim_v", 0))
     out = pa.decode(pl, t["q"], kp, vp, t["block_table"], t["seq_lens"], case.scale,
                     softcap=case.softcap, window=case.window, k_scale=case.k_scale,
                     v_scale=case.v_scale, **extras(t))

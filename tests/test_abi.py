@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_runtime():
-    assert pa.lib().paged_attn_abi_version() == 2
+    assert pa.lib().paged_attn_abi_version() == B.ABI_VERSION == 3
     assert pa.lib().paged_attn_hip_runtime_path().decode().endswith(".so")
 
 
@@ -51,7 +51,7 @@ def test_status_strings():
 def prob(**kw):
     d = dict(mode=0, num_seqs=4, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
              kv_dtype=0, window=0, max_pages_per_seq=256, max_kv_len=4096, total_q=0,
-             max_q_len=0, num_splits=0)
+             max_q_len=0, num_splits=0, head_dim_v=0)
     d.update(kw)
     return B.PaProblem(**d)
 
@@ -80,6 +80,21 @@ def plan_status(**kw):
     (dict(mode=2, max_q_len=16), OK),            # 64 rows per kv head: 4 waves
     (dict(mode=2, max_q_len=17), UNSUP),         # 68 rows per kv head
     (dict(mode=2, max_q_len=0), SHAPE),
+    # latent cache: values the first head_dim_v entries of the key row
+    (dict(head_dim=576, head_dim_v=512, num_q_heads=16, num_kv_heads=1), OK),
+    (dict(head_dim=288, head_dim_v=256, num_q_heads=128, num_kv_heads=1), OK),
+    (dict(head_dim=576, head_dim_v=512, num_q_heads=48, num_kv_heads=1), OK),   # G = 48
+    (dict(head_dim=576, head_dim_v=512, num_q_heads=129, num_kv_heads=1), UNSUP),
+    (dict(head_dim=576, head_dim_v=256, num_q_heads=16, num_kv_heads=1), UNSUP),
+    (dict(head_dim=512, head_dim_v=448, num_q_heads=16, num_kv_heads=1), UNSUP),
+    (dict(head_dim=576, head_dim_v=512, num_q_heads=16, num_kv_heads=1, kv_dtype=1), UNSUP),
+    (dict(head_dim=576, head_dim_v=512, num_q_heads=16, num_kv_heads=1, mode=2,
+          max_q_len=2), UNSUP),
+    (dict(head_dim=576, head_dim_v=512, num_q_heads=16, num_kv_heads=1, mode=1,
+          total_q=10, max_q_len=5), UNSUP),
+    (dict(head_dim_v=128), OK),                  # = head_dim: ordinary decode
+    (dict(head_dim_v=64), UNSUP),                # narrower values need D 576 / 288
+    (dict(head_dim_v=-1), SHAPE),
 ])
 def test_plan_validation(kw, status):
     assert plan_status(**kw)[0] == status
@@ -104,6 +119,18 @@ def test_plan_decisions():
     st, pl = plan_status(num_seqs=0)
     assert st == OK
     assert "splits=" in pa.Plan(pl).describe()
+
+
+def test_plan_latent_decisions():
+    """Latent cache: one wave per 16 query heads, rounded up to 1, 2, 4 or 8
+    waves; partial rows of head_dim_v floats."""
+    for G, nw in ((1, 1), (16, 1), (17, 2), (32, 2), (48, 4), (64, 4), (100, 8), (128, 8)):
+        st, pl = plan_status(head_dim=576, head_dim_v=512, num_q_heads=G, num_kv_heads=1)
+        assert st == OK and pl.waves_per_block == nw, (G, pl.waves_per_block)
+        assert pl.workspace_bytes >= pl.num_splits * 2 * G * 513 * 4
+    st, pl = plan_status(head_dim=576, head_dim_v=512, num_q_heads=16, num_kv_heads=1)
+    assert pl.num_splits == 256 * 2
+    assert "D=576 Dv=512" in pa.Plan(pl).describe()
 
 
 # ---- decode argument validation: fake, never dereferenced, pointers ----
@@ -162,6 +189,24 @@ def decode_status(plan_kw=None, fn="paged_attn_decode", **kw):
 @pytest.mark.parametrize("fn", DECODE_FNS)
 def test_decode_validation(fn, kw, status):
     assert decode_status(fn=fn, **kw) == status
+
+
+LATENT = dict(head_dim=576, head_dim_v=512, num_q_heads=16, num_kv_heads=1)
+
+
+def test_latent_decode_validation():
+    """q rows of Hq x 576, out rows of Hq x 512; the gather test aid takes
+    ordinary rows only."""
+    lat = dict(plan_kw=LATENT, q_stride_b=16 * 576, sp=16 * 576, st=576, sh=576,
+               out_stride_b=16 * 512)
+    assert decode_status(**{**lat, "q": None}) == NULLP
+    assert decode_status(**{**lat, "q_stride_b": 16 * 576 - 8}) == SHAPE
+    assert decode_status(**{**lat, "out_stride_b": 16 * 512 - 8}) == SHAPE
+    assert decode_status(**{**lat, "ws_bytes": 16}) == WS
+    st, pl = plan_status(**LATENT)
+    v = ctypes.c_void_p(A)
+    assert pa.lib().paged_attn_gather(ctypes.byref(pl), v, v, 16 * 576, 576, 576, 10, v, 256,
+                                      v, v, v, None) == UNSUP
 
 
 def test_decode_empty_batch_launches_nothing():
