@@ -14,6 +14,9 @@ the 256 MB last-level cache.  Prints one JSON line.
 
 Workloads 1-4 are the decode workloads of paged_gqa_attention_02_amd.inputs;
 5 is the prefix-prefill/extend workload (MFMA-bound; reports TFLOP/s).
+`--op verify` runs q_len query tokens per sequence on a decode workload,
+`--op mla` the latent-cache decode (576/512 head dims), `--op append` the
+KV-cache append.
 """
 import argparse
 import hashlib
@@ -30,6 +33,7 @@ MALL_BYTES = 256 << 20
 # the sources the split-pass kernel is compiled from (counter figures taken
 # from other sources are not reported)
 DECODE_SPLIT_SOURCES = ["decode.hip", "decode_geom.h", "pa_device.h", "pa_internal.h"]
+MLA_SPLIT_SOURCES = ["mla.hip", "decode_geom.h", "pa_device.h", "pa_internal.h"]
 
 
 def parse():
@@ -43,11 +47,15 @@ def parse():
     ap.add_argument("--splits", type=int, default=0, help="force the decode split cap")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU-baseline budget (0 disables the oracle leg)")
-    ap.add_argument("--op", default="attention", choices=["attention", "append", "verify"],
+    ap.add_argument("--op", default="attention",
+                    choices=["attention", "append", "verify", "mla"],
                     help="append: KV-cache append of the extend workload's new tokens; "
                          "verify: --q-len query tokens per sequence on a decode workload")
     ap.add_argument("--q-len", type=int, default=4,
                     help="query tokens per sequence for --op verify (1 + speculative tokens)")
+    ap.add_argument("--mla-heads", type=int, default=16,
+                    help="--op mla: query heads over the one latent kv head")
+    ap.add_argument("--mla-batch", type=int, default=128, help="--op mla: sequences")
     ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8_e4m3"],
                     help="cache element type for --op append")
     ap.add_argument("--copy-probe", action="store_true",
@@ -131,16 +139,20 @@ def time_first_pass(torch, first, second, K):
     return sum(a.elapsed_time(b) for a, b in ev) / K
 
 
-def bench_decode(args, torch, pa, I):
+def bench_decode(args, torch, pa, I, case=None):
     dev = "cuda:0"
-    case = I.decode_config(args.workload, page_size=args.page_size)
+    if case is None:
+        case = I.decode_config(args.workload, page_size=args.page_size)
+    latent = case.dv != case.head_dim
     alg = case.algorithmic_bytes()
     copies = max(2, math.ceil(2 * MALL_BYTES / max(case.kv_bytes(), 1)) + 1)
     tensors = [I.decode_tensors(case, dev) for _ in range(copies)]
     t0 = tensors[0]
     plan = pa.decode_plan(t0["q"], t0["k_pool"], t0["block_table"], case.max_kv_len,
-                          window=case.window, num_splits=args.splits)
-    out = torch.empty_like(t0["q"])
+                          window=case.window, num_splits=args.splits,
+                          head_dim_v=case.dv if latent else 0)
+    out = torch.empty(case.batch, case.num_q_heads, case.dv, dtype=torch.bfloat16,
+                      device=dev)
     ws = pa.workspace_for(plan, dev)
 
     def call(fn, i):
@@ -161,7 +173,8 @@ def bench_decode(args, torch, pa, I):
     split_ms = time_first_pass(torch, lambda i: call(pa.decode_split, i),
                                lambda i: call(pa.decode_merge, i), K)
     achieved = alg / (split_ms * 1e-3) / 1e9
-    traffic = traffic_for("decode_split", case.name, DECODE_SPLIT_SOURCES)
+    traffic = traffic_for("decode_split", case.name,
+                          MLA_SPLIT_SOURCES if latent else DECODE_SPLIT_SOURCES)
     res = {
         "metric": "paged-attn decode KV GB/s (fraction of HBM peak) + us/call on 1 MI355X",
         "value": alg / (ms_step * 1e-3) / 1e9,
@@ -173,10 +186,11 @@ def bench_decode(args, torch, pa, I):
         "data": "synthetic",
         "config": {"workload": f"{case.name} decode", "batch": case.batch,
                    "num_q_heads": case.num_q_heads, "num_kv_heads": case.num_kv_heads,
-                   "head_dim": case.head_dim, "page_size": case.page_size,
+                   "head_dim": case.head_dim, "head_dim_v": case.dv,
+                   "page_size": case.page_size,
                    "kv_dtype": case.kv_dtype, "window": case.window,
                    "softcap": case.softcap, "total_tokens": int(case.seq_lens.sum()),
-                   "seed": args.workload, "input_copies": copies},
+                   "seed": 6 if latent else args.workload, "input_copies": copies},
         "us_per_call": ev_ms * 1e3, "split_us_per_launch": split_ms * 1e3,
         "hbm_frac": (alg / (ms_step * 1e-3) / 1e9) / HBM_PEAK_GBS,
         "algorithmic_bytes": alg, "kv_bytes": case.kv_bytes(),
@@ -238,10 +252,11 @@ def bench_verify(args, torch, pa, I):
         "config": {"workload": f"{case.name} verify, q_len {ql}", "batch": case.batch,
                    "q_len": ql, "rows_per_kv_head": rows,
                    "num_q_heads": case.num_q_heads, "num_kv_heads": case.num_kv_heads,
-                   "head_dim": case.head_dim, "page_size": case.page_size,
+                   "head_dim": case.head_dim, "head_dim_v": case.dv,
+                   "page_size": case.page_size,
                    "kv_dtype": case.kv_dtype, "window": case.window,
                    "softcap": case.softcap, "total_tokens": int(case.seq_lens.sum()),
-                   "seed": args.workload, "input_copies": copies},
+                   "seed": 6 if latent else args.workload, "input_copies": copies},
         "us_per_call": ev_ms * 1e3, "algorithmic_bytes": alg,
         "plan": plan.describe(),
         "roofline": {"bound": "hbm", "kernel": "decode_split + merge (whole call)",
@@ -375,6 +390,10 @@ def main():
         if args.workload == 5:
             sys.exit("bench.py: --op verify runs on a decode workload (1-4)")
         res = bench_verify(args, torch, pa, I)
+    elif args.op == "mla":
+        res = bench_decode(args, torch, pa, I,
+                           case=I.mla_config(args.mla_heads, args.mla_batch,
+                                             args.page_size or 64))
     elif args.workload == 5:
         res = bench_extend(args, torch, pa, I)
     else:
