@@ -194,8 +194,13 @@ __global__ __launch_bounds__(64 * NW) void mla_split_kernel(DecodeParams p) {
     const int64_t w = blockIdx.x;
 
     __shared__ int sm_pages[kMlaPages];
-    __shared__ __attribute__((aligned(1024))) uint8_t sm_k[2][T::kKBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t sm_v[ALIAS ? 1 : 2][ALIAS ? 16 : T::kMainBytes];
+    // Two buffers, each its own LDS object: the compiler then knows that the
+    // next tile's direct-to-LDS loads do not write the buffer being read, and
+    // issues no wait for them before this tile's operand reads.
+    __shared__ __attribute__((aligned(1024))) uint8_t sm_k0[T::kKBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t sm_k1[T::kKBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t sm_v0[ALIAS ? 16 : T::kMainBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t sm_v1[ALIAS ? 16 : T::kMainBytes];
 
     const int64_t N = total_tiles(p);
     const int64_t r0 = range_start(w, N, W);
@@ -288,35 +293,46 @@ __global__ __launch_bounds__(64 * NW) void mla_split_kernel(DecodeParams p) {
             }
             __syncthreads();
 
-            mla_stage<DQK, DV, NW, ALIAS>(ch, tile0, uniform, sm_k[0], sm_v[0], wv, lane);
+            mla_stage<DQK, DV, NW, ALIAS>(ch, tile0, uniform, sm_k0, sm_v0, wv, lane);
             wait_vm0();
             __syncthreads();
             for (int i = 0; i < ct; ++i) {
                 const int t0 = tile0 + i * kTile;
-                const uint8_t* kt = sm_k[i & 1];
-                const uint8_t* vt = ALIAS ? kt : sm_v[ALIAS ? 0 : (i & 1)];
+                const uint8_t* kt = (i & 1) ? sm_k1 : sm_k0;
+                const uint8_t* vt = ALIAS ? kt : ((i & 1) ? sm_v1 : sm_v0);
                 if (i + 1 < ct)
-                    mla_stage<DQK, DV, NW, ALIAS>(ch, t0 + kTile, uniform, sm_k[(i + 1) & 1],
-                                                  sm_v[ALIAS ? 0 : ((i + 1) & 1)], wv, lane);
+                    mla_stage<DQK, DV, NW, ALIAS>(ch, t0 + kTile, uniform,
+                                                  (i & 1) ? sm_k0 : sm_k1,
+                                                  (i & 1) ? sm_v0 : sm_v1, wv, lane);
 
-                // ---- S^T = K Q^T: s[kb][j] = score of key t0 + 16kb + 4grp + j ----
-                f32x4 s[2];
+                // ---- S^T = K Q^T: s[kb][j] = score of key t0 + 16kb + 4grp + j.
+                // A wave is alone on its SIMD (the LDS tiles allow two blocks
+                // per compute unit), so nothing hides LDS latency but this
+                // wave's own queue: all operand reads of the tile are issued
+                // before the MFMAs, and the two key halves' accumulation
+                // chains alternate. ----
+                f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+                constexpr int kKB = (KM + KR) % 6 == 0 ? 6 : 3;   // contraction steps per batch
+                static_assert((KM + KR) % kKB == 0, "whole batches");
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    const uint8_t* kr = kt + kb * 16 * T::kMainPitch;
+                for (int d0 = 0; d0 < KM + KR; d0 += kKB) {
+                    u32x4 ka[2][kKB];
 #pragma unroll
-                    for (int ds = 0; ds < KM; ++ds) {
-                        const u32x4 a = *reinterpret_cast<const u32x4*>(
-                            kr + lo.kmain[ds & 3] + 256 * (ds >> 2));
-                        s[kb] = mfma_bf16_16x16x32(a, qop[ds], s[kb]);
-                    }
-                    const uint8_t* rr = kt + kb * 16 * T::kRopePitch;
+                    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                    for (int ds = 0; ds < KR; ++ds) {
-                        const u32x4 a = *reinterpret_cast<const u32x4*>(rr + lo.krope[ds]);
-                        s[kb] = mfma_bf16_16x16x32(a, qop[KM + ds], s[kb]);
-                    }
+                        for (int u = 0; u < kKB; ++u) {
+                            const int ds = d0 + u;
+                            ka[kb][u] = *reinterpret_cast<const u32x4*>(
+                                ds < KM ? kt + kb * 16 * T::kMainPitch + lo.kmain[ds & 3] +
+                                              256 * (ds >> 2)
+                                        : kt + kb * 16 * T::kRopePitch + lo.krope[ds - KM]);
+                        }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int u = 0; u < kKB; ++u)
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb)
+                            s[kb] = mfma_bf16_16x16x32(ka[kb][u], qop[d0 + u], s[kb]);
                 }
 
                 // ---- scale / cap, ALiBi, mask; online softmax (log2 units) ----
@@ -363,14 +379,23 @@ __global__ __launch_bounds__(64 * NW) void mla_split_kernel(DecodeParams p) {
                 const u32x4 pop = {pack_bf16x2(s[0][0], s[0][1]), pack_bf16x2(s[0][2], s[0][3]),
                                    pack_bf16x2(s[1][0], s[1][1]), pack_bf16x2(s[1][2], s[1][3])};
 
-                // ---- O^T += V^T P^T: two transposing reads per 16 entries ----
+                // ---- O^T += V^T P^T: two transposing reads per 16 entries, a
+                // batch of kVB blocks' reads ahead of their MFMAs ----
+                constexpr int kVB = 8;
 #pragma unroll
-                for (int dblk = 0; dblk < VE; ++dblk) {
-                    const int off = lo.vtr[dblk & 7] + 256 * (dblk >> 3);
-                    const u32x2 v0 = lds_read_tr16(vt + off);
-                    const u32x2 v1 = lds_read_tr16(vt + 16 * T::kMainPitch + off);
-                    const u32x4 a = {v0.x, v0.y, v1.x, v1.y};
-                    o[dblk] = mfma_bf16_16x16x32(a, pop, o[dblk]);
+                for (int d0 = 0; d0 < VE; d0 += kVB) {
+                    u32x4 va[kVB];
+#pragma unroll
+                    for (int u = 0; u < kVB; ++u) {
+                        const int dblk = d0 + u;
+                        const int off = lo.vtr[dblk & 7] + 256 * (dblk >> 3);
+                        const u32x2 v0 = lds_read_tr16(vt + off);
+                        const u32x2 v1 = lds_read_tr16(vt + 16 * T::kMainPitch + off);
+                        va[u] = u32x4{v0.x, v0.y, v1.x, v1.y};
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int u = 0; u < kVB; ++u) o[d0 + u] = mfma_bf16_16x16x32(va[u], pop, o[d0 + u]);
                 }
                 wait_vm0();
                 __syncthreads();
