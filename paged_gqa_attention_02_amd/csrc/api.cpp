@@ -22,7 +22,6 @@ namespace {
 using namespace pa;
 
 constexpr int kDefaultCus = 256;        // MI355X
-constexpr int kDefaultWavesPerCu = 8;   // split-pass occupancy when no device is queried
 constexpr int kDefaultExtendBlocksPerCu = 2;   // extend occupancy when no device is queried
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -234,7 +233,10 @@ pa_status paged_attn_plan(const pa_problem* prob, int hip_device, pa_plan* out) 
         } else {
             // latent cache: two blocks of at most two waves share a compute
             // unit's LDS (the plan assumes v_pool == k_pool)
-            int per_cu = is_latent(pr) ? (nw <= 2 ? 2 : 1) : kDefaultWavesPerCu / nw;
+            int per_cu = is_latent(pr) ? (nw <= 2 ? 2 : 1)
+                                       : 4 * split_waves_per_simd(pr.head_dim,
+                                                                  pr.kv_dtype == PA_KV_FP8_E4M3,
+                                                                  nw) / nw;
             if (hip_device >= 0) {
                 int cur = -1;
                 if (hipGetDevice(&cur) != hipSuccess) return PA_ERR_HIP;

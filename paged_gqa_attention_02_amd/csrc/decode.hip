@@ -431,7 +431,8 @@ __device__ __forceinline__ void tile_pv(Acc<D>& A, VRegs<D, FP8>& R, u32x4 pop,
 // Split pass: persistent waves, one contiguous range of tiles each
 // ---------------------------------------------------------------------------
 template <int D, bool FP8, bool UNIFORM, int SCORE, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(kDecodeOccupancy)))
+__global__ __launch_bounds__(64 * NW)
+__attribute__((amdgpu_waves_per_eu(split_waves_per_simd(D, FP8, NW))))
 void decode_split_kernel(DecodeParams p) {
     constexpr int KK = D / 32;                  // QK MFMAs per 16-token half
     constexpr int VE = D / 16;                  // PV MFMAs per tile

@@ -15,6 +15,14 @@ constexpr int kMaxWorkers = 1 << 20;
 #define PA_DECODE_OCCUPANCY 2
 #endif
 constexpr int kDecodeOccupancy = PA_DECODE_OCCUPANCY;   // waves per SIMD the kernel must allow
+// Waves per SIMD a split-pass variant is compiled for.  The bf16 D = 128
+// one-wave-block variant gets the SIMD's registers to itself (1024 persistent
+// waves on 256 compute units): it streams as fast with half the waves, and
+// half as many range boundaries leave fewer partials to merge.  The plan asks
+// the runtime for the occupancy of the variant it launches.
+constexpr int split_waves_per_simd(int head_dim, bool fp8, int waves_per_block) {
+    return (head_dim == 128 && !fp8 && waves_per_block == 1) ? 1 : kDecodeOccupancy;
+}
 // Page-table entries staged in LDS for one chunk of a wave's range: a chunk
 // of T tokens touches at most T/page_size + 2 pages.
 constexpr int kMaxSplitPages = 2080;
