@@ -256,7 +256,7 @@ def bench_verify(args, torch, pa, I):
                    "page_size": case.page_size,
                    "kv_dtype": case.kv_dtype, "window": case.window,
                    "softcap": case.softcap, "total_tokens": int(case.seq_lens.sum()),
-                   "seed": 6 if latent else args.workload, "input_copies": copies},
+                   "seed": args.workload, "input_copies": copies},
         "us_per_call": ev_ms * 1e3, "algorithmic_bytes": alg,
         "plan": plan.describe(),
         "roofline": {"bound": "hbm", "kernel": "decode_split + merge (whole call)",
