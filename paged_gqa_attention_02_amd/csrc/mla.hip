@@ -312,27 +312,45 @@ __global__ __launch_bounds__(64 * NW) void mla_split_kernel(DecodeParams p) {
                 // before the MFMAs, and the two key halves' accumulation
                 // chains alternate. ----
                 f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-                constexpr int kKB = (KM + KR) % 6 == 0 ? 6 : 3;   // contraction steps per batch
-                static_assert((KM + KR) % kKB == 0, "whole batches");
+                // (batched reads where the registers allow: one- and two-wave
+                // blocks over one pool; larger blocks are held to fewer
+                // registers and read each operand right before its MFMA)
+                constexpr bool kBatch = NW <= 2 && ALIAS;
+                if constexpr (kBatch) {
+                    constexpr int kKB = (KM + KR) % 6 == 0 ? 6 : 3;   // contraction steps per batch
+                    static_assert((KM + KR) % kKB == 0, "whole batches");
 #pragma unroll
-                for (int d0 = 0; d0 < KM + KR; d0 += kKB) {
-                    u32x4 ka[2][kKB];
+                    for (int d0 = 0; d0 < KM + KR; d0 += kKB) {
+                        u32x4 ka[2][kKB];
 #pragma unroll
-                    for (int kb = 0; kb < 2; ++kb)
+                        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                        for (int u = 0; u < kKB; ++u) {
-                            const int ds = d0 + u;
-                            ka[kb][u] = *reinterpret_cast<const u32x4*>(
+                            for (int u = 0; u < kKB; ++u) {
+                                const int ds = d0 + u;
+                                ka[kb][u] = *reinterpret_cast<const u32x4*>(
+                                    ds < KM ? kt + kb * 16 * T::kMainPitch + lo.kmain[ds & 3] +
+                                                  256 * (ds >> 2)
+                                            : kt + kb * 16 * T::kRopePitch + lo.krope[ds - KM]);
+                            }
+                        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                        for (int u = 0; u < kKB; ++u)
+#pragma unroll
+                            for (int kb = 0; kb < 2; ++kb)
+                                s[kb] = mfma_bf16_16x16x32(ka[kb][u], qop[d0 + u], s[kb]);
+                    }
+                } else {
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                        for (int ds = 0; ds < KM + KR; ++ds) {
+                            const u32x4 a = *reinterpret_cast<const u32x4*>(
                                 ds < KM ? kt + kb * 16 * T::kMainPitch + lo.kmain[ds & 3] +
                                               256 * (ds >> 2)
                                         : kt + kb * 16 * T::kRopePitch + lo.krope[ds - KM]);
+                            s[kb] = mfma_bf16_16x16x32(a, qop[ds], s[kb]);
                         }
-                    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                    for (int u = 0; u < kKB; ++u)
-#pragma unroll
-                        for (int kb = 0; kb < 2; ++kb)
-                            s[kb] = mfma_bf16_16x16x32(ka[kb][u], qop[d0 + u], s[kb]);
+                    }
                 }
 
                 // ---- scale / cap, ALiBi, mask; online softmax (log2 units) ----
@@ -379,23 +397,32 @@ __global__ __launch_bounds__(64 * NW) void mla_split_kernel(DecodeParams p) {
                 const u32x4 pop = {pack_bf16x2(s[0][0], s[0][1]), pack_bf16x2(s[0][2], s[0][3]),
                                    pack_bf16x2(s[1][0], s[1][1]), pack_bf16x2(s[1][2], s[1][3])};
 
-                // ---- O^T += V^T P^T: two transposing reads per 16 entries, a
-                // batch of kVB blocks' reads ahead of their MFMAs ----
-                constexpr int kVB = 8;
+                // ---- O^T += V^T P^T: two transposing reads per 16 entries ----
+                if constexpr (kBatch) {
+                    constexpr int kVB = 8;
 #pragma unroll
-                for (int d0 = 0; d0 < VE; d0 += kVB) {
-                    u32x4 va[kVB];
+                    for (int d0 = 0; d0 < VE; d0 += kVB) {
+                        u32x4 va[kVB];
 #pragma unroll
-                    for (int u = 0; u < kVB; ++u) {
-                        const int dblk = d0 + u;
+                        for (int u = 0; u < kVB; ++u) {
+                            const int dblk = d0 + u;
+                            const int off = lo.vtr[dblk & 7] + 256 * (dblk >> 3);
+                            const u32x2 v0 = lds_read_tr16(vt + off);
+                            const u32x2 v1 = lds_read_tr16(vt + 16 * T::kMainPitch + off);
+                            va[u] = u32x4{v0.x, v0.y, v1.x, v1.y};
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                        for (int u = 0; u < kVB; ++u) o[d0 + u] = mfma_bf16_16x16x32(va[u], pop, o[d0 + u]);
+                    }
+                } else {
+#pragma unroll
+                    for (int dblk = 0; dblk < VE; ++dblk) {
                         const int off = lo.vtr[dblk & 7] + 256 * (dblk >> 3);
                         const u32x2 v0 = lds_read_tr16(vt + off);
                         const u32x2 v1 = lds_read_tr16(vt + 16 * T::kMainPitch + off);
-                        va[u] = u32x4{v0.x, v0.y, v1.x, v1.y};
+                        o[dblk] = mfma_bf16_16x16x32(u32x4{v0.x, v0.y, v1.x, v1.y}, pop, o[dblk]);
                     }
-                    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                    for (int u = 0; u < kVB; ++u) o[d0 + u] = mfma_bf16_16x16x32(va[u], pop, o[d0 + u]);
                 }
                 wait_vm0();
                 __syncthreads();
