@@ -324,12 +324,43 @@ struct LaneOffs {
     }
 };
 
-typedef short v4i16 __attribute__((ext_vector_type(4)));
+// LDS byte address (32 bits) of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
 
-__device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* p) {
-    const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4i16*)(p));
-    return __builtin_bit_cast(u32x2, r);
+// Eight transposing reads issued together and waited for inside one asm
+// block, so every output is complete when the block ends.  Through the
+// builtin the compiler has no alias information for these reads, and it
+// waits for every direct-to-LDS load in flight before them -- here the next
+// tile's loads into the other buffer, which P*V of this tile does not need.
+// Nothing writes the bytes read: this tile's loads completed before the
+// barrier that precedes its reads.
+__device__ __forceinline__ void lds_read_tr16_x8(u32x2 (&out)[8], const uint32_t (&a)[8]) {
+    uint64_t r0, r1, r2, r3, r4, r5, r6, r7;
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %9\n\t"
+        "ds_read_b64_tr_b16 %2, %10\n\t"
+        "ds_read_b64_tr_b16 %3, %11\n\t"
+        "ds_read_b64_tr_b16 %4, %12\n\t"
+        "ds_read_b64_tr_b16 %5, %13\n\t"
+        "ds_read_b64_tr_b16 %6, %14\n\t"
+        "ds_read_b64_tr_b16 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6),
+          "=&v"(r7)
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
+          "v"(a[7])
+        : "memory");
+    out[0] = __builtin_bit_cast(u32x2, r0);
+    out[1] = __builtin_bit_cast(u32x2, r1);
+    out[2] = __builtin_bit_cast(u32x2, r2);
+    out[3] = __builtin_bit_cast(u32x2, r3);
+    out[4] = __builtin_bit_cast(u32x2, r4);
+    out[5] = __builtin_bit_cast(u32x2, r5);
+    out[6] = __builtin_bit_cast(u32x2, r6);
+    out[7] = __builtin_bit_cast(u32x2, r7);
 }
 
 // Logit (log2 domain) of a raw score for kScale / kCap.  SPLIT: the tile
@@ -466,17 +497,28 @@ __device__ __forceinline__ void tile_compute(const uint8_t* kl, const uint8_t* v
     tile_softmax<D, MODE, !FAST, !FAST>(s, pop, A, p, si, pos_q, al2, jt);
 
     // ---- O^T += V^T P^T: MFMA dblk covers d = 16*dblk .. +15; its A operand
-    // (V^T rows d, keys in step_key order) comes from two transposing reads ----
+    // (V^T rows d, keys in step_key order) comes from two transposing reads,
+    // four blocks' reads at a time ----
+    const uint32_t vb = lds_addr(vl);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-        for (int dblk = 0; dblk < kVE; ++dblk) {
-            const u32x2 v0 = lds_read_tr16(vl + ks * 32 * kPitch + lo.vtr[dblk]);
-            const u32x2 v1 = lds_read_tr16(vl + ks * 32 * kPitch + 16 * kPitch + lo.vtr[dblk]);
-            const u32x4 a = {v0.x, v0.y, v1.x, v1.y};
+        for (int d0 = 0; d0 < kVE; d0 += 4) {
+            uint32_t ad[8];
 #pragma unroll
-            for (int rb = 0; rb < kRB; ++rb)
-                A.o[rb][dblk] = mfma_bf16_16x16x32(a, pop[rb][ks], A.o[rb][dblk]);
+            for (int u = 0; u < 4; ++u) {
+                ad[2 * u] = vb + ks * 32 * kPitch + lo.vtr[d0 + u];
+                ad[2 * u + 1] = ad[2 * u] + 16 * kPitch;
+            }
+            u32x2 v[8];
+            lds_read_tr16_x8(v, ad);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const u32x4 a = {v[2 * u].x, v[2 * u].y, v[2 * u + 1].x, v[2 * u + 1].y};
+#pragma unroll
+                for (int rb = 0; rb < kRB; ++rb)
+                    A.o[rb][d0 + u] = mfma_bf16_16x16x32(a, pop[rb][ks], A.o[rb][d0 + u]);
+            }
         }
     }
 }
