@@ -103,12 +103,13 @@ def test_plan_validation(kw, status):
 def test_plan_decisions():
     """Decode: the split pass is cut into `num_splits` equal ranges (one per
     persistent wave; planned without a device, 4 per compute unit for the bf16
-    D = 128 kernel, built for one wave per SIMD, 8 for the others); the
-    workspace holds two partial slots of G x (D + 1) floats per wave."""
+    D = 128 kernel, built for one wave per SIMD, 7 of 8 for fp8 and 8 for the
+    others); the workspace holds two partial slots of G x (D + 1) floats per
+    wave."""
     st, pl = plan_status()
     assert st == OK and pl.tokens_per_split == 32
     assert pl.num_splits == 256 * 4
-    assert plan_status(kv_dtype=1)[1].num_splits == 256 * 8
+    assert plan_status(kv_dtype=1)[1].num_splits == 256 * 7
     assert plan_status(head_dim=64)[1].num_splits == 256 * 8
     assert pl.workspace_bytes >= pl.num_splits * 2 * 4 * 129 * 4
     st, pl = plan_status(num_seqs=2, num_q_heads=4, num_kv_heads=1, head_dim=64,
