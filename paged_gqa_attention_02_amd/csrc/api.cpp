@@ -105,12 +105,13 @@ ExtLayout extend_layout(const pa_problem& pr, int64_t workers) {
 }
 
 // Split-pass waves per block: one per 16 query rows of a kv head (latent
-// cache: rounded up to 1, 2, 4 or 8).
+// cache: rounded up to 2, 4 or 8; with at most 16 rows the second wave stages
+// the tiles for the first).
 int decode_waves_per_block(const pa_problem& pr) {
     const int q_len = pr.mode == PA_MODE_VERIFY ? pr.max_q_len : 1;
     const int nw = ((pr.num_q_heads / pr.num_kv_heads) * q_len + 15) / 16;
     if (is_latent(pr)) {
-        int p2 = 1;
+        int p2 = 2;
         while (p2 < nw) p2 *= 2;
         return p2;
     }
@@ -243,7 +244,8 @@ pa_status paged_attn_plan(const pa_problem* prob, int hip_device, pa_plan* out) 
                 if (cur != hip_device && hipSetDevice(hip_device) != hipSuccess) return PA_ERR_HIP;
                 const hipError_t e =
                     is_latent(pr)
-                        ? mla_blocks_per_cu(pr.head_dim, pr.head_dim_v, true, nw, &per_cu)
+                        ? mla_blocks_per_cu(pr.head_dim, pr.head_dim_v, true, nw,
+                                            pr.num_q_heads / pr.num_kv_heads, &per_cu)
                         : decode_blocks_per_cu(pr.head_dim, pr.kv_dtype == PA_KV_FP8_E4M3,
                                                pr.page_size >= 16, nw, &per_cu);
                 if (cur != hip_device) (void)hipSetDevice(cur);

@@ -28,6 +28,12 @@
 // loads (lane i of a wave fills bytes 16i..16i+15 of a 1 KB run): a main run
 // is whole rows, a rope run 8 (or 16) rows.  Two buffers: the next tile's
 // loads are in flight while this tile is computed.
+//
+// One pool and at most 16 query heads (the common latent case): blocks of two
+// waves, one computing and one staging the tiles through registers (plain
+// 16-byte loads, then LDS stores) with one barrier per tile.  On MI355X the
+// direct-to-LDS path streams at most about 5.2 TB/s, register loads about
+// 6.9 TB/s.
 #include <climits>
 
 #include "decode_geom.h"
@@ -142,6 +148,64 @@ __device__ __forceinline__ void mla_stage(const MlaChunk& ch, int t0, bool unifo
     }
 }
 
+// Producer wave of a two-wave block (latent cache, at most 16 query heads):
+// stages the chunk's tiles through registers, tile i into buffer i & 1, with
+// one barrier per tile after the tile is in LDS; the consumer wave passes the
+// same barrier before it reads the tile.  Two tiles are in flight.  Every
+// step issues the same loads -- the last steps re-read the chunk's last tile,
+// which the cache still holds -- so the load counts the compiler waits on are
+// the same on every path.
+template <int DQK, int DV>
+__device__ __forceinline__ void mla_produce(const MlaChunk& ch, int tile0, int ct, bool uniform,
+                                            uint8_t* b0, uint8_t* b1, int lane) {
+    using T = MlaTile<DQK, DV>;
+    constexpr int kRuns = T::kMainRuns + T::kRopeRuns;
+    const int pmask = (1 << ch.page_shift) - 1;
+    auto load = [&](u32x4 (&r)[kRuns], int i) {
+        const int t0 = tile0 + i * kTile;
+        // page_size >= 32: the whole tile lies in one page
+        const int64_t tile_page = uniform ? ch.pages[(t0 >> ch.page_shift) - ch.first_page] : 0;
+#pragma unroll
+        for (int run = 0; run < kRuns; ++run) {
+            int row, off;
+            if (run < T::kMainRuns) {
+                row = run * T::kMainRows + lane / T::kMainSlots;
+                off = 16 * ((lane % T::kMainSlots) ^ T::mswz(row));
+            } else {
+                const int rr = run - T::kMainRuns;
+                row = rr * T::kRopeRows + lane / T::kRopeSlots;
+                off = 2 * DV + 16 * ((lane % T::kRopeSlots) ^ T::rswz(row));
+            }
+            const int t = min(max(t0 + row, ch.t_begin), ch.t_end - 1);
+            const int64_t page =
+                uniform ? tile_page : (int64_t)ch.pages[(t >> ch.page_shift) - ch.first_page];
+            r[run] = *reinterpret_cast<const u32x4*>(
+                ch.kbase + page * ch.page_bytes + (uint32_t)((t & pmask) * ch.tok_bytes + off));
+        }
+    };
+    auto store = [&](const u32x4 (&r)[kRuns], uint8_t* buf) {
+#pragma unroll
+        for (int run = 0; run < kRuns; ++run) {
+            uint8_t* dst = run < T::kMainRuns ? buf + run * 1024
+                                              : buf + T::kMainBytes + (run - T::kMainRuns) * 1024;
+            *reinterpret_cast<u32x4*>(dst + 16 * lane) = r[run];
+        }
+    };
+    const int last = ct - 1;
+    u32x4 ra[kRuns], rb[kRuns];
+    load(ra, 0);
+    load(rb, min(1, last));
+    for (int i = 0; i < ct; i += 2) {
+        store(ra, b0);
+        load(ra, min(i + 2, last));
+        __syncthreads();                       // tile i is in buffer 0
+        if (i + 1 >= ct) break;
+        store(rb, b1);
+        load(rb, min(i + 3, last));
+        __syncthreads();                       // tile i + 1 is in buffer 1
+    }
+}
+
 // Per-lane byte offsets of the operand reads inside a tile (rows 16kb + c
 // and 16h + 4grp + e share the swizzle of c and 4grp + e).
 //   K main, MFMA step ds (entries 32ds + 8grp ..): kmain[ds & 3] + 256 (ds >> 2)
@@ -178,8 +242,13 @@ struct MlaOffs {
 // ---------------------------------------------------------------------------
 // Split pass
 // ---------------------------------------------------------------------------
-template <int DQK, int DV, int NW, bool ALIAS>
+// PC: two-wave blocks over one pool with at most 16 query heads; wave 0
+// computes and wave 1 stages the tiles through registers (mla_produce).
+// Otherwise the NW waves stage each tile with direct-to-LDS loads and each
+// computes its 16 query heads.
+template <int DQK, int DV, int NW, bool ALIAS, bool PC>
 __global__ __launch_bounds__(64 * NW) void mla_split_kernel(DecodeParams p) {
+    static_assert(!PC || (NW == 2 && ALIAS), "producer/consumer blocks: two waves, one pool");
     using T = MlaTile<DQK, DV>;
     constexpr int KM = DV / 32;                // QK steps over the main entries
     constexpr int KR = (DQK - DV) / 32;        // QK steps over the rope entries
@@ -240,6 +309,52 @@ __global__ __launch_bounds__(64 * NW) void mla_split_kernel(DecodeParams p) {
                 int4{(int)w, (int)w_last, slot, 0};
         }
 
+        MlaChunk ch;
+        ch.kbase = static_cast<const uint8_t*>(p.k_pool) + (int64_t)kvh * p.s_head * 2;
+        ch.vbase = static_cast<const uint8_t*>(p.v_pool) + (int64_t)kvh * p.s_head * 2;
+        ch.page_bytes = p.s_page * 2;
+        ch.tok_bytes = (int)(p.s_tok * 2);
+        ch.page_shift = p.page_shift;
+        ch.pages = sm_pages;
+
+        // Chunk c0 of the piece: its key range, and its page ids staged in LDS
+        // between two barriers that every wave of the block takes.
+        auto begin_chunk = [&](int c0) {
+            const int ct = min(cnt - c0, chunk_tiles);
+            const int tile0 = sr.base + (i0 + c0) * kTile;
+            ch.t_begin = max(tile0, sr.lo);
+            ch.t_end = min(tile0 + ct * kTile, sr.L);
+            ch.first_page = ch.t_begin >> p.page_shift;
+            const int n_pages = ((ch.t_end - 1) >> p.page_shift) - ch.first_page + 1;
+            __syncthreads();     // the previous chunk's readers are done with the list
+            const int32_t* bt = p.block_table + (int64_t)b * p.bt_stride + ch.first_page;
+            for (int i = threadIdx.x; i < n_pages; i += 64 * NW) sm_pages[i] = bt[i];
+            __syncthreads();
+        };
+        auto next_piece = [&]() {
+            pos += cnt;
+            slot = 1;
+            if (pos < r1 && pos == seq_start + (int64_t)n * p.num_kv_heads) {
+                seq_start = pos;
+                do {
+                    ++b;
+                    sr = seq_range(p, b);
+                } while (sr.tiles == 0);
+            }
+        };
+        if constexpr (PC) {
+            if (wv == 1) {
+                // the producer wave: stage the piece's tiles, chunk by chunk
+                for (int c0 = 0; c0 < cnt; c0 += chunk_tiles) {
+                    begin_chunk(c0);
+                    mla_produce<DQK, DV>(ch, sr.base + (i0 + c0) * kTile,
+                                         min(cnt - c0, chunk_tiles), uniform, sm_k0, sm_k1, lane);
+                }
+                next_piece();
+                continue;
+            }
+        }
+
         // ---- Q^T as B operands: column c is head kvh*G + cg; step ds covers
         // entries 32ds + 8grp + j (main), DV + 32ds + 8grp + j (rope) ----
         u32x4 qop[KM + KR];
@@ -270,41 +385,15 @@ __global__ __launch_bounds__(64 * NW) void mla_split_kernel(DecodeParams p) {
         for (int e = 0; e < VE; ++e) o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
         float m = -INFINITY, l = 0.f;
 
-        MlaChunk ch;
-        ch.kbase = static_cast<const uint8_t*>(p.k_pool) + (int64_t)kvh * p.s_head * 2;
-        ch.vbase = static_cast<const uint8_t*>(p.v_pool) + (int64_t)kvh * p.s_head * 2;
-        ch.page_bytes = p.s_page * 2;
-        ch.tok_bytes = (int)(p.s_tok * 2);
-        ch.page_shift = p.page_shift;
-        ch.pages = sm_pages;
-
         // ---- the piece's tiles, chunk by chunk (page list staged in LDS) ----
         for (int c0 = 0; c0 < cnt; c0 += chunk_tiles) {
             const int ct = min(cnt - c0, chunk_tiles);
             const int tile0 = sr.base + (i0 + c0) * kTile;
-            ch.t_begin = max(tile0, sr.lo);
-            ch.t_end = min(tile0 + ct * kTile, sr.L);
-            ch.first_page = ch.t_begin >> p.page_shift;
-            const int n_pages = ((ch.t_end - 1) >> p.page_shift) - ch.first_page + 1;
-            __syncthreads();     // the previous chunk's readers are done with the list
-            {
-                const int32_t* bt = p.block_table + (int64_t)b * p.bt_stride + ch.first_page;
-                for (int i = threadIdx.x; i < n_pages; i += 64 * NW) sm_pages[i] = bt[i];
-            }
-            __syncthreads();
+            begin_chunk(c0);
 
-            mla_stage<DQK, DV, NW, ALIAS>(ch, tile0, uniform, sm_k0, sm_v0, wv, lane);
-            wait_vm0();
-            __syncthreads();
-            for (int i = 0; i < ct; ++i) {
+            // one tile of the chunk, staged in kt (vt: its value rows)
+            auto compute = [&](int i, const uint8_t* kt, const uint8_t* vt) {
                 const int t0 = tile0 + i * kTile;
-                const uint8_t* kt = (i & 1) ? sm_k1 : sm_k0;
-                const uint8_t* vt = ALIAS ? kt : ((i & 1) ? sm_v1 : sm_v0);
-                if (i + 1 < ct)
-                    mla_stage<DQK, DV, NW, ALIAS>(ch, t0 + kTile, uniform,
-                                                  (i & 1) ? sm_k0 : sm_k1,
-                                                  (i & 1) ? sm_v0 : sm_v1, wv, lane);
-
                 // ---- S^T = K Q^T: s[kb][j] = score of key t0 + 16kb + 4grp + j.
                 // A wave is alone on its SIMD (the LDS tiles allow two blocks
                 // per compute unit), so nothing hides LDS latency but this
@@ -424,8 +513,29 @@ __global__ __launch_bounds__(64 * NW) void mla_split_kernel(DecodeParams p) {
                         o[dblk] = mfma_bf16_16x16x32(u32x4{v0.x, v0.y, v1.x, v1.y}, pop, o[dblk]);
                     }
                 }
+            };
+            if constexpr (PC) {
+                // the consumer wave (the producer took its own path above)
+                for (int i = 0; i < ct; ++i) {
+                    __syncthreads();                  // tile i is in buffer i & 1
+                    const uint8_t* kt = (i & 1) ? sm_k1 : sm_k0;
+                    compute(i, kt, kt);
+                }
+            } else {
+                mla_stage<DQK, DV, NW, ALIAS>(ch, tile0, uniform, sm_k0, sm_v0, wv, lane);
                 wait_vm0();
                 __syncthreads();
+                for (int i = 0; i < ct; ++i) {
+                    const uint8_t* kt = (i & 1) ? sm_k1 : sm_k0;
+                    const uint8_t* vt = ALIAS ? kt : ((i & 1) ? sm_v1 : sm_v0);
+                    if (i + 1 < ct)
+                        mla_stage<DQK, DV, NW, ALIAS>(ch, tile0 + (i + 1) * kTile, uniform,
+                                                      (i & 1) ? sm_k0 : sm_k1,
+                                                      (i & 1) ? sm_v0 : sm_v1, wv, lane);
+                    compute(i, kt, vt);
+                    wait_vm0();
+                    __syncthreads();
+                }
             }
         }
 
@@ -455,37 +565,34 @@ __global__ __launch_bounds__(64 * NW) void mla_split_kernel(DecodeParams p) {
             }
         }
 
-        // ---- next piece ----
-        pos += cnt;
-        slot = 1;
-        if (pos < r1 && pos == seq_start + (int64_t)n * p.num_kv_heads) {
-            seq_start = pos;
-            do {
-                ++b;
-                sr = seq_range(p, b);
-            } while (sr.tiles == 0);
-        }
+        next_piece();
     }
 }
 
 using MlaFn = void (*)(DecodeParams);
 
 template <int DQK, int DV, bool ALIAS>
-MlaFn mla_by_waves(int nw) {
+MlaFn mla_by_waves(int nw, bool pc) {
+    if (pc) return ALIAS && nw == 2 ? mla_split_kernel<DQK, DV, 2, true, true> : nullptr;
     switch (nw) {
-        case 1: return mla_split_kernel<DQK, DV, 1, ALIAS>;
-        case 2: return mla_split_kernel<DQK, DV, 2, ALIAS>;
-        case 4: return mla_split_kernel<DQK, DV, 4, ALIAS>;
-        case 8: return mla_split_kernel<DQK, DV, 8, ALIAS>;
+        case 1: return mla_split_kernel<DQK, DV, 1, ALIAS, false>;
+        case 2: return mla_split_kernel<DQK, DV, 2, ALIAS, false>;
+        case 4: return mla_split_kernel<DQK, DV, 4, ALIAS, false>;
+        case 8: return mla_split_kernel<DQK, DV, 8, ALIAS, false>;
         default: return nullptr;
     }
 }
 
-MlaFn mla_kernel(int dqk, int dv, bool alias, int nw) {
+// rows: query rows per kv head.  Two-wave blocks over one pool with at most
+// 16 rows are producer/consumer blocks.
+MlaFn mla_kernel(int dqk, int dv, bool alias, int nw, int rows) {
+    const bool pc = alias && nw == 2 && rows <= 16;
     if (dqk == 576 && dv == 512)
-        return alias ? mla_by_waves<576, 512, true>(nw) : mla_by_waves<576, 512, false>(nw);
+        return alias ? mla_by_waves<576, 512, true>(nw, pc)
+                     : mla_by_waves<576, 512, false>(nw, pc);
     if (dqk == 288 && dv == 256)
-        return alias ? mla_by_waves<288, 256, true>(nw) : mla_by_waves<288, 256, false>(nw);
+        return alias ? mla_by_waves<288, 256, true>(nw, pc)
+                     : mla_by_waves<288, 256, false>(nw, pc);
     return nullptr;
 }
 
@@ -493,15 +600,15 @@ MlaFn mla_kernel(int dqk, int dv, bool alias, int nw) {
 
 hipError_t launch_mla_decode(const DecodeParams& p, int head_dim, int head_dim_v, bool alias,
                              int waves_per_block, int workers, hipStream_t stream) {
-    const MlaFn f = mla_kernel(head_dim, head_dim_v, alias, waves_per_block);
+    const MlaFn f = mla_kernel(head_dim, head_dim_v, alias, waves_per_block, p.rows);
     if (!f) return hipErrorInvalidValue;
     hipLaunchKernelGGL(f, dim3(workers), dim3(64 * waves_per_block), 0, stream, p);
     return hipGetLastError();
 }
 
 hipError_t mla_blocks_per_cu(int head_dim, int head_dim_v, bool alias, int waves_per_block,
-                             int* out) {
-    const MlaFn f = mla_kernel(head_dim, head_dim_v, alias, waves_per_block);
+                             int rows, int* out) {
+    const MlaFn f = mla_kernel(head_dim, head_dim_v, alias, waves_per_block, rows);
     if (!f) return hipErrorInvalidValue;
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, reinterpret_cast<const void*>(f),
                                                         64 * waves_per_block, 0);

@@ -138,8 +138,9 @@ constexpr int kMaxDecodeRows = 64;   // query rows per kv head: 16 per wave, 4 w
 // merge is launch_decode_merge with head_dim_v.  alias: v_pool == k_pool.
 hipError_t launch_mla_decode(const DecodeParams& p, int head_dim, int head_dim_v, bool alias,
                              int waves_per_block, int workers, hipStream_t stream);
+// rows: query rows per kv head (the variant depends on it).
 hipError_t mla_blocks_per_cu(int head_dim, int head_dim_v, bool alias, int waves_per_block,
-                             int* out);
+                             int rows, int* out);
 constexpr int kMaxLatentGroup = 128;   // query heads per kv head: 16 per wave, 8 waves
 hipError_t launch_gather(const GatherParams& p, int head_dim, bool fp8, hipStream_t stream);
 // Extend: a scan of the items' tile counts, `workers` persistent blocks, and a

@@ -126,9 +126,10 @@ def test_plan_decisions():
 
 
 def test_plan_latent_decisions():
-    """Latent cache: one wave per 16 query heads, rounded up to 1, 2, 4 or 8
-    waves; partial rows of head_dim_v floats."""
-    for G, nw in ((1, 1), (16, 1), (17, 2), (32, 2), (48, 4), (64, 4), (100, 8), (128, 8)):
+    """Latent cache: one wave per 16 query heads, rounded up to 2, 4 or 8
+    waves (with at most 16 heads the second wave stages the tiles); partial
+    rows of head_dim_v floats."""
+    for G, nw in ((1, 2), (16, 2), (17, 2), (32, 2), (48, 4), (64, 4), (100, 8), (128, 8)):
         st, pl = plan_status(head_dim=576, head_dim_v=512, num_q_heads=G, num_kv_heads=1)
         assert st == OK and pl.waves_per_block == nw, (G, pl.waves_per_block)
         assert pl.workspace_bytes >= pl.num_splits * 2 * G * 513 * 4
