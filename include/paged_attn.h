@@ -162,7 +162,8 @@ typedef struct {
                                   blocks */
     int32_t tokens_per_split;  /* decode/verify: tile granularity of the pieces (32) */
     int32_t waves_per_block;   /* decode/verify: waves per block, one per 16
-                                  query rows (token, head) of a kv head */
+                                  query rows (token, head) of a kv head
+                                  (latent cache: rounded up to 2, 4 or 8) */
     int32_t num_cus;           /* compute units the plan was made for */
     uint64_t workspace_bytes;  /* device scratch the compute call needs */
     int32_t reserved[8];
@@ -177,7 +178,11 @@ typedef struct {
  * split pass; the plan takes as many as the device keeps resident (compute
  * units x resident blocks per unit), or prob->num_splits when that is > 0.
  * A block has one wave per 16 query rows of a kv head (G for decode,
- * G * q_len for verify); its waves walk the same tiles.
+ * G * q_len for verify); its waves walk the same tiles.  Latent cache: the
+ * count is rounded up to 2, 4 or 8; with at most 16 query heads over one pool
+ * the second wave stages the tiles for the first.  The resident count per
+ * unit is the runtime's occupancy for the kernel variant (one fewer of eight
+ * for fp8 caches, which stream faster so).
  * Pieces of one key range are merged by log-sum-exp (the split partition
  * and merge of `_fwd_kernel_stage1/2`; any partition gives the same result).
  * Verify: as decode, with lo = max(0, L - q_len + 1 - W), the window start of
