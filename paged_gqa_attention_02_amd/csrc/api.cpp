@@ -43,6 +43,16 @@ bool is_latent(const pa_problem& pr) {
 // Entries of a value (and output) row.
 int value_dim(const pa_problem& pr) { return is_latent(pr) ? pr.head_dim_v : pr.head_dim; }
 
+// A latent cache with one kv head and more than 64 query heads is run as two
+// virtual kv heads of half the heads each, over the same rows (head stride
+// 0): blocks of four waves, which keep their registers, instead of eight,
+// which are held to 256 VGPRs and spill.  Query head h stays head h: virtual
+// kv head v serves heads [v*G/2, (v+1)*G/2).
+int latent_head_split(const pa_problem& pr) {
+    if (!is_latent(pr) || pr.num_kv_heads != 1) return 1;
+    return (pr.num_q_heads > 64 && pr.num_q_heads % 2 == 0) ? 2 : 1;
+}
+
 pa_status check_problem(const pa_problem& pr) {
     if (pr.mode != PA_MODE_DECODE && pr.mode != PA_MODE_EXTEND && pr.mode != PA_MODE_VERIFY)
         return PA_ERR_UNSUPPORTED;
@@ -109,7 +119,8 @@ ExtLayout extend_layout(const pa_problem& pr, int64_t workers) {
 // the tiles for the first).
 int decode_waves_per_block(const pa_problem& pr) {
     const int q_len = pr.mode == PA_MODE_VERIFY ? pr.max_q_len : 1;
-    const int nw = ((pr.num_q_heads / pr.num_kv_heads) * q_len + 15) / 16;
+    const int g = pr.num_q_heads / pr.num_kv_heads / latent_head_split(pr);
+    const int nw = (g * q_len + 15) / 16;
     if (is_latent(pr)) {
         int p2 = 2;
         while (p2 < nw) p2 *= 2;
@@ -245,7 +256,9 @@ pa_status paged_attn_plan(const pa_problem* prob, int hip_device, pa_plan* out) 
                 const hipError_t e =
                     is_latent(pr)
                         ? mla_blocks_per_cu(pr.head_dim, pr.head_dim_v, true, nw,
-                                            pr.num_q_heads / pr.num_kv_heads, &per_cu)
+                                            pr.num_q_heads / pr.num_kv_heads /
+                                                latent_head_split(pr),
+                                            &per_cu)
                         : decode_blocks_per_cu(pr.head_dim, pr.kv_dtype == PA_KV_FP8_E4M3,
                                                pr.page_size >= 16, nw, &per_cu);
                 if (cur != hip_device) (void)hipSetDevice(cur);
@@ -263,12 +276,13 @@ pa_status paged_attn_plan(const pa_problem* prob, int hip_device, pa_plan* out) 
         pl.tokens_per_split = kTile;
         pl.waves_per_block = nw;
         const int64_t q_len = pr.mode == PA_MODE_VERIFY ? pr.max_q_len : 1;
-        const int64_t rows = workers * 2 * (pr.num_q_heads / pr.num_kv_heads) * q_len;
+        const int split = latent_head_split(pr);
+        const int64_t rows = workers * 2 * (pr.num_q_heads / pr.num_kv_heads / split) * q_len;
         // partial rows, their log-sum-exp, and one record per segment
         pl.workspace_bytes = (uint64_t)(round_up(rows * value_dim(pr) * 4, 256) +
                                         round_up(rows * 4, 256) +
                                         round_up(16 * (int64_t)pr.num_seqs *
-                                                     pr.num_kv_heads, 256));
+                                                     pr.num_kv_heads * split, 256));
     }
     if (pr.mode == PA_MODE_EXTEND) {
         // Persistent blocks, each owning an equal contiguous range of the key
@@ -380,14 +394,16 @@ pa_status decode_impl(int passes, int mode, const pa_plan* plan, const void* q, 
     p.v_pool = v_pool;
     p.s_page = kv_stride_page;
     p.s_tok = kv_stride_tok;
-    p.s_head = kv_stride_head;
+    // (a split latent cache: virtual kv heads over the same rows)
+    const int split = latent_head_split(pr);
+    p.s_head = split > 1 ? 0 : kv_stride_head;
     p.block_table = block_table;
     p.bt_stride = bt_stride;
     p.seq_lens = seq_lens;
     p.num_seqs = pr.num_seqs;
     p.num_q_heads = pr.num_q_heads;
-    p.num_kv_heads = pr.num_kv_heads;
-    p.group = pr.num_q_heads / pr.num_kv_heads;
+    p.num_kv_heads = pr.num_kv_heads * split;
+    p.group = pr.num_q_heads / p.num_kv_heads;
     p.q_len = q_len;
     p.rows = p.group * q_len;
     p.q_stride_t = row;
@@ -429,7 +445,7 @@ pa_status decode_impl(int passes, int mode, const pa_plan* plan, const void* q, 
         if (e != hipSuccess) return PA_ERR_HIP;
     }
     if ((passes & kMergePass) &&
-        launch_decode_merge(p, value_dim(pr), pr.num_seqs, pr.num_kv_heads, stream) !=
+        launch_decode_merge(p, value_dim(pr), pr.num_seqs, p.num_kv_heads, stream) !=
             hipSuccess)
         return PA_ERR_HIP;
     return PA_OK;

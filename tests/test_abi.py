@@ -127,12 +127,16 @@ def test_plan_decisions():
 
 def test_plan_latent_decisions():
     """Latent cache: one wave per 16 query heads, rounded up to 2, 4 or 8
-    waves (with at most 16 heads the second wave stages the tiles); partial
-    rows of head_dim_v floats."""
-    for G, nw in ((1, 2), (16, 2), (17, 2), (32, 2), (48, 4), (64, 4), (100, 8), (128, 8)):
+    waves (with at most 16 heads the second wave stages the tiles; more than
+    64 heads over one kv head run as two halves of four waves); partial rows
+    of head_dim_v floats."""
+    for G, nw, rows in ((1, 2, 1), (16, 2, 16), (17, 2, 17), (32, 2, 32), (48, 4, 48),
+                        (64, 4, 64), (100, 4, 50), (128, 4, 64), (65, 8, 65)):
         st, pl = plan_status(head_dim=576, head_dim_v=512, num_q_heads=G, num_kv_heads=1)
         assert st == OK and pl.waves_per_block == nw, (G, pl.waves_per_block)
-        assert pl.workspace_bytes >= pl.num_splits * 2 * G * 513 * 4
+        assert pl.workspace_bytes >= pl.num_splits * 2 * rows * 513 * 4
+    st, pl = plan_status(head_dim=576, head_dim_v=512, num_q_heads=256, num_kv_heads=2)
+    assert st == OK and pl.waves_per_block == 8      # two kv heads: no virtual split
     st, pl = plan_status(head_dim=576, head_dim_v=512, num_q_heads=16, num_kv_heads=1)
     assert pl.num_splits == 256 * 2
     assert "D=576 Dv=512" in pa.Plan(pl).describe()

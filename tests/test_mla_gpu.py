@@ -48,6 +48,9 @@ def check(case, num_splits=None, what=""):
     ([77, 400, 3000], 16, 1, 288, 256, 16, True, {}),
     ([77, 400], 64, 2, 288, 256, 8, False, dict(softcap=10.0, window=50)),
     ([0, 50, 0, 3], 16, 1, 576, 512, 16, True, {}),                      # empty sequences
+    ([300, 64, 1000], 100, 1, 576, 512, 16, True, dict(softcap=12.0)),   # two halves of 50 heads
+    ([200, 31], 65, 1, 576, 512, 32, True, {}),                          # 65 heads: 8-wave blocks
+    ([0, 90, 2100], 128, 1, 288, 256, 64, True, dict(window=500)),       # halves, 288/256
 ])
 def test_mla_decode_matches_oracle(lens, Hq, Hkv, D, Dv, P, alias, kw):
     case = mla_case(lens, Hq, Hkv, D, Dv, P, 100 + Hq + P, alias=alias, **kw)
@@ -71,6 +74,15 @@ def test_mla_extras():
                          sinks=True, descales=True, alibi=True)
     check(case, what="sinks+descales+alibi")
     check(case, num_splits=5, what="sinks+descales+alibi split")
+
+
+def test_mla_extras_head_halves():
+    """128 heads over one kv head run as two virtual kv heads of 64: sinks,
+    ALiBi slopes and descales must still reach their own query heads."""
+    case = I.with_extras(mla_case([700, 1500, 3], 128, 1, 576, 512, 16, 15), 16,
+                         sinks=True, descales=True, alibi=True)
+    check(case, what="128 heads, sinks+descales+alibi")
+    check(case, num_splits=9, what="128 heads, sinks+descales+alibi split")
 
 
 def test_mla_alias_and_copy_agree():
