@@ -22,7 +22,7 @@ namespace {
 // in one round -- and the kR piece lanes are combined through LDS.
 // Sequences with no keys get zero rows.
 // ---------------------------------------------------------------------------
-constexpr int kMergeThreads = 512;
+constexpr int kMergeThreads = 256;
 
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParams p,
@@ -127,7 +127,7 @@ hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, int B, int H
     // to fill the chip, a divisor of them (more blocks, more piece lanes
     // each) otherwise.
     const int64_t segs = (int64_t)B * Hkv;
-    // at most kMergeThreads / (D/4) rows per block (16 for D = 128, 4 for 512)
+    // at most kMergeThreads / (D/4) rows per block (8 for D = 128, 2 for 512)
     const int max_rows = kMergeThreads / (head_dim / 4);
     int per_block = p.rows;
     while (per_block > max_rows || p.rows % per_block) --per_block;
