@@ -161,26 +161,44 @@ __device__ __forceinline__ void mla_produce(const MlaChunk& ch, int tile0, int c
     using T = MlaTile<DQK, DV>;
     constexpr int kRuns = T::kMainRuns + T::kRopeRuns;
     const int pmask = (1 << ch.page_shift) - 1;
+    // (row, byte offset) of this lane's 16 bytes in run `run` of a tile
+    auto slot_of = [&](int run, int& row, int& off) {
+        if (run < T::kMainRuns) {
+            row = run * T::kMainRows + lane / T::kMainSlots;
+            off = 16 * ((lane % T::kMainSlots) ^ T::mswz(row));
+        } else {
+            const int rr = run - T::kMainRuns;
+            row = rr * T::kRopeRows + lane / T::kRopeSlots;
+            off = 2 * DV + 16 * ((lane % T::kRopeSlots) ^ T::rswz(row));
+        }
+    };
+    // Straight-line loads into r (a branch per load would make the compiler
+    // land each load in a temporary and wait for it before the copy).
     auto load = [&](u32x4 (&r)[kRuns], int i) {
         const int t0 = tile0 + i * kTile;
-        // page_size >= 32: the whole tile lies in one page
-        const int64_t tile_page = uniform ? ch.pages[(t0 >> ch.page_shift) - ch.first_page] : 0;
+        if (uniform) {
+            // page_size >= 32: the whole tile lies in one page
+            const uint8_t* base =
+                ch.kbase + (int64_t)ch.pages[(t0 >> ch.page_shift) - ch.first_page] * ch.page_bytes;
 #pragma unroll
-        for (int run = 0; run < kRuns; ++run) {
-            int row, off;
-            if (run < T::kMainRuns) {
-                row = run * T::kMainRows + lane / T::kMainSlots;
-                off = 16 * ((lane % T::kMainSlots) ^ T::mswz(row));
-            } else {
-                const int rr = run - T::kMainRuns;
-                row = rr * T::kRopeRows + lane / T::kRopeSlots;
-                off = 2 * DV + 16 * ((lane % T::kRopeSlots) ^ T::rswz(row));
+            for (int run = 0; run < kRuns; ++run) {
+                int row, off;
+                slot_of(run, row, off);
+                const int t = min(max(t0 + row, ch.t_begin), ch.t_end - 1);
+                r[run] = *reinterpret_cast<const u32x4*>(
+                    base + (uint32_t)((t & pmask) * ch.tok_bytes + off));
             }
-            const int t = min(max(t0 + row, ch.t_begin), ch.t_end - 1);
-            const int64_t page =
-                uniform ? tile_page : (int64_t)ch.pages[(t >> ch.page_shift) - ch.first_page];
-            r[run] = *reinterpret_cast<const u32x4*>(
-                ch.kbase + page * ch.page_bytes + (uint32_t)((t & pmask) * ch.tok_bytes + off));
+        } else {
+#pragma unroll
+            for (int run = 0; run < kRuns; ++run) {
+                int row, off;
+                slot_of(run, row, off);
+                const int t = min(max(t0 + row, ch.t_begin), ch.t_end - 1);
+                const int64_t page = ch.pages[(t >> ch.page_shift) - ch.first_page];
+                r[run] = *reinterpret_cast<const u32x4*>(
+                    ch.kbase + page * ch.page_bytes +
+                    (uint32_t)((t & pmask) * ch.tok_bytes + off));
+            }
         }
     };
     auto store = [&](const u32x4 (&r)[kRuns], uint8_t* buf) {
