@@ -419,9 +419,9 @@ __global__ __launch_bounds__(64 * NW) void mla_split_kernel(DecodeParams p) {
                 // before the MFMAs, and the two key halves' accumulation
                 // chains alternate. ----
                 f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-                // (batched reads where the registers allow: one- and two-wave
-                // blocks over one pool; larger blocks are held to fewer
-                // registers and read each operand right before its MFMA)
+                // (batched reads where the registers allow: two-wave blocks
+                // over one pool; larger blocks are held to fewer registers and
+                // read each operand right before its MFMA)
                 constexpr bool kBatch = NW <= 2 && ALIAS;
                 if constexpr (kBatch) {
                     constexpr int kKB = (KM + KR) % 6 == 0 ? 6 : 3;   // contraction steps per batch
@@ -593,7 +593,6 @@ template <int DQK, int DV, bool ALIAS>
 MlaFn mla_by_waves(int nw, bool pc) {
     if (pc) return ALIAS && nw == 2 ? mla_split_kernel<DQK, DV, 2, true, true> : nullptr;
     switch (nw) {
-        case 1: return mla_split_kernel<DQK, DV, 1, ALIAS, false>;
         case 2: return mla_split_kernel<DQK, DV, 2, ALIAS, false>;
         case 4: return mla_split_kernel<DQK, DV, 4, ALIAS, false>;
         case 8: return mla_split_kernel<DQK, DV, 8, ALIAS, false>;
