@@ -455,9 +455,8 @@ void decode_split_kernel(DecodeParams p) {
     uint8_t* const sm_k = sm_kv[0];
     uint8_t* const sm_v = sm_kv[NW == 1 ? 0 : 1];
 
-    const int64_t N = total_tiles(p);
-    const int64_t r0 = range_start(w, N, W);
-    const int64_t r1 = range_start(w + 1, N, W);
+    const RangeStart rs = locate_range(p, w, W);
+    const int64_t N = rs.N, r0 = rs.r0, r1 = rs.r1;
     if (r0 >= r1) {
         // an empty range (N < W): the merge may read this wave's slot 0
         for (int i = threadIdx.x; i < p.rows; i += 64 * NW)
@@ -465,10 +464,9 @@ void decode_split_kernel(DecodeParams p) {
         return;
     }
 
-    int b;
-    int64_t seq_start;
-    find_seq(p, r0, b, seq_start);
-    SeqRange sr = seq_range(p, b);
+    int b = rs.b;
+    int64_t seq_start = rs.seq_start;
+    SeqRange sr = rs.sr;
 
     // tiles of one chunk whose pages fit the LDS page list
     const int chunk_tiles = ((kMaxSplitPages - 2) << p.page_shift) / kTile;

@@ -91,6 +91,50 @@ __device__ __forceinline__ int64_t range_start(int64_t w, int64_t N, int64_t W) 
     return w * N / W;
 }
 
+// Where wave (or block) w of W starts: the total N, its range [r0, r1), and,
+// when the range is not empty, the sequence b holding tile r0, the global
+// index of b's first tile and b's key range.  With at most 64 sequences one
+// read of the lengths serves it all (lane i holds sequence i); otherwise the
+// lengths are scanned twice (total_tiles, find_seq).
+struct RangeStart {
+    int64_t N, r0, r1, seq_start;
+    int b;
+    SeqRange sr;
+};
+
+__device__ __forceinline__ RangeStart locate_range(const DecodeParams& p, int64_t w, int64_t W) {
+    RangeStart rs;
+    if (p.num_seqs <= 64) {
+        const int lane = __lane_id();
+        const SeqRange mine = lane < p.num_seqs ? seq_range(p, lane) : SeqRange{0, 0, 0, 0};
+        const int64_t n = (int64_t)mine.tiles * p.num_kv_heads;
+        int64_t incl = n;                     // inclusive scan across the wave
+#pragma unroll
+        for (int k = 1; k < 64; k <<= 1) {
+            const int64_t t = __shfl_up(incl, k, 64);
+            if (lane >= k) incl += t;
+        }
+        rs.N = __shfl(incl, 63, 64);
+        rs.r0 = range_start(w, rs.N, W);
+        rs.r1 = range_start(w + 1, rs.N, W);
+        if (rs.r0 >= rs.r1) return rs;
+        // the first sequence whose segments end past r0 (it has tiles)
+        const int j = __builtin_ctzll(__ballot(incl > rs.r0));
+        rs.b = j;
+        rs.seq_start = __shfl(incl - n, j, 64);
+        rs.sr = SeqRange{__shfl(mine.L, j, 64), __shfl(mine.lo, j, 64), __shfl(mine.base, j, 64),
+                         __shfl(mine.tiles, j, 64)};
+        return rs;
+    }
+    rs.N = total_tiles(p);
+    rs.r0 = range_start(w, rs.N, W);
+    rs.r1 = range_start(w + 1, rs.N, W);
+    if (rs.r0 >= rs.r1) return rs;
+    find_seq(p, rs.r0, rs.b, rs.seq_start);
+    rs.sr = seq_range(p, rs.b);
+    return rs;
+}
+
 // Partial slots of wave w: slot 0 holds its first segment when incomplete,
 // slot 1 its last one when incomplete (a middle segment is always complete).
 __device__ __forceinline__ int64_t part_row(const DecodeParams& p, int64_t w, int slot) {

@@ -289,9 +289,8 @@ __global__ __launch_bounds__(64 * NW) void mla_split_kernel(DecodeParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t sm_v0[ALIAS ? 16 : T::kMainBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t sm_v1[ALIAS ? 16 : T::kMainBytes];
 
-    const int64_t N = total_tiles(p);
-    const int64_t r0 = range_start(w, N, W);
-    const int64_t r1 = range_start(w + 1, N, W);
+    const RangeStart rs = locate_range(p, w, W);
+    const int64_t N = rs.N, r0 = rs.r0, r1 = rs.r1;
     if (r0 >= r1) {
         // an empty range (N < W): the merge may read this block's slot 0
         for (int i = threadIdx.x; i < p.rows; i += 64 * NW)
@@ -299,10 +298,9 @@ __global__ __launch_bounds__(64 * NW) void mla_split_kernel(DecodeParams p) {
         return;
     }
 
-    int b;
-    int64_t seq_start;
-    find_seq(p, r0, b, seq_start);
-    SeqRange sr = seq_range(p, b);
+    int b = rs.b;
+    int64_t seq_start = rs.seq_start;
+    SeqRange sr = rs.sr;
 
     const int chunk_tiles = ((kMlaPages - 2) << p.page_shift) / kTile;
     const bool uniform = p.page_shift >= 5;
