@@ -455,7 +455,7 @@ void decode_split_kernel(DecodeParams p) {
     uint8_t* const sm_k = sm_kv[0];
     uint8_t* const sm_v = sm_kv[NW == 1 ? 0 : 1];
 
-    const RangeStart rs = locate_range(p, w, W);
+    const RangeStart rs = locate_range<FP8>(p, w, W);
     const int64_t N = rs.N, r0 = rs.r0, r1 = rs.r1;
     if (r0 >= r1) {
         // an empty range (N < W): the merge may read this wave's slot 0

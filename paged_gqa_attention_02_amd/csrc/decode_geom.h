@@ -93,39 +93,73 @@ __device__ __forceinline__ int64_t range_start(int64_t w, int64_t N, int64_t W) 
 
 // Where wave (or block) w of W starts: the total N, its range [r0, r1), and,
 // when the range is not empty, the sequence b holding tile r0, the global
-// index of b's first tile and b's key range.  With at most 64 sequences one
-// read of the lengths serves it all (lane i holds sequence i); otherwise the
-// lengths are scanned twice (total_tiles, find_seq).
+// index of b's first tile and b's key range.
 struct RangeStart {
     int64_t N, r0, r1, seq_start;
     int b;
     SeqRange sr;
 };
 
-__device__ __forceinline__ RangeStart locate_range(const DecodeParams& p, int64_t w, int64_t W) {
+// One round of reads for at most 64*E sequences: lane i holds sequences
+// E*i .. E*i + E - 1, read together; the lane sums are scanned across the
+// wave.
+template <int E>
+__device__ __forceinline__ RangeStart locate_range_wave(const DecodeParams& p, int64_t w,
+                                                        int64_t W) {
     RangeStart rs;
-    if (p.num_seqs <= 64) {
-        const int lane = __lane_id();
-        const SeqRange mine = lane < p.num_seqs ? seq_range(p, lane) : SeqRange{0, 0, 0, 0};
-        const int64_t n = (int64_t)mine.tiles * p.num_kv_heads;
-        int64_t incl = n;                     // inclusive scan across the wave
+    const int lane = __lane_id();
+    SeqRange mine[E];
+    int64_t n[E], lsum = 0;
 #pragma unroll
-        for (int k = 1; k < 64; k <<= 1) {
-            const int64_t t = __shfl_up(incl, k, 64);
-            if (lane >= k) incl += t;
-        }
-        rs.N = __shfl(incl, 63, 64);
-        rs.r0 = range_start(w, rs.N, W);
-        rs.r1 = range_start(w + 1, rs.N, W);
-        if (rs.r0 >= rs.r1) return rs;
-        // the first sequence whose segments end past r0 (it has tiles)
-        const int j = __builtin_ctzll(__ballot(incl > rs.r0));
-        rs.b = j;
-        rs.seq_start = __shfl(incl - n, j, 64);
-        rs.sr = SeqRange{__shfl(mine.L, j, 64), __shfl(mine.lo, j, 64), __shfl(mine.base, j, 64),
-                         __shfl(mine.tiles, j, 64)};
-        return rs;
+    for (int e = 0; e < E; ++e) {
+        const int bb = E * lane + e;
+        mine[e] = bb < p.num_seqs ? seq_range(p, bb) : SeqRange{0, 0, 0, 0};
+        n[e] = (int64_t)mine[e].tiles * p.num_kv_heads;
+        lsum += n[e];
     }
+    int64_t incl = lsum;                      // inclusive scan of the lane sums
+#pragma unroll
+    for (int k = 1; k < 64; k <<= 1) {
+        const int64_t t = __shfl_up(incl, k, 64);
+        if (lane >= k) incl += t;
+    }
+    rs.N = __shfl(incl, 63, 64);
+    rs.r0 = range_start(w, rs.N, W);
+    rs.r1 = range_start(w + 1, rs.N, W);
+    if (rs.r0 >= rs.r1) return rs;
+    // the first lane whose sequences end past r0, then the first of its
+    // sequences that does (it has tiles)
+    const int j = __builtin_ctzll(__ballot(incl > rs.r0));
+    int64_t start = __shfl(incl - lsum, j, 64);
+    rs.b = E * j + E - 1;
+    rs.seq_start = start;
+    bool found = false;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int64_t nj = __shfl(n[e], j, 64);
+        if (!found && start + nj > rs.r0) {
+            found = true;
+            rs.b = E * j + e;
+            rs.seq_start = start;
+            rs.sr = SeqRange{__shfl(mine[e].L, j, 64), __shfl(mine[e].lo, j, 64),
+                             __shfl(mine[e].base, j, 64), __shfl(mine[e].tiles, j, 64)};
+        }
+        start += nj;
+    }
+    return rs;
+}
+
+// Up to 64 sequences (WIDE: up to 256, four a lane): one round of reads;
+// more: the lengths are scanned twice (total_tiles, find_seq).  WIDE is for
+// the kernels that meet large batches (the fp8 ones); it measured slower for
+// the bf16 kernel at 64 sequences although that path does not run there.
+template <bool WIDE>
+__device__ __forceinline__ RangeStart locate_range(const DecodeParams& p, int64_t w, int64_t W) {
+    if (p.num_seqs <= 64) return locate_range_wave<1>(p, w, W);
+    if constexpr (WIDE) {
+        if (p.num_seqs <= 256) return locate_range_wave<4>(p, w, W);
+    }
+    RangeStart rs;
     rs.N = total_tiles(p);
     rs.r0 = range_start(w, rs.N, W);
     rs.r1 = range_start(w + 1, rs.N, W);
