@@ -201,3 +201,19 @@ def test_fp8_table_on_device():
     out, _ = run_decode(case)
     ref = np.array([oracle.decode_e4m3fn(int(c)) for c in codes])
     np.testing.assert_array_equal(to_f64(out)[:, 0, 0], ref)
+
+
+@pytest.mark.parametrize("kv_dtype", ["fp8_e4m3", "bf16"])
+@pytest.mark.parametrize("splits", [0, 1, 7, 500, 3000])
+def test_batches_between_64_and_256_with_empty_sequences(kv_dtype, splits):
+    """65..256 sequences (the fp8 kernels find their first sequence in one
+    round of length reads, four sequences a lane; the bf16 ones scan twice),
+    with empty sequences at lane boundaries and some waves holding no tile."""
+    rng = np.random.default_rng(77)
+    lens = rng.integers(1, 300, size=150)
+    lens[[0, 3, 4, 63, 64, 127, 128, 149]] = 0
+    case = rand_case(lens, 16, 2, 128, 16, 78, kv_dtype=kv_dtype, window=200,
+                     scale_range=(0.5, 2.0) if kv_dtype != "bf16" else None)
+    out, _ = check(case, num_splits=splits or None, what=f"B150 {kv_dtype} splits={splits}")
+    for b in np.flatnonzero(lens == 0):
+        assert not out[b].any()
