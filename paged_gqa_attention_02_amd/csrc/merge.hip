@@ -124,14 +124,15 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
 hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, int B, int Hkv,
                                hipStream_t stream) {
     // Rows of a segment per block: all of them when there are enough segments
-    // to fill the chip, a divisor of them (more blocks, more piece lanes
-    // each) otherwise.
+    // for two blocks per compute unit, a divisor of them (more blocks, more
+    // piece lanes each) otherwise.  (A floor of 512 blocks was about 0.8 us
+    // faster than 1024 at 512 segments of 4 rows; 2048 was slower.)
     const int64_t segs = (int64_t)B * Hkv;
     // at most kMergeThreads / (D/4) rows per block (8 for D = 128, 2 for 512)
     const int max_rows = kMergeThreads / (head_dim / 4);
     int per_block = p.rows;
     while (per_block > max_rows || p.rows % per_block) --per_block;
-    while (per_block % 2 == 0 && segs * (p.rows / per_block) < 1024) per_block /= 2;
+    while (per_block % 2 == 0 && segs * (p.rows / per_block) < 512) per_block /= 2;
     dim3 grid((unsigned)(segs * (p.rows / per_block)));
     switch (head_dim) {
         case 64:
