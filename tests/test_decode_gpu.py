@@ -81,6 +81,9 @@ def test_long_context_page_size_1_vs_64():
                                        window=50)),
     ([300, 40], 16, 4, 64, 1, dict(kv_dtype="fp8_e4m3", scale_range=(0.5, 2.0))),
     ([0, 5, 0, 70], 8, 2, 128, 16, {}),                            # empty sequences
+    ([1500, 9, 2100], 16, 4, 128, 256, dict(kv_dtype="fp8_e4m3", scale_range=(0.5, 2.0))),
+    ([5000, 129], 8, 1, 64, 1024, dict(window=1500, softcap=8.0)),  # P 1024
+    ([3000, 5, 4097, 700], 32, 8, 128, 4096, {}),                  # P 4096: one or two pages
 ])
 def test_shapes(lens, Hq, Hkv, D, P, kw):
     case = rand_case(lens, Hq, Hkv, D, P, 100 + len(lens), **kw)

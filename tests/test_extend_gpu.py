@@ -71,6 +71,7 @@ def test_extend_workload_sampled_rows():
     ([1000, 20], [150, 70], 16, 2, 64, 64, dict(window=64)),          # window < q_len
     ([300, 700], [90, 300], 8, 1, 128, 16, dict(window=400, softcap=20.0)),
     ([500, 3], [64, 128], 16, 4, 128, 16, dict(kv_dtype="fp8_e4m3", scale_range=(0.5, 2.0))),
+    ([5000, 3], [70, 200], 16, 4, 128, 4096, {}),                    # P 4096
     ([77, 640], [129, 31], 32, 8, 64, 8, dict(kv_dtype="fp8_e4m3", scale_range=(0.5, 2.0),
                                                 window=100)),
     ([40, 0, 90], [0, 12, 3], 8, 2, 128, 16, {}),                     # a sequence with no rows

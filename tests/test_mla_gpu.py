@@ -51,6 +51,7 @@ def check(case, num_splits=None, what=""):
     ([300, 64, 1000], 100, 1, 576, 512, 16, True, dict(softcap=12.0)),   # two halves of 50 heads
     ([200, 31], 65, 1, 576, 512, 32, True, {}),                          # 65 heads: 8-wave blocks
     ([0, 90, 2100], 128, 1, 288, 256, 64, True, dict(window=500)),       # halves, 288/256
+    ([700, 2000, 3], 16, 1, 576, 512, 256, True, {}),                    # P 256
 ])
 def test_mla_decode_matches_oracle(lens, Hq, Hkv, D, Dv, P, alias, kw):
     case = mla_case(lens, Hq, Hkv, D, Dv, P, 100 + Hq + P, alias=alias, **kw)
