@@ -43,7 +43,7 @@ def run_append(key, value, kp, vp, slots, kv_dtype, ks=1.0, vs=1.0):
 
 
 @pytest.mark.parametrize("kv_dtype,ks,vs", [("bf16", 1.0, 1.0), ("fp8_e4m3", 0.8, 1.7)])
-@pytest.mark.parametrize("D,P", [(128, 16), (64, 1), (128, 64)])
+@pytest.mark.parametrize("D,P", [(128, 16), (64, 1), (128, 64), (128, 4096)])
 def test_append_matches_oracle(kv_dtype, ks, vs, D, P):
     """The new tokens of the extend workload (3,577 rows, 8 kv heads) at seeded
     random distinct slots, every fifth token padding."""
