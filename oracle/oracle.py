@@ -57,8 +57,22 @@ def lib():
     return _LIB
 
 
+def host_cpus() -> dict:
+    """The host's CPU counts: all of them, the ones this process may run on,
+    and the share the environment grants a job (OMP_NUM_THREADS, when set)."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    return {"nproc": os.cpu_count() or 1, "affinity": len(os.sched_getaffinity(0)),
+            "omp_num_threads": int(env) if env.isdigit() and int(env) > 0 else None}
+
+
 def default_threads() -> int:
-    return max(1, min(16, len(os.sched_getaffinity(0))))
+    """Every core this process may use: the affinity set, or the job's share
+    of it when the environment fixes one (OMP_NUM_THREADS)."""
+    c = host_cpus()
+    n = c["affinity"]
+    if c["omp_num_threads"]:
+        n = min(n, c["omp_num_threads"])
+    return max(1, n)
 
 
 def _ptr(a: Optional[np.ndarray]):

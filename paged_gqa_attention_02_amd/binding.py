@@ -158,7 +158,7 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _extras(sinks, k_descale, v_descale, alibi_slopes=None):
+def _extras(sinks, k_descale, v_descale, alibi_slopes=None, num_q_heads=0):
     """pa_extras for optional fp32 device tensors (None when all are None):
     sinks [Hq]; k_descale/v_descale with 1 or >= B entries; alibi_slopes [Hq]."""
     if sinks is None and k_descale is None and v_descale is None and alibi_slopes is None:
@@ -168,6 +168,9 @@ def _extras(sinks, k_descale, v_descale, alibi_slopes=None):
         if t is not None and (t.dtype != torch.float32 or t.dim() != 1 or
                               not t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous fp32 vector")
+    for name, t in (("sinks", sinks), ("alibi_slopes", alibi_slopes)):
+        if t is not None and t.numel() < num_q_heads:
+            raise ValueError(f"{name} must hold one value per query head ({num_q_heads})")
     n = [t.numel() for t in (k_descale, v_descale) if t is not None]
     if len(n) == 2 and n[0] != n[1]:
         raise ValueError("k_descale and v_descale must have the same length")
@@ -197,6 +200,37 @@ def _pool_strides(k_pool: torch.Tensor, v_pool: torch.Tensor):
     if k_pool.stride(3) != 1:
         raise ValueError("head_dim must be contiguous")
     return k_pool.stride(0), k_pool.stride(1), k_pool.stride(2)
+
+
+_KV_NAME = {v: k for k, v in PA_KV.items()}
+
+
+def _same_device(ref: torch.Tensor, **tensors):
+    for name, t in tensors.items():
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, expected {ref.device}")
+
+
+def _check_cache(pl: Plan, k_pool: torch.Tensor, block_table: torch.Tensor,
+                 lens: torch.Tensor, lens_name: str):
+    """The pools, block table and per-sequence lengths against the plan: the
+    kernels take every size from the plan, so a tensor smaller than it
+    describes would be read past its end."""
+    pr = pl.problem
+    if _kv_dtype_name(k_pool) != _KV_NAME[pr.kv_dtype]:
+        raise TypeError(f"k_pool/v_pool hold {k_pool.dtype}, the plan was made for "
+                        f"{_KV_NAME[pr.kv_dtype]}")
+    if k_pool.dim() != 4 or k_pool.shape[1] != pr.page_size or \
+            k_pool.shape[2] != pr.num_kv_heads or k_pool.shape[3] != pr.head_dim:
+        raise ValueError(f"k_pool/v_pool must be [pages, {pr.page_size}, {pr.num_kv_heads}, "
+                         f"{pr.head_dim}] as planned, got {tuple(k_pool.shape)}")
+    if block_table.dim() != 2 or block_table.shape[0] < pr.num_seqs or \
+            block_table.shape[1] < pr.max_pages_per_seq:
+        raise ValueError(f"block_table must be [>= {pr.num_seqs}, >= {pr.max_pages_per_seq}] "
+                         f"as planned, got {tuple(block_table.shape)}")
+    if lens.dim() != 1 or lens.numel() < pr.num_seqs or not lens.is_contiguous():
+        raise ValueError(f"{lens_name} must be a contiguous int32 vector of >= {pr.num_seqs} "
+                         f"entries")
 
 
 def workspace_for(pl: Plan, device) -> Optional[torch.Tensor]:
@@ -307,7 +341,16 @@ def _decode(fn, pl, q, k_pool, v_pool, block_table, seq_lens, scale, softcap, wi
         raise TypeError("block_table and seq_lens must be int32")
     if block_table.stride(1) != 1:
         raise ValueError("block_table rows must be contiguous")
-    dv = pl.problem.head_dim_v or q.shape[-1]
+    pr = pl.problem
+    want = (pr.num_seqs,) + ((pr.max_q_len,) if dims == 4 else ()) + (pr.num_q_heads,
+                                                                       pr.head_dim)
+    if tuple(q.shape) != want:
+        raise ValueError(f"q must be {want} as planned, got {tuple(q.shape)}")
+    _check_cache(pl, k_pool, block_table, seq_lens, "seq_lens")
+    _same_device(q, k_pool=k_pool, v_pool=v_pool, block_table=block_table,
+                 seq_lens=seq_lens, out=out, workspace=workspace, sinks=sinks,
+                 k_descale=k_descale, v_descale=v_descale, alibi_slopes=alibi_slopes)
+    dv = pr.head_dim_v or q.shape[-1]
     oshape = q.shape[:-1] + (dv,)
     if out is None:
         out = torch.empty(oshape, dtype=torch.bfloat16, device=q.device)
@@ -322,7 +365,7 @@ def _decode(fn, pl, q, k_pool, v_pool, block_table, seq_lens, scale, softcap, wi
         k_pool.shape[0], _ptr(block_table), block_table.stride(0), _ptr(seq_lens),
         k_pool.shape[1], float(scale), float(softcap), int(window), float(k_scale),
         float(v_scale), _ptr(out), out.stride(0), _ptr(workspace), wbytes,
-        _extras(sinks, k_descale, v_descale, alibi_slopes), _stream(stream)))
+        _extras(sinks, k_descale, v_descale, alibi_slopes, pr.num_q_heads), _stream(stream)))
     return out
 
 
@@ -352,6 +395,25 @@ def extend(pl: Plan, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
     if cu_seqlens_q.dtype != torch.int32 or ctx_lens.dtype != torch.int32 \
             or block_table.dtype != torch.int32:
         raise TypeError("cu_seqlens_q, ctx_lens and block_table must be int32")
+    if block_table.stride(1) != 1:
+        raise ValueError("block_table rows must be contiguous")
+    pr = pl.problem
+    if tuple(q.shape) != (pr.total_q, pr.num_q_heads, pr.head_dim):
+        raise ValueError(f"q must be ({pr.total_q}, {pr.num_q_heads}, {pr.head_dim}) as "
+                         f"planned, got {tuple(q.shape)}")
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if tuple(t.shape) != (pr.total_q, pr.num_kv_heads, pr.head_dim):
+            raise ValueError(f"{name} must be ({pr.total_q}, {pr.num_kv_heads}, "
+                             f"{pr.head_dim}) as planned, got {tuple(t.shape)}")
+    if cu_seqlens_q.dim() != 1 or cu_seqlens_q.numel() < pr.num_seqs + 1 or \
+            not cu_seqlens_q.is_contiguous():
+        raise ValueError(f"cu_seqlens_q must be a contiguous vector of >= {pr.num_seqs + 1} "
+                         "entries")
+    _check_cache(pl, k_pool, block_table, ctx_lens, "ctx_lens")
+    _same_device(q, k_new=k_new, v_new=v_new, cu_seqlens_q=cu_seqlens_q, ctx_lens=ctx_lens,
+                 k_pool=k_pool, v_pool=v_pool, block_table=block_table, out=out,
+                 workspace=workspace, sinks=sinks, k_descale=k_descale, v_descale=v_descale,
+                 alibi_slopes=alibi_slopes)
     if out is None:
         out = torch.empty_like(q)
     if out.dtype != torch.bfloat16 or out.shape != q.shape or not out.is_contiguous():
@@ -364,8 +426,8 @@ def extend(pl: Plan, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
         _ptr(ctx_lens), _ptr(k_pool), _ptr(v_pool), sp, st, sh, k_pool.shape[0],
         _ptr(block_table), block_table.stride(0), k_pool.shape[1], float(scale),
         float(softcap), int(window), float(k_scale), float(v_scale), _ptr(out),
-        _ptr(workspace), wbytes, _extras(sinks, k_descale, v_descale, alibi_slopes),
-        _stream(stream)))
+        _ptr(workspace), wbytes,
+        _extras(sinks, k_descale, v_descale, alibi_slopes, pr.num_q_heads), _stream(stream)))
     return out
 
 
@@ -393,6 +455,12 @@ def cache_append(key: torch.Tensor, value: torch.Tensor, k_pool: torch.Tensor,
 def gather(pl: Plan, k_pool: torch.Tensor, v_pool: torch.Tensor, block_table: torch.Tensor,
            seq_lens: torch.Tensor, total_tokens: int, stream=None):
     """paged_attn_gather: every cached row, dense [sum L, Hkv, D] (test aid)."""
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_table and seq_lens must be int32")
+    if block_table.stride(1) != 1:
+        raise ValueError("block_table rows must be contiguous")
+    _check_cache(pl, k_pool, block_table, seq_lens, "seq_lens")
+    _same_device(k_pool, v_pool=v_pool, block_table=block_table, seq_lens=seq_lens)
     sp, st, sh = _pool_strides(k_pool, v_pool)
     shape = (total_tokens, k_pool.shape[2], k_pool.shape[3])
     k_out = torch.empty(shape, dtype=k_pool.dtype, device=k_pool.device)

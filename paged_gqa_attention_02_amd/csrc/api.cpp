@@ -131,6 +131,23 @@ int decode_waves_per_block(const pa_problem& pr) {
 
 int elem_bytes(int kv_dtype) { return kv_dtype == PA_KV_FP8_E4M3 ? 1 : 2; }
 
+// Decode/verify workspace: two partial slots (rows of Dv floats and their
+// log-sum-exp) per persistent block, and one record per segment.
+struct DecLayout {
+    int64_t lse, rec, total;
+};
+
+DecLayout decode_layout(const pa_problem& pr, int64_t workers) {
+    DecLayout L;
+    const int64_t q_len = pr.mode == PA_MODE_VERIFY ? pr.max_q_len : 1;
+    const int split = latent_head_split(pr);
+    const int64_t rows = workers * 2 * (pr.num_q_heads / pr.num_kv_heads / split) * q_len;
+    L.lse = round_up(rows * value_dim(pr) * 4, 256);
+    L.rec = L.lse + round_up(rows * 4, 256);
+    L.total = L.rec + round_up(16 * (int64_t)pr.num_seqs * pr.num_kv_heads * split, 256);
+    return L;
+}
+
 // Optional sinks and per-request descales (NULL extras: none).
 struct Extras {
     const float* sinks = nullptr;
@@ -275,14 +292,7 @@ pa_status paged_attn_plan(const pa_problem* prob, int hip_device, pa_plan* out) 
         pl.num_splits = (int32_t)workers;
         pl.tokens_per_split = kTile;
         pl.waves_per_block = nw;
-        const int64_t q_len = pr.mode == PA_MODE_VERIFY ? pr.max_q_len : 1;
-        const int split = latent_head_split(pr);
-        const int64_t rows = workers * 2 * (pr.num_q_heads / pr.num_kv_heads / split) * q_len;
-        // partial rows, their log-sum-exp, and one record per segment
-        pl.workspace_bytes = (uint64_t)(round_up(rows * value_dim(pr) * 4, 256) +
-                                        round_up(rows * 4, 256) +
-                                        round_up(16 * (int64_t)pr.num_seqs *
-                                                     pr.num_kv_heads * split, 256));
+        pl.workspace_bytes = (uint64_t)decode_layout(pr, workers).total;
     }
     if (pr.mode == PA_MODE_EXTEND) {
         // Persistent blocks, each owning an equal contiguous range of the key
@@ -358,8 +368,11 @@ pa_status decode_impl(int passes, int mode, const pa_plan* plan, const void* q, 
     if (st != PA_OK) return st;
     if (pr.mode != mode) return PA_ERR_PLAN_MISMATCH;
     if (page_size != pr.page_size || window != pr.window) return PA_ERR_PLAN_MISMATCH;
+    // the workspace layout follows from (num_splits, problem): a plan edited
+    // after paged_attn_plan must not make the kernels write past it
     if (pl.tokens_per_split != kTile || pl.num_splits < 1 || pl.num_splits > kMaxWorkers ||
-        pl.waves_per_block != decode_waves_per_block(pr))
+        pl.waves_per_block != decode_waves_per_block(pr) ||
+        pl.workspace_bytes != (uint64_t)decode_layout(pr, pl.num_splits).total)
         return PA_ERR_PLAN_MISMATCH;
     if (pr.num_seqs == 0) return PA_OK;
     if (!q || !seq_lens || !out) return PA_ERR_NULL_POINTER;
@@ -379,12 +392,9 @@ pa_status decode_impl(int passes, int mode, const pa_plan* plan, const void* q, 
     Extras ex;
     st = read_extras(extras, pr.num_seqs, &ex);
     if (st != PA_OK) return st;
-    const uint64_t need = pl.workspace_bytes;
-    if (need > 0) {
-        if (workspace_bytes < need) return PA_ERR_WORKSPACE_TOO_SMALL;
-        if (!workspace) return PA_ERR_NULL_POINTER;
-        if (!aligned16(workspace)) return PA_ERR_MISALIGNED;
-    }
+    if (workspace_bytes < pl.workspace_bytes) return PA_ERR_WORKSPACE_TOO_SMALL;
+    if (!workspace) return PA_ERR_NULL_POINTER;
+    if (!aligned16(workspace)) return PA_ERR_MISALIGNED;
 
     DecodeParams p;
     memset(&p, 0, sizeof p);
@@ -426,12 +436,11 @@ pa_status decode_impl(int passes, int mode, const pa_plan* plan, const void* q, 
     p.out = out;
     p.out_stride_b = out_stride_b;
     {
-        const int64_t rows = (int64_t)pl.num_splits * 2 * p.rows;
+        const DecLayout L = decode_layout(pr, pl.num_splits);
         char* ws = static_cast<char*>(workspace);
         p.part_o = reinterpret_cast<float*>(ws);
-        const int64_t o_bytes = round_up(rows * value_dim(pr) * 4, 256);
-        p.part_lse = reinterpret_cast<float*>(ws + o_bytes);
-        p.seg_rec = reinterpret_cast<int32_t*>(ws + o_bytes + round_up(rows * 4, 256));
+        p.part_lse = reinterpret_cast<float*>(ws + L.lse);
+        p.seg_rec = reinterpret_cast<int32_t*>(ws + L.rec);
     }
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     const bool uniform = pr.page_size >= 16;

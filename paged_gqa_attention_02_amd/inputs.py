@@ -297,6 +297,15 @@ def decode_config(n: int, page_size: Optional[int] = None) -> DecodeCase:
     raise ValueError(f"no decode workload {n}")
 
 
+def mha_config(page_size: int = 16) -> DecodeCase:
+    """Multi-head decode (G = 1: one query head per kv head) at the
+    Llama-3-8B-shaped workload's sizes: B 64, 32/32 heads, D 128, bf16,
+    P 16, L ~ U{512..4096}, seed 7."""
+    rng = np.random.default_rng(7)
+    lens = rng.integers(512, 4096, size=64, endpoint=True)
+    return make_decode("mha", lens, 32, 32, 128, page_size, 7, lens_rng=rng)
+
+
 def make_mla_decode(name: str, lens: Sequence[int], Hq: int, Hkv: int, D: int, Dv: int,
                     page_size: int, seed: int, alias: bool = True, softcap: float = 0.0,
                     window: int = 0, num_splits: int = 0,

@@ -149,9 +149,11 @@ A = 1 << 20          # 16-byte aligned fake address
 DECODE_FNS = ["paged_attn_decode", "paged_attn_decode_split", "paged_attn_decode_merge"]
 
 
-def decode_status(plan_kw=None, fn="paged_attn_decode", **kw):
+def decode_status(plan_kw=None, fn="paged_attn_decode", edit=None, **kw):
     st, pl = plan_status(**(plan_kw or {}))
     assert st == OK
+    if edit is not None:
+        edit(pl)
     args = dict(q=A, q_stride_b=32 * 128, k=A, v=A, sp=16 * 8 * 128, st=8 * 128, sh=128,
                 num_pages=10, bt=A, bt_stride=256, sl=A, page_size=16, scale=0.1,
                 softcap=0.0, window=0, ks=1.0, vs=1.0, out=A, out_stride_b=32 * 128,
@@ -216,6 +218,30 @@ def test_latent_decode_validation():
     v = ctypes.c_void_p(A)
     assert pa.lib().paged_attn_gather(ctypes.byref(pl), v, v, 16 * 576, 576, 576, 10, v, 256,
                                       v, v, v, None) == UNSUP
+
+
+def _set(**fields):
+    def edit(pl):
+        for k, v in fields.items():
+            if k.startswith("prob."):
+                setattr(pl.prob, k[5:], v)
+            else:
+                setattr(pl, k, v)
+    return edit
+
+
+@pytest.mark.parametrize("edit", [
+    _set(num_splits=2048),                  # more blocks than the workspace was sized for
+    _set(**{"prob.num_seqs": 64}),          # more segment records
+    _set(**{"prob.num_q_heads": 64}),       # more partial rows per slot
+    _set(workspace_bytes=1 << 40),          # a size the layout does not give
+])
+@pytest.mark.parametrize("fn", DECODE_FNS + ["paged_attn_verify"])
+def test_decode_rejects_plan_edited_after_planning(fn, edit):
+    """The workspace layout follows from the plan's block count and problem;
+    a plan changed after paged_attn_plan is refused, not trusted."""
+    plan_kw = VERIFY if fn == "paged_attn_verify" else None
+    assert decode_status(plan_kw=plan_kw, fn=fn, edit=edit, ws_bytes=1 << 40) == MISMATCH
 
 
 def test_decode_empty_batch_launches_nothing():

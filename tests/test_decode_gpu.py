@@ -48,6 +48,12 @@ def test_workload_full_size(n, P):
     check(case, what=f"workload {n} P={case.page_size}")
 
 
+def test_mha_workload_full_size():
+    """G = 1 (one query head per kv head) at the Llama-3-8B-shaped sizes:
+    B 64, 32/32 heads, D 128, L ~ U{512..4096}."""
+    check(I.mha_config(), what="mha G1")
+
+
 @pytest.mark.parametrize("splits", [8, 32, 20000])
 def test_long_context_forced_splits(splits):
     case = I.decode_config(3)

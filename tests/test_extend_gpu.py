@@ -51,6 +51,12 @@ def check(case, what="", rows=None, num_splits=0):
     return out
 
 
+def test_extend_workload_all_rows():
+    """The full extend workload (3,577 new rows x 32 heads): every output
+    element against the oracle."""
+    check(I.extend_config(5), "extend workload (all rows)")
+
+
 def test_extend_workload_sampled_rows():
     """The full extend workload; 192 seeded rows (all heads) checked against
     the oracle, including each sequence's first and last row."""
