@@ -6,4 +6,5 @@ library (``paged_gqa_attention_02_amd``) and never imports it.
 """
 from .oracle import (bind, brute_decode, brute_extend, cache_append, decode,  # noqa: F401
                      decode_bf16, decode_e4m3fn, default_threads, encode_e4m3fn, extend,
+                     host_cpus,
                      lib, verify)
