@@ -7,32 +7,31 @@
 // new-token phase with its causal mask), finished by the division of the
 // accumulator by the softmax sum.
 //
-// Work: one block of kExtWaves waves per (tile of kExtRows rows, sequence b,
-// kv head g).  A row is (new token t, query head h of the group): the G heads
-// of a kv head share every K/V byte the block stages.  Each wave owns kRB MFMA
-// column blocks of 16 rows.  The block walks its key range [lo, C + t_last]
-// (lo from the sliding window of its first token) in tiles of 64 keys: key
-// j < C comes from page block_table[b][j / P], key j >= C is new row j - C.
-// Context and new keys share the key loop; the tiles are walked in runs of
-// one kind, and only the tiles that cross the causal diagonal or the window
-// edge, or hold both context and new keys, take the masked per-key path.
+// Work: an item is (sequence b, kv head g, row tile): kExtRows rows, a row
+// being (new token t, query head h of the group), so the G heads of a kv head
+// share every K/V byte a block stages.  Its keys are [lo, C + t_last] (lo from
+// the sliding window of its first token) in tiles of 64: key j < C comes from
+// page block_table[b][j / P], key j >= C is new row j - C.  Persistent blocks
+// take equal ranges of the key tiles of all items laid end to end (stream-K);
+// an item several blocks cover is finished by a log-sum-exp merge.
 //
-// Per tile, with v_mfma_f32_16x16x32_bf16:
-//   S^T[64 keys x 16 rows] = K[64 x D] Q^T[D x 16]     K read from LDS in the A
-//                                                     layout, Q^T in registers
-//   online softmax per row (a row is one MFMA column: 4 lanes hold its keys)
-//   O^T[D x 16] += V^T[D x 64] P^T[64 x 16]          P^T is the S^T accumulator
-//                                                     itself; V rows read from
-//                                                     LDS are transposed in
-//                                                     registers (v_perm)
-// K/V tiles live in LDS as bf16 rows of 2*D bytes whose 16-byte slots are
-// XOR-swizzled by the row index (slot s of row r holds chunk s ^ (r mod
-// slots)), so the operand reads of 16 lanes hit 16 different bank groups.
-// bf16 caches are staged with direct global->LDS loads (global_load_lds,
-// lane i of a wave fills bytes 16i..16i+15 of a 1 KB run); fp8 context rows go
-// through registers to be converted.  Two buffers: the next tile's loads are
-// in flight while this tile is computed.  The cache scales apply per key, to
-// the score (k_scale) and to P (v_scale).
+// Each wave owns 32 rows; per tile, with v_mfma_f32_32x32x16_bf16:
+//   S^T[64 keys x 32 rows] = K[64 x D] Q^T[D x 32]   K from LDS (A operand),
+//                                                   Q^T in registers
+//   online softmax: a row is one MFMA column, held by a lane pair (l, l^32)
+//   O^T[D x 32] += V^T[D x 64] P^T[64 x 32]          P^T is the S^T accumulator
+//                                                   itself; V^T comes from
+//                                                   transposing LDS reads
+// The wave computes the next tile's S^T while it runs this tile's softmax (the
+// two are independent), then this tile's P V.
+//
+// K/V tiles live in LDS as bf16 rows of 2*D bytes with 16-byte slots
+// XOR-swizzled by row, so that operand reads hit distinct banks.  bf16 caches
+// are staged with direct global->LDS loads (a wave fills whole 1 KB runs of
+// its own rows of a tile; with pages of >= 16 rows a run has one page, so its
+// base is wave-uniform and each lane adds a fixed offset); fp8 context rows go
+// through registers to be converted.  K is staged two tiles ahead, V one: the
+// loads of the next tiles are in flight while this tile is computed.
 #include <type_traits>
 
 #include "pa_device.h"
@@ -45,20 +44,16 @@ namespace {
 #ifndef PA_EXTEND_WAVES
 #define PA_EXTEND_WAVES 4
 #endif
-#ifndef PA_EXTEND_RB
-#define PA_EXTEND_RB 2
-#endif
 #ifndef PA_EXTEND_OCCUPANCY
 #define PA_EXTEND_OCCUPANCY 2
 #endif
 constexpr int kExtWaves = PA_EXTEND_WAVES;       // waves per block
-constexpr int kRB = PA_EXTEND_RB;                // 16-row column blocks per wave
 constexpr int kExtThreads = 64 * kExtWaves;
-constexpr int kExtRows = 16 * kRB * kExtWaves;   // rows (token, head) per block
+constexpr int kExtRows = 32 * kExtWaves;         // rows (token, head) per block
 constexpr int kExtKeys = 64;                     // keys per tile
 constexpr int kExtPages = 2048;                  // page ids staged in LDS at a time
-// waves per SIMD the kernel is compiled for
-constexpr int kExtOccupancy = PA_EXTEND_OCCUPANCY;
+constexpr int kExtOccupancy = PA_EXTEND_OCCUPANCY;   // waves per SIMD (bf16 caches)
+constexpr int kStageRows = kExtKeys / kExtWaves; // rows of a tile one wave stages
 
 // How scores become log2-domain logits.
 enum ScoreMode {
@@ -67,19 +62,8 @@ enum ScoreMode {
     kScale = 1,   // no cap, any scale: s*scale per score
     kCap = 2,     // soft-cap c*tanh(s*scale/c), per score
     kAlibi = 4,   // flag on kScale / kCap: plus slope * (key - query position)
-};
-
-// Key position (0..31) inside a 32-key step for MFMA contraction slot
-// (grp, jj): the S^T accumulators of key blocks 2ks and 2ks+1 are the P^T
-// operand with this order.
-__device__ __forceinline__ int step_key(int grp, int jj) {
-    return (jj < 4) ? 4 * grp + jj : 16 + 4 * grp + (jj - 4);
-}
-
-struct SeqInfo {
-    int b, kvh, n, C, q0;       // q0 = cu_seqlens_q[b]
-    int pg0;                    // first logical page of the staged page list
-    const int* pages;           // LDS: block_table[b][pg0 .. pg0 + kExtPages)
+    kVScale = 8,  // flag: cached values are scaled (v_scale != 1 or per-request
+                  // value descales); without it P V takes the values as stored
 };
 
 // LDS tile geometry: 64 rows of 2*D bytes, 16-byte slots swizzled by row.
@@ -88,16 +72,25 @@ struct Tile {
     static constexpr int kPitch = 2 * D;
     static constexpr int kSlots = kPitch / 16;
     static constexpr int kBytes = kExtKeys * kPitch;
-    static __device__ __forceinline__ int off(int row, int slot) {
-        return row * kPitch + 16 * (slot ^ (row & (kSlots - 1)));
+    static constexpr int kRowsPerRun = 1024 / kPitch;       // rows of a 1 KB run
+    static constexpr int kRuns = kStageRows / kRowsPerRun;  // runs one wave stages
+    static_assert(kRuns >= 1, "a wave stages whole runs");
+    // K: the 16-byte operand reads of 16 consecutive rows at one logical slot
+    // land on 16 different 16-byte bank groups.
+    static __device__ __forceinline__ int kswz(int r) {
+        return (kPitch == 256 ? r : (r >> 1)) & (kSlots - 1);
     }
-    // V tiles: slot s of row r is stored at slot s ^ vswz(r), so the four
-    // rows a 16-lane transposing read takes (4 consecutive keys, 32 bytes
-    // each) fall on four different 32-byte bank groups.
-    static __device__ __forceinline__ int vswz(int row) { return 2 * (row & 3); }
-    static __device__ __forceinline__ int voff(int row, int slot) {
-        return row * kPitch + 16 * (slot ^ vswz(row));
+    // V: a half-wave's transposing reads cover one 64-byte window of four
+    // consecutive rows; the window moves with the row so the four are disjoint.
+    static __device__ __forceinline__ int vswz(int r) {
+        return kPitch == 256 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
     }
+};
+
+struct SeqInfo {
+    int b, kvh, n, C, q0;       // q0 = cu_seqlens_q[b]
+    int pg0;                    // first logical page of the staged page list
+    const int* pages;           // LDS: block_table[b][pg0 .. pg0 + kExtPages)
 };
 
 // Addresses of key j's K and V rows: context rows through the staged page list
@@ -122,122 +115,109 @@ __device__ __forceinline__ void key_rows(const ExtendParams& p, const SeqInfo& s
                : static_cast<const uint8_t*>(p.v_new) + nw;
 }
 
-// bf16: one tile of K and V rows straight into LDS.  The tile is kRuns runs of
-// 1 KB (kRowsPer rows); wave w issues runs w, w + kExtWaves, ...  Lane l fills
-// slot l % kSlots of its row with the row's chunk (slot ^ swizzle).
-template <int D>
-__device__ __forceinline__ void stage_direct(const ExtendParams& p, const SeqInfo& si, int jt,
-                                             uint8_t* kd, uint8_t* vd) {
-    using TL = Tile<D>;
-    constexpr int kRowsPer = 1024 / TL::kPitch;
-    constexpr int kRuns = kExtKeys / kRowsPer;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int slot = lane % TL::kSlots;
-#pragma unroll
-    for (int run = wave; run < kRuns; run += kExtWaves) {
-        const int row = run * kRowsPer + lane / TL::kSlots;
-        const uint8_t *k, *v;
-        key_rows<D, false>(p, si, jt + row, k, v);
-        const int kchunk = 16 * (slot ^ (row & (TL::kSlots - 1)));
-        const int vchunk = 16 * (slot ^ TL::vswz(row));
-        __builtin_amdgcn_global_load_lds(
-            (const void __attribute__((address_space(1)))*)(k + kchunk),
-            (void __attribute__((address_space(3)))*)(kd + run * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(
-            (const void __attribute__((address_space(1)))*)(v + vchunk),
-            (void __attribute__((address_space(3)))*)(vd + run * 1024), 16, 0, 0);
-    }
+// A value the compiler can neither see through nor hoist out of a loop.
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+    asm volatile("" : "+v"(x));
+    return x;
 }
 
-// bf16 with page size >= 16: a run (kRowsPer rows) never crosses a page, so
-// each run takes one wave-uniform base address (its page from the staged
-// list, or its first new row) and every lane a fixed offset: its row within
-// the run times the row stride, plus its swizzled chunk (the swizzle of the
-// rows a wave stages does not change from run to run).  A run that holds
-// both context and new keys, or new rows past the sequence, takes the
-// per-lane path above.
-template <int D>
-struct StageLane {
-    uint32_t ctx_off, new_off;       // K
-    uint32_t vctx_off, vnew_off;     // V (its own swizzle)
-    __device__ __forceinline__ void init(const ExtendParams& p) {
-        using TL = Tile<D>;
-        constexpr int kRowsPer = 1024 / TL::kPitch;
-        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-        const int slot = lane % TL::kSlots;
-        const int row = wave * kRowsPer + lane / TL::kSlots;   // its first run's row
-        const uint32_t kchunk = 16 * (slot ^ (row & (TL::kSlots - 1)));
-        const uint32_t vchunk = 16 * (slot ^ TL::vswz(row));
-        const uint32_t ctx_row = (uint32_t)(lane / TL::kSlots) * (uint32_t)(p.s_tok * 2);
-        const uint32_t new_row = (uint32_t)(lane / TL::kSlots) * (uint32_t)(p.num_kv_heads * D * 2);
-        ctx_off = ctx_row + kchunk;
-        new_off = new_row + kchunk;
-        vctx_off = ctx_row + vchunk;
-        vnew_off = new_row + vchunk;
-    }
-};
+// LDS byte address (32 bits) of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
 
-template <int D>
-__device__ __forceinline__ void stage_runs(const ExtendParams& p, const SeqInfo& si, int jt,
-                                           uint8_t* kd, uint8_t* vd, const StageLane<D>& sl) {
+// Global -> LDS loads of 16 bytes a lane: lane i fills LDS bytes lds + 16i ..
+// + 15 (lds wave-uniform).  They are issued in inline asm, so the compiler
+// does not track these LDS writes and puts no wait for them in front of the
+// operand reads of the other buffer; the kernel waits for them itself
+// (s_waitcnt vmcnt(0)) before the barrier that hands the buffer to its
+// readers.  Two address forms: a wave-uniform base plus a 32-bit lane offset,
+// or a per-lane 64-bit address.
+// (M0, which the instruction takes the LDS address from, is saved and
+// restored around it.)
+__device__ __forceinline__ void load_lds16(const uint8_t* base, uint32_t off, uint32_t lds) {
+    uint32_t keep;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\t"
+                 "global_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+                 : "=&s"(keep) : "v"(off), "s"(base), "s"(lds) : "memory");
+}
+__device__ __forceinline__ void load_lds16(const uint8_t* addr, uint32_t lds) {
+    uint32_t keep;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\t"
+                 "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(keep) : "v"(addr), "s"(lds) : "memory");
+}
+
+// bf16: this wave's rows of tile jt of K (V = false) or V straight into LDS
+// at the byte address dst.  In a 1 KB run (kRowsPerRun rows) lane i fills LDS
+// bytes 16i..16i+15, i.e. slot i % kSlots of row i / kSlots, with the row's
+// chunk (slot ^ swizzle).  Rows in one page (pages of >= kStageRows rows) or
+// all new rows inside the sequence take one wave-uniform base and a 32-bit
+// lane offset; others go lane by lane.
+template <int D, bool V>
+__device__ __forceinline__ void stage_rows(const ExtendParams& p, const SeqInfo& si, int jt,
+                                           uint32_t dst) {
     using TL = Tile<D>;
-    constexpr int kRowsPer = 1024 / TL::kPitch;
-    constexpr int kRuns = kExtKeys / kRowsPer;
-    constexpr int kPer = kRuns / kExtWaves;                  // runs per wave
+    // (the lane's row and slot are recomputed per call: nothing lane-dependent
+    // of the staging stays live across the tile loop)
+    const int lane = (int)opaque(threadIdx.x & 63);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int pmask = (1 << p.page_shift) - 1;
-    // the runs' page ids first (one wait for all of them)
-    int pg[kPer];
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-        const int j0 = jt + (wave + k * kExtWaves) * kRowsPer;
+    const int rr = lane / TL::kSlots, sl = lane % TL::kSlots;
+    const int j0 = jt + wave * kStageRows;
+    const uint32_t d0 = dst + wave * TL::kRuns * 1024;
+    auto chunk = [&](int k) {
+        const int r = wave * kStageRows + k * TL::kRowsPerRun + rr;
+        return (uint32_t)(16 * (sl ^ (V ? TL::vswz(r) : TL::kswz(r))));
+    };
+    if ((1 << p.page_shift) >= kStageRows && j0 + kStageRows <= si.C) {
         const int idx = min(max((j0 >> p.page_shift) - si.pg0, 0), kExtPages - 1);
-        pg[k] = si.pages[idx];
-    }
+        const int64_t page = __builtin_amdgcn_readfirstlane(si.pages[idx]);
+        const int pmask = (1 << p.page_shift) - 1;
+        const uint8_t* pool = static_cast<const uint8_t*>(V ? p.v_pool : p.k_pool);
+        const uint8_t* base = pool + (page * p.s_page + (int64_t)(j0 & pmask) * p.s_tok +
+                                      (int64_t)si.kvh * p.s_head) * 2;
+        const uint32_t lrow = (uint32_t)rr * (uint32_t)(p.s_tok * 2);
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-        const int run = wave + k * kExtWaves;
-        const int j0 = jt + run * kRowsPer;                  // the run's first key
-        const uint8_t *kb, *vb;
-        uint32_t off, voff;
-        if (j0 + kRowsPer <= si.C) {
-            const int64_t page = __builtin_amdgcn_readfirstlane(pg[k]);
-            const int64_t o = (page * p.s_page + (int64_t)(j0 & pmask) * p.s_tok +
-                               (int64_t)si.kvh * p.s_head) * 2;
-            kb = static_cast<const uint8_t*>(p.k_pool) + o;
-            vb = static_cast<const uint8_t*>(p.v_pool) + o;
-            off = sl.ctx_off;
-            voff = sl.vctx_off;
-        } else if (j0 >= si.C && j0 + kRowsPer <= si.C + si.n) {
-            const int64_t o = ((int64_t)(si.q0 + j0 - si.C) * p.num_kv_heads + si.kvh) * D * 2;
-            kb = static_cast<const uint8_t*>(p.k_new) + o;
-            vb = static_cast<const uint8_t*>(p.v_new) + o;
-            off = sl.new_off;
-            voff = sl.vnew_off;
-        } else {
-            const int lane = threadIdx.x & 63;
-            const int row = run * kRowsPer + lane / TL::kSlots;
-            key_rows<D, false>(p, si, jt + row, kb, vb);
-            off = 16 * ((lane % TL::kSlots) ^ (row & (TL::kSlots - 1)));
-            voff = 16 * ((lane % TL::kSlots) ^ TL::vswz(row));
+        for (int k = 0; k < TL::kRuns; ++k)
+            load_lds16(base + (int64_t)k * TL::kRowsPerRun * p.s_tok * 2, lrow + chunk(k),
+                       d0 + k * 1024);
+    } else if (j0 >= si.C && j0 + kStageRows <= si.C + si.n) {
+        const uint8_t* nrow = static_cast<const uint8_t*>(V ? p.v_new : p.k_new);
+        const int64_t rs = (int64_t)p.num_kv_heads * D * 2;
+        const uint8_t* base = nrow + ((int64_t)(si.q0 + j0 - si.C) * p.num_kv_heads + si.kvh) *
+                                         D * 2;
+        const uint32_t lrow = (uint32_t)rr * (uint32_t)rs;
+#pragma unroll
+        for (int k = 0; k < TL::kRuns; ++k)
+            load_lds16(base + k * TL::kRowsPerRun * rs, lrow + chunk(k), d0 + k * 1024);
+    } else {
+        // lane by lane: context rows through the page list, new rows (clamped
+        // to the sequence's last one: finite, masked by the consumer) from
+        // k_new / v_new
+        const uint8_t* pool = static_cast<const uint8_t*>(V ? p.v_pool : p.k_pool);
+        const uint8_t* nrow = static_cast<const uint8_t*>(V ? p.v_new : p.k_new);
+        const int pmask = (1 << p.page_shift) - 1;
+#pragma unroll
+        for (int k = 0; k < TL::kRuns; ++k) {
+            const int j = jt + wave * kStageRows + k * TL::kRowsPerRun + rr;
+            const int idx = min(max((j >> p.page_shift) - si.pg0, 0), kExtPages - 1);
+            const int64_t ctx = ((int64_t)si.pages[idx] * p.s_page +
+                                 (int64_t)(j & pmask) * p.s_tok + (int64_t)si.kvh * p.s_head) * 2;
+            const int r = min(max(j - si.C, 0), si.n - 1);
+            const int64_t nw = ((int64_t)(si.q0 + r) * p.num_kv_heads + si.kvh) * D * 2;
+            const uint8_t* src = j < si.C ? pool + ctx : nrow + nw;
+            load_lds16(src + chunk(k), d0 + k * 1024);
         }
-        __builtin_amdgcn_global_load_lds(
-            (const void __attribute__((address_space(1)))*)(kb + off),
-            (void __attribute__((address_space(3)))*)(kd + run * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(
-            (const void __attribute__((address_space(1)))*)(vb + voff),
-            (void __attribute__((address_space(3)))*)(vd + run * 1024), 16, 0, 0);
     }
 }
 
-// fp8: global -> registers (16 elements a thread), converted and written to
-// the swizzled LDS tile as bf16.  Threads past kRowsPerPass * kLanesPerRow idle.
+// fp8 caches: a tile of K or V through registers, 16 elements a thread per
+// pass: context rows are e4m3fn (converted to bf16 while stored), new rows
+// bf16.  Threads past the tile's chunks idle.
 template <int D>
 struct Stage8 {
-    static constexpr int kLanesPerRow = D / 16;
-    static constexpr int kRowsPerPass = kExtThreads / kLanesPerRow < kExtKeys
-                                            ? kExtThreads / kLanesPerRow : kExtKeys;
-    static constexpr int kPasses = kExtKeys / kRowsPerPass;
+    static constexpr int kChunks = kExtKeys * D / 16;        // 16-element chunks a tile
+    static constexpr int kPasses = (kChunks + kExtThreads - 1) / kExtThreads;
     u32x4 a[kPasses], b[kPasses];
     bool ctx[kPasses];
 };
@@ -246,21 +226,22 @@ template <int D>
 __device__ __forceinline__ void stage8_load(Stage8<D>& S, const ExtendParams& p,
                                             const SeqInfo& si, int jt, bool second) {
     using ST = Stage8<D>;
-    if (threadIdx.x >= ST::kRowsPerPass * ST::kLanesPerRow) return;
-    const int chunk = threadIdx.x % ST::kLanesPerRow;
 #pragma unroll
     for (int i = 0; i < ST::kPasses; ++i) {
-        const int j = jt + i * ST::kRowsPerPass + threadIdx.x / ST::kLanesPerRow;
+        const int c = threadIdx.x + i * kExtThreads;
+        S.ctx[i] = true;
+        S.a[i] = S.b[i] = u32x4{0, 0, 0, 0};
+        if (c >= ST::kChunks) continue;
+        const int row = c / (D / 16), ch = c % (D / 16);
         const uint8_t *kr, *vr;
-        key_rows<D, true>(p, si, j, kr, vr);
-        const uint8_t* row = second ? vr : kr;
-        S.ctx[i] = j < si.C;
+        key_rows<D, true>(p, si, jt + row, kr, vr);
+        const uint8_t* r = second ? vr : kr;
+        S.ctx[i] = jt + row < si.C;
         if (S.ctx[i]) {
-            S.a[i] = *reinterpret_cast<const u32x4*>(row + 16 * chunk);
-            S.b[i] = u32x4{0, 0, 0, 0};
+            S.a[i] = *reinterpret_cast<const u32x4*>(r + 16 * ch);
         } else {
-            S.a[i] = *reinterpret_cast<const u32x4*>(row + 32 * chunk);
-            S.b[i] = *reinterpret_cast<const u32x4*>(row + 32 * chunk + 16);
+            S.a[i] = *reinterpret_cast<const u32x4*>(r + 32 * ch);
+            S.b[i] = *reinterpret_cast<const u32x4*>(r + 32 * ch + 16);
         }
     }
 }
@@ -269,11 +250,11 @@ template <int D, bool V>
 __device__ __forceinline__ void stage8_store(const Stage8<D>& S, uint8_t* lds) {
     using ST = Stage8<D>;
     using TL = Tile<D>;
-    if (threadIdx.x >= ST::kRowsPerPass * ST::kLanesPerRow) return;
-    const int chunk = threadIdx.x % ST::kLanesPerRow;
 #pragma unroll
     for (int i = 0; i < ST::kPasses; ++i) {
-        const int row = i * ST::kRowsPerPass + threadIdx.x / ST::kLanesPerRow;
+        const int c = threadIdx.x + i * kExtThreads;
+        if (c >= ST::kChunks) continue;
+        const int row = c / (D / 16), ch = c % (D / 16);
         u32x4 lo = S.a[i], hi = S.b[i];
         if (S.ctx[i]) {
             const u32x2 e0 = e4m3x4_to_bf16x4(S.a[i].x), e1 = e4m3x4_to_bf16x4(S.a[i].y);
@@ -281,10 +262,9 @@ __device__ __forceinline__ void stage8_store(const Stage8<D>& S, uint8_t* lds) {
             lo = u32x4{e0.x, e0.y, e1.x, e1.y};
             hi = u32x4{e2.x, e2.y, e3.x, e3.y};
         }
-        const int o0 = V ? TL::voff(row, 2 * chunk) : TL::off(row, 2 * chunk);
-        const int o1 = V ? TL::voff(row, 2 * chunk + 1) : TL::off(row, 2 * chunk + 1);
-        *reinterpret_cast<u32x4*>(lds + o0) = lo;
-        *reinterpret_cast<u32x4*>(lds + o1) = hi;
+        const int sw = V ? TL::vswz(row) : TL::kswz(row);
+        *reinterpret_cast<u32x4*>(lds + row * TL::kPitch + 16 * ((2 * ch) ^ sw)) = lo;
+        *reinterpret_cast<u32x4*>(lds + row * TL::kPitch + 16 * ((2 * ch + 1) ^ sw)) = hi;
     }
 }
 
@@ -292,235 +272,263 @@ __device__ __forceinline__ void stage8_store(const Stage8<D>& S, uint8_t* lds) {
 // left at their maxima).
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// Running state of one wave: kRB column blocks of 16 rows.
-template <int D>
-struct ExtAcc {
-    static constexpr int kVE = D / 16;
-    float m[kRB], l[kRB];
-    f32x4 o[kRB][kVE];
-};
 
-// Per-lane byte offsets of the operand reads inside a swizzled tile.
-//   K: row 16kb + c, slot 4ds + grp is at kb*16*pitch + koff[ds].
-//   V: transposing reads (ds_read_b64_tr_b16: within each 16 lanes, lane i
-//      receives element e from the 8 bytes lane 4e + i/4 read, element i % 4).
-//      Lane (grp, s = 4e + q) reads key row 32ks + 16h + 4grp + e, elements
-//      16*dblk + 4q .. +3, at ks*32*pitch + h*16*pitch + vtr[dblk]; lane i
-//      then holds d = 16*dblk + i of keys 32ks + 16h + 4grp + 0..3, the A
-//      operand of O^T += V^T P^T in the step_key order.
+// Per-lane LDS byte offsets of the operand reads (lane l, h = l / 32).
+//   K (A operand of S^T): key row 32kb + l%32, d = 16ds + 8h .. +7, i.e.
+//     logical slot 2ds + h: koff[ds] (+ 32kb rows; the swizzle depends on
+//     l % 32 only).
+//   V^T (A operand of O^T, 32 d x 16 keys for 32x32x16): transposing reads
+//     (ds_read_b64_tr_b16: within each 16 lanes, lane i receives element e
+//     from the 8 bytes lane 4e + i/4 read, element i % 4).  Lane (group g =
+//     l/16, e = (l%16)/4, q = l%4) reads key row R + 4h + e (and R + 8 + 4h + e)
+//     at d = 32db + 16(g%2) + 4q; lane l then holds d = 32db + l%32 of keys
+//     R + 4h + 0..3 (and R + 8 + 4h + 0..3): contraction slots 0..7 of lane
+//     half h.  R = 32kb + 16(s%2) for P V step s: voff[db] (R = 0).
 template <int D>
 struct LaneOffs {
-    int koff[D / 32];
-    int vtr[D / 16];
-    __device__ __forceinline__ void init(int c, int grp) {
+    int koff[D / 16];
+    int voff[D / 32];
+    // offsets into buffer `buf` (0 or 1) of the K and V tile pairs
+    __device__ __forceinline__ void init(int lane, int buf) {
         using TL = Tile<D>;
+        const int r = lane & 31, h = lane >> 5;
 #pragma unroll
-        for (int ds = 0; ds < D / 32; ++ds) koff[ds] = TL::off(c, 4 * ds + grp);
-        const int e = c >> 2, q = c & 3;
-        const int row = 4 * grp + e;                    // (+ 32ks + 16h: same swizzle)
+        for (int ds = 0; ds < D / 16; ++ds)
+            koff[ds] = buf * TL::kBytes + r * TL::kPitch + 16 * ((2 * ds + h) ^ TL::kswz(r));
+        const int g = lane >> 4, e = (lane & 15) >> 2, q = lane & 3;
+        const int row = 4 * h + e;                   // (+ R: same swizzle)
 #pragma unroll
-        for (int dblk = 0; dblk < D / 16; ++dblk)
-            vtr[dblk] = TL::voff(row, 2 * dblk + (q >> 1)) + 8 * (q & 1);
+        for (int db = 0; db < D / 32; ++db)
+            voff[db] = buf * TL::kBytes + row * TL::kPitch +
+                       16 * ((4 * db + 2 * (g & 1) + (q >> 1)) ^ TL::vswz(row)) + 8 * (q & 1);
+    }
+    // the other buffer (kBytes is a power of two and offsets stay below
+    // 2 * kBytes)
+    __device__ __forceinline__ void toggle() {
+#pragma unroll
+        for (int ds = 0; ds < D / 16; ++ds) koff[ds] ^= Tile<D>::kBytes;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) voff[db] ^= Tile<D>::kBytes;
     }
 };
 
-// LDS byte address (32 bits) of a pointer into __shared__ memory.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// Eight transposing reads issued together and waited for inside one asm
-// block, so every output is complete when the block ends.  Through the
-// builtin the compiler has no alias information for these reads, and it
-// waits for every direct-to-LDS load in flight before them -- here the next
-// tile's loads into the other buffer, which P*V of this tile does not need.
-// Nothing writes the bytes read: this tile's loads completed before the
-// barrier that precedes its reads.
-__device__ __forceinline__ void lds_read_tr16_x8(u32x2 (&out)[8], const uint32_t (&a)[8]) {
-    uint64_t r0, r1, r2, r3, r4, r5, r6, r7;
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %8\n\t"
-        "ds_read_b64_tr_b16 %1, %9\n\t"
-        "ds_read_b64_tr_b16 %2, %10\n\t"
-        "ds_read_b64_tr_b16 %3, %11\n\t"
-        "ds_read_b64_tr_b16 %4, %12\n\t"
-        "ds_read_b64_tr_b16 %5, %13\n\t"
-        "ds_read_b64_tr_b16 %6, %14\n\t"
-        "ds_read_b64_tr_b16 %7, %15\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6),
-          "=&v"(r7)
-        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
-          "v"(a[7])
-        : "memory");
-    out[0] = __builtin_bit_cast(u32x2, r0);
-    out[1] = __builtin_bit_cast(u32x2, r1);
-    out[2] = __builtin_bit_cast(u32x2, r2);
-    out[3] = __builtin_bit_cast(u32x2, r3);
-    out[4] = __builtin_bit_cast(u32x2, r4);
-    out[5] = __builtin_bit_cast(u32x2, r5);
-    out[6] = __builtin_bit_cast(u32x2, r6);
-    out[7] = __builtin_bit_cast(u32x2, r7);
-}
-
-// Logit (log2 domain) of a raw score for kScale / kCap.  SPLIT: the tile
-// holds context and new keys, whose scales differ.
-template <int MODE, bool SPLIT>
-__device__ __forceinline__ float logit(float v, const ExtendParams& p, bool ctx, float qs,
-                                       float c1) {
-    if constexpr (MODE == kCap) {
-        const float k1 = SPLIT ? (ctx ? p.cap_c1_ctx : p.cap_c1) : c1;
-        return p.cap_c2 - 2.f * p.cap_c2 * fast_rcp(fast_exp2(v * k1) + 1.f);
-    } else {
-        return v * (SPLIT ? (ctx ? p.qk_scale2_ctx : p.qk_scale2) : qs);
-    }
-}
-
-// Scale (or soft-cap), mask and online softmax of one tile's scores, then
-// P^T as B operands.  MASK: the tile crosses the causal diagonal or the
-// window edge; SPLIT: it holds context and new keys (per-key scales).
-template <int D, int MODE, bool MASK, bool SPLIT>
-__device__ __forceinline__ void tile_softmax(f32x4 (&s)[kRB][4], u32x4 (&pop)[kRB][2],
-                                             ExtAcc<D>& A, const ExtendParams& p,
-                                             const SeqInfo& si, const int (&pos_q)[kRB],
-                                             const float (&al2)[kRB], int jt) {
-    constexpr int kVE = D / 16;
-    constexpr int kBase = MODE & 3;
-    constexpr bool kAl = (MODE & kAlibi) != 0;
-    constexpr bool kFolded = kBase == kFold && !SPLIT;
-    static_assert(!(kAl && kBase == kFold), "ALiBi takes the per-score path");
-    const int grp = (threadIdx.x & 63) >> 4;
-    const bool all_ctx = jt + kExtKeys <= si.C;
-    const float qs = all_ctx ? p.qk_scale2_ctx : p.qk_scale2;
-    const float c1 = all_ctx ? p.cap_c1_ctx : p.cap_c1;
-    const float vsu = all_ctx ? p.v_scale : 1.f;          // (not SPLIT)
-    const int key0 = jt + 4 * grp;                          // key of s[.][kb][j]: key0 + 16kb + j
-#pragma unroll
-    for (int rb = 0; rb < kRB; ++rb) {
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int key = key0 + 16 * kb + j;
-                float v = s[rb][kb][j];
-                if constexpr (!kFolded)
-                    v = logit<kBase == kFold ? kScale : kBase, SPLIT>(v, p, key < si.C, qs, c1);
-                if constexpr (kAl) v += al2[rb] * (float)(key - pos_q[rb]);
-                if constexpr (MASK) {
-                    const bool keep = key <= pos_q[rb] &&
-                                      (p.window <= 0 || pos_q[rb] - key < p.window);
-                    v = keep ? v : -INFINITY;
-                }
-                s[rb][kb][j] = v;
-                tmax = fmaxf(tmax, v);
-            }
-        tmax = col4_max(tmax);
-        if constexpr (kFolded) tmax *= qs;
-        // Lazy rescale: the reference max m of a row moves only when a score
-        // exceeds it by more than kSlack (log2 units), so p <= 2^kSlack and
-        // the accumulators are rescaled rarely (for every row of the wave at
-        // once, each by its own factor).
-        constexpr float kSlack = 8.f;
-        const bool move = __any(tmax > A.m[rb] + kSlack);
-        const float m_new = move ? fmaxf(A.m[rb], tmax) : A.m[rb];
-        const float ms = m_new == -INFINITY ? 0.f : m_new;   // row with no key yet
-        const float alpha = fast_exp2(A.m[rb] - ms);
-        float psum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                float pr;
-                if constexpr (kFolded) pr = fast_exp2(__builtin_fmaf(s[rb][kb][j], qs, -ms));
-                else pr = fast_exp2(s[rb][kb][j] - ms);
-                psum += pr;
-                if constexpr (SPLIT)
-                    s[rb][kb][j] = key0 + 16 * kb + j < si.C ? pr * p.v_scale : pr;
-                else
-                    s[rb][kb][j] = pr;
-            }
-        if constexpr (!SPLIT) {
-            if (vsu != 1.f) {
-#pragma unroll
-                for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) s[rb][kb][j] *= vsu;
-            }
-        }
-        A.l[rb] = A.l[rb] * alpha + psum;
-        A.m[rb] = m_new;
-        if (move) {
-#pragma unroll
-            for (int e = 0; e < kVE; ++e) A.o[rb][e] *= alpha;
-        }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-            pop[rb][ks] = u32x4{pack_bf16x2(s[rb][2 * ks][0], s[rb][2 * ks][1]),
-                                pack_bf16x2(s[rb][2 * ks][2], s[rb][2 * ks][3]),
-                                pack_bf16x2(s[rb][2 * ks + 1][0], s[rb][2 * ks + 1][1]),
-                                pack_bf16x2(s[rb][2 * ks + 1][2], s[rb][2 * ks + 1][3])};
-    }
-}
-
-// One tile of 64 keys starting at jt, K and V in the swizzled LDS tiles.
-// FAST: the tile needs no mask and holds one kind of key (context or new).
-template <int D, int MODE, bool FAST>
-__device__ __forceinline__ void tile_compute(const uint8_t* kl, const uint8_t* vl,
-                                             const LaneOffs<D>& lo,
-                                             const u32x4 (&qop)[kRB][D / 32], ExtAcc<D>& A,
-                                             const ExtendParams& p, const SeqInfo& si,
-                                             const int (&pos_q)[kRB], const float (&al2)[kRB],
-                                             int jt) {
+// S^T = K Q^T for key half H (keys 32H .. 32H+31) of a 64-key tile (kt: the
+// K buffer pair; koff selects the buffer): s[j] is the score of key
+// 32H + 8(j/4) + 4h + j%4 against the lane's row.
+template <int D, int H>
+__device__ __forceinline__ void qk_half(f32x16& s, const uint8_t* kt, const LaneOffs<D>& lo,
+                                        const u32x4 (&q)[D / 16]) {
     constexpr int kPitch = Tile<D>::kPitch;
-    constexpr int kDS = D / 32;
-    constexpr int kVE = D / 16;
+    // every operand read is issued before the first MFMA, so the reads'
+    // latencies overlap
+    u32x4 a[D / 16];
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds)
+        a[ds] = *reinterpret_cast<const u32x4*>(kt + H * 32 * kPitch + lo.koff[ds]);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 acc = {};
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) acc = mfma_bf16_32x32x16(a[ds], q[ds], acc);
+    s = acc;
+}
 
-    // ---- S^T = K Q^T: s[rb][kb][j] = score of key 16kb + 4grp + j, row c ----
-    f32x4 s[kRB][4];
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+
+// One transposing read (ds_read_b64_tr_b16) of 8 bytes at an LDS address.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* p) {
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (i16x4 __attribute__((address_space(3)))*)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+// O^T += V^T P^T for key half H (vt: the V buffer pair; voff selects the
+// buffer): P V steps s = 2H + t (t = 0, 1) cover keys
+// 32H + 16t + ..., with B operands pk[t] (accumulator slots 8t .. 8t+7).
+// The D/32 operands of a step are read (two transposing reads each) before
+// its MFMAs.
+template <int D, int H>
+__device__ __forceinline__ void pv_half(f32x16 (&o)[D / 32], const uint8_t* vt,
+                                        const LaneOffs<D>& lo, const u32x4 (&pk)[2]) {
+    constexpr int kPitch = Tile<D>::kPitch;
+    constexpr int kDB = D / 32;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int t = 0; t < 2; ++t) {
+        u32x2 v[2 * kDB];
 #pragma unroll
-        for (int rb = 0; rb < kRB; ++rb) s[rb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int db = 0; db < kDB; ++db) {
+            const uint8_t* r = vt + (32 * H + 16 * t) * kPitch + lo.voff[db];
+            v[2 * db] = lds_read_tr16(r);
+            v[2 * db + 1] = lds_read_tr16(r + 8 * kPitch);
+        }
 #pragma unroll
-        for (int ds = 0; ds < kDS; ++ds) {
-            const u32x4 a =
-                *reinterpret_cast<const u32x4*>(kl + kb * 16 * kPitch + lo.koff[ds]);
+        for (int db = 0; db < kDB; ++db)
+            o[db] = mfma_bf16_32x32x16(u32x4{v[2 * db].x, v[2 * db].y, v[2 * db + 1].x,
+                                             v[2 * db + 1].y},
+                                       pk[t], o[db]);
+    }
+}
+
+__device__ __forceinline__ float vmax(float a, float b) {
+    return __builtin_elementwise_maximum(a, b);
+}
+
+// Running state of one wave's lane: its row's max (log2 units, lazy) and this
+// lane's share of the row sum; O^T accumulators.
+template <int D>
+struct ExtAcc {
+    float m, l;
+    f32x16 o[D / 32];
+};
+
+// Per-tile constants of the softmax (one key kind).
+struct TileScale {
+    float qs, c1, vs;       // score scale, soft-cap factor, value scale
+};
+
+// The online softmax of one key half's scores, in steps:
+//   logits: scale (or soft-cap) in place -- FAST tiles (no mask, one key kind)
+//     with MODE kFold keep raw scores, the positive scale is folded into the
+//     exponent -- masks of a non-FAST tile (causal limit and window of the
+//     lane's row, per-key kind), and the lane's max;
+//   row_max: the lane pair's max; whether any row of the wave moves its
+//     reference max (lazy rescale: only when a score exceeds it by more than
+//     8 in log2 units, so p <= 2^8), and the rescale factor;
+//   exps: p = 2^(logit - m) in place, and their sum;
+//   pack: value scales and the bf16 B operands of P V.
+struct SoftmaxState {
+    float m_new, ms, alpha;
+    bool move;
+};
+
+template <int MODE, bool FAST>
+__device__ __forceinline__ float sm_logits(f32x16& s, const ExtendParams& p, const SeqInfo& si,
+                                           const TileScale& ts, int pos_q, float al2,
+                                           int key0) {
+    constexpr bool kAl = (MODE & kAlibi) != 0;
+    constexpr bool kFolded = (MODE & 7) == kFold && FAST;
 #pragma unroll
-            for (int rb = 0; rb < kRB; ++rb)
-                s[rb][kb] = mfma_bf16_16x16x32(a, qop[rb][ds], s[rb][kb]);
+    for (int j = 0; j < 16; ++j) {
+        float v = s[j];
+        const int key = key0 + 8 * (j >> 2) + (j & 3);
+        if constexpr (!kFolded) {
+            const bool ctx = key < si.C;
+            const float qs = FAST ? ts.qs : (ctx ? p.qk_scale2_ctx : p.qk_scale2);
+            if constexpr ((MODE & 3) == kCap) {
+                const float c1 = FAST ? ts.c1 : (ctx ? p.cap_c1_ctx : p.cap_c1);
+                v = p.cap_c2 - 2.f * p.cap_c2 * fast_rcp(fast_exp2(v * c1) + 1.f);
+            } else {
+                v *= qs;
+            }
+        }
+        if constexpr (kAl) v += al2 * (float)(key - pos_q);
+        if constexpr (!FAST) {
+            const bool keep = key <= pos_q && (p.window <= 0 || pos_q - key < p.window);
+            v = keep ? v : -INFINITY;
+        }
+        s[j] = v;
+    }
+    // (maximum: NaN-propagating, no input canonicalisation; three-input
+    // instructions on gfx950)
+    const float a = vmax(vmax(s[0], s[1]), s[2]), b = vmax(vmax(s[3], s[4]), s[5]);
+    const float c = vmax(vmax(s[6], s[7]), s[8]), d = vmax(vmax(s[9], s[10]), s[11]);
+    const float e = vmax(vmax(s[12], s[13]), s[14]);
+    return vmax(vmax(vmax(a, b), c), vmax(vmax(d, e), s[15]));
+}
+
+template <int MODE, bool FAST>
+__device__ __forceinline__ SoftmaxState sm_row_max(float lane_max, float m, const TileScale& ts) {
+    constexpr float kSlack = 8.f;
+    float tmax = pair_max(lane_max);
+    if constexpr ((MODE & 7) == kFold && FAST) tmax *= ts.qs;
+    SoftmaxState st;
+    st.move = __builtin_amdgcn_ballot_w64(tmax > m + kSlack) != 0;
+    st.m_new = st.move ? fmaxf(m, tmax) : m;
+    st.ms = st.m_new == -INFINITY ? 0.f : st.m_new;   // a row with no key yet
+    st.alpha = fast_exp2(m - st.ms);
+    return st;
+}
+
+template <int MODE, bool FAST>
+__device__ __forceinline__ float sm_exps(f32x16& s, const SoftmaxState& st, float qs) {
+    constexpr bool kFolded = (MODE & 7) == kFold && FAST;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        s[j] = kFolded ? fast_exp2(__builtin_fmaf(s[j], qs, -st.ms)) : fast_exp2(s[j] - st.ms);
+    float t[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t[i] = (s[4 * i] + s[4 * i + 1]) + (s[4 * i + 2] + s[4 * i + 3]);
+    return (t[0] + t[1]) + (t[2] + t[3]);
+}
+
+template <int MODE, bool FAST>
+__device__ __forceinline__ void sm_pack(f32x16& s, u32x4 (&pk)[2], const SeqInfo& si,
+                                        const TileScale& ts, int key0) {
+    if constexpr ((MODE & kVScale) != 0) {
+        if constexpr (FAST) {
+            s *= ts.vs;
+        } else {
+            // context keys take the cache's value scale, new keys none
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                s[j] *= key0 + 8 * (j >> 2) + (j & 3) < si.C ? ts.vs : 1.f;
         }
     }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+        pk[t] = u32x4{pack_bf16x2(s[8 * t], s[8 * t + 1]), pack_bf16x2(s[8 * t + 2], s[8 * t + 3]),
+                      pack_bf16x2(s[8 * t + 4], s[8 * t + 5]),
+                      pack_bf16x2(s[8 * t + 6], s[8 * t + 7])};
+}
 
-    // ---- scale / cap, mask, online softmax; P^T operands ----
-    u32x4 pop[kRB][2];
-    tile_softmax<D, MODE, !FAST, !FAST>(s, pop, A, p, si, pos_q, al2, jt);
+// The online softmax of a key half's scores s: updates the row statistics and
+// returns the packed probabilities and whether (and by what) to rescale O.
+template <int MODE, bool FAST>
+__device__ __forceinline__ SoftmaxState half_softmax(f32x16& s, u32x4 (&pk)[2], float& m,
+                                                     float& l, const ExtendParams& p,
+                                                     const SeqInfo& si, const TileScale& ts,
+                                                     int pos_q, float al2, int key0) {
+    const float lane_max = sm_logits<MODE, FAST>(s, p, si, ts, pos_q, al2, key0);
+    const SoftmaxState st = sm_row_max<MODE, FAST>(lane_max, m, ts);
+    const float ps = sm_exps<MODE, FAST>(s, st, ts.qs);
+    l = l * st.alpha + ps;
+    m = st.m_new;
+    sm_pack<MODE, FAST>(s, pk, si, ts, key0);
+    return st;
+}
 
-    // ---- O^T += V^T P^T: MFMA dblk covers d = 16*dblk .. +15; its A operand
-    // (V^T rows d, keys in step_key order) comes from two transposing reads,
-    // four blocks' reads at a time ----
-    const uint32_t vb = lds_addr(vl);
+// Key half H of a tile in order: S^T = K Q^T, the online softmax (the masked
+// variant unless the tile is FAST), P V.  Only the softmax differs between
+// the variants, so the accumulators never pass through the branch.
+template <int D, int MODE, int H>
+__device__ __forceinline__ void half_step(bool fast, const uint8_t* kbuf, const uint8_t* vbuf,
+                                          const LaneOffs<D>& lo, const u32x4 (&q)[D / 16],
+                                          ExtAcc<D>& A, const ExtendParams& p,
+                                          const SeqInfo& si, const TileScale& ts, int pos_q,
+                                          float al2, int jt) {
+    constexpr int kDB = D / 32;
+    const int key0 = jt + 32 * H + 4 * ((threadIdx.x & 63) >> 5);
+    f32x16 s;
+    qk_half<D, H>(s, kbuf, lo, q);
+    u32x4 pk[2];
+    const SoftmaxState st =
+        fast ? half_softmax<MODE, true>(s, pk, A.m, A.l, p, si, ts, pos_q, al2, key0)
+             : half_softmax<MODE, false>(s, pk, A.m, A.l, p, si, ts, pos_q, al2, key0);
+    if (st.move) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-        for (int d0 = 0; d0 < kVE; d0 += 4) {
-            uint32_t ad[8];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                ad[2 * u] = vb + ks * 32 * kPitch + lo.vtr[d0 + u];
-                ad[2 * u + 1] = ad[2 * u] + 16 * kPitch;
-            }
-            u32x2 v[8];
-            lds_read_tr16_x8(v, ad);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const u32x4 a = {v[2 * u].x, v[2 * u].y, v[2 * u + 1].x, v[2 * u + 1].y};
-#pragma unroll
-                for (int rb = 0; rb < kRB; ++rb)
-                    A.o[rb][d0 + u] = mfma_bf16_16x16x32(a, pop[rb][ks], A.o[rb][d0 + u]);
-            }
-        }
+        for (int db = 0; db < kDB; ++db) A.o[db] *= st.alpha;
     }
+    pv_half<D, H>(A.o, vbuf, lo, pk);
+}
+
+// One 64-key tile: its two key halves in order.
+template <int D, int MODE>
+__device__ __forceinline__ void tile_inorder(bool fast, const uint8_t* kbuf,
+                                             const uint8_t* vbuf, const LaneOffs<D>& lo,
+                                             const u32x4 (&q)[D / 16], ExtAcc<D>& A,
+                                             const ExtendParams& p, const SeqInfo& si,
+                                             const TileScale& ts, int pos_q, float al2, int jt) {
+    half_step<D, MODE, 0>(fast, kbuf, vbuf, lo, q, A, p, si, ts, pos_q, al2, jt);
+    half_step<D, MODE, 1>(fast, kbuf, vbuf, lo, q, A, p, si, ts, pos_q, al2, jt);
 }
 
 // An item: row tile mt (kExtRows rows (token, head)) of sequence b, kv head
@@ -603,7 +611,7 @@ __global__ __launch_bounds__(kScanThreads) void extend_scan_kernel(ExtendParams 
 // writes normalised fp32 rows and their log2-sum-exp to the block's slot.
 // ---------------------------------------------------------------------------
 struct ExtLds {
-    uint8_t *k0, *v0, *k1, *v1;
+    uint8_t *k, *v;     // two K and two V tiles each (tile i in buffer i & 1)
     int* pages;
 };
 
@@ -611,8 +619,8 @@ template <int D, bool FP8, int MODE>
 __device__ __forceinline__ void extend_piece(const ExtendParams& pk, const Item& it, int from,
                                              int to, bool complete, int64_t w, int slot,
                                              const ExtLds& L) {
-    constexpr int kDS = D / 32;        // QK contraction steps
-    constexpr int kVE = D / 16;        // PV MFMAs per (row block, key step)
+    constexpr int kDS = D / 16;        // QK contraction steps
+    constexpr int kDB = D / 32;        // O^T blocks of 32 d
     ExtendParams p = pk;
     const int G = p.group;
     SeqInfo si;
@@ -631,175 +639,157 @@ __device__ __forceinline__ void extend_piece(const ExtendParams& pk, const Item&
     const int t0 = it.t0, t1 = it.t1;
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int c = lane & 15, grp = lane >> 4;
+    const int h = lane >> 5;
 
-    // ---- rows of this lane's column blocks, and Q^T as B operands ----
-    int row_t[kRB], pos_q[kRB];
-    bool row_ok[kRB];
-    float al2[kRB];                    // ALiBi slope of the row's head, log2 units
-    u32x4 qop[kRB][kDS];
-#pragma unroll
-    for (int rb = 0; rb < kRB; ++rb) {
-        const int r = (wave * kRB + rb) * 16 + c;
-        row_t[rb] = t0 + r / G;
-        row_ok[rb] = row_t[rb] < t1;
-        pos_q[rb] = si.C + row_t[rb];
-        al2[rb] = p.alibi ? p.alibi[si.kvh * G + r % G] * kLog2e : 0.f;
+    // ---- this lane's row (a lane pair shares it) and Q^T as B operands:
+    // lane l holds Q[row][16ds + 8h .. +7] ----
+    const int r = wave * 32 + (lane & 31);
+    const int row_t = t0 + r / G;
+    const bool row_ok = row_t < t1;
+    const int head = si.kvh * G + r % G;
+    const int pos_q = si.C + row_t;
+    const float al2 = p.alibi ? p.alibi[head] * kLog2e : 0.f;
+    u32x4 q[kDS];
+    {
         const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
-                               ((int64_t)(si.q0 + (row_ok[rb] ? row_t[rb] : t0)) * p.num_q_heads +
-                                si.kvh * G + r % G) * D;
+                               ((int64_t)(si.q0 + (row_ok ? row_t : t0)) * p.num_q_heads + head) * D;
 #pragma unroll
         for (int ds = 0; ds < kDS; ++ds) {
-            const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 32 * ds + 8 * grp);
-            qop[rb][ds] = row_ok[rb] ? v : u32x4{0, 0, 0, 0};
+            const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 16 * ds + 8 * h);
+            q[ds] = row_ok ? v : u32x4{0, 0, 0, 0};
         }
     }
 
-    // ---- key range ----
-    const int pos_first = si.C + t0, pos_last = si.C + t1 - 1;
     const int jt0 = it.jt0;
-    const int ntiles = it.ntiles;
-
-    // Context page ids in LDS, kExtPages at a time: `need(jt)` reloads the list
-    // (between barriers) when tile jt's context keys are not all in it.
-    si.pages = L.pages;
-    si.pg0 = -kExtPages;
-    auto need = [&](int jt) {
-        const int last = min(jt + kExtKeys, si.C) - 1;          // last context key
-        if (last < jt) return;                                 // no context keys
-        if ((last >> p.page_shift) - si.pg0 < kExtPages && (jt >> p.page_shift) >= si.pg0)
-            return;
-        __syncthreads();                                       // old list unused
-        si.pg0 = jt >> p.page_shift;
-        const int cnt = min(kExtPages, ((si.C - 1) >> p.page_shift) - si.pg0 + 1);
-        const int32_t* row = p.block_table + (int64_t)si.b * p.bt_stride + si.pg0;
-        for (int i = threadIdx.x; i < cnt; i += kExtThreads) L.pages[i] = row[i];
-        __syncthreads();
+    const int pos_first = si.C + t0, pos_last = si.C + t1 - 1;
+    // a tile needs no mask when it ends at or before the first row's diagonal
+    // and starts inside the last row's window; it has one key kind when it
+    // does not straddle the context's end
+    auto fast_tile = [&](int jt) {
+        return jt + kExtKeys - 1 <= pos_first &&
+               (p.window <= 0 || jt >= pos_last - p.window + 1) &&
+               (jt + kExtKeys <= si.C || jt >= si.C);
+    };
+    auto tile_scale = [&](int jt) {
+        const bool ctx = jt < si.C;
+        return TileScale{ctx ? p.qk_scale2_ctx : p.qk_scale2, ctx ? p.cap_c1_ctx : p.cap_c1,
+                         ctx ? p.v_scale : 1.f};
     };
 
     LaneOffs<D> lo;
-    lo.init(c, grp);
     ExtAcc<D> A;
+    A.m = -INFINITY;
+    A.l = 0.f;
 #pragma unroll
-    for (int rb = 0; rb < kRB; ++rb) {
-        A.m[rb] = -INFINITY;
-        A.l[rb] = 0.f;
-#pragma unroll
-        for (int e = 0; e < kVE; ++e) A.o[rb][e] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int db = 0; db < kDB; ++db) A.o[db] = f32x16{};
 
-    // ---- the tiles [from, to), in phases of one kind: tiles [it_win,
-    // it_diag) need no mask (inside every row's window and below every row's
-    // diagonal); the tile holding key C mixes context and new keys.  A phase
-    // of full single-kind tiles runs the FAST variant, the others the general
-    // one; each phase is its own loop. ----
-    const int nd = pos_first - (kExtKeys - 1) - jt0;     // tiles it <= nd/64 end at or
-    const int it_diag = nd < 0 ? 0 : nd / kExtKeys + 1;   // before the first row's diagonal
-    const int it_win = p.window > 0 ? max(0, (pos_last - p.window + 1 - jt0 + kExtKeys - 1) /
-                                                 kExtKeys)
-                                    : 0;
-    const int it_split = (si.C % kExtKeys != 0 && si.C > jt0) ? (si.C - jt0) / kExtKeys : -1;
-    int cut[6] = {0, min(it_win, ntiles), 0, 0, min(max(it_diag, it_win), ntiles), ntiles};
-    cut[2] = (it_split >= cut[1] && it_split < cut[4]) ? it_split : cut[4];
-    cut[3] = (it_split >= cut[1] && it_split < cut[4]) ? it_split + 1 : cut[4];
-    // phases: [cut0,cut1) general, [cut1,cut2) fast, [cut2,cut3) general (split),
-    //         [cut3,cut4) fast, [cut4,cut5) general; each clipped to [from, to)
-#pragma unroll
-    for (int k = 0; k < 6; ++k) cut[k] = min(max(cut[k], from), to);
+    si.pages = L.pages;
+    si.pg0 = 0;
+    auto jt_of = [&](int i) { return jt0 + i * kExtKeys; };
 
-    if constexpr (!FP8) {
-        StageLane<D> sl;
-        sl.init(p);
-        const bool runs = p.page_shift >= 4;                 // runs stay inside a page
-        auto stage = [&](int jt, uint8_t* kd, uint8_t* vd) {
-            need(jt);
-            if (runs) stage_runs<D>(p, si, jt, kd, vd, sl);
-            else stage_direct<D>(p, si, jt, kd, vd);
-        };
-        auto run = [&](int a, int e, auto fast) {
-            for (int i = a; i < e; ++i) {
-                const int jt = jt0 + i * kExtKeys;
-                uint8_t* kc = (i & 1) ? L.k1 : L.k0;
-                uint8_t* vc = (i & 1) ? L.v1 : L.v0;
-                if (i + 1 < to) stage(jt + kExtKeys, (i & 1) ? L.k0 : L.k1,
-                                      (i & 1) ? L.v0 : L.v1);
-                tile_compute<D, MODE, decltype(fast)::value>(kc, vc, lo, qop, A, p, si, pos_q,
-                                                             al2, jt);
-                wait_vm0();
-                __syncthreads();
+    // Tile i (K and V in buffer i & 1): its loads are issued at the start of
+    // tile i - 1 and waited for before the barrier that ends it; tile i + 1's
+    // loads overwrite tile i - 1's buffers, which the barrier ending tile
+    // i - 1 released.  The operand offsets move to the other buffer after
+    // every tile.
+    using TL = Tile<D>;
+    const uint32_t k_lds = lds_addr(L.k), v_lds = lds_addr(L.v);
+    auto tile = [&](int i, int c1) {
+        const int jt = jt_of(i);
+        const bool more = i + 1 < c1;
+        const int nb = (i + 1) & 1;                           // tile i + 1's buffers
+        if constexpr (!FP8) {
+            if (more) {
+                stage_rows<D, false>(p, si, jt_of(i + 1), k_lds + nb * TL::kBytes);
+                stage_rows<D, true>(p, si, jt_of(i + 1), v_lds + nb * TL::kBytes);
             }
-        };
-        stage(jt0 + from * kExtKeys, (from & 1) ? L.k1 : L.k0, (from & 1) ? L.v1 : L.v0);
-        wait_vm0();
-        __syncthreads();
-        run(cut[0], cut[1], std::false_type{});
-        run(cut[1], cut[2], std::true_type{});
-        run(cut[2], cut[3], std::false_type{});
-        run(cut[3], cut[4], std::true_type{});
-        run(cut[4], cut[5], std::false_type{});
-    } else {
-        Stage8<D> sk, sv;
-        auto load = [&](int jt) {
-            need(jt);
-            stage8_load<D>(sk, p, si, jt, false);
-            stage8_load<D>(sv, p, si, jt, true);
-        };
-        auto store = [&](uint8_t* kd, uint8_t* vd) {
-            stage8_store<D, false>(sk, kd);
-            stage8_store<D, true>(sv, vd);
-        };
-        auto run = [&](int a, int e, auto fast) {
-            for (int i = a; i < e; ++i) {
-                const int jt = jt0 + i * kExtKeys;
-                const bool more = i + 1 < to;
-                if (more) load(jt + kExtKeys);
-                tile_compute<D, MODE, decltype(fast)::value>((i & 1) ? L.k1 : L.k0,
-                                                             (i & 1) ? L.v1 : L.v0, lo, qop,
-                                                             A, p, si, pos_q, al2, jt);
-                if (more) store((i & 1) ? L.k0 : L.k1, (i & 1) ? L.v0 : L.v1);
-                __syncthreads();
-            }
-        };
-        load(jt0 + from * kExtKeys);
-        store((from & 1) ? L.k1 : L.k0, (from & 1) ? L.v1 : L.v0);
-        __syncthreads();
-        run(cut[0], cut[1], std::false_type{});
-        run(cut[1], cut[2], std::true_type{});
-        run(cut[2], cut[3], std::false_type{});
-        run(cut[3], cut[4], std::true_type{});
-        run(cut[4], cut[5], std::false_type{});
-    }
-
-    // ---- finish: O^T[d][row c] / l; MFMA dblk, accumulator row 4grp + j
-    // holds d = 16*dblk + 4grp + j ----
-#pragma unroll
-    for (int rb = 0; rb < kRB; ++rb) {
-        const float lt = col4_sum(A.l[rb]);
-        if (!row_ok[rb]) continue;
-        const int r = (wave * kRB + rb) * 16 + c;
-        if (complete) {
-            uint16_t* orow = static_cast<uint16_t*>(p.out) +
-                             ((int64_t)(si.q0 + row_t[rb]) * p.num_q_heads + si.kvh * G + r % G) *
-                                 D;
-            // a sink logit joins the normaliser (no value row)
-            float den = lt;
-            if (p.sinks) den += fast_exp2(p.sinks[si.kvh * G + r % G] * kLog2e - A.m[rb]);
-            const float inv = 1.f / den;
-#pragma unroll
-            for (int dblk = 0; dblk < kVE; ++dblk)
-                *reinterpret_cast<u32x2*>(orow + 16 * dblk + 4 * grp) =
-                    u32x2{pack_bf16x2(A.o[rb][dblk][0] * inv, A.o[rb][dblk][1] * inv),
-                          pack_bf16x2(A.o[rb][dblk][2] * inv, A.o[rb][dblk][3] * inv)};
-        } else {
-            // a part: normalised rows and log2-sum-exp (no sink), for the merge
-            const int64_t prow = ext_part_row(w, slot, r);
-            const float inv = 1.f / lt;
-            float* po = p.part_o + prow * D;
-#pragma unroll
-            for (int dblk = 0; dblk < kVE; ++dblk)
-                *reinterpret_cast<f32x4*>(po + 16 * dblk + 4 * grp) = A.o[rb][dblk] * inv;
-            if (grp == 0) p.part_lse[prow] = A.m[rb] + __log2f(lt);
         }
+        Stage8<D> sk, sv;
+        if constexpr (FP8) {
+            if (more) {
+                stage8_load<D>(sk, p, si, jt_of(i + 1), false);
+                stage8_load<D>(sv, p, si, jt_of(i + 1), true);
+            }
+        }
+        const TileScale ts = tile_scale(jt);
+        tile_inorder<D, MODE>(fast_tile(jt), L.k, L.v, lo, q, A, p, si, ts, pos_q, al2, jt);
+        if constexpr (FP8) {
+            if (more) {
+                stage8_store<D, false>(sk, L.k + nb * TL::kBytes);
+                stage8_store<D, true>(sv, L.v + nb * TL::kBytes);
+            }
+        } else {
+            wait_vm0();
+        }
+        __syncthreads();
+        lo.toggle();
+    };
+
+    // The tiles in chunks whose context pages fit the LDS page list.
+    lo.init(lane, from & 1);
+    const int chunk_tiles = max(1, ((kExtPages - 2) << p.page_shift) / kExtKeys);
+#pragma nounroll
+    for (int c0 = from; c0 < to; c0 += chunk_tiles) {
+        const int c1 = min(to, c0 + chunk_tiles);
+        {
+            __syncthreads();                                   // the old list is unused
+            const int jlo = jt_of(c0);
+            const int jhi = min(jt_of(c1), si.C) - 1;          // last context key
+            si.pg0 = jlo >> p.page_shift;
+            const int cnt = jhi >= jlo ? (jhi >> p.page_shift) - si.pg0 + 1 : 0;
+            const int32_t* row = p.block_table + (int64_t)si.b * p.bt_stride + si.pg0;
+            for (int i = threadIdx.x; i < cnt; i += kExtThreads) L.pages[i] = row[i];
+            __syncthreads();
+        }
+        // tile c0's K and V
+        const int b0 = c0 & 1;
+        if constexpr (!FP8) {
+            stage_rows<D, false>(p, si, jt_of(c0), k_lds + b0 * TL::kBytes);
+            stage_rows<D, true>(p, si, jt_of(c0), v_lds + b0 * TL::kBytes);
+            wait_vm0();
+        } else {
+            Stage8<D> sk, sv;
+            stage8_load<D>(sk, p, si, jt_of(c0), false);
+            stage8_load<D>(sv, p, si, jt_of(c0), true);
+            stage8_store<D, false>(sk, L.k + b0 * TL::kBytes);
+            stage8_store<D, true>(sv, L.v + b0 * TL::kBytes);
+        }
+        __syncthreads();
+#pragma nounroll
+        for (int i = c0; i < c1; ++i) tile(i, c1);
+    }
+
+    // ---- finish: the lane pair's sums; O^T[d][row] / l, d = 32db + 8(j/4) +
+    // 4h + j%4 for accumulator slot j ----
+    const float lt = pair_sum(A.l);
+    if (!row_ok) return;
+    if (complete) {
+        uint16_t* orow = static_cast<uint16_t*>(p.out) +
+                         ((int64_t)(si.q0 + row_t) * p.num_q_heads + head) * D;
+        // a sink logit joins the normaliser (no value row)
+        float den = lt;
+        if (p.sinks) den += fast_exp2(p.sinks[head] * kLog2e - A.m);
+        const float inv = 1.f / den;
+#pragma unroll
+        for (int db = 0; db < kDB; ++db)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * jj + 4 * h) =
+                    u32x2{pack_bf16x2(A.o[db][4 * jj] * inv, A.o[db][4 * jj + 1] * inv),
+                          pack_bf16x2(A.o[db][4 * jj + 2] * inv, A.o[db][4 * jj + 3] * inv)};
+    } else {
+        // a part: normalised rows and log2-sum-exp (no sink), for the merge
+        const int64_t prow = ext_part_row(w, slot, r);
+        const float inv = 1.f / lt;
+        float* po = p.part_o + prow * D;
+#pragma unroll
+        for (int db = 0; db < kDB; ++db)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                *reinterpret_cast<f32x4*>(po + 32 * db + 8 * jj + 4 * h) =
+                    f32x4{A.o[db][4 * jj], A.o[db][4 * jj + 1], A.o[db][4 * jj + 2],
+                          A.o[db][4 * jj + 3]} * inv;
+        if (h == 0) p.part_lse[prow] = A.m + __log2f(lt);
     }
 }
 
@@ -808,16 +798,19 @@ __device__ __forceinline__ void extend_piece(const ExtendParams& pk, const Item&
 // laid end to end (N tiles in all), cut into pieces at item boundaries.  The
 // owner of an item's first tile records which blocks cover it.
 // ---------------------------------------------------------------------------
+template <int D, bool FP8>
+constexpr int ext_occupancy() { return FP8 ? 1 : kExtOccupancy; }
+
 template <int D, bool FP8, int MODE>
-__global__ __launch_bounds__(kExtThreads, kExtOccupancy) void extend_kernel(ExtendParams p) {
+__global__ __launch_bounds__(kExtThreads)
+__attribute__((amdgpu_waves_per_eu(ext_occupancy<D, FP8>(), ext_occupancy<D, FP8>())))
+void extend_kernel(ExtendParams p) {
     using TL = Tile<D>;
-    // two buffers of K and V (tile `it` in buffer it & 1)
-    __shared__ __attribute__((aligned(1024))) uint8_t sm_k0[TL::kBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t sm_v0[TL::kBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t sm_k1[TL::kBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t sm_v1[TL::kBytes];
+    // two buffers of K and V (tile `i` in buffer i & 1)
+    __shared__ __attribute__((aligned(1024))) uint8_t sm_k[2 * TL::kBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t sm_v[2 * TL::kBytes];
     __shared__ int sm_pages[kExtPages];
-    const ExtLds L{sm_k0, sm_v0, sm_k1, sm_v1, sm_pages};
+    const ExtLds L{sm_k, sm_v, sm_pages};
 
     // Blocks are dealt to the 8 XCDs in turn; the logical index w gives each
     // XCD a contiguous run of the tile stream, so the row tiles of one
@@ -875,7 +868,7 @@ template <int D>
 __global__ __launch_bounds__(kExtMergeThreads) void extend_merge_kernel(ExtendParams p) {
     constexpr int kQ = D / 4;
     constexpr int kSliceRows = kExtRows / kMergeSlices;
-    constexpr int kUnits = kSliceRows * kQ / kExtMergeThreads;
+    constexpr int kUnits = (kSliceRows * kQ + kExtMergeThreads - 1) / kExtMergeThreads;
     const int64_t i = blockIdx.x / kMergeSlices;
     const int slice = blockIdx.x % kMergeSlices;
     const Item it = item_of(p, i);
@@ -903,7 +896,7 @@ __global__ __launch_bounds__(kExtMergeThreads) void extend_merge_kernel(ExtendPa
             const int r = slice * kSliceRows + u / kQ, q = u % kQ;
             lse[k] = -INFINITY;
             o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (r < rows) {
+            if (u < kSliceRows * kQ && r < rows) {
                 lse[k] = p.part_lse[base + r];
                 o[k] = *reinterpret_cast<const f32x4*>(p.part_o + (base + r) * D + 4 * q);
             }
@@ -923,7 +916,7 @@ __global__ __launch_bounds__(kExtMergeThreads) void extend_merge_kernel(ExtendPa
     for (int k = 0; k < kUnits; ++k) {
         const int u = threadIdx.x + kExtMergeThreads * k;
         const int r = slice * kSliceRows + u / kQ, q = u % kQ;
-        if (r >= rows) continue;
+        if (u >= kSliceRows * kQ || r >= rows) continue;
         const int h = it.kvh * G + r % G;
         float s = sum[k];
         if (p.sinks && s > 0.f) s += fast_exp2(p.sinks[h] * kLog2e - m[k]);
@@ -935,17 +928,23 @@ __global__ __launch_bounds__(kExtMergeThreads) void extend_merge_kernel(ExtendPa
     }
 }
 
+template <int D, bool FP8, int V>
+const void* extend_kernel_mode(int mode) {
+    switch (mode) {
+        case kCap: return reinterpret_cast<const void*>(&extend_kernel<D, FP8, kCap | V>);
+        case kFold: return reinterpret_cast<const void*>(&extend_kernel<D, FP8, kFold | V>);
+        case kScale | kAlibi:
+            return reinterpret_cast<const void*>(&extend_kernel<D, FP8, kScale | kAlibi | V>);
+        case kCap | kAlibi:
+            return reinterpret_cast<const void*>(&extend_kernel<D, FP8, kCap | kAlibi | V>);
+        default: return reinterpret_cast<const void*>(&extend_kernel<D, FP8, kScale | V>);
+    }
+}
+
 template <int D, bool FP8>
 const void* extend_kernel_ptr(int mode) {
-    switch (mode) {
-        case kCap: return reinterpret_cast<const void*>(&extend_kernel<D, FP8, kCap>);
-        case kFold: return reinterpret_cast<const void*>(&extend_kernel<D, FP8, kFold>);
-        case kScale | kAlibi:
-            return reinterpret_cast<const void*>(&extend_kernel<D, FP8, kScale | kAlibi>);
-        case kCap | kAlibi:
-            return reinterpret_cast<const void*>(&extend_kernel<D, FP8, kCap | kAlibi>);
-        default: return reinterpret_cast<const void*>(&extend_kernel<D, FP8, kScale>);
-    }
+    return (mode & kVScale) ? extend_kernel_mode<D, FP8, kVScale>(mode & ~kVScale)
+                            : extend_kernel_mode<D, FP8, 0>(mode);
 }
 
 const void* extend_kernel_for(int head_dim, bool fp8, int mode) {
@@ -960,9 +959,10 @@ int extend_rows_per_block() { return kExtRows; }
 
 hipError_t launch_extend(const ExtendParams& p, int head_dim, bool fp8, int workers,
                          hipStream_t stream) {
-    const int mode = p.has_cap ? (p.alibi ? kCap | kAlibi : kCap)
-                     : p.alibi ? kScale | kAlibi
-                     : (p.qk_scale2 > 0.f && p.qk_scale2_ctx > 0.f) ? kFold : kScale;
+    const int mode = (p.has_cap ? (p.alibi ? kCap | kAlibi : kCap)
+                      : p.alibi ? kScale | kAlibi
+                      : (p.qk_scale2 > 0.f && p.qk_scale2_ctx > 0.f) ? kFold : kScale) |
+                     ((p.v_scale != 1.f || p.v_desc) ? kVScale : 0);
     hipLaunchKernelGGL(extend_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, p);
     const void* f = extend_kernel_for(head_dim, fp8, mode);
     void* args[] = {const_cast<ExtendParams*>(&p)};

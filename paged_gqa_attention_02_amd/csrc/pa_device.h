@@ -24,6 +24,18 @@ typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+// v_mfma_f32_32x32x16_bf16 (one wave computes D[32x32] += A[32x16] * B[16x32]):
+//   A: lane l holds A[l % 32][8*(l/32) + j], j = 0..7
+//   B: lane l holds B[8*(l/32) + j][l % 32], j = 0..7
+//   D: lane l holds D[8*(j/4) + 4*(l/32) + j%4][l % 32], j = 0..15
+__device__ __forceinline__ f32x16 mfma_bf16_32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b),
+                                                   c, 0, 0, 0);
+}
+
 __device__ __forceinline__ f32x4 mfma_bf16_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b),
@@ -73,6 +85,18 @@ __device__ __forceinline__ float col4_max(float v) {
                                                     false, false);
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
+// Max / sum over the lane pair l, l^32 (one column of a 32x32 MFMA result).
+__device__ __forceinline__ float pair_max(float v) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+}
+__device__ __forceinline__ float pair_sum(float v) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+
 __device__ __forceinline__ float col4_sum(float v) {
     const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
                                                     false, false);
