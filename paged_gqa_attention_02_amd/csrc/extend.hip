@@ -42,7 +42,7 @@ namespace pa {
 namespace {
 
 #ifndef PA_EXTEND_WAVES
-#define PA_EXTEND_WAVES 4
+#define PA_EXTEND_WAVES 8
 #endif
 #ifndef PA_EXTEND_OCCUPANCY
 #define PA_EXTEND_OCCUPANCY 2
@@ -54,6 +54,14 @@ constexpr int kExtKeys = 64;                     // keys per tile
 constexpr int kExtPages = 2048;                  // page ids staged in LDS at a time
 constexpr int kExtOccupancy = PA_EXTEND_OCCUPANCY;   // waves per SIMD (bf16 caches)
 constexpr int kStageRows = kExtKeys / kExtWaves; // rows of a tile one wave stages
+// K and V tile buffers: tile i lives in buffer gray(i mod 4) (consecutive tiles
+// differ in one bit of the buffer index, so moving to the next tile's buffer
+// is one XOR); bf16 loads run two tiles ahead.
+constexpr int kExtBuffers = 4;
+__host__ __device__ constexpr int gray4(int i) { return (i & 3) ^ ((i & 3) >> 1); }
+static_assert(gray4(0) == 0 && gray4(1) == 1 && gray4(2) == 3 && gray4(3) == 2 &&
+                  gray4(4) == 0 && gray4(7) == 2,
+              "the buffer sequence 0 1 3 2 repeats every four tiles");
 
 // How scores become log2-domain logits.
 enum ScoreMode {
@@ -288,7 +296,7 @@ template <int D>
 struct LaneOffs {
     int koff[D / 16];
     int voff[D / 32];
-    // offsets into buffer `buf` (0 or 1) of the K and V tile pairs
+    // offsets into buffer `buf` of the K and V tile rings
     __device__ __forceinline__ void init(int lane, int buf) {
         using TL = Tile<D>;
         const int r = lane & 31, h = lane >> 5;
@@ -302,13 +310,14 @@ struct LaneOffs {
             voff[db] = buf * TL::kBytes + row * TL::kPitch +
                        16 * ((4 * db + 2 * (g & 1) + (q >> 1)) ^ TL::vswz(row)) + 8 * (q & 1);
     }
-    // the other buffer (kBytes is a power of two and offsets stay below
-    // 2 * kBytes)
-    __device__ __forceinline__ void toggle() {
+    // from tile i's buffer to tile i + 1's: one bit of the buffer index flips
+    // (bit 0 after an even tile, bit 1 after an odd one)
+    __device__ __forceinline__ void next(int i) {
+        const int x = (i & 1) ? 2 * Tile<D>::kBytes : Tile<D>::kBytes;
 #pragma unroll
-        for (int ds = 0; ds < D / 16; ++ds) koff[ds] ^= Tile<D>::kBytes;
+        for (int ds = 0; ds < D / 16; ++ds) koff[ds] ^= x;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) voff[db] ^= Tile<D>::kBytes;
+        for (int db = 0; db < D / 32; ++db) voff[db] ^= x;
     }
 };
 
@@ -393,7 +402,7 @@ struct TileScale {
 //   row_max: the lane pair's max; whether any row of the wave moves its
 //     reference max (lazy rescale: only when a score exceeds it by more than
 //     8 in log2 units, so p <= 2^8), and the rescale factor;
-//   exps: p = 2^(logit - m) in place, and their sum;
+//   exps: p = 2^(logit - m) in place;
 //   pack: value scales and the bf16 B operands of P V.
 struct SoftmaxState {
     float m_new, ms, alpha;
@@ -449,15 +458,11 @@ __device__ __forceinline__ SoftmaxState sm_row_max(float lane_max, float m, cons
 }
 
 template <int MODE, bool FAST>
-__device__ __forceinline__ float sm_exps(f32x16& s, const SoftmaxState& st, float qs) {
+__device__ __forceinline__ void sm_exps(f32x16& s, const SoftmaxState& st, float qs) {
     constexpr bool kFolded = (MODE & 7) == kFold && FAST;
 #pragma unroll
     for (int j = 0; j < 16; ++j)
         s[j] = kFolded ? fast_exp2(__builtin_fmaf(s[j], qs, -st.ms)) : fast_exp2(s[j] - st.ms);
-    float t[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) t[i] = (s[4 * i] + s[4 * i + 1]) + (s[4 * i + 2] + s[4 * i + 3]);
-    return (t[0] + t[1]) + (t[2] + t[3]);
 }
 
 template <int MODE, bool FAST>
@@ -480,55 +485,59 @@ __device__ __forceinline__ void sm_pack(f32x16& s, u32x4 (&pk)[2], const SeqInfo
                       pack_bf16x2(s[8 * t + 6], s[8 * t + 7])};
 }
 
-// The online softmax of a key half's scores s: updates the row statistics and
-// returns the packed probabilities and whether (and by what) to rescale O.
+// The online softmax of one tile's scores (s[H]: key half H): updates the
+// row statistics and returns the packed probabilities (pk[2H + t]: P V step
+// 2H + t) and whether (and by what) to rescale O.
 template <int MODE, bool FAST>
-__device__ __forceinline__ SoftmaxState half_softmax(f32x16& s, u32x4 (&pk)[2], float& m,
+__device__ __forceinline__ SoftmaxState tile_softmax(f32x16 (&s)[2], u32x4 (&pk)[4], float& m,
                                                      float& l, const ExtendParams& p,
                                                      const SeqInfo& si, const TileScale& ts,
                                                      int pos_q, float al2, int key0) {
-    const float lane_max = sm_logits<MODE, FAST>(s, p, si, ts, pos_q, al2, key0);
-    const SoftmaxState st = sm_row_max<MODE, FAST>(lane_max, m, ts);
-    const float ps = sm_exps<MODE, FAST>(s, st, ts.qs);
-    l = l * st.alpha + ps;
+    const float m0 = sm_logits<MODE, FAST>(s[0], p, si, ts, pos_q, al2, key0);
+    const float m1 = sm_logits<MODE, FAST>(s[1], p, si, ts, pos_q, al2, key0 + 32);
+    const SoftmaxState st = sm_row_max<MODE, FAST>(vmax(m0, m1), m, ts);
+    sm_exps<MODE, FAST>(s[0], st, ts.qs);
+    sm_exps<MODE, FAST>(s[1], st, ts.qs);
+    // the row sum (before any value scale), as a tree of independent adds
+    float t4[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const f32x16& v = s[i >> 2];
+        const int o = 4 * (i & 3);
+        t4[i] = (v[o] + v[o + 1]) + (v[o + 2] + v[o + 3]);
+    }
+    l = l * st.alpha + (((t4[0] + t4[1]) + (t4[2] + t4[3])) + ((t4[4] + t4[5]) + (t4[6] + t4[7])));
+    sm_pack<MODE, FAST>(s[0], reinterpret_cast<u32x4(&)[2]>(pk[0]), si, ts, key0);
+    sm_pack<MODE, FAST>(s[1], reinterpret_cast<u32x4(&)[2]>(pk[2]), si, ts, key0 + 32);
     m = st.m_new;
-    sm_pack<MODE, FAST>(s, pk, si, ts, key0);
     return st;
 }
 
-// Key half H of a tile in order: S^T = K Q^T, the online softmax (the masked
-// variant unless the tile is FAST), P V.  Only the softmax differs between
-// the variants, so the accumulators never pass through the branch.
-template <int D, int MODE, int H>
-__device__ __forceinline__ void half_step(bool fast, const uint8_t* kbuf, const uint8_t* vbuf,
-                                          const LaneOffs<D>& lo, const u32x4 (&q)[D / 16],
-                                          ExtAcc<D>& A, const ExtendParams& p,
-                                          const SeqInfo& si, const TileScale& ts, int pos_q,
-                                          float al2, int jt) {
-    constexpr int kDB = D / 32;
-    const int key0 = jt + 32 * H + 4 * ((threadIdx.x & 63) >> 5);
-    f32x16 s;
-    qk_half<D, H>(s, kbuf, lo, q);
-    u32x4 pk[2];
-    const SoftmaxState st =
-        fast ? half_softmax<MODE, true>(s, pk, A.m, A.l, p, si, ts, pos_q, al2, key0)
-             : half_softmax<MODE, false>(s, pk, A.m, A.l, p, si, ts, pos_q, al2, key0);
-    if (st.move) {
-#pragma unroll
-        for (int db = 0; db < kDB; ++db) A.o[db] *= st.alpha;
-    }
-    pv_half<D, H>(A.o, vbuf, lo, pk);
-}
-
-// One 64-key tile: its two key halves in order.
+// One 64-key tile (K and V at the offsets lo selects): S^T = K Q^T for both
+// key halves, the online softmax (the masked variant unless the tile is
+// FAST), P V.  Only the softmax differs between the variants, so the
+// accumulators never pass through the branch.
 template <int D, int MODE>
-__device__ __forceinline__ void tile_inorder(bool fast, const uint8_t* kbuf,
+__device__ __forceinline__ void tile_compute(bool fast, const uint8_t* kbuf,
                                              const uint8_t* vbuf, const LaneOffs<D>& lo,
                                              const u32x4 (&q)[D / 16], ExtAcc<D>& A,
                                              const ExtendParams& p, const SeqInfo& si,
                                              const TileScale& ts, int pos_q, float al2, int jt) {
-    half_step<D, MODE, 0>(fast, kbuf, vbuf, lo, q, A, p, si, ts, pos_q, al2, jt);
-    half_step<D, MODE, 1>(fast, kbuf, vbuf, lo, q, A, p, si, ts, pos_q, al2, jt);
+    constexpr int kDB = D / 32;
+    const int key0 = jt + 4 * ((threadIdx.x & 63) >> 5);
+    f32x16 s[2];
+    qk_half<D, 0>(s[0], kbuf, lo, q);
+    qk_half<D, 1>(s[1], kbuf, lo, q);
+    u32x4 pk[4];
+    const SoftmaxState st =
+        fast ? tile_softmax<MODE, true>(s, pk, A.m, A.l, p, si, ts, pos_q, al2, key0)
+             : tile_softmax<MODE, false>(s, pk, A.m, A.l, p, si, ts, pos_q, al2, key0);
+    if (st.move) {
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) A.o[db] *= st.alpha;
+    }
+    pv_half<D, 0>(A.o, vbuf, lo, reinterpret_cast<const u32x4(&)[2]>(pk[0]));
+    pv_half<D, 1>(A.o, vbuf, lo, reinterpret_cast<const u32x4(&)[2]>(pk[2]));
 }
 
 // An item: row tile mt (kExtRows rows (token, head)) of sequence b, kv head
@@ -611,7 +620,7 @@ __global__ __launch_bounds__(kScanThreads) void extend_scan_kernel(ExtendParams 
 // writes normalised fp32 rows and their log2-sum-exp to the block's slot.
 // ---------------------------------------------------------------------------
 struct ExtLds {
-    uint8_t *k, *v;     // two K and two V tiles each (tile i in buffer i & 1)
+    uint8_t *k, *v;     // rings of kExtBuffers K and V tiles
     int* pages;
 };
 
@@ -687,46 +696,54 @@ __device__ __forceinline__ void extend_piece(const ExtendParams& pk, const Item&
     si.pg0 = 0;
     auto jt_of = [&](int i) { return jt0 + i * kExtKeys; };
 
-    // Tile i (K and V in buffer i & 1): its loads are issued at the start of
-    // tile i - 1 and waited for before the barrier that ends it; tile i + 1's
-    // loads overwrite tile i - 1's buffers, which the barrier ending tile
-    // i - 1 released.  The operand offsets move to the other buffer after
-    // every tile.
+    // Tile i's K and V live in buffer gray(i mod 4).  bf16: tile i's loads
+    // are issued at the start of tile i - 2 (the prologue issues the chunk's
+    // first two tiles); the end of tile i waits for tile i + 1's (the loads
+    // issued during this tile may stay in flight) and a barrier publishes
+    // them.  Tile i + 2's buffer last held tile i - 2, released by the
+    // barrier that ended tile i - 2.  fp8 goes through registers one tile
+    // ahead: loads at the start of tile i, converted stores at its end.
     using TL = Tile<D>;
     const uint32_t k_lds = lds_addr(L.k), v_lds = lds_addr(L.v);
+    auto buf_of = [](int i) { return (uint32_t)(gray4(i) * TL::kBytes); };
+    auto stage_bf16 = [&](int i) {
+        stage_rows<D, false>(p, si, jt_of(i), k_lds + buf_of(i));
+        stage_rows<D, true>(p, si, jt_of(i), v_lds + buf_of(i));
+    };
+    constexpr int kLoads = 2 * TL::kRuns;                   // a wave's loads per tile
     auto tile = [&](int i, int c1) {
         const int jt = jt_of(i);
-        const bool more = i + 1 < c1;
-        const int nb = (i + 1) & 1;                           // tile i + 1's buffers
-        if constexpr (!FP8) {
-            if (more) {
-                stage_rows<D, false>(p, si, jt_of(i + 1), k_lds + nb * TL::kBytes);
-                stage_rows<D, true>(p, si, jt_of(i + 1), v_lds + nb * TL::kBytes);
-            }
-        }
+        bool issued = false;
         Stage8<D> sk, sv;
-        if constexpr (FP8) {
-            if (more) {
+        if constexpr (!FP8) {
+            if (i + 2 < c1) {
+                stage_bf16(i + 2);
+                issued = true;
+            }
+        } else {
+            if (i + 1 < c1) {
                 stage8_load<D>(sk, p, si, jt_of(i + 1), false);
                 stage8_load<D>(sv, p, si, jt_of(i + 1), true);
             }
         }
         const TileScale ts = tile_scale(jt);
-        tile_inorder<D, MODE>(fast_tile(jt), L.k, L.v, lo, q, A, p, si, ts, pos_q, al2, jt);
+        tile_compute<D, MODE>(fast_tile(jt), L.k, L.v, lo, q, A, p, si, ts, pos_q, al2, jt);
         if constexpr (FP8) {
-            if (more) {
-                stage8_store<D, false>(sk, L.k + nb * TL::kBytes);
-                stage8_store<D, true>(sv, L.v + nb * TL::kBytes);
+            if (i + 1 < c1) {
+                stage8_store<D, false>(sk, L.k + buf_of(i + 1));
+                stage8_store<D, true>(sv, L.v + buf_of(i + 1));
             }
         } else {
-            wait_vm0();
+            // vmcnt(kLoads) / vmcnt(0), expcnt and lgkmcnt left at their maxima
+            if (issued) __builtin_amdgcn_s_waitcnt(0x0F70 | (kLoads & 15) | ((kLoads >> 4) << 14));
+            else wait_vm0();
         }
         __syncthreads();
-        lo.toggle();
+        lo.next(i);
     };
 
     // The tiles in chunks whose context pages fit the LDS page list.
-    lo.init(lane, from & 1);
+    lo.init(lane, gray4(from));
     const int chunk_tiles = max(1, ((kExtPages - 2) << p.page_shift) / kExtKeys);
 #pragma nounroll
     for (int c0 = from; c0 < to; c0 += chunk_tiles) {
@@ -741,18 +758,16 @@ __device__ __forceinline__ void extend_piece(const ExtendParams& pk, const Item&
             for (int i = threadIdx.x; i < cnt; i += kExtThreads) L.pages[i] = row[i];
             __syncthreads();
         }
-        // tile c0's K and V
-        const int b0 = c0 & 1;
         if constexpr (!FP8) {
-            stage_rows<D, false>(p, si, jt_of(c0), k_lds + b0 * TL::kBytes);
-            stage_rows<D, true>(p, si, jt_of(c0), v_lds + b0 * TL::kBytes);
+            stage_bf16(c0);
+            if (c0 + 1 < c1) stage_bf16(c0 + 1);
             wait_vm0();
         } else {
             Stage8<D> sk, sv;
             stage8_load<D>(sk, p, si, jt_of(c0), false);
             stage8_load<D>(sv, p, si, jt_of(c0), true);
-            stage8_store<D, false>(sk, L.k + b0 * TL::kBytes);
-            stage8_store<D, true>(sv, L.v + b0 * TL::kBytes);
+            stage8_store<D, false>(sk, L.k + buf_of(c0));
+            stage8_store<D, true>(sv, L.v + buf_of(c0));
         }
         __syncthreads();
 #pragma nounroll
@@ -806,9 +821,9 @@ __global__ __launch_bounds__(kExtThreads)
 __attribute__((amdgpu_waves_per_eu(ext_occupancy<D, FP8>(), ext_occupancy<D, FP8>())))
 void extend_kernel(ExtendParams p) {
     using TL = Tile<D>;
-    // two buffers of K and V (tile `i` in buffer i & 1)
-    __shared__ __attribute__((aligned(1024))) uint8_t sm_k[2 * TL::kBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t sm_v[2 * TL::kBytes];
+    // rings of K and V tile buffers
+    __shared__ __attribute__((aligned(1024))) uint8_t sm_k[kExtBuffers * TL::kBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t sm_v[kExtBuffers * TL::kBytes];
     __shared__ int sm_pages[kExtPages];
     const ExtLds L{sm_k, sm_v, sm_pages};
 
