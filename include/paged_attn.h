@@ -160,10 +160,12 @@ typedef struct {
     pa_problem prob;
     int32_t num_splits;        /* decode/verify: split-pass pieces = persistent
                                   blocks */
-    int32_t tokens_per_split;  /* decode/verify: tile granularity of the pieces (32) */
+    int32_t tokens_per_split;  /* tile granularity of the pieces: 32 keys
+                                  (decode/verify), 64 keys (extend) */
     int32_t waves_per_block;   /* decode/verify: waves per block, one per 16
                                   query rows (token, head) of a kv head
-                                  (latent cache: rounded up to 2, 4 or 8) */
+                                  (latent cache: rounded up to 2, 4 or 8);
+                                  extend: waves per block, one per 32 rows */
     int32_t num_cus;           /* compute units the plan was made for */
     uint64_t workspace_bytes;  /* device scratch the compute call needs */
     int32_t reserved[8];
@@ -187,7 +189,12 @@ typedef struct {
  * and merge of `_fwd_kernel_stage1/2`; any partition gives the same result).
  * Verify: as decode, with lo = max(0, L - q_len + 1 - W), the window start of
  * the first query token.
- * Extend: validates the shape; no workspace is needed.
+ * Extend: the key tiles (64 keys) of every item -- a sequence, a kv head and
+ * one block's worth of its new (token, query head) rows -- laid end to end,
+ * are cut into out->num_splits equal contiguous pieces, one per persistent
+ * block (as many as the device keeps resident, or prob->num_splits when
+ * > 0).  The workspace holds the items' tile prefix sums, the blocks covering
+ * each item, and two partial slots per block.
  *
  * hip_device >= 0 queries that device's compute-unit count; hip_device < 0
  * plans for an MI355X (256 compute units) without touching any device.
@@ -323,9 +330,17 @@ pa_status paged_attn_verify(const pa_plan* plan,
  *                 i of sequence b sits at position C_b + i
  *   k_pool...bt_stride  the cached context, as for decode
  *   out           bf16 [total_q, Hq, D]
- *   workspace     may be NULL when plan->workspace_bytes == 0
+ *   workspace     >= plan->workspace_bytes of device memory, 16-byte
+ *                 aligned (required: extend always has one); no initial
+ *                 contents needed; calls that share a workspace must not
+ *                 overlap
  *   extras        optional sinks and per-request descales (see pa_extras),
  *                 or NULL; descales apply to the cached context only
+ *
+ * Three kernels run on hip_stream: a scan of the items' key-tile counts, the
+ * persistent blocks (each walks its piece of the tiles with online softmax,
+ * writing items it covers whole to out and the ends of the others to the
+ * workspace), and a merge by log-sum-exp of the items several blocks share.
  */
 pa_status paged_attn_extend(const pa_plan* plan,
                             const void* q, const void* k_new, const void* v_new,

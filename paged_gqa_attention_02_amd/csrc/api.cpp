@@ -317,7 +317,7 @@ pa_status paged_attn_plan(const pa_problem* prob, int hip_device, pa_plan* out) 
         if (workers > kMaxWorkers) return PA_ERR_UNSUPPORTED;
         pl.num_splits = (int32_t)workers;
         pl.tokens_per_split = 64;
-        pl.waves_per_block = 4;
+        pl.waves_per_block = extend_waves_per_block();
         pl.workspace_bytes = (uint64_t)extend_layout(pr, workers).total;
     }
     *out = pl;

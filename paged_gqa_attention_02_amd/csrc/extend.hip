@@ -971,6 +971,7 @@ const void* extend_kernel_for(int head_dim, bool fp8, int mode) {
 }  // namespace
 
 int extend_rows_per_block() { return kExtRows; }
+int extend_waves_per_block() { return kExtWaves; }
 
 hipError_t launch_extend(const ExtendParams& p, int head_dim, bool fp8, int workers,
                          hipStream_t stream) {

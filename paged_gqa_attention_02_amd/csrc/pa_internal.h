@@ -152,5 +152,6 @@ hipError_t extend_blocks_per_cu(int head_dim, bool fp8, int* out);
 constexpr int64_t kMaxExtendItems = (int64_t)1 << 24;   // (sequence, kv head, row tile)
 // Rows (new token, query head) one extend block covers.
 int extend_rows_per_block();
+int extend_waves_per_block();
 
 }  // namespace pa

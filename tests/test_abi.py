@@ -337,13 +337,14 @@ def test_extend_validation(kw, status):
 
 
 def test_extend_plan_persistent_blocks():
-    """Extend plans 2 persistent blocks per compute unit without a device, and
-    a workspace for the tile prefix, the records and two partial slots of 128
-    rows per block."""
+    """Extend plans 2 persistent blocks of 8 waves per compute unit without a
+    device, 64-key tiles, and a workspace for the tile prefix, the records and
+    two partial slots of 256 rows (32 a wave) per block."""
     st, pl = plan_status(mode=1, total_q=100, max_q_len=50)
-    assert st == OK and pl.num_splits == 512 and pl.waves_per_block == 4
-    items = 4 * 8 * 2          # seqs x kv heads x ceil(50 * 4 / 128)
-    assert pl.workspace_bytes >= (items + 1) * 8 + items * 16 + 512 * 2 * 128 * 129 * 4
+    assert st == OK and pl.num_splits == 512 and pl.waves_per_block == 8
+    assert pl.tokens_per_split == 64
+    items = 4 * 8 * 1          # seqs x kv heads x ceil(50 * 4 / 256)
+    assert pl.workspace_bytes >= (items + 1) * 8 + items * 16 + 512 * 2 * 256 * 129 * 4
     st, pl2 = plan_status(mode=1, total_q=100, max_q_len=50, num_splits=7)
     assert st == OK and pl2.num_splits == 7 and pl2.workspace_bytes < pl.workspace_bytes
     assert plan_status(mode=1, total_q=1 << 30, max_q_len=1 << 29, num_seqs=64)[0] == UNSUP
