@@ -53,7 +53,8 @@
  * --------------------
  * The caller owns every buffer, including the workspace; the library never
  * allocates device memory, never synchronises, and keeps no state between
- * calls.  Compute calls enqueue kernels on `hip_stream` (a hipStream_t, NULL =
+ * calls (the one exception is paged_attn_decode_noalloc, whose scratch is a
+ * fixed array inside the library).  Compute calls enqueue kernels on `hip_stream` (a hipStream_t, NULL =
  * the null stream) and return; buffers must stay valid until the stream
  * reaches that point.  All host-visible arguments are validated before
  * anything is enqueued: on error nothing is launched and the output is
@@ -70,7 +71,7 @@
 extern "C" {
 #endif
 
-#define PAGED_ATTN_ABI_VERSION 3
+#define PAGED_ATTN_ABI_VERSION 4
 
 typedef enum {
     PA_OK = 0,
@@ -285,6 +286,43 @@ pa_status paged_attn_decode_merge(const pa_plan* plan,
                                   void* workspace, uint64_t workspace_bytes,
                                   const pa_extras* extras,
                                   void* hip_stream);
+
+/*
+ * paged_attn_decode_noalloc -- paged_attn_decode for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops and
+ * harnesses that forbid hipMalloc): the same arguments and kernels, without
+ * the workspace.  The scratch is a fixed array of
+ * PAGED_ATTN_NOALLOC_SCRATCH_BYTES inside this library, one copy per GPU,
+ * held from the library's first use on that GPU until the process ends.
+ *
+ * - A plan whose workspace_bytes exceeds PAGED_ATTN_NOALLOC_SCRATCH_BYTES is
+ *   rejected with PA_ERR_WORKSPACE_TOO_SMALL before anything is enqueued
+ *   (a decode plan needs about 4 to 14 MiB for 64 to 256 sequences of
+ *   Llama-3-8B-like heads; a latent cache with 16 heads per kv head at 512
+ *   splits needs 32 MiB).
+ * - The call allocates nothing: no hipMalloc, no hipFree.  Its first call on
+ *   a device looks up that device's copy of the array (hipGetSymbolAddress)
+ *   and keeps the address; the kernels run on hip_stream's device.
+ * - Every call on one GPU shares that GPU's array: calls that overlap on one
+ *   GPU (other streams, or other threads) race and give wrong results.  Calls
+ *   in order on one stream are safe.  Nothing in the array needs initial
+ *   contents (the split pass writes what the merge reads).
+ * - Decode mode only (plans made with PA_MODE_DECODE, latent caches
+ *   included); errors otherwise as paged_attn_decode.
+ */
+#define PAGED_ATTN_NOALLOC_SCRATCH_BYTES (48ull << 20)
+pa_status paged_attn_decode_noalloc(const pa_plan* plan,
+                                    const void* q, int64_t q_stride_b,
+                                    const void* k_pool, const void* v_pool,
+                                    int64_t kv_stride_page, int64_t kv_stride_tok,
+                                    int64_t kv_stride_head, int64_t num_pages,
+                                    const int32_t* block_table, int64_t bt_stride,
+                                    const int32_t* seq_lens,
+                                    int32_t page_size, float scale, float softcap,
+                                    int32_t window, float k_scale, float v_scale,
+                                    void* out, int64_t out_stride_b,
+                                    const pa_extras* extras,
+                                    void* hip_stream);
 
 /*
  * paged_attn_verify -- q_len query tokens per sequence against the cache

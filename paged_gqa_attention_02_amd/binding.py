@@ -18,7 +18,8 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpaged_attn.so")
 
 PA_MODE_DECODE, PA_MODE_EXTEND, PA_MODE_VERIFY = 0, 1, 2
-ABI_VERSION = 3          # PAGED_ATTN_ABI_VERSION these structures mirror
+NOALLOC_SCRATCH_BYTES = 48 << 20   # PAGED_ATTN_NOALLOC_SCRATCH_BYTES
+ABI_VERSION = 4          # PAGED_ATTN_ABI_VERSION these structures mirror
 PA_KV = {"bf16": 0, "fp8_e4m3": 1}
 
 
@@ -72,6 +73,9 @@ def lib():
     for fn in ("paged_attn_decode_split", "paged_attn_decode_merge", "paged_attn_verify"):
         getattr(L, fn).argtypes = L.paged_attn_decode.argtypes
         getattr(L, fn).restype = ctypes.c_int
+    L.paged_attn_decode_noalloc.argtypes = [PP, p, i64, p, p, i64, i64, i64, i64, p, i64, p,
+                                            i32, f32, f32, i32, f32, f32, p, i64, PX, p]
+    L.paged_attn_decode_noalloc.restype = ctypes.c_int
     L.paged_attn_extend.argtypes = [PP, p, p, p, p, p, p, p, i64, i64, i64, i64, p, i64,
                                     i32, f32, f32, i32, f32, f32, p, p, u64, PX, p]
     L.paged_attn_extend.restype = ctypes.c_int
@@ -293,6 +297,18 @@ def decode_merge(pl: Plan, q, k_pool, v_pool, block_table, seq_lens, scale, soft
                    sinks, k_descale, v_descale, alibi_slopes)
 
 
+def decode_noalloc(pl: Plan, q, k_pool, v_pool, block_table, seq_lens, scale, softcap=0.0,
+                   window=0, k_scale=1.0, v_scale=1.0, out=None, stream=None, sinks=None,
+                   k_descale=None, v_descale=None, alibi_slopes=None):
+    """paged_attn_decode_noalloc: decode with the library's fixed scratch array
+    instead of a workspace (no device allocation in the library; pass `out`
+    to allocate nothing here either).  Plans needing more than
+    NOALLOC_SCRATCH_BYTES are rejected; calls overlapping on one GPU race."""
+    return _decode("paged_attn_decode_noalloc", pl, q, k_pool, v_pool, block_table, seq_lens,
+                   scale, softcap, window, k_scale, v_scale, out, None, stream,
+                   sinks, k_descale, v_descale, alibi_slopes)
+
+
 def verify_plan(q: torch.Tensor, k_pool: torch.Tensor, block_table: torch.Tensor,
                 max_kv_len: int, window: int = 0, num_splits: int = 0) -> Plan:
     """Plan a verify call for q shaped [B, q_len, Hq, D]."""
@@ -330,7 +346,7 @@ def _rows_contiguous(t: torch.Tensor) -> bool:
 def _decode(fn, pl, q, k_pool, v_pool, block_table, seq_lens, scale, softcap, window,
             k_scale, v_scale, out, workspace, stream, sinks=None, k_descale=None,
             v_descale=None, alibi_slopes=None):
-    if fn not in ("paged_attn_decode", "paged_attn_verify") and (
+    if fn not in ("paged_attn_decode", "paged_attn_verify", "paged_attn_decode_noalloc") and (
             out is None or (workspace is None and pl.workspace_bytes > 0)):
         raise ValueError(f"{fn}: the passes share `out` and the workspace; pass both")
     dims = 4 if fn == "paged_attn_verify" else 3
@@ -358,6 +374,15 @@ def _decode(fn, pl, q, k_pool, v_pool, block_table, seq_lens, scale, softcap, wi
         raise ValueError(f"out must be bf16 {shape} like q (last dim {dv}), dense after the "
                          "sequence dimension")
     sp, st, sh = _pool_strides(k_pool, v_pool)
+    if fn == "paged_attn_decode_noalloc":
+        _check(fn, lib().paged_attn_decode_noalloc(
+            ctypes.byref(pl.c), _ptr(q), q.stride(0), _ptr(k_pool), _ptr(v_pool), sp, st, sh,
+            k_pool.shape[0], _ptr(block_table), block_table.stride(0), _ptr(seq_lens),
+            k_pool.shape[1], float(scale), float(softcap), int(window), float(k_scale),
+            float(v_scale), _ptr(out), out.stride(0),
+            _extras(sinks, k_descale, v_descale, alibi_slopes, pr.num_q_heads),
+            _stream(stream)))
+        return out
     workspace = _workspace(pl, workspace, q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(fn, getattr(lib(), fn)(

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpaged_attn.so")
 SOURCES = ["api.cpp", "decode.hip", "merge.hip", "gather.hip", "extend.hip", "append.hip",
-           "mla.hip"]
+           "mla.hip", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

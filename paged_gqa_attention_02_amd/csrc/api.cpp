@@ -348,19 +348,17 @@ int paged_attn_plan_describe(const pa_plan* pl, char* buf, int buf_len) {
 
 }  // extern "C"
 
-namespace {
+namespace pa {
 
-// Passes of a decode call: the split pass, the merge, or both in order.
-enum DecodePasses { kSplitPass = 1, kMergePass = 2, kBothPasses = 3 };
-
-pa_status decode_impl(int passes, int mode, const pa_plan* plan, const void* q, int64_t q_stride_b,
-                      const void* k_pool, const void* v_pool, int64_t kv_stride_page,
-                      int64_t kv_stride_tok, int64_t kv_stride_head, int64_t num_pages,
-                      const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
-                      int32_t page_size, float scale, float softcap, int32_t window,
-                      float k_scale, float v_scale, void* out, int64_t out_stride_b,
-                      void* workspace, uint64_t workspace_bytes, const pa_extras* extras,
-                      void* hip_stream) {
+pa_status decode_prepare(int mode, const pa_plan* plan, const void* q, int64_t q_stride_b,
+                         const void* k_pool, const void* v_pool, int64_t kv_stride_page,
+                         int64_t kv_stride_tok, int64_t kv_stride_head, int64_t num_pages,
+                         const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
+                         int32_t page_size, float scale, float softcap, int32_t window,
+                         float k_scale, float v_scale, void* out, int64_t out_stride_b,
+                         uint64_t workspace_bytes, const pa_extras* extras, DecodeParams* pp,
+                         bool* empty) {
+    *empty = false;
     if (!plan) return PA_ERR_NULL_POINTER;
     const pa_plan& pl = *plan;
     const pa_problem& pr = pl.prob;
@@ -374,7 +372,10 @@ pa_status decode_impl(int passes, int mode, const pa_plan* plan, const void* q, 
         pl.waves_per_block != decode_waves_per_block(pr) ||
         pl.workspace_bytes != (uint64_t)decode_layout(pr, pl.num_splits).total)
         return PA_ERR_PLAN_MISMATCH;
-    if (pr.num_seqs == 0) return PA_OK;
+    if (pr.num_seqs == 0) {
+        *empty = true;
+        return PA_OK;
+    }
     if (!q || !seq_lens || !out) return PA_ERR_NULL_POINTER;
     st = check_pools(pl, k_pool, v_pool, kv_stride_page, kv_stride_tok, kv_stride_head,
                      num_pages, block_table, bt_stride);
@@ -393,10 +394,8 @@ pa_status decode_impl(int passes, int mode, const pa_plan* plan, const void* q, 
     st = read_extras(extras, pr.num_seqs, &ex);
     if (st != PA_OK) return st;
     if (workspace_bytes < pl.workspace_bytes) return PA_ERR_WORKSPACE_TOO_SMALL;
-    if (!workspace) return PA_ERR_NULL_POINTER;
-    if (!aligned16(workspace)) return PA_ERR_MISALIGNED;
 
-    DecodeParams p;
+    DecodeParams& p = *pp;
     memset(&p, 0, sizeof p);
     p.q = q;
     p.q_stride_b = q_stride_b;
@@ -435,29 +434,56 @@ pa_status decode_impl(int passes, int mode, const pa_plan* plan, const void* q, 
     p.desc_per_seq = ex.per_seq;
     p.out = out;
     p.out_stride_b = out_stride_b;
-    {
-        const DecLayout L = decode_layout(pr, pl.num_splits);
-        char* ws = static_cast<char*>(workspace);
-        p.part_o = reinterpret_cast<float*>(ws);
-        p.part_lse = reinterpret_cast<float*>(ws + L.lse);
-        p.seg_rec = reinterpret_cast<int32_t*>(ws + L.rec);
-    }
-    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    return PA_OK;
+}
+
+pa_status decode_launch(int passes, const pa_plan& pl, DecodeParams& p, void* workspace,
+                        hipStream_t stream) {
+    const pa_problem& pr = pl.prob;
+    const DecLayout L = decode_layout(pr, pl.num_splits);
+    char* ws = static_cast<char*>(workspace);
+    p.part_o = reinterpret_cast<float*>(ws);
+    p.part_lse = reinterpret_cast<float*>(ws + L.lse);
+    p.seg_rec = reinterpret_cast<int32_t*>(ws + L.rec);
     const bool uniform = pr.page_size >= 16;
-    if (passes & kSplitPass) {
+    if (passes & kDecodeSplitPass) {
         const hipError_t e =
             is_latent(pr)
-                ? launch_mla_decode(p, pr.head_dim, pr.head_dim_v, k_pool == v_pool,
+                ? launch_mla_decode(p, pr.head_dim, pr.head_dim_v, p.k_pool == p.v_pool,
                                     pl.waves_per_block, pl.num_splits, stream)
                 : launch_decode(p, pr.head_dim, pr.kv_dtype == PA_KV_FP8_E4M3, uniform,
                                 pl.waves_per_block, pl.num_splits, stream);
         if (e != hipSuccess) return PA_ERR_HIP;
     }
-    if ((passes & kMergePass) &&
+    if ((passes & kDecodeMergePass) &&
         launch_decode_merge(p, value_dim(pr), pr.num_seqs, p.num_kv_heads, stream) !=
             hipSuccess)
         return PA_ERR_HIP;
     return PA_OK;
+}
+
+}  // namespace pa
+
+namespace {
+
+pa_status decode_impl(int passes, int mode, const pa_plan* plan, const void* q, int64_t q_stride_b,
+                      const void* k_pool, const void* v_pool, int64_t kv_stride_page,
+                      int64_t kv_stride_tok, int64_t kv_stride_head, int64_t num_pages,
+                      const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
+                      int32_t page_size, float scale, float softcap, int32_t window,
+                      float k_scale, float v_scale, void* out, int64_t out_stride_b,
+                      void* workspace, uint64_t workspace_bytes, const pa_extras* extras,
+                      void* hip_stream) {
+    DecodeParams p;
+    bool empty = false;
+    const pa_status st = decode_prepare(
+        mode, plan, q, q_stride_b, k_pool, v_pool, kv_stride_page, kv_stride_tok,
+        kv_stride_head, num_pages, block_table, bt_stride, seq_lens, page_size, scale, softcap,
+        window, k_scale, v_scale, out, out_stride_b, workspace_bytes, extras, &p, &empty);
+    if (st != PA_OK || empty) return st;
+    if (!workspace) return PA_ERR_NULL_POINTER;
+    if (!aligned16(workspace)) return PA_ERR_MISALIGNED;
+    return decode_launch(passes, *plan, p, workspace, static_cast<hipStream_t>(hip_stream));
 }
 
 }  // namespace
@@ -478,19 +504,19 @@ extern "C" {
         const pa_extras *extras, void *hip_stream
 
 pa_status paged_attn_decode(PA_DECODE_PARAMS) {
-    return decode_impl(kBothPasses, PA_MODE_DECODE, PA_DECODE_ARGS);
+    return decode_impl(kDecodeBothPasses, PA_MODE_DECODE, PA_DECODE_ARGS);
 }
 
 pa_status paged_attn_decode_split(PA_DECODE_PARAMS) {
-    return decode_impl(kSplitPass, PA_MODE_DECODE, PA_DECODE_ARGS);
+    return decode_impl(kDecodeSplitPass, PA_MODE_DECODE, PA_DECODE_ARGS);
 }
 
 pa_status paged_attn_decode_merge(PA_DECODE_PARAMS) {
-    return decode_impl(kMergePass, PA_MODE_DECODE, PA_DECODE_ARGS);
+    return decode_impl(kDecodeMergePass, PA_MODE_DECODE, PA_DECODE_ARGS);
 }
 
 pa_status paged_attn_verify(PA_DECODE_PARAMS) {
-    return decode_impl(kBothPasses, PA_MODE_VERIFY, PA_DECODE_ARGS);
+    return decode_impl(kDecodeBothPasses, PA_MODE_VERIFY, PA_DECODE_ARGS);
 }
 
 pa_status paged_attn_gather(const pa_plan* plan, const void* k_pool, const void* v_pool,

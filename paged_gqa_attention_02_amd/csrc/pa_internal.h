@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "paged_attn.h"
+
 namespace pa {
 
 // Decode works on tiles of 32 consecutive token positions; every split starts
@@ -153,5 +155,24 @@ constexpr int64_t kMaxExtendItems = (int64_t)1 << 24;   // (sequence, kv head, r
 // Rows (new token, query head) one extend block covers.
 int extend_rows_per_block();
 int extend_waves_per_block();
+
+// Passes of a decode call: the split pass, the merge, or both in order.
+enum DecodePasses { kDecodeSplitPass = 1, kDecodeMergePass = 2, kDecodeBothPasses = 3 };
+// Checks a decode/verify call (mode PA_MODE_DECODE or PA_MODE_VERIFY) with a
+// workspace of workspace_bytes bytes and fills *p but for its workspace
+// pointers.  *empty: the call is valid and launches nothing.  The workspace
+// pointer itself is the caller's to check.
+pa_status decode_prepare(int mode, const pa_plan* plan, const void* q, int64_t q_stride_b,
+                         const void* k_pool, const void* v_pool, int64_t kv_stride_page,
+                         int64_t kv_stride_tok, int64_t kv_stride_head, int64_t num_pages,
+                         const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
+                         int32_t page_size, float scale, float softcap, int32_t window,
+                         float k_scale, float v_scale, void* out, int64_t out_stride_b,
+                         uint64_t workspace_bytes, const pa_extras* extras, DecodeParams* p,
+                         bool* empty);
+// Lays the plan's workspace out at `workspace` (16-byte aligned, at least
+// plan.workspace_bytes) and enqueues the passes.
+pa_status decode_launch(int passes, const pa_plan& pl, DecodeParams& p, void* workspace,
+                        hipStream_t stream);
 
 }  // namespace pa

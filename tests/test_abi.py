@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_runtime():
-    assert pa.lib().paged_attn_abi_version() == B.ABI_VERSION == 3
+    assert pa.lib().paged_attn_abi_version() == B.ABI_VERSION == 4
     assert pa.lib().paged_attn_hip_runtime_path().decode().endswith(".so")
 
 
@@ -242,6 +242,54 @@ def test_decode_rejects_plan_edited_after_planning(fn, edit):
     a plan changed after paged_attn_plan is refused, not trusted."""
     plan_kw = VERIFY if fn == "paged_attn_verify" else None
     assert decode_status(plan_kw=plan_kw, fn=fn, edit=edit, ws_bytes=1 << 40) == MISMATCH
+
+
+def noalloc_status(plan_kw=None, edit=None, **kw):
+    st, pl = plan_status(**(plan_kw or {}))
+    assert st == OK
+    if edit is not None:
+        edit(pl)
+    args = dict(q=A, q_stride_b=32 * 128, k=A, v=A, sp=16 * 8 * 128, st=8 * 128, sh=128,
+                num_pages=10, bt=A, bt_stride=256, sl=A, page_size=16, scale=0.1,
+                softcap=0.0, window=0, ks=1.0, vs=1.0, out=A, out_stride_b=32 * 128,
+                extras=None, stream=None)
+    args.update(kw)
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    ex = None if args["extras"] is None else ctypes.byref(B.PaExtras(*args["extras"]))
+    return pa.lib().paged_attn_decode_noalloc(
+        ctypes.byref(pl), v(args["q"]), args["q_stride_b"], v(args["k"]), v(args["v"]),
+        args["sp"], args["st"], args["sh"], args["num_pages"], v(args["bt"]),
+        args["bt_stride"], v(args["sl"]), args["page_size"], args["scale"], args["softcap"],
+        args["window"], args["ks"], args["vs"], v(args["out"]), args["out_stride_b"], ex,
+        args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), NULLP),
+    (dict(out=None), NULLP),
+    (dict(page_size=32), MISMATCH),
+    (dict(q=A + 2), MISAL),
+    (dict(bt_stride=100), SHAPE),
+    (dict(scale=float("nan")), SHAPE),
+    (dict(extras=(None, A, None, None, 2, 0)), SHAPE),
+    (dict(plan_kw=dict(mode=2, max_q_len=2)), MISMATCH),      # decode plans only
+    (dict(plan_kw=dict(num_splits=1 << 19)), WS),             # needs more than the array
+    (dict(edit=_set(num_splits=2048)), MISMATCH),
+])
+def test_decode_noalloc_validation(kw, status):
+    """The no-workspace decode checks everything paged_attn_decode checks, and
+    refuses a plan whose workspace exceeds its fixed array, before it looks
+    the array up on a device."""
+    assert noalloc_status(**kw) == status
+
+
+def test_decode_noalloc_array_size():
+    assert pa.NOALLOC_SCRATCH_BYTES == 48 << 20
+    src = open(HEADER).read()
+    assert "#define PAGED_ATTN_NOALLOC_SCRATCH_BYTES (48ull << 20)" in src
+    st, pl = plan_status(num_splits=1 << 19)
+    assert pl.workspace_bytes > pa.NOALLOC_SCRATCH_BYTES
+    assert noalloc_status(plan_kw=dict(num_seqs=0), q=None, out=None) == OK
 
 
 def test_decode_empty_batch_launches_nothing():
