@@ -81,7 +81,8 @@ typedef enum {
     PA_ERR_WORKSPACE_TOO_SMALL = 4,/* workspace below plan->workspace_bytes (b12x: RuntimeError) */
     PA_ERR_MISALIGNED = 5,         /* pointer or stride breaks 16-byte alignment */
     PA_ERR_PLAN_MISMATCH = 6,      /* call arguments disagree with the plan */
-    PA_ERR_HIP = 7                 /* a HIP runtime call or launch failed */
+    PA_ERR_HIP = 7,                /* a HIP runtime call or launch failed */
+    PA_STATUS_MAX_ENUM = 0x7fffffff /* not a status: gives the type every int32 value */
 } pa_status;
 
 typedef enum { PA_KV_BF16 = 0, PA_KV_FP8_E4M3 = 1 } pa_kv_dtype;
@@ -437,6 +438,34 @@ pa_status paged_attn_gather(const pa_plan* plan,
                             const int32_t* block_table, int64_t bt_stride,
                             const int32_t* seq_lens,
                             void* k_out, void* v_out, void* hip_stream);
+
+/*
+ * paged_attn_check_inputs -- host-side check of the device-content contract
+ * of a compute call, on host copies of its metadata (the b12x page's
+ * `forward` validates its metadata on the host the same way).  For callers
+ * and tests that want a wrong length, page id or offset reported instead of
+ * read out of bounds on the GPU.  Host only: reads host memory, no HIP call.
+ *
+ *   plan          the plan of the call
+ *   lens          int32 [B]: seq_lens (decode/verify) or ctx_lens (extend);
+ *                 each must lie in [0, prob.max_kv_len]
+ *   block_table   int32 [B, >= ceil(L_b/P)] with row stride bt_stride: every
+ *                 entry t/P < ceil(L_b/P) must lie in [0, num_pages)
+ *   cu_seqlens_q  extend: int32 [B+1] with cu[0] = 0, 0 <= cu[b+1] - cu[b] <=
+ *                 prob.max_q_len, cu[B] = prob.total_q; NULL otherwise
+ *   bad_array,    on PA_ERR_INVALID_SHAPE (either may be NULL): which array
+ *   bad_index     broke the contract (1 lens, 2 block_table, 3 cu_seqlens_q)
+ *                 and the element's index in it (block_table: b*bt_stride +
+ *                 entry)
+ *
+ * Returns PA_OK, PA_ERR_INVALID_SHAPE for a broken contract, or the status
+ * paged_attn_plan would give the plan's problem / PA_ERR_NULL_POINTER /
+ * PA_ERR_INVALID_SHAPE (bt_stride below max_pages_per_seq, num_pages < 1).
+ */
+pa_status paged_attn_check_inputs(const pa_plan* plan, const int32_t* lens,
+                                  const int32_t* block_table, int64_t bt_stride,
+                                  int64_t num_pages, const int32_t* cu_seqlens_q,
+                                  int32_t* bad_array, int64_t* bad_index);
 
 /* Human-readable name of a status code (static storage). */
 const char* paged_attn_status_str(pa_status status);

@@ -10,9 +10,25 @@ SRC = os.path.join(HERE, "pa_oracle.c")
 LIB = os.path.join(HERE, "libpa_oracle.so")
 
 
-def build(verbose: bool = False, src: str = SRC, out: str = None) -> str:
-    cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-pthread",
-           "-Wall", "-Wextra", "-o", (out or LIB) + ".tmp", src, "-lm"]
+# AddressSanitizer + UndefinedBehaviorSanitizer build: every finding aborts.
+# A process loading it must preload gcc's libasan and libubsan
+# (sanitizer_preload()).
+SANITIZE = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+            "-fno-sanitize-recover=all"]
+
+
+def sanitizer_preload() -> str:
+    """LD_PRELOAD value for a process that loads the sanitized build."""
+    libs = [subprocess.run(["gcc", "-print-file-name=" + n], capture_output=True, text=True,
+                           check=True).stdout.strip() for n in ("libasan.so", "libubsan.so")]
+    return ":".join(libs)
+
+
+def build(verbose: bool = False, src: str = SRC, out: str = None,
+          sanitize: bool = False) -> str:
+    opt = SANITIZE if sanitize else ["-O2"]
+    cmd = ["gcc"] + opt + ["-std=c99", "-fPIC", "-shared", "-pthread",
+                           "-Wall", "-Wextra", "-o", (out or LIB) + ".tmp", src, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)

@@ -49,11 +49,16 @@ def bind(path: str):
 
 
 def lib():
+    """The oracle's C library: the in-tree build, or the build PA_ORACLE_LIB
+    names (the sanitized build the CPU tests load)."""
     global _LIB
     if _LIB is None:
-        if not os.path.exists(_build.LIB):
-            _build.build()
-        _LIB = bind(_build.LIB)
+        path = os.environ.get("PA_ORACLE_LIB")
+        if not path:
+            path = _build.LIB
+            if not os.path.exists(path):
+                _build.build()
+        _LIB = bind(path)
     return _LIB
 
 

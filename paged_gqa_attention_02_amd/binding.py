@@ -15,7 +15,10 @@ from typing import Optional
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpaged_attn.so")
+# PAGED_ATTN_LIB names another build of the same sources (the host-sanitized
+# build the CPU tests load); by default the in-tree library.
+LIB_PATH = os.environ.get("PAGED_ATTN_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libpaged_attn.so")
 
 PA_MODE_DECODE, PA_MODE_EXTEND, PA_MODE_VERIFY = 0, 1, 2
 NOALLOC_SCRATCH_BYTES = 48 << 20   # PAGED_ATTN_NOALLOC_SCRATCH_BYTES
@@ -85,6 +88,9 @@ def lib():
                                           ctypes.c_float, ctypes.c_float, p]
     L.paged_attn_cache_append.restype = ctypes.c_int
     L.paged_attn_gather.restype = ctypes.c_int
+    L.paged_attn_check_inputs.argtypes = [PP, p, p, i64, i64, p, ctypes.POINTER(i32),
+                                          ctypes.POINTER(i64)]
+    L.paged_attn_check_inputs.restype = ctypes.c_int
     L.paged_attn_status_str.argtypes = [ctypes.c_int]
     L.paged_attn_status_str.restype = ctypes.c_char_p
     L.paged_attn_plan_describe.argtypes = [PP, ctypes.c_char_p, ctypes.c_int]
@@ -237,6 +243,43 @@ def _check_cache(pl: Plan, k_pool: torch.Tensor, block_table: torch.Tensor,
                          f"entries")
 
 
+_INPUT_CHECKS = False
+_BAD_ARRAY = {1: "lens", 2: "block_table", 3: "cu_seqlens_q"}
+
+
+def set_input_checks(on: bool) -> bool:
+    """Make every compute call check the device-content contract on the host
+    first (check_inputs; it copies the metadata to the host and so
+    synchronises).  Returns the previous setting."""
+    global _INPUT_CHECKS
+    prev, _INPUT_CHECKS = _INPUT_CHECKS, bool(on)
+    return prev
+
+
+def check_inputs(pl: Plan, block_table: torch.Tensor, lens: torch.Tensor, num_pages: int,
+                 cu_seqlens_q: Optional[torch.Tensor] = None) -> None:
+    """paged_attn_check_inputs on host copies: lengths within the plan's
+    bound, every page id a call reads in [0, num_pages), and (extend) the
+    query offsets cu_seqlens_q.  Raises ValueError naming the bad element."""
+    bt = block_table.detach().to("cpu", torch.int32).contiguous()
+    ln = lens.detach().to("cpu", torch.int32).contiguous()
+    cu = None if cu_seqlens_q is None else cu_seqlens_q.detach().to("cpu", torch.int32).contiguous()
+    arr, idx = ctypes.c_int32(0), ctypes.c_int64(-1)
+    st = lib().paged_attn_check_inputs(
+        ctypes.byref(pl.c), _ptr(ln), _ptr(bt), bt.stride(0) if bt.dim() == 2 else 0,
+        int(num_pages), _ptr(cu), ctypes.byref(arr), ctypes.byref(idx))
+    if st == 2 and arr.value:
+        name = _BAD_ARRAY[arr.value]
+        i = idx.value
+        if name == "block_table":
+            where = f"[{i // bt.stride(0)}, {i % bt.stride(0)}] = {int(bt.view(-1)[i])}"
+        else:
+            where = f"[{i}] = {int((ln if name == 'lens' else cu)[i])}"
+        raise ValueError(f"device-content contract broken: {name}{where} "
+                         f"({pl.describe()}, num_pages={num_pages})")
+    _check("paged_attn_check_inputs", st)
+
+
 def workspace_for(pl: Plan, device) -> Optional[torch.Tensor]:
     """Device scratch of plan.workspace_bytes bytes (None when none is needed)."""
     if pl.workspace_bytes == 0:
@@ -366,6 +409,8 @@ def _decode(fn, pl, q, k_pool, v_pool, block_table, seq_lens, scale, softcap, wi
     _same_device(q, k_pool=k_pool, v_pool=v_pool, block_table=block_table,
                  seq_lens=seq_lens, out=out, workspace=workspace, sinks=sinks,
                  k_descale=k_descale, v_descale=v_descale, alibi_slopes=alibi_slopes)
+    if _INPUT_CHECKS:
+        check_inputs(pl, block_table, seq_lens, k_pool.shape[0])
     dv = pr.head_dim_v or q.shape[-1]
     oshape = q.shape[:-1] + (dv,)
     if out is None:
@@ -439,6 +484,8 @@ def extend(pl: Plan, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
                  k_pool=k_pool, v_pool=v_pool, block_table=block_table, out=out,
                  workspace=workspace, sinks=sinks, k_descale=k_descale, v_descale=v_descale,
                  alibi_slopes=alibi_slopes)
+    if _INPUT_CHECKS:
+        check_inputs(pl, block_table, ctx_lens, k_pool.shape[0], cu_seqlens_q)
     if out is None:
         out = torch.empty_like(q)
     if out.dtype != torch.bfloat16 or out.shape != q.shape or not out.is_contiguous():
@@ -471,6 +518,14 @@ def cache_append(key: torch.Tensor, value: torch.Tensor, k_pool: torch.Tensor,
         raise TypeError("slot_mapping must be int64 [T]")
     sp, st, sh = _pool_strides(k_pool, v_pool)
     T, Hkv, D = key.shape
+    if _INPUT_CHECKS and T > 0:
+        top = int(slot_mapping.max())
+        if top >= k_pool.shape[0] * k_pool.shape[1]:
+            raise ValueError(f"device-content contract broken: slot_mapping holds {top}, "
+                             f"the pools have {k_pool.shape[0] * k_pool.shape[1]} slots")
+        live = slot_mapping[slot_mapping >= 0]
+        if live.numel() != torch.unique(live).numel():
+            raise ValueError("device-content contract broken: slot_mapping repeats a slot")
     _check("paged_attn_cache_append", lib().paged_attn_cache_append(
         _ptr(key), _ptr(value), T, key.stride(0), Hkv, D, _ptr(k_pool), _ptr(v_pool), sp, st,
         sh, k_pool.shape[0], k_pool.shape[1], PA_KV[_kv_dtype_name(k_pool)],
@@ -486,6 +541,11 @@ def gather(pl: Plan, k_pool: torch.Tensor, v_pool: torch.Tensor, block_table: to
         raise ValueError("block_table rows must be contiguous")
     _check_cache(pl, k_pool, block_table, seq_lens, "seq_lens")
     _same_device(k_pool, v_pool=v_pool, block_table=block_table, seq_lens=seq_lens)
+    if _INPUT_CHECKS:
+        check_inputs(pl, block_table, seq_lens, k_pool.shape[0])
+        need = int(seq_lens[:pl.problem.num_seqs].to("cpu", torch.int64).sum())
+        if total_tokens < need:
+            raise ValueError(f"total_tokens {total_tokens} < sum(seq_lens) = {need}")
     sp, st, sh = _pool_strides(k_pool, v_pool)
     shape = (total_tokens, k_pool.shape[2], k_pool.shape[3])
     k_out = torch.empty(shape, dtype=k_pool.dtype, device=k_pool.device)

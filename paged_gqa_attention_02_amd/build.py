@@ -60,5 +60,54 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
     return LIB
 
 
+# Host-sanitized variant: the host code (planning, argument checks, the
+# scratch lookup) under AddressSanitizer and UndefinedBehaviorSanitizer, every
+# finding fatal; device code is built as usual.  A process loading it must
+# preload clang's ASan runtime (sanitizer_preload()).
+HOST_SOURCES = ["api.cpp", "noalloc.hip"]
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host",
+                 "-fno-omit-frame-pointer", "-g"]
+
+
+def sanitizer_preload() -> str:
+    res = subprocess.run([HIPCC, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                         capture_output=True, text=True, check=True)
+    path = res.stdout.strip()
+    if not os.path.isabs(path):
+        # older drivers print the bare name: look in the compiler's resource dir
+        rd = subprocess.run([HIPCC, "-print-resource-dir"], capture_output=True, text=True,
+                            check=True).stdout.strip()
+        path = os.path.join(rd, "lib", "linux", "libclang_rt.asan-x86_64.so")
+    return path
+
+
+def build_host_sanitized(outdir: str, verbose: bool = False) -> str:
+    """Build libpaged_attn.so into outdir with the host sources sanitized and
+    the kernels' objects from the last build() (built first if missing)."""
+    objdir = os.path.join(PKG, "_build")
+    kernels = [s for s in SOURCES if s not in HOST_SOURCES]
+    kobjs = [os.path.join(objdir, s + ".o") for s in kernels]
+    if not all(os.path.exists(o) for o in kobjs):
+        build(verbose=verbose)
+    os.makedirs(outdir, exist_ok=True)
+    hobjs = []
+    for s in HOST_SOURCES:
+        o = os.path.join(outdir, s + ".o")
+        cmd = [HIPCC] + flags() + ["-O1"] + SANITIZE_HOST + ["-c", "-o", o,
+                                                           os.path.join(CSRC, s)]
+        rc, err = _run(cmd)
+        if rc != 0:
+            raise RuntimeError(f"hipcc failed on {s} ({rc}):\n{err}")
+        hobjs.append(o)
+    out = os.path.join(outdir, "libpaged_attn.so")
+    rc, err = _run([HIPCC] + flags() + SANITIZE_HOST + ["-Xarch_host", "-shared-libsan",
+                                                        "-shared", "-o", out] +
+                   hobjs + kobjs + ["-ldl"])
+    if rc != 0:
+        raise RuntimeError(f"hipcc link failed ({rc}):\n{err}")
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

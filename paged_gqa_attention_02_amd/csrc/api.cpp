@@ -212,6 +212,7 @@ const char* paged_attn_status_str(pa_status s) {
         case PA_ERR_MISALIGNED: return "misaligned pointer or stride";
         case PA_ERR_PLAN_MISMATCH: return "arguments do not match the plan";
         case PA_ERR_HIP: return "HIP runtime error";
+        case PA_STATUS_MAX_ENUM: break;
     }
     return "unknown status";
 }
@@ -604,6 +605,45 @@ pa_status paged_attn_cache_append(const void* key, const void* value, int64_t nu
     if (launch_cache_append(p, kv_dtype == PA_KV_FP8_E4M3, static_cast<hipStream_t>(hip_stream)) !=
         hipSuccess)
         return PA_ERR_HIP;
+    return PA_OK;
+}
+
+pa_status paged_attn_check_inputs(const pa_plan* plan, const int32_t* lens,
+                                  const int32_t* block_table, int64_t bt_stride,
+                                  int64_t num_pages, const int32_t* cu_seqlens_q,
+                                  int32_t* bad_array, int64_t* bad_index) {
+    if (bad_array) *bad_array = 0;
+    if (bad_index) *bad_index = -1;
+    if (!plan) return PA_ERR_NULL_POINTER;
+    const pa_problem& pr = plan->prob;
+    const pa_status st = check_problem(pr);
+    if (st != PA_OK) return st;
+    if (bt_stride < pr.max_pages_per_seq || num_pages < 1) return PA_ERR_INVALID_SHAPE;
+    if (pr.num_seqs == 0) return PA_OK;
+    const bool extend = pr.mode == PA_MODE_EXTEND;
+    if (!lens || !block_table || (extend && !cu_seqlens_q)) return PA_ERR_NULL_POINTER;
+    const auto fail = [&](int32_t array, int64_t index) {
+        if (bad_array) *bad_array = array;
+        if (bad_index) *bad_index = index;
+        return PA_ERR_INVALID_SHAPE;
+    };
+    for (int64_t b = 0; b < pr.num_seqs; ++b) {
+        const int32_t L = lens[b];
+        if (L < 0 || L > pr.max_kv_len) return fail(1, b);
+        const int64_t pages = cdiv(L, pr.page_size);
+        for (int64_t j = 0; j < pages; ++j) {
+            const int32_t page = block_table[b * bt_stride + j];
+            if (page < 0 || page >= num_pages) return fail(2, b * bt_stride + j);
+        }
+    }
+    if (extend) {
+        if (cu_seqlens_q[0] != 0) return fail(3, 0);
+        for (int64_t b = 0; b < pr.num_seqs; ++b) {
+            const int64_t n = (int64_t)cu_seqlens_q[b + 1] - cu_seqlens_q[b];
+            if (n < 0 || n > pr.max_q_len) return fail(3, b + 1);
+        }
+        if (cu_seqlens_q[pr.num_seqs] != pr.total_q) return fail(3, pr.num_seqs);
+    }
     return PA_OK;
 }
 

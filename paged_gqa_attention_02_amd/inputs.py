@@ -75,10 +75,12 @@ def deal_pages(lens: Sequence[int], page_size: int, rng: np.random.Generator,
                pool_pages: Optional[int] = None,
                width: Optional[int] = None) -> tuple[np.ndarray, int]:
     """Give each sequence ceil(L/P) distinct physical pages from a seeded
-    random permutation of the pool, dealt in sequence order."""
+    random permutation of the pool, dealt in sequence order.  The pool has at
+    least one page (the C ABI takes no empty pool), also when every length
+    is 0."""
     need = [-(-int(L) // page_size) for L in lens]
     total = sum(need)
-    num_pages = total if pool_pages is None else int(pool_pages)
+    num_pages = max(total, 1) if pool_pages is None else int(pool_pages)
     if num_pages < total:
         raise ValueError("pool too small")
     perm = rng.permutation(num_pages).astype(np.int32)

@@ -17,3 +17,18 @@ def pytest_configure(config):
 def oracle_mod():
     from tests._orc import Oracle
     return Oracle()
+
+
+@pytest.fixture(autouse=True)
+def _device_contract_checks(request):
+    """GPU tests check every call's device-content contract (lengths, page
+    ids, query offsets, slots) on the host before it is launched."""
+    if request.node.get_closest_marker("gpu") is None:
+        yield
+        return
+    import paged_gqa_attention_02_amd as pa
+    prev = pa.set_input_checks(True)
+    try:
+        yield
+    finally:
+        pa.set_input_checks(prev)

@@ -434,3 +434,69 @@ def test_cache_append_validation(kw, status):
 
 def test_cache_append_no_tokens_launches_nothing():
     assert append_status(T=0, key=None, value=None, slots=None) == OK
+
+
+# ---- host-side check of the device-content contract ----
+def _contract_plan(mode=0, **kw):
+    args = dict(mode=mode, num_seqs=3, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                page_size=16, max_pages_per_seq=4, max_kv_len=64, device=-1)
+    args.update(kw)
+    return pa.plan(**args)
+
+
+def _table():
+    return torch.arange(12, dtype=torch.int32).reshape(3, 4)
+
+
+def test_check_inputs_accepts_a_valid_call():
+    pl = _contract_plan()
+    pa.check_inputs(pl, _table(), torch.tensor([64, 0, 17], dtype=torch.int32), 12)
+    # entries past ceil(L/P) are never read: padding may hold anything
+    bt = _table()
+    bt[2, 2:] = -1
+    pa.check_inputs(pl, bt, torch.tensor([64, 0, 32], dtype=torch.int32), 12)
+    ext = _contract_plan(mode=1, total_q=9, max_q_len=5)
+    pa.check_inputs(ext, _table(), torch.tensor([64, 0, 3], dtype=torch.int32), 12,
+                    torch.tensor([0, 5, 5, 9], dtype=torch.int32))
+
+
+@pytest.mark.parametrize("lens,bt_edit,num_pages,cu,what", [
+    ([65, 0, 1], None, 12, None, "lens[0] = 65"),                 # above max_kv_len
+    ([3, -1, 1], None, 12, None, "lens[1] = -1"),
+    ([64, 0, 17], (2, 1, 12), 12, None, "block_table[2, 1] = 12"),  # page id = num_pages
+    ([64, 0, 17], (0, 3, -1), 12, None, "block_table[0, 3] = -1"),  # read, so must be valid
+    ([64, 0, 17], None, 9, None, "block_table[2, 1] = 9"),           # fewer pages in the pool
+])
+def test_check_inputs_names_the_bad_element(lens, bt_edit, num_pages, cu, what):
+    pl = _contract_plan()
+    bt = _table()
+    if bt_edit:
+        bt[bt_edit[0], bt_edit[1]] = bt_edit[2]
+    with pytest.raises(ValueError, match=re.escape(what)):
+        pa.check_inputs(pl, bt, torch.tensor(lens, dtype=torch.int32), num_pages)
+
+
+@pytest.mark.parametrize("cu,what", [
+    ([1, 5, 5, 9], "cu_seqlens_q[0] = 1"),      # must start at 0
+    ([0, 6, 6, 9], "cu_seqlens_q[1] = 6"),      # 6 rows > max_q_len 5
+    ([0, 5, 4, 9], "cu_seqlens_q[2] = 4"),      # not monotone
+    ([0, 5, 5, 8], "cu_seqlens_q[3] = 8"),      # does not end at total_q
+])
+def test_check_inputs_extend_offsets(cu, what):
+    ext = _contract_plan(mode=1, total_q=9, max_q_len=5)
+    with pytest.raises(ValueError, match=re.escape(what)):
+        pa.check_inputs(ext, _table(), torch.tensor([64, 0, 3], dtype=torch.int32), 12,
+                        torch.tensor(cu, dtype=torch.int32))
+
+
+def test_check_inputs_argument_errors():
+    pl = _contract_plan()
+    lens = torch.tensor([1, 1, 1], dtype=torch.int32)
+    with pytest.raises(pa.PagedAttnError) as e:
+        pa.check_inputs(pl, _table()[:, :2], lens, 12)      # row stride below the plan's
+    assert e.value.status == SHAPE
+    ext = _contract_plan(mode=1, total_q=9, max_q_len=5)
+    with pytest.raises(pa.PagedAttnError) as e:
+        pa.check_inputs(ext, _table(), lens, 12)             # extend needs cu_seqlens_q
+    assert e.value.status == NULLP
+    assert pa.lib().paged_attn_check_inputs(None, None, None, 0, 1, None, None, None) == NULLP
