@@ -203,7 +203,11 @@ def decode_entry(args, torch, pa, I, case, steps, warmup, cpu_s, seed_note):
                      "traffic": traffic_for("decode_split", case.name, srcs),
                      "us_per_launch": split_ms * 1e3,
                      "timing": f"HIP events around {steps} back-to-back split-pass launches",
-                     "rocprof_us_per_launch": None if trace is None else trace["avg_us"]},
+                     # the committed rocprofv3 kernel average of these sources, and
+                     # the fraction it gives
+                     "rocprof_us_per_launch": None if trace is None else trace["avg_us"],
+                     "frac_rocprof": None if trace is None else
+                     alg / (trace["avg_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS},
     }
     if cpu_s > 0:
         import oracle
@@ -237,6 +241,15 @@ def extend_entry(args, torch, pa, I, steps, warmup, cpu_s):
     achieved = flops / (k_ms * 1e-3) / 1e12
     trace = profile_record("trace", "extend", "extend", EXTEND_SOURCES)
     sq = profile_record("sq", "extend", "extend", EXTEND_SOURCES)
+    traffic = traffic_for("extend", "extend", EXTEND_SOURCES)
+    # bytes every call must move at least once: the attended context K/V,
+    # the new K/V rows, Q and out
+    D, Hq, Hkv = case.head_dim, case.num_q_heads, case.num_kv_heads
+    # (with a window W the first new token, at position C, sees the context
+    # keys from C - W + 1)
+    ctx_keys = sum((min(int(c), case.window - 1) if case.window > 0 else int(c)) if n else 0
+                   for c, n in zip(case.ctx_lens, case.q_lens))
+    unique = (ctx_keys + case.total_q) * Hkv * D * 2 * 2 + 2 * case.total_q * Hq * D * 2
     e = {
         "workload": "extend", "batch": case.batch,
         "num_q_heads": case.num_q_heads, "num_kv_heads": case.num_kv_heads,
@@ -244,13 +257,19 @@ def extend_entry(args, torch, pa, I, steps, warmup, cpu_s):
         "total_q": case.total_q, "context_tokens": int(case.ctx_lens.sum()), "seed": 5,
         "ms_per_step": ms_step, "us_per_call": k_ms * 1e3,
         "value": flops / (ms_step * 1e-3) / 1e12, "unit": "TFLOP/s",
-        "algorithmic_flops": flops, "plan": plan.describe(),
-        "roofline": {"bound": "mfma", "kernel": "extend (whole call)", "achieved": achieved,
-                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+        "algorithmic_flops": flops, "unique_bytes": unique, "plan": plan.describe(),
+        "roofline": {"bound": "mfma", "kernel": "extend (whole call: scan, blocks, merge)",
+                     "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": traffic_for("extend", "extend", EXTEND_SOURCES),
+                     "traffic": traffic,
+                     "traffic_over_unique": None if traffic is None else traffic / unique,
                      "timing": f"HIP events around {steps} back-to-back calls",
+                     # committed rocprofv3 averages of these sources: the main
+                     # kernel, and the three kernels of a call together
                      "rocprof_us_per_launch": None if trace is None else trace["avg_us"],
+                     "rocprof_us_per_call": None if trace is None else trace["call_us"],
+                     "frac_rocprof": None if trace is None else
+                     flops / (trace["call_us"] * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                      "mfma_busy": None if sq is None else sq.get("mfma_busy")},
     }
     if cpu_s > 0:
@@ -283,7 +302,7 @@ def line(e, args, metric):
            "dtype": "bf16" if kv == "bf16" else "fp8_e4m3 KV, bf16 Q/out",
            "data": "synthetic", "config": config}
     for k in ("us_per_call", "hbm_frac", "algorithmic_bytes", "algorithmic_flops", "kv_bytes",
-              "plan", "roofline", "cpu_baseline"):
+              "unique_bytes", "plan", "roofline", "cpu_baseline"):
         if k in e:
             res[k] = e[k]
     return res

@@ -246,6 +246,60 @@ def test_decode_split_invariance(oracle_mod, splits):
     close(la, lb)
 
 
+def _lse_merge(a, b):
+    """Softmax over the union of two disjoint key sets from the two sets'
+    normalised sums and natural-log normalisers (a, b: (out, lse))."""
+    (oa, la), (ob, lb) = a, b
+    m = np.maximum(la, lb)
+    wa, wb = np.exp(la - m), np.exp(lb - m)
+    return ((wa[..., None] * oa + wb[..., None] * ob) / (wa + wb)[..., None],
+            m + np.log(wa + wb))
+
+
+def test_decode_key_ranges_merge_associatively(oracle_mod):
+    """Decode over three disjoint key ranges of one sequence, each run as its
+    own sequence, merged by log-sum-exp in either grouping, equals decode
+    over all the keys: the lse the oracle returns is the normaliser of the
+    softmax (no positional term enters without window or ALiBi)."""
+    rng = np.random.default_rng(44)
+    Hq, Hkv, D, L = 8, 2, 64, 150
+    q = I.bf16_bits(rng.standard_normal((1, Hq, D)).astype(np.float32))
+    k, v = _tokens(Hkv, D, L, rng), _tokens(Hkv, D, L, rng)
+
+    def part(a, b):
+        case = I.decode_case_from_tokens(f"r{a}", q, k[a:b], v[a:b], [b - a], 16, 45 + a,
+                                         softcap=20.0)
+        return oracle_mod.decode(case)
+
+    full = part(0, L)
+    A, B, C = part(0, 40), part(40, 97), part(97, L)
+    left = _lse_merge(_lse_merge(A, B), C)
+    right = _lse_merge(A, _lse_merge(B, C))
+    for got in (left, right):
+        close(got[0], full[0])
+        close(got[1], full[1])
+
+
+def test_decode_window_is_decode_of_the_last_w_keys(oracle_mod):
+    """A window W gives the same result as no window over the sequence's
+    last min(L, W) tokens."""
+    rng = np.random.default_rng(46)
+    Hq, Hkv, D, W = 8, 2, 64, 37
+    lens = [100, 20, 37, 38, 1]
+    q = I.bf16_bits(rng.standard_normal((len(lens), Hq, D)).astype(np.float32))
+    k, v = _tokens(Hkv, D, sum(lens), rng), _tokens(Hkv, D, sum(lens), rng)
+    win = I.decode_case_from_tokens("win", q, k, v, lens, 16, 47, window=W)
+    starts = np.concatenate([[0], np.cumsum(lens)])
+    keep = np.concatenate([np.arange(starts[b + 1] - min(L, W), starts[b + 1])
+                           for b, L in enumerate(lens)])
+    tail = I.decode_case_from_tokens("tail", q, k[keep], v[keep], [min(L, W) for L in lens],
+                                     16, 48)
+    a, la = oracle_mod.decode(win)
+    b, lb = oracle_mod.decode(tail)
+    close(a, b)
+    close(la, lb)
+
+
 def test_decode_page_permutation_bit_identical(oracle_mod):
     case = rand_decode([45, 200, 16], 8, 2, 64, 16, 19)
     a, _ = oracle_mod.decode(case)
