@@ -58,6 +58,9 @@ constexpr int kStageRows = kExtKeys / kExtWaves; // rows of a tile one wave stag
 // differ in one bit of the buffer index, so moving to the next tile's buffer
 // is one XOR); bf16 loads run two tiles ahead.
 constexpr int kExtBuffers = 4;
+#ifndef PA_EXTEND_PIPE
+#define PA_EXTEND_PIPE 1
+#endif
 __host__ __device__ constexpr int gray4(int i) { return (i & 3) ^ ((i & 3) >> 1); }
 static_assert(gray4(0) == 0 && gray4(1) == 1 && gray4(2) == 3 && gray4(3) == 2 &&
                   gray4(4) == 0 && gray4(7) == 2,
@@ -513,6 +516,79 @@ __device__ __forceinline__ SoftmaxState tile_softmax(f32x16 (&s)[2], u32x4 (&pk)
     return st;
 }
 
+// The V^T operands of P V step st (keys 16 st .. 16 st + 15), block db.
+template <int D>
+__device__ __forceinline__ void read_v_step(u32x2 (&v)[D / 16], const uint8_t* vt,
+                                            const LaneOffs<D>& lo, int st) {
+    constexpr int kPitch = Tile<D>::kPitch;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+        const uint8_t* r = vt + 16 * st * kPitch + lo.voff[db];
+        v[2 * db] = lds_read_tr16(r);
+        v[2 * db + 1] = lds_read_tr16(r + 8 * kPitch);
+    }
+}
+
+// S^T = K Q^T for both key halves with the operand reads of key half 1
+// issued one by one behind the MFMAs of half 0 (each register takes its
+// half-1 operand as soon as its half-0 MFMA has it), and the V^T operands
+// of the first P V step read after them, to arrive during the softmax.
+template <int D>
+__device__ __forceinline__ void qk_tile(f32x16 (&s)[2], u32x2 (&v0)[D / 16],
+                                        const uint8_t* kt, const uint8_t* vt,
+                                        const LaneOffs<D>& lo, const u32x4 (&q)[D / 16]) {
+    constexpr int kPitch = Tile<D>::kPitch;
+    constexpr int kDS = D / 16;
+    u32x4 a[kDS];
+#pragma unroll
+    for (int ds = 0; ds < kDS; ++ds)
+        a[ds] = *reinterpret_cast<const u32x4*>(kt + lo.koff[ds]);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 acc = {};
+#pragma unroll
+    for (int ds = 0; ds < kDS; ++ds) {
+        acc = mfma_bf16_32x32x16(a[ds], q[ds], acc);
+        a[ds] = *reinterpret_cast<const u32x4*>(kt + 32 * kPitch + lo.koff[ds]);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
+    }
+    s[0] = acc;
+    __builtin_amdgcn_sched_barrier(0);
+    acc = f32x16{};
+#pragma unroll
+    for (int ds = 0; ds < kDS; ++ds) acc = mfma_bf16_32x32x16(a[ds], q[ds], acc);
+    read_v_step<D>(v0, vt, lo, 0);
+    s[1] = acc;
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// O^T += V^T P^T over the four 16-key steps; step st's operands (v, read
+// ahead) feed its MFMAs while step st + 1's are read into the registers
+// each MFMA has just taken.
+template <int D>
+__device__ __forceinline__ void pv_tile(f32x16 (&o)[D / 32], u32x2 (&v)[D / 16],
+                                        const uint8_t* vt, const LaneOffs<D>& lo,
+                                        const u32x4 (&pk)[4]) {
+    constexpr int kPitch = Tile<D>::kPitch;
+    constexpr int kDB = D / 32;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) {
+            o[db] = mfma_bf16_32x32x16(u32x4{v[2 * db].x, v[2 * db].y, v[2 * db + 1].x,
+                                             v[2 * db + 1].y},
+                                       pk[st], o[db]);
+            if (st < 3) {
+                const uint8_t* r = vt + 16 * (st + 1) * kPitch + lo.voff[db];
+                v[2 * db] = lds_read_tr16(r);
+                v[2 * db + 1] = lds_read_tr16(r + 8 * kPitch);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+        }
+    }
+}
+
 // One 64-key tile (K and V at the offsets lo selects): S^T = K Q^T for both
 // key halves, the online softmax (the masked variant unless the tile is
 // FAST), P V.  Only the softmax differs between the variants, so the
@@ -526,8 +602,13 @@ __device__ __forceinline__ void tile_compute(bool fast, const uint8_t* kbuf,
     constexpr int kDB = D / 32;
     const int key0 = jt + 4 * ((threadIdx.x & 63) >> 5);
     f32x16 s[2];
+#if PA_EXTEND_PIPE
+    u32x2 v[D / 16];
+    qk_tile<D>(s, v, kbuf, vbuf, lo, q);
+#else
     qk_half<D, 0>(s[0], kbuf, lo, q);
     qk_half<D, 1>(s[1], kbuf, lo, q);
+#endif
     u32x4 pk[4];
     const SoftmaxState st =
         fast ? tile_softmax<MODE, true>(s, pk, A.m, A.l, p, si, ts, pos_q, al2, key0)
@@ -536,8 +617,12 @@ __device__ __forceinline__ void tile_compute(bool fast, const uint8_t* kbuf,
 #pragma unroll
         for (int db = 0; db < kDB; ++db) A.o[db] *= st.alpha;
     }
+#if PA_EXTEND_PIPE
+    pv_tile<D>(A.o, v, vbuf, lo, pk);
+#else
     pv_half<D, 0>(A.o, vbuf, lo, reinterpret_cast<const u32x4(&)[2]>(pk[0]));
     pv_half<D, 1>(A.o, vbuf, lo, reinterpret_cast<const u32x4(&)[2]>(pk[2]));
+#endif
 }
 
 // An item: row tile mt (kExtRows rows (token, head)) of sequence b, kv head
