@@ -159,15 +159,15 @@ __device__ __forceinline__ void load_lds16(const uint8_t* addr, uint32_t lds) {
                  : "=&s"(keep) : "v"(addr), "s"(lds) : "memory");
 }
 
-// bf16: this wave's rows of tile jt of K (V = false) or V straight into LDS
-// at the byte address dst.  In a 1 KB run (kRowsPerRun rows) lane i fills LDS
+// bf16: this wave's rows of tile jt of K and of V straight into LDS at the
+// byte addresses kdst and vdst.  In a 1 KB run (kRowsPerRun rows) lane i fills LDS
 // bytes 16i..16i+15, i.e. slot i % kSlots of row i / kSlots, with the row's
 // chunk (slot ^ swizzle).  Rows in one page (pages of >= kStageRows rows) or
 // all new rows inside the sequence take one wave-uniform base and a 32-bit
 // lane offset; others go lane by lane.
-template <int D, bool V>
-__device__ __forceinline__ void stage_rows(const ExtendParams& p, const SeqInfo& si, int jt,
-                                           uint32_t dst) {
+template <int D>
+__device__ __forceinline__ void stage_kv(const ExtendParams& p, const SeqInfo& si, int jt,
+                                         uint32_t kdst, uint32_t vdst) {
     using TL = Tile<D>;
     // (the lane's row and slot are recomputed per call: nothing lane-dependent
     // of the staging stays live across the tile loop)
@@ -175,38 +175,47 @@ __device__ __forceinline__ void stage_rows(const ExtendParams& p, const SeqInfo&
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int rr = lane / TL::kSlots, sl = lane % TL::kSlots;
     const int j0 = jt + wave * kStageRows;
-    const uint32_t d0 = dst + wave * TL::kRuns * 1024;
-    auto chunk = [&](int k) {
+    const uint32_t dk = kdst + wave * TL::kRuns * 1024, dv = vdst + wave * TL::kRuns * 1024;
+    auto kchunk = [&](int k) {
         const int r = wave * kStageRows + k * TL::kRowsPerRun + rr;
-        return (uint32_t)(16 * (sl ^ (V ? TL::vswz(r) : TL::kswz(r))));
+        return (uint32_t)(16 * (sl ^ TL::kswz(r)));
+    };
+    auto vchunk = [&](int k) {
+        const int r = wave * kStageRows + k * TL::kRowsPerRun + rr;
+        return (uint32_t)(16 * (sl ^ TL::vswz(r)));
     };
     if ((1 << p.page_shift) >= kStageRows && j0 + kStageRows <= si.C) {
+        // K and V rows sit at the same offsets of their pools: one page
+        // lookup for both
         const int idx = min(max((j0 >> p.page_shift) - si.pg0, 0), kExtPages - 1);
         const int64_t page = __builtin_amdgcn_readfirstlane(si.pages[idx]);
         const int pmask = (1 << p.page_shift) - 1;
-        const uint8_t* pool = static_cast<const uint8_t*>(V ? p.v_pool : p.k_pool);
-        const uint8_t* base = pool + (page * p.s_page + (int64_t)(j0 & pmask) * p.s_tok +
-                                      (int64_t)si.kvh * p.s_head) * 2;
+        const int64_t off = (page * p.s_page + (int64_t)(j0 & pmask) * p.s_tok +
+                             (int64_t)si.kvh * p.s_head) * 2;
+        const uint8_t* kb = static_cast<const uint8_t*>(p.k_pool) + off;
+        const uint8_t* vb = static_cast<const uint8_t*>(p.v_pool) + off;
+        const int64_t run = (int64_t)TL::kRowsPerRun * p.s_tok * 2;
         const uint32_t lrow = (uint32_t)rr * (uint32_t)(p.s_tok * 2);
 #pragma unroll
-        for (int k = 0; k < TL::kRuns; ++k)
-            load_lds16(base + (int64_t)k * TL::kRowsPerRun * p.s_tok * 2, lrow + chunk(k),
-                       d0 + k * 1024);
+        for (int k = 0; k < TL::kRuns; ++k) load_lds16(kb + k * run, lrow + kchunk(k), dk + k * 1024);
+#pragma unroll
+        for (int k = 0; k < TL::kRuns; ++k) load_lds16(vb + k * run, lrow + vchunk(k), dv + k * 1024);
     } else if (j0 >= si.C && j0 + kStageRows <= si.C + si.n) {
-        const uint8_t* nrow = static_cast<const uint8_t*>(V ? p.v_new : p.k_new);
         const int64_t rs = (int64_t)p.num_kv_heads * D * 2;
-        const uint8_t* base = nrow + ((int64_t)(si.q0 + j0 - si.C) * p.num_kv_heads + si.kvh) *
-                                         D * 2;
+        const int64_t off = ((int64_t)(si.q0 + j0 - si.C) * p.num_kv_heads + si.kvh) * D * 2;
+        const uint8_t* kb = static_cast<const uint8_t*>(p.k_new) + off;
+        const uint8_t* vb = static_cast<const uint8_t*>(p.v_new) + off;
         const uint32_t lrow = (uint32_t)rr * (uint32_t)rs;
 #pragma unroll
         for (int k = 0; k < TL::kRuns; ++k)
-            load_lds16(base + k * TL::kRowsPerRun * rs, lrow + chunk(k), d0 + k * 1024);
+            load_lds16(kb + k * TL::kRowsPerRun * rs, lrow + kchunk(k), dk + k * 1024);
+#pragma unroll
+        for (int k = 0; k < TL::kRuns; ++k)
+            load_lds16(vb + k * TL::kRowsPerRun * rs, lrow + vchunk(k), dv + k * 1024);
     } else {
         // lane by lane: context rows through the page list, new rows (clamped
         // to the sequence's last one: finite, masked by the consumer) from
         // k_new / v_new
-        const uint8_t* pool = static_cast<const uint8_t*>(V ? p.v_pool : p.k_pool);
-        const uint8_t* nrow = static_cast<const uint8_t*>(V ? p.v_new : p.k_new);
         const int pmask = (1 << p.page_shift) - 1;
 #pragma unroll
         for (int k = 0; k < TL::kRuns; ++k) {
@@ -216,8 +225,13 @@ __device__ __forceinline__ void stage_rows(const ExtendParams& p, const SeqInfo&
                                  (int64_t)(j & pmask) * p.s_tok + (int64_t)si.kvh * p.s_head) * 2;
             const int r = min(max(j - si.C, 0), si.n - 1);
             const int64_t nw = ((int64_t)(si.q0 + r) * p.num_kv_heads + si.kvh) * D * 2;
-            const uint8_t* src = j < si.C ? pool + ctx : nrow + nw;
-            load_lds16(src + chunk(k), d0 + k * 1024);
+            const bool in_ctx = j < si.C;
+            const uint8_t* ks = in_ctx ? static_cast<const uint8_t*>(p.k_pool) + ctx
+                                       : static_cast<const uint8_t*>(p.k_new) + nw;
+            const uint8_t* vs = in_ctx ? static_cast<const uint8_t*>(p.v_pool) + ctx
+                                       : static_cast<const uint8_t*>(p.v_new) + nw;
+            load_lds16(ks + kchunk(k), dk + k * 1024);
+            load_lds16(vs + vchunk(k), dv + k * 1024);
         }
     }
 }
@@ -792,8 +806,7 @@ __device__ __forceinline__ void extend_piece(const ExtendParams& pk, const Item&
     const uint32_t k_lds = lds_addr(L.k), v_lds = lds_addr(L.v);
     auto buf_of = [](int i) { return (uint32_t)(gray4(i) * TL::kBytes); };
     auto stage_bf16 = [&](int i) {
-        stage_rows<D, false>(p, si, jt_of(i), k_lds + buf_of(i));
-        stage_rows<D, true>(p, si, jt_of(i), v_lds + buf_of(i));
+        stage_kv<D>(p, si, jt_of(i), k_lds + buf_of(i), v_lds + buf_of(i));
     };
     constexpr int kLoads = 2 * TL::kRuns;                   // a wave's loads per tile
     auto tile = [&](int i, int c1) {
