@@ -972,10 +972,14 @@ void extend_kernel(ExtendParams p) {
 // Merge: kMergeSlices blocks per item covered by several blocks, each taking a
 // slice of its rows; per row and column quad, the pieces' rows weighted by
 // 2^(lse - max) (the stage-2 merge of the decode page), a sink joining the
-// sum once.  A thread folds kMergeUnits (row, quad) units side by side.
+// sum once.  A thread folds kUnits (row, quad) units side by side, the loads
+// of two pieces in flight together.
 // ---------------------------------------------------------------------------
 constexpr int kExtMergeThreads = 256;
-constexpr int kMergeSlices = 4;
+#ifndef PA_EXTEND_MERGE_SLICES
+#define PA_EXTEND_MERGE_SLICES 16
+#endif
+constexpr int kMergeSlices = PA_EXTEND_MERGE_SLICES;
 
 template <int D>
 __global__ __launch_bounds__(kExtMergeThreads) void extend_merge_kernel(ExtendParams p) {
@@ -999,31 +1003,39 @@ __global__ __launch_bounds__(kExtMergeThreads) void extend_merge_kernel(ExtendPa
         sum[k] = 0.f;
         acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    for (int piece = 0; piece <= rec.y - rec.x; ++piece) {
-        const int64_t base = ext_part_row(rec.x + piece, piece == 0 ? rec.z : 0, 0);
-        float lse[kUnits];
-        f32x4 o[kUnits];
+    // two pieces at a time: both pieces' loads are in flight together
+    const int npieces = rec.y - rec.x + 1;
+    for (int piece0 = 0; piece0 < npieces; piece0 += 2) {
+        float lse[2][kUnits];
+        f32x4 o[2][kUnits];
 #pragma unroll
-        for (int k = 0; k < kUnits; ++k) {
-            const int u = threadIdx.x + kExtMergeThreads * k;
-            const int r = slice * kSliceRows + u / kQ, q = u % kQ;
-            lse[k] = -INFINITY;
-            o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (u < kSliceRows * kQ && r < rows) {
-                lse[k] = p.part_lse[base + r];
-                o[k] = *reinterpret_cast<const f32x4*>(p.part_o + (base + r) * D + 4 * q);
+        for (int pp = 0; pp < 2; ++pp) {
+            const int piece = piece0 + pp;
+            const int64_t base = ext_part_row(rec.x + piece, piece == 0 ? rec.z : 0, 0);
+#pragma unroll
+            for (int k = 0; k < kUnits; ++k) {
+                const int u = threadIdx.x + kExtMergeThreads * k;
+                const int r = slice * kSliceRows + u / kQ, q = u % kQ;
+                lse[pp][k] = -INFINITY;
+                o[pp][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (piece < npieces && u < kSliceRows * kQ && r < rows) {
+                    lse[pp][k] = p.part_lse[base + r];
+                    o[pp][k] = *reinterpret_cast<const f32x4*>(p.part_o + (base + r) * D + 4 * q);
+                }
             }
         }
 #pragma unroll
-        for (int k = 0; k < kUnits; ++k) {
-            if (lse[k] == -INFINITY) continue;          // (an empty block's slot)
-            const float mn = fmaxf(m[k], lse[k]);
-            const float f = m[k] == -INFINITY ? 0.f : fast_exp2(m[k] - mn);
-            const float wt = fast_exp2(lse[k] - mn);
-            sum[k] = sum[k] * f + wt;
-            acc[k] = acc[k] * f + wt * o[k];
-            m[k] = mn;
-        }
+        for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+            for (int k = 0; k < kUnits; ++k) {
+                if (lse[pp][k] == -INFINITY) continue;      // (an empty block's slot)
+                const float mn = fmaxf(m[k], lse[pp][k]);
+                const float f = m[k] == -INFINITY ? 0.f : fast_exp2(m[k] - mn);
+                const float wt = fast_exp2(lse[pp][k] - mn);
+                sum[k] = sum[k] * f + wt;
+                acc[k] = acc[k] * f + wt * o[pp][k];
+                m[k] = mn;
+            }
     }
 #pragma unroll
     for (int k = 0; k < kUnits; ++k) {
