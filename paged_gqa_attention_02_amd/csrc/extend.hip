@@ -32,6 +32,7 @@
 // base is wave-uniform and each lane adds a fixed offset); fp8 context rows go
 // through registers to be converted.  K is staged two tiles ahead, V one: the
 // loads of the next tiles are in flight while this tile is computed.
+#include <climits>
 #include <type_traits>
 
 #include "pa_device.h"
@@ -75,6 +76,13 @@ enum ScoreMode {
     kAlibi = 4,   // flag on kScale / kCap: plus slope * (key - query position)
     kVScale = 8,  // flag: cached values are scaled (v_scale != 1 or per-request
                   // value descales); without it P V takes the values as stored
+};
+
+// What a tile's softmax must handle.
+enum TileKind {
+    kTileMixed = 0,   // masks, and context and new keys scored differently
+    kTileFast = 1,    // no mask, one key kind (or both kinds scored alike)
+    kTileMasked = 2,  // masks (causal limit, window), one key kind
 };
 
 // LDS tile geometry: 64 rows of 2*D bytes, 16-byte slots swizzled by row.
@@ -412,10 +420,10 @@ struct TileScale {
 };
 
 // The online softmax of one key half's scores, in steps:
-//   logits: scale (or soft-cap) in place -- FAST tiles (no mask, one key kind)
-//     with MODE kFold keep raw scores, the positive scale is folded into the
-//     exponent -- masks of a non-FAST tile (causal limit and window of the
-//     lane's row, per-key kind), and the lane's max;
+//   logits: scale (or soft-cap) in place -- tiles of one key kind with MODE
+//     kFold keep raw scores, the positive scale is folded into the exponent
+//     -- masks of a masked tile (causal limit and window of the lane's row),
+//     per-key scales of a mixed one, and the lane's max;
 //   row_max: the lane pair's max; whether any row of the wave moves its
 //     reference max (lazy rescale: only when a score exceeds it by more than
 //     8 in log2 units, so p <= 2^8), and the rescale factor;
@@ -426,30 +434,33 @@ struct SoftmaxState {
     bool move;
 };
 
-template <int MODE, bool FAST>
+template <int MODE, int KIND>
 __device__ __forceinline__ float sm_logits(f32x16& s, const ExtendParams& p, const SeqInfo& si,
                                            const TileScale& ts, int pos_q, float al2,
                                            int key0) {
     constexpr bool kAl = (MODE & kAlibi) != 0;
-    constexpr bool kFolded = (MODE & 7) == kFold && FAST;
+    constexpr bool kFolded = (MODE & 7) == kFold && KIND != kTileMixed;
+    // key key0 + c is kept iff lo_c < c <= hi_c (causal limit; window start)
+    const int hi_c = pos_q - key0;
+    const int lo_c = p.window > 0 ? hi_c - p.window : INT_MIN;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         float v = s[j];
         const int key = key0 + 8 * (j >> 2) + (j & 3);
         if constexpr (!kFolded) {
             const bool ctx = key < si.C;
-            const float qs = FAST ? ts.qs : (ctx ? p.qk_scale2_ctx : p.qk_scale2);
+            const float qs = KIND != kTileMixed ? ts.qs : (ctx ? p.qk_scale2_ctx : p.qk_scale2);
             if constexpr ((MODE & 3) == kCap) {
-                const float c1 = FAST ? ts.c1 : (ctx ? p.cap_c1_ctx : p.cap_c1);
+                const float c1 = KIND != kTileMixed ? ts.c1 : (ctx ? p.cap_c1_ctx : p.cap_c1);
                 v = p.cap_c2 - 2.f * p.cap_c2 * fast_rcp(fast_exp2(v * c1) + 1.f);
             } else {
                 v *= qs;
             }
         }
         if constexpr (kAl) v += al2 * (float)(key - pos_q);
-        if constexpr (!FAST) {
-            const bool keep = key <= pos_q && (p.window <= 0 || pos_q - key < p.window);
-            v = keep ? v : -INFINITY;
+        if constexpr (KIND != kTileFast) {
+            const int c = 8 * (j >> 2) + (j & 3);
+            v = (c <= hi_c && c > lo_c) ? v : -INFINITY;
         }
         s[j] = v;
     }
@@ -461,11 +472,11 @@ __device__ __forceinline__ float sm_logits(f32x16& s, const ExtendParams& p, con
     return vmax(vmax(vmax(a, b), c), vmax(vmax(d, e), s[15]));
 }
 
-template <int MODE, bool FAST>
+template <int MODE, int KIND>
 __device__ __forceinline__ SoftmaxState sm_row_max(float lane_max, float m, const TileScale& ts) {
     constexpr float kSlack = 8.f;
     float tmax = pair_max(lane_max);
-    if constexpr ((MODE & 7) == kFold && FAST) tmax *= ts.qs;
+    if constexpr ((MODE & 7) == kFold && KIND != kTileMixed) tmax *= ts.qs;
     SoftmaxState st;
     st.move = __builtin_amdgcn_ballot_w64(tmax > m + kSlack) != 0;
     st.m_new = st.move ? fmaxf(m, tmax) : m;
@@ -474,19 +485,19 @@ __device__ __forceinline__ SoftmaxState sm_row_max(float lane_max, float m, cons
     return st;
 }
 
-template <int MODE, bool FAST>
+template <int MODE, int KIND>
 __device__ __forceinline__ void sm_exps(f32x16& s, const SoftmaxState& st, float qs) {
-    constexpr bool kFolded = (MODE & 7) == kFold && FAST;
+    constexpr bool kFolded = (MODE & 7) == kFold && KIND != kTileMixed;
 #pragma unroll
     for (int j = 0; j < 16; ++j)
         s[j] = kFolded ? fast_exp2(__builtin_fmaf(s[j], qs, -st.ms)) : fast_exp2(s[j] - st.ms);
 }
 
-template <int MODE, bool FAST>
+template <int MODE, int KIND>
 __device__ __forceinline__ void sm_pack(f32x16& s, u32x4 (&pk)[2], const SeqInfo& si,
                                         const TileScale& ts, int key0) {
     if constexpr ((MODE & kVScale) != 0) {
-        if constexpr (FAST) {
+        if constexpr (KIND != kTileMixed) {
             s *= ts.vs;
         } else {
             // context keys take the cache's value scale, new keys none
@@ -505,16 +516,16 @@ __device__ __forceinline__ void sm_pack(f32x16& s, u32x4 (&pk)[2], const SeqInfo
 // The online softmax of one tile's scores (s[H]: key half H): updates the
 // row statistics and returns the packed probabilities (pk[2H + t]: P V step
 // 2H + t) and whether (and by what) to rescale O.
-template <int MODE, bool FAST>
+template <int MODE, int KIND>
 __device__ __forceinline__ SoftmaxState tile_softmax(f32x16 (&s)[2], u32x4 (&pk)[4], float& m,
                                                      float& l, const ExtendParams& p,
                                                      const SeqInfo& si, const TileScale& ts,
                                                      int pos_q, float al2, int key0) {
-    const float m0 = sm_logits<MODE, FAST>(s[0], p, si, ts, pos_q, al2, key0);
-    const float m1 = sm_logits<MODE, FAST>(s[1], p, si, ts, pos_q, al2, key0 + 32);
-    const SoftmaxState st = sm_row_max<MODE, FAST>(vmax(m0, m1), m, ts);
-    sm_exps<MODE, FAST>(s[0], st, ts.qs);
-    sm_exps<MODE, FAST>(s[1], st, ts.qs);
+    const float m0 = sm_logits<MODE, KIND>(s[0], p, si, ts, pos_q, al2, key0);
+    const float m1 = sm_logits<MODE, KIND>(s[1], p, si, ts, pos_q, al2, key0 + 32);
+    const SoftmaxState st = sm_row_max<MODE, KIND>(vmax(m0, m1), m, ts);
+    sm_exps<MODE, KIND>(s[0], st, ts.qs);
+    sm_exps<MODE, KIND>(s[1], st, ts.qs);
     // the row sum (before any value scale), as a tree of independent adds
     float t4[8];
 #pragma unroll
@@ -524,8 +535,8 @@ __device__ __forceinline__ SoftmaxState tile_softmax(f32x16 (&s)[2], u32x4 (&pk)
         t4[i] = (v[o] + v[o + 1]) + (v[o + 2] + v[o + 3]);
     }
     l = l * st.alpha + (((t4[0] + t4[1]) + (t4[2] + t4[3])) + ((t4[4] + t4[5]) + (t4[6] + t4[7])));
-    sm_pack<MODE, FAST>(s[0], reinterpret_cast<u32x4(&)[2]>(pk[0]), si, ts, key0);
-    sm_pack<MODE, FAST>(s[1], reinterpret_cast<u32x4(&)[2]>(pk[2]), si, ts, key0 + 32);
+    sm_pack<MODE, KIND>(s[0], reinterpret_cast<u32x4(&)[2]>(pk[0]), si, ts, key0);
+    sm_pack<MODE, KIND>(s[1], reinterpret_cast<u32x4(&)[2]>(pk[2]), si, ts, key0 + 32);
     m = st.m_new;
     return st;
 }
@@ -604,11 +615,11 @@ __device__ __forceinline__ void pv_tile(f32x16 (&o)[D / 32], u32x2 (&v)[D / 16],
 }
 
 // One 64-key tile (K and V at the offsets lo selects): S^T = K Q^T for both
-// key halves, the online softmax (the masked variant unless the tile is
-// FAST), P V.  Only the softmax differs between the variants, so the
-// accumulators never pass through the branch.
+// key halves, the online softmax (the variant of the tile's kind), P V.  Only
+// the softmax differs between the variants, so the accumulators never pass
+// through the branch.
 template <int D, int MODE>
-__device__ __forceinline__ void tile_compute(bool fast, const uint8_t* kbuf,
+__device__ __forceinline__ void tile_compute(int kind, const uint8_t* kbuf,
                                              const uint8_t* vbuf, const LaneOffs<D>& lo,
                                              const u32x4 (&q)[D / 16], ExtAcc<D>& A,
                                              const ExtendParams& p, const SeqInfo& si,
@@ -625,8 +636,11 @@ __device__ __forceinline__ void tile_compute(bool fast, const uint8_t* kbuf,
 #endif
     u32x4 pk[4];
     const SoftmaxState st =
-        fast ? tile_softmax<MODE, true>(s, pk, A.m, A.l, p, si, ts, pos_q, al2, key0)
-             : tile_softmax<MODE, false>(s, pk, A.m, A.l, p, si, ts, pos_q, al2, key0);
+        kind == kTileFast
+            ? tile_softmax<MODE, kTileFast>(s, pk, A.m, A.l, p, si, ts, pos_q, al2, key0)
+        : kind == kTileMasked
+            ? tile_softmax<MODE, kTileMasked>(s, pk, A.m, A.l, p, si, ts, pos_q, al2, key0)
+            : tile_softmax<MODE, kTileMixed>(s, pk, A.m, A.l, p, si, ts, pos_q, al2, key0);
     if (st.move) {
 #pragma unroll
         for (int db = 0; db < kDB; ++db) A.o[db] *= st.alpha;
@@ -773,10 +787,14 @@ __device__ __forceinline__ void extend_piece(const ExtendParams& pk, const Item&
     // a tile needs no mask when it ends at or before the first row's diagonal
     // and starts inside the last row's window; it has one key kind when it
     // does not straddle the context's end
-    auto fast_tile = [&](int jt) {
-        return jt + kExtKeys - 1 <= pos_first &&
-               (p.window <= 0 || jt >= pos_last - p.window + 1) &&
-               (jt + kExtKeys <= si.C || jt >= si.C);
+    // context and new keys are scored and weighted alike (unit cache scales)
+    const bool one_scale = p.qk_scale2_ctx == p.qk_scale2 && p.cap_c1_ctx == p.cap_c1 &&
+                           (MODE & kVScale) == 0;
+    auto tile_kind = [&](int jt) {
+        const bool one_kind = one_scale || jt + kExtKeys <= si.C || jt >= si.C;
+        const bool unmasked = jt + kExtKeys - 1 <= pos_first &&
+                              (p.window <= 0 || jt >= pos_last - p.window + 1);
+        return !one_kind ? kTileMixed : unmasked ? kTileFast : kTileMasked;
     };
     auto tile_scale = [&](int jt) {
         const bool ctx = jt < si.C;
@@ -825,7 +843,7 @@ __device__ __forceinline__ void extend_piece(const ExtendParams& pk, const Item&
             }
         }
         const TileScale ts = tile_scale(jt);
-        tile_compute<D, MODE>(fast_tile(jt), L.k, L.v, lo, q, A, p, si, ts, pos_q, al2, jt);
+        tile_compute<D, MODE>(tile_kind(jt), L.k, L.v, lo, q, A, p, si, ts, pos_q, al2, jt);
         if constexpr (FP8) {
             if (i + 1 < c1) {
                 stage8_store<D, false>(sk, L.k + buf_of(i + 1));
