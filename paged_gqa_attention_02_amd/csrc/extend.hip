@@ -22,18 +22,18 @@
 //   O^T[D x 32] += V^T[D x 64] P^T[64 x 32]          P^T is the S^T accumulator
 //                                                   itself; V^T comes from
 //                                                   transposing LDS reads
-// The wave computes the next tile's S^T while it runs this tile's softmax (the
-// two are independent), then this tile's P V.
+// The LDS operand reads run ahead of the MFMAs that take them: key half 1's
+// K operands behind half 0's MFMAs, each P V step's V operands behind the
+// previous step's, the first step's under the softmax.
 //
 // K/V tiles live in LDS as bf16 rows of 2*D bytes with 16-byte slots
-// XOR-swizzled by row, so that operand reads hit distinct banks.  bf16 caches
-// are staged with direct global->LDS loads (a wave fills whole 1 KB runs of
-// its own rows of a tile; with pages of >= 16 rows a run has one page, so its
-// base is wave-uniform and each lane adds a fixed offset); fp8 context rows go
-// through registers to be converted.  K is staged two tiles ahead, V one: the
-// loads of the next tiles are in flight while this tile is computed.
+// XOR-swizzled by row, so that operand reads hit distinct banks, in a ring
+// of four buffers per kind.  bf16 caches are staged with direct global->LDS
+// loads two tiles ahead (a wave fills whole 1 KB runs of its own rows of a
+// tile, K and V at once; with pages of >= 8 rows a run has one page, so its
+// base is wave-uniform and each lane adds a fixed offset); fp8 context rows
+// go through registers to be converted, one tile ahead.
 #include <climits>
-#include <type_traits>
 
 #include "pa_device.h"
 #include "pa_internal.h"
