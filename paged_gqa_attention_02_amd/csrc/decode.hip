@@ -559,7 +559,7 @@ void decode_split_kernel(DecodeParams p) {
             {
                 const int32_t* bt_row =
                     p.block_table + (int64_t)b * p.bt_stride + x.first_page;
-                for (int i = threadIdx.x; i < n_pages; i += 64 * NW) sm_pages[i] = bt_row[i];
+                copy_ids_to_lds<8>(sm_pages, bt_row, n_pages, threadIdx.x, 64 * NW);
             }
             __syncthreads();
 

@@ -871,7 +871,7 @@ __device__ __forceinline__ void extend_piece(const ExtendParams& pk, const Item&
             si.pg0 = jlo >> p.page_shift;
             const int cnt = jhi >= jlo ? (jhi >> p.page_shift) - si.pg0 + 1 : 0;
             const int32_t* row = p.block_table + (int64_t)si.b * p.bt_stride + si.pg0;
-            for (int i = threadIdx.x; i < cnt; i += kExtThreads) L.pages[i] = row[i];
+            copy_ids_to_lds<4>(L.pages, row, cnt, threadIdx.x, kExtThreads);
             __syncthreads();
         }
         if constexpr (!FP8) {

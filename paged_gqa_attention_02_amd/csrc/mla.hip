@@ -344,7 +344,7 @@ __global__ __launch_bounds__(64 * NW) void mla_split_kernel(DecodeParams p) {
             const int n_pages = ((ch.t_end - 1) >> p.page_shift) - ch.first_page + 1;
             __syncthreads();     // the previous chunk's readers are done with the list
             const int32_t* bt = p.block_table + (int64_t)b * p.bt_stride + ch.first_page;
-            for (int i = threadIdx.x; i < n_pages; i += 64 * NW) sm_pages[i] = bt[i];
+            copy_ids_to_lds<8>(sm_pages, bt, n_pages, threadIdx.x, 64 * NW);
             __syncthreads();
         };
         auto next_piece = [&]() {

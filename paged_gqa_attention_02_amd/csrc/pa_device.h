@@ -106,4 +106,26 @@ __device__ __forceinline__ float col4_sum(float v) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Copy of n page ids from global memory to LDS by `threads` threads (thread
+// t takes entries t, t + threads, ...).  Each thread issues kInFlight loads
+// before it stores any, so the copy waits on memory about
+// n / (threads * kInFlight) times rather than n / threads (pages of one
+// token make a chunk's list thousands of ids long).
+template <int kInFlight>
+__device__ __forceinline__ void copy_ids_to_lds(int* dst, const int32_t* src, int n, int t,
+                                                int threads) {
+    for (int i0 = t; i0 < n; i0 += kInFlight * threads) {
+        int v[kInFlight];
+        // (an index past the list reads its last entry: no branch between
+        // the loads, and nothing read outside the list)
+#pragma unroll
+        for (int u = 0; u < kInFlight; ++u) v[u] = src[min(i0 + u * threads, n - 1)];
+#pragma unroll
+        for (int u = 0; u < kInFlight; ++u) {
+            const int i = i0 + u * threads;
+            if (i < n) dst[i] = v[u];
+        }
+    }
+}
+
 }  // namespace pa
