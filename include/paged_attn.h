@@ -143,7 +143,10 @@ typedef struct {
                                   verify: the query tokens per sequence
                                   (q_len >= 1, G * q_len <= 64) */
     int32_t num_splits;        /* decode: 0 = plan chooses; > 0 forces the
-                                  number of split-pass pieces (waves) */
+                                  number of split-pass pieces (blocks),
+                                  rounded up to a multiple of num_kv_heads
+                                  when that is at most 8 (not for a latent
+                                  cache) */
     int32_t head_dim_v;        /* value head dim: 0 (or head_dim) = head_dim;
                                   head_dim_v < head_dim selects a latent cache
                                   (decode, bf16, (576, 512) or (288, 256)):
@@ -176,11 +179,17 @@ typedef struct {
 /*
  * paged_attn_plan -- choose the split-KV decomposition and size the workspace.
  *
- * Decode: the 32-token tiles of every (sequence, kv head) key range [lo, L)
- * (lo = max(0, L-W) with a window), laid end to end, are cut into
- * out->num_splits equal contiguous pieces, one per persistent block of the
- * split pass; the plan takes as many as the device keeps resident (compute
- * units x resident blocks per unit), or prob->num_splits when that is > 0.
+ * Decode with Hkv <= 8 kv heads: for each kv head h, the 32-token tiles of
+ * its key ranges [lo, L) (lo = max(0, L-W) with a window) over all
+ * sequences, laid end to end, are cut into out->num_splits / Hkv equal
+ * contiguous pieces; block h * (num_splits / Hkv) + j of the split pass takes
+ * piece j of head h, so the blocks reading the kv heads of one token range
+ * run side by side (a token's heads are adjacent in the pool).  With more kv
+ * heads, and for a latent cache, all (sequence, head) ranges laid end to end
+ * are cut into num_splits pieces.  The plan takes as many blocks as the
+ * device keeps resident (compute units x resident blocks per unit, rounded
+ * down to a multiple of Hkv <= 8), or prob->num_splits (rounded up to one)
+ * when that is > 0.
  * A block has one wave per 16 query rows of a kv head (G for decode,
  * G * q_len for verify); its waves walk the same tiles.  Latent cache: the
  * count is rounded up to 2, 4 or 8; with at most 16 query heads over one pool

@@ -445,8 +445,18 @@ void decode_split_kernel(DecodeParams p) {
     const int grp = lane >> 4;
     const int cg = 16 * wv + c;                 // this lane's query row
     const int G = p.group;
+    // With per-head streams (HG = Hkv), block h*Wg + j takes kv head h over
+    // range j of that head's stream (the plan makes the block count a
+    // multiple of HG), so the blocks of the heads of one token range run side
+    // by side; otherwise (HG = 1) one stream holds hm = Hkv segments per
+    // sequence.
     const int64_t W = gridDim.x;
     const int64_t w = blockIdx.x;
+    const int HG = split_head_groups(p.num_kv_heads, false);
+    const int hm = p.num_kv_heads / HG;
+    const int64_t Wg = W / HG;
+    const int head0 = (int)(w / Wg);
+    if (head0 >= HG) return;                    // (no range: never merged)
 
     __shared__ int sm_pages[kMaxSplitPages];
     // one wave: its own K tile; several: the block's shared K and V tiles
@@ -455,7 +465,7 @@ void decode_split_kernel(DecodeParams p) {
     uint8_t* const sm_k = sm_kv[0];
     uint8_t* const sm_v = sm_kv[NW == 1 ? 0 : 1];
 
-    const RangeStart rs = locate_range<FP8>(p, w, W);
+    const RangeStart rs = locate_range<FP8>(p, hm, w % Wg, Wg);
     const int64_t N = rs.N, r0 = rs.r0, r1 = rs.r1;
     if (r0 >= r1) {
         // an empty range (N < W): the merge may read this wave's slot 0
@@ -477,15 +487,16 @@ void decode_split_kernel(DecodeParams p) {
     int slot = 0;
     while (pos < r1) {
         const int n = sr.tiles;                               // > 0 here
-        const int kvh = (int)((pos - seq_start) / n);
+        const int kvh = head0 + (int)((pos - seq_start) / n);
         const int i0 = (int)((pos - seq_start) % n);
-        const int64_t seg_end = seq_start + (int64_t)(kvh + 1) * n;
+        const int64_t seg_end = seq_start + (int64_t)(kvh - head0 + 1) * n;
         const int cnt = (int)(min(r1, seg_end) - pos);
         const bool complete = (i0 == 0) && (cnt == n);
         if (i0 == 0 && threadIdx.x == 0) {
             // this wave owns the segment's first tile: tell the merge which
             // waves cover it
-            const int64_t w_last = complete ? w : tile_owner(seg_end - 1, N, W);
+            const int64_t w_last =
+                complete ? w : (int64_t)head0 * Wg + tile_owner(seg_end - 1, N, Wg);
             *reinterpret_cast<int4*>(p.seg_rec + 4 * ((int64_t)b * p.num_kv_heads + kvh)) =
                 int4{(int)w, (int)w_last, slot, 0};
         }
@@ -665,7 +676,7 @@ void decode_split_kernel(DecodeParams p) {
         // ---- next piece ----
         pos += cnt;
         slot = 1;
-        if (pos < r1 && pos == seq_start + (int64_t)n * p.num_kv_heads) {
+        if (pos < r1 && pos == seq_start + (int64_t)n * hm) {
             seq_start = pos;
             do {
                 ++b;

@@ -5,9 +5,16 @@
 //
 // A segment is one (sequence b, kv head g): the 32-token tiles from
 // base = lo rounded down to 32 that cover the key range [lo, L), lo = L - W
-// under a sliding window W.  Segments are laid end to end, sequence-major and
-// kv head minor, into one list of N tiles; wave w of W owns the tiles
-// [floor(w*N/W), floor((w+1)*N/W)).
+// under a sliding window W.  Segments are laid end to end into streams of N
+// tiles, and worker w of W owns the tiles [floor(w*N/W), floor((w+1)*N/W))
+// of its stream.  The GQA split pass with at most kAlignedHeadsMax kv heads
+// keeps one stream per kv head (its sequences' segments in order, hm = 1)
+// and Hkv groups of W/Hkv blocks, block h*W/Hkv + j taking kv head h of
+// range j: the blocks reading the heads of one token range run at the same
+// time, so the heads' rows of a token, which sit together in the pool, are
+// fetched together.  With more kv heads, and in the latent split pass, one
+// stream holds all segments, sequence-major and (virtual) head minor
+// (hm = heads).
 #pragma once
 
 #include "pa_device.h"
@@ -45,26 +52,27 @@ __device__ __forceinline__ int64_t wave_sum64(int64_t v) {
     return v;
 }
 
-// Total tiles N over all segments (every lane gets the sum).
-__device__ __forceinline__ int64_t total_tiles(const DecodeParams& p) {
+// Total tiles N of a stream holding hm segments per sequence (every lane
+// gets the sum).
+__device__ __forceinline__ int64_t total_tiles(const DecodeParams& p, int hm) {
     const int lane = __lane_id();
     int64_t n = 0;
     for (int b0 = 0; b0 < p.num_seqs; b0 += 64) {
         const int b = b0 + lane;
         n += b < p.num_seqs ? (int64_t)seq_range(p, b).tiles : 0;
     }
-    return wave_sum64(n) * p.num_kv_heads;
+    return wave_sum64(n) * hm;
 }
 
-// Sequence whose segments contain global tile `pos` (< N), and the global
+// Sequence whose segments contain stream tile `pos` (< N), and the stream
 // index of its first tile.  Sequences without tiles are skipped.
-__device__ __forceinline__ void find_seq(const DecodeParams& p, int64_t pos, int& b_out,
+__device__ __forceinline__ void find_seq(const DecodeParams& p, int hm, int64_t pos, int& b_out,
                                          int64_t& start_out) {
     const int lane = __lane_id();
     int64_t carry = 0;
     for (int b0 = 0; b0 < p.num_seqs; b0 += 64) {
         const int b = b0 + lane;
-        int64_t n = b < p.num_seqs ? (int64_t)seq_range(p, b).tiles * p.num_kv_heads : 0;
+        int64_t n = b < p.num_seqs ? (int64_t)seq_range(p, b).tiles * hm : 0;
         // inclusive scan across the wave
         int64_t incl = n;
 #pragma unroll
@@ -104,8 +112,8 @@ struct RangeStart {
 // E*i .. E*i + E - 1, read together; the lane sums are scanned across the
 // wave.
 template <int E>
-__device__ __forceinline__ RangeStart locate_range_wave(const DecodeParams& p, int64_t w,
-                                                        int64_t W) {
+__device__ __forceinline__ RangeStart locate_range_wave(const DecodeParams& p, int hm,
+                                                        int64_t w, int64_t W) {
     RangeStart rs;
     const int lane = __lane_id();
     SeqRange mine[E];
@@ -114,7 +122,7 @@ __device__ __forceinline__ RangeStart locate_range_wave(const DecodeParams& p, i
     for (int e = 0; e < E; ++e) {
         const int bb = E * lane + e;
         mine[e] = bb < p.num_seqs ? seq_range(p, bb) : SeqRange{0, 0, 0, 0};
-        n[e] = (int64_t)mine[e].tiles * p.num_kv_heads;
+        n[e] = (int64_t)mine[e].tiles * hm;
         lsum += n[e];
     }
     int64_t incl = lsum;                      // inclusive scan of the lane sums
@@ -154,17 +162,18 @@ __device__ __forceinline__ RangeStart locate_range_wave(const DecodeParams& p, i
 // the kernels that meet large batches (the fp8 ones); it measured slower for
 // the bf16 kernel at 64 sequences although that path does not run there.
 template <bool WIDE>
-__device__ __forceinline__ RangeStart locate_range(const DecodeParams& p, int64_t w, int64_t W) {
-    if (p.num_seqs <= 64) return locate_range_wave<1>(p, w, W);
+__device__ __forceinline__ RangeStart locate_range(const DecodeParams& p, int hm, int64_t w,
+                                                   int64_t W) {
+    if (p.num_seqs <= 64) return locate_range_wave<1>(p, hm, w, W);
     if constexpr (WIDE) {
-        if (p.num_seqs <= 256) return locate_range_wave<4>(p, w, W);
+        if (p.num_seqs <= 256) return locate_range_wave<4>(p, hm, w, W);
     }
     RangeStart rs;
-    rs.N = total_tiles(p);
+    rs.N = total_tiles(p, hm);
     rs.r0 = range_start(w, rs.N, W);
     rs.r1 = range_start(w + 1, rs.N, W);
     if (rs.r0 >= rs.r1) return rs;
-    find_seq(p, rs.r0, rs.b, rs.seq_start);
+    find_seq(p, hm, rs.r0, rs.b, rs.seq_start);
     rs.sr = seq_range(p, rs.b);
     return rs;
 }

@@ -289,7 +289,7 @@ __global__ __launch_bounds__(64 * NW) void mla_split_kernel(DecodeParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t sm_v0[ALIAS ? 16 : T::kMainBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t sm_v1[ALIAS ? 16 : T::kMainBytes];
 
-    const RangeStart rs = locate_range<false>(p, w, W);
+    const RangeStart rs = locate_range<false>(p, p.num_kv_heads, w, W);
     const int64_t N = rs.N, r0 = rs.r0, r1 = rs.r1;
     if (r0 >= r1) {
         // an empty range (N < W): the merge may read this block's slot 0
