@@ -145,8 +145,8 @@ typedef struct {
     int32_t num_splits;        /* decode: 0 = plan chooses; > 0 forces the
                                   number of split-pass pieces (blocks),
                                   rounded up to a multiple of num_kv_heads
-                                  when that is at most 8 (not for a latent
-                                  cache) */
+                                  when that is at most 8 (a latent cache
+                                  with over 64 query heads: of 2) */
     int32_t head_dim_v;        /* value head dim: 0 (or head_dim) = head_dim;
                                   head_dim_v < head_dim selects a latent cache
                                   (decode, bf16, (576, 512) or (288, 256)):
@@ -184,12 +184,14 @@ typedef struct {
  * sequences, laid end to end, are cut into out->num_splits / Hkv equal
  * contiguous pieces; block h * (num_splits / Hkv) + j of the split pass takes
  * piece j of head h, so the blocks reading the kv heads of one token range
- * run side by side (a token's heads are adjacent in the pool).  With more kv
- * heads, and for a latent cache, all (sequence, head) ranges laid end to end
- * are cut into num_splits pieces.  The plan takes as many blocks as the
- * device keeps resident (compute units x resident blocks per unit, rounded
- * down to a multiple of Hkv <= 8), or prob->num_splits (rounded up to one)
- * when that is > 0.
+ * run side by side (a token's heads are adjacent in the pool).  A latent
+ * cache with more than 64 query heads runs as two virtual kv heads over the
+ * same rows, laid out the same way (the two blocks of a token range read the
+ * same rows together).  With more kv heads all (sequence, head) ranges laid
+ * end to end are cut into num_splits pieces.  The plan takes as many blocks
+ * as the device keeps resident (compute units x resident blocks per unit,
+ * rounded down to a multiple of the heads laid out so), or prob->num_splits
+ * (rounded up to one) when that is > 0.
  * A block has one wave per 16 query rows of a kv head (G for decode,
  * G * q_len for verify); its waves walk the same tiles.  Latent cache: the
  * count is rounded up to 2, 4 or 8; with at most 16 query heads over one pool

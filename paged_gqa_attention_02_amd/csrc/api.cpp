@@ -293,7 +293,7 @@ pa_status paged_attn_plan(const pa_problem* prob, int hip_device, pa_plan* out) 
             // a multiple of the per-head streams: block h*W/HG + j takes head
             // h over range j of that head's tiles (a forced count is rounded
             // up, the device count down)
-            const int64_t H = split_head_groups(pr.num_kv_heads, is_latent(pr));
+            const int64_t H = split_head_groups(pr.num_kv_heads * latent_head_split(pr));
             workers = pr.num_splits > 0 ? (workers + H - 1) / H * H
                                         : std::max<int64_t>(H, workers / H * H);
         }
@@ -378,7 +378,7 @@ pa_status decode_prepare(int mode, const pa_plan* plan, const void* q, int64_t q
     // the workspace layout follows from (num_splits, problem): a plan edited
     // after paged_attn_plan must not make the kernels write past it
     if (pl.tokens_per_split != kTile || pl.num_splits < 1 || pl.num_splits > kMaxWorkers ||
-        pl.num_splits % split_head_groups(pr.num_kv_heads, is_latent(pr)) != 0 ||
+        pl.num_splits % split_head_groups(pr.num_kv_heads * latent_head_split(pr)) != 0 ||
         pl.waves_per_block != decode_waves_per_block(pr) ||
         pl.workspace_bytes != (uint64_t)decode_layout(pr, pl.num_splits).total)
         return PA_ERR_PLAN_MISMATCH;

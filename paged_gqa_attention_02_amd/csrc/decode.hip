@@ -452,7 +452,7 @@ void decode_split_kernel(DecodeParams p) {
     // sequence.
     const int64_t W = gridDim.x;
     const int64_t w = blockIdx.x;
-    const int HG = split_head_groups(p.num_kv_heads, false);
+    const int HG = split_head_groups(p.num_kv_heads);
     const int hm = p.num_kv_heads / HG;
     const int64_t Wg = W / HG;
     const int head0 = (int)(w / Wg);

@@ -277,8 +277,17 @@ __global__ __launch_bounds__(64 * NW) void mla_split_kernel(DecodeParams p) {
     const int c = lane & 15, grp = lane >> 4;
     const int cg = 16 * wv + c;                // this lane's query row (head of the kv head)
     const int G = p.group;
+    // Block h*Wg + j takes virtual head h over range j of that head's stream
+    // (the plan makes the block count a multiple of the virtual heads), so
+    // the blocks of the heads of one token range, which read the same rows,
+    // run side by side.
     const int64_t W = gridDim.x;
     const int64_t w = blockIdx.x;
+    const int HG = split_head_groups(p.num_kv_heads);
+    const int hm = p.num_kv_heads / HG;
+    const int64_t Wg = W / HG;
+    const int head0 = (int)(w / Wg);
+    if (head0 >= HG) return;                    // (no range: never merged)
 
     __shared__ int sm_pages[kMlaPages];
     // Two buffers, each its own LDS object: the compiler then knows that the
@@ -289,7 +298,7 @@ __global__ __launch_bounds__(64 * NW) void mla_split_kernel(DecodeParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t sm_v0[ALIAS ? 16 : T::kMainBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t sm_v1[ALIAS ? 16 : T::kMainBytes];
 
-    const RangeStart rs = locate_range<false>(p, p.num_kv_heads, w, W);
+    const RangeStart rs = locate_range<false>(p, hm, w % Wg, Wg);
     const int64_t N = rs.N, r0 = rs.r0, r1 = rs.r1;
     if (r0 >= r1) {
         // an empty range (N < W): the merge may read this block's slot 0
@@ -312,15 +321,16 @@ __global__ __launch_bounds__(64 * NW) void mla_split_kernel(DecodeParams p) {
     int slot = 0;
     while (pos < r1) {
         const int n = sr.tiles;                               // > 0 here
-        const int kvh = (int)((pos - seq_start) / n);
+        const int kvh = head0 + (int)((pos - seq_start) / n);
         const int i0 = (int)((pos - seq_start) % n);
-        const int64_t seg_end = seq_start + (int64_t)(kvh + 1) * n;
+        const int64_t seg_end = seq_start + (int64_t)(kvh - head0 + 1) * n;
         const int cnt = (int)(min(r1, seg_end) - pos);
         const bool complete = (i0 == 0) && (cnt == n);
         if (i0 == 0 && threadIdx.x == 0) {
             // this block owns the segment's first tile: tell the merge which
             // blocks cover it
-            const int64_t w_last = complete ? w : tile_owner(seg_end - 1, N, W);
+            const int64_t w_last =
+                complete ? w : (int64_t)head0 * Wg + tile_owner(seg_end - 1, N, Wg);
             *reinterpret_cast<int4*>(p.seg_rec + 4 * ((int64_t)b * p.num_kv_heads + kvh)) =
                 int4{(int)w, (int)w_last, slot, 0};
         }
@@ -350,7 +360,7 @@ __global__ __launch_bounds__(64 * NW) void mla_split_kernel(DecodeParams p) {
         auto next_piece = [&]() {
             pos += cnt;
             slot = 1;
-            if (pos < r1 && pos == seq_start + (int64_t)n * p.num_kv_heads) {
+            if (pos < r1 && pos == seq_start + (int64_t)n * hm) {
                 seq_start = pos;
                 do {
                     ++b;

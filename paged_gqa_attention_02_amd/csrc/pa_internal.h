@@ -28,14 +28,16 @@ constexpr int split_waves_per_simd(int head_dim, bool fp8, int waves_per_block) 
 // Page-table entries staged in LDS for one chunk of a wave's range: a chunk
 // of T tokens touches at most T/page_size + 2 pages.
 constexpr int kMaxSplitPages = 2080;
-// GQA decode with at most this many kv heads: one key-tile stream per kv
+// Decode with at most this many (virtual) kv heads: one key-tile stream per
 // head, and the split-pass blocks of one token range take its heads side by
-// side (their rows of a token are adjacent in the pool, so they are fetched
-// together).  With more heads (whose rows of a token span more memory than
-// benefits from it) one stream holds all (sequence, kv head) ranges.
+// side (GQA: a token's rows of all heads are adjacent in the pool, so they
+// are fetched together; latent cache: the two virtual heads read the same
+// rows, the second from L2).  With more heads (whose rows of a token span
+// more memory than benefits from it) one stream holds all (sequence, kv
+// head) ranges.
 constexpr int kAlignedHeadsMax = 8;
-__host__ __device__ inline int split_head_groups(int num_kv_heads, bool latent) {
-    return !latent && num_kv_heads <= kAlignedHeadsMax ? num_kv_heads : 1;
+__host__ __device__ inline int split_head_groups(int num_kv_heads) {
+    return num_kv_heads <= kAlignedHeadsMax ? num_kv_heads : 1;
 }
 
 struct DecodeParams {
