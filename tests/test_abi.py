@@ -296,6 +296,25 @@ def test_decode_empty_batch_launches_nothing():
     assert decode_status(plan_kw=dict(num_seqs=0), q=None, out=None, ws=None) == OK
 
 
+def test_decode_blocks_per_kv_head():
+    """With at most 8 kv heads each head has its own stream of key tiles and
+    the split-pass block count is a multiple of the kv heads (a forced count
+    rounded up, the device count down); with more heads (32) one stream holds
+    every range and any count stands; a latent cache with over 64 query
+    heads rounds to its 2 virtual heads."""
+    for kv, hq, forced, want in [(8, 32, 3, 8), (8, 32, 8, 8), (8, 32, 1000, 1000),
+                                 (8, 32, 1001, 1008), (2, 8, 3, 4), (1, 4, 3, 3),
+                                 (32, 32, 3, 3), (3, 12, 0, 1023)]:
+        st, pl = plan_status(num_q_heads=hq, num_kv_heads=kv, num_splits=forced)
+        assert st == OK and pl.num_splits == want, (kv, forced, pl.num_splits)
+    latent = dict(head_dim=576, head_dim_v=512, num_kv_heads=1)
+    assert plan_status(num_q_heads=128, num_splits=3, **latent)[1].num_splits == 4
+    assert plan_status(num_q_heads=16, num_splits=3, **latent)[1].num_splits == 3
+    # an edited count breaks the rule (and the workspace size): refused
+    assert decode_status(plan_kw=dict(num_splits=16),
+                         edit=lambda pl: setattr(pl, "num_splits", 12)) == MISMATCH
+
+
 def test_decode_plan_mode_mismatch():
     assert decode_status(plan_kw=dict(mode=1, total_q=10, max_q_len=10)) == MISMATCH
     assert decode_status(plan_kw=dict(mode=2, max_q_len=2)) == MISMATCH

@@ -90,6 +90,8 @@ def test_long_context_page_size_1_vs_64():
     ([1500, 9, 2100], 16, 4, 128, 256, dict(kv_dtype="fp8_e4m3", scale_range=(0.5, 2.0))),
     ([5000, 129], 8, 1, 64, 1024, dict(window=1500, softcap=8.0)),  # P 1024
     ([3000, 5, 4097, 700], 32, 8, 128, 4096, {}),                  # P 4096: one or two pages
+    ([100, 2000, 37], 12, 3, 128, 16, {}),                         # 3 kv heads: 1023 blocks
+    ([700, 50, 1300], 48, 12, 128, 16, {}),                        # 12 kv heads: one stream
 ])
 def test_shapes(lens, Hq, Hkv, D, P, kw):
     case = rand_case(lens, Hq, Hkv, D, P, 100 + len(lens), **kw)
@@ -98,8 +100,9 @@ def test_shapes(lens, Hq, Hkv, D, P, kw):
 
 @pytest.mark.parametrize("splits", [1, 2, 3, 8, 32, 257, 5000])
 def test_split_counts(splits):
-    """Any cut of the tile list into `splits` ranges gives the same result
-    (5000 ranges exceed the tiles: empty ranges must write nothing)."""
+    """Any cut of the tile lists into ranges gives the same result (the 8 kv
+    heads each cut into splits / 8 ranges, the count rounded up to a multiple
+    of 8; 5000 ranges exceed the tiles: empty ranges must write nothing)."""
     case = rand_case([1, 31, 100, 257, 1000, 4000], 32, 8, 128, 16, 7, softcap=10.0,
                      window=900)
     check(case, num_splits=splits, what=f"S={splits}")
