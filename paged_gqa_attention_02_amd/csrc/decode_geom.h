@@ -6,8 +6,11 @@
 // A segment is one (sequence b, kv head g): the 32-token tiles from
 // base = lo rounded down to 32 that cover the key range [lo, L), lo = L - W
 // under a sliding window W.  Segments are laid end to end into streams of N
-// tiles, and worker w of W owns the tiles [floor(w*N/W), floor((w+1)*N/W))
-// of its stream.  The GQA split pass with at most kAlignedHeadsMax kv heads
+// units, a segment with n tiles taking A + n of them (A = piece_cost: what
+// starting a piece costs, in tiles' worth of work, put in front of its first
+// tile), and worker w of W owns the tiles whose units fall in
+// [floor(w*N/W), floor((w+1)*N/W)) of its stream.  The GQA split pass with
+// at most kAlignedHeadsMax kv heads
 // keeps one stream per kv head (its sequences' segments in order, hm = 1)
 // and Hkv groups of W/Hkv blocks, block h*W/Hkv + j taking kv head h of
 // range j: the blocks reading the heads of one token range run at the same
@@ -36,6 +39,11 @@ struct SeqRange {
     int L, lo, base, tiles;   // tiles: 32-token tiles from base covering [lo, L)
 };
 
+// Stream units of one segment with n tiles (none without tiles).
+__device__ __forceinline__ int seg_units(const DecodeParams& p, int n) {
+    return n > 0 ? n + p.piece_cost : 0;
+}
+
 __device__ __forceinline__ SeqRange seq_range(const DecodeParams& p, int b) {
     SeqRange r;
     r.L = p.seq_lens[b];
@@ -52,27 +60,27 @@ __device__ __forceinline__ int64_t wave_sum64(int64_t v) {
     return v;
 }
 
-// Total tiles N of a stream holding hm segments per sequence (every lane
+// Total units N of a stream holding hm segments per sequence (every lane
 // gets the sum).
 __device__ __forceinline__ int64_t total_tiles(const DecodeParams& p, int hm) {
     const int lane = __lane_id();
     int64_t n = 0;
     for (int b0 = 0; b0 < p.num_seqs; b0 += 64) {
         const int b = b0 + lane;
-        n += b < p.num_seqs ? (int64_t)seq_range(p, b).tiles : 0;
+        n += b < p.num_seqs ? (int64_t)seg_units(p, seq_range(p, b).tiles) : 0;
     }
     return wave_sum64(n) * hm;
 }
 
-// Sequence whose segments contain stream tile `pos` (< N), and the stream
-// index of its first tile.  Sequences without tiles are skipped.
+// Sequence whose segments contain stream unit `pos` (< N), and the stream
+// index of its first unit.  Sequences without tiles are skipped.
 __device__ __forceinline__ void find_seq(const DecodeParams& p, int hm, int64_t pos, int& b_out,
                                          int64_t& start_out) {
     const int lane = __lane_id();
     int64_t carry = 0;
     for (int b0 = 0; b0 < p.num_seqs; b0 += 64) {
         const int b = b0 + lane;
-        int64_t n = b < p.num_seqs ? (int64_t)seq_range(p, b).tiles * hm : 0;
+        int64_t n = b < p.num_seqs ? (int64_t)seg_units(p, seq_range(p, b).tiles) * hm : 0;
         // inclusive scan across the wave
         int64_t incl = n;
 #pragma unroll
@@ -94,14 +102,14 @@ __device__ __forceinline__ void find_seq(const DecodeParams& p, int hm, int64_t 
     start_out = carry;
 }
 
-// First tile of wave w's range.
+// First unit of wave w's range.
 __device__ __forceinline__ int64_t range_start(int64_t w, int64_t N, int64_t W) {
     return w * N / W;
 }
 
-// Where wave (or block) w of W starts: the total N, its range [r0, r1), and,
-// when the range is not empty, the sequence b holding tile r0, the global
-// index of b's first tile and b's key range.
+// Where wave (or block) w of W starts: the total N, its range [r0, r1) (in
+// stream units), and, when the range is not empty, the sequence b holding
+// unit r0, the stream index of b's first unit and b's key range.
 struct RangeStart {
     int64_t N, r0, r1, seq_start;
     int b;
@@ -122,7 +130,7 @@ __device__ __forceinline__ RangeStart locate_range_wave(const DecodeParams& p, i
     for (int e = 0; e < E; ++e) {
         const int bb = E * lane + e;
         mine[e] = bb < p.num_seqs ? seq_range(p, bb) : SeqRange{0, 0, 0, 0};
-        n[e] = (int64_t)mine[e].tiles * hm;
+        n[e] = (int64_t)seg_units(p, mine[e].tiles) * hm;
         lsum += n[e];
     }
     int64_t incl = lsum;                      // inclusive scan of the lane sums
@@ -184,7 +192,7 @@ __device__ __forceinline__ int64_t part_row(const DecodeParams& p, int64_t w, in
     return (w * 2 + slot) * p.rows;
 }
 
-// Wave holding global tile t: the largest w with floor(w*N/W) <= t.
+// Wave holding stream unit t: the largest w with floor(w*N/W) <= t.
 __device__ __forceinline__ int64_t tile_owner(int64_t t, int64_t N, int64_t W) {
     return ((t + 1) * W + N - 1) / N - 1;
 }

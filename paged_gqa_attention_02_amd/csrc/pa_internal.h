@@ -28,6 +28,16 @@ constexpr int split_waves_per_simd(int head_dim, bool fp8, int waves_per_block) 
 // Page-table entries staged in LDS for one chunk of a wave's range: a chunk
 // of T tokens touches at most T/page_size + 2 pages.
 constexpr int kMaxSplitPages = 2080;
+// What starting a piece of a segment costs the split pass, in tiles' worth
+// of work (the stream-K cut charges it to every segment).
+#ifndef PA_FP8_PIECE_COST
+#define PA_FP8_PIECE_COST 4
+#endif
+#ifndef PA_BF16_PIECE_COST
+#define PA_BF16_PIECE_COST 1
+#endif
+constexpr int kFp8PieceCost = PA_FP8_PIECE_COST;
+constexpr int kBf16PieceCost = PA_BF16_PIECE_COST;
 // Decode with at most this many (virtual) kv heads: one key-tile stream per
 // head, and the split-pass blocks of one token range take its heads side by
 // side (GQA: a token's rows of all heads are adjacent in the pool, so they
@@ -76,6 +86,9 @@ struct DecodeParams {
     int32_t* seg_rec;         // [B * Hkv][4]: for a segment with keys, the waves owning its
                               // first and last tile and the first one's slot (written by
                               // the owner of the first tile).  Split pass -> merge.
+    int32_t piece_cost;       // tiles' worth of work a piece costs beyond its tiles: the
+                              // stream-K cut gives every segment this much extra length
+                              // in front of its first tile (0: tiles only)
 };
 
 struct GatherParams {

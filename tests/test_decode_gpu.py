@@ -229,3 +229,21 @@ def test_batches_between_64_and_256_with_empty_sequences(kv_dtype, splits):
     out, _ = check(case, num_splits=splits or None, what=f"B150 {kv_dtype} splits={splits}")
     for b in np.flatnonzero(lens == 0):
         assert not out[b].any()
+
+
+@pytest.mark.parametrize("kv_dtype", ["fp8_e4m3", "bf16"])
+@pytest.mark.parametrize("splits", [0, 16, 600, 4000])
+def test_many_short_sequences(kv_dtype, splits):
+    """300 sequences, most of 1..70 tokens: the ranges charge every segment
+    a fixed cost in front of its first tile, so here many ranges begin or end
+    in that part, some hold no tile at all, and with 4000 splits most are
+    empty.  8 kv heads (one stream per head) at fp8 and bf16."""
+    rng = np.random.default_rng(91)
+    lens = rng.integers(1, 71, size=300)
+    lens[rng.choice(300, size=12, replace=False)] = rng.integers(500, 3000, size=12)
+    lens[[5, 64, 200]] = 0
+    case = rand_case(lens, 32, 8, 128, 16, 92, kv_dtype=kv_dtype,
+                     scale_range=(0.5, 2.0) if kv_dtype != "bf16" else None)
+    out, _ = check(case, num_splits=splits or None, what=f"B300 short {kv_dtype} splits={splits}")
+    for b in np.flatnonzero(lens == 0):
+        assert not out[b].any()
