@@ -444,13 +444,12 @@ pa_status decode_prepare(int mode, const pa_plan* plan, const void* q, int64_t q
     p.desc_per_seq = ex.per_seq;
     p.out = out;
     p.out_stride_b = out_stride_b;
-    // fp8 pieces cost about two tiles' worth of wave time beyond their tiles
-    // (the next sequence's page list, Q rows and first tile are waited for),
-    // so the ranges charge each segment that much: a range holding many
-    // short sequences gets fewer tiles
-    p.piece_cost = (split == 1 && !is_latent(pr))
-                       ? (pr.kv_dtype == PA_KV_FP8_E4M3 ? kFp8PieceCost : kBf16PieceCost)
-                       : 0;
+    // a piece costs its wave work beyond its tiles (the next sequence's page
+    // list, Q rows and first tile are waited for); the ranges charge each
+    // segment that much, in tiles' worth, so a range holding many short
+    // sequences gets fewer tiles
+    p.piece_cost = is_latent(pr) ? kLatentPieceCost
+                   : pr.kv_dtype == PA_KV_FP8_E4M3 ? kFp8PieceCost : kBf16PieceCost;
     return PA_OK;
 }
 

@@ -317,14 +317,22 @@ __global__ __launch_bounds__(64 * NW) void mla_split_kernel(DecodeParams p) {
     MlaOffs<DQK, DV> lo;
     lo.init(c, grp, lane);
 
+    // (stream units: a segment of n tiles is piece_cost units, then one a
+    // tile)
+    const int A = p.piece_cost;
     int64_t pos = r0;
     int slot = 0;
     while (pos < r1) {
         const int n = sr.tiles;                               // > 0 here
-        const int kvh = head0 + (int)((pos - seq_start) / n);
-        const int i0 = (int)((pos - seq_start) % n);
-        const int64_t seg_end = seq_start + (int64_t)(kvh - head0 + 1) * n;
-        const int cnt = (int)(min(r1, seg_end) - pos);
+        const int nu = n + A;                                 // units of a segment
+        const int kvh = head0 + (int)((pos - seq_start) / nu);
+        const int64_t seg_end = seq_start + (int64_t)(kvh - head0 + 1) * nu;
+        const int64_t u0 = seg_end - n;                       // unit of the first tile
+        // the segment's tiles whose units are in [pos, r1); none when the
+        // range ends in front of its first tile
+        const int i0 = (int)max(pos - u0, (int64_t)0);
+        const int cnt = (int)(min(r1, seg_end) - u0) - i0;
+        if (cnt <= 0) break;
         const bool complete = (i0 == 0) && (cnt == n);
         if (i0 == 0 && threadIdx.x == 0) {
             // this block owns the segment's first tile: tell the merge which
@@ -358,9 +366,9 @@ __global__ __launch_bounds__(64 * NW) void mla_split_kernel(DecodeParams p) {
             __syncthreads();
         };
         auto next_piece = [&]() {
-            pos += cnt;
+            pos = min(r1, seg_end);
             slot = 1;
-            if (pos < r1 && pos == seq_start + (int64_t)n * hm) {
+            if (pos < r1 && pos == seq_start + (int64_t)nu * hm) {
                 seq_start = pos;
                 do {
                     ++b;

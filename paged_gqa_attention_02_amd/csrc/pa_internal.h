@@ -36,8 +36,12 @@ constexpr int kMaxSplitPages = 2080;
 #ifndef PA_BF16_PIECE_COST
 #define PA_BF16_PIECE_COST 1
 #endif
+#ifndef PA_LATENT_PIECE_COST
+#define PA_LATENT_PIECE_COST 3
+#endif
 constexpr int kFp8PieceCost = PA_FP8_PIECE_COST;
 constexpr int kBf16PieceCost = PA_BF16_PIECE_COST;
+constexpr int kLatentPieceCost = PA_LATENT_PIECE_COST;
 // Decode with at most this many (virtual) kv heads: one key-tile stream per
 // head, and the split-pass blocks of one token range take its heads side by
 // side (GQA: a token's rows of all heads are adjacent in the pool, so they
