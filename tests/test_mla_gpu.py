@@ -69,6 +69,21 @@ def test_mla_forced_splits(splits):
     check(case, num_splits=splits, what=f"splits={splits}")
 
 
+@pytest.mark.parametrize("splits", [0, 37, 500])
+def test_mla_many_short_sequences(splits):
+    """80 sequences of 1..40 tokens and two long ones: the ranges charge
+    every segment a fixed cost in front of its first tile, so many ranges
+    begin or end inside that part and some hold no tile."""
+    rng = np.random.default_rng(13)
+    lens = rng.integers(1, 41, size=82)
+    lens[[10, 60]] = [1500, 900]
+    lens[[3, 70]] = 0
+    case = mla_case(lens, 16, 1, 576, 512, 16, 14)
+    out, _ = check(case, num_splits=splits or None, what=f"short splits={splits}")
+    for b in np.flatnonzero(lens == 0):
+        assert not out[b].any()
+
+
 def test_mla_extras():
     """Sinks, per-request descales and ALiBi slopes on a latent cache."""
     case = I.with_extras(mla_case([300, 1200, 45], 16, 1, 576, 512, 16, 11), 12,
