@@ -699,6 +699,9 @@ pa_status paged_attn_extend(const pa_plan* plan, const void* q, const void* k_ne
 
     ExtendParams p;
     memset(&p, 0, sizeof p);
+    // (a piece costs its block a prologue and an output beyond its tiles:
+    // the item stream charges each item that many tiles' worth)
+    p.piece_cost = kExtendPieceCost;
     {
         const ExtLayout L = extend_layout(pr, pl.num_splits);
         char* ws = static_cast<char*>(workspace);

@@ -696,7 +696,8 @@ __device__ __forceinline__ int64_t ext_part_row(int64_t w, int slot, int r) {
 }
 
 // ---------------------------------------------------------------------------
-// Tile prefix over the items: pfx[i] = key tiles of items 0..i-1 (one block).
+// Unit prefix over the items: pfx[i] = stream units of items 0..i-1 (one
+// block).
 // ---------------------------------------------------------------------------
 constexpr int kScanThreads = 1024;
 
@@ -708,7 +709,12 @@ __global__ __launch_bounds__(kScanThreads) void extend_scan_kernel(ExtendParams 
     if (threadIdx.x == 0) p.pfx[0] = 0;
     for (int64_t c0 = 0; c0 < items; c0 += kScanThreads) {
         const int64_t i = c0 + threadIdx.x;
-        int v = i < items ? item_of(p, i).ntiles : 0;       // < 2^24 each
+        // an item with tiles takes piece_cost units, then one a tile
+        int v = 0;
+        if (i < items) {
+            const int nt = item_of(p, i).ntiles;           // < 2^24
+            v = nt > 0 ? nt + p.piece_cost : 0;
+        }
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
             const int u = __shfl_up(v, d, 64);
@@ -925,9 +931,12 @@ __device__ __forceinline__ void extend_piece(const ExtendParams& pk, const Item&
 }
 
 // ---------------------------------------------------------------------------
-// Persistent blocks: block w owns key tiles [w*N/W, (w+1)*N/W) of the items
-// laid end to end (N tiles in all), cut into pieces at item boundaries.  The
-// owner of an item's first tile records which blocks cover it.
+// Persistent blocks: the items are laid end to end as a stream of N units,
+// an item with tiles taking piece_cost units (what starting a piece costs a
+// block, in tiles' worth) and then one unit a key tile; block w owns the
+// tiles whose units fall in [w*N/W, (w+1)*N/W), cut into pieces at item
+// boundaries.  The owner of an item's first tile records which blocks cover
+// it.
 // ---------------------------------------------------------------------------
 template <int D, bool FP8>
 constexpr int ext_occupancy() { return FP8 ? 1 : kExtOccupancy; }
@@ -958,7 +967,7 @@ void extend_kernel(ExtendParams p) {
             p.part_lse[ext_part_row(w, 0, r)] = -INFINITY;
         return;
     }
-    // the item holding tile r0: the last i with pfx[i] <= r0
+    // the item holding unit r0: the last i with pfx[i] <= r0
     int64_t lo = 0, hi = items;
     while (hi - lo > 1) {
         const int64_t mid = (lo + hi) >> 1;
@@ -971,9 +980,13 @@ void extend_kernel(ExtendParams p) {
     while (pos < r1) {
         while (p.pfx[i + 1] <= pos) ++i;                 // (items without tiles)
         const Item it = item_of(p, i);
-        const int64_t start = p.pfx[i], end = p.pfx[i + 1];
-        const int from = (int)(pos - start);
-        const int to = (int)(min(r1, end) - start);
+        const int64_t end = p.pfx[i + 1];
+        const int64_t u0 = end - it.ntiles;              // unit of the item's first tile
+        // the item's tiles whose units are in [pos, r1); none when the range
+        // ends in front of its first tile
+        const int from = (int)max(pos - u0, (int64_t)0);
+        const int to = (int)(min(r1, end) - u0);
+        if (to <= from) break;
         const bool complete = from == 0 && to == it.ntiles;
         if (from == 0 && threadIdx.x == 0) {
             // the owner of the item's first tile: which blocks cover it
@@ -981,7 +994,7 @@ void extend_kernel(ExtendParams p) {
             *reinterpret_cast<int4*>(p.rec + 4 * i) = int4{(int)w, (int)w_last, slot, 0};
         }
         extend_piece<D, FP8, MODE>(p, it, from, to, complete, w, slot, L);
-        pos += to - from;
+        pos = min(r1, end);
         slot = 1;
     }
 }

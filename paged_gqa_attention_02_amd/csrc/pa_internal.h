@@ -42,6 +42,10 @@ constexpr int kMaxSplitPages = 2080;
 constexpr int kFp8PieceCost = PA_FP8_PIECE_COST;
 constexpr int kBf16PieceCost = PA_BF16_PIECE_COST;
 constexpr int kLatentPieceCost = PA_LATENT_PIECE_COST;
+#ifndef PA_EXTEND_PIECE_COST
+#define PA_EXTEND_PIECE_COST 6
+#endif
+constexpr int kExtendPieceCost = PA_EXTEND_PIECE_COST;
 // Decode with at most this many (virtual) kv heads: one key-tile stream per
 // head, and the split-pass blocks of one token range take its heads side by
 // side (GQA: a token's rows of all heads are adjacent in the pool, so they
@@ -134,10 +138,11 @@ struct ExtendParams {
     int32_t desc_per_seq;
     void* out;                // bf16 [total_q, Hq, D]
     // persistent-block split of the key tiles (workspace)
-    int64_t* pfx;             // [items + 1]: key tiles of items 0..i-1
+    int64_t* pfx;             // [items + 1]: stream units of items 0..i-1
     int32_t* rec;             // [items][4]: blocks covering an item, first block's slot
     float* part_lse;          // [workers][2][rows per block] (log2 domain)
     float* part_o;            // [workers][2][rows per block][D]
+    int32_t piece_cost;       // units an item with tiles takes in front of its first tile
 };
 
 struct AppendParams {
