@@ -181,9 +181,11 @@ typedef struct {
  *
  * Decode with Hkv <= 8 kv heads: for each kv head h, the 32-token tiles of
  * its key ranges [lo, L) (lo = max(0, L-W) with a window) over all
- * sequences, laid end to end, are cut into out->num_splits / Hkv equal
- * contiguous pieces; block h * (num_splits / Hkv) + j of the split pass takes
- * piece j of head h, so the blocks reading the kv heads of one token range
+ * sequences, laid end to end, are cut into out->num_splits / Hkv contiguous
+ * pieces of equal weight, a key range weighing its tiles plus a fixed number
+ * of tiles' worth (what starting a piece costs a block: 1 at bf16, 4 at fp8,
+ * 3 for a latent cache); block h * (num_splits / Hkv) + j of the split pass
+ * takes piece j of head h, so the blocks reading the kv heads of one token range
  * run side by side (a token's heads are adjacent in the pool).  A latent
  * cache with more than 64 query heads runs as two virtual kv heads over the
  * same rows, laid out the same way (the two blocks of a token range read the
@@ -204,10 +206,11 @@ typedef struct {
  * the first query token.
  * Extend: the key tiles (64 keys) of every item -- a sequence, a kv head and
  * one block's worth of its new (token, query head) rows -- laid end to end,
- * are cut into out->num_splits equal contiguous pieces, one per persistent
- * block (as many as the device keeps resident, or prob->num_splits when
- * > 0).  The workspace holds the items' tile prefix sums, the blocks covering
- * each item, and two partial slots per block.
+ * are cut into out->num_splits contiguous pieces of equal weight (an item
+ * weighing its tiles plus 6), one per persistent block (as many as the
+ * device keeps resident, or prob->num_splits when > 0).  The workspace holds
+ * the items' weight prefix sums, the blocks covering each item, and two
+ * partial slots per block.
  *
  * hip_device >= 0 queries that device's compute-unit count; hip_device < 0
  * plans for an MI355X (256 compute units) without touching any device.
@@ -238,8 +241,8 @@ pa_status paged_attn_plan(const pa_problem* prob, int hip_device, pa_plan* out);
  *                 or NULL
  *
  * Two kernels run: the key ranges of all (sequence, kv head) pairs, laid end
- * to end, are cut into plan->num_splits equal pieces, one per persistent
- * block of the split pass; a second kernel merges by log-sum-exp every pair
+ * to end, are cut into plan->num_splits pieces of equal weight (see
+ * paged_attn_plan), one per persistent block of the split pass; a second kernel merges by log-sum-exp every pair
  * that spans several pieces (the split/merge of `_fwd_grouped_kernel_stage1`
  * / `_fwd_kernel_stage2`).
  */
