@@ -242,9 +242,9 @@ pa_status paged_attn_plan(const pa_problem* prob, int hip_device, pa_plan* out);
  *
  * Two kernels run: the key ranges of all (sequence, kv head) pairs, laid end
  * to end, are cut into plan->num_splits pieces of equal weight (see
- * paged_attn_plan), one per persistent block of the split pass; a second kernel merges by log-sum-exp every pair
- * that spans several pieces (the split/merge of `_fwd_grouped_kernel_stage1`
- * / `_fwd_kernel_stage2`).
+ * paged_attn_plan), one per persistent block of the split pass; a second
+ * kernel merges by log-sum-exp every pair that spans several pieces (the
+ * split/merge of `_fwd_grouped_kernel_stage1` / `_fwd_kernel_stage2`).
  */
 pa_status paged_attn_decode(const pa_plan* plan,
                             const void* q, int64_t q_stride_b,
