@@ -967,12 +967,18 @@ void extend_kernel(ExtendParams p) {
             p.part_lse[ext_part_row(w, 0, r)] = -INFINITY;
         return;
     }
-    // the item holding unit r0: the last i with pfx[i] <= r0
-    int64_t lo = 0, hi = items;
-    while (hi - lo > 1) {
-        const int64_t mid = (lo + hi) >> 1;
-        if (p.pfx[mid] <= r0) lo = mid;
-        else hi = mid;
+    // the item holding unit r0: the last i with pfx[i] <= r0, by a 64-way
+    // search (each round a lane reads one candidate of [lo, lo + cnt); the
+    // last one at or below r0 narrows the range to its step)
+    int64_t lo = 0, cnt = items;         // pfx[lo] <= r0 < pfx[lo + cnt]
+    while (cnt > 1) {
+        const int64_t step = (cnt + 63) / 64;
+        const int64_t k = lo + (int64_t)(threadIdx.x & 63) * step;
+        const bool at_or_below = k < lo + cnt && p.pfx[k] <= r0;
+        const int j = 63 - __builtin_clzll(__ballot(at_or_below));   // lane 0's k = lo is
+        const int64_t kj = lo + (int64_t)j * step;                   // always at or below
+        cnt = min(step, lo + cnt - kj);
+        lo = kj;
     }
     int64_t i = lo;
     int64_t pos = r0;
