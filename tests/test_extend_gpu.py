@@ -97,6 +97,19 @@ def test_extend_persistent_block_counts(splits):
     check(case, f"{splits} blocks", num_splits=splits)
 
 
+@pytest.mark.parametrize("splits", [0, 50, 333])
+def test_extend_many_short_items(splits):
+    """40 sequences with short contexts and few new tokens: every item is
+    charged a fixed cost in front of its key tiles, so many block ranges
+    begin or end inside that part and some hold no tile."""
+    rng = np.random.default_rng(71)
+    ctx = [int(x) for x in rng.integers(0, 200, size=40)]
+    ql = [int(x) for x in rng.integers(1, 40, size=40)]
+    ctx[7], ql[7] = 2500, 300
+    case = case_of(ctx, ql, 8, 2, 64, 16, 710)
+    check(case, f"40 short, {splits} blocks", num_splits=splits)
+
+
 @pytest.mark.parametrize("kw", [dict(window=300), dict(kv_dtype="fp8_e4m3",
                                                        scale_range=(0.5, 2.0))])
 def test_extend_parts_with_window_and_fp8(kw):
