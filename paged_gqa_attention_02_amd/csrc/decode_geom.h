@@ -10,14 +10,13 @@
 // starting a piece costs, in tiles' worth of work, put in front of its first
 // tile), and worker w of W owns the tiles whose units fall in
 // [floor(w*N/W), floor((w+1)*N/W)) of its stream.  The GQA split pass with
-// at most kAlignedHeadsMax kv heads
-// keeps one stream per kv head (its sequences' segments in order, hm = 1)
-// and Hkv groups of W/Hkv blocks, block h*W/Hkv + j taking kv head h of
-// range j: the blocks reading the heads of one token range run at the same
-// time, so the heads' rows of a token, which sit together in the pool, are
-// fetched together.  With more kv heads, and in the latent split pass, one
-// stream holds all segments, sequence-major and (virtual) head minor
-// (hm = heads).
+// at most kAlignedHeadsMax kv heads keeps one stream per kv head (its
+// sequences' segments in order, hm = 1) and Hkv groups of W/Hkv blocks,
+// block h*W/Hkv + j taking kv head h of range j: the blocks reading the
+// heads of one token range run at the same time, so the heads' rows of a
+// token, which sit together in the pool, are fetched together.  With more kv
+// heads, and in the latent split pass, one stream holds all segments,
+// sequence-major and (virtual) head minor (hm = heads).
 #pragma once
 
 #include "pa_device.h"
